@@ -1,0 +1,175 @@
+/*
+ * nsa.h -- C ABI of libnsa.so: the VideoNSA attention layer forward pass on
+ * AMD Instinct MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * What the layer computes (VideoNSA paper summary page, "Method"; model card,
+ * "Model Architecture"; paper summary "Key claims", §2.2):
+ *   tokens are split by position into vision and text tokens. Vision tokens
+ *   run the three NSA branches -- compression (each 64-token frame block is
+ *   averaged and mapped through a learned linear map into one block key and
+ *   value, then attended), selection (the top-k blocks ranked by an
+ *   importance score are attended token by token) and a causal sliding window
+ *   -- and per-head sigmoid gates mix the three outputs. Text tokens use dense
+ *   causal GQA over every earlier position. Outputs land at the tokens'
+ *   original positions.
+ * Readings where the pages leave a step open (all shared with the oracle):
+ *   a compressed block is visible once complete; the learned map is y = W x
+ *   on the block mean (no bias), one W for keys and one for values, shared by
+ *   the KV heads; query head h reads KV head h / (Hq/Hkv); a block's
+ *   importance for KV group g is the sum over the group's query heads of the
+ *   normalised compression-attention probability; ties go to the lower block
+ *   index; the query's own block is always selected and counts toward k; the
+ *   window holds exactly `window` keys including the query; a query with no
+ *   complete block gets a zero compression output; vision queries see vision
+ *   keys only; the softmax scale defaults to 1/sqrt(head_dim).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device memory; "host" marks host memory.
+ *   - All tensors are dense, row-major, with the last dimension contiguous,
+ *     and 16-byte aligned.
+ *   - The caller owns every buffer, including the workspace; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     asynchronously; the call does not synchronise.
+ *   - Every argument is validated before anything is enqueued. On any
+ *     non-OK status nothing has been written or launched.
+ *   - Kernel faults surface at the caller's next synchronisation;
+ *     NSA_ERR_HIP reports errors returned by launches themselves.
+ */
+#ifndef NSA_H_
+#define NSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NSA_OK = 0,
+  NSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer    */
+  NSA_ERR_UNSUPPORTED = 2, /* valid arguments outside what the kernels take */
+  NSA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than needed */
+  NSA_ERR_HIP = 4          /* a HIP launch reported an error                */
+} nsa_status;
+
+typedef enum {
+  NSA_DTYPE_BF16 = 0, /* q, k, v, w_cmp_* in bfloat16                          */
+  NSA_DTYPE_FP32 = 1  /* q, k, v, w_cmp_* in float32 (block scores computed from
+                         split-bf16 operands to near-fp32 accuracy)             */
+} nsa_dtype;
+
+/* ------------------------------------------------------------------ prefill
+ * One sequence of n_tokens tokens. Supported: head_dim in {64, 128},
+ * block_size == 64, n_q_heads % n_kv_heads == 0 with at most 8 query heads per
+ * KV head, the vision tokens forming one contiguous run (text may precede
+ * and/or follow it), top_k >= 1, window >= 1. */
+typedef struct {
+  int64_t n_tokens;   /* N = vision + text tokens                                 */
+  int32_t n_q_heads;  /* Hq                                                       */
+  int32_t n_kv_heads; /* Hkv                                                      */
+  int32_t head_dim;   /* d                                                        */
+  int32_t block_size; /* B: compression block == selection block (64)            */
+  int32_t top_k;      /* k: selected blocks per (query, KV group), own block incl. */
+  int32_t window;     /* w: sliding-window keys, the query included              */
+  float scale;        /* softmax scale; <= 0 selects 1/sqrt(d)                    */
+  int32_t dtype;      /* nsa_dtype of q, k, v, w_cmp_k, w_cmp_v                   */
+} nsa_prefill_desc;
+
+/* Bytes of device workspace nsa_prefill needs for this descriptor and mask.
+ * is_vision: host, [N] uint8 (1 = vision token). Returns 0 and leaves
+ * *bytes untouched if the arguments are invalid or unsupported (the status
+ * says which). */
+nsa_status nsa_prefill_workspace_size(const nsa_prefill_desc *desc,
+                                      const uint8_t *is_vision,
+                                      size_t *bytes);
+
+/* Forward pass of the layer for one sequence.
+ *   q            device [N, Hq, d]   (dtype)   queries after positional encoding
+ *   k, v         device [N, Hkv, d]  (dtype)   keys / values
+ *   is_vision    host   [N] uint8              1 = vision token, 0 = text token
+ *   w_cmp_k      device [d, d]       (dtype)   compression map for keys, y = W x
+ *   w_cmp_v      device [d, d]       (dtype)   compression map for values
+ *   gate_logits  device [N, Hq, 3]   float32   (cmp, sel, swa) logits; a
+ *                sigmoid turns them into gates; text rows are not read
+ *   out          device [N, Hq, d]   float32   written for every token
+ * Optional outputs (NULL to skip):
+ *   k_cmp_out, v_cmp_out device [N_v/B, Hkv, d] float32  compressed keys/values
+ *                                                          before bf16 rounding
+ *   sel_idx_out  device [N_v, Hkv, top_k] int32  selected block indices per
+ *                vision query (vision-local numbering), ascending, -1 padded
+ *   lse_out      device [N_v, Hq] float32  log-sum-exp of the compression
+ *                attention logits (-inf where no block is complete yet)
+ *   workspace    device, >= nsa_prefill_workspace_size bytes, 256-B aligned
+ */
+nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *k,
+                       const void *v, const uint8_t *is_vision, const void *w_cmp_k,
+                       const void *w_cmp_v, const float *gate_logits, float *out,
+                       float *k_cmp_out, float *v_cmp_out, int32_t *sel_idx_out,
+                       float *lse_out, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* ------------------------------------------------------------------- decode
+ * One new query per sequence, at the last slot (L-1) of its vision cache: its
+ * own key and value are already in slot L-1, every one of the L/B compressed
+ * blocks is complete, and block L/B-1 is the query's own. Supported: bf16,
+ * head_dim in {64, 128}, block_size == 64, cache_len % 64 == 0, at most 8
+ * query heads per KV head, top_k <= 64, window <= cache_len. */
+typedef struct {
+  int32_t batch;      /* Bt sequences                        */
+  int32_t cache_len;  /* L tokens per sequence               */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t top_k;
+  int32_t window;
+  float scale;        /* <= 0 selects 1/sqrt(d)              */
+  int32_t dtype;      /* NSA_DTYPE_BF16 only                 */
+} nsa_decode_desc;
+
+nsa_status nsa_decode_workspace_size(const nsa_decode_desc *desc, size_t *bytes);
+
+/*   q            device [Bt, Hq, d]        bf16
+ *   k_cache      device [Bt, L, Hkv, d]    bf16
+ *   v_cache      device [Bt, L, Hkv, d]    bf16
+ *   k_cmp, v_cmp device [Bt, L/B, Hkv, d]  bf16  compressed cache (for example
+ *                from nsa_cmp_pool)
+ *   gate_logits  device [Bt, Hq, 3]        float32
+ *   out          device [Bt, Hq, d]        float32
+ *   sel_idx_out  device [Bt, Hkv, top_k]   int32 or NULL (ascending, -1 padded)
+ *   lse_out      device [Bt, Hq]           float32 or NULL
+ */
+nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_cache,
+                      const void *v_cache, const void *k_cmp, const void *v_cmp,
+                      const float *gate_logits, float *out, int32_t *sel_idx_out,
+                      float *lse_out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* ------------------------------------------------------------- compression
+ * The compression branch's pooling step on its own (VideoNSA model card,
+ * "Model Architecture": frame KV blocks are averaged; paper summary,
+ * "Method": a learned map turns each block into one key/value): for each of
+ * the n_rows/B complete blocks b and head g,
+ *   out[b, g, :] = W * mean(x[b*B .. b*B+B-1, g, :]).
+ *   x     device [n_rows, n_heads, d] (dtype)
+ *   w     device [d, d]               (dtype), y = W x
+ *   out_bf16 device [n_rows/B, n_heads, d] bf16 or NULL
+ *   out_f32  device [n_rows/B, n_heads, d] float32 or NULL
+ * Used to build the compressed cache that nsa_decode reads. */
+nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim,
+                        int32_t block_size, int32_t dtype, const void *x, const void *w,
+                        void *out_bf16, float *out_f32, void *stream);
+
+/* Static description of a status code. */
+const char *nsa_status_string(nsa_status status);
+
+/* Library version, "major.minor.patch". */
+const char *nsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_H_ */

@@ -1,0 +1,256 @@
+"""Thin ctypes binding over libnsa.so (the C ABI declared in include/nsa.h).
+
+Only argument marshalling lives here: torch tensors supply device memory and
+the current HIP stream; every step of the layer runs in the library's HIP
+kernels. Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnsa.so")
+
+NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP = range(5)
+NSA_DTYPE_BF16, NSA_DTYPE_FP32 = 0, 1
+
+EXPORTED = (
+    "nsa_prefill_workspace_size", "nsa_prefill", "nsa_decode_workspace_size", "nsa_decode",
+    "nsa_cmp_pool", "nsa_status_string", "nsa_version",
+)
+
+
+class NsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("cache_len", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if libnsa.so has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m sparse_attention_long_nsa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.c_size_t
+        L.nsa_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), P, ctypes.POINTER(S)]
+        L.nsa_prefill_workspace_size.restype = ctypes.c_int
+        L.nsa_prefill.argtypes = [ctypes.POINTER(PrefillDesc)] + [P] * 13 + [S, P]
+        L.nsa_prefill.restype = ctypes.c_int
+        L.nsa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.POINTER(S)]
+        L.nsa_decode_workspace_size.restype = ctypes.c_int
+        L.nsa_decode.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 10 + [S, P]
+        L.nsa_decode.restype = ctypes.c_int
+        L.nsa_cmp_pool.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, P, P, P, P, P]
+        L.nsa_cmp_pool.restype = ctypes.c_int
+        L.nsa_status_string.argtypes = [ctypes.c_int]
+        L.nsa_status_string.restype = ctypes.c_char_p
+        L.nsa_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().nsa_status_string(status).decode()
+
+
+def version() -> str:
+    return lib().nsa_version().decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data_as(ctypes.c_void_p)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_dev(name, t, dtype, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _mask_host(is_vision) -> np.ndarray:
+    if isinstance(is_vision, torch.Tensor):
+        is_vision = is_vision.detach().cpu().numpy()
+    return np.ascontiguousarray(is_vision, dtype=np.uint8)
+
+
+def prefill_desc(q, k, top_k, window, block=64, scale=0.0) -> PrefillDesc:
+    n, hq, d = q.shape
+    dt = {torch.bfloat16: NSA_DTYPE_BF16, torch.float32: NSA_DTYPE_FP32}[q.dtype]
+    return PrefillDesc(n, hq, k.shape[1], d, block, top_k, window, float(scale), dt)
+
+
+def prefill_workspace_size(desc: PrefillDesc, is_vision) -> int:
+    mask = _mask_host(is_vision)
+    n = ctypes.c_size_t(0)
+    st = lib().nsa_prefill_workspace_size(ctypes.byref(desc), _ptr(mask), ctypes.byref(n))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_prefill_workspace_size")
+    return n.value
+
+
+def prefill(q, k, v, is_vision, w_cmp_k, w_cmp_v, gate_logits, top_k, window, block=64,
+            scale=0.0, out=None, want_kcmp=False, want_sel=False, want_lse=False,
+            workspace=None, stream=None) -> dict:
+    """Runs nsa_prefill. q [N,Hq,d], k/v [N,Hkv,d], w_cmp_* [d,d] (bf16 or fp32,
+    all the same dtype), gate_logits [N,Hq,3] fp32 on the device; is_vision [N]
+    on the host (numpy or CPU tensor). Returns a dict with "out" (fp32) and
+    the requested optional outputs."""
+    desc = prefill_desc(q, k, top_k, window, block, scale)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    for name, t, shape in (("q", q, (n, hq, d)), ("k", k, (n, hkv, d)), ("v", v, (n, hkv, d)),
+                           ("w_cmp_k", w_cmp_k, (d, d)), ("w_cmp_v", w_cmp_v, (d, d))):
+        _check_dev(name, t, q.dtype, shape)
+    _check_dev("gate_logits", gate_logits, torch.float32, (n, hq, 3))
+    mask = _mask_host(is_vision)
+    if mask.shape != (n,):
+        raise ValueError("is_vision must have one entry per token")
+    n_vis = int(mask.astype(bool).sum())
+    dev = q.device
+    res = {}
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (n, hq, d))
+    res["out"] = out
+    kc = vc = sel = lse = None
+    if want_kcmp:
+        kc = res["k_cmp"] = torch.empty((n_vis // block, hkv, d), dtype=torch.float32, device=dev)
+        vc = res["v_cmp"] = torch.empty((n_vis // block, hkv, d), dtype=torch.float32, device=dev)
+    if want_sel:
+        sel = res["sel_idx"] = torch.empty((n_vis, hkv, top_k), dtype=torch.int32, device=dev)
+    if want_lse:
+        lse = res["lse"] = torch.empty((n_vis, hq), dtype=torch.float32, device=dev)
+    ws_bytes = prefill_workspace_size(desc, mask)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    st = lib().nsa_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
+                           _ptr(w_cmp_k), _ptr(w_cmp_v), _ptr(gate_logits), _ptr(out), _ptr(kc),
+                           _ptr(vc), _ptr(sel), _ptr(lse), _ptr(workspace), workspace.numel(),
+                           _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_prefill")
+    res["workspace"] = workspace
+    return res
+
+
+def decode_desc(q, k_cache, top_k, window, block=64, scale=0.0) -> DecodeDesc:
+    bt, hq, d = q.shape
+    L, hkv = k_cache.shape[1], k_cache.shape[2]
+    dt = {torch.bfloat16: NSA_DTYPE_BF16, torch.float32: NSA_DTYPE_FP32}[q.dtype]
+    return DecodeDesc(bt, L, hq, hkv, d, block, top_k, window, float(scale), dt)
+
+
+def decode_workspace_size(desc: DecodeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().nsa_decode_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_decode_workspace_size")
+    return n.value
+
+
+def decode(q, k_cache, v_cache, k_cmp, v_cmp, gate_logits, top_k, window, block=64, scale=0.0,
+           out=None, want_sel=False, want_lse=False, workspace=None, stream=None) -> dict:
+    """Runs nsa_decode: q [Bt,Hq,d], caches [Bt,L,Hkv,d], compressed caches
+    [Bt,L/B,Hkv,d] (bf16), gate_logits [Bt,Hq,3] fp32."""
+    desc = decode_desc(q, k_cache, top_k, window, block, scale)
+    bt, hq, d = q.shape
+    L, hkv = k_cache.shape[1], k_cache.shape[2]
+    for name, t, shape in (("q", q, (bt, hq, d)), ("k_cache", k_cache, (bt, L, hkv, d)),
+                           ("v_cache", v_cache, (bt, L, hkv, d)),
+                           ("k_cmp", k_cmp, (bt, L // block, hkv, d)),
+                           ("v_cmp", v_cmp, (bt, L // block, hkv, d))):
+        _check_dev(name, t, q.dtype, shape)
+    _check_dev("gate_logits", gate_logits, torch.float32, (bt, hq, 3))
+    dev = q.device
+    if out is None:
+        out = torch.empty((bt, hq, d), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (bt, hq, d))
+    res = {"out": out}
+    sel = lse = None
+    if want_sel:
+        sel = res["sel_idx"] = torch.empty((bt, hkv, top_k), dtype=torch.int32, device=dev)
+    if want_lse:
+        lse = res["lse"] = torch.empty((bt, hq), dtype=torch.float32, device=dev)
+    ws_bytes = decode_workspace_size(desc)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    st = lib().nsa_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_cmp),
+                          _ptr(v_cmp), _ptr(gate_logits), _ptr(out), _ptr(sel), _ptr(lse),
+                          _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_decode")
+    res["workspace"] = workspace
+    return res
+
+
+def cmp_pool(x, w, block=64, out_bf16=True, out_f32=False, stream=None) -> dict:
+    """Runs nsa_cmp_pool over x [n_rows, H, d] with map w [d, d]."""
+    n, h, d = x.shape
+    _check_dev("x", x, x.dtype, (n, h, d))
+    _check_dev("w", w, x.dtype, (d, d))
+    dt = {torch.bfloat16: NSA_DTYPE_BF16, torch.float32: NSA_DTYPE_FP32}[x.dtype]
+    res = {}
+    ob = of = None
+    if out_bf16:
+        ob = res["bf16"] = torch.empty((n // block, h, d), dtype=torch.bfloat16, device=x.device)
+    if out_f32:
+        of = res["f32"] = torch.empty((n // block, h, d), dtype=torch.float32, device=x.device)
+    st = lib().nsa_cmp_pool(n, h, d, block, dt, _ptr(x), _ptr(w), _ptr(ob), _ptr(of), _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_cmp_pool")
+    return res

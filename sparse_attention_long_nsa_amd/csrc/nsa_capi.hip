@@ -1,0 +1,240 @@
+// C ABI of libnsa.so: argument validation, workspace planning and the launch
+// sequence of the VideoNSA attention layer (declarations and contract in
+// include/nsa.h).
+#include <math.h>
+#include <string.h>
+
+#include "../../include/nsa.h"
+#include "nsa_kernels.h"
+
+namespace nsa {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxTopK = 64;
+constexpr int kMaxBlocks = 8192;  // selection union bitmask / top-k register budget
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct PrefillPlan {
+  int64_t N = 0, v0 = 0, v1 = 0, n_vis = 0, n_text = 0;
+  int hq = 0, hkv = 0, d = 0, G = 0, k = 0, w = 0;
+  int n_blk = 0, n_frames = 0;
+  bool fp32 = false;
+  float scale = 0.f;
+  int n_split = 0, split_len = 0, text_tiles = 0;
+  size_t off_kc = 0, off_vc = 0, off_kcl = 0, off_qh = 0, off_ql = 0, off_q16 = 0, off_k16 = 0,
+         off_v16 = 0;
+  size_t off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0, total = 0;
+};
+
+nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, PrefillPlan &pl) {
+  if (!ds || !is_vision) return NSA_ERR_INVALID_ARG;
+  if (ds->n_tokens < 1 || ds->n_q_heads < 1 || ds->n_kv_heads < 1 || ds->head_dim < 1 ||
+      ds->block_size < 1 || ds->top_k < 1 || ds->window < 1)
+    return NSA_ERR_INVALID_ARG;
+  if (ds->n_q_heads % ds->n_kv_heads != 0) return NSA_ERR_INVALID_ARG;
+  if (ds->dtype != NSA_DTYPE_BF16 && ds->dtype != NSA_DTYPE_FP32) return NSA_ERR_INVALID_ARG;
+  if (!(ds->scale == ds->scale)) return NSA_ERR_INVALID_ARG;  // NaN
+  pl.N = ds->n_tokens;
+  pl.hq = ds->n_q_heads;
+  pl.hkv = ds->n_kv_heads;
+  pl.d = ds->head_dim;
+  pl.G = pl.hq / pl.hkv;
+  pl.k = ds->top_k;
+  pl.w = ds->window;
+  pl.fp32 = ds->dtype == NSA_DTYPE_FP32;
+  if (ds->block_size != kBlk) return NSA_ERR_UNSUPPORTED;
+  if (!supported_heads(pl.d, pl.G, pl.fp32)) return NSA_ERR_UNSUPPORTED;
+  if (pl.k > kMaxTopK) return NSA_ERR_UNSUPPORTED;
+  if (pl.N > (int64_t)INT32_MAX / 2) return NSA_ERR_UNSUPPORTED;
+  pl.scale = ds->scale > 0.f ? ds->scale : 1.0f / sqrtf((float)pl.d);
+
+  // vision tokens must form one contiguous run
+  int64_t first = -1, last = -1;
+  for (int64_t i = 0; i < pl.N; ++i)
+    if (is_vision[i]) { if (first < 0) first = i; last = i; }
+  if (first < 0) { pl.v0 = pl.v1 = 0; }
+  else {
+    for (int64_t i = first; i <= last; ++i)
+      if (!is_vision[i]) return NSA_ERR_UNSUPPORTED;
+    pl.v0 = first;
+    pl.v1 = last + 1;
+  }
+  pl.n_vis = pl.v1 - pl.v0;
+  pl.n_text = pl.N - pl.n_vis;
+  pl.n_blk = (int)(pl.n_vis / kBlk);
+  pl.n_frames = (int)((pl.n_vis + kBlk - 1) / kBlk);
+  if (pl.n_frames > kMaxBlocks) return NSA_ERR_UNSUPPORTED;
+
+  // text split-K: enough (tile, group, split) workgroups to fill the chip
+  pl.text_tiles = (int)((pl.n_text + kBlk - 1) / kBlk);
+  if (pl.n_text > 0) {
+    const int64_t want = 1024;
+    int64_t ns = want / ((int64_t)pl.text_tiles * pl.hkv);
+    if (ns < 1) ns = 1;
+    int64_t len = (pl.N + ns - 1) / ns;
+    len = (len + kBlk - 1) / kBlk * kBlk;
+    if (len < 4 * kBlk) len = 4 * kBlk;
+    pl.split_len = (int)len;
+    pl.n_split = (int)((pl.N + len - 1) / len);
+  }
+
+  const size_t H = (size_t)pl.hq, Hk = (size_t)pl.hkv, D = (size_t)pl.d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  pl.off_kc = take(sizeof(uint16_t) * pl.n_blk * Hk * D);
+  pl.off_vc = take(sizeof(uint16_t) * pl.n_blk * Hk * D);
+  if (pl.fp32) {
+    pl.off_kcl = take(sizeof(uint16_t) * pl.n_blk * Hk * D);
+    pl.off_qh = take(sizeof(uint16_t) * pl.N * H * D);
+    pl.off_ql = take(sizeof(uint16_t) * pl.N * H * D);
+    pl.off_q16 = take(sizeof(uint16_t) * pl.N * H * D);
+    pl.off_k16 = take(sizeof(uint16_t) * pl.N * Hk * D);
+    pl.off_v16 = take(sizeof(uint16_t) * pl.N * Hk * D);
+  }
+  pl.off_lse = take(sizeof(float) * pl.n_vis * H);
+  pl.off_gs = take(sizeof(float) * (size_t)frame_off(pl.n_frames, pl.hkv));
+  pl.off_sel = take(sizeof(int32_t) * pl.n_vis * Hk * pl.k);
+  pl.off_po = take(sizeof(float) * (size_t)pl.n_split * pl.n_text * H * D);
+  pl.off_pml = take(sizeof(float2) * (size_t)pl.n_split * pl.n_text * H);
+  pl.total = off;
+  return NSA_OK;
+}
+
+template <class T> T *at(void *base, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(base) + off);
+}
+
+}  // namespace
+}  // namespace nsa
+
+using namespace nsa;
+
+extern "C" {
+
+const char *nsa_status_string(nsa_status s) {
+  switch (s) {
+    case NSA_OK: return "ok";
+    case NSA_ERR_INVALID_ARG: return "invalid argument";
+    case NSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case NSA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+const char *nsa_version(void) { return "0.1.0"; }
+
+nsa_status nsa_prefill_workspace_size(const nsa_prefill_desc *desc, const uint8_t *is_vision,
+                                      size_t *bytes) {
+  if (!bytes) return NSA_ERR_INVALID_ARG;
+  PrefillPlan pl;
+  const nsa_status st = plan_prefill(desc, is_vision, pl);
+  if (st != NSA_OK) return st;
+  *bytes = pl.total;
+  return NSA_OK;
+}
+
+nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *k, const void *v,
+                       const uint8_t *is_vision, const void *w_cmp_k, const void *w_cmp_v,
+                       const float *gate_logits, float *out, float *k_cmp_out, float *v_cmp_out,
+                       int32_t *sel_idx_out, float *lse_out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  PrefillPlan pl;
+  nsa_status st = plan_prefill(desc, is_vision, pl);
+  if (st != NSA_OK) return st;
+  if (!q || !k || !v || !gate_logits || !out) return NSA_ERR_INVALID_ARG;
+  if (pl.n_blk > 0 && (!w_cmp_k || !w_cmp_v)) return NSA_ERR_INVALID_ARG;
+  const void *ptrs[] = {q, k, v, w_cmp_k, w_cmp_v, gate_logits, out, k_cmp_out, v_cmp_out,
+                        sel_idx_out, lse_out};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return NSA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < pl.total) return NSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return NSA_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t H = pl.hq, Hk = pl.hkv, D = pl.d;
+  const uint16_t *qb = static_cast<const uint16_t *>(q);
+  const uint16_t *kb = static_cast<const uint16_t *>(k);
+  const uint16_t *vb = static_cast<const uint16_t *>(v);
+  const uint16_t *ql = nullptr;
+  uint16_t *kc = at<uint16_t>(workspace, pl.off_kc);
+  uint16_t *vc = at<uint16_t>(workspace, pl.off_vc);
+  uint16_t *kcl = nullptr;
+  hipError_t e = hipSuccess;
+#define NSA_CHECK(expr)                      \
+  do {                                       \
+    e = (expr);                              \
+    if (e != hipSuccess) return NSA_ERR_HIP; \
+  } while (0)
+
+  // fp32 inputs: block scores from split bf16 operands (q_hi, q_lo), every
+  // other product in fp16
+  const uint16_t *qc = qb;  // queries of the compression branch
+  if (pl.fp32) {
+    uint16_t *qh = at<uint16_t>(workspace, pl.off_qh), *qlo = at<uint16_t>(workspace, pl.off_ql);
+    uint16_t *q16 = at<uint16_t>(workspace, pl.off_q16), *k16 = at<uint16_t>(workspace, pl.off_k16);
+    uint16_t *v16 = at<uint16_t>(workspace, pl.off_v16);
+    NSA_CHECK(launch_split_bf16(static_cast<const float *>(q), pl.N * H * D, qh, qlo, s));
+    NSA_CHECK(launch_to_f16(static_cast<const float *>(q), pl.N * H * D, q16, s));
+    NSA_CHECK(launch_to_f16(static_cast<const float *>(k), pl.N * Hk * D, k16, s));
+    NSA_CHECK(launch_to_f16(static_cast<const float *>(v), pl.N * Hk * D, v16, s));
+    qc = qh; ql = qlo; qb = q16; kb = k16; vb = v16;
+    kcl = at<uint16_t>(workspace, pl.off_kcl);
+  }
+  const float sl2 = pl.scale * kLog2e;
+
+  if (pl.n_vis > 0) {
+    float *lse = lse_out ? lse_out : at<float>(workspace, pl.off_lse);
+    int32_t *sel = sel_idx_out ? sel_idx_out : at<int32_t>(workspace, pl.off_sel);
+    float *gs = at<float>(workspace, pl.off_gs);
+    const size_t esz = pl.fp32 ? sizeof(float) : sizeof(uint16_t);
+    if (pl.n_blk > 0) {
+      // compressed keys: fp16 (bf16 hi/lo for fp32 inputs); values: fp16
+      PoolJob jk{static_cast<const char *>(k) + esz * pl.v0 * Hk * D, w_cmp_k, pl.hkv, pl.n_blk,
+                 pl.fp32 ? kc : nullptr, kcl, pl.fp32 ? nullptr : kc, k_cmp_out};
+      PoolJob jv{static_cast<const char *>(v) + esz * pl.v0 * Hk * D, w_cmp_v, pl.hkv, pl.n_blk,
+                 nullptr, nullptr, vc, v_cmp_out};
+      NSA_CHECK(launch_cmp_pool(jk, &jv, pl.d, pl.fp32, s));
+    }
+    CmpAttnParams cp{qc, ql, kc, kcl, vc, gate_logits, out, lse, gs, pl.v0,
+                     (int)pl.n_vis, pl.hq, pl.hkv, pl.n_frames, sl2};
+    NSA_CHECK(launch_cmp_attn(cp, pl.d, pl.G, pl.fp32, s));
+    TopkParams tp{gs, sel, (int)pl.n_vis, pl.hkv, pl.k};
+    NSA_CHECK(launch_topk(tp, pl.n_frames, s));
+    SwaParams wp{qb, kb, vb, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.w,
+                 pl.n_frames, sl2};
+    NSA_CHECK(launch_swa_attn(wp, pl.d, pl.G, pl.fp32, s));
+    SelParams sp{qb, kb, vb, sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
+                 pl.n_frames, sl2};
+    NSA_CHECK(launch_sel_attn(sp, pl.d, pl.G, pl.fp32, s));
+  }
+  if (pl.n_text > 0) {
+    TextParams tp{qb, kb, vb, at<float>(workspace, pl.off_po), at<float2>(workspace, pl.off_pml),
+                  out, pl.v0, pl.v1, pl.N, (int)pl.n_text, pl.hq, pl.hkv, pl.n_split,
+                  pl.split_len, pl.text_tiles, sl2};
+    NSA_CHECK(launch_text_attn(tp, pl.d, pl.G, pl.fp32, s));
+  }
+  return NSA_OK;
+}
+
+nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim, int32_t block_size,
+                        int32_t dtype, const void *x, const void *w, void *out_bf16,
+                        float *out_f32, void *stream) {
+  if (n_rows < 0 || n_heads < 1 || !x || !w) return NSA_ERR_INVALID_ARG;
+  if (dtype != NSA_DTYPE_BF16 && dtype != NSA_DTYPE_FP32) return NSA_ERR_INVALID_ARG;
+  if (!out_bf16 && !out_f32) return NSA_ERR_INVALID_ARG;
+  const void *ptrs[] = {x, w, out_bf16, out_f32};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return NSA_ERR_INVALID_ARG;
+  if (block_size != kBlk || (head_dim != 64 && head_dim != 128)) return NSA_ERR_UNSUPPORTED;
+  PoolJob j{x, w, n_heads, n_rows / kBlk, static_cast<uint16_t *>(out_bf16), nullptr, nullptr, out_f32};
+  if (launch_cmp_pool(j, nullptr, head_dim, dtype == NSA_DTYPE_FP32, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return NSA_ERR_HIP;
+  return NSA_OK;
+}
+
+}  // extern "C"

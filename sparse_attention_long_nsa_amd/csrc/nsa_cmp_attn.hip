@@ -1,0 +1,264 @@
+// Compression-branch attention and block importance scores.
+//
+// Every vision query attends to the compressed block keys/values of the
+// complete blocks before it (VideoNSA paper summary page, "Method", branch
+// (a); readings: a block is visible once complete, empty set -> zero output).
+// The selection branch ranks blocks by an importance score taken from this
+// attention (same section, branch (b)); the reading used is the sum over the
+// KV group's query heads of each head's normalised probability, so the
+// kernel runs two passes over the compressed keys: pass 1 finds every
+// query's log-sum-exp, pass 2 forms exact probabilities, which feed the PV
+// product (no running rescale needed) and, summed over the group's heads in
+// registers, the frame-packed group-score rows read by the top-k kernel.
+//
+// Layout: one workgroup = one 64-token frame x one KV group, four waves of
+// 16 tokens each; every wave carries all G query heads of its tokens, so a
+// K or V^T fragment read from LDS feeds G matrix-core ops and the head sum
+// of the importance score never leaves the lane. Workgroups are ordered
+// heaviest (latest frame) first and interleave KV groups so that consecutive
+// workgroup ids -- which land on different XCDs -- keep one group's
+// compressed keys per XCD L2.
+#include "nsa_kernels.h"
+
+namespace nsa {
+
+namespace {
+
+constexpr int kThreadsH = 256;  // 4 waves x 16 tokens
+
+// Folds four scaled logits (log2 units, -inf = masked) into a lane-partial
+// (max, sum) pair.
+__device__ __forceinline__ void fold4(float &m, float &l, const f32x4 x) {
+  const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  const float mn = fmaxf(m, mx);
+  if (mn == -INFINITY) return;
+  l = l * exp2f(m - mn) + exp2f(x[0] - mn) + exp2f(x[1] - mn) + exp2f(x[2] - mn) + exp2f(x[3] - mn);
+  m = mn;
+}
+
+// Scores of 16 compressed keys: fp16 q x fp16 keys, or (split operands, for
+// fp32 inputs) bf16 q_hi*k_hi + q_hi*k_lo + q_lo*k_hi.
+template <int D, int G, bool SPLIT>
+__device__ __forceinline__ void scores16(f32x4 (&s)[G], const uint16_t *ks, const uint16_t *ksl, int kt,
+                                         const u16x8 (&qf)[G][D / 32],
+                                         const u16x8 (&ql)[SPLIT ? G : 1][D / 32], int lane) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) s[h] = zero4();
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) {
+    const u16x8 a = k_frag<D>(ks, kt, ds, lane);
+    if constexpr (SPLIT) {
+      const u16x8 al = k_frag<D>(ksl, kt, ds, lane);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s[h] = mfma_bf16(a, qf[h][ds], s[h]);
+        s[h] = mfma_bf16(al, qf[h][ds], s[h]);
+        s[h] = mfma_bf16(a, ql[h][ds], s[h]);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[h] = mfma_f16(a, qf[h][ds], s[h]);
+    }
+  }
+}
+
+template <int D, int G, bool SPLIT>
+__global__ __launch_bounds__(kThreadsH) void cmp_attn_kernel(CmpAttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[Tile<D>::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t ksl[SPLIT ? Tile<D>::kElems : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[Tile<D>::vElems];
+  constexpr int DS = D / 32, DT = D / 16;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int row = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.x % p.hkv;
+  const int f = p.n_frames - 1 - (int)(blockIdx.x / p.hkv);
+  const int t = f * kBlk + wv * 16 + row;  // this lane's query (vision-local)
+  const bool tvalid = t < p.n_vis;
+  const int nc_t = tvalid ? (t + 1) / kBlk : 0;  // complete blocks visible to it
+  const int t_last = min(f * kBlk + kBlk - 1, p.n_vis - 1);
+  const int nk = (t_last + 1) / kBlk;            // blocks any query of the frame sees
+  const int64_t kvs = (int64_t)p.hkv * D;
+  const uint16_t *kc = p.kc + (int64_t)g * D;
+  const uint16_t *kcl = SPLIT ? p.kc_lo + (int64_t)g * D : nullptr;
+  const uint16_t *vc = p.vc + (int64_t)g * D;
+
+  u16x8 qf[G][DS];
+  u16x8 ql[SPLIT ? G : 1][DS];
+  {
+    const int64_t q0 = ((p.v0 + (tvalid ? t : 0)) * p.hq + (int64_t)g * G) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const u16x8 raw = tvalid ? q_frag_global(p.q + q0 + h * D, ds, lane) : zero8();
+        qf[h][ds] = SPLIT ? raw : bf2h8(raw);  // fp16 scores unless split
+        if constexpr (SPLIT) ql[h][ds] = tvalid ? q_frag_global(p.q_lo + q0 + h * D, ds, lane) : zero8();
+      }
+  }
+
+  // ---- pass 1: log-sum-exp of every (query, head)
+  float m[G], l[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
+  for (int c = 0; c * kBlk < nk; ++c) {
+    const int nvalid = min(kBlk, nk - c * kBlk);
+    __syncthreads();
+    stage_k<D>(ks, kc + (int64_t)c * kBlk * kvs, kvs, nvalid, tid, kThreadsH);
+    if constexpr (SPLIT) stage_k<D>(ksl, kcl + (int64_t)c * kBlk * kvs, kvs, nvalid, tid, kThreadsH);
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 s[G];
+      scores16<D, G, SPLIT>(s, ks, ksl, kt, qf, ql, lane);
+      const int b0 = c * kBlk + 16 * kt + 4 * grp;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        f32x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (b0 + i < nc_t) ? s[h][i] * p.sl2 : -INFINITY;
+        fold4(m[h], l[h], x);
+      }
+    }
+  }
+  float lse2[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float M = grp_max(m[h]);
+    const float part = (m[h] == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - M);
+    const float L = grp_sum(part);
+    lse2[h] = (L > 0.f) ? M + log2f(L) : -INFINITY;
+  }
+  if (tvalid && grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) p.lse[(int64_t)t * p.hq + g * G + h] = lse2[h] * (1.0f / kLog2e);
+  }
+
+  // ---- pass 2: probabilities -> o_cmp and group scores
+  f32x4 o[G][DT];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[h][dt] = zero4();
+  float *gsrow = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + (t - f * kBlk)) * f;
+  for (int c = 0; c * kBlk < nk; ++c) {
+    const int nvalid = min(kBlk, nk - c * kBlk);
+    __syncthreads();
+    stage_k<D>(ks, kc + (int64_t)c * kBlk * kvs, kvs, nvalid, tid, kThreadsH);
+    if constexpr (SPLIT) stage_k<D>(ksl, kcl + (int64_t)c * kBlk * kvs, kvs, nvalid, tid, kThreadsH);
+    stage_vt<D, false>(vt, vc + (int64_t)c * kBlk * kvs, kvs, nvalid, tid, kThreadsH);
+    __syncthreads();
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      f32x4 s[2][G];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int kt = 2 * ks2 + kk;
+        scores16<D, G, SPLIT>(s[kk], ks, ksl, kt, qf, ql, lane);
+        const int b0 = c * kBlk + 16 * kt + 4 * grp;
+        f32x4 gsum = zero4();
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s[kk][h][i] = (b0 + i < nc_t) ? exp2f(s[kk][h][i] * p.sl2 - lse2[h]) : 0.f;
+          gsum += s[kk][h];
+        }
+        if (tvalid) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (b0 + i < f) gsrow[b0 + i] = gsum[i];
+        }
+      }
+      u16x8 pf[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pf[h] = pack_p(s[0][h], s[1][h]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u16x8 a = v_frag<D>(vt, dt, ks2, lane);
+#pragma unroll
+        for (int h = 0; h < G; ++h) o[h][dt] = mfma_f16(a, pf[h], o[h][dt]);
+      }
+    }
+  }
+
+  // ---- epilogue: out = sigmoid(g_cmp) * o_cmp (first writer of vision rows)
+  if (tvalid) {
+    const int64_t r0 = (p.v0 + t) * p.hq + (int64_t)g * G;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float gate = sigmoidf_(p.gates[(r0 + h) * 3 + 0]);
+      float *dst = p.out + (r0 + h) * D + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[h][dt] * gate;
+    }
+  }
+}
+
+template <int D, int G, bool SPLIT>
+hipError_t run(const CmpAttnParams &p, hipStream_t st) {
+  const unsigned nwg = (unsigned)p.n_frames * (unsigned)p.hkv;
+  if (nwg == 0) return hipSuccess;
+  hipLaunchKernelGGL((cmp_attn_kernel<D, G, SPLIT>), dim3(nwg), dim3(kThreadsH), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cmp_attn(const CmpAttnParams &p, int d, int G, bool split, hipStream_t st) {
+  if (split) {
+    if (d == 64) {
+      switch (G) {
+        case 1: return run<64, 1, true>(p, st);
+        case 2: return run<64, 2, true>(p, st);
+        case 3: return run<64, 3, true>(p, st);
+        case 4: return run<64, 4, true>(p, st);
+        case 5: return run<64, 5, true>(p, st);
+        case 6: return run<64, 6, true>(p, st);
+        case 7: return run<64, 7, true>(p, st);
+        case 8: return run<64, 8, true>(p, st);
+      }
+    } else {
+      switch (G) {
+        case 1: return run<128, 1, true>(p, st);
+        case 2: return run<128, 2, true>(p, st);
+        case 3: return run<128, 3, true>(p, st);
+        case 4: return run<128, 4, true>(p, st);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
+  if (d == 64) {
+    switch (G) {
+      case 1: return run<64, 1, false>(p, st);
+      case 2: return run<64, 2, false>(p, st);
+      case 3: return run<64, 3, false>(p, st);
+      case 4: return run<64, 4, false>(p, st);
+      case 5: return run<64, 5, false>(p, st);
+      case 6: return run<64, 6, false>(p, st);
+      case 7: return run<64, 7, false>(p, st);
+      case 8: return run<64, 8, false>(p, st);
+    }
+  } else {
+    switch (G) {
+      case 1: return run<128, 1, false>(p, st);
+      case 2: return run<128, 2, false>(p, st);
+      case 3: return run<128, 3, false>(p, st);
+      case 4: return run<128, 4, false>(p, st);
+      case 5: return run<128, 5, false>(p, st);
+      case 6: return run<128, 6, false>(p, st);
+      case 7: return run<128, 7, false>(p, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+bool supported_heads(int d, int G, bool split) {
+  if (d != 64 && d != 128) return false;
+  if (G < 1 || G > 8) return false;
+  if (d == 128 && G > 7) return false;     // G x 16 x 128 accumulators per wave
+  if (split && G * d > 512) return false;  // split operands double the query registers
+  return true;
+}
+
+}  // namespace nsa

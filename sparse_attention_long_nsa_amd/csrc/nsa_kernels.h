@@ -1,0 +1,106 @@
+// Internal launch interface between the C-ABI host code and the kernels.
+#pragma once
+
+#include "nsa_common.h"
+
+namespace nsa {
+
+// Offset (in floats) of frame f's block in the frame-packed group-score
+// buffer: frame f's 64 tokens x Hkv groups each own a row of f scores, one
+// per candidate block 0 .. f-1 (the frame's own block is never a candidate).
+__host__ __device__ __forceinline__ int64_t frame_off(int64_t f, int hkv) {
+  return (int64_t)kBlk * hkv * (f * (f - 1) / 2);
+}
+
+struct PoolJob {
+  const void *x;     // first row of the pooled run, [n_rows, n_heads, d]
+  const void *w;     // [d, d]
+  int n_heads;
+  int64_t n_blk;
+  uint16_t *out_hi;  // bf16 rounding of the result (or null)
+  uint16_t *out_lo;  // bf16 residual (or null)
+  uint16_t *out_h16; // fp16 rounding of the result (or null)
+  float *out_f32;    // fp32 result (or null)
+};
+
+struct CmpAttnParams {
+  const uint16_t *q, *q_lo;    // [N, Hq, d] bf16; q_lo only for split operands
+  const uint16_t *kc, *kc_lo;  // [n_blk, Hkv, d]: fp16, or bf16 hi/lo when split
+  const uint16_t *vc;          // [n_blk, Hkv, d] fp16
+  const float *gates;      // [N, Hq, 3]
+  float *out;              // [N, Hq, d]
+  float *lse;              // [n_vis, Hq]
+  float *gs;               // frame-packed group scores
+  int64_t v0;              // first vision position
+  int n_vis, hq, hkv, n_frames;
+  float sl2;               // softmax scale * log2(e)
+};
+
+struct TopkParams {
+  const float *gs;
+  int32_t *sel;            // [n_vis, Hkv, k]
+  int n_vis, hkv, k;
+};
+
+struct SwaParams {
+  const uint16_t *q, *k, *v;   // [N, H, d]: all bf16, or all fp16
+  const float *gates;
+  float *out;
+  int64_t v0;
+  int n_vis, hq, hkv, window, n_tiles;
+  float sl2;
+};
+
+struct SelParams {
+  const uint16_t *q, *k, *v;
+  const int32_t *sel;      // [n_vis, Hkv, k]
+  const float *gates;
+  float *out;
+  int64_t v0;
+  int n_vis, hq, hkv, topk, n_frames;
+  float sl2;
+};
+
+struct TextParams {
+  const uint16_t *q, *k, *v;
+  float *part_o;           // [n_split, n_text, Hq, d]
+  float2 *part_ml;         // [n_split, n_text, Hq] (max in log2 units, sum)
+  float *out;              // merge target [N, Hq, d]
+  int64_t v0, v1, n_tokens;
+  int n_text, hq, hkv, n_split, split_len, n_tiles;
+  float sl2;
+};
+
+struct DecodeParams {
+  const bf16 *q;           // [Bt, Hq, d]
+  const bf16 *kcache, *vcache;  // [Bt, L, Hkv, d]
+  const bf16 *kc, *vc;     // [Bt, L/64, Hkv, d]
+  const float *gates;      // [Bt, Hq, 3]
+  float *out;              // [Bt, Hq, d]
+  int32_t *sel;            // [Bt, Hkv, k]
+  float *lse;              // [Bt, Hq]
+  float *logits;           // workspace [Bt, Hq, n_blk] scaled log2 logits
+  float2 *part_ml;         // workspace [Bt, Hq, n_split]
+  float *part_o;           // workspace [Bt, Hq, n_split, d]
+  int batch, L, hq, hkv, topk, window, n_blk, n_split;
+  float sl2;
+};
+
+size_t pool_smem_bytes(int n_heads, int d);
+hipError_t launch_cmp_pool(const PoolJob &j0, const PoolJob *j1, int d, bool fp32, hipStream_t st);
+// fp32 -> bf16 high part (+ optional bf16 residual), or fp32 -> fp16.
+hipError_t launch_split_bf16(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t st);
+hipError_t launch_to_f16(const float *x, int64_t n, uint16_t *out, hipStream_t st);
+hipError_t launch_cmp_attn(const CmpAttnParams &p, int d, int G, bool split, hipStream_t st);
+hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st);
+// f16: q, k, v hold fp16 (else bf16; values are converted while staging)
+hipError_t launch_swa_attn(const SwaParams &p, int d, int G, bool f16, hipStream_t st);
+hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st);
+hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st);
+hipError_t launch_decode(const DecodeParams &p, int d, int G, hipStream_t st);
+
+// Which (head_dim, query heads per KV head) pairs have kernels.
+bool supported_heads(int d, int G, bool split);
+bool decode_supported(int d, int G);
+
+}  // namespace nsa

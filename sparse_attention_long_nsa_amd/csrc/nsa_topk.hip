@@ -1,0 +1,124 @@
+// Top-k block selection (VideoNSA paper summary page, "Method", branch (b):
+// keep the top blocks by importance score). Readings: the query's own block
+// is always kept and counts toward k; the other k-1 are the highest-scoring
+// complete earlier blocks, ties going to the lower block index; the result
+// is emitted in ascending block order, -1 padded.
+//
+// One wave per (vision query, KV group). The wave streams the query's row of
+// group scores (frame-packed, written by the compression kernel) once into
+// registers, finds the (k-1)-th largest score exactly by an MSB-first radix
+// select over the fp32 bit patterns (non-negative floats order like their
+// bits), then emits the chosen indices in ascending order with ballots.
+#include "nsa_kernels.h"
+
+namespace nsa {
+
+namespace {
+
+constexpr int kWavesPerWG = 1;  // one wave per workgroup: early exits need no barrier care
+
+template <int NPL>
+__global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
+  __shared__ uint32_t hist[256];
+  const int lane = threadIdx.x;
+  const int64_t wid = blockIdx.x;
+  const int t = (int)(wid / p.hkv);
+  const int g = (int)(wid % p.hkv);
+  if (t >= p.n_vis) return;
+  const int f = t / kBlk;  // own block == number of candidate blocks
+  int32_t *out = p.sel + ((int64_t)t * p.hkv + g) * p.k;
+  const int need = p.k - 1;
+
+  if (f <= need) {  // every candidate is kept
+    for (int i = lane; i < p.k; i += 64) out[i] = i < f ? i : (i == f ? f : -1);
+    return;
+  }
+
+  const float *row = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + (t - f * kBlk)) * f;
+  // key = bits + 1 for candidates (so 0.0f still beats padding), 0 otherwise
+  uint32_t key[NPL];
+#pragma unroll
+  for (int s = 0; s < NPL; ++s) {
+    const int e = s * 64 + lane;
+    key[s] = e < f ? __float_as_uint(row[e]) + 1u : 0u;
+  }
+
+  uint32_t prefix = 0, pmask = 0;
+  int rem = need;  // how many of the elements matching `prefix` are still wanted
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = lane; i < 256; i += 64) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NPL; ++s)
+      if (key[s] != 0u && (key[s] & pmask) == prefix) atomicAdd(&hist[(key[s] >> shift) & 255u], 1u);
+    __syncthreads();
+    // lane L owns digits 255-4L .. 252-4L (descending)
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
+    const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+    uint32_t incl = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    const uint64_t hit = __ballot(incl >= (uint32_t)rem);
+    const int lt = __ffsll((unsigned long long)hit) - 1;
+    uint32_t digit = 0, before = 0;
+    if (lane == lt) {
+      uint32_t cum = incl - tot;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (cum + c[i] >= (uint32_t)rem) { digit = 255 - 4 * lane - i; before = cum; break; }
+        cum += c[i];
+      }
+    }
+    digit = __shfl(digit, lt);
+    before = __shfl(before, lt);
+    rem -= (int)before;
+    prefix |= digit << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+
+  // keys > prefix are all kept; of the keys == prefix keep the `rem` lowest indices
+  int pos = 0, eq_taken = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int s = 0; s < NPL; ++s) {
+    const bool gt = key[s] > prefix;
+    const bool eq = key[s] == prefix;
+    const uint64_t eqb = __ballot(eq);
+    const bool eq_take = eq && (eq_taken + __popcll(eqb & below) < rem);
+    const bool take = gt || eq_take;
+    const uint64_t tb = __ballot(take);
+    if (take) out[pos + __popcll(tb & below)] = s * 64 + lane;
+    pos += __popcll(tb);
+    eq_taken += __popcll(__ballot(eq_take));
+  }
+  if (lane == 0) out[need] = f;  // own block, larger than every candidate
+}
+
+template <int NPL>
+hipError_t run(const TopkParams &p, hipStream_t st) {
+  const int64_t n = (int64_t)p.n_vis * p.hkv;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL((topk_kernel<NPL>), dim3((unsigned)n), dim3(64 * kWavesPerWG), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st) {
+  if (n_blk_max <= 64 * 4) return run<4>(p, st);
+  if (n_blk_max <= 64 * 16) return run<16>(p, st);
+  if (n_blk_max <= 64 * 32) return run<32>(p, st);
+  if (n_blk_max <= 64 * 64) return run<64>(p, st);
+  if (n_blk_max <= 64 * 128) return run<128>(p, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nsa

@@ -1,0 +1,137 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+entry point include/nsa.h declares, and rejects bad arguments with the
+documented status before anything is launched (pointers here are fake,
+16-byte-aligned integers that validation never dereferences)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_attention_long_nsa_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # aligned fake device address
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "nsa.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(nsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = binding.lib()
+    names = header_functions()
+    assert set(names) == set(binding.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert binding.status_string(0) == "ok"
+    assert "workspace" in binding.status_string(3)
+    assert re.match(r"^\d+\.\d+\.\d+$", binding.version())
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libnsa.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
+
+
+def desc(n=1024, hq=28, hkv=4, d=128, block=64, k=16, w=512, dtype=0):
+    return binding.PrefillDesc(n, hq, hkv, d, block, k, w, 0.0, dtype)
+
+
+def call_prefill(ds, mask, ptrs=None, ws=FAKE, ws_bytes=1 << 40):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, wk=FAKE, wv=FAKE, g=FAKE, out=FAKE)
+    if ptrs:
+        p.update(ptrs)
+    L = binding.lib()
+    return L.nsa_prefill(ctypes.byref(ds) if ds is not None else None, p["q"], p["k"], p["v"],
+                         mask.ctypes.data_as(ctypes.c_void_p), p["wk"], p["wv"], p["g"], p["out"],
+                         None, None, None, None, ws, ws_bytes, None)
+
+
+def ws_size(ds, mask):
+    n = ctypes.c_size_t(0)
+    st = binding.lib().nsa_prefill_workspace_size(ctypes.byref(ds), mask.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n))
+    return st, n.value
+
+
+def vision_mask(n, a, b):
+    m = np.zeros(n, np.uint8)
+    m[a:b] = 1
+    return m
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=28, hkv=5), binding.NSA_ERR_INVALID_ARG),
+    (dict(k=0), binding.NSA_ERR_INVALID_ARG),
+    (dict(w=0), binding.NSA_ERR_INVALID_ARG),
+    (dict(n=0), binding.NSA_ERR_INVALID_ARG),
+    (dict(dtype=7), binding.NSA_ERR_INVALID_ARG),
+    (dict(block=32), binding.NSA_ERR_UNSUPPORTED),
+    (dict(d=96), binding.NSA_ERR_UNSUPPORTED),
+    (dict(hq=36, hkv=4), binding.NSA_ERR_UNSUPPORTED),   # 9 query heads per KV head
+    (dict(hq=32, hkv=4, d=128), binding.NSA_ERR_UNSUPPORTED),
+    (dict(k=65), binding.NSA_ERR_UNSUPPORTED),
+    (dict(dtype=1), binding.NSA_ERR_UNSUPPORTED),        # fp32 with 7 x 128 query registers
+])
+def test_descriptor_validation(kw, status):
+    ds = desc(**kw)
+    n = max(ds.n_tokens, 1)
+    mask = vision_mask(n, 0, n)
+    assert ws_size(ds, mask)[0] == status
+    assert call_prefill(ds, mask) == status
+
+
+def test_null_descriptor_and_pointers():
+    mask = vision_mask(1024, 0, 1024)
+    assert call_prefill(None, mask) == binding.NSA_ERR_INVALID_ARG
+    for name in ("q", "k", "v", "g", "out", "wk"):
+        assert call_prefill(desc(), mask, {name: None}) == binding.NSA_ERR_INVALID_ARG, name
+
+
+def test_misaligned_pointer_rejected():
+    mask = vision_mask(1024, 0, 1024)
+    assert call_prefill(desc(), mask, {"q": FAKE + 2}) == binding.NSA_ERR_INVALID_ARG
+
+
+def test_interleaved_vision_spans_unsupported():
+    mask = vision_mask(1024, 0, 1024)
+    mask[500] = 0
+    assert call_prefill(desc(), mask) == binding.NSA_ERR_UNSUPPORTED
+
+
+def test_workspace_checks():
+    ds = desc(n=4096 + 512)
+    mask = vision_mask(4096 + 512, 0, 4096)
+    st, need = ws_size(ds, mask)
+    assert st == binding.NSA_OK and need > 0
+    assert call_prefill(ds, mask, ws=None) == binding.NSA_ERR_WORKSPACE
+    assert call_prefill(ds, mask, ws_bytes=need - 1) == binding.NSA_ERR_WORKSPACE
+    assert call_prefill(ds, mask, ws=FAKE + 16, ws_bytes=need) == binding.NSA_ERR_WORKSPACE
+
+
+def test_workspace_grows_with_context():
+    sizes = []
+    for nv in (4096, 8192, 16384):
+        ds = desc(n=nv + 512)
+        st, n = ws_size(ds, vision_mask(nv + 512, 0, nv))
+        assert st == binding.NSA_OK
+        sizes.append(n)
+    assert sizes[0] < sizes[1] < sizes[2]
+    # the frame-packed score buffer dominates: ~2.15 GB at 131,072 vision tokens
+    st, n = ws_size(desc(n=131072 + 512, k=32, w=256), vision_mask(131072 + 512, 0, 131072))
+    assert st == binding.NSA_OK and 2.1e9 < n < 3.0e9
+
+
+def test_cmp_pool_validation():
+    L = binding.lib()
+    assert L.nsa_cmp_pool(640, 4, 128, 64, 0, None, FAKE, FAKE, None, None) == binding.NSA_ERR_INVALID_ARG
+    assert L.nsa_cmp_pool(640, 4, 128, 64, 0, FAKE, FAKE, None, None, None) == binding.NSA_ERR_INVALID_ARG
+    assert L.nsa_cmp_pool(640, 4, 96, 64, 0, FAKE, FAKE, FAKE, None, None) == binding.NSA_ERR_UNSUPPORTED
