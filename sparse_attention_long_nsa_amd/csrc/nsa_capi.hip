@@ -27,7 +27,7 @@ struct PrefillPlan {
   int n_split = 0, split_len = 0, text_tiles = 0;
   size_t off_kc = 0, off_vc = 0, off_kcl = 0, off_qh = 0, off_ql = 0, off_q16 = 0, off_k16 = 0,
          off_v16 = 0;
-  size_t off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0, total = 0;
+  size_t off_vt = 0, off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0, total = 0;
 };
 
 nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, PrefillPlan &pl) {
@@ -95,6 +95,9 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
     pl.off_k16 = take(sizeof(uint16_t) * pl.N * Hk * D);
     pl.off_v16 = take(sizeof(uint16_t) * pl.N * Hk * D);
   }
+  // packed V^T blocks: [Hkv][n_frames][d][64 + 4] fp16, whole 1-KB pieces per block
+  const size_t vt_block = (size_t)((pl.d * (kBlk + 4) + 511) / 512) * 512;
+  pl.off_vt = take(sizeof(uint16_t) * (size_t)pl.n_frames * Hk * vt_block);
   pl.off_lse = take(sizeof(float) * pl.n_vis * H);
   pl.off_gs = take(sizeof(float) * (size_t)frame_off(pl.n_frames, pl.hkv));
   pl.off_sel = take(sizeof(int32_t) * pl.n_vis * Hk * pl.k);
@@ -208,7 +211,7 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
     SwaParams wp{qb, kb, vb, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.w,
                  pl.n_frames, sl2};
     NSA_CHECK(launch_swa_attn(wp, pl.d, pl.G, pl.fp32, s));
-    SelParams sp{qb, kb, vb, sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
+    SelParams sp{qb, kb, vb, at<uint16_t>(workspace, pl.off_vt), sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
                  pl.n_frames, sl2};
     NSA_CHECK(launch_sel_attn(sp, pl.d, pl.G, pl.fp32, s));
   }

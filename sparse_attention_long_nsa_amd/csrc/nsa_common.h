@@ -56,6 +56,13 @@ __device__ __forceinline__ f32x4 mfma_f16(u16x8 a, u16x8 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// Scores in the operands' own type: bf16 inputs (exact products) or fp16.
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma_qk(u16x8 a, u16x8 b, f32x4 c) {
+  if constexpr (F16) return mfma_f16(a, b, c);
+  else return mfma_bf16(a, b, c);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ u16x8 zero8() { return u16x8{0, 0, 0, 0, 0, 0, 0, 0}; }
 

@@ -1,15 +1,10 @@
-// Token-level branches of the layer: the sliding window and the selected
-// blocks for vision queries (VideoNSA paper summary page, "Method",
-// branches (b) and (c)), and dense causal GQA for text queries (same
-// section: text tokens use standard GQA).
+// Token-level branches with a shared key set per query tile: the sliding
+// window of vision queries (VideoNSA paper summary page, "Method", branch
+// (c)) and dense causal GQA for text queries (same section: text tokens use
+// standard GQA).
 //
-// Sliding window and text use layout H: a wave owns 16 queries and all G
-// query heads of one KV group, so each K / V^T fragment read from LDS feeds
-// G matrix-core ops. Selection uses layout S: a 16-row tile holds TP = 16/G
-// queries x G heads (the only rows that share a selected-block set), and a
-// workgroup iterates, in ascending order, the union of the blocks its
-// frame's 64 queries selected, staging each block once and running only the
-// tiles whose queries picked it.
+// Layout H: a wave owns 16 queries and all G query heads of one KV group, so
+// each K / V^T fragment read from LDS feeds G matrix-core ops.
 #include "nsa_kernels.h"
 
 namespace nsa {
@@ -29,14 +24,6 @@ __device__ __forceinline__ void fold4(float &m, float &l, const f32x4 x) {
   if (mn == -INFINITY) return;
   l = l * exp2f(m - mn) + exp2f(x[0] - mn) + exp2f(x[1] - mn) + exp2f(x[2] - mn) + exp2f(x[3] - mn);
   m = mn;
-}
-
-// Scores in the operands' own type: bf16 inputs (exact products) or fp16
-// (fp32 inputs converted once up front).
-template <bool F16>
-__device__ __forceinline__ f32x4 mfma_qk(u16x8 a, u16x8 b, f32x4 c) {
-  if constexpr (F16) return mfma_f16(a, b, c);
-  else return mfma_bf16(a, b, c);
 }
 
 template <int D, int G, bool F16>
@@ -265,175 +252,6 @@ __global__ __launch_bounds__(D) void text_merge_kernel(TextParams p) {
   p.out[(text_pos(r, p.v0, p.v1) * p.hq + h) * D + d] = acc / L;
 }
 
-// ----------------------------------------------------------- selection (S)
-constexpr int kSelMaxK = 64;
-constexpr int kSelMaxBlk = 8192;
-
-template <int D, int G>
-struct SelCfg {
-  static constexpr int TP = 16 / G;                          // queries per row tile
-  static constexpr int NRT = (kBlk + TP - 1) / TP;           // row tiles per frame
-  static constexpr int RT = 4;                               // tiles per wave
-  static constexpr int NW = (NRT + RT - 1) / RT;             // waves
-};
-
-template <int D, int G, bool F16>
-__global__ __launch_bounds__((64 * SelCfg<D, G>::NW)) void sel_attn_kernel(SelParams p) {
-  using C = SelCfg<D, G>;
-  constexpr int TP = C::TP, RT = C::RT, NRT = C::NRT;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[Tile<D>::kElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[Tile<D>::vElems];
-  __shared__ int32_t sl[kBlk * kSelMaxK];
-  __shared__ uint32_t ubits[kSelMaxBlk / 32 + 1];
-  __shared__ int32_t ulist[kBlk * kSelMaxK];
-  __shared__ int n_union;
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4;
-  const int nthr = 64 * C::NW;
-  const int g = blockIdx.x % p.hkv;
-  const int f = p.n_frames - 1 - (int)(blockIdx.x / p.hkv);
-  const int tok0 = f * kBlk;
-  const int ntok = min(kBlk, p.n_vis - tok0);
-  const int k = p.topk;
-  const int64_t kvs = (int64_t)p.hkv * D;
-
-  // selected blocks of the frame's queries, and their union as a bitmask
-  const int nwords = f / 32 + 1;
-  for (int i = tid; i < nwords; i += nthr) ubits[i] = 0u;
-  for (int idx = tid; idx < kBlk * k; idx += nthr) {
-    const int tk = idx / k;
-    sl[idx] = tk < ntok ? p.sel[((int64_t)(tok0 + tk) * p.hkv + g) * k + (idx % k)] : -1;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < kBlk * k; idx += nthr) {
-    const int b = sl[idx];
-    if (b >= 0 && b <= f) atomicOr(&ubits[b >> 5], 1u << (b & 31));
-  }
-  __syncthreads();
-  if (wv == 0) {  // compact the bitmask into an ascending list
-    int running = 0;
-    for (int base = 0; base < nwords; base += 64) {
-      const int wi = base + lane;
-      uint32_t bits = wi < nwords ? ubits[wi] : 0u;
-      const int cnt = __popc(bits);
-      int incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-      }
-      int o = running + incl - cnt;
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        ulist[o++] = wi * 32 + b;
-        bits &= bits - 1;
-      }
-      running += __shfl(incl, 63);
-    }
-    if (lane == 0) n_union = running;
-  }
-  __syncthreads();
-  const int nU = n_union;
-
-  // this lane's row in each of the wave's tiles
-  const int r16 = lane & 15;
-  const int tau = r16 / G, hh = r16 % G;
-  bool valid[RT];
-  int tq[RT];
-  u16x8 qf[RT][D / 32];
-  f32x4 o[RT][D / 16];
-  float m[RT], l[RT];
-  int cur[RT][TP];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int ti = wv * RT + r;
-    const int tk = ti * TP + tau;
-    valid[r] = ti < NRT && tau < TP && tk < ntok;
-    tq[r] = tok0 + tk;
-    const int64_t qrow = (p.v0 + (valid[r] ? tq[r] : 0)) * p.hq + (int64_t)g * G + hh;
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds)
-      qf[r][ds] = valid[r] ? q_frag_global(p.q + qrow * D, ds, lane) : zero8();
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[r][dt] = zero4();
-    m[r] = -INFINITY;
-    l[r] = 0.f;
-#pragma unroll
-    for (int i = 0; i < TP; ++i) cur[r][i] = 0;
-  }
-
-  for (int u = 0; u < nU; ++u) {
-    const int b = ulist[u];
-    const int nvalid = min(kBlk, p.n_vis - b * kBlk);
-    const int64_t src = ((p.v0 + (int64_t)b * kBlk) * p.hkv + g) * (int64_t)D;
-    __syncthreads();
-    stage_k<D>(ks, p.k + src, kvs, nvalid, tid, nthr);
-    stage_vt<D, !F16>(vt, p.v + src, kvs, nvalid, tid, nthr);
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int ti = wv * RT + r;
-      if (ti >= NRT) continue;
-      uint32_t needmask = 0;
-#pragma unroll
-      for (int i = 0; i < TP; ++i) {
-        const int tk = ti * TP + i;
-        if (tk < ntok && cur[r][i] < k) {
-          const int sb = __builtin_amdgcn_readfirstlane(sl[tk * k + cur[r][i]]);
-          if (sb == b) { needmask |= 1u << i; ++cur[r][i]; }
-        }
-      }
-      if (needmask == 0) continue;
-      const bool rowneed = valid[r] && ((needmask >> tau) & 1u);
-      const int t = tq[r];
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        f32x4 s[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int kt = 2 * ks2 + kk;
-          s[kk] = zero4();
-#pragma unroll
-          for (int ds = 0; ds < D / 32; ++ds) s[kk] = mfma_qk<F16>(k_frag<D>(ks, kt, ds, lane), qf[r][ds], s[kk]);
-          const int j0 = b * kBlk + 16 * kt + 4 * grp;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[kk][i] = (rowneed && j0 + i <= t) ? s[kk][i] * p.sl2 : -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mx = grp_max(mx);
-        const float mn = fmaxf(m[r], mx);
-        const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[r] - mn);
-        const float base = (mn == -INFINITY) ? 0.f : mn;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[kk][i] = exp2f(s[kk][i] - base);
-        l[r] = l[r] * alpha + (s[0][0] + s[0][1] + s[0][2] + s[0][3]) + (s[1][0] + s[1][1] + s[1][2] + s[1][3]);
-        m[r] = mn;
-        const u16x8 pf = pack_p(s[0], s[1]);
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[r][dt] = mfma_f16(v_frag<D>(vt, dt, ks2, lane), pf, o[r][dt] * alpha);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const float L = grp_sum(l[r]);
-    if (valid[r]) {
-      const int64_t qrow = (p.v0 + tq[r]) * p.hq + (int64_t)g * G + hh;
-      const float gate = sigmoidf_(p.gates[qrow * 3 + 1]) / L;
-      float *dst = p.out + qrow * D + 4 * grp;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        f32x4 *d4 = reinterpret_cast<f32x4 *>(dst + 16 * dt);
-        *d4 = *d4 + o[r][dt] * gate;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------- launchers
 template <int D, int G, bool F16>
 hipError_t run_swa(const SwaParams &p, hipStream_t st) {
@@ -451,14 +269,6 @@ hipError_t run_text(const TextParams &p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((text_merge_kernel<D>), dim3((unsigned)(p.n_text * p.hq)), dim3(D), 0, st, p);
-  return hipGetLastError();
-}
-
-template <int D, int G, bool F16>
-hipError_t run_sel(const SelParams &p, hipStream_t st) {
-  const unsigned n = (unsigned)p.n_frames * (unsigned)p.hkv;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((sel_attn_kernel<D, G, F16>), dim3(n), dim3(64 * SelCfg<D, G>::NW), 0, st, p);
   return hipGetLastError();
 }
 
@@ -497,9 +307,4 @@ hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStre
   if (f16) { NSA_SWITCH_G(run_text, true, p, st) }
   NSA_SWITCH_G(run_text, false, p, st)
 }
-hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st) {
-  if (f16) { NSA_SWITCH_G(run_sel, true, p, st) }
-  NSA_SWITCH_G(run_sel, false, p, st)
-}
-
 }  // namespace nsa

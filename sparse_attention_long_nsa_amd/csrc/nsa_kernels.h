@@ -53,6 +53,7 @@ struct SwaParams {
 
 struct SelParams {
   const uint16_t *q, *k, *v;
+  uint16_t *vt;            // workspace: values packed [Hkv][n_frames][d][64] fp16
   const int32_t *sel;      // [n_vis, Hkv, k]
   const float *gates;
   float *out;
