@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the VideoNSA attention layer forward pass (nsa_prefill) on one
+MI355X, at 131,072 vision + 512 text tokens (Qwen2.5-VL-7B layer shape: 28
+query heads, 4 KV heads, d = 128, bf16), top-32 blocks of 64 and a 256-token
+window -- the paper's own defaults (VideoNSA paper summary page, "Method").
+
+One step = one nsa_prefill call over the whole sequence with inputs resident
+in HBM. Prints one JSON line on stdout; everything else goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NSA attention tokens/s/layer at 128K vision tokens; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+SWEEP = ((8, 1024), (16, 512))  # fixed-budget trade of blocks against window
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def closed_form_work(shape, n_text_positions):
+    """Algorithmic work per kernel (flops for matrix kernels, bytes for
+    streaming ones) of one layer call, from the per-query key counts."""
+    s = shape
+    B, d, hq, hkv, k, w = s.block, s.head_dim, s.n_q_heads, s.n_kv_heads, s.top_k, s.window
+    t = np.arange(s.n_vis, dtype=np.int64)
+    cur = t // B
+    n_cmp = (t + 1) // B
+    n_sel = (np.minimum(k, cur + 1) - 1) * B + (t - cur * B + 1)
+    n_swa = np.minimum(w, t + 1)
+    text_keys = np.asarray(n_text_positions, dtype=np.int64) + 1
+    n_blk = s.n_vis // B
+    n_frames = -(-s.n_vis // B)
+    f4 = 4.0 * d * hq
+    vt_block = -(-d * (B + 4) // 512) * 512
+    return {
+        "cmp_pool": ("bytes", 2.0 * n_blk * B * hkv * d * 2 + 2.0 * n_blk * hkv * d * 2),
+        "cmp_attn": ("flops", f4 * float(n_cmp.sum())),
+        "blk_score_topk": ("bytes", 4.0 * hkv * float(cur.sum()) + 4.0 * s.n_vis * hkv * k),
+        "swa_attn": ("flops", f4 * float(n_swa.sum())),
+        "pack_vt": ("bytes", 2.0 * s.n_vis * hkv * d + 2.0 * n_frames * hkv * vt_block),
+        "sel_attn": ("flops", f4 * float(n_sel.sum())),
+        "text_attn": ("flops", f4 * float(text_keys.sum())),
+    }
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pmc_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary for
+    this kernel and workload, or None when the kernel source changed since."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or source_digest(src) != rec["source_sha256_16"]:
+        return None
+    return float(rec["hbm_bytes_per_launch"])
+
+
+def run_gpu(inp, dev, top_k, window, steps, warmup, per_kernel):
+    import torch
+    from sparse_attention_long_nsa_amd import binding
+    s = inp["shape"]
+
+    def call(out, ws):
+        return binding.prefill(dev["q"], dev["k"], dev["v"], inp["is_vision"], dev["w_k"],
+                               dev["w_v"], dev["gates"], top_k, window, block=s.block,
+                               out=out, workspace=ws)
+
+    r = call(None, None)
+    out, ws = r["out"], r["workspace"]
+    for _ in range(warmup):
+        call(out, ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call(out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kernels = None
+    if per_kernel:
+        binding.timing_reset()
+        binding.timing_enable(True)
+        for _ in range(steps):
+            call(out, ws)
+        torch.cuda.synchronize()
+        kernels = {n: (tot / cnt, cnt) for n, (tot, cnt) in binding.timing_read().items()}
+        binding.timing_enable(False)
+        binding.timing_reset()
+    return ms, kernels, out
+
+
+def cpu_baseline(inp, n_vis_rows, n_text_rows):
+    """The fp64 oracle, as it stands, on a bounded row sample of the same
+    workload; per-row times extrapolated to the whole sequence."""
+    import oracle
+    s = inp["shape"]
+    isv = inp["is_vision"].astype(bool)
+    V, T = np.nonzero(isv)[0], np.nonzero(~isv)[0]
+    rng = np.random.default_rng(1)
+    rv = np.sort(rng.choice(V, size=min(n_vis_rows, len(V)), replace=False))
+    t0 = time.perf_counter()
+    oracle.prefill(inp, rows=rv, want=())
+    tv = time.perf_counter() - t0
+    tt, rt = 0.0, np.zeros(0, dtype=np.int64)
+    if len(T):
+        rt = np.sort(rng.choice(T, size=min(n_text_rows, len(T)), replace=False))
+        t0 = time.perf_counter()
+        oracle.prefill(inp, rows=rt, want=())
+        tt = time.perf_counter() - t0
+    est = tv / len(rv) * len(V) + (tt / len(rt) * len(T) if len(rt) else 0.0)
+    return {
+        "value": s.n_tokens / est,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{len(rv)} random vision rows ({tv:.1f} s) + {len(rt)} random text rows "
+                   f"({tt:.1f} s) of the same workload, per-row time extrapolated to all "
+                   f"{s.n_tokens} rows"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen_128k_k32_w256")
+    ap.add_argument("--cpu-vision-rows", type=int, default=6000)
+    ap.add_argument("--cpu-text-rows", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this layer library runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_long_nsa_amd import binding
+    from sparse_attention_long_nsa_amd.inputs import PREFILL_PRESETS, make_prefill_inputs
+    binding.lib()  # fail loudly if the HIP library is missing
+    shape = PREFILL_PRESETS[args.workload]
+    t0 = time.time()
+    inp = make_prefill_inputs(shape, seed=0)
+    log(f"inputs {args.workload}: {time.time() - t0:.1f} s")
+    dev = {k: torch.from_numpy(inp[k]).to("cuda:0").to(torch.bfloat16).contiguous()
+           for k in ("q", "k", "v", "w_k", "w_v")}
+    dev["gates"] = torch.from_numpy(inp["gates"]).to("cuda:0")
+
+    ms, kern, _ = run_gpu(inp, dev, shape.top_k, shape.window, args.steps, args.warmup, True)
+    tokens = shape.n_tokens
+    value = tokens / (ms * 1e-3)
+    text_pos = np.nonzero(inp["is_vision"] == 0)[0]
+    work = closed_form_work(shape, text_pos)
+    layer_flops = sum(v for kind, v in work.values() if kind == "flops")
+    log(f"{ms:.3f} ms/step, {value / 1e6:.2f} M tokens/s")
+
+    per_kernel = {}
+    for name, (avg_ms, cnt) in sorted(kern.items(), key=lambda x: -x[1][0]):
+        kind, amount = work.get(name, (None, None))
+        ent = {"avg_ms": round(avg_ms, 4), "launches": cnt}
+        if kind == "flops":
+            ent["tflops"] = round(amount / (avg_ms * 1e-3) / 1e12, 1)
+            ent["frac_of_peak"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
+        elif kind == "bytes":
+            ent["gbs"] = round(amount / (avg_ms * 1e-3) / 1e9, 1)
+            ent["frac_of_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+        per_kernel[name] = ent
+        log(f"  {name:16s} {avg_ms:8.3f} ms  {ent}")
+    dom = max((n for n in kern if n in work), key=lambda n: kern[n][0])
+    kind, amount = work[dom]
+    avg = kern[dom][0] * 1e-3
+    if kind == "flops":
+        achieved, peak, unit, bound = amount / avg / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = amount / avg / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": pmc_traffic(dom, args.workload)}
+
+    def ms_of(*names):
+        return round(sum(kern.get(n, (0.0, 0))[0] for n in names), 4)
+
+    branch_ms = {"cmp": ms_of("cmp_pool", "cmp_attn"),
+                 "sel": ms_of("blk_score_topk", "pack_vt", "sel_attn"),
+                 "swa": ms_of("swa_attn"), "text": ms_of("text_attn", "text_merge")}
+
+    sweep = []
+    if not args.no_sweep:
+        for k, w in SWEEP:
+            sms, _, _ = run_gpu(inp, dev, k, w, max(3, args.steps // 2), 1, False)
+            sw = closed_form_work(shape.replace(top_k=k, window=w), text_pos)
+            fl = sum(v for kd, v in sw.values() if kd == "flops")
+            sweep.append({"top_k": k, "window": w, "ms_per_step": round(sms, 3),
+                          "tokens_per_s": round(tokens / (sms * 1e-3), 1),
+                          "mfma_peak_frac": round(fl / (sms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+            log(f"  sweep k={k} w={w}: {sms:.3f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_vision_rows, args.cpu_text_rows)
+        log(f"cpu baseline: {cpu}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n_vision": shape.n_vis, "n_text": shape.n_text,
+                   "n_q_heads": shape.n_q_heads, "n_kv_heads": shape.n_kv_heads,
+                   "head_dim": shape.head_dim, "block": shape.block, "top_k": shape.top_k,
+                   "window": shape.window, "seq_len": shape.n_tokens, "global_batch": 1,
+                   "parallelism": "single GPU"},
+        "mfma_peak_frac": round(layer_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_tflop": round(layer_flops / 1e12, 3),
+        "roofline": roofline,
+        "branch_ms": branch_ms,
+        "kernels": per_kernel,
+        "sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

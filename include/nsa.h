@@ -162,6 +162,17 @@ nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim,
                         int32_t block_size, int32_t dtype, const void *x, const void *w,
                         void *out_bf16, float *out_f32, void *stream);
 
+/* ------------------------------------------------------------- benchmark
+ * Opt-in per-kernel timing (for benchmarks; off by default). While enabled,
+ * each kernel launched by the library is bracketed by two HIP events on its
+ * launch stream. nsa_timing_read() waits for the recorded events, folds them
+ * into per-kernel totals and returns the number of distinct kernels; names
+ * point into library storage valid until the next read or reset. Entries are
+ * copied for the first max_entries kernels (arrays may be NULL). */
+nsa_status nsa_timing_enable(int enable);
+nsa_status nsa_timing_reset(void);
+int nsa_timing_read(int max_entries, const char **names, double *total_ms, int *counts);
+
 /* Static description of a status code. */
 const char *nsa_status_string(nsa_status status);
 

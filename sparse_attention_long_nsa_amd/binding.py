@@ -20,7 +20,8 @@ NSA_DTYPE_BF16, NSA_DTYPE_FP32 = 0, 1
 
 EXPORTED = (
     "nsa_prefill_workspace_size", "nsa_prefill", "nsa_decode_workspace_size", "nsa_decode",
-    "nsa_cmp_pool", "nsa_status_string", "nsa_version",
+    "nsa_cmp_pool", "nsa_timing_enable", "nsa_timing_reset", "nsa_timing_read",
+    "nsa_status_string", "nsa_version",
 )
 
 
@@ -82,11 +83,35 @@ def lib() -> ctypes.CDLL:
         L.nsa_cmp_pool.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, P, P, P, P, P]
         L.nsa_cmp_pool.restype = ctypes.c_int
+        L.nsa_timing_enable.argtypes = [ctypes.c_int]
+        L.nsa_timing_enable.restype = ctypes.c_int
+        L.nsa_timing_reset.restype = ctypes.c_int
+        L.nsa_timing_read.argtypes = [ctypes.c_int, P, P, P]
+        L.nsa_timing_read.restype = ctypes.c_int
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
         L.nsa_version.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def timing_enable(on: bool = True) -> None:
+    lib().nsa_timing_enable(1 if on else 0)
+
+
+def timing_reset() -> None:
+    lib().nsa_timing_reset()
+
+
+def timing_read() -> dict:
+    """{kernel: (total_ms, launches)} over the launches timed since the last
+    reset (waits for their events)."""
+    n = lib().nsa_timing_read(0, None, None, None)
+    names = (ctypes.c_char_p * max(n, 1))()
+    ms = (ctypes.c_double * max(n, 1))()
+    cnt = (ctypes.c_int * max(n, 1))()
+    n = lib().nsa_timing_read(n, names, ms, cnt)
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(n)}
 
 
 def status_string(status: int) -> str:

@@ -6,6 +6,7 @@
 
 #include "../../include/nsa.h"
 #include "nsa_kernels.h"
+#include "nsa_timing.h"
 
 namespace nsa {
 namespace {
@@ -173,6 +174,11 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
     e = (expr);                              \
     if (e != hipSuccess) return NSA_ERR_HIP; \
   } while (0)
+#define NSA_LAUNCH(name, expr) \
+  do {                         \
+    Timed tm_(name, s);        \
+    NSA_CHECK(expr);           \
+  } while (0)
 
   // fp32 inputs: block scores from split bf16 operands (q_hi, q_lo), every
   // other product in fp16
@@ -181,10 +187,10 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
     uint16_t *qh = at<uint16_t>(workspace, pl.off_qh), *qlo = at<uint16_t>(workspace, pl.off_ql);
     uint16_t *q16 = at<uint16_t>(workspace, pl.off_q16), *k16 = at<uint16_t>(workspace, pl.off_k16);
     uint16_t *v16 = at<uint16_t>(workspace, pl.off_v16);
-    NSA_CHECK(launch_split_bf16(static_cast<const float *>(q), pl.N * H * D, qh, qlo, s));
-    NSA_CHECK(launch_to_f16(static_cast<const float *>(q), pl.N * H * D, q16, s));
-    NSA_CHECK(launch_to_f16(static_cast<const float *>(k), pl.N * Hk * D, k16, s));
-    NSA_CHECK(launch_to_f16(static_cast<const float *>(v), pl.N * Hk * D, v16, s));
+    NSA_LAUNCH("split_q", launch_split_bf16(static_cast<const float *>(q), pl.N * H * D, qh, qlo, s));
+    NSA_LAUNCH("to_f16_q", launch_to_f16(static_cast<const float *>(q), pl.N * H * D, q16, s));
+    NSA_LAUNCH("to_f16_k", launch_to_f16(static_cast<const float *>(k), pl.N * Hk * D, k16, s));
+    NSA_LAUNCH("to_f16_v", launch_to_f16(static_cast<const float *>(v), pl.N * Hk * D, v16, s));
     qc = qh; ql = qlo; qb = q16; kb = k16; vb = v16;
     kcl = at<uint16_t>(workspace, pl.off_kcl);
   }
@@ -201,25 +207,27 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
                  pl.fp32 ? kc : nullptr, kcl, pl.fp32 ? nullptr : kc, k_cmp_out};
       PoolJob jv{static_cast<const char *>(v) + esz * pl.v0 * Hk * D, w_cmp_v, pl.hkv, pl.n_blk,
                  nullptr, nullptr, vc, v_cmp_out};
-      NSA_CHECK(launch_cmp_pool(jk, &jv, pl.d, pl.fp32, s));
+      NSA_LAUNCH("cmp_pool", launch_cmp_pool(jk, &jv, pl.d, pl.fp32, s));
     }
     CmpAttnParams cp{qc, ql, kc, kcl, vc, gate_logits, out, lse, gs, pl.v0,
                      (int)pl.n_vis, pl.hq, pl.hkv, pl.n_frames, sl2};
-    NSA_CHECK(launch_cmp_attn(cp, pl.d, pl.G, pl.fp32, s));
+    NSA_LAUNCH("cmp_attn", launch_cmp_attn(cp, pl.d, pl.G, pl.fp32, s));
     TopkParams tp{gs, sel, (int)pl.n_vis, pl.hkv, pl.k};
-    NSA_CHECK(launch_topk(tp, pl.n_frames, s));
+    NSA_LAUNCH("blk_score_topk", launch_topk(tp, pl.n_frames, s));
     SwaParams wp{qb, kb, vb, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.w,
                  pl.n_frames, sl2};
-    NSA_CHECK(launch_swa_attn(wp, pl.d, pl.G, pl.fp32, s));
+    NSA_LAUNCH("swa_attn", launch_swa_attn(wp, pl.d, pl.G, pl.fp32, s));
     SelParams sp{qb, kb, vb, at<uint16_t>(workspace, pl.off_vt), sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
                  pl.n_frames, sl2};
-    NSA_CHECK(launch_sel_attn(sp, pl.d, pl.G, pl.fp32, s));
+    NSA_LAUNCH("pack_vt", launch_pack_vt(sp, pl.d, pl.fp32, s));
+    NSA_LAUNCH("sel_attn", launch_sel_attn(sp, pl.d, pl.G, pl.fp32, s));
   }
   if (pl.n_text > 0) {
     TextParams tp{qb, kb, vb, at<float>(workspace, pl.off_po), at<float2>(workspace, pl.off_pml),
                   out, pl.v0, pl.v1, pl.N, (int)pl.n_text, pl.hq, pl.hkv, pl.n_split,
                   pl.split_len, pl.text_tiles, sl2};
-    NSA_CHECK(launch_text_attn(tp, pl.d, pl.G, pl.fp32, s));
+    NSA_LAUNCH("text_attn", launch_text_attn(tp, pl.d, pl.G, pl.fp32, s));
+    NSA_LAUNCH("text_merge", launch_text_merge(tp, pl.d, s));
   }
   return NSA_OK;
 }

@@ -266,9 +266,6 @@ hipError_t run_text(const TextParams &p, hipStream_t st) {
   const unsigned n = (unsigned)p.n_tiles * (unsigned)p.hkv * (unsigned)p.n_split;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((text_attn_kernel<D, G, F16>), dim3(n), dim3(kThreadsH), 0, st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((text_merge_kernel<D>), dim3((unsigned)(p.n_text * p.hq)), dim3(D), 0, st, p);
   return hipGetLastError();
 }
 
@@ -303,6 +300,13 @@ hipError_t launch_swa_attn(const SwaParams &p, int d, int G, bool f16, hipStream
   if (f16) { NSA_SWITCH_G(run_swa, true, p, st) }
   NSA_SWITCH_G(run_swa, false, p, st)
 }
+hipError_t launch_text_merge(const TextParams &p, int d, hipStream_t st) {
+  if (p.n_text == 0) return hipSuccess;
+  if (d == 64) hipLaunchKernelGGL((text_merge_kernel<64>), dim3((unsigned)(p.n_text * p.hq)), dim3(64), 0, st, p);
+  else hipLaunchKernelGGL((text_merge_kernel<128>), dim3((unsigned)(p.n_text * p.hq)), dim3(128), 0, st, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st) {
   if (f16) { NSA_SWITCH_G(run_text, true, p, st) }
   NSA_SWITCH_G(run_text, false, p, st)

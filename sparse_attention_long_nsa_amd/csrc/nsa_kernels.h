@@ -96,8 +96,10 @@ hipError_t launch_cmp_attn(const CmpAttnParams &p, int d, int G, bool split, hip
 hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st);
 // f16: q, k, v hold fp16 (else bf16; values are converted while staging)
 hipError_t launch_swa_attn(const SwaParams &p, int d, int G, bool f16, hipStream_t st);
+hipError_t launch_pack_vt(const SelParams &p, int d, bool f16, hipStream_t st);
 hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st);
+hipError_t launch_text_merge(const TextParams &p, int d, hipStream_t st);
 hipError_t launch_decode(const DecodeParams &p, int d, int G, hipStream_t st);
 
 // Which (head_dim, query heads per KV head) pairs have kernels.

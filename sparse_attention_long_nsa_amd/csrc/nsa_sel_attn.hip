@@ -336,10 +336,6 @@ template <int D, int G, bool F16>
 hipError_t run_sel(const SelParams &p, hipStream_t st) {
   const unsigned n = (unsigned)p.n_frames * (unsigned)p.hkv;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((pack_vt_kernel<D, F16>), dim3(n), dim3(256), 0, st, p.v, p.v0, p.n_vis, p.hkv,
-                     p.n_frames, p.vt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // two halves per (frame, group), ids padded to whole groups of 16
   const unsigned nwg = (2 * n + 15) / 16 * 16;
   hipLaunchKernelGGL((sel_attn_kernel<D, G, F16>), dim3(nwg), dim3(SelCfg<D, G>::NT), 0, st, p);
@@ -377,6 +373,19 @@ hipError_t dispatch(const SelParams &p, int d, int G, hipStream_t st) {
 
 hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st) {
   return f16 ? dispatch<true>(p, d, G, st) : dispatch<false>(p, d, G, st);
+}
+
+hipError_t launch_pack_vt(const SelParams &p, int d, bool f16, hipStream_t st) {
+  const unsigned n = (unsigned)p.n_frames * (unsigned)p.hkv;
+  if (n == 0) return hipSuccess;
+  if (d == 64) {
+    if (f16) hipLaunchKernelGGL((pack_vt_kernel<64, true>), dim3(n), dim3(256), 0, st, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.vt);
+    else hipLaunchKernelGGL((pack_vt_kernel<64, false>), dim3(n), dim3(256), 0, st, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.vt);
+  } else {
+    if (f16) hipLaunchKernelGGL((pack_vt_kernel<128, true>), dim3(n), dim3(256), 0, st, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.vt);
+    else hipLaunchKernelGGL((pack_vt_kernel<128, false>), dim3(n), dim3(256), 0, st, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.vt);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace nsa
