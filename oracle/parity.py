@@ -152,3 +152,32 @@ def sample_rows(inp: dict, n_random: int = 256, seed: int = 0, n_text: int = 32)
         picks.append(T[[0, -1]])
         picks.append(rng.choice(T, size=min(n_text, len(T)), replace=False))
     return np.unique(np.concatenate(picks))
+
+
+def decode_inputs_cmp(inp: dict, round_fn) -> tuple:
+    """Compressed caches for a decode workload, pooled by the oracle and
+    rounded by round_fn (to the dtype both sides then consume)."""
+    s = inp["shape"]
+    kc = np.stack([cmp_pool_f32(inp["k_cache"][b], inp["w_k"], s.block) for b in range(s.batch)])
+    vc = np.stack([cmp_pool_f32(inp["v_cache"][b], inp["w_v"], s.block) for b in range(s.batch)])
+    return round_fn(kc), round_fn(vc)
+
+
+def cmp_pool_f32(x, w, block):
+    return oracle.cmp_pool(x, w, block).astype(np.float32)
+
+
+def check_decode(inp: dict, kc: np.ndarray, vc: np.ndarray, gpu_out: np.ndarray,
+                 gpu_sel: np.ndarray, tie_tol: float = TIE_TOL):
+    """Oracle decode on the same compressed caches; index parity with the
+    near-tie rule, then output parity with the GPU selection injected on
+    exempt sequences."""
+    s = inp["shape"]
+    ref = oracle.decode(inp, kc, vc, want=("sel", "scores", "lse"))
+    cur = np.full(s.batch, s.cache_len // s.block - 1)
+    rep = index_parity(gpu_sel, ref["sel"], lambda idx: ref["scores"][idx], cur, tie_tol)
+    out_ref = ref["out"].copy()
+    if len(rep.exempt_rows):
+        inj = oracle.decode(inp, kc, vc, inject_sel=gpu_sel, want=())
+        out_ref[rep.exempt_rows] = inj["out"][rep.exempt_rows]
+    return rep, compare(gpu_out, out_ref), ref

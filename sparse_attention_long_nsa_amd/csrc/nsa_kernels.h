@@ -73,17 +73,18 @@ struct TextParams {
 };
 
 struct DecodeParams {
-  const bf16 *q;           // [Bt, Hq, d]
-  const bf16 *kcache, *vcache;  // [Bt, L, Hkv, d]
-  const bf16 *kc, *vc;     // [Bt, L/64, Hkv, d]
-  const float *gates;      // [Bt, Hq, 3]
-  float *out;              // [Bt, Hq, d]
-  int32_t *sel;            // [Bt, Hkv, k]
-  float *lse;              // [Bt, Hq]
-  float *logits;           // workspace [Bt, Hq, n_blk] scaled log2 logits
-  float2 *part_ml;         // workspace [Bt, Hq, n_split]
-  float *part_o;           // workspace [Bt, Hq, n_split, d]
-  int batch, L, hq, hkv, topk, window, n_blk, n_split;
+  const uint16_t *q;                // [Bt, Hq, d] bf16
+  const uint16_t *kcache, *vcache;  // [Bt, L, Hkv, d] bf16
+  const uint16_t *kc, *vc;          // [Bt, L/64, Hkv, d] bf16
+  const float *gates;               // [Bt, Hq, 3]
+  float *out;                       // [Bt, Hq, d]
+  int32_t *sel;                     // [Bt, Hkv, k]
+  float *lse;                       // [Bt, Hq] or null
+  float *logits;                    // workspace [Bt, Hq, n_blk] scaled log2 logits
+  float *cmp_part;                  // workspace [Bt, Hq, n_chunk, d + 2] (max, sum, o)
+  float *ocmp;                      // workspace [Bt, Hq, d]
+  float *fine_part;                 // workspace [Bt, Hq, n_items, d + 2]
+  int batch, L, hq, hkv, topk, window, n_blk, n_chunk, n_items;
   float sl2;
 };
 

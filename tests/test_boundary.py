@@ -135,3 +135,34 @@ def test_cmp_pool_validation():
     assert L.nsa_cmp_pool(640, 4, 128, 64, 0, None, FAKE, FAKE, None, None) == binding.NSA_ERR_INVALID_ARG
     assert L.nsa_cmp_pool(640, 4, 128, 64, 0, FAKE, FAKE, None, None, None) == binding.NSA_ERR_INVALID_ARG
     assert L.nsa_cmp_pool(640, 4, 96, 64, 0, FAKE, FAKE, FAKE, None, None) == binding.NSA_ERR_UNSUPPORTED
+
+
+def ddesc(batch=16, L=131072, hq=28, hkv=4, d=128, block=64, k=16, w=512, dtype=0):
+    return binding.DecodeDesc(batch, L, hq, hkv, d, block, k, w, 0.0, dtype)
+
+
+def dws(ds):
+    n = ctypes.c_size_t(0)
+    return binding.lib().nsa_decode_workspace_size(ctypes.byref(ds), ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=1000), binding.NSA_ERR_UNSUPPORTED),      # not a whole number of blocks
+    (dict(dtype=1), binding.NSA_ERR_UNSUPPORTED),
+    (dict(w=131073), binding.NSA_ERR_UNSUPPORTED),
+    (dict(k=65), binding.NSA_ERR_UNSUPPORTED),
+    (dict(hq=27), binding.NSA_ERR_INVALID_ARG),
+    (dict(batch=0), binding.NSA_ERR_INVALID_ARG),
+])
+def test_decode_validation(kw, status):
+    assert dws(ddesc(**kw))[0] == status
+
+
+def test_decode_workspace_and_pointer_checks():
+    st, need = dws(ddesc())
+    assert st == binding.NSA_OK and need > 0
+    L = binding.lib()
+    args = [FAKE] * 7
+    assert L.nsa_decode(ctypes.byref(ddesc()), *args, None, None, FAKE, need - 1, None) == binding.NSA_ERR_WORKSPACE
+    args[0] = None
+    assert L.nsa_decode(ctypes.byref(ddesc()), *args, None, None, FAKE, need, None) == binding.NSA_ERR_INVALID_ARG

@@ -141,6 +141,7 @@ def test_full_size_sampled_rows(preset):
     sel = gpu["sel"]
     cur = np.arange(sel.shape[0]) // 64
     assert np.all(sel.max(axis=2) == cur[:, None])
-    v = np.where(sel < 0, np.iinfo(np.int32).max, sel)
+    pad = 10**9 + np.arange(sel.shape[2])  # -1 padding sorts last, strictly increasing
+    v = np.where(sel < 0, pad, sel)
     assert np.all(np.diff(v, axis=2) > 0)
     assert np.all(np.isfinite(gpu["out"]))
