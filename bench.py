@@ -47,13 +47,13 @@ def closed_form_work(shape, n_text_positions):
     n_blk = s.n_vis // B
     n_frames = -(-s.n_vis // B)
     f4 = 4.0 * d * hq
-    vt_block = -(-d * (B + 4) // 512) * 512
+    kv_block = (-(-(d + 8) * B // 512) + -(-d * (B + 4) // 512)) * 512
     return {
         "cmp_pool": ("bytes", 2.0 * n_blk * B * hkv * d * 2 + 2.0 * n_blk * hkv * d * 2),
         "cmp_attn": ("flops", f4 * float(n_cmp.sum())),
         "blk_score_topk": ("bytes", 4.0 * hkv * float(cur.sum()) + 4.0 * s.n_vis * hkv * k),
         "swa_attn": ("flops", f4 * float(n_swa.sum())),
-        "pack_vt": ("bytes", 2.0 * s.n_vis * hkv * d + 2.0 * n_frames * hkv * vt_block),
+        "pack_kv": ("bytes", 4.0 * s.n_vis * hkv * d + 2.0 * n_frames * hkv * kv_block),
         "sel_attn": ("flops", f4 * float(n_sel.sum())),
         "text_attn": ("flops", f4 * float(text_keys.sum())),
     }
@@ -207,7 +207,7 @@ def main():
         return round(sum(kern.get(n, (0.0, 0))[0] for n in names), 4)
 
     branch_ms = {"cmp": ms_of("cmp_pool", "cmp_attn"),
-                 "sel": ms_of("blk_score_topk", "pack_vt", "sel_attn"),
+                 "sel": ms_of("blk_score_topk", "pack_kv", "sel_attn"),
                  "swa": ms_of("swa_attn"), "text": ms_of("text_attn", "text_merge")}
 
     sweep = []

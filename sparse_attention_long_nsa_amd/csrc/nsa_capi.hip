@@ -96,9 +96,8 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
     pl.off_k16 = take(sizeof(uint16_t) * pl.N * Hk * D);
     pl.off_v16 = take(sizeof(uint16_t) * pl.N * Hk * D);
   }
-  // packed V^T blocks: [Hkv][n_frames][d][64 + 4] fp16, whole 1-KB pieces per block
-  const size_t vt_block = (size_t)((pl.d * (kBlk + 4) + 511) / 512) * 512;
-  pl.off_vt = take(sizeof(uint16_t) * (size_t)pl.n_frames * Hk * vt_block);
+  // packed key/value blocks of the selection kernel: [Hkv][n_frames][K tile, V^T tile]
+  pl.off_vt = take(sizeof(uint16_t) * (size_t)pl.n_frames * Hk * packed_kv_block_elems(pl.d));
   pl.off_lse = take(sizeof(float) * pl.n_vis * H);
   pl.off_gs = take(sizeof(float) * (size_t)frame_off(pl.n_frames, pl.hkv));
   pl.off_sel = take(sizeof(int32_t) * pl.n_vis * Hk * pl.k);
@@ -219,7 +218,7 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
     NSA_LAUNCH("swa_attn", launch_swa_attn(wp, pl.d, pl.G, pl.fp32, s));
     SelParams sp{qb, kb, vb, at<uint16_t>(workspace, pl.off_vt), sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
                  pl.n_frames, sl2};
-    NSA_LAUNCH("pack_vt", launch_pack_vt(sp, pl.d, pl.fp32, s));
+    NSA_LAUNCH("pack_kv", launch_pack_kv(sp, pl.d, pl.fp32, s));
     NSA_LAUNCH("sel_attn", launch_sel_attn(sp, pl.d, pl.G, pl.fp32, s));
   }
   if (pl.n_text > 0) {

@@ -74,15 +74,25 @@ __device__ __forceinline__ float bfbits2f(uint16_t b) { return __uint_as_float(u
 // bf16 -> fp16: exact for magnitudes in fp16's normal range.
 __device__ __forceinline__ uint16_t bf2h_bits(uint16_t b) { return f2h_bits(bfbits2f(b)); }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (one query row of a
+// transposed score tile) with the row-swap permutes: the 32-lane swap of x
+// with itself yields x[l mod 32] and x[(l mod 32) + 32] in the two results,
+// the 16-lane swap likewise pairs rows 0/1 and 2/3.
 __device__ __forceinline__ float grp_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float grp_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }

@@ -53,7 +53,7 @@ struct SwaParams {
 
 struct SelParams {
   const uint16_t *q, *k, *v;
-  uint16_t *vt;            // workspace: values packed [Hkv][n_frames][d][64] fp16
+  uint16_t *kv;            // workspace: packed [Hkv][n_frames][K tile, V^T tile]
   const int32_t *sel;      // [n_vis, Hkv, k]
   const float *gates;
   float *out;
@@ -97,7 +97,8 @@ hipError_t launch_cmp_attn(const CmpAttnParams &p, int d, int G, bool split, hip
 hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st);
 // f16: q, k, v hold fp16 (else bf16; values are converted while staging)
 hipError_t launch_swa_attn(const SwaParams &p, int d, int G, bool f16, hipStream_t st);
-hipError_t launch_pack_vt(const SelParams &p, int d, bool f16, hipStream_t st);
+hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st);
+size_t packed_kv_block_elems(int d);  // elements of one packed (K, V^T) block
 hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_merge(const TextParams &p, int d, hipStream_t st);
