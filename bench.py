@@ -47,7 +47,7 @@ def closed_form_work(shape, n_text_positions):
     n_blk = s.n_vis // B
     n_frames = -(-s.n_vis // B)
     f4 = 4.0 * d * hq
-    kv_block = (-(-(d + 8) * B // 512) + -(-d * (B + 4) // 512)) * 512
+    kv_block = 2 * B * d
     return {
         "cmp_pool": ("bytes", 2.0 * n_blk * B * hkv * d * 2 + 2.0 * n_blk * hkv * d * 2),
         "cmp_attn": ("flops", f4 * float(n_cmp.sum())),

@@ -3,17 +3,21 @@
 // query's own block is causal inside.
 //
 // Selected blocks differ per query, and only the G query heads of one token
-// share a set, so a 16-row matrix-core tile holds TP = 16/G tokens x G heads,
-// one tile per consumer wave. A workgroup takes TOK consecutive tokens of one
-// KV group and the union of the blocks they selected, in ascending order.
-// Two producer waves stream the union's blocks into a ring of LDS slots with
-// direct global->LDS copies; each consumer wave jumps straight to the next
-// block its own tile needs, waits only for that block, and runs at its own
-// pace: there is no workgroup barrier per block, so a block that few tiles
-// need costs only those tiles. A slot is refilled once every consumer has
-// moved past its block. Keys and values are first packed once per call into
-// block-major tiles (K as laid out in LDS, V transposed to fp16), so each
-// block is one contiguous region and the copies are plain linear ones.
+// share a set, so a 16-row matrix-core tile holds TP = 16/G tokens x G heads;
+// a consumer wave owns RT such tiles. A workgroup takes TOK consecutive
+// tokens (half a 64-token frame where the tiles allow: tokens of one frame
+// pick largely the same blocks) of one KV group and the union of the blocks
+// they selected, in ascending order. Two producer waves stream the union's
+// blocks into a ring of LDS slots with direct global->LDS copies; each
+// consumer wave walks the union positions its own tokens selected, waits
+// only for those blocks, and runs at its own pace: there is no workgroup
+// barrier per block, so a block that few tiles need costs only those tiles.
+// A slot is refilled once every consumer has moved past its block. Keys and
+// values are first packed once per call into block-major tiles, exactly as
+// they sit in LDS (K row-major, V transposed to fp16, both with 16-byte
+// chunks XOR-swizzled per row so that the 16-byte fragment reads are free of
+// bank conflicts without padding), so each block is one contiguous 2*64*d
+// element region and the copies are plain linear ones.
 //
 // Producer/consumer protocol (all counters in LDS, each written by one wave):
 //   ready[p]  blocks 0..ready[p]-1 of producer p's pieces are in LDS
@@ -33,26 +37,60 @@ constexpr int kSelMaxBlk = 8192;
 constexpr int kSpinLimit = 1 << 22;   // s_sleep(1) rounds, about 0.1 s
 constexpr float kRescaleSlack = 8.f;  // log2 units a running max may lag behind
 
+// Swizzled LDS/global layout of one packed block: K tile [64 keys][D] then
+// V^T tile [D dims][64 keys], 16-byte chunks (8 elements) permuted per row.
+// A fragment read by lanes 0..15 (16 consecutive rows, one chunk index)
+// then touches 16 distinct 16-byte bank groups.
+template <int D>
+struct SelTile {
+  static constexpr int KE = kBlk * D, VE = D * kBlk;  // elements
+  // chunk position of logical chunk c in row r of a row of `bytes` bytes
+  template <int BYTES>
+  __host__ __device__ static constexpr int swz(int r, int c) {
+    return BYTES >= 256 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+  }
+  // V^T rows hold each 32-key half with keys permuted so that lane group j
+  // of the PV fragment finds its eight keys {4j..4j+3, 16+4j..16+4j+3} in
+  // one chunk: stored key slot 8j+i <- key 4j+i (i < 4), 16+4j+i-4 (i >= 4)
+  __host__ __device__ static constexpr int vkey(int slot) {
+    const int h = slot / 32, p = slot % 32, j = p / 8, i = p % 8;
+    return 32 * h + (i < 4 ? 4 * j + i : 16 + 4 * j + (i - 4));
+  }
+};
+
+// A operand of S^T = K Q^T from a staged K tile: keys 16*kt + (l%16), dims
+// 32*ds + 8*(l/16) .. +7.
+template <int D>
+__device__ __forceinline__ u16x8 sel_k_frag(const uint16_t *ks, int kt, int ds, int lane) {
+  const int r = 16 * kt + (lane & 15), c = 4 * ds + (lane >> 4);
+  return *reinterpret_cast<const u16x8 *>(ks + r * D + 8 * SelTile<D>::template swz<2 * D>(r, c));
+}
+// A operand of O^T = V^T P^T from a staged V^T tile: dim 16*dt + (l%16),
+// the eight keys of lane group l/16 in half ks (one swizzled chunk).
+template <int D>
+__device__ __forceinline__ u16x8 sel_v_frag(const uint16_t *vt, int dt, int ks, int lane) {
+  const int r = 16 * dt + (lane & 15), c = 4 * ks + (lane >> 4);
+  return *reinterpret_cast<const u16x8 *>(vt + r * kBlk + 8 * SelTile<D>::template swz<2 * kBlk>(r, c));
+}
+
 template <int D, int G>
 struct SelCfg {
-  static constexpr int TP = 16 / G;                          // tokens per row tile
-  static constexpr int TOK = (14 * TP < 32) ? 14 * TP : 32;  // tokens per workgroup
-  static constexpr int NC = (TOK + TP - 1) / TP;             // consumer waves, one tile each
-  static constexpr int NPW = 2;                              // producer waves
+  static constexpr int TP = 16 / G;                   // tokens per row tile
+  static constexpr int RT = (TP <= 4) ? 2 : 1;        // row tiles per consumer wave
+  static constexpr int TT = RT * TP;                  // tokens per consumer wave
+  static constexpr int NC = (32 / TT > 0) ? 32 / TT : 1;  // consumer waves
+  static constexpr int TOK = NC * TT;                 // tokens per workgroup
+  static constexpr int NPW = 2;                       // producer waves
   static constexpr int NW = NC + NPW;
   static constexpr int NT = 64 * NW;
-  // LDS tiles use the padded, conflict-free layouts of Tile<D>, rounded up
-  // to whole 1-KB copy pieces (512 elements).
-  static constexpr int KP = (Tile<D>::kElems + 511) / 512;  // pieces of a K tile
-  static constexpr int VP = (Tile<D>::vElems + 511) / 512;  // pieces of a V^T tile
-  static constexpr int KE = KP * 512, VE = VP * 512;        // tile sizes (elements)
-  static constexpr int SE = KE + VE;                        // one slot
-  static constexpr int NP = KP + VP;                        // pieces per block
-  static constexpr int PPP = NP / NPW;                      // pieces per producer per block
-  static constexpr int R = (D == 64) ? 6 : 4;               // ring slots
+  static constexpr int KE = SelTile<D>::KE, VE = SelTile<D>::VE;
+  static constexpr int SE = KE + VE;                  // one slot (elements)
+  static constexpr int NP = SE / 512;                 // 1-KB copy pieces per block
+  static constexpr int PPP = NP / NPW;                // pieces per producer per block
+  static constexpr int R = (D == 64) ? 8 : 4;         // ring slots
   static constexpr int INFL = (63 / PPP < R) ? 63 / PPP : R;  // blocks in flight per producer
-  static_assert(NP % NPW == 0, "pieces split evenly between the producers");
-  static_assert(NW <= 16, "at most 16 waves");
+  static_assert(NP % NPW == 0 && PPP % 4 == 0, "pieces split evenly, four per address set-up");
+  static_assert(TOK <= 32 && NW <= 16, "workgroup shape");
 };
 
 // Waits until at most N vector-memory operations of this wave are in flight
@@ -71,6 +109,7 @@ __device__ __forceinline__ void wait_blocks(int n) {
     case 3: if constexpr (3 * PPP < 64) wait_vm_c<3 * PPP>(); else wait_vm_c<0>(); break;
     case 4: if constexpr (4 * PPP < 64) wait_vm_c<4 * PPP>(); else wait_vm_c<0>(); break;
     case 5: if constexpr (5 * PPP < 64) wait_vm_c<5 * PPP>(); else wait_vm_c<0>(); break;
+    case 6: if constexpr (6 * PPP < 64) wait_vm_c<6 * PPP>(); else wait_vm_c<0>(); break;
     default: wait_vm_c<0>(); break;
   }
 }
@@ -83,24 +122,81 @@ typedef __attribute__((address_space(3))) int lds_int;
 __device__ __forceinline__ int lds_load(int *p) { return *(volatile lds_int *)(p); }
 __device__ __forceinline__ void lds_store(int *p, int v) { *(volatile lds_int *)(p) = v; }
 
+// Consumes one staged block for one row tile: S^T = K Q^T, causal mask in
+// the own block, lazily rescaled softmax, O^T += V^T P^T.
+template <int D, int G, bool F16>
+__device__ __forceinline__ void sel_tile(const uint16_t *ks, const uint16_t *vt, const u16x8 (&qf)[D / 32],
+                                         f32x4 (&o)[D / 16], float &m, float &l, bool rowneed,
+                                         int mask_b, int t, float sl2, int lane) {
+  const int grp = lane >> 4;
+  f32x4 s[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    s[kt] = zero4();
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) s[kt] = mfma_qk<F16>(sel_k_frag<D>(ks, kt, ds, lane), qf[ds], s[kt]);
+  }
+  if (mask_b >= 0) {  // causal inside the own block
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int j0 = mask_b * kBlk + 16 * kt + 4 * grp;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[kt][e] = (j0 + e <= t) ? s[kt][e] : -INFINITY;
+    }
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                       fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+  const float gmx = grp_max(mx);  // all lanes take part in the exchange
+  mx = rowneed ? gmx * sl2 : -INFINITY;
+  // the running max only moves when a row's new max exceeds it by the
+  // slack; probabilities then stay below 2^slack, exact in fp16's range
+  if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
+    const float mn = fmaxf(m, mx);
+    const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
+    m = mn;
+  }
+  // rows that do not take this block get probability exp2(-inf) = 0
+  const float nbase = (rowneed && m != -INFINITY) ? -m : -INFINITY;
+  float ls = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[kt][e] = __builtin_amdgcn_exp2f(fmaf(s[kt][e], sl2, nbase));
+      ls += s[kt][e];
+    }
+  l += ls;
+  const u16x8 pp0 = pack_p(s[0], s[1]), pp1 = pack_p(s[2], s[3]);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    o[dt] = mfma_f16(sel_v_frag<D>(vt, dt, 0, lane), pp0, o[dt]);
+    o[dt] = mfma_f16(sel_v_frag<D>(vt, dt, 1, lane), pp1, o[dt]);
+  }
+}
+
 template <int D, int G, bool F16>
 __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams p) {
   using C = SelCfg<D, G>;
-  constexpr int TP = C::TP, TOK = C::TOK, NC = C::NC, R = C::R;
-  constexpr int UW = TOK * kSelMaxK / 32;      // words of a union-position bitmap
+  constexpr int TP = C::TP, RT = C::RT, TT = C::TT, TOK = C::TOK, NC = C::NC, R = C::R;
+  constexpr int kSent = 0x7fffffff;
   __shared__ __attribute__((aligned(16))) uint16_t ring[R * C::SE];
   __shared__ int16_t sl[TOK * kSelMaxK];       // selected blocks per token, -1 padded
   __shared__ int16_t ulist[TOK * kSelMaxK];    // union, ascending
   __shared__ uint32_t ubits[kSelMaxBlk / 32];  // union as a bitmask over blocks
   __shared__ int16_t wpre[kSelMaxBlk / 32];    // union entries before each bitmask word
-  __shared__ uint32_t need_bm[TOK][UW];        // per token: union positions it selected
   __shared__ int pass_[NC], ready_[C::NPW];
   __shared__ int n_union;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4;
-  // Workgroup -> (KV group, chunk): chunks 2c and 2c+1 of a group go to ids
-  // 8 apart, i.e. to the same XCD at about the same time, so the blocks they
-  // both selected are served from that XCD's L2; heaviest chunks first.
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // Workgroup -> (KV group, chunk): chunks 2c and 2c+1 of a group (the two
+  // halves of a frame) go to ids 8 apart, i.e. to the same XCD at about the
+  // same time, so the blocks they both selected are served from that XCD's
+  // L2; heaviest chunks first.
   const int n_chunk = (p.n_vis + TOK - 1) / TOK;
   const int n_pair = (n_chunk + 1) / 2;
   const unsigned i = blockIdx.x;
@@ -117,10 +213,8 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   const int n_blk_all = (p.n_vis + kBlk - 1) / kBlk;
   const int nwords = (n_blk_all + 31) / 32;
 
-  // ---- selected blocks of the workgroup's tokens, their union, and per
-  //      token the set of union positions it needs
+  // ---- selected blocks of the workgroup's tokens and their union
   for (int w = tid; w < nwords; w += C::NT) ubits[w] = 0u;
-  for (int w = tid; w < TOK * UW; w += C::NT) (&need_bm[0][0])[w] = 0u;
   if (tid < NC) pass_[tid] = 0;
   if (tid < C::NPW) ready_[tid] = 0;
   for (int idx = tid; idx < TOK * k; idx += C::NT) {
@@ -159,14 +253,6 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
     if (lane == 0) n_union = running;
   }
   __syncthreads();
-  for (int idx = tid; idx < TOK * k; idx += C::NT) {
-    const int b = sl[idx];
-    if (b >= 0) {
-      const int u = wpre[b >> 5] + __popc(ubits[b >> 5] & ((1u << (b & 31)) - 1u));
-      atomicOr(&need_bm[idx / k][u >> 5], 1u << (u & 31));
-    }
-  }
-  __syncthreads();
   const int nU = n_union;
 
   if (wv >= NC) {
@@ -176,15 +262,21 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
     const int pw = wv - NC;
     const uint16_t *kvg = p.kv + (int64_t)g * p.n_frames * C::SE + pw * C::PPP * 512 + lane * 8;
     int issued = 0, pub = 0, spins = 0;
+    int free_until = R - 1;  // highest block whose slot is known to be free
+    int ul = 0;              // ulist[(issued & ~63) + lane]
     while (pub < nU) {
       if (issued < nU && issued - pub < C::INFL) {
-        bool free_slot = issued < R;
-        if (!free_slot) {
-          const int v = lane < NC ? lds_load(&pass_[lane]) : 0x7fffffff;
-          free_slot = __builtin_amdgcn_ballot_w64(v < issued - R + 1) == 0;
+        if (issued > free_until) {
+          const int v = lane < NC ? lds_load(&pass_[lane]) : kSent;
+          int mn = v;
+#pragma unroll
+          for (int q = 0; q < NC; ++q) mn = min(mn, __builtin_amdgcn_readlane(v, q));
+          free_until = mn + R - 1;
         }
-        if (free_slot) {
-          const uint16_t *src = kvg + (int64_t)ulist[issued] * C::SE;
+        if (issued <= free_until) {
+          if ((issued & 63) == 0) ul = issued + lane < nU ? (int)ulist[issued + lane] : 0;
+          const int blk = __builtin_amdgcn_readlane(ul, issued & 63);
+          const uint16_t *src = kvg + (int64_t)blk * C::SE;
           uint16_t *dst = ring + (issued % R) * C::SE + pw * C::PPP * 512;
           asm volatile("" ::: "memory");
 #pragma unroll
@@ -192,9 +284,9 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
             const uint16_t *s4 = src + q0 * 512;
             lds_void *d4 = (lds_void *)(dst + q0 * 512);
             __builtin_amdgcn_global_load_lds(s4, d4, 16, 0, 0);
-            if (q0 + 1 < C::PPP) __builtin_amdgcn_global_load_lds(s4, d4, 16, 1024, 0);
-            if (q0 + 2 < C::PPP) __builtin_amdgcn_global_load_lds(s4, d4, 16, 2048, 0);
-            if (q0 + 3 < C::PPP) __builtin_amdgcn_global_load_lds(s4, d4, 16, 3072, 0);
+            __builtin_amdgcn_global_load_lds(s4, d4, 16, 1024, 0);
+            __builtin_amdgcn_global_load_lds(s4, d4, 16, 2048, 0);
+            __builtin_amdgcn_global_load_lds(s4, d4, 16, 3072, 0);
           }
           ++issued;
           continue;
@@ -220,56 +312,66 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   // ------------------------------------------------------------ consumer
   const int c = wv;
   const int r16 = lane & 15, tau = r16 / G, hh = r16 % G;
-  const int tk = c * TP + tau;
-  const bool rowvalid = tau < TP && tk < ntok;
-  const int t = tok0 + tk;
-  const int64_t qrow = (p.v0 + (rowvalid ? t : 0)) * p.hq + (int64_t)g * G + hh;
-  u16x8 qf[D / 32];
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds) qf[ds] = rowvalid ? q_frag_global(p.q + qrow * D, ds, lane) : zero8();
-  f32x4 o[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = zero4();
-  float m = -INFINITY, l = 0.f;
-  bool bad = false;
   const float sl2 = p.sl2;
-
-  // Own blocks of the tile's first and last token, and their union
-  // positions (-1 when not in the union): only these need the causal mask.
-  const int tfirst = tok0 + c * TP, tlast = tok0 + min(c * TP + TP, ntok) - 1;
-  int own_b[2] = {tfirst / kBlk, tlast / kBlk}, own_u[2];
+  u16x8 qf[RT][D / 32];
+  f32x4 o[RT][D / 16];
+  float m[RT], l[RT];
+  int trow[RT], own_b[RT][2], own_u[RT][2];
+  bool rowvalid[RT];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int b = own_b[e];
-    const uint32_t w = ubits[b >> 5];
-    own_u[e] = ((w >> (b & 31)) & 1u) ? (int)wpre[b >> 5] + __popc(w & ((1u << (b & 31)) - 1u)) : -1;
-    own_u[e] = __builtin_amdgcn_readfirstlane(own_u[e]);
-  }
-
-  // walk the union positions the tile's tokens need, one bitmap word at a time
-  const int nUW = (nU + 31) / 32;
-  int wi = 0;
-  uint32_t cw[TP];
+  for (int r = 0; r < RT; ++r) {
+    const int tk = c * TT + r * TP + tau;
+    rowvalid[r] = tau < TP && tk < ntok;
+    trow[r] = tok0 + tk;
+    const int64_t qrow = (p.v0 + (rowvalid[r] ? trow[r] : 0)) * p.hq + (int64_t)g * G + hh;
 #pragma unroll
-  for (int q = 0; q < TP; ++q) cw[q] = (c * TP + q < ntok) ? __builtin_amdgcn_readfirstlane(need_bm[c * TP + q][0]) : 0u;
-  for (;;) {
-    uint32_t any = 0;
+    for (int ds = 0; ds < D / 32; ++ds)
+      qf[r][ds] = rowvalid[r] ? q_frag_global(p.q + qrow * D, ds, lane) : zero8();
 #pragma unroll
-    for (int q = 0; q < TP; ++q) any |= cw[q];
-    if (any == 0) {
-      if (++wi >= nUW) break;
+    for (int dt = 0; dt < D / 16; ++dt) o[r][dt] = zero4();
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+    // own blocks of the tile's first and last token and their union
+    // positions (-1 when absent): only these need the causal mask
+    const int t0 = c * TT + r * TP;
+    const int tfirst = tok0 + min(t0, ntok - 1), tlast = tok0 + min(t0 + TP, ntok) - 1;
+    own_b[r][0] = tfirst / kBlk;
+    own_b[r][1] = tlast / kBlk;
 #pragma unroll
-      for (int q = 0; q < TP; ++q)
-        cw[q] = (c * TP + q < ntok) ? __builtin_amdgcn_readfirstlane(need_bm[c * TP + q][wi]) : 0u;
-      continue;
+    for (int e = 0; e < 2; ++e) {
+      const int b = own_b[r][e];
+      const uint32_t w = ubits[b >> 5];
+      const int u = ((w >> (b & 31)) & 1u) ? (int)wpre[b >> 5] + __popc(w & ((1u << (b & 31)) - 1u)) : -1;
+      own_u[r][e] = __builtin_amdgcn_readfirstlane(u);
     }
-    const int bit = __ffs(any) - 1;
-    const int u = wi * 32 + bit;
-    uint32_t need = 0;
+  }
+  // per token of the wave: lane j holds the union position of its j-th
+  // selected block (ascending; sentinel past the end)
+  int lst[TT], cur[TT], nxt[TT];
 #pragma unroll
-    for (int q = 0; q < TP; ++q) {
-      need |= ((cw[q] >> bit) & 1u) << q;
-      cw[q] &= ~(1u << bit);
+  for (int q = 0; q < TT; ++q) {
+    const int tq = c * TT + q;
+    const int b = (tq < ntok && lane < k) ? sl[tq * k + lane] : -1;
+    lst[q] = b < 0 ? kSent : (int)wpre[b >> 5] + __popc(ubits[b >> 5] & ((1u << (b & 31)) - 1u));
+    cur[q] = 0;
+    nxt[q] = __builtin_amdgcn_readlane(lst[q], 0);
+  }
+  bool bad = false;
+  for (;;) {
+    int u = kSent;
+#pragma unroll
+    for (int q = 0; q < TT; ++q) u = min(u, nxt[q]);
+    if (u == kSent) break;
+    uint32_t need[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) need[r] = 0u;
+#pragma unroll
+    for (int q = 0; q < TT; ++q) {
+      if (nxt[q] == u) {
+        need[q / TP] |= 1u << (q % TP);
+        ++cur[q];
+        nxt[q] = cur[q] < k ? __builtin_amdgcn_readlane(lst[q], cur[q]) : kSent;
+      }
     }
     if (lane == 0) lds_store(&pass_[c], u);
     // wait for both producers' pieces of block u
@@ -281,94 +383,57 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
     asm volatile("" ::: "memory");
     const uint16_t *ks = ring + (u % R) * C::SE;
     const uint16_t *vt = ks + C::KE;
-
-    f32x4 s[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = zero4();
-#pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) s[kt] = mfma_qk<F16>(k_frag<D>(ks, kt, ds, lane), qf[ds], s[kt]);
-    }
-    const bool rowneed = rowvalid && ((need >> tau) & 1u);
-    if (u == own_u[0] || u == own_u[1]) {  // causal inside the own block
-      const int b = (u == own_u[0]) ? own_b[0] : own_b[1];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int j0 = b * kBlk + 16 * kt + 4 * grp;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[kt][e] = (j0 + e <= t) ? s[kt][e] : -INFINITY;
+    for (int r = 0; r < RT; ++r) {
+      if (need[r]) {
+        const int mask_b = (u == own_u[r][0]) ? own_b[r][0] : (u == own_u[r][1]) ? own_b[r][1] : -1;
+        const bool rowneed = rowvalid[r] && ((need[r] >> tau) & 1u);
+        sel_tile<D, G, F16>(ks, vt, qf[r], o[r], m[r], l[r], rowneed, mask_b, trow[r], sl2, lane);
       }
-    }
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
-                         fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
-    const float gmx = grp_max(mx);  // all lanes take part in the exchange
-    mx = rowneed ? gmx * sl2 : -INFINITY;
-    // the running max only moves when a row's new max exceeds it by the
-    // slack; probabilities then stay below 2^slack, exact in fp16's range
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
-      m = mn;
-    }
-    // rows that do not take this block get probability exp2(-inf) = 0
-    const float nbase = (rowneed && m != -INFINITY) ? -m : -INFINITY;
-    float ls = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[kt][e] = __builtin_amdgcn_exp2f(fmaf(s[kt][e], sl2, nbase));
-        ls += s[kt][e];
-      }
-    l += ls;
-    const u16x8 pp0 = pack_p(s[0], s[1]), pp1 = pack_p(s[2], s[3]);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      o[dt] = mfma_f16(v_frag<D>(vt, dt, 0, lane), pp0, o[dt]);
-      o[dt] = mfma_f16(v_frag<D>(vt, dt, 1, lane), pp1, o[dt]);
     }
   }
   // all reads of ring slots have returned before the final release
   __builtin_amdgcn_s_waitcnt(0xC07F);
   if (lane == 0) lds_store(&pass_[c], nU);
 
-  const float L = grp_sum(l);
-  if (rowvalid) {
-    const float gate = bad ? __builtin_nanf("") : sigmoidf_(p.gates[qrow * 3 + 1]) / L;
-    float *dst = p.out + qrow * D + 4 * grp;
+  const int grp = lane >> 4;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      f32x4 *d4 = reinterpret_cast<f32x4 *>(dst + 16 * dt);
-      *d4 = *d4 + o[dt] * gate;
+  for (int r = 0; r < RT; ++r) {
+    const float L = grp_sum(l[r]);
+    if (rowvalid[r]) {
+      const int64_t qrow = (p.v0 + trow[r]) * p.hq + (int64_t)g * G + hh;
+      const float gate = bad ? __builtin_nanf("") : sigmoidf_(p.gates[qrow * 3 + 1]) / L;
+      float *dst = p.out + qrow * D + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        f32x4 *d4 = reinterpret_cast<f32x4 *>(dst + 16 * dt);
+        *d4 = *d4 + o[r][dt] * gate;
+      }
     }
   }
 }
 
 // Packs one KV head's keys and values into the selection kernel's block
-// layout: per (head, block) the padded K tile [64][d+8] (as given: bf16, or
-// fp16 for fp32 inputs) followed by the padded V^T tile [d][64+4] in fp16,
-// each rounded up to whole 1-KB pieces; keys past the sequence are zero.
+// layout (SelTile): per (head, block) the swizzled K tile (as given: bf16,
+// or fp16 for fp32 inputs) followed by the swizzled, key-permuted V^T tile
+// in fp16; keys past the sequence are zero.
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v, int64_t v0,
                                                       int n_vis, int hkv, int n_frames,
                                                       uint16_t *__restrict__ kv) {
-  constexpr int KE = ((Tile<D>::kElems + 511) / 512) * 512;
-  constexpr int VE = ((Tile<D>::vElems + 511) / 512) * 512;
-  constexpr int KS = Tile<D>::kStr, VS = Tile<D>::vStr;
+  using T = SelTile<D>;
   __shared__ uint16_t tile[kBlk][D + 2];
   const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
   const int tid = threadIdx.x;
-  uint16_t *dst = kv + ((int64_t)g * n_frames + b) * (KE + VE);
-  for (int idx = tid; idx < KE; idx += 256) {
-    const int r = idx / KS, c = idx % KS;
+  uint16_t *dst = kv + ((int64_t)g * n_frames + b) * (T::KE + T::VE);
+  // K: chunk c of key row r goes to chunk position swz(r, c)
+  for (int idx = tid; idx < kBlk * (D / 8); idx += 256) {
+    const int r = idx / (D / 8), c = idx % (D / 8);
     const int t = b * kBlk + r;
-    dst[idx] = (r < kBlk && c < D && t < n_vis) ? k[((v0 + t) * hkv + g) * (int64_t)D + c] : 0;
+    u16x8 val = zero8();
+    if (t < n_vis) val = *reinterpret_cast<const u16x8 *>(k + ((v0 + t) * hkv + g) * (int64_t)D + 8 * c);
+    *reinterpret_cast<u16x8 *>(dst + r * D + 8 * T::template swz<2 * D>(r, c)) = val;
   }
   for (int idx = tid; idx < kBlk * D; idx += 256) {
     const int key = idx / D, d = idx % D;
@@ -381,9 +446,13 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict
     tile[key][d] = x;
   }
   __syncthreads();
-  for (int idx = tid; idx < VE; idx += 256) {
-    const int d = idx / VS, key = idx % VS;
-    dst[KE + idx] = (d < D && key < kBlk) ? tile[key][d] : 0;
+  // V^T: row d, stored key slot s <- key vkey(s); chunk c at swz(d, c)
+  for (int idx = tid; idx < D * (kBlk / 8); idx += 256) {
+    const int d = idx / (kBlk / 8), c = idx % (kBlk / 8);
+    u16x8 val;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) val[i] = tile[T::vkey(8 * c + i)][d];
+    *reinterpret_cast<u16x8 *>(dst + T::KE + d * kBlk + 8 * T::template swz<2 * kBlk>(d, c)) = val;
   }
 }
 
@@ -445,8 +514,6 @@ hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st) {
   return hipGetLastError();
 }
 
-size_t packed_kv_block_elems(int d) {
-  return (size_t)(((d + 8) * kBlk + 511) / 512 + (d * (kBlk + 4) + 511) / 512) * 512;
-}
+size_t packed_kv_block_elems(int d) { return (size_t)2 * kBlk * d; }
 
 }  // namespace nsa
