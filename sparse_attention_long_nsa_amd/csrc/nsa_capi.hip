@@ -22,13 +22,13 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct PrefillPlan {
   int64_t N = 0, v0 = 0, v1 = 0, n_vis = 0, n_text = 0;
   int hq = 0, hkv = 0, d = 0, G = 0, k = 0, w = 0;
-  int n_blk = 0, n_frames = 0;
+  int n_blk = 0, n_frames = 0, n_cch = 0;
   bool fp32 = false;
   float scale = 0.f;
   int n_split = 0, split_len = 0, text_tiles = 0;
   size_t off_kc = 0, off_vc = 0, off_kcl = 0, off_qh = 0, off_ql = 0, off_q16 = 0, off_k16 = 0,
          off_v16 = 0;
-  size_t off_vt = 0, off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0, total = 0;
+  size_t off_kvc = 0, off_vt = 0, off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0, total = 0;
 };
 
 nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, PrefillPlan &pl) {
@@ -96,6 +96,9 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
     pl.off_k16 = take(sizeof(uint16_t) * pl.N * Hk * D);
     pl.off_v16 = take(sizeof(uint16_t) * pl.N * Hk * D);
   }
+  // packed compressed key/value chunks of the compression branch (fp16 path)
+  pl.n_cch = (pl.n_blk + kBlk - 1) / kBlk;
+  if (!pl.fp32) pl.off_kvc = take(sizeof(uint16_t) * (size_t)pl.n_cch * Hk * packed_kv_block_elems(pl.d));
   // packed key/value blocks of the selection kernel: [Hkv][n_frames][K tile, V^T tile]
   pl.off_vt = take(sizeof(uint16_t) * (size_t)pl.n_frames * Hk * packed_kv_block_elems(pl.d));
   pl.off_lse = take(sizeof(float) * pl.n_vis * H);
@@ -208,7 +211,12 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
                  nullptr, nullptr, vc, v_cmp_out};
       NSA_LAUNCH("cmp_pool", launch_cmp_pool(jk, &jv, pl.d, pl.fp32, s));
     }
-    CmpAttnParams cp{qc, ql, kc, kcl, vc, gate_logits, out, lse, gs, pl.v0,
+    uint16_t *kvc = nullptr;
+    if (!pl.fp32 && pl.n_cch > 0) {
+      kvc = at<uint16_t>(workspace, pl.off_kvc);
+      NSA_LAUNCH("pack_cmp", launch_pack_tiles(kc, vc, 0, pl.n_blk, pl.hkv, pl.n_cch, kvc, pl.d, true, s));
+    }
+    CmpAttnParams cp{qc, ql, kc, kcl, vc, kvc, pl.n_cch, gate_logits, out, lse, gs, pl.v0,
                      (int)pl.n_vis, pl.hq, pl.hkv, pl.n_frames, sl2};
     NSA_LAUNCH("cmp_attn", launch_cmp_attn(cp, pl.d, pl.G, pl.fp32, s));
     TopkParams tp{gs, sel, (int)pl.n_vis, pl.hkv, pl.k};

@@ -18,7 +18,16 @@
 // heaviest (latest frame) first and interleave KV groups so that consecutive
 // workgroup ids -- which land on different XCDs -- keep one group's
 // compressed keys per XCD L2.
+//
+// Staging (bf16 inputs): the compressed keys/values are first packed into
+// PackedTile chunks of 64 blocks, which stream into LDS by direct
+// global->LDS copies: pass 1 (keys only, no global stores in flight) runs a
+// ring of eight chunk slots with explicit vmcnt waits; pass 2 writes the
+// score rows as it goes, so it double-buffers and waits for all of its
+// memory operations before each chunk. fp32 inputs (split operands) keep
+// the synchronous staging.
 #include "nsa_kernels.h"
+#include "nsa_tiles.h"
 
 namespace nsa {
 
@@ -195,11 +204,225 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_kernel(CmpAttnParams p) {
   }
 }
 
+// Pipelined variant for fp16 operands (bf16 inputs); same math as above.
+// The ring slots are separate LDS objects and every step names its slot at
+// compile time: reads of one slot then need not wait for copies still
+// landing in another.
+template <int D, int G>
+__device__ __forceinline__ void cmp_pass1_chunk(const uint16_t *ks, int c, const u16x8 (&qf)[G][D / 32],
+                                                float (&m)[G], float (&l)[G], int nc_t, float sl2, int lane) {
+  const int grp = lane >> 4;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    f32x4 s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = zero4();
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const u16x8 a = pk_k_frag<D>(ks, kt, ds, lane);
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[h] = mfma_f16(a, qf[h][ds], s[h]);
+    }
+    const int b0 = c * kBlk + 16 * kt + 4 * grp;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      f32x4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (b0 + i < nc_t) ? s[h][i] * sl2 : -INFINITY;
+      fold4(m[h], l[h], x);
+    }
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void cmp_pass2_chunk(const uint16_t *ks, const uint16_t *vt, int c,
+                                                const u16x8 (&qf)[G][D / 32], f32x4 (&o)[G][D / 16],
+                                                const float (&lse2)[G], float *gsrow, bool tvalid, int f,
+                                                int nc_t, float sl2, int lane) {
+  const int grp = lane >> 4;
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+    f32x4 s[2][G];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kt = 2 * ks2 + kk;
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[kk][h] = zero4();
+#pragma unroll
+      for (int ds = 0; ds < D / 32; ++ds) {
+        const u16x8 a = pk_k_frag<D>(ks, kt, ds, lane);
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[kk][h] = mfma_f16(a, qf[h][ds], s[kk][h]);
+      }
+      const int b0 = c * kBlk + 16 * kt + 4 * grp;
+      f32x4 gsum = zero4();
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[kk][h][i] = (b0 + i < nc_t) ? __builtin_amdgcn_exp2f(fmaf(s[kk][h][i], sl2, -lse2[h])) : 0.f;
+        gsum += s[kk][h];
+      }
+      if (tvalid) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (b0 + i < f) gsrow[b0 + i] = gsum[i];
+      }
+    }
+    u16x8 pf[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) pf[h] = pack_p(s[0][h], s[1][h]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u16x8 a = pk_v_frag<D>(vt, dt, ks2, lane);
+#pragma unroll
+      for (int h = 0; h < G; ++h) o[h][dt] = mfma_f16(a, pf[h], o[h][dt]);
+    }
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p) {
+  using T = PackedTile<D>;
+  constexpr int KE = T::KE, SE = T::KE + T::VE;
+  constexpr int PK = KE / 512 / 4;  // pieces per wave of a key tile (a value tile alike)
+  static_assert(T::VE == KE, "square tiles");
+  // eight slots of one tile each: pass 1 rings keys through all eight,
+  // pass 2 pairs them (K, V^T) into two double-buffered chunk slots
+  __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
+  __shared__ __attribute__((aligned(16))) uint16_t r4[KE], r5[KE], r6[KE], r7[KE];
+  constexpr int DS = D / 32, DT = D / 16;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int row = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.x % p.hkv;
+  const int f = p.n_frames - 1 - (int)(blockIdx.x / p.hkv);
+  const int t = f * kBlk + wv * 16 + row;  // this lane's query (vision-local)
+  const bool tvalid = t < p.n_vis;
+  const int nc_t = tvalid ? (t + 1) / kBlk : 0;  // complete blocks visible to it
+  const int t_last = min(f * kBlk + kBlk - 1, p.n_vis - 1);
+  const int nk = (t_last + 1) / kBlk;            // blocks any query of the frame sees
+  const int nch = (nk + kBlk - 1) / kBlk;        // packed chunks holding them
+  const uint16_t *cg = p.kvc + (int64_t)g * p.n_cch * SE + wv * PK * 512;
+
+  u16x8 qf[G][DS];
+  {
+    const int64_t q0 = ((p.v0 + (tvalid ? t : 0)) * p.hq + (int64_t)g * G) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) qf[h][ds] = tvalid ? bf2h8(q_frag_global(p.q + q0 + h * D, ds, lane)) : zero8();
+  }
+
+  // ---- pass 1: log-sum-exp of every (query, head); keys only, 8-slot ring
+  // (7 chunks in flight), explicit vmcnt waits (no other memory operations)
+  float m[G], l[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
+#define NSA_ISSUE_K(DST, C) dma_pieces<PK>(cg + (int64_t)(C) * SE, (DST) + wv * PK * 512, lane)
+  // Every step issues exactly PK copies, so "chunk c landed" is always
+  // vmcnt <= 6 * PK (one straight-line wait the compiler's own tracking
+  // follows too). Past the last chunk the copies repeat chunk 0 into slots
+  // that are never read again.
+#define NSA_ISSUE_K_OR_PAD(DST, C) NSA_ISSUE_K(DST, ((C) < nch ? (C) : 0))
+#define NSA_P1_STEP(CUR, NXT)                                             \
+  {                                                                       \
+    wait_vm_c<6 * PK>();                                                  \
+    bare_barrier();                                                       \
+    NSA_ISSUE_K_OR_PAD(NXT, c + 7);                                       \
+    cmp_pass1_chunk<D, G>(CUR, c, qf, m, l, nc_t, p.sl2, lane);           \
+    if (++c >= nch) break;                                                \
+  }
+  if (nch > 0) {
+    NSA_ISSUE_K_OR_PAD(r0, 0);
+    NSA_ISSUE_K_OR_PAD(r1, 1);
+    NSA_ISSUE_K_OR_PAD(r2, 2);
+    NSA_ISSUE_K_OR_PAD(r3, 3);
+    NSA_ISSUE_K_OR_PAD(r4, 4);
+    NSA_ISSUE_K_OR_PAD(r5, 5);
+    NSA_ISSUE_K_OR_PAD(r6, 6);
+  }
+  for (int c = 0; c < nch;) {
+    NSA_P1_STEP(r0, r7)
+    NSA_P1_STEP(r1, r0)
+    NSA_P1_STEP(r2, r1)
+    NSA_P1_STEP(r3, r2)
+    NSA_P1_STEP(r4, r3)
+    NSA_P1_STEP(r5, r4)
+    NSA_P1_STEP(r6, r5)
+    NSA_P1_STEP(r7, r6)
+  }
+#undef NSA_P1_STEP
+#undef NSA_ISSUE_K_OR_PAD
+  float lse2[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float M = grp_max(m[h]);
+    const float part = (m[h] == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - M);
+    const float L = grp_sum(part);
+    lse2[h] = (L > 0.f) ? M + log2f(L) : -INFINITY;
+  }
+  if (tvalid && grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) p.lse[(int64_t)t * p.hq + g * G + h] = lse2[h] * (1.0f / kLog2e);
+  }
+
+  // ---- pass 2: probabilities -> o_cmp and group scores. The score rows are
+  // stored as the loop goes, so each chunk waits for all of this wave's
+  // memory operations (double buffering: chunk c+1 flies during chunk c).
+  f32x4 o[G][DT];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[h][dt] = zero4();
+  float *gsrow = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + (t - f * kBlk)) * f;
+#define NSA_ISSUE_KV(DK, DV, C)                                           \
+  {                                                                       \
+    NSA_ISSUE_K(DK, C);                                                   \
+    dma_pieces<PK>(cg + (int64_t)(C) * SE + KE, (DV) + wv * PK * 512, lane); \
+  }
+  wait_vm_c<0>();  // no copy of pass 1 (padding included) still in flight
+  bare_barrier();  // every wave is done with the pass-1 slots
+  if (nch > 0) NSA_ISSUE_KV(r0, r1, 0);
+#define NSA_P2_STEP(CK, CV, NK, NV)                                       \
+  {                                                                       \
+    wait_vm_c<0>();                                                       \
+    bare_barrier();                                                       \
+    if (c + 1 < nch) NSA_ISSUE_KV(NK, NV, c + 1);                         \
+    cmp_pass2_chunk<D, G>(CK, CV, c, qf, o, lse2, gsrow, tvalid, f, nc_t, p.sl2, lane); \
+    if (++c >= nch) break;                                                \
+  }
+  for (int c = 0; c < nch;) {
+    NSA_P2_STEP(r0, r1, r2, r3)
+    NSA_P2_STEP(r2, r3, r0, r1)
+  }
+#undef NSA_P2_STEP
+#undef NSA_ISSUE_KV
+#undef NSA_ISSUE_K
+
+  // ---- epilogue: out = sigmoid(g_cmp) * o_cmp (first writer of vision rows)
+  if (tvalid) {
+    const int64_t r0w = (p.v0 + t) * p.hq + (int64_t)g * G;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float gate = sigmoidf_(p.gates[(r0w + h) * 3 + 0]);
+      float *dst = p.out + (r0w + h) * D + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[h][dt] * gate;
+    }
+  }
+}
+
 template <int D, int G, bool SPLIT>
 hipError_t run(const CmpAttnParams &p, hipStream_t st) {
   const unsigned nwg = (unsigned)p.n_frames * (unsigned)p.hkv;
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL((cmp_attn_kernel<D, G, SPLIT>), dim3(nwg), dim3(kThreadsH), 0, st, p);
+  if constexpr (SPLIT) {
+    hipLaunchKernelGGL((cmp_attn_kernel<D, G, true>), dim3(nwg), dim3(kThreadsH), 0, st, p);
+  } else {
+    if (!p.kvc && p.n_cch > 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((cmp_attn_dma_kernel<D, G>), dim3(nwg), dim3(kThreadsH), 0, st, p);
+  }
   return hipGetLastError();
 }
 

@@ -27,6 +27,8 @@ struct CmpAttnParams {
   const uint16_t *q, *q_lo;    // [N, Hq, d] bf16; q_lo only for split operands
   const uint16_t *kc, *kc_lo;  // [n_blk, Hkv, d]: fp16, or bf16 hi/lo when split
   const uint16_t *vc;          // [n_blk, Hkv, d] fp16
+  const uint16_t *kvc;         // packed tiles [Hkv][n_cch][K, V^T] (fp16 path), or null
+  int n_cch;                   // chunks of 64 compressed blocks in kvc
   const float *gates;      // [N, Hq, 3]
   float *out;              // [N, Hq, d]
   float *lse;              // [n_vis, Hq]
@@ -98,6 +100,11 @@ hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st);
 // f16: q, k, v hold fp16 (else bf16; values are converted while staging)
 hipError_t launch_swa_attn(const SwaParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st);
+// Packs rows row0 .. row0+n_rows-1 of k, v ([rows][Hkv][d]) into PackedTile
+// blocks [Hkv][n_chunks][K tile, V^T tile]; v_f16: v is fp16 already (else
+// bf16, converted).
+hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
+                             int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st);
 size_t packed_kv_block_elems(int d);  // elements of one packed (K, V^T) block
 hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st);

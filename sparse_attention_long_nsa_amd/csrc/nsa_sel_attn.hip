@@ -27,6 +27,7 @@
 // Every wait is a bounded spin, so a broken protocol ends the kernel with
 // NaN outputs instead of a hang.
 #include "nsa_kernels.h"
+#include "nsa_tiles.h"
 
 namespace nsa {
 
@@ -36,42 +37,6 @@ constexpr int kSelMaxK = 64;
 constexpr int kSelMaxBlk = 8192;
 constexpr int kSpinLimit = 1 << 22;   // s_sleep(1) rounds, about 0.1 s
 constexpr float kRescaleSlack = 8.f;  // log2 units a running max may lag behind
-
-// Swizzled LDS/global layout of one packed block: K tile [64 keys][D] then
-// V^T tile [D dims][64 keys], 16-byte chunks (8 elements) permuted per row.
-// A fragment read by lanes 0..15 (16 consecutive rows, one chunk index)
-// then touches 16 distinct 16-byte bank groups.
-template <int D>
-struct SelTile {
-  static constexpr int KE = kBlk * D, VE = D * kBlk;  // elements
-  // chunk position of logical chunk c in row r of a row of `bytes` bytes
-  template <int BYTES>
-  __host__ __device__ static constexpr int swz(int r, int c) {
-    return BYTES >= 256 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
-  }
-  // V^T rows hold each 32-key half with keys permuted so that lane group j
-  // of the PV fragment finds its eight keys {4j..4j+3, 16+4j..16+4j+3} in
-  // one chunk: stored key slot 8j+i <- key 4j+i (i < 4), 16+4j+i-4 (i >= 4)
-  __host__ __device__ static constexpr int vkey(int slot) {
-    const int h = slot / 32, p = slot % 32, j = p / 8, i = p % 8;
-    return 32 * h + (i < 4 ? 4 * j + i : 16 + 4 * j + (i - 4));
-  }
-};
-
-// A operand of S^T = K Q^T from a staged K tile: keys 16*kt + (l%16), dims
-// 32*ds + 8*(l/16) .. +7.
-template <int D>
-__device__ __forceinline__ u16x8 sel_k_frag(const uint16_t *ks, int kt, int ds, int lane) {
-  const int r = 16 * kt + (lane & 15), c = 4 * ds + (lane >> 4);
-  return *reinterpret_cast<const u16x8 *>(ks + r * D + 8 * SelTile<D>::template swz<2 * D>(r, c));
-}
-// A operand of O^T = V^T P^T from a staged V^T tile: dim 16*dt + (l%16),
-// the eight keys of lane group l/16 in half ks (one swizzled chunk).
-template <int D>
-__device__ __forceinline__ u16x8 sel_v_frag(const uint16_t *vt, int dt, int ks, int lane) {
-  const int r = 16 * dt + (lane & 15), c = 4 * ks + (lane >> 4);
-  return *reinterpret_cast<const u16x8 *>(vt + r * kBlk + 8 * SelTile<D>::template swz<2 * kBlk>(r, c));
-}
 
 template <int D, int G>
 struct SelCfg {
@@ -83,7 +48,7 @@ struct SelCfg {
   static constexpr int NPW = 2;                       // producer waves
   static constexpr int NW = NC + NPW;
   static constexpr int NT = 64 * NW;
-  static constexpr int KE = SelTile<D>::KE, VE = SelTile<D>::VE;
+  static constexpr int KE = PackedTile<D>::KE, VE = PackedTile<D>::VE;
   static constexpr int SE = KE + VE;                  // one slot (elements)
   static constexpr int NP = SE / 512;                 // 1-KB copy pieces per block
   static constexpr int PPP = NP / NPW;                // pieces per producer per block
@@ -92,35 +57,6 @@ struct SelCfg {
   static_assert(NP % NPW == 0 && PPP % 4 == 0, "pieces split evenly, four per address set-up");
   static_assert(TOK <= 32 && NW <= 16, "workgroup shape");
 };
-
-// Waits until at most N vector-memory operations of this wave are in flight
-// (s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, other counters at max).
-template <int N> __device__ __forceinline__ void wait_vm_c() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-// Waits until at most n blocks of PPP copies each are still in flight.
-template <int PPP>
-__device__ __forceinline__ void wait_blocks(int n) {
-  switch (n) {
-    case 0: wait_vm_c<0>(); break;
-    case 1: wait_vm_c<PPP>(); break;
-    case 2: if constexpr (2 * PPP < 64) wait_vm_c<2 * PPP>(); else wait_vm_c<0>(); break;
-    case 3: if constexpr (3 * PPP < 64) wait_vm_c<3 * PPP>(); else wait_vm_c<0>(); break;
-    case 4: if constexpr (4 * PPP < 64) wait_vm_c<4 * PPP>(); else wait_vm_c<0>(); break;
-    case 5: if constexpr (5 * PPP < 64) wait_vm_c<5 * PPP>(); else wait_vm_c<0>(); break;
-    case 6: if constexpr (6 * PPP < 64) wait_vm_c<6 * PPP>(); else wait_vm_c<0>(); break;
-    default: wait_vm_c<0>(); break;
-  }
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-typedef __attribute__((address_space(3))) int lds_int;
-// Uncached LDS accesses of the protocol counters (explicitly in the LDS
-// address space, so they are ds_* instructions and never wait on the copies)
-__device__ __forceinline__ int lds_load(int *p) { return *(volatile lds_int *)(p); }
-__device__ __forceinline__ void lds_store(int *p, int v) { *(volatile lds_int *)(p) = v; }
 
 // Consumes one staged block for one row tile: S^T = K Q^T, causal mask in
 // the own block, lazily rescaled softmax, O^T += V^T P^T.
@@ -134,7 +70,7 @@ __device__ __forceinline__ void sel_tile(const uint16_t *ks, const uint16_t *vt,
   for (int kt = 0; kt < 4; ++kt) {
     s[kt] = zero4();
 #pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) s[kt] = mfma_qk<F16>(sel_k_frag<D>(ks, kt, ds, lane), qf[ds], s[kt]);
+    for (int ds = 0; ds < D / 32; ++ds) s[kt] = mfma_qk<F16>(pk_k_frag<D>(ks, kt, ds, lane), qf[ds], s[kt]);
   }
   if (mask_b >= 0) {  // causal inside the own block
 #pragma unroll
@@ -174,8 +110,8 @@ __device__ __forceinline__ void sel_tile(const uint16_t *ks, const uint16_t *vt,
   const u16x8 pp0 = pack_p(s[0], s[1]), pp1 = pack_p(s[2], s[3]);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
-    o[dt] = mfma_f16(sel_v_frag<D>(vt, dt, 0, lane), pp0, o[dt]);
-    o[dt] = mfma_f16(sel_v_frag<D>(vt, dt, 1, lane), pp1, o[dt]);
+    o[dt] = mfma_f16(pk_v_frag<D>(vt, dt, 0, lane), pp0, o[dt]);
+    o[dt] = mfma_f16(pk_v_frag<D>(vt, dt, 1, lane), pp1, o[dt]);
   }
 }
 
@@ -260,7 +196,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
     // producer pw moves the contiguous pieces [pw*PPP, (pw+1)*PPP) of each
     // block, four per address set-up (immediate offsets of 0..3 KB)
     const int pw = wv - NC;
-    const uint16_t *kvg = p.kv + (int64_t)g * p.n_frames * C::SE + pw * C::PPP * 512 + lane * 8;
+    const uint16_t *kvg = p.kv + (int64_t)g * p.n_frames * C::SE + pw * C::PPP * 512;
     int issued = 0, pub = 0, spins = 0;
     int free_until = R - 1;  // highest block whose slot is known to be free
     int ul = 0;              // ulist[(issued & ~63) + lane]
@@ -279,15 +215,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
           const uint16_t *src = kvg + (int64_t)blk * C::SE;
           uint16_t *dst = ring + (issued % R) * C::SE + pw * C::PPP * 512;
           asm volatile("" ::: "memory");
-#pragma unroll
-          for (int q0 = 0; q0 < C::PPP; q0 += 4) {
-            const uint16_t *s4 = src + q0 * 512;
-            lds_void *d4 = (lds_void *)(dst + q0 * 512);
-            __builtin_amdgcn_global_load_lds(s4, d4, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(s4, d4, 16, 1024, 0);
-            __builtin_amdgcn_global_load_lds(s4, d4, 16, 2048, 0);
-            __builtin_amdgcn_global_load_lds(s4, d4, 16, 3072, 0);
-          }
+          dma_pieces<C::PPP>(src, dst, lane);
           ++issued;
           continue;
         }
@@ -414,7 +342,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
 }
 
 // Packs one KV head's keys and values into the selection kernel's block
-// layout (SelTile): per (head, block) the swizzled K tile (as given: bf16,
+// layout (PackedTile): per (head, block) the swizzled K tile (as given: bf16,
 // or fp16 for fp32 inputs) followed by the swizzled, key-permuted V^T tile
 // in fp16; keys past the sequence are zero.
 template <int D, bool F16>
@@ -422,7 +350,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict
                                                       const uint16_t *__restrict__ v, int64_t v0,
                                                       int n_vis, int hkv, int n_frames,
                                                       uint16_t *__restrict__ kv) {
-  using T = SelTile<D>;
+  using T = PackedTile<D>;
   __shared__ uint16_t tile[kBlk][D + 2];
   const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
   const int tid = threadIdx.x;
@@ -501,17 +429,22 @@ hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream
   return f16 ? dispatch<true>(p, d, G, st) : dispatch<false>(p, d, G, st);
 }
 
-hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st) {
-  const unsigned n = (unsigned)p.n_frames * (unsigned)p.hkv;
+hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
+                             int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st) {
+  const unsigned n = (unsigned)n_chunks * (unsigned)hkv;
   if (n == 0) return hipSuccess;
   if (d == 64) {
-    if (f16) hipLaunchKernelGGL((pack_kv_kernel<64, true>), dim3(n), dim3(256), 0, st, p.k, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.kv);
-    else hipLaunchKernelGGL((pack_kv_kernel<64, false>), dim3(n), dim3(256), 0, st, p.k, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.kv);
+    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<64, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, hkv, n_chunks, out);
+    else hipLaunchKernelGGL((pack_kv_kernel<64, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, hkv, n_chunks, out);
   } else {
-    if (f16) hipLaunchKernelGGL((pack_kv_kernel<128, true>), dim3(n), dim3(256), 0, st, p.k, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.kv);
-    else hipLaunchKernelGGL((pack_kv_kernel<128, false>), dim3(n), dim3(256), 0, st, p.k, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.kv);
+    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<128, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, hkv, n_chunks, out);
+    else hipLaunchKernelGGL((pack_kv_kernel<128, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, hkv, n_chunks, out);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st) {
+  return launch_pack_tiles(p.k, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.kv, d, f16, st);
 }
 
 size_t packed_kv_block_elems(int d) { return (size_t)2 * kBlk * d; }
