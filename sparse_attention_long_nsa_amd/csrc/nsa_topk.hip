@@ -6,9 +6,13 @@
 //
 // One wave per (vision query, KV group). The wave streams the query's row of
 // group scores (frame-packed, written by the compression kernel) once into
-// registers, finds the (k-1)-th largest score exactly by an MSB-first radix
-// select over the fp32 bit patterns (non-negative floats order like their
-// bits), then emits the chosen indices in ascending order with ballots.
+// registers (non-negative floats order like their bit patterns). Fast path:
+// the (k-1)-th largest of the 64 lane maxima is a lower bound T0 for the
+// (k-1)-th largest score (those lane maxima are k-1 distinct scores >= T0),
+// so every score of the answer is >= T0; when at most 64 scores reach T0 the
+// wave ranks just those (score descending, index ascending) and keeps the
+// top k-1. Otherwise it finds the (k-1)-th largest score exactly by an
+// MSB-first radix select. The chosen indices are emitted in ascending order.
 #include "nsa_kernels.h"
 
 namespace nsa {
@@ -41,6 +45,54 @@ __global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
   for (int s = 0; s < NPL; ++s) {
     const int e = s * 64 + lane;
     key[s] = e < f ? __float_as_uint(row[e]) + 1u : 0u;
+  }
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  {
+    // rank of each lane maximum among the 64 (ties: lower lane first)
+    uint32_t lm = 0;
+#pragma unroll
+    for (int s = 0; s < NPL; ++s) lm = max(lm, key[s]);
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+      const uint32_t v = __builtin_amdgcn_readlane(lm, j);
+      rank += (v > lm || (v == lm && j < lane)) ? 1 : 0;
+    }
+    const uint64_t at = __ballot(rank == need - 1);
+    const uint32_t t0 = __builtin_amdgcn_readlane(lm, __ffsll((unsigned long long)at) - 1);
+    int c0 = 0;
+#pragma unroll
+    for (int s = 0; s < NPL; ++s) c0 += __popcll(__ballot(key[s] >= t0));
+    if (c0 <= 64) {
+      // compact the candidates (ascending index order) into LDS
+      int base = 0;
+#pragma unroll
+      for (int s = 0; s < NPL; ++s) {
+        const bool cand = key[s] >= t0;
+        const uint64_t cb = __ballot(cand);
+        if (cand) {
+          const int q = base + __popcll(cb & below);
+          hist[q] = key[s];
+          hist[64 + q] = (uint32_t)(s * 64 + lane);
+        }
+        base += __popcll(cb);
+      }
+      __syncthreads();
+      const uint32_t ck = lane < c0 ? hist[lane] : 0u;
+      const uint32_t ci = lane < c0 ? hist[64 + lane] : 0xffffffffu;
+      // rank among candidates: larger score first, then lower index
+      int r = 0;
+      for (int j = 0; j < c0; ++j) {
+        const uint32_t vk = __builtin_amdgcn_readlane(ck, j);
+        const uint32_t vi = __builtin_amdgcn_readlane(ci, j);
+        r += (vk > ck || (vk == ck && vi < ci)) ? 1 : 0;
+      }
+      const bool take = lane < c0 && r < need;
+      const uint64_t tb = __ballot(take);  // candidates sit in ascending index order
+      if (take) out[__popcll(tb & below)] = (int32_t)ci;
+      if (lane == 0) out[need] = f;  // own block, larger than every candidate
+      return;
+    }
   }
 
   uint32_t prefix = 0, pmask = 0;
@@ -86,7 +138,6 @@ __global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
 
   // keys > prefix are all kept; of the keys == prefix keep the `rem` lowest indices
   int pos = 0, eq_taken = 0;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int s = 0; s < NPL; ++s) {
     const bool gt = key[s] > prefix;
