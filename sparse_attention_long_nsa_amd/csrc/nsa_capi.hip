@@ -25,10 +25,10 @@ struct PrefillPlan {
   int n_blk = 0, n_frames = 0, n_cch = 0;
   bool fp32 = false;
   float scale = 0.f;
-  int n_split = 0, split_len = 0, text_tiles = 0;
+  int n_split = 0, chunks_per_split = 0, text_tiles = 0, n_tchunks = 0;
   size_t off_kc = 0, off_vc = 0, off_kcl = 0, off_qh = 0, off_ql = 0, off_q16 = 0, off_k16 = 0,
          off_v16 = 0;
-  size_t off_kvc = 0, off_vt = 0, off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0, total = 0;
+  size_t off_kvc = 0, off_kvt = 0, off_vt = 0, off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0, total = 0;
 };
 
 nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, PrefillPlan &pl) {
@@ -70,17 +70,19 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
   pl.n_frames = (int)((pl.n_vis + kBlk - 1) / kBlk);
   if (pl.n_frames > kMaxBlocks) return NSA_ERR_UNSUPPORTED;
 
-  // text split-K: enough (tile, group, split) workgroups to fill the chip
+  // text split-K over the packed key chunks (vision blocks, then text
+  // rows): enough (tile, group, split) workgroups to fill the chip
   pl.text_tiles = (int)((pl.n_text + kBlk - 1) / kBlk);
+  pl.n_tchunks = pl.text_tiles;
   if (pl.n_text > 0) {
     const int64_t want = 1024;
+    const int64_t nch = (int64_t)pl.n_frames + pl.n_tchunks;
     int64_t ns = want / ((int64_t)pl.text_tiles * pl.hkv);
     if (ns < 1) ns = 1;
-    int64_t len = (pl.N + ns - 1) / ns;
-    len = (len + kBlk - 1) / kBlk * kBlk;
-    if (len < 4 * kBlk) len = 4 * kBlk;
-    pl.split_len = (int)len;
-    pl.n_split = (int)((pl.N + len - 1) / len);
+    int64_t cps = (nch + ns - 1) / ns;
+    if (cps < 4) cps = 4;
+    pl.chunks_per_split = (int)cps;
+    pl.n_split = (int)((nch + cps - 1) / cps);
   }
 
   const size_t H = (size_t)pl.hq, Hk = (size_t)pl.hkv, D = (size_t)pl.d;
@@ -99,7 +101,9 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
   // packed compressed key/value chunks of the compression branch (fp16 path)
   pl.n_cch = (pl.n_blk + kBlk - 1) / kBlk;
   if (!pl.fp32) pl.off_kvc = take(sizeof(uint16_t) * (size_t)pl.n_cch * Hk * packed_kv_block_elems(pl.d));
-  // packed key/value blocks of the selection kernel: [Hkv][n_frames][K tile, V^T tile]
+  // packed text rows of the text branch: [Hkv][n_tchunks][K tile, V^T tile]
+  if (pl.n_text > 0) pl.off_kvt = take(sizeof(uint16_t) * (size_t)pl.n_tchunks * Hk * packed_kv_block_elems(pl.d));
+  // packed vision blocks (window, selection and text branches): [Hkv][n_frames][K tile, V^T tile]
   pl.off_vt = take(sizeof(uint16_t) * (size_t)pl.n_frames * Hk * packed_kv_block_elems(pl.d));
   pl.off_lse = take(sizeof(float) * pl.n_vis * H);
   pl.off_gs = take(sizeof(float) * (size_t)frame_off(pl.n_frames, pl.hkv));
@@ -221,18 +225,22 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
     NSA_LAUNCH("cmp_attn", launch_cmp_attn(cp, pl.d, pl.G, pl.fp32, s));
     TopkParams tp{gs, sel, (int)pl.n_vis, pl.hkv, pl.k};
     NSA_LAUNCH("blk_score_topk", launch_topk(tp, pl.n_frames, s));
-    SwaParams wp{qb, kb, vb, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.w,
-                 pl.n_frames, sl2};
-    NSA_LAUNCH("swa_attn", launch_swa_attn(wp, pl.d, pl.G, pl.fp32, s));
     SelParams sp{qb, kb, vb, at<uint16_t>(workspace, pl.off_vt), sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
                  pl.n_frames, sl2};
     NSA_LAUNCH("pack_kv", launch_pack_kv(sp, pl.d, pl.fp32, s));
+    SwaParams wp{qb, at<uint16_t>(workspace, pl.off_vt), gate_logits, out, pl.v0, (int)pl.n_vis,
+                 pl.hq, pl.hkv, pl.w, pl.n_frames, sl2};
+    NSA_LAUNCH("swa_attn", launch_swa_attn(wp, pl.d, pl.G, pl.fp32, s));
     NSA_LAUNCH("sel_attn", launch_sel_attn(sp, pl.d, pl.G, pl.fp32, s));
   }
   if (pl.n_text > 0) {
-    TextParams tp{qb, kb, vb, at<float>(workspace, pl.off_po), at<float2>(workspace, pl.off_pml),
-                  out, pl.v0, pl.v1, pl.N, (int)pl.n_text, pl.hq, pl.hkv, pl.n_split,
-                  pl.split_len, pl.text_tiles, sl2};
+    uint16_t *kvt = at<uint16_t>(workspace, pl.off_kvt);
+    NSA_LAUNCH("pack_text", launch_pack_tiles(kb, vb, 0, (int)pl.n_text, pl.hkv, pl.n_tchunks, kvt,
+                                              pl.d, pl.fp32, s, (int)pl.v0, pl.v1 - pl.v0));
+    TextParams tp{qb, at<uint16_t>(workspace, pl.off_vt), kvt, at<float>(workspace, pl.off_po),
+                  at<float2>(workspace, pl.off_pml), out, pl.v0, pl.v1, pl.N, (int)pl.n_text,
+                  pl.hq, pl.hkv, pl.n_split, pl.chunks_per_split, pl.text_tiles,
+                  (int)(pl.n_vis > 0 ? pl.n_frames : 0), pl.n_tchunks, sl2};
     NSA_LAUNCH("text_attn", launch_text_attn(tp, pl.d, pl.G, pl.fp32, s));
     NSA_LAUNCH("text_merge", launch_text_merge(tp, pl.d, s));
   }

@@ -303,7 +303,8 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
   const int t_last = min(f * kBlk + kBlk - 1, p.n_vis - 1);
   const int nk = (t_last + 1) / kBlk;            // blocks any query of the frame sees
   const int nch = (nk + kBlk - 1) / kBlk;        // packed chunks holding them
-  const uint16_t *cg = p.kvc + (int64_t)g * p.n_cch * SE + wv * PK * 512;
+  const int off = __builtin_amdgcn_readfirstlane(wv * PK * 512);  // wave-uniform, scalar
+  const uint16_t *cg = p.kvc + (int64_t)g * p.n_cch * SE + off;
 
   u16x8 qf[G][DS];
   {
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
   float m[G], l[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
-#define NSA_ISSUE_K(DST, C) dma_pieces<PK>(cg + (int64_t)(C) * SE, (DST) + wv * PK * 512, lane)
+#define NSA_ISSUE_K(DST, C) dma_pieces<PK>(cg + (int64_t)(C) * SE, (DST) + off, lane)
   // Every step issues exactly PK copies, so "chunk c landed" is always
   // vmcnt <= 6 * PK (one straight-line wait the compiler's own tracking
   // follows too). Past the last chunk the copies repeat chunk 0 into slots
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
 #define NSA_ISSUE_KV(DK, DV, C)                                           \
   {                                                                       \
     NSA_ISSUE_K(DK, C);                                                   \
-    dma_pieces<PK>(cg + (int64_t)(C) * SE + KE, (DV) + wv * PK * 512, lane); \
+    dma_pieces<PK>(cg + (int64_t)(C) * SE + KE, (DV) + off, lane);        \
   }
   wait_vm_c<0>();  // no copy of pass 1 (padding included) still in flight
   bare_barrier();  // every wave is done with the pass-1 slots

@@ -4,40 +4,20 @@
 // standard GQA).
 //
 // Layout H: a wave owns 16 queries and all G query heads of one KV group, so
-// each K / V^T fragment read from LDS feeds G matrix-core ops.
+// each K / V^T fragment read from LDS feeds G matrix-core ops. Keys and
+// values come from the packed block tiles (PackedTile, one 64-key chunk per
+// tile) by direct global->LDS copies, issued several chunks ahead.
 #include "nsa_kernels.h"
+#include "nsa_tiles.h"
 
 namespace nsa {
 
 namespace {
 
-// ---------------------------------------------------------------- layout H
-// Two passes over the keys: pass 1 accumulates each row's (max, sum) to get
-// its exact log-sum-exp; pass 2 forms normalised probabilities and runs the
-// PV product. No accumulator is ever rescaled, so the G heads' accumulators
-// stay in the matrix-core register file.
 constexpr int kThreadsH = 256;  // 4 waves x 16 queries
-
-__device__ __forceinline__ void fold4(float &m, float &l, const f32x4 x) {
-  const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  const float mn = fmaxf(m, mx);
-  if (mn == -INFINITY) return;
-  l = l * exp2f(m - mn) + exp2f(x[0] - mn) + exp2f(x[1] - mn) + exp2f(x[2] - mn) + exp2f(x[3] - mn);
-  m = mn;
-}
-
-template <int D, int G, bool F16>
-__device__ __forceinline__ void qk16(f32x4 (&s)[G], const uint16_t *ks, int kt,
-                                     const u16x8 (&qf)[G][D / 32], int lane) {
-#pragma unroll
-  for (int h = 0; h < G; ++h) s[h] = zero4();
-#pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds) {
-    const u16x8 a = k_frag<D>(ks, kt, ds, lane);
-#pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = mfma_qk<F16>(a, qf[h][ds], s[h]);
-  }
-}
+// a row's running max only moves when a new max exceeds it by this many
+// log2 units; probabilities stay below 2^slack
+constexpr float kSlack = 8.f;
 
 template <int D, int G>
 __device__ __forceinline__ void load_q_h(u16x8 (&qf)[G][D / 32], const uint16_t *q, int64_t row0,
@@ -49,43 +29,141 @@ __device__ __forceinline__ void load_q_h(u16x8 (&qf)[G][D / 32], const uint16_t 
       qf[h][ds] = valid ? q_frag_global(q + (row0 + h) * D, ds, lane) : zero8();
 }
 
-// Attends this lane's query row (all G heads) over n_chunks staged chunks.
-// chunk(c, key0, src, nvalid) gives chunk c's first key index, source row
-// pointer and number of rows present; valid(key) masks keys per row.
-// Returns o normalised by the row sum and the row lse (log2 units).
-template <int D, int G, bool F16, class Chunk, class Valid>
-__device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G], uint16_t *ks,
-                                         uint16_t *vt, const u16x8 (&qf)[G][D / 32], float sl2,
-                                         int n_chunks, int64_t kv_stride, Chunk chunk, Valid valid) {
-  const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4;
+template <int D, int G, bool F16>
+__device__ __forceinline__ void qk16(f32x4 (&s)[G], const uint16_t *ks, int kt,
+                                     const u16x8 (&qf)[G][D / 32], int lane) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) s[h] = zero4();
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) {
+    const u16x8 a = pk_k_frag<D>(ks, kt, ds, lane);
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = mfma_qk<F16>(a, qf[h][ds], s[h]);
+  }
+}
+
+// Pass 1 on one staged key chunk: lane-partial (max, sum) of the scaled
+// logits in log2 units, with the lazily moved max. Keys klo..khi of the
+// chunk (shifted by this lane's 4*(l/16)) are valid for the lane's row.
+template <int D, int G, bool F16>
+__device__ __forceinline__ void pass1_chunk(const uint16_t *ks, const u16x8 (&qf)[G][D / 32],
+                                            float (&m)[G], float (&l)[G], float sl2, int lane,
+                                            int klo, int khi) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    f32x4 s[G];
+    qk16<D, G, F16>(s, ks, kt, qf, lane);
+    const int b = 16 * kt;
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok[i] = b + i >= klo && b + i <= khi;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      f32x4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = ok[i] ? s[h][i] * sl2 : -INFINITY;
+      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(mx > m[h] + kSlack)) {
+        const float mn = fmaxf(m[h], mx);
+        l[h] = (mn == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - mn);
+        m[h] = mn;
+      }
+      const float base = (m[h] == -INFINITY) ? 0.f : m[h];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l[h] += __builtin_amdgcn_exp2f(x[i] - base);
+    }
+  }
+}
+
+// Pass 2 on one staged chunk: exact probabilities (row lse known) and the
+// PV product. Keys klo..khi of the chunk (shifted by this lane's 4*(l/16))
+// are valid for the lane's row.
+template <int D, int G, bool F16>
+__device__ __forceinline__ void pass2_chunk(const uint16_t *ks, const uint16_t *vt,
+                                            const u16x8 (&qf)[G][D / 32], f32x4 (&o)[G][D / 16],
+                                            const float (&lse2)[G], float sl2, int lane, int klo,
+                                            int khi) {
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+    f32x4 s[2][G];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kt = 2 * ks2 + kk;
+      qk16<D, G, F16>(s[kk], ks, kt, qf, lane);
+      const int b = 16 * kt;
+      bool ok[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ok[i] = b + i >= klo && b + i <= khi;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[kk][h][i] = ok[i] ? __builtin_amdgcn_exp2f(fmaf(s[kk][h][i], sl2, -lse2[h])) : 0.f;
+    }
+    u16x8 pf[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) pf[h] = pack_p(s[0][h], s[1][h]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u16x8 a = pk_v_frag<D>(vt, dt, ks2, lane);
+#pragma unroll
+      for (int h = 0; h < G; ++h) o[h][dt] = mfma_f16(a, pf[h], o[h][dt]);
+    }
+  }
+}
+
+// Two passes of this lane's query row (all G heads) over n_chunks packed
+// chunks: pass 1 gets the exact log-sum-exp, pass 2 forms normalised
+// probabilities for the PV product, so no accumulator is ever rescaled and
+// the G heads' accumulators stay in the matrix-core register file.
+// tile_at(c) is chunk c's packed tile; key_range(c, lo, hi) gives the keys
+// lo..hi (inclusive, empty if lo > hi) of chunk c valid for this lane's row.
+// Returns o normalised and the lse (log2 units).
+//
+// Copies: pass 1 rings key tiles through eight LDS slots (seven chunks in
+// flight), pass 2 rings (K, V^T) pairs through four (three in flight). Each
+// ring step issues exactly one chunk's copies -- past the last chunk they
+// repeat chunk 0 into slots that are never read -- so "chunk c landed" is a
+// single straight-line vmcnt wait; the slots are separate LDS objects named
+// at compile time, so the compiler adds no waits of its own.
+template <int D, int G, bool F16, class TileAt, class KeyRange>
+__device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G],
+                                         const u16x8 (&qf)[G][D / 32], float sl2, int n_chunks,
+                                         TileAt tile_at, KeyRange key_range) {
+  using T = PackedTile<D>;
+  constexpr int KE = T::KE;
+  constexpr int PK = KE / 512 / 4;  // copies per wave of one tile
+  __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
+  __shared__ __attribute__((aligned(16))) uint16_t r4[KE], r5[KE], r6[KE], r7[KE];
+  const int lane = threadIdx.x & 63, g4 = 4 * (lane >> 4);
+  // wave-uniform copy offsets kept in scalar registers
+  const int off = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) * PK * 512);
+
   float m[G], l[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
-  for (int c = 0; c < n_chunks; ++c) {
-    int key0;
-    const uint16_t *ksrc, *vsrc;
-    int nvalid;
-    chunk(c, key0, ksrc, vsrc, nvalid);
-    __syncthreads();
-    stage_k<D>(ks, ksrc, kv_stride, nvalid, tid, kThreadsH);
-    __syncthreads();
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f32x4 s[G];
-      qk16<D, G, F16>(s, ks, kt, qf, lane);
-      const int kb = key0 + 16 * kt + 4 * grp;
-      bool ok[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ok[i] = valid(kb + i);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        f32x4 x;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = ok[i] ? s[h][i] * sl2 : -INFINITY;
-        fold4(m[h], l[h], x);
-      }
-    }
+#define NSA_K(DST, C) dma_pieces<PK>(tile_at((C) < n_chunks ? (C) : 0) + off, (DST) + off, lane)
+#define NSA_P1(CUR, NXT)                                                  \
+  {                                                                       \
+    wait_vm_c<6 * PK>();                                                  \
+    bare_barrier();                                                       \
+    NSA_K(NXT, c + 7);                                                    \
+    {                                                                     \
+      int lo_, hi_;                                                       \
+      key_range(c, lo_, hi_);                                             \
+      pass1_chunk<D, G, F16>(CUR, qf, m, l, sl2, lane, lo_ - g4, hi_ - g4); \
+    }                                                                     \
+    if (++c >= n_chunks) break;                                           \
   }
+  if (n_chunks > 0) {
+    NSA_K(r0, 0); NSA_K(r1, 1); NSA_K(r2, 2); NSA_K(r3, 3);
+    NSA_K(r4, 4); NSA_K(r5, 5); NSA_K(r6, 6);
+  }
+  for (int c = 0; c < n_chunks;) {
+    NSA_P1(r0, r7) NSA_P1(r1, r0) NSA_P1(r2, r1) NSA_P1(r3, r2)
+    NSA_P1(r4, r3) NSA_P1(r5, r4) NSA_P1(r6, r5) NSA_P1(r7, r6)
+  }
+#undef NSA_P1
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float M = grp_max(m[h]);
@@ -95,60 +173,50 @@ __device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G]
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[h][dt] = zero4();
   }
-  for (int c = 0; c < n_chunks; ++c) {
-    int key0;
-    const uint16_t *ksrc, *vsrc;
-    int nvalid;
-    chunk(c, key0, ksrc, vsrc, nvalid);
-    __syncthreads();
-    stage_k<D>(ks, ksrc, kv_stride, nvalid, tid, kThreadsH);
-    stage_vt<D, !F16>(vt, vsrc, kv_stride, nvalid, tid, kThreadsH);
-    __syncthreads();
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      f32x4 s[2][G];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int kt = 2 * ks2 + kk;
-        qk16<D, G, F16>(s[kk], ks, kt, qf, lane);
-        const int kb = key0 + 16 * kt + 4 * grp;
-        bool ok[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ok[i] = valid(kb + i);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[kk][h][i] = ok[i] ? exp2f(s[kk][h][i] * sl2 - lse2[h]) : 0.f;
-      }
-      u16x8 pf[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pf[h] = pack_p(s[0][h], s[1][h]);
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const u16x8 a = v_frag<D>(vt, dt, ks2, lane);
-#pragma unroll
-        for (int h = 0; h < G; ++h) o[h][dt] = mfma_f16(a, pf[h], o[h][dt]);
-      }
-    }
+
+  wait_vm_c<0>();  // no pass-1 copy (padding included) still in flight
+  bare_barrier();  // every wave is done with the pass-1 slots
+#define NSA_KV(DK, DV, C)                                                             \
+  {                                                                                   \
+    const uint16_t *src_ = tile_at((C) < n_chunks ? (C) : 0);                         \
+    dma_pieces<PK>(src_ + off, (DK) + off, lane);                                     \
+    dma_pieces<PK>(src_ + KE + off, (DV) + off, lane);                                \
   }
+#define NSA_P2(CK, CV, NK, NV)                                            \
+  {                                                                       \
+    wait_vm_c<4 * PK>();                                                  \
+    bare_barrier();                                                       \
+    NSA_KV(NK, NV, c + 3);                                                \
+    {                                                                     \
+      int lo_, hi_;                                                       \
+      key_range(c, lo_, hi_);                                             \
+      pass2_chunk<D, G, F16>(CK, CV, qf, o, lse2, sl2, lane, lo_ - g4, hi_ - g4); \
+    }                                                                     \
+    if (++c >= n_chunks) break;                                           \
+  }
+  if (n_chunks > 0) { NSA_KV(r0, r1, 0); NSA_KV(r2, r3, 1); NSA_KV(r4, r5, 2); }
+  for (int c = 0; c < n_chunks;) {
+    NSA_P2(r0, r1, r6, r7) NSA_P2(r2, r3, r0, r1) NSA_P2(r4, r5, r2, r3) NSA_P2(r6, r7, r4, r5)
+  }
+#undef NSA_P2
+#undef NSA_KV
+#undef NSA_K
+  wait_vm_c<0>();  // padding copies land before the workgroup's LDS is reused
 }
 
 // ----------------------------------------------------------- sliding window
-// Chunks start at the tile's first window key (not 64-aligned): a 64-query
-// tile needs keys [t0 - w + 1, t0 + 63], i.e. ceil((w + 63) / 64) chunks.
+// A 64-query tile (vision frame f) needs keys [t0 - w + 1, t0 + 63], i.e.
+// the packed blocks from (t0 - w + 1) / 64 to f.
 template <int D, int G, bool F16>
 __global__ __launch_bounds__(kThreadsH) void swa_attn_kernel(SwaParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[Tile<D>::kElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[Tile<D>::vElems];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4;
+  using T = PackedTile<D>;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4;
   const int g = blockIdx.x % p.hkv;
-  const int tile = (int)(blockIdx.x / p.hkv);
-  const int t0 = tile * kBlk;
+  const int f = p.n_tiles - 1 - (int)(blockIdx.x / p.hkv);  // heaviest first
+  const int t0 = f * kBlk;
   const int t = t0 + wv * 16 + (lane & 15);
   const bool tvalid = t < p.n_vis;
-  const int lo = max(0, t0 - p.window + 1);
-  const int hi = min(t0 + kBlk - 1, p.n_vis - 1);
-  const int64_t kvs = (int64_t)p.hkv * D;
+  const int b_lo = max(0, t0 - p.window + 1) / kBlk;
   const int wnd = p.window;
 
   u16x8 qf[G][D / 32];
@@ -156,16 +224,14 @@ __global__ __launch_bounds__(kThreadsH) void swa_attn_kernel(SwaParams p) {
   load_q_h<D, G>(qf, p.q, qrow, tvalid, lane);
   f32x4 o[G][D / 16];
   float lse2[G];
-  const uint16_t *kbase = p.k + (p.v0 * p.hkv + g) * (int64_t)D;
-  const uint16_t *vbase = p.v + (p.v0 * p.hkv + g) * (int64_t)D;
-  two_pass<D, G, F16>(o, lse2, ks, vt, qf, p.sl2, (hi - lo + kBlk) / kBlk, kvs,
-                 [&](int c, int &key0, const uint16_t *&ksrc, const uint16_t *&vsrc, int &nvalid) {
-                   key0 = lo + c * kBlk;
-                   ksrc = kbase + (int64_t)key0 * kvs;
-                   vsrc = vbase + (int64_t)key0 * kvs;
-                   nvalid = min(kBlk, hi + 1 - key0);
-                 },
-                 [&](int j) { return tvalid && j <= t && j > t - wnd; });
+  const uint16_t *tiles = p.kv + ((int64_t)g * p.n_tiles + b_lo) * (T::KE + T::VE);
+  two_pass<D, G, F16>(o, lse2, qf, p.sl2, f - b_lo + 1,
+                      [&](int c) { return tiles + (int64_t)c * (T::KE + T::VE); },
+                      [&](int c, int &lo, int &hi) {
+                        const int key0 = (b_lo + c) * kBlk;  // keys t-w+1 .. t
+                        lo = t - wnd + 1 - key0;
+                        hi = tvalid ? t - key0 : -1;
+                      });
   if (tvalid) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -185,41 +251,48 @@ __device__ __forceinline__ int64_t text_pos(int r, int64_t v0, int64_t v1) {
   return r < v0 ? (int64_t)r : v1 + (r - v0);
 }
 
-// One (64-query tile, KV group, key split) per workgroup; writes the split's
-// normalised output and lse for the merge kernel.
+// One (64-query text tile, KV group, key split) per workgroup. The keys of
+// the whole sequence are the packed vision chunks followed by the packed
+// text chunks; split sp takes chunks [sp * cps, (sp + 1) * cps). Writes the
+// split's normalised output and lse for the merge kernel.
 template <int D, int G, bool F16>
 __global__ __launch_bounds__(kThreadsH) void text_attn_kernel(TextParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[Tile<D>::kElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[Tile<D>::vElems];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4;
+  using T = PackedTile<D>;
+  constexpr int SE = T::KE + T::VE;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4;
   const int sp = blockIdx.x % p.n_split;
   const int rest = blockIdx.x / p.n_split;
   const int g = rest % p.hkv;
   const int tile = rest / p.hkv;
   const int r = tile * kBlk + wv * 16 + (lane & 15);
   const bool rvalid = r < p.n_text;
-  const int pos = rvalid ? (int)text_pos(r, p.v0, p.v1) : -1;
-  const int pos_last = (int)text_pos(min(tile * kBlk + kBlk - 1, p.n_text - 1), p.v0, p.v1);
-  const int kb = sp * p.split_len;
-  const int ke = min(kb + p.split_len, pos_last + 1);
-  const int64_t kvs = (int64_t)p.hkv * D;
+  const int64_t pos = rvalid ? text_pos(r, p.v0, p.v1) : -1;
+  const int nvc = p.n_vchunks, nch = p.n_vchunks + p.n_tchunks;
+  const int cb = sp * p.chunks_per_split, ce = min(cb + p.chunks_per_split, nch);
+  const int64_t n_vis = p.v1 - p.v0;
 
   u16x8 qf[G][D / 32];
-  const int64_t qrow = (int64_t)(rvalid ? pos : 0) * p.hq + (int64_t)g * G;
+  const int64_t qrow = (rvalid ? pos : 0) * p.hq + (int64_t)g * G;
   load_q_h<D, G>(qf, p.q, qrow, rvalid, lane);
   f32x4 o[G][D / 16];
   float lse2[G];
-  const int n_chunks = ke > kb ? (ke - kb + kBlk - 1) / kBlk : 0;
-  const uint16_t *kbase = p.k + (int64_t)g * D;
-  const uint16_t *vbase = p.v + (int64_t)g * D;
-  two_pass<D, G, F16>(o, lse2, ks, vt, qf, p.sl2, n_chunks, kvs,
-                 [&](int c, int &key0, const uint16_t *&ksrc, const uint16_t *&vsrc, int &nvalid) {
-                   key0 = kb + c * kBlk;
-                   ksrc = kbase + (int64_t)key0 * kvs;
-                   vsrc = vbase + (int64_t)key0 * kvs;
-                   nvalid = min(kBlk, ke - key0);
-                 },
-                 [&](int j) { return rvalid && j <= pos; });
+  const uint16_t *vis = p.kv_vis + (int64_t)g * p.n_vchunks * SE;
+  const uint16_t *txt = p.kv_txt + (int64_t)g * p.n_tchunks * SE;
+  two_pass<D, G, F16>(o, lse2, qf, p.sl2, max(0, ce - cb),
+                      [&](int c) {
+                        const int cc = cb + c;
+                        return cc < nvc ? vis + (int64_t)cc * SE : txt + (int64_t)(cc - nvc) * SE;
+                      },
+                      [&](int c, int &lo, int &hi) {
+                        const int cc = cb + c;
+                        lo = 0;
+                        if (cc < nvc) {  // vision-local keys j: j < n_vis, v0 + j <= pos
+                          const int key0 = cc * kBlk;
+                          hi = (int)min((int64_t)n_vis - 1, pos - p.v0) - key0;
+                        } else {  // text-local keys j: positions increase with j, so j <= r
+                          hi = (rvalid ? r : -1) - (cc - nvc) * kBlk;
+                        }
+                      });
   if (rvalid) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {

@@ -45,7 +45,8 @@ struct TopkParams {
 };
 
 struct SwaParams {
-  const uint16_t *q, *k, *v;   // [N, H, d]: all bf16, or all fp16
+  const uint16_t *q;           // [N, Hq, d]: bf16, or fp16
+  const uint16_t *kv;          // packed vision blocks [Hkv][n_tiles][K, V^T]
   const float *gates;
   float *out;
   int64_t v0;
@@ -65,12 +66,14 @@ struct SelParams {
 };
 
 struct TextParams {
-  const uint16_t *q, *k, *v;
+  const uint16_t *q;       // [N, Hq, d]
+  const uint16_t *kv_vis;  // packed vision blocks [Hkv][n_vchunks][K, V^T]
+  const uint16_t *kv_txt;  // packed text rows [Hkv][n_tchunks][K, V^T]
   float *part_o;           // [n_split, n_text, Hq, d]
-  float2 *part_ml;         // [n_split, n_text, Hq] (max in log2 units, sum)
+  float2 *part_ml;         // [n_split, n_text, Hq] (lse in log2 units, unused)
   float *out;              // merge target [N, Hq, d]
   int64_t v0, v1, n_tokens;
-  int n_text, hq, hkv, n_split, split_len, n_tiles;
+  int n_text, hq, hkv, n_split, chunks_per_split, n_tiles, n_vchunks, n_tchunks;
   float sl2;
 };
 
@@ -100,11 +103,13 @@ hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st);
 // f16: q, k, v hold fp16 (else bf16; values are converted while staging)
 hipError_t launch_swa_attn(const SwaParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st);
-// Packs rows row0 .. row0+n_rows-1 of k, v ([rows][Hkv][d]) into PackedTile
-// blocks [Hkv][n_chunks][K tile, V^T tile]; v_f16: v is fp16 already (else
-// bf16, converted).
+// Packs n_rows rows of k, v ([rows][Hkv][d]) into PackedTile blocks
+// [Hkv][n_chunks][K tile, V^T tile]: packed row i is source row row0 + i,
+// plus `jump` for i >= split_at; v_f16: v is fp16 already (else bf16,
+// converted).
 hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
-                             int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st);
+                             int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st,
+                             int split_at = 0x7fffffff, int64_t jump = 0);
 size_t packed_kv_block_elems(int d);  // elements of one packed (K, V^T) block
 hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st);

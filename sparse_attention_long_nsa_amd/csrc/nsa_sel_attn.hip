@@ -195,7 +195,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
     // ---------------------------------------------------------- producer
     // producer pw moves the contiguous pieces [pw*PPP, (pw+1)*PPP) of each
     // block, four per address set-up (immediate offsets of 0..3 KB)
-    const int pw = wv - NC;
+    const int pw = __builtin_amdgcn_readfirstlane(wv - NC);
     const uint16_t *kvg = p.kv + (int64_t)g * p.n_frames * C::SE + pw * C::PPP * 512;
     int issued = 0, pub = 0, spins = 0;
     int free_until = R - 1;  // highest block whose slot is known to be free
@@ -341,15 +341,16 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   }
 }
 
-// Packs one KV head's keys and values into the selection kernel's block
-// layout (PackedTile): per (head, block) the swizzled K tile (as given: bf16,
-// or fp16 for fp32 inputs) followed by the swizzled, key-permuted V^T tile
-// in fp16; keys past the sequence are zero.
+// Packs one KV head's keys and values into the block layout (PackedTile):
+// per (head, block) the swizzled K tile (as given: bf16, or fp16 for fp32
+// inputs) followed by the swizzled, key-permuted V^T tile in fp16; rows past
+// n_vis are zero. Packed row t reads source row v0 + t, plus `jump` from
+// row split_at on (to skip a run of rows, e.g. the vision run for text).
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v, int64_t v0,
-                                                      int n_vis, int hkv, int n_frames,
-                                                      uint16_t *__restrict__ kv) {
+                                                      int n_vis, int split_at, int64_t jump, int hkv,
+                                                      int n_frames, uint16_t *__restrict__ kv) {
   using T = PackedTile<D>;
   __shared__ uint16_t tile[kBlk][D + 2];
   const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict
     const int r = idx / (D / 8), c = idx % (D / 8);
     const int t = b * kBlk + r;
     u16x8 val = zero8();
-    if (t < n_vis) val = *reinterpret_cast<const u16x8 *>(k + ((v0 + t) * hkv + g) * (int64_t)D + 8 * c);
+    if (t < n_vis) val = *reinterpret_cast<const u16x8 *>(k + ((v0 + t + (t >= split_at ? jump : 0)) * hkv + g) * (int64_t)D + 8 * c);
     *reinterpret_cast<u16x8 *>(dst + r * D + 8 * T::template swz<2 * D>(r, c)) = val;
   }
   for (int idx = tid; idx < kBlk * D; idx += 256) {
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict
     const int t = b * kBlk + key;
     uint16_t x = 0;
     if (t < n_vis) {
-      x = v[((v0 + t) * hkv + g) * (int64_t)D + d];
+      x = v[((v0 + t + (t >= split_at ? jump : 0)) * hkv + g) * (int64_t)D + d];
       if (!F16) x = bf2h_bits(x);
     }
     tile[key][d] = x;
@@ -430,15 +431,16 @@ hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream
 }
 
 hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
-                             int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st) {
+                             int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st,
+                             int split_at, int64_t jump) {
   const unsigned n = (unsigned)n_chunks * (unsigned)hkv;
   if (n == 0) return hipSuccess;
   if (d == 64) {
-    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<64, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, hkv, n_chunks, out);
-    else hipLaunchKernelGGL((pack_kv_kernel<64, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, hkv, n_chunks, out);
+    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<64, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out);
+    else hipLaunchKernelGGL((pack_kv_kernel<64, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out);
   } else {
-    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<128, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, hkv, n_chunks, out);
-    else hipLaunchKernelGGL((pack_kv_kernel<128, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, hkv, n_chunks, out);
+    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<128, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out);
+    else hipLaunchKernelGGL((pack_kv_kernel<128, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out);
   }
   return hipGetLastError();
 }
