@@ -54,6 +54,8 @@ def closed_form_work(shape, n_text_positions):
         "blk_score_topk": ("bytes", 4.0 * hkv * float(cur.sum()) + 4.0 * s.n_vis * hkv * k),
         "swa_attn": ("flops", f4 * float(n_swa.sum())),
         "pack_kv": ("bytes", 4.0 * s.n_vis * hkv * d + 2.0 * n_frames * hkv * kv_block),
+        "pack_cmp": ("bytes", 4.0 * n_blk * hkv * d + 2.0 * (-(-n_blk // B)) * hkv * kv_block),
+        "pack_text": ("bytes", 4.0 * len(text_keys) * hkv * d + 2.0 * (-(-len(text_keys) // B)) * hkv * kv_block),
         "sel_attn": ("flops", f4 * float(n_sel.sum())),
         "text_attn": ("flops", f4 * float(text_keys.sum())),
     }
@@ -206,9 +208,9 @@ def main():
     def ms_of(*names):
         return round(sum(kern.get(n, (0.0, 0))[0] for n in names), 4)
 
-    branch_ms = {"cmp": ms_of("cmp_pool", "cmp_attn"),
+    branch_ms = {"cmp": ms_of("cmp_pool", "pack_cmp", "cmp_attn"),
                  "sel": ms_of("blk_score_topk", "pack_kv", "sel_attn"),
-                 "swa": ms_of("swa_attn"), "text": ms_of("text_attn", "text_merge")}
+                 "swa": ms_of("swa_attn"), "text": ms_of("pack_text", "text_attn", "text_merge")}
 
     sweep = []
     if not args.no_sweep:

@@ -1,13 +1,162 @@
-"""Profiling helpers: a plain device copy of known size, used to calibrate
-rocprofv3's memory counters (FETCH_SIZE / WRITE_SIZE) before they are read
-for the layer's kernels.
+"""Profiling helpers around rocprofv3 (run on the GPU machine, summarised on
+any machine):
+
+* ``copy``: a plain device copy of known size, used to calibrate the memory
+  counters (FETCH_SIZE / WRITE_SIZE, KiB per dispatch) before they are read
+  for the layer's kernels;
+* ``trace-summary``: per-kernel call counts and average durations from a
+  ``rocprofv3 --kernel-trace --output-format csv`` run of bench.py, beside
+  the event-timed averages bench.py printed in the same run;
+* ``pmc-summary``: HBM-side bytes per launch of every kernel from two
+  ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE) scaled by the copy probe's
+  factors; writes a text table and one JSON record per kernel, which bench.py
+  reads as the roofline's ``traffic`` while the kernel source is unchanged.
 
   python -m sparse_attention_long_nsa_amd.profiling copy --mib 1024 --reps 3
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
+import json
+import os
 import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:  # also runnable as a plain script
+    sys.path.insert(0, ROOT)
+
+# kernel symbol substring -> (short name, source file); pack_kv_kernel serves
+# three launches told apart by their grid (vision blocks / compressed chunks
+# / text rows), see short_name
+KERNELS = [
+    ("sel_attn_kernel", "sel_attn", "sparse_attention_long_nsa_amd/csrc/nsa_sel_attn.hip"),
+    ("cmp_attn_dma_kernel", "cmp_attn", "sparse_attention_long_nsa_amd/csrc/nsa_cmp_attn.hip"),
+    ("cmp_attn_kernel", "cmp_attn", "sparse_attention_long_nsa_amd/csrc/nsa_cmp_attn.hip"),
+    ("swa_attn_kernel", "swa_attn", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
+    ("text_attn_kernel", "text_attn", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
+    ("text_merge_kernel", "text_merge", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
+    ("topk_kernel", "blk_score_topk", "sparse_attention_long_nsa_amd/csrc/nsa_topk.hip"),
+    ("cmp_pool_kernel", "cmp_pool", "sparse_attention_long_nsa_amd/csrc/nsa_pool.hip"),
+    ("pack_kv_kernel", "pack", "sparse_attention_long_nsa_amd/csrc/nsa_sel_attn.hip"),
+]
+
+
+def short_name(kernel_name: str, grid: int, pack_grids: dict):
+    for sub, short, src in KERNELS:
+        if sub in kernel_name or sub.replace("_", "") in kernel_name:
+            if short == "pack":
+                return pack_grids.get(grid, "pack_other"), src
+            return short, src
+    return None, None
+
+
+def pack_grid_names(n_frames: int, n_cch: int, n_tchunks: int, hkv: int) -> dict:
+    """Grid sizes (threads) of the three packing launches -> names."""
+    return {n_frames * hkv * 256: "pack_kv", n_cch * hkv * 256: "pack_cmp", n_tchunks * hkv * 256: "pack_text"}
+
+
+def _grid(row: dict) -> int:
+    if "Grid_Size" in row:
+        return int(row["Grid_Size"])
+    return int(row["Grid_Size_X"]) * int(row.get("Grid_Size_Y", 1)) * int(row.get("Grid_Size_Z", 1))
+
+
+def _bench_line(log_path: str):
+    with open(log_path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{") and '"metric"' in line:
+                return json.loads(line)
+    return None
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def trace_summary(trace_csv: str, bench_log: str, pack_grids: dict, title: str, command: str,
+                  out_md: str) -> None:
+    dur = defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        name, _ = short_name(r["Kernel_Name"], _grid(r), pack_grids)
+        if name:
+            dur[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6)
+    bench = _bench_line(bench_log)
+    kern = bench["kernels"] if bench else {}
+    total = sum(sum(v) / len(v) for v in dur.values())
+    rows = sorted(dur.items(), key=lambda kv: -sum(kv[1]) / len(kv[1]))
+    lines = [f"# Kernel trace: {title}", "", "Command (from the repository root, on one MI355X):", "",
+             "```", command, "```", ""]
+    if bench:
+        lines += [f"bench.py in the same process reported {bench['ms_per_step']} ms/step "
+                  f"({bench['value']:.0f} tokens/s); its event-timed per-kernel averages are listed "
+                  "beside the profiler's.", ""]
+    lines += ["| kernel | calls | avg ms (rocprofv3) | avg ms (bench events) | share |", "|---|---|---|---|---|"]
+    for name, v in rows:
+        avg = sum(v) / len(v)
+        ev = kern.get(name, {}).get("avg_ms", "")
+        lines.append(f"| {name} | {len(v)} | {avg:.3f} | {ev} | {100 * avg / total:.1f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _counter_avgs(path: str, pack_grids: dict) -> dict:
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        name, src = short_name(r["Kernel_Name"], _grid(r), pack_grids)
+        if name:
+            vals[(name, src)].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def _copy_kib(path: str) -> float:
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if "copyBuffer" in r["Kernel_Name"]]
+    return sum(vals) / len(vals)
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                copy_mib: int, pack_grids: dict, workload: str, commands: list, bench_log: str,
+                out_md: str, out_dir: str) -> None:
+    copy_kib = copy_mib * 1024.0
+    f_fetch = copy_kib / _copy_kib(copy_fetch_csv)
+    f_write = copy_kib / _copy_kib(copy_write_csv)
+    fetch = _counter_avgs(fetch_csv, pack_grids)
+    write = _counter_avgs(write_csv, pack_grids)
+    bench = _bench_line(bench_log) if bench_log else None
+    kern = bench["kernels"] if bench else {}
+    lines = [f"# HBM-side traffic per launch: {workload}", "",
+             "Counters: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one run each), "
+             "averaged over the dispatches of each kernel, scaled by a plain 1 GiB device copy "
+             f"(`profiling.py copy`): FETCH x {f_fetch:.3f}, WRITE x {f_write:.3f} "
+             "(the copy reads and writes exactly 1 GiB). FETCH_SIZE counts everything the L2 "
+             "fetches from the memory fabric, Infinity Cache hits included, so these are upper "
+             "bounds on HBM bytes.", "", "Commands (from the repository root, on one MI355X):", "", "```"]
+    lines += commands + ["```", "",
+                         "| kernel | read GB | write GB | total GB | kernel ms (events) | GB/s |",
+                         "|---|---|---|---|---|---|"]
+    recs = []
+    for key in sorted(fetch, key=lambda k: -(fetch[k] * f_fetch + write.get(k, 0.0) * f_write)):
+        name, src = key
+        rd = fetch[key] * f_fetch * 1024
+        wr = write.get(key, 0.0) * f_write * 1024
+        ms = kern.get(name, {}).get("avg_ms")
+        gbs = f"{(rd + wr) / (ms * 1e-3) / 1e9:.0f}" if ms else ""
+        lines.append(f"| {name} | {rd / 1e9:.3f} | {wr / 1e9:.3f} | {(rd + wr) / 1e9:.3f} | {ms or ''} | {gbs} |")
+        recs.append({"kernel": name, "workload": workload, "source": src,
+                     "source_sha256_16": source_digest(os.path.join(ROOT, src)),
+                     "fetch_kib_per_dispatch": round(fetch[key], 3),
+                     "write_kib_per_dispatch": round(write.get(key, 0.0), 3),
+                     "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
+                     "hbm_bytes_per_launch": round(rd + wr), "commands": commands})
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    for rec in recs:
+        with open(os.path.join(out_dir, f"{rec['kernel']}_{workload}_pmc.json"), "w") as f:
+            json.dump(rec, f, indent=1)
 
 
 def copy_probe(mib: int, reps: int) -> None:
@@ -22,15 +171,44 @@ def copy_probe(mib: int, reps: int) -> None:
           flush=True)
 
 
+def _layer_grids(workload: str) -> dict:
+    from sparse_attention_long_nsa_amd.inputs import PREFILL_PRESETS
+    s = PREFILL_PRESETS[workload]
+    n_frames = -(-s.n_vis // s.block)
+    n_cch = -(-(s.n_vis // s.block) // s.block)
+    return pack_grid_names(n_frames, n_cch, -(-s.n_text // s.block), s.n_kv_heads)
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=3)
+    t = sub.add_parser("trace-summary")
+    t.add_argument("--trace-csv", required=True)
+    t.add_argument("--bench-log", required=True)
+    t.add_argument("--workload", default="qwen_128k_k32_w256")
+    t.add_argument("--title", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--out", required=True)
+    m = sub.add_parser("pmc-summary")
+    for k in ("fetch", "write", "copy-fetch", "copy-write"):
+        m.add_argument(f"--{k}-csv", required=True)
+    m.add_argument("--copy-mib", type=int, default=1024)
+    m.add_argument("--workload", default="qwen_128k_k32_w256")
+    m.add_argument("--bench-log", default=None)
+    m.add_argument("--command", action="append", default=[])
+    m.add_argument("--out-md", required=True)
+    m.add_argument("--out-dir", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         copy_probe(a.mib, a.reps)
+    elif a.cmd == "trace-summary":
+        trace_summary(a.trace_csv, a.bench_log, _layer_grids(a.workload), a.title, a.command, a.out)
+    else:
+        pmc_summary(a.fetch_csv, a.write_csv, a.copy_fetch_csv, a.copy_write_csv, a.copy_mib,
+                    _layer_grids(a.workload), a.workload, a.command, a.bench_log, a.out_md, a.out_dir)
 
 
 if __name__ == "__main__":
