@@ -152,8 +152,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen_128k_k32_w256")
-    ap.add_argument("--cpu-vision-rows", type=int, default=6000)
-    ap.add_argument("--cpu-text-rows", type=int, default=32)
+    ap.add_argument("--cpu-vision-rows", type=int, default=15000)
+    ap.add_argument("--cpu-text-rows", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     args = ap.parse_args()
