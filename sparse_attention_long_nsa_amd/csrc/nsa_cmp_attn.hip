@@ -34,6 +34,7 @@ namespace nsa {
 namespace {
 
 constexpr int kThreadsH = 256;  // 4 waves x 16 tokens
+constexpr float kSlack = 8.f;   // lazy running max, probabilities below 2^8
 
 // Folds four scaled logits (log2 units, -inf = masked) into a lane-partial
 // (max, sum) pair.
@@ -229,7 +230,17 @@ __device__ __forceinline__ void cmp_pass1_chunk(const uint16_t *ks, int c, const
       f32x4 x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = (b0 + i < nc_t) ? s[h][i] * sl2 : -INFINITY;
-      fold4(m[h], l[h], x);
+      // running max moved only when a new max exceeds it by kSlack (log2
+      // units): most tiles then cost one exponential per score
+      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(mx > m[h] + kSlack)) {
+        const float mn = fmaxf(m[h], mx);
+        l[h] = (mn == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - mn);
+        m[h] = mn;
+      }
+      const float base = (m[h] == -INFINITY) ? 0.f : m[h];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l[h] += __builtin_amdgcn_exp2f(x[i] - base);
     }
   }
 }

@@ -302,9 +302,15 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
       }
     }
     if (lane == 0) lds_store(&pass_[c], u);
-    // wait for both producers' pieces of block u
+    // wait for every producer's pieces of block u
     int spins = 0;
-    while (min(lds_load(&ready_[0]), lds_load(&ready_[1])) <= u) {
+    auto min_ready = [&]() {
+      int r = lds_load(&ready_[0]);
+#pragma unroll
+      for (int q = 1; q < C::NPW; ++q) r = min(r, lds_load(&ready_[q]));
+      return r;
+    };
+    while (min_ready() <= u) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) { bad = true; break; }
     }
