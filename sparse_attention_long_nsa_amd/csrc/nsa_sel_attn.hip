@@ -65,12 +65,21 @@ __device__ __forceinline__ void sel_tile(const uint16_t *ks, const uint16_t *vt,
                                          f32x4 (&o)[D / 16], float &m, float &l, bool rowneed,
                                          int mask_b, int t, float sl2, int lane) {
   const int grp = lane >> 4;
+  // dims outer, key subtiles inner (two at a time): independent accumulators
+  // keep the matrix pipe fed while the next fragments load
   f32x4 s[4];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    s[kt] = zero4();
+  for (int kt = 0; kt < 4; ++kt) s[kt] = zero4();
 #pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) s[kt] = mfma_qk<F16>(pk_k_frag<D>(ks, kt, ds, lane), qf[ds], s[kt]);
+  for (int ds = 0; ds < D / 32; ++ds) {
+#pragma unroll
+    for (int k0 = 0; k0 < 4; k0 += 2) {
+      u16x8 kf[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) kf[kt] = pk_k_frag<D>(ks, k0 + kt, ds, lane);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[k0 + kt] = mfma_qk<F16>(kf[kt], qf[ds], s[k0 + kt]);
+    }
   }
   if (mask_b >= 0) {  // causal inside the own block
 #pragma unroll
@@ -107,11 +116,18 @@ __device__ __forceinline__ void sel_tile(const uint16_t *ks, const uint16_t *vt,
       ls += s[kt][e];
     }
   l += ls;
-  const u16x8 pp0 = pack_p(s[0], s[1]), pp1 = pack_p(s[2], s[3]);
+  const u16x8 pp[2] = {pack_p(s[0], s[1]), pack_p(s[2], s[3])};
+  // key halves outer, dims inner: eight independent accumulators per half
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    o[dt] = mfma_f16(pk_v_frag<D>(vt, dt, 0, lane), pp0, o[dt]);
-    o[dt] = mfma_f16(pk_v_frag<D>(vt, dt, 1, lane), pp1, o[dt]);
+  for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+    for (int d0 = 0; d0 < D / 16; d0 += 4) {
+      u16x8 vf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vf[i] = pk_v_frag<D>(vt, d0 + i, kh, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[d0 + i] = mfma_f16(vf[i], pp[kh], o[d0 + i]);
+    }
   }
 }
 
