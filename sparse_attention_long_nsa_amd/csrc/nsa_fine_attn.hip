@@ -3,8 +3,9 @@
 // (c)) and dense causal GQA for text queries (same section: text tokens use
 // standard GQA).
 //
-// Layout H: a wave owns 16 queries and all G query heads of one KV group, so
-// each K / V^T fragment read from LDS feeds G matrix-core ops. Keys and
+// Layout H: a wave owns 16 queries and up to three of the G query heads of
+// one KV group, so each K / V^T fragment read from LDS feeds up to three
+// matrix-core ops. Keys and
 // values come from the packed block tiles (PackedTile, one 64-key chunk per
 // tile) by direct global->LDS copies, issued several chunks ahead.
 #include "nsa_kernels.h"
@@ -112,29 +113,33 @@ __device__ __forceinline__ void pass2_chunk(const uint16_t *ks, const uint16_t *
   }
 }
 
-// Two passes of this lane's query row (all G heads) over n_chunks packed
-// chunks: pass 1 gets the exact log-sum-exp, pass 2 forms normalised
-// probabilities for the PV product, so no accumulator is ever rescaled and
-// the G heads' accumulators stay in the matrix-core register file.
-// tile_at(c) is chunk c's packed tile; key_range(c, lo, hi) gives the keys
-// lo..hi (inclusive, empty if lo > hi) of chunk c valid for this lane's row.
-// Returns o normalised and the lse (log2 units).
+// Two passes of this lane's query row (G heads) over n_chunks packed chunks:
+// pass 1 gets the exact log-sum-exp, pass 2 forms normalised probabilities
+// for the PV product, so no accumulator is ever rescaled and the heads'
+// accumulators stay in the matrix-core register file. tile_at(c) is chunk
+// c's packed tile; key_range(c, lo, hi) gives the keys lo..hi (inclusive,
+// empty if lo > hi) of chunk c valid for this lane's row. Returns o
+// normalised and the lse (log2 units).
 //
-// Copies: pass 1 rings key tiles through eight LDS slots (seven chunks in
-// flight), pass 2 rings (K, V^T) pairs through four (three in flight). Each
-// ring step issues exactly one chunk's copies -- past the last chunk they
-// repeat chunk 0 into slots that are never read -- so "chunk c landed" is a
-// single straight-line vmcnt wait; the slots are separate LDS objects named
-// at compile time, so the compiler adds no waits of its own.
-template <int D, int G, bool F16, class TileAt, class KeyRange>
+// Copies: four separate LDS tiles (64 KB at d = 128, so that two workgroups
+// share a CU). Pass 1 rings key tiles through all four (three chunks in
+// flight), pass 2 double-buffers (K, V^T) pairs. Each ring step issues exactly one chunk's copies -- past the last
+// chunk they repeat chunk 0 into slots that are never read again -- so
+// "chunk c landed" is one straight-line vmcnt wait; the slots are separate
+// LDS objects named at compile time, so the compiler adds no waits of its
+// own.
+// The slots are the kernel's LDS tiles, passed in so that every caller in
+// one kernel shares them.
+template <int D, int G, bool F16, int SLOTS, class TileAt, class KeyRange>
 __device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G],
                                          const u16x8 (&qf)[G][D / 32], float sl2, int n_chunks,
+                                         uint16_t (&r0)[PackedTile<D>::KE], uint16_t (&r1)[PackedTile<D>::KE],
+                                         uint16_t (&r2)[PackedTile<D>::KE], uint16_t (&r3)[PackedTile<D>::KE],
                                          TileAt tile_at, KeyRange key_range) {
+  static_assert(SLOTS == 4, "ring size");
   using T = PackedTile<D>;
   constexpr int KE = T::KE;
   constexpr int PK = KE / 512 / 4;  // copies per wave of one tile
-  __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
-  __shared__ __attribute__((aligned(16))) uint16_t r4[KE], r5[KE], r6[KE], r7[KE];
   const int lane = threadIdx.x & 63, g4 = 4 * (lane >> 4);
   // wave-uniform copy offsets kept in scalar registers
   const int off = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) * PK * 512);
@@ -145,9 +150,9 @@ __device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G]
 #define NSA_K(DST, C) dma_pieces<PK>(tile_at((C) < n_chunks ? (C) : 0) + off, (DST) + off, lane)
 #define NSA_P1(CUR, NXT)                                                  \
   {                                                                       \
-    wait_vm_c<6 * PK>();                                                  \
+    wait_vm_c<(SLOTS - 2) * PK>();                                        \
     bare_barrier();                                                       \
-    NSA_K(NXT, c + 7);                                                    \
+    NSA_K(NXT, c + SLOTS - 1);                                            \
     {                                                                     \
       int lo_, hi_;                                                       \
       key_range(c, lo_, hi_);                                             \
@@ -155,13 +160,9 @@ __device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G]
     }                                                                     \
     if (++c >= n_chunks) break;                                           \
   }
-  if (n_chunks > 0) {
-    NSA_K(r0, 0); NSA_K(r1, 1); NSA_K(r2, 2); NSA_K(r3, 3);
-    NSA_K(r4, 4); NSA_K(r5, 5); NSA_K(r6, 6);
-  }
+  if (n_chunks > 0) { NSA_K(r0, 0); NSA_K(r1, 1); NSA_K(r2, 2); }
   for (int c = 0; c < n_chunks;) {
-    NSA_P1(r0, r7) NSA_P1(r1, r0) NSA_P1(r2, r1) NSA_P1(r3, r2)
-    NSA_P1(r4, r3) NSA_P1(r5, r4) NSA_P1(r6, r5) NSA_P1(r7, r6)
+    NSA_P1(r0, r3) NSA_P1(r1, r0) NSA_P1(r2, r1) NSA_P1(r3, r2)
   }
 #undef NSA_P1
 #pragma unroll
@@ -184,9 +185,9 @@ __device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G]
   }
 #define NSA_P2(CK, CV, NK, NV)                                            \
   {                                                                       \
-    wait_vm_c<4 * PK>();                                                  \
+    wait_vm_c<(SLOTS / 2 - 2) * 2 * PK>();                                \
     bare_barrier();                                                       \
-    NSA_KV(NK, NV, c + 3);                                                \
+    NSA_KV(NK, NV, c + SLOTS / 2 - 1);                                    \
     {                                                                     \
       int lo_, hi_;                                                       \
       key_range(c, lo_, hi_);                                             \
@@ -194,9 +195,9 @@ __device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G]
     }                                                                     \
     if (++c >= n_chunks) break;                                           \
   }
-  if (n_chunks > 0) { NSA_KV(r0, r1, 0); NSA_KV(r2, r3, 1); NSA_KV(r4, r5, 2); }
+  if (n_chunks > 0) NSA_KV(r0, r1, 0);
   for (int c = 0; c < n_chunks;) {
-    NSA_P2(r0, r1, r6, r7) NSA_P2(r2, r3, r0, r1) NSA_P2(r4, r5, r2, r3) NSA_P2(r6, r7, r4, r5)
+    NSA_P2(r0, r1, r2, r3) NSA_P2(r2, r3, r0, r1)
   }
 #undef NSA_P2
 #undef NSA_KV
@@ -204,37 +205,49 @@ __device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G]
   wait_vm_c<0>();  // padding copies land before the workgroup's LDS is reused
 }
 
+// Query heads are split over N workgroups of at most three heads each
+// (sizes differing by at most one), so that a wave's accumulators fit half
+// the register file: two workgroups share a CU and one's loads and epilogue
+// overlap the other's math.
+template <int G> struct HeadSplit {
+  static constexpr int N = (G + 2) / 3;
+  static constexpr int size(int i) { return G / N + (i < G % N ? 1 : 0); }
+  static constexpr int first(int i) { return i == 0 ? 0 : first(i - 1) + size(i - 1); }
+};
+
 // ----------------------------------------------------------- sliding window
 // A 64-query tile (vision frame f) needs keys [t0 - w + 1, t0 + 63], i.e.
 // the packed blocks from (t0 - w + 1) / 64 to f.
-template <int D, int G, bool F16>
-__global__ __launch_bounds__(kThreadsH) void swa_attn_kernel(SwaParams p) {
+template <int D> struct Ring4 {
+  uint16_t (&r0)[PackedTile<D>::KE], (&r1)[PackedTile<D>::KE], (&r2)[PackedTile<D>::KE], (&r3)[PackedTile<D>::KE];
+};
+
+template <int D, int G, bool F16, int HW, int H0>
+__device__ __forceinline__ void swa_body(const SwaParams &p, int g, int f, Ring4<D> rg) {
   using T = PackedTile<D>;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4;
-  const int g = blockIdx.x % p.hkv;
-  const int f = p.n_tiles - 1 - (int)(blockIdx.x / p.hkv);  // heaviest first
   const int t0 = f * kBlk;
   const int t = t0 + wv * 16 + (lane & 15);
   const bool tvalid = t < p.n_vis;
   const int b_lo = max(0, t0 - p.window + 1) / kBlk;
   const int wnd = p.window;
 
-  u16x8 qf[G][D / 32];
-  const int64_t qrow = (p.v0 + (tvalid ? t : 0)) * p.hq + (int64_t)g * G;
-  load_q_h<D, G>(qf, p.q, qrow, tvalid, lane);
-  f32x4 o[G][D / 16];
-  float lse2[G];
+  u16x8 qf[HW][D / 32];
+  const int64_t qrow = (p.v0 + (tvalid ? t : 0)) * p.hq + (int64_t)g * G + H0;
+  load_q_h<D, HW>(qf, p.q, qrow, tvalid, lane);
+  f32x4 o[HW][D / 16];
+  float lse2[HW];
   const uint16_t *tiles = p.kv + ((int64_t)g * p.n_tiles + b_lo) * (T::KE + T::VE);
-  two_pass<D, G, F16>(o, lse2, qf, p.sl2, f - b_lo + 1,
-                      [&](int c) { return tiles + (int64_t)c * (T::KE + T::VE); },
-                      [&](int c, int &lo, int &hi) {
-                        const int key0 = (b_lo + c) * kBlk;  // keys t-w+1 .. t
-                        lo = t - wnd + 1 - key0;
-                        hi = tvalid ? t - key0 : -1;
-                      });
+  two_pass<D, HW, F16, 4>(o, lse2, qf, p.sl2, f - b_lo + 1, rg.r0, rg.r1, rg.r2, rg.r3,
+                          [&](int c) { return tiles + (int64_t)c * (T::KE + T::VE); },
+                          [&](int c, int &lo, int &hi) {
+                            const int key0 = (b_lo + c) * kBlk;  // keys t-w+1 .. t
+                            lo = t - wnd + 1 - key0;
+                            hi = tvalid ? t - key0 : -1;
+                          });
   if (tvalid) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < HW; ++h) {
       const float gate = sigmoidf_(p.gates[(qrow + h) * 3 + 2]);
       float *dst = p.out + (qrow + h) * D + 4 * grp;
 #pragma unroll
@@ -246,24 +259,37 @@ __global__ __launch_bounds__(kThreadsH) void swa_attn_kernel(SwaParams p) {
   }
 }
 
+template <int D, int G, bool F16>
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void swa_attn_kernel(SwaParams p) {
+  using S = HeadSplit<G>;
+  constexpr int KE = PackedTile<D>::KE;
+  __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
+  const Ring4<D> rg{r0, r1, r2, r3};
+  const int half = blockIdx.x % S::N, rest = blockIdx.x / S::N;
+  const int g = rest % p.hkv;
+  const int f = p.n_tiles - 1 - rest / p.hkv;  // heaviest first
+  if (half == 0) swa_body<D, G, F16, S::size(0), 0>(p, g, f, rg);
+  else if constexpr (S::N > 1) {
+    if (half == 1) swa_body<D, G, F16, S::size(1), S::first(1)>(p, g, f, rg);
+    else if constexpr (S::N > 2) swa_body<D, G, F16, S::size(2), S::first(2)>(p, g, f, rg);
+  }
+}
+
 // --------------------------------------------------------------- text rows
 __device__ __forceinline__ int64_t text_pos(int r, int64_t v0, int64_t v1) {
   return r < v0 ? (int64_t)r : v1 + (r - v0);
 }
 
-// One (64-query text tile, KV group, key split) per workgroup. The keys of
-// the whole sequence are the packed vision chunks followed by the packed
-// text chunks; split sp takes chunks [sp * cps, (sp + 1) * cps). Writes the
-// split's normalised output and lse for the merge kernel.
-template <int D, int G, bool F16>
-__global__ __launch_bounds__(kThreadsH) void text_attn_kernel(TextParams p) {
+// One (64-query text tile, KV group, key split, head part) per workgroup.
+// The keys of the whole sequence are the packed vision chunks followed by
+// the packed text chunks; split sp takes chunks [sp * cps, (sp + 1) * cps).
+// Writes the split's normalised output and lse for the merge kernel.
+template <int D, int G, bool F16, int HW, int H0>
+__device__ __forceinline__ void text_body(const TextParams &p, int sp, int g, int tile, Ring4<D> rg) {
   using T = PackedTile<D>;
   constexpr int SE = T::KE + T::VE;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4;
-  const int sp = blockIdx.x % p.n_split;
-  const int rest = blockIdx.x / p.n_split;
-  const int g = rest % p.hkv;
-  const int tile = rest / p.hkv;
   const int r = tile * kBlk + wv * 16 + (lane & 15);
   const bool rvalid = r < p.n_text;
   const int64_t pos = rvalid ? text_pos(r, p.v0, p.v1) : -1;
@@ -271,37 +297,57 @@ __global__ __launch_bounds__(kThreadsH) void text_attn_kernel(TextParams p) {
   const int cb = sp * p.chunks_per_split, ce = min(cb + p.chunks_per_split, nch);
   const int64_t n_vis = p.v1 - p.v0;
 
-  u16x8 qf[G][D / 32];
-  const int64_t qrow = (rvalid ? pos : 0) * p.hq + (int64_t)g * G;
-  load_q_h<D, G>(qf, p.q, qrow, rvalid, lane);
-  f32x4 o[G][D / 16];
-  float lse2[G];
+  u16x8 qf[HW][D / 32];
+  const int64_t qrow = (rvalid ? pos : 0) * p.hq + (int64_t)g * G + H0;
+  load_q_h<D, HW>(qf, p.q, qrow, rvalid, lane);
+  f32x4 o[HW][D / 16];
+  float lse2[HW];
   const uint16_t *vis = p.kv_vis + (int64_t)g * p.n_vchunks * SE;
   const uint16_t *txt = p.kv_txt + (int64_t)g * p.n_tchunks * SE;
-  two_pass<D, G, F16>(o, lse2, qf, p.sl2, max(0, ce - cb),
-                      [&](int c) {
-                        const int cc = cb + c;
-                        return cc < nvc ? vis + (int64_t)cc * SE : txt + (int64_t)(cc - nvc) * SE;
-                      },
-                      [&](int c, int &lo, int &hi) {
-                        const int cc = cb + c;
-                        lo = 0;
-                        if (cc < nvc) {  // vision-local keys j: j < n_vis, v0 + j <= pos
-                          const int key0 = cc * kBlk;
-                          hi = (int)min((int64_t)n_vis - 1, pos - p.v0) - key0;
-                        } else {  // text-local keys j: positions increase with j, so j <= r
-                          hi = (rvalid ? r : -1) - (cc - nvc) * kBlk;
-                        }
-                      });
+  two_pass<D, HW, F16, 4>(o, lse2, qf, p.sl2, max(0, ce - cb), rg.r0, rg.r1, rg.r2, rg.r3,
+                          [&](int c) {
+                            const int cc = cb + c;
+                            return cc < nvc ? vis + (int64_t)cc * SE : txt + (int64_t)(cc - nvc) * SE;
+                          },
+                          [&](int c, int &lo, int &hi) {
+                            const int cc = cb + c;
+                            lo = 0;
+                            if (cc < nvc) {  // vision-local keys j: j < n_vis, v0 + j <= pos
+                              const int key0 = cc * kBlk;
+                              hi = (int)min((int64_t)n_vis - 1, pos - p.v0) - key0;
+                            } else {  // text-local keys j: positions increase with j, so j <= r
+                              hi = (rvalid ? r : -1) - (cc - nvc) * kBlk;
+                            }
+                          });
   if (rvalid) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int64_t pr = ((int64_t)sp * p.n_text + r) * p.hq + g * G + h;
+    for (int h = 0; h < HW; ++h) {
+      const int64_t pr = ((int64_t)sp * p.n_text + r) * p.hq + g * G + H0 + h;
       if (grp == 0) p.part_ml[pr] = make_float2(lse2[h], 0.f);
       float *dst = p.part_o + pr * D + 4 * grp;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[h][dt];
     }
+  }
+}
+
+template <int D, int G, bool F16>
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void text_attn_kernel(TextParams p) {
+  using S = HeadSplit<G>;
+  constexpr int KE = PackedTile<D>::KE;
+  __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
+  const Ring4<D> rg{r0, r1, r2, r3};
+  const int half = blockIdx.x % S::N;
+  const int rest0 = blockIdx.x / S::N;
+  const int sp = rest0 % p.n_split;
+  const int rest = rest0 / p.n_split;
+  const int g = rest % p.hkv;
+  const int tile = rest / p.hkv;
+  if (half == 0) text_body<D, G, F16, S::size(0), 0>(p, sp, g, tile, rg);
+  else if constexpr (S::N > 1) {
+    if (half == 1) text_body<D, G, F16, S::size(1), S::first(1)>(p, sp, g, tile, rg);
+    else if constexpr (S::N > 2) text_body<D, G, F16, S::size(2), S::first(2)>(p, sp, g, tile, rg);
   }
 }
 
@@ -328,7 +374,7 @@ __global__ __launch_bounds__(D) void text_merge_kernel(TextParams p) {
 // ------------------------------------------------------------- launchers
 template <int D, int G, bool F16>
 hipError_t run_swa(const SwaParams &p, hipStream_t st) {
-  const unsigned n = (unsigned)p.n_tiles * (unsigned)p.hkv;
+  const unsigned n = (unsigned)p.n_tiles * (unsigned)p.hkv * HeadSplit<G>::N;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((swa_attn_kernel<D, G, F16>), dim3(n), dim3(kThreadsH), 0, st, p);
   return hipGetLastError();
@@ -336,7 +382,7 @@ hipError_t run_swa(const SwaParams &p, hipStream_t st) {
 
 template <int D, int G, bool F16>
 hipError_t run_text(const TextParams &p, hipStream_t st) {
-  const unsigned n = (unsigned)p.n_tiles * (unsigned)p.hkv * (unsigned)p.n_split;
+  const unsigned n = (unsigned)p.n_tiles * (unsigned)p.hkv * (unsigned)p.n_split * HeadSplit<G>::N;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((text_attn_kernel<D, G, F16>), dim3(n), dim3(kThreadsH), 0, st, p);
   return hipGetLastError();
