@@ -215,31 +215,41 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
     const uint16_t *kvg = p.kv + (int64_t)g * p.n_frames * C::SE + pw * C::PPP * 512;
     int issued = 0, pub = 0, spins = 0;
     int free_until = R - 1;  // highest block whose slot is known to be free
-    int ul = 0;              // ulist[(issued & ~63) + lane]
+    // union entries of the current 64-block window and of the next one
+    // (the next window is loaded a window ahead, off the critical path)
+    int ul = lane < nU ? (int)ulist[lane] : 0;
+    int ul_next = 64 + lane < nU ? (int)ulist[64 + lane] : 0;
+    // The consumers' pass counters are read one check ahead: the LDS load
+    // for the next check is issued as soon as the previous one is consumed,
+    // so its latency overlaps the copies and the waits in between.
+    int pv = lane < NC ? lds_load(&pass_[lane]) : kSent;
     while (pub < nU) {
       if (issued < nU && issued - pub < C::INFL) {
         if (issued > free_until) {
-          const int v = lane < NC ? lds_load(&pass_[lane]) : kSent;
-          int mn = v;
+          int mn = pv;
 #pragma unroll
-          for (int q = 0; q < NC; ++q) mn = min(mn, __builtin_amdgcn_readlane(v, q));
-          free_until = mn + R - 1;
+          for (int q = 0; q < NC; ++q) mn = min(mn, __builtin_amdgcn_readlane(pv, q));
+          free_until = __builtin_amdgcn_readfirstlane(mn + R - 1);
+          pv = lane < NC ? lds_load(&pass_[lane]) : kSent;
         }
         if (issued <= free_until) {
-          if ((issued & 63) == 0) ul = issued + lane < nU ? (int)ulist[issued + lane] : 0;
+          if (issued > 0 && (issued & 63) == 0) {
+            ul = ul_next;
+            ul_next = issued + 64 + lane < nU ? (int)ulist[issued + 64 + lane] : 0;
+          }
           const int blk = __builtin_amdgcn_readlane(ul, issued & 63);
           const uint16_t *src = kvg + (int64_t)blk * C::SE;
           uint16_t *dst = ring + (issued % R) * C::SE + pw * C::PPP * 512;
           asm volatile("" ::: "memory");
           dma_pieces<C::PPP>(src, dst, lane);
-          ++issued;
+          issued = __builtin_amdgcn_readfirstlane(issued + 1);
           continue;
         }
       }
       if (issued > pub) {  // publish the oldest block in flight
         wait_blocks<C::PPP>(issued - pub - 1);
         asm volatile("" ::: "memory");
-        ++pub;
+        pub = __builtin_amdgcn_readfirstlane(pub + 1);
         if (lane == 0) lds_store(&ready_[pw], pub);
         asm volatile("" ::: "memory");
       } else {
