@@ -146,6 +146,76 @@ def cpu_baseline(inp, n_vis_rows, n_text_rows):
     }
 
 
+def decode_bytes(s):
+    """Algorithmic HBM bytes of one decode step: per (sequence, KV group) the
+    compressed K/V cache, the k selected blocks' K/V and the window's K/V
+    (bf16), plus queries, gates and outputs."""
+    kv = 2 * 2 * s.head_dim  # K and V, bf16
+    n_blk = s.cache_len // s.block
+    per_group = n_blk * kv + min(s.top_k, n_blk) * s.block * kv + min(s.window, s.cache_len) * kv
+    other = s.batch * s.n_q_heads * (s.head_dim * 2 + 3 * 4 + s.head_dim * 4)
+    return float(s.batch * s.n_kv_heads * per_group + other)
+
+
+def run_decode_bench(steps, warmup):
+    """One nsa_decode step over 16 sequences with 131,072-token caches
+    (compressed caches pooled on the GPU beforehand, outside the timed
+    region); per-kernel event times as for prefill."""
+    import torch
+    from sparse_attention_long_nsa_amd import binding
+    from sparse_attention_long_nsa_amd.inputs import DECODE_PRESETS, make_decode_inputs
+    name = "decode_16x128k"
+    s = DECODE_PRESETS[name]
+    t0 = time.time()
+    inp = make_decode_inputs(s, seed=0)
+    log(f"inputs {name}: {time.time() - t0:.1f} s")
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0").to(torch.bfloat16)
+
+    q, kcache, vcache = bf(inp["q"]), bf(inp["k_cache"]), bf(inp["v_cache"])
+    del inp["k_cache"], inp["v_cache"]
+    wk, wv = bf(inp["w_k"]), bf(inp["w_v"])
+    gates = torch.from_numpy(inp["gates"]).to("cuda:0")
+    kc = torch.stack([binding.cmp_pool(kcache[b], wk, s.block)["bf16"] for b in range(s.batch)])
+    vc = torch.stack([binding.cmp_pool(vcache[b], wv, s.block)["bf16"] for b in range(s.batch)])
+
+    def call(out, ws):
+        return binding.decode(q, kcache, vcache, kc, vc, gates, s.top_k, s.window, block=s.block,
+                              out=out, workspace=ws)
+
+    r = call(None, None)
+    out, ws = r["out"], r["workspace"]
+    for _ in range(warmup):
+        call(out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call(out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    binding.timing_reset()
+    binding.timing_enable(True)
+    for _ in range(steps):
+        call(out, ws)
+    torch.cuda.synchronize()
+    kern = binding.timing_read()
+    binding.timing_enable(False)
+    nbytes = decode_bytes(s)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": name, "batch": s.batch, "cache_len": s.cache_len, "top_k": s.top_k,
+           "window": s.window, "us_per_step": round(ms * 1e3, 2),
+           "sequences_per_s": round(s.batch / (ms * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes": nbytes},
+           "kernels": {k: {"avg_us": round(v[0] / v[1] * 1e3, 2), "launches": v[1]} for k, v in kern.items()}}
+    log(f"decode {name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s algorithmic")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +226,7 @@ def main():
     ap.add_argument("--cpu-text-rows", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer library runs on a single MI355X and has no "
@@ -223,6 +294,10 @@ def main():
                           "mfma_peak_frac": round(fl / (sms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
             log(f"  sweep k={k} w={w}: {sms:.3f} ms")
 
+    decode = None
+    if not args.no_decode:
+        decode = run_decode_bench(max(10, args.steps), args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_vision_rows, args.cpu_text_rows)
@@ -252,6 +327,7 @@ def main():
         "branch_ms": branch_ms,
         "kernels": per_kernel,
         "sweep": sweep,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
