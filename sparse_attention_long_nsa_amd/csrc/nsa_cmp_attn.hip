@@ -209,7 +209,10 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_kernel(CmpAttnParams p) {
 // The ring slots are separate LDS objects and every step names its slot at
 // compile time: reads of one slot then need not wait for copies still
 // landing in another.
-template <int D, int G>
+// MASK: the chunk may hold blocks some query of the workgroup must not see.
+// Only a frame's last chunk can (every earlier one ends at or before the
+// frame's first query's own block), so the others skip the per-score tests.
+template <int D, int G, bool MASK>
 __device__ __forceinline__ void cmp_pass1_chunk(const uint16_t *ks, int c, const u16x8 (&qf)[G][D / 32],
                                                 float (&m)[G], float (&l)[G], int nc_t, float sl2, int lane) {
   const int grp = lane >> 4;
@@ -227,20 +230,20 @@ __device__ __forceinline__ void cmp_pass1_chunk(const uint16_t *ks, int c, const
     const int b0 = c * kBlk + 16 * kt + 4 * grp;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      f32x4 x;
+      f32x4 x;  // raw scores; the scale sl2 > 0 is folded into the exponent
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = (b0 + i < nc_t) ? s[h][i] * sl2 : -INFINITY;
+      for (int i = 0; i < 4; ++i) x[i] = (!MASK || b0 + i < nc_t) ? s[h][i] : -INFINITY;
       // running max moved only when a new max exceeds it by kSlack (log2
       // units): most tiles then cost one exponential per score
-      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) * sl2;
       if (__builtin_amdgcn_ballot_w64(mx > m[h] + kSlack)) {
         const float mn = fmaxf(m[h], mx);
         l[h] = (mn == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - mn);
         m[h] = mn;
       }
-      const float base = (m[h] == -INFINITY) ? 0.f : m[h];
+      const float nbase = (m[h] == -INFINITY) ? 0.f : -m[h];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l[h] += __builtin_amdgcn_exp2f(x[i] - base);
+      for (int i = 0; i < 4; ++i) l[h] += __builtin_amdgcn_exp2f(fmaf(x[i], sl2, nbase));
     }
   }
 }
@@ -337,13 +340,17 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
   // follows too). Past the last chunk the copies repeat chunk 0 into slots
   // that are never read again.
 #define NSA_ISSUE_K_OR_PAD(DST, C) NSA_ISSUE_K(DST, ((C) < nch ? (C) : 0))
+  // The last chunk (the only one that needs masking) leaves the ring loop
+  // and is taken after a full wait, from whichever slot holds it.
+  const uint16_t *last = r0;
 #define NSA_P1_STEP(CUR, NXT)                                             \
   {                                                                       \
+    if (c == nch - 1) { last = CUR; break; }                              \
     wait_vm_c<6 * PK>();                                                  \
     bare_barrier();                                                       \
     NSA_ISSUE_K_OR_PAD(NXT, c + 7);                                       \
-    cmp_pass1_chunk<D, G>(CUR, c, qf, m, l, nc_t, p.sl2, lane);           \
-    if (++c >= nch) break;                                                \
+    cmp_pass1_chunk<D, G, false>(CUR, c, qf, m, l, nc_t, p.sl2, lane);    \
+    ++c;                                                                  \
   }
   if (nch > 0) {
     NSA_ISSUE_K_OR_PAD(r0, 0);
@@ -365,6 +372,11 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
     NSA_P1_STEP(r7, r6)
   }
 #undef NSA_P1_STEP
+  if (nch > 0) {
+    wait_vm_c<0>();
+    bare_barrier();
+    cmp_pass1_chunk<D, G, true>(last, nch - 1, qf, m, l, nc_t, p.sl2, lane);
+  }
 #undef NSA_ISSUE_K_OR_PAD
   float lse2[G];
 #pragma unroll

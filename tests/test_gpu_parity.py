@@ -145,3 +145,19 @@ def test_full_size_sampled_rows(preset):
     v = np.where(sel < 0, pad, sel)
     assert np.all(np.diff(v, axis=2) > 0)
     assert np.all(np.isfinite(gpu["out"]))
+
+
+def test_all_tied_scores_take_lowest_blocks():
+    # every vision key zero: all compressed keys are zero, every block score
+    # ties, and the reading's tie rule (lowest index first) fixes the answer:
+    # blocks 0 .. k-2 plus the own block. Rows with more than 64 candidates
+    # exercise the top-k's radix-select path, the others its ranking path.
+    s = PrefillShape(64 * 100, 0, 20, 28, 4, 128, 64, 8, 128, "bf16")
+    inp = make_prefill_inputs(s, seed=8)
+    inp["k"][inp["is_vision"].astype(bool)] = 0.0
+    gpu, rep, orep = check_full(inp, "all_tied")
+    assert rep.exempt == 0 and rep.counted == 0, rep
+    sel = gpu["sel"]
+    for t in (64 * 7 + 3, 64 * 40, 64 * 66 + 5, 64 * 99 + 63):
+        f = t // 64
+        assert sel[t, :, :].tolist() == [list(range(s.top_k - 1)) + [f]] * s.n_kv_heads, (t, sel[t])
