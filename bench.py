@@ -298,6 +298,12 @@ def main():
     if not args.no_decode:
         decode = run_decode_bench(max(10, args.steps), args.warmup)
 
+    # the published peak checked on this GPU with an MFMA-loop probe
+    from sparse_attention_long_nsa_amd.profiling import mfma_peak
+    probe = mfma_peak()
+    probe["frac_of_published"] = round(probe["tflops"] / PEAK_BF16_TFLOPS, 4)
+    log(f"mfma loop probe: {probe}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_vision_rows, args.cpu_text_rows)
@@ -323,6 +329,7 @@ def main():
                    "parallelism": "single GPU"},
         "mfma_peak_frac": round(layer_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "algorithmic_tflop": round(layer_flops / 1e12, 3),
+        "mfma_loop_probe": probe,
         "roofline": roofline,
         "branch_ms": branch_ms,
         "kernels": per_kernel,

@@ -173,6 +173,16 @@ nsa_status nsa_timing_enable(int enable);
 nsa_status nsa_timing_reset(void);
 int nsa_timing_read(int max_entries, const char **names, double *total_ms, int *counts);
 
+/* Matrix-core peak probe (measurement aid; computes nothing of the layer).
+ * Launches n_wg workgroups of four waves; each wave runs `iters` rounds of
+ * 128 v_mfma_f32_16x16x32_bf16 products (bf16 operands, fp32 accumulators,
+ * eight independent chains) and writes one float per lane to
+ * out[n_wg * 256] (device, caller-owned) so the work cannot be dropped.
+ * Work per call: n_wg * 4 * iters * 128 * 16384 flops; time it with events
+ * on `stream`.
+ * NSA_ERR_INVALID_ARG for n_wg < 1, iters < 1 or out == NULL. */
+nsa_status nsa_probe_mfma_bf16(int32_t n_wg, int32_t iters, float *out, void *stream);
+
 /* Static description of a status code. */
 const char *nsa_status_string(nsa_status status);
 

@@ -21,7 +21,7 @@ NSA_DTYPE_BF16, NSA_DTYPE_FP32 = 0, 1
 EXPORTED = (
     "nsa_prefill_workspace_size", "nsa_prefill", "nsa_decode_workspace_size", "nsa_decode",
     "nsa_cmp_pool", "nsa_timing_enable", "nsa_timing_reset", "nsa_timing_read",
-    "nsa_status_string", "nsa_version",
+    "nsa_status_string", "nsa_version", "nsa_probe_mfma_bf16",
 )
 
 
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
         L.nsa_version.restype = ctypes.c_char_p
+        L.nsa_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
+        L.nsa_probe_mfma_bf16.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -279,3 +281,16 @@ def cmp_pool(x, w, block=64, out_bf16=True, out_f32=False, stream=None) -> dict:
     if st != NSA_OK:
         raise NsaError(st, "nsa_cmp_pool")
     return res
+
+
+MFMA_PROBE_FLOPS_PER_WAVE_ROUND = 128 * 16384  # 128 products of 16x16x32 per round
+
+
+def probe_mfma_bf16(n_wg: int, iters: int, out, stream=None) -> int:
+    """Runs nsa_probe_mfma_bf16 into out (float32 [n_wg * 256], device);
+    returns the flops it issues."""
+    _check_dev("out", out, torch.float32, (n_wg * 256,))
+    st = lib().nsa_probe_mfma_bf16(n_wg, iters, _ptr(out), _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_probe_mfma_bf16")
+    return n_wg * 4 * iters * MFMA_PROBE_FLOPS_PER_WAVE_ROUND

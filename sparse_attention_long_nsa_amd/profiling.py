@@ -171,6 +171,29 @@ def copy_probe(mib: int, reps: int) -> None:
           flush=True)
 
 
+def mfma_peak(n_wg: int = 256 * 8, iters: int = 400, reps: int = 8) -> dict:
+    """Dense bf16 matrix-core rate measured by the MFMA-loop probe: the best
+    of `reps` timed launches (events on the launch stream)."""
+    import torch
+    from sparse_attention_long_nsa_amd import binding
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    binding.probe_mfma_bf16(n_wg, 4, out, st)  # warm-up
+    best = float("inf")
+    flops = 0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        flops = binding.probe_mfma_bf16(n_wg, iters, out, st)
+        e1.record(st)
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("MFMA probe produced non-finite values")
+    return {"tflops": round(flops / (best * 1e-3) / 1e12, 1), "ms": round(best, 4), "flops": flops,
+            "workgroups": n_wg, "rounds": iters, "instr": "v_mfma_f32_16x16x32_bf16"}
+
+
 def _layer_grids(workload: str) -> dict:
     from sparse_attention_long_nsa_amd.inputs import PREFILL_PRESETS
     s = PREFILL_PRESETS[workload]
@@ -185,6 +208,7 @@ def main(argv=None) -> None:
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=3)
+    sub.add_parser("mfma-peak")
     t = sub.add_parser("trace-summary")
     t.add_argument("--trace-csv", required=True)
     t.add_argument("--bench-log", required=True)
@@ -204,6 +228,8 @@ def main(argv=None) -> None:
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         copy_probe(a.mib, a.reps)
+    elif a.cmd == "mfma-peak":
+        print(json.dumps(mfma_peak()), flush=True)
     elif a.cmd == "trace-summary":
         trace_summary(a.trace_csv, a.bench_log, _layer_grids(a.workload), a.title, a.command, a.out)
     else:

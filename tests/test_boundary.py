@@ -137,6 +137,13 @@ def test_cmp_pool_validation():
     assert L.nsa_cmp_pool(640, 4, 96, 64, 0, FAKE, FAKE, FAKE, None, None) == binding.NSA_ERR_UNSUPPORTED
 
 
+def test_mfma_probe_validation():
+    L = binding.lib()
+    assert L.nsa_probe_mfma_bf16(0, 10, FAKE, None) == binding.NSA_ERR_INVALID_ARG
+    assert L.nsa_probe_mfma_bf16(8, 0, FAKE, None) == binding.NSA_ERR_INVALID_ARG
+    assert L.nsa_probe_mfma_bf16(8, 10, None, None) == binding.NSA_ERR_INVALID_ARG
+
+
 def ddesc(batch=16, L=131072, hq=28, hkv=4, d=128, block=64, k=16, w=512, dtype=0):
     return binding.DecodeDesc(batch, L, hq, hkv, d, block, k, w, 0.0, dtype)
 
