@@ -34,7 +34,7 @@ namespace nsa {
 namespace {
 
 constexpr int kThreadsH = 256;  // 4 waves x 16 tokens
-constexpr float kSlack = 8.f;   // lazy running max, probabilities below 2^8
+constexpr int kBufWord3 = 0x00020000;  // buffer resource word 3 (raw, 32-bit) on gfx9
 
 // Folds four scaled logits (log2 units, -inf = masked) into a lane-partial
 // (max, sum) pair.
@@ -209,89 +209,119 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_kernel(CmpAttnParams p) {
 // The ring slots are separate LDS objects and every step names its slot at
 // compile time: reads of one slot then need not wait for copies still
 // landing in another.
-// MASK: the chunk may hold blocks some query of the workgroup must not see.
-// Only a frame's last chunk can (every earlier one ends at or before the
-// frame's first query's own block), so the others skip the per-score tests.
-template <int D, int G, bool MASK>
+// Both passes walk a chunk head by head as a software pipeline: the scores of
+// head h+1 are issued to the matrix cores before head h's exponentials, so
+// the two overlap within the one wave. The K fragments (and in pass 2 the V
+// fragments) of the chunk stay in registers across the heads. Blocks a query
+// must not see are masked by starting their score accumulators at -inf (one
+// bias per block, shared by every head), and score rows are written with
+// buffer stores whose out-of-range lanes the hardware drops: no branches, so
+// each chunk is one straight run of instructions the scheduler can interleave.
+template <int D, int NT>
+__device__ __forceinline__ void cmp_scores(const u16x8 (&kf)[NT][D / 32], const u16x8 (&q)[D / 32],
+                                           const f32x4 (&bias)[NT], f32x4 (&s)[NT]) {
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) s[kt] = bias[kt];
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds)
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt) s[kt] = mfma_f16(kf[kt][ds], q[ds], s[kt]);
+}
+
+template <int D, int G>
 __device__ __forceinline__ void cmp_pass1_chunk(const uint16_t *ks, int c, const u16x8 (&qf)[G][D / 32],
                                                 float (&m)[G], float (&l)[G], int nc_t, float sl2, int lane) {
   const int grp = lane >> 4;
+  u16x8 kf[4][D / 32];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    f32x4 s[G];
+  for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = zero4();
+    for (int ds = 0; ds < D / 32; ++ds) kf[kt][ds] = pk_k_frag<D>(ks, kt, ds, lane);
+  const int b0 = c * kBlk + 4 * grp;  // block of element (kt, i): b0 + 16 kt + i
+  f32x4 bias[4];
 #pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      const u16x8 a = pk_k_frag<D>(ks, kt, ds, lane);
+  for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = mfma_f16(a, qf[h][ds], s[h]);
-    }
-    const int b0 = c * kBlk + 16 * kt + 4 * grp;
+    for (int i = 0; i < 4; ++i) bias[kt][i] = (b0 + 16 * kt + i < nc_t) ? 0.f : -INFINITY;
+  f32x4 sc[4], sn[4];
+  cmp_scores<D, 4>(kf, qf[0], bias, sc);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      f32x4 x;  // raw scores; the scale sl2 > 0 is folded into the exponent
+  for (int h = 0; h < G; ++h) {
+    if (h + 1 < G) cmp_scores<D, 4>(kf, qf[h + 1], bias, sn);
+    float mx = sc[0][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = (!MASK || b0 + i < nc_t) ? s[h][i] : -INFINITY;
-      // running max moved only when a new max exceeds it by kSlack (log2
-      // units): most tiles then cost one exponential per score
-      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) * sl2;
-      if (__builtin_amdgcn_ballot_w64(mx > m[h] + kSlack)) {
-        const float mn = fmaxf(m[h], mx);
-        l[h] = (mn == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - mn);
-        m[h] = mn;
-      }
-      const float nbase = (m[h] == -INFINITY) ? 0.f : -m[h];
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l[h] += __builtin_amdgcn_exp2f(fmaf(x[i], sl2, nbase));
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kt][i]);
+    // exact running max per chunk and head (raw scores; the scale sl2 > 0
+    // is folded into the exponent)
+    const float mn = fmaxf(m[h], mx * sl2);
+    const float nb = (mn == -INFINITY) ? 0.f : -mn;
+    float acc = (m[h] == -INFINITY) ? 0.f : l[h] * __builtin_amdgcn_exp2f(m[h] + nb);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc += __builtin_amdgcn_exp2f(fmaf(sc[kt][i], sl2, nb));
+    l[h] = acc;
+    m[h] = mn;
+    if (h + 1 < G) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sc[kt] = sn[kt];
     }
   }
 }
 
+// gsr: buffer resource over this workgroup's score rows (64 rows of f
+// floats); srow: byte offset of this lane's row.
 template <int D, int G>
 __device__ __forceinline__ void cmp_pass2_chunk(const uint16_t *ks, const uint16_t *vt, int c,
                                                 const u16x8 (&qf)[G][D / 32], f32x4 (&o)[G][D / 16],
-                                                const float (&lse2)[G], float *gsrow, bool tvalid, int f,
-                                                int nc_t, float sl2, int lane) {
+                                                const float (&nlse2)[G], __amdgpu_buffer_rsrc_t gsr,
+                                                int srow, int f, int nc_t, float sl2, int lane) {
   const int grp = lane >> 4;
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2) {
-    f32x4 s[2][G];
+    // keys 32*ks2 .. 32*ks2+31 of the chunk: key subtiles kt = 2*ks2 + kk
+    u16x8 kf[2][D / 32], vf[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int kt = 2 * ks2 + kk;
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[kk][h] = zero4();
+      for (int ds = 0; ds < D / 32; ++ds) kf[kk][ds] = pk_k_frag<D>(ks, 2 * ks2 + kk, ds, lane);
 #pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) {
-        const u16x8 a = pk_k_frag<D>(ks, kt, ds, lane);
+    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = pk_v_frag<D>(vt, dt, ks2, lane);
+    const int b0 = c * kBlk + 32 * ks2 + 4 * grp;  // block of element (kk, i): b0 + 16 kk + i
+    f32x4 bias[2];
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[kk][h] = mfma_f16(a, qf[h][ds], s[kk][h]);
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bias[kk][i] = (b0 + 16 * kk + i < nc_t) ? 0.f : -INFINITY;
+    f32x4 sc[2], sn[2], gsum[2] = {zero4(), zero4()};
+    cmp_scores<D, 2>(kf, qf[0], bias, sc);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (h + 1 < G) cmp_scores<D, 2>(kf, qf[h + 1], bias, sn);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[kk][i] = __builtin_amdgcn_exp2f(fmaf(sc[kk][i], sl2, nlse2[h]));
+        gsum[kk] += sc[kk];
       }
-      const int b0 = c * kBlk + 16 * kt + 4 * grp;
-      f32x4 gsum = zero4();
+      const u16x8 pf = pack_p(sc[0], sc[1]);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s[kk][h][i] = (b0 + i < nc_t) ? __builtin_amdgcn_exp2f(fmaf(s[kk][h][i], sl2, -lse2[h])) : 0.f;
-        gsum += s[kk][h];
-      }
-      if (tvalid) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (b0 + i < f) gsrow[b0 + i] = gsum[i];
+      for (int dt = 0; dt < D / 16; ++dt) o[h][dt] = mfma_f16(vf[dt], pf, o[h][dt]);
+      if (h + 1 < G) {
+        sc[0] = sn[0];
+        sc[1] = sn[1];
       }
     }
-    u16x8 pf[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) pf[h] = pack_p(s[0][h], s[1][h]);
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const u16x8 a = pk_v_frag<D>(vt, dt, ks2, lane);
-#pragma unroll
-      for (int h = 0; h < G; ++h) o[h][dt] = mfma_f16(a, pf[h], o[h][dt]);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int b = b0 + 16 * kk + i;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gsum[kk][i]), gsr,
+                                              b < f ? srow + 4 * b : 0x7ffffff0, 0, 0);
+      }
   }
 }
 
@@ -340,17 +370,13 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
   // follows too). Past the last chunk the copies repeat chunk 0 into slots
   // that are never read again.
 #define NSA_ISSUE_K_OR_PAD(DST, C) NSA_ISSUE_K(DST, ((C) < nch ? (C) : 0))
-  // The last chunk (the only one that needs masking) leaves the ring loop
-  // and is taken after a full wait, from whichever slot holds it.
-  const uint16_t *last = r0;
 #define NSA_P1_STEP(CUR, NXT)                                             \
   {                                                                       \
-    if (c == nch - 1) { last = CUR; break; }                              \
     wait_vm_c<6 * PK>();                                                  \
     bare_barrier();                                                       \
     NSA_ISSUE_K_OR_PAD(NXT, c + 7);                                       \
-    cmp_pass1_chunk<D, G, false>(CUR, c, qf, m, l, nc_t, p.sl2, lane);    \
-    ++c;                                                                  \
+    cmp_pass1_chunk<D, G>(CUR, c, qf, m, l, nc_t, p.sl2, lane);           \
+    if (++c >= nch) break;                                                \
   }
   if (nch > 0) {
     NSA_ISSUE_K_OR_PAD(r0, 0);
@@ -372,11 +398,6 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
     NSA_P1_STEP(r7, r6)
   }
 #undef NSA_P1_STEP
-  if (nch > 0) {
-    wait_vm_c<0>();
-    bare_barrier();
-    cmp_pass1_chunk<D, G, true>(last, nch - 1, qf, m, l, nc_t, p.sl2, lane);
-  }
 #undef NSA_ISSUE_K_OR_PAD
   float lse2[G];
 #pragma unroll
@@ -399,7 +420,14 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[h][dt] = zero4();
-  float *gsrow = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + (t - f * kBlk)) * f;
+  // the workgroup's score rows: 64 rows (padding rows of a partial frame
+  // included) of f floats; stores past a row's end fall outside and are dropped
+  const __amdgpu_buffer_rsrc_t gsr = __builtin_amdgcn_make_buffer_rsrc(
+      p.gs + frame_off(f, p.hkv) + (int64_t)g * kBlk * f, 0, kBlk * f * (int)sizeof(float), kBufWord3);
+  const int srow = (t - f * kBlk) * f * (int)sizeof(float);
+  float nlse2[G];  // -lse2, 0 where no block is visible (every score masked)
+#pragma unroll
+  for (int h = 0; h < G; ++h) nlse2[h] = (lse2[h] == -INFINITY) ? 0.f : -lse2[h];
 #define NSA_ISSUE_KV(DK, DV, C)                                           \
   {                                                                       \
     NSA_ISSUE_K(DK, C);                                                   \
@@ -413,7 +441,7 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
     wait_vm_c<0>();                                                       \
     bare_barrier();                                                       \
     if (c + 1 < nch) NSA_ISSUE_KV(NK, NV, c + 1);                         \
-    cmp_pass2_chunk<D, G>(CK, CV, c, qf, o, lse2, gsrow, tvalid, f, nc_t, p.sl2, lane); \
+    cmp_pass2_chunk<D, G>(CK, CV, c, qf, o, nlse2, gsr, srow, f, nc_t, p.sl2, lane); \
     if (++c >= nch) break;                                                \
   }
   for (int c = 0; c < nch;) {
