@@ -10,9 +10,12 @@
 // the (k-1)-th largest of the 64 lane maxima is a lower bound T0 for the
 // (k-1)-th largest score (those lane maxima are k-1 distinct scores >= T0),
 // so every score of the answer is >= T0; when at most 64 scores reach T0 the
-// wave ranks just those (score descending, index ascending) and keeps the
-// top k-1. Otherwise it finds the (k-1)-th largest score exactly by an
-// MSB-first radix select. The chosen indices are emitted in ascending order.
+// wave compacts just those (one per lane, ascending index), finds the
+// (k-1)-th largest of them, and keeps every larger one plus the lowest-index
+// ones equal to it. Both order statistics come from a bitwise search over
+// 64 lane values (32 ballot counts, mostly scalar work). Otherwise it finds
+// the (k-1)-th largest score exactly by an MSB-first radix select over all
+// scores. The chosen indices are emitted in ascending order.
 #include "nsa_kernels.h"
 
 namespace nsa {
@@ -20,6 +23,18 @@ namespace nsa {
 namespace {
 
 constexpr int kWavesPerWG = 1;  // one wave per workgroup: early exits need no barrier care
+
+// The largest T with at least `need` lanes holding v >= T (need <= lanes with
+// a nonzero v): the need-th largest of the 64 lane values. Bits MSB first.
+__device__ __forceinline__ uint32_t kth_largest_lane(uint32_t v, int need) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    if (__popcll(__ballot(v >= c)) >= need) t = c;
+  }
+  return t;
+}
 
 template <int NPL>
 __global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
@@ -44,22 +59,19 @@ __global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
 #pragma unroll
   for (int s = 0; s < NPL; ++s) {
     const int e = s * 64 + lane;
-    key[s] = e < f ? __float_as_uint(row[e]) + 1u : 0u;
+    key[s] = 0u;
+    if (s * 64 < f) {  // wave-uniform; lanes past the row re-read its last entry
+      const uint32_t bits = __float_as_uint(row[min(e, f - 1)]);
+      key[s] = e < f ? bits + 1u : 0u;
+    }
   }
 
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   {
-    // rank of each lane maximum among the 64 (ties: lower lane first)
     uint32_t lm = 0;
 #pragma unroll
     for (int s = 0; s < NPL; ++s) lm = max(lm, key[s]);
-    int rank = 0;
-    for (int j = 0; j < 64; ++j) {
-      const uint32_t v = __builtin_amdgcn_readlane(lm, j);
-      rank += (v > lm || (v == lm && j < lane)) ? 1 : 0;
-    }
-    const uint64_t at = __ballot(rank == need - 1);
-    const uint32_t t0 = __builtin_amdgcn_readlane(lm, __ffsll((unsigned long long)at) - 1);
+    const uint32_t t0 = kth_largest_lane(lm, need);
     int c0 = 0;
 #pragma unroll
     for (int s = 0; s < NPL; ++s) c0 += __popcll(__ballot(key[s] >= t0));
@@ -80,15 +92,13 @@ __global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
       __syncthreads();
       const uint32_t ck = lane < c0 ? hist[lane] : 0u;
       const uint32_t ci = lane < c0 ? hist[64 + lane] : 0xffffffffu;
-      // rank among candidates: larger score first, then lower index
-      int r = 0;
-      for (int j = 0; j < c0; ++j) {
-        const uint32_t vk = __builtin_amdgcn_readlane(ck, j);
-        const uint32_t vi = __builtin_amdgcn_readlane(ci, j);
-        r += (vk > ck || (vk == ck && vi < ci)) ? 1 : 0;
-      }
-      const bool take = lane < c0 && r < need;
-      const uint64_t tb = __ballot(take);  // candidates sit in ascending index order
+      // keep the candidates above the need-th largest key, then the
+      // lowest-index ones equal to it (candidates sit in ascending index order)
+      const uint32_t t1 = kth_largest_lane(ck, need);
+      const uint64_t gt = __ballot(ck > t1), eq = __ballot(ck == t1);
+      const int rest = need - __popcll(gt);
+      const bool take = (ck > t1) || (ck == t1 && __popcll(eq & below) < rest);
+      const uint64_t tb = __ballot(take);
       if (take) out[__popcll(tb & below)] = (int32_t)ci;
       if (lane == 0) out[need] = f;  // own block, larger than every candidate
       return;
