@@ -4,17 +4,21 @@
 // blocks is complete and visible; the query's own block (the last) is always
 // selected.
 //
-// One query per sequence makes this GEMV-shaped and HBM-bound (compressed
-// cache, selected blocks and window are each read once), so the kernels use
-// fp32 vector math and split the work over blocks for occupancy:
-//   dec_cmp     per (sequence, KV group, chunk of 128 compressed blocks):
-//               scaled logits of the group's query heads, and a softmax
-//               partial (max, sum, unnormalised output) of the chunk
-//   dec_select  per (sequence, KV group): merged log-sum-exp and o_cmp,
-//               group importance scores, exact top-(k-1) + own block
-//   dec_fine    per (sequence, KV group, item): one selected block or one
-//               64-key slice of the window -> softmax partial
-//   dec_combine per (sequence, query head): merge partials, apply gates
+// One query per sequence makes this HBM-bound: the compressed caches, the
+// selected blocks and the window are each read once. All three branches are
+// cut into items of 64 keys, one wave each, so thousands of waves stream the
+// caches at once:
+//   dec_item (phase 0) a chunk of 64 compressed blocks, or a 64-key slice of
+//                      the window: scores of the group's heads by matrix-core
+//                      products (bf16 in, fp32 out), the chunk's softmax
+//                      partial (max, sum, unnormalised output); compressed
+//                      chunks also keep their logits
+//   dec_select         per (sequence, KV group): merged log-sum-exp and o_cmp,
+//                      group importance of every earlier block
+//   (top-k kernel)     exact top-(k-1) of those scores + the own block
+//   dec_item (phase 1) one selected block per item
+//   dec_combine        per (sequence, query head): merge the partials of the
+//                      selected and window branches, apply the gates
 #include "../../include/nsa.h"
 #include "nsa_kernels.h"
 #include "nsa_timing.h"
@@ -24,7 +28,6 @@ namespace nsa {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kCmpChunk = 128;     // compressed blocks per dec_cmp workgroup
 constexpr int kDecMaxBlk = 8192;
 constexpr int kDecMaxK = 64;
 
@@ -32,297 +35,219 @@ struct DecPlan {
   int batch = 0, L = 0, hq = 0, hkv = 0, d = 0, G = 0, k = 0, w = 0;
   int n_blk = 0, n_chunk = 0, n_win = 0, n_items = 0;
   float scale = 0.f;
-  size_t off_logits = 0, off_cmp = 0, off_ocmp = 0, off_fine = 0, off_sel = 0, off_lse = 0, total = 0;
+  size_t off_logits = 0, off_scores = 0, off_cmp = 0, off_ocmp = 0, off_fine = 0, off_sel = 0, total = 0;
 };
 
-__device__ __forceinline__ float block_reduce_max(float v, float *red) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  __syncthreads();
-  if (lane == 0) red[wv] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, red[i]);
-  return r;
+  return v;
 }
 
-__device__ __forceinline__ float block_reduce_sum(float v, float *red) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  __syncthreads();
-  if (lane == 0) red[wv] = v;
-  __syncthreads();
-  float r = 0.f;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r += red[i];
-  return r;
+  return v;
 }
 
-// ------------------------------------------------------------------ dec_cmp
+// ------------------------------------------------------------------ dec_item
+// One wave, one item of up to 64 keys (rows key0 .. key0+nk-1 of a
+// [Bt, rows, Hkv, D] cache). S^T = K Q^T on the matrix cores: a 16-column
+// tile holds the group's G query heads (zero columns past G); lane l owns
+// head l % 16 and keys 16 kt + 4 (l / 16) + i. P goes through LDS to the
+// output product, which runs on the vector units: lane l accumulates dims
+// 8 (l % DC) .. +7 over its group of rows, then lanes sharing dims are summed.
 template <int D, int G>
-__global__ __launch_bounds__(kDecThreads) void dec_cmp_kernel(DecodeParams p) {
-  __shared__ float qs[G][D];
-  __shared__ float ps[G][kCmpChunk];
-  __shared__ float red[kDecThreads / 64];
-  const int tid = threadIdx.x;
-  const int c = blockIdx.x % p.n_chunk;
-  const int g = (blockIdx.x / p.n_chunk) % p.hkv;
-  const int bi = blockIdx.x / (p.n_chunk * p.hkv);
-  const int b0 = c * kCmpChunk;
-  const int nb = min(kCmpChunk, p.n_blk - b0);
-  for (int i = tid; i < G * D; i += kDecThreads)
-    qs[i / D][i % D] = bfbits2f(p.q[((int64_t)bi * p.hq + g * G + i / D) * D + i % D]);
-  __syncthreads();
-  // logits: one compressed block per thread
-  if (tid < nb) {
-    const uint16_t *kr = p.kc + (((int64_t)bi * p.n_blk + b0 + tid) * p.hkv + g) * D;
-    float acc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.f;
-    for (int i = 0; i < D; i += 8) {
-      const u16x8 x = *reinterpret_cast<const u16x8 *>(kr + i);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kv = bfbits2f(x[e]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] += kv * qs[h][i + e];
+__global__ __launch_bounds__(64) void dec_item_kernel(DecodeParams p, int phase) {
+  constexpr int DS = D / 32, DC = D / 8, RG = 64 / DC, RPG = kBlk / RG;
+  __shared__ __attribute__((aligned(16))) float pl[kBlk][16];
+  const int lane = threadIdx.x, row = lane & 15, grp = lane >> 4;
+  const int n_it = phase == 0 ? p.n_chunk + p.n_win : p.topk;
+  const int it = (int)(blockIdx.x % n_it);
+  const int g = (int)((blockIdx.x / n_it) % p.hkv);
+  const int bi = (int)(blockIdx.x / ((unsigned)n_it * p.hkv));
+  const uint16_t *kb = p.kcache, *vb = p.vcache;
+  int nrows = p.L, key0 = 0, nk = 0;
+  bool is_cmp = false;
+  float *dst;
+  int64_t hstride;  // floats between consecutive heads' partials
+  if (phase == 0 && it < p.n_chunk) {
+    kb = p.kc;
+    vb = p.vc;
+    nrows = p.n_blk;
+    key0 = it * kBlk;
+    nk = min(kBlk, p.n_blk - key0);
+    is_cmp = true;
+    hstride = (int64_t)p.n_chunk * (D + 2);
+    dst = p.cmp_part + ((int64_t)bi * p.hq + g * G) * hstride + (int64_t)it * (D + 2);
+  } else {
+    int slot;
+    if (phase == 0) {
+      const int j = it - p.n_chunk;
+      key0 = p.L - p.window + j * kBlk;
+      nk = min(kBlk, p.L - key0);
+      slot = p.topk + j;
+    } else {
+      const int b = p.sel[((int64_t)bi * p.hkv + g) * p.topk + it];
+      if (b >= 0) {
+        key0 = b * kBlk;
+        nk = kBlk;
       }
+      slot = it;
     }
+    hstride = (int64_t)p.n_items * (D + 2);
+    dst = p.fine_part + ((int64_t)bi * p.hq + g * G) * hstride + (int64_t)slot * (D + 2);
+  }
+  if (nk <= 0) {  // an unused selection slot
+    if (lane < G) {
+      dst[lane * hstride] = -INFINITY;
+      dst[lane * hstride + 1] = 0.f;
+    }
+    return;
+  }
+  const int64_t rs = (int64_t)p.hkv * D;  // elements between consecutive rows
+  const int64_t r0 = (((int64_t)bi * nrows + key0) * p.hkv + g) * D;
+  const uint16_t *kr = kb + r0, *vr = vb + r0;
+  // every load of the item is issued up front; rows past nk re-read the
+  // last row (their scores are masked, their probabilities are zero)
+  u16x8 kf[4][DS];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int key = min(16 * kt + row, nk - 1);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) kf[kt][ds] = *reinterpret_cast<const u16x8 *>(kr + key * rs + 32 * ds + 8 * grp);
+  }
+  u16x8 qf[DS];
+  {
+    const uint16_t *qr = p.q + ((int64_t)bi * p.hq + g * G + (row < G ? row : 0)) * D + 8 * grp;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[ds] = row < G ? *reinterpret_cast<const u16x8 *>(qr + 32 * ds) : zero8();
+  }
+  const int dc = lane % DC, rg = lane / DC;
+  u16x8 vv[RPG];
+#pragma unroll
+  for (int r = 0; r < RPG; ++r) {
+    const int key = min(rg * RPG + r, nk - 1);
+    vv[r] = *reinterpret_cast<const u16x8 *>(vr + key * rs + 8 * dc);
+  }
+
+  f32x4 s[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    s[kt] = zero4();
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) s[kt] = mfma_bf16(kf[kt][ds], qf[ds], s[kt]);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 16 * kt + 4 * grp + i;
+      s[kt][i] = key < nk ? s[kt][i] * p.sl2 : -INFINITY;
+      mx = fmaxf(mx, s[kt][i]);
+    }
+  if (is_cmp && row < G) {  // logits of the compressed blocks, for the importance scores
+    float *lg = p.logits + ((int64_t)bi * p.hq + g * G + row) * p.n_blk + key0;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * kt + 4 * grp + i;
+        if (key < nk) lg[key] = s[kt][i];
+      }
+  }
+  const float m = grp_max(mx);  // key 0 is always valid: m is finite
+  float ls = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(s[kt][i] - m);
+      pl[16 * kt + 4 * grp + i][row] = pv;
+      ls += pv;
+    }
+  const float l = grp_sum(ls);
+  __syncthreads();
+
+  float o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPG; ++r) {
+    const int j = rg * RPG + r;
+    float pj[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) pj[h] = pl[j][h];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = bfbits2f(vv[r][e]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) o[h][e] = fmaf(pj[h], v, o[h][e]);
+    }
+  }
+#pragma unroll
+  for (int off = DC; off < 64; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], off);
+  if (rg == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float s = acc[h] * p.sl2;
-      ps[h][tid] = s;
-      p.logits[((int64_t)bi * p.hq + g * G + h) * p.n_blk + b0 + tid] = s;
+      f32x4 *d4 = reinterpret_cast<f32x4 *>(dst + h * hstride + 2 + 8 * dc);
+      d4[0] = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+      d4[1] = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
     }
   }
-  __syncthreads();
-  // chunk softmax partial per head
-  float m[G], l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = block_reduce_max(tid < nb ? ps[h][tid] : -INFINITY, red);
-    const float e = tid < nb ? exp2f(ps[h][tid] - m[h]) : 0.f;
-    __syncthreads();
-    if (tid < nb) ps[h][tid] = e;
-    l[h] = block_reduce_sum(e, red);
-  }
-  __syncthreads();
-  // unnormalised o over the chunk: thread (dim, half of the blocks)
-  const int dim = tid % D, part = tid / D, nparts = kDecThreads / D;
-  float o[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) o[h] = 0.f;
-  for (int b = part; b < nb; b += nparts) {
-    const float vv = bfbits2f(p.vc[(((int64_t)bi * p.n_blk + b0 + b) * p.hkv + g) * D + dim]);
-#pragma unroll
-    for (int h = 0; h < G; ++h) o[h] += ps[h][b] * vv;
-  }
-  __shared__ float op[kDecThreads / 64 * 64][G];
-  if (nparts > 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) op[tid][h] = o[h];
-    __syncthreads();
-    if (part == 0)
-      for (int q = 1; q < nparts; ++q)
-#pragma unroll
-        for (int h = 0; h < G; ++h) o[h] += op[q * D + dim][h];
-  }
-  if (part == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float *dst = p.cmp_part + (((int64_t)bi * p.hq + g * G + h) * p.n_chunk + c) * (D + 2);
-      dst[2 + dim] = o[h];
-      if (dim == 0) { dst[0] = m[h]; dst[1] = l[h]; }
-    }
+  if (lane < G) {
+    dst[lane * hstride] = m;
+    dst[lane * hstride + 1] = l;
   }
 }
 
 // --------------------------------------------------------------- dec_select
+// Per (sequence, KV group): merge the compressed chunks' partials into each
+// head's log-sum-exp and o_cmp, then score every earlier block (sum over the
+// group's heads of the normalised probability) for the top-k kernel.
 template <int D, int G>
 __global__ __launch_bounds__(kDecThreads) void dec_select_kernel(DecodeParams p) {
-  __shared__ float sc[kDecMaxBlk];
   __shared__ float lse2s[G];
-  __shared__ uint32_t hist[256];
-  __shared__ float red[kDecThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = blockIdx.x % p.hkv, bi = blockIdx.x / p.hkv;
-  // merge the chunk partials: lse and o_cmp per head
-  for (int h = 0; h < G; ++h) {
+  for (int h = wv; h < G; h += kDecThreads / 64) {
     const int64_t hr = (int64_t)bi * p.hq + g * G + h;
     const float *part = p.cmp_part + hr * p.n_chunk * (D + 2);
     float M = -INFINITY;
-    for (int c = 0; c < p.n_chunk; ++c) M = fmaxf(M, part[c * (D + 2)]);
+    for (int c = lane; c < p.n_chunk; c += 64) M = fmaxf(M, part[(int64_t)c * (D + 2)]);
+    M = wave_max(M);
     float L = 0.f;
-    for (int c = 0; c < p.n_chunk; ++c) L += part[c * (D + 2) + 1] * exp2f(part[c * (D + 2)] - M);
-    if (tid < D) {
+    for (int c = lane; c < p.n_chunk; c += 64) L += part[(int64_t)c * (D + 2) + 1] * exp2f(part[(int64_t)c * (D + 2)] - M);
+    L = wave_sum(L);
+    const float inv = 1.f / L;
+    for (int d = lane; d < D; d += 64) {
       float o = 0.f;
-      for (int c = 0; c < p.n_chunk; ++c) o += part[c * (D + 2) + 2 + tid] * exp2f(part[c * (D + 2)] - M);
-      p.ocmp[hr * D + tid] = o / L;
+#pragma unroll 8
+      for (int c = 0; c < p.n_chunk; ++c)
+        o += part[(int64_t)c * (D + 2) + 2 + d] * exp2f(part[(int64_t)c * (D + 2)] - M);
+      p.ocmp[hr * D + d] = o * inv;
     }
-    if (tid == 0) {
+    if (lane == 0) {
       lse2s[h] = M + log2f(L);
       if (p.lse) p.lse[hr] = (M + log2f(L)) * (1.0f / kLog2e);
     }
   }
   __syncthreads();
-  // group importance of every candidate block (all but the query's own)
   const int n_cand = p.n_blk - 1;
+  float *sc = p.scores + ((int64_t)bi * p.hkv + g) * p.n_blk;
+  const float *lg = p.logits + ((int64_t)bi * p.hq + g * G) * p.n_blk;
   for (int b = tid; b < n_cand; b += kDecThreads) {
     float s = 0.f;
-    for (int h = 0; h < G; ++h)
-      s += exp2f(p.logits[((int64_t)bi * p.hq + g * G + h) * p.n_blk + b] - lse2s[h]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) s += exp2f(lg[(int64_t)h * p.n_blk + b] - lse2s[h]);
     sc[b] = s;
-  }
-  __syncthreads();
-  int32_t *out = p.sel + ((int64_t)bi * p.hkv + g) * p.topk;
-  const int need = p.topk - 1;
-  if (n_cand <= need) {
-    for (int i = tid; i < p.topk; i += kDecThreads)
-      out[i] = i < n_cand ? i : (i == n_cand ? n_cand : -1);
-    return;
-  }
-  if (wv != 0) return;  // wave 0 selects; no barriers follow except the wave's own
-  // exact radix select of the need-th largest score (key = bits + 1)
-  uint32_t prefix = 0, pmask = 0;
-  int rem = need;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = lane; i < 256; i += 64) hist[i] = 0;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    for (int b = lane; b < n_cand; b += 64) {
-      const uint32_t key = __float_as_uint(sc[b]) + 1u;
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    uint32_t cc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cc[i] = hist[255 - 4 * lane - i];
-    const uint32_t tot = cc[0] + cc[1] + cc[2] + cc[3];
-    uint32_t incl = tot;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    const uint64_t hit = __ballot(incl >= (uint32_t)rem);
-    const int lt = __builtin_ctzll(hit);
-    uint32_t digit = 0, before = 0;
-    if (lane == lt) {
-      uint32_t cum = incl - tot;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (cum + cc[i] >= (uint32_t)rem) { digit = 255 - 4 * lane - i; before = cum; break; }
-        cum += cc[i];
-      }
-    }
-    digit = __shfl(digit, lt);
-    before = __shfl(before, lt);
-    rem -= (int)before;
-    prefix |= digit << shift;
-    pmask |= 255u << shift;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-  }
-  int pos = 0, eq_taken = 0;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < n_cand; base += 64) {
-    const int b = base + lane;
-    const uint32_t key = b < n_cand ? __float_as_uint(sc[b]) + 1u : 0u;
-    const bool gt = key > prefix, eq = key == prefix;
-    const uint64_t eqb = __ballot(eq);
-    const bool eq_take = eq && (eq_taken + __popcll(eqb & below) < rem);
-    const bool take = gt || eq_take;
-    const uint64_t tb = __ballot(take);
-    if (take) out[pos + __popcll(tb & below)] = b;
-    pos += __popcll(tb);
-    eq_taken += __popcll(__ballot(eq_take));
-  }
-  if (lane == 0) out[need] = n_cand;  // the query's own block
-}
-
-// ----------------------------------------------------------------- dec_fine
-template <int D, int G>
-__global__ __launch_bounds__(kDecThreads) void dec_fine_kernel(DecodeParams p) {
-  __shared__ float qs[G][D];
-  __shared__ float ks[kBlk][D + 1];
-  __shared__ float ps[G][kBlk];
-  __shared__ float red[kDecThreads / 64];
-  const int tid = threadIdx.x;
-  const int item = blockIdx.x % p.n_items;
-  const int g = (blockIdx.x / p.n_items) % p.hkv;
-  const int bi = blockIdx.x / (p.n_items * p.hkv);
-  // keys of this item: a selected block, or a 64-key slice of the window
-  int key0 = 0, nk = 0;
-  if (item < p.topk) {
-    const int b = p.sel[((int64_t)bi * p.hkv + g) * p.topk + item];
-    if (b >= 0) { key0 = b * kBlk; nk = kBlk; }
-  } else {
-    key0 = p.L - p.window + (item - p.topk) * kBlk;
-    nk = min(kBlk, p.L - key0);
-  }
-  float *dst_base = p.fine_part + ((int64_t)bi * p.hq + g * G) * p.n_items * (D + 2);
-  if (nk <= 0) {  // empty item
-    for (int i = tid; i < G; i += kDecThreads) {
-      float *dst = dst_base + ((int64_t)i * p.n_items + item) * (D + 2);
-      dst[0] = -INFINITY;
-      dst[1] = 0.f;
-    }
-    return;
-  }
-  for (int i = tid; i < G * D; i += kDecThreads)
-    qs[i / D][i % D] = bfbits2f(p.q[((int64_t)bi * p.hq + g * G + i / D) * D + i % D]);
-  const int64_t row0 = ((int64_t)bi * p.L + key0) * p.hkv + g;
-  for (int i = tid; i < nk * D; i += kDecThreads)
-    ks[i / D][i % D] = bfbits2f(p.kcache[(row0 + (int64_t)(i / D) * p.hkv) * D + i % D]);
-  __syncthreads();
-  for (int i = tid; i < G * kBlk; i += kDecThreads) {
-    const int h = i / kBlk, j = i % kBlk;
-    float s = -INFINITY;
-    if (j < nk) {
-      float acc = 0.f;
-      for (int e = 0; e < D; ++e) acc += qs[h][e] * ks[j][e];
-      s = acc * p.sl2;
-    }
-    ps[h][j] = s;
-  }
-  __syncthreads();
-  float m[G], l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = block_reduce_max(tid < kBlk ? ps[h][tid] : -INFINITY, red);
-    const float e = (tid < kBlk && tid < nk) ? exp2f(ps[h][tid] - m[h]) : 0.f;
-    __syncthreads();
-    if (tid < kBlk) ps[h][tid] = e;
-    l[h] = block_reduce_sum(e, red);
-  }
-  __syncthreads();
-  const int dim = tid % D, part = tid / D, nparts = kDecThreads / D;
-  float o[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) o[h] = 0.f;
-  for (int j = part; j < nk; j += nparts) {
-    const float vv = bfbits2f(p.vcache[(row0 + (int64_t)j * p.hkv) * D + dim]);
-#pragma unroll
-    for (int h = 0; h < G; ++h) o[h] += ps[h][j] * vv;
-  }
-  __shared__ float op[kDecThreads][G];
-  if (nparts > 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) op[tid][h] = o[h];
-    __syncthreads();
-    if (part == 0)
-      for (int q = 1; q < nparts; ++q)
-#pragma unroll
-        for (int h = 0; h < G; ++h) o[h] += op[q * D + dim][h];
-  }
-  if (part == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float *dst = dst_base + ((int64_t)h * p.n_items + item) * (D + 2);
-      dst[2 + dim] = o[h];
-      if (dim == 0) { dst[0] = m[h]; dst[1] = l[h]; }
-    }
   }
 }
 
@@ -333,17 +258,19 @@ __global__ __launch_bounds__(D) void dec_combine_kernel(DecodeParams p) {
   const int d = threadIdx.x;
   const float *part = p.fine_part + (int64_t)hr * p.n_items * (D + 2);
   float res[2];
+#pragma unroll
   for (int br = 0; br < 2; ++br) {  // 0: selected blocks, 1: window
     const int i0 = br == 0 ? 0 : p.topk, i1 = br == 0 ? p.topk : p.n_items;
     float M = -INFINITY;
-    for (int i = i0; i < i1; ++i) M = fmaxf(M, part[i * (D + 2)]);
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) M = fmaxf(M, part[(int64_t)i * (D + 2)]);
     float L = 0.f, o = 0.f;
+#pragma unroll 8
     for (int i = i0; i < i1; ++i) {
-      const float m = part[i * (D + 2)];
-      if (m == -INFINITY) continue;
-      const float w = exp2f(m - M);
-      L += w * part[i * (D + 2) + 1];
-      o += w * part[i * (D + 2) + 2 + d];
+      const float m = part[(int64_t)i * (D + 2)];
+      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      L += w * part[(int64_t)i * (D + 2) + 1];
+      o += w * part[(int64_t)i * (D + 2) + 2 + d];
     }
     res[br] = o / L;
   }
@@ -354,19 +281,27 @@ __global__ __launch_bounds__(D) void dec_combine_kernel(DecodeParams p) {
 
 template <int D, int G>
 hipError_t run_decode(const DecodeParams &p, hipStream_t st) {
+  const unsigned pairs = (unsigned)p.batch * p.hkv;
   {
-    Timed t("dec_cmp", st);
-    hipLaunchKernelGGL((dec_cmp_kernel<D, G>), dim3(p.batch * p.hkv * p.n_chunk), dim3(kDecThreads), 0, st, p);
+    Timed t("dec_item_cmp_win", st);
+    hipLaunchKernelGGL((dec_item_kernel<D, G>), dim3(pairs * (p.n_chunk + p.n_win)), dim3(64), 0, st, p, 0);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   {
     Timed t("dec_select", st);
-    hipLaunchKernelGGL((dec_select_kernel<D, G>), dim3(p.batch * p.hkv), dim3(kDecThreads), 0, st, p);
+    hipLaunchKernelGGL((dec_select_kernel<D, G>), dim3(pairs), dim3(kDecThreads), 0, st, p);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   {
-    Timed t("dec_fine", st);
-    hipLaunchKernelGGL((dec_fine_kernel<D, G>), dim3(p.batch * p.hkv * p.n_items), dim3(kDecThreads), 0, st, p);
+    Timed t("dec_topk", st);
+    TopkParams tp{p.scores, p.sel, (int)pairs, p.hkv, p.topk};
+    tp.row_stride = p.n_blk;
+    tp.fixed_f = p.n_blk - 1;
+    if (launch_topk(tp, p.n_blk - 1, st) != hipSuccess) return hipErrorLaunchFailure;
+  }
+  {
+    Timed t("dec_item_sel", st);
+    hipLaunchKernelGGL((dec_item_kernel<D, G>), dim3(pairs * p.topk), dim3(64), 0, st, p, 1);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   {
@@ -399,7 +334,7 @@ nsa_status plan_decode(const nsa_decode_desc *ds, DecPlan &pl) {
   if (pl.k > kDecMaxK || pl.w > pl.L) return NSA_ERR_UNSUPPORTED;
   pl.n_blk = pl.L / kBlk;
   if (pl.n_blk > kDecMaxBlk) return NSA_ERR_UNSUPPORTED;
-  pl.n_chunk = (pl.n_blk + kCmpChunk - 1) / kCmpChunk;
+  pl.n_chunk = (pl.n_blk + kBlk - 1) / kBlk;
   pl.n_win = (pl.w + kBlk - 1) / kBlk;
   pl.n_items = pl.k + pl.n_win;
   pl.scale = ds->scale > 0.f ? ds->scale : 1.0f / sqrtf((float)pl.d);
@@ -407,6 +342,7 @@ nsa_status plan_decode(const nsa_decode_desc *ds, DecPlan &pl) {
   auto take = [&](size_t bytes) { const size_t o = off; off = (off + bytes + 255) / 256 * 256; return o; };
   const size_t BH = (size_t)pl.batch * pl.hq;
   pl.off_logits = take(sizeof(float) * BH * pl.n_blk);
+  pl.off_scores = take(sizeof(float) * (size_t)pl.batch * pl.hkv * pl.n_blk);
   pl.off_cmp = take(sizeof(float) * BH * pl.n_chunk * (pl.d + 2));
   pl.off_ocmp = take(sizeof(float) * BH * pl.d);
   pl.off_fine = take(sizeof(float) * BH * pl.n_items * (pl.d + 2));
@@ -486,6 +422,7 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
   p.sel = sel_idx_out ? sel_idx_out : reinterpret_cast<int32_t *>(ws + pl.off_sel);
   p.lse = lse_out;
   p.logits = reinterpret_cast<float *>(ws + pl.off_logits);
+  p.scores = reinterpret_cast<float *>(ws + pl.off_scores);
   p.cmp_part = reinterpret_cast<float *>(ws + pl.off_cmp);
   p.ocmp = reinterpret_cast<float *>(ws + pl.off_ocmp);
   p.fine_part = reinterpret_cast<float *>(ws + pl.off_fine);
@@ -497,6 +434,7 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
   p.window = pl.w;
   p.n_blk = pl.n_blk;
   p.n_chunk = pl.n_chunk;
+  p.n_win = pl.n_win;
   p.n_items = pl.n_items;
   p.sl2 = pl.scale * kLog2e;
   if (launch_decode(p, pl.d, pl.G, static_cast<hipStream_t>(stream)) != hipSuccess) return NSA_ERR_HIP;

@@ -41,11 +41,22 @@ __global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
   __shared__ uint32_t hist[256];
   const int lane = threadIdx.x;
   const int64_t wid = blockIdx.x;
-  const int t = (int)(wid / p.hkv);
-  const int g = (int)(wid % p.hkv);
-  if (t >= p.n_vis) return;
-  const int f = t / kBlk;  // own block == number of candidate blocks
-  int32_t *out = p.sel + ((int64_t)t * p.hkv + g) * p.k;
+  int f;  // own block == number of candidate blocks
+  int32_t *out;
+  const float *row;
+  if (p.row_stride > 0) {
+    if (wid >= p.n_vis) return;
+    f = p.fixed_f;
+    out = p.sel + wid * p.k;
+    row = p.gs + wid * p.row_stride;
+  } else {
+    const int t = (int)(wid / p.hkv);
+    const int g = (int)(wid % p.hkv);
+    if (t >= p.n_vis) return;
+    f = t / kBlk;
+    out = p.sel + ((int64_t)t * p.hkv + g) * p.k;
+    row = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + (t - f * kBlk)) * f;
+  }
   const int need = p.k - 1;
 
   if (f <= need) {  // every candidate is kept
@@ -53,7 +64,6 @@ __global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
     return;
   }
 
-  const float *row = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + (t - f * kBlk)) * f;
   // key = bits + 1 for candidates (so 0.0f still beats padding), 0 otherwise
   uint32_t key[NPL];
 #pragma unroll
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
 
 template <int NPL>
 hipError_t run(const TopkParams &p, hipStream_t st) {
-  const int64_t n = (int64_t)p.n_vis * p.hkv;
+  const int64_t n = p.row_stride > 0 ? (int64_t)p.n_vis : (int64_t)p.n_vis * p.hkv;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((topk_kernel<NPL>), dim3((unsigned)n), dim3(64 * kWavesPerWG), 0, st, p);
   return hipGetLastError();
