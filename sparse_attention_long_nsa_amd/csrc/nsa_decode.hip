@@ -14,13 +14,16 @@
 //                      partial (max, sum, unnormalised output); compressed
 //                      chunks also keep their logits
 //   dec_select         per (sequence, KV group): merged log-sum-exp and o_cmp,
-//                      group importance of every earlier block
-//   (top-k kernel)     exact top-(k-1) of those scores + the own block
+//                      group importance of every earlier block, exact
+//                      top-(k-1) of those scores + the own block
 //   dec_item (phase 1) one selected block per item
 //   dec_combine        per (sequence, query head): merge the partials of the
 //                      selected and window branches, apply the gates
+#include <type_traits>
+
 #include "../../include/nsa.h"
 #include "nsa_kernels.h"
+#include "nsa_select.h"
 #include "nsa_timing.h"
 
 namespace nsa {
@@ -35,7 +38,7 @@ struct DecPlan {
   int batch = 0, L = 0, hq = 0, hkv = 0, d = 0, G = 0, k = 0, w = 0;
   int n_blk = 0, n_chunk = 0, n_win = 0, n_items = 0;
   float scale = 0.f;
-  size_t off_logits = 0, off_scores = 0, off_cmp = 0, off_ocmp = 0, off_fine = 0, off_sel = 0, total = 0;
+  size_t off_logits = 0, off_cmp = 0, off_ocmp = 0, off_fine = 0, off_sel = 0, total = 0;
 };
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -51,17 +54,23 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ------------------------------------------------------------------ dec_item
-// One wave, one item of up to 64 keys (rows key0 .. key0+nk-1 of a
-// [Bt, rows, Hkv, D] cache). S^T = K Q^T on the matrix cores: a 16-column
-// tile holds the group's G query heads (zero columns past G); lane l owns
-// head l % 16 and keys 16 kt + 4 (l / 16) + i. P goes through LDS to the
-// output product, which runs on the vector units: lane l accumulates dims
-// 8 (l % DC) .. +7 over its group of rows, then lanes sharing dims are summed.
+// One workgroup of four waves per item of up to 64 keys (rows key0 ..
+// key0+nk-1 of a [Bt, rows, Hkv, D] cache); wave w takes keys 16w .. 16w+15.
+// S^T = K Q^T on the matrix cores: a 16-column tile holds the group's G query
+// heads (zero columns past G); lane l owns head l % 16 and keys
+// 16w + 4 (l / 16) + i. The item's per-head max and sum combine through LDS.
+// The output product runs on the vector units: lane l owns dims
+// DL l .. DL l + DL - 1 (DL = D / 64) over the wave's 16 rows, so each row of
+// V is one coalesced load across the wave; the four waves' sums meet in LDS.
+constexpr int kItemWaves = 4;
+
 template <int D, int G>
-__global__ __launch_bounds__(64) void dec_item_kernel(DecodeParams p, int phase) {
-  constexpr int DS = D / 32, DC = D / 8, RG = 64 / DC, RPG = kBlk / RG;
+__global__ __launch_bounds__(64 * kItemWaves) void dec_item_kernel(DecodeParams p, int phase) {
+  constexpr int DS = D / 32, DL = D / 64, KW = kBlk / kItemWaves;
   __shared__ __attribute__((aligned(16))) float pl[kBlk][16];
-  const int lane = threadIdx.x, row = lane & 15, grp = lane >> 4;
+  __shared__ float red[2][kItemWaves][16];
+  __shared__ __attribute__((aligned(16))) float osum[kItemWaves][G][D];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, row = lane & 15, grp = lane >> 4;
   const int n_it = phase == 0 ? p.n_chunk + p.n_win : p.topk;
   const int it = (int)(blockIdx.x % n_it);
   const int g = (int)((blockIdx.x / n_it) % p.hkv);
@@ -98,24 +107,24 @@ __global__ __launch_bounds__(64) void dec_item_kernel(DecodeParams p, int phase)
     hstride = (int64_t)p.n_items * (D + 2);
     dst = p.fine_part + ((int64_t)bi * p.hq + g * G) * hstride + (int64_t)slot * (D + 2);
   }
-  if (nk <= 0) {  // an unused selection slot
-    if (lane < G) {
-      dst[lane * hstride] = -INFINITY;
-      dst[lane * hstride + 1] = 0.f;
+  if (nk <= 0) {  // an unused selection slot (uniform over the workgroup)
+    if (tid < G) {
+      dst[tid * hstride] = -INFINITY;
+      dst[tid * hstride + 1] = 0.f;
     }
     return;
   }
   const int64_t rs = (int64_t)p.hkv * D;  // elements between consecutive rows
   const int64_t r0 = (((int64_t)bi * nrows + key0) * p.hkv + g) * D;
   const uint16_t *kr = kb + r0, *vr = vb + r0;
-  // every load of the item is issued up front; rows past nk re-read the
-  // last row (their scores are masked, their probabilities are zero)
-  u16x8 kf[4][DS];
+  const int j0 = KW * wv;  // this wave's first key
+  // every load is issued up front; rows past nk re-read the last row (their
+  // scores are masked, their probabilities are zero)
+  u16x8 kf[DS];
+  {
+    const int key = min(j0 + row, nk - 1);
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int key = min(16 * kt + row, nk - 1);
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) kf[kt][ds] = *reinterpret_cast<const u16x8 *>(kr + key * rs + 32 * ds + 8 * grp);
+    for (int ds = 0; ds < DS; ++ds) kf[ds] = *reinterpret_cast<const u16x8 *>(kr + key * rs + 32 * ds + 8 * grp);
   }
   u16x8 qf[DS];
   {
@@ -123,131 +132,157 @@ __global__ __launch_bounds__(64) void dec_item_kernel(DecodeParams p, int phase)
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[ds] = row < G ? *reinterpret_cast<const u16x8 *>(qr + 32 * ds) : zero8();
   }
-  const int dc = lane % DC, rg = lane / DC;
-  u16x8 vv[RPG];
+  using VT = typename std::conditional<DL == 2, uint32_t, uint16_t>::type;  // DL bf16 values
+  VT vv[KW];
 #pragma unroll
-  for (int r = 0; r < RPG; ++r) {
-    const int key = min(rg * RPG + r, nk - 1);
-    vv[r] = *reinterpret_cast<const u16x8 *>(vr + key * rs + 8 * dc);
-  }
+  for (int j = 0; j < KW; ++j) vv[j] = *reinterpret_cast<const VT *>(vr + min(j0 + j, nk - 1) * rs + DL * lane);
 
-  f32x4 s[4];
+  f32x4 s = zero4();
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    s[kt] = zero4();
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) s[kt] = mfma_bf16(kf[kt][ds], qf[ds], s[kt]);
-  }
+  for (int ds = 0; ds < DS; ++ds) s = mfma_bf16(kf[ds], qf[ds], s);
   float mx = -INFINITY;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 16 * kt + 4 * grp + i;
-      s[kt][i] = key < nk ? s[kt][i] * p.sl2 : -INFINITY;
-      mx = fmaxf(mx, s[kt][i]);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int key = j0 + 4 * grp + i;
+    s[i] = key < nk ? s[i] * p.sl2 : -INFINITY;
+    mx = fmaxf(mx, s[i]);
+  }
   if (is_cmp && row < G) {  // logits of the compressed blocks, for the importance scores
     float *lg = p.logits + ((int64_t)bi * p.hq + g * G + row) * p.n_blk + key0;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * kt + 4 * grp + i;
-        if (key < nk) lg[key] = s[kt][i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int key = j0 + 4 * grp + i;
+      if (key < nk) lg[key] = s[i];
+    }
   }
-  const float m = grp_max(mx);  // key 0 is always valid: m is finite
+  mx = grp_max(mx);
+  if (lane < 16) red[0][wv][lane] = mx;
+  __syncthreads();
+  // key 0 is always valid: the item's max is finite
+  const float m = fmaxf(fmaxf(red[0][0][row], red[0][1][row]), fmaxf(red[0][2][row], red[0][3][row]));
   float ls = 0.f;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(s[kt][i] - m);
-      pl[16 * kt + 4 * grp + i][row] = pv;
-      ls += pv;
-    }
-  const float l = grp_sum(ls);
+  for (int i = 0; i < 4; ++i) {
+    const float pv = __builtin_amdgcn_exp2f(s[i] - m);
+    pl[j0 + 4 * grp + i][row] = pv;
+    ls += pv;
+  }
+  ls = grp_sum(ls);
+  if (lane < 16) red[1][wv][lane] = ls;
   __syncthreads();
 
-  float o[G][8];
+  float o[G][DL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+    for (int e = 0; e < DL; ++e) o[h][e] = 0.f;
 #pragma unroll
-  for (int r = 0; r < RPG; ++r) {
-    const int j = rg * RPG + r;
-    float pj[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) pj[h] = pl[j][h];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = bfbits2f(vv[r][e]);
-#pragma unroll
-      for (int h = 0; h < G; ++h) o[h][e] = fmaf(pj[h], v, o[h][e]);
+  for (int j = 0; j < KW; ++j) {
+    float v[DL];
+    if constexpr (DL == 2) {
+      v[0] = __uint_as_float(vv[j] << 16);
+      v[1] = __uint_as_float(vv[j] & 0xffff0000u);
+    } else {
+      v[0] = bfbits2f(vv[j]);
     }
-  }
-#pragma unroll
-  for (int off = DC; off < 64; off <<= 1)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], off);
-  if (rg == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      f32x4 *d4 = reinterpret_cast<f32x4 *>(dst + h * hstride + 2 + 8 * dc);
-      d4[0] = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
-      d4[1] = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
+      const float pj = pl[j0 + j][h];
+#pragma unroll
+      for (int e = 0; e < DL; ++e) o[h][e] = fmaf(pj, v[e], o[h][e]);
     }
   }
-  if (lane < G) {
-    dst[lane * hstride] = m;
-    dst[lane * hstride + 1] = l;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < DL; ++e) osum[wv][h][DL * lane + e] = o[h][e];
+  __syncthreads();
+  for (int i = tid; i < G * D; i += 64 * kItemWaves) {
+    const int h = i / D, d = i % D;
+    dst[h * hstride + 2 + d] = (osum[0][h][d] + osum[1][h][d]) + (osum[2][h][d] + osum[3][h][d]);
+  }
+  if (tid < G) {
+    dst[tid * hstride] = m;
+    dst[tid * hstride + 1] = (red[1][0][tid] + red[1][1][tid]) + (red[1][2][tid] + red[1][3][tid]);
   }
 }
 
 // --------------------------------------------------------------- dec_select
 // Per (sequence, KV group): merge the compressed chunks' partials into each
-// head's log-sum-exp and o_cmp, then score every earlier block (sum over the
-// group's heads of the normalised probability) for the top-k kernel.
-template <int D, int G>
+// head's log-sum-exp and o_cmp, score every earlier block (sum over the
+// group's heads of the normalised probability) into LDS, and select the
+// top k-1 of them plus the own block (select_topk_row, wave 0).
+template <int D, int G, int NPL>
 __global__ __launch_bounds__(kDecThreads) void dec_select_kernel(DecodeParams p) {
+  constexpr int NO = kDecThreads - 64;             // threads of waves 1..
+  constexpr int OPT = (G * D + NO - 1) / NO;       // o_cmp outputs per thread
   __shared__ float lse2s[G];
+  __shared__ float sc[kDecMaxBlk];
+  __shared__ uint32_t hist[256];
+  __shared__ float wt[G][kDecMaxBlk / kBlk];  // chunk max, then chunk weight
+  __shared__ float ls[G][kDecMaxBlk / kBlk];  // chunk sum
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = blockIdx.x % p.hkv, bi = blockIdx.x / p.hkv;
+  const int64_t hr0 = (int64_t)bi * p.hq + g * G;
+  const int64_t hs = (int64_t)p.n_chunk * (D + 2);  // floats per head of partials
+  const float *part = p.cmp_part + hr0 * hs;
+  // every chunk's (max, sum) of every head in one round of loads
+  for (int i = tid; i < G * p.n_chunk; i += kDecThreads) {
+    const int h = i / p.n_chunk, c = i % p.n_chunk;
+    wt[h][c] = part[h * hs + (int64_t)c * (D + 2)];
+    ls[h][c] = part[h * hs + (int64_t)c * (D + 2) + 1];
+  }
+  __syncthreads();
   for (int h = wv; h < G; h += kDecThreads / 64) {
-    const int64_t hr = (int64_t)bi * p.hq + g * G + h;
-    const float *part = p.cmp_part + hr * p.n_chunk * (D + 2);
     float M = -INFINITY;
-    for (int c = lane; c < p.n_chunk; c += 64) M = fmaxf(M, part[(int64_t)c * (D + 2)]);
+    for (int c = lane; c < p.n_chunk; c += 64) M = fmaxf(M, wt[h][c]);
     M = wave_max(M);
     float L = 0.f;
-    for (int c = lane; c < p.n_chunk; c += 64) L += part[(int64_t)c * (D + 2) + 1] * exp2f(part[(int64_t)c * (D + 2)] - M);
+    for (int c = lane; c < p.n_chunk; c += 64) L += ls[h][c] * exp2f(wt[h][c] - M);
     L = wave_sum(L);
     const float inv = 1.f / L;
-    for (int d = lane; d < D; d += 64) {
-      float o = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < p.n_chunk; ++c)
-        o += part[(int64_t)c * (D + 2) + 2 + d] * exp2f(part[(int64_t)c * (D + 2)] - M);
-      p.ocmp[hr * D + d] = o * inv;
-    }
+    for (int c = lane; c < p.n_chunk; c += 64) wt[h][c] = exp2f(wt[h][c] - M) * inv;
     if (lane == 0) {
       lse2s[h] = M + log2f(L);
-      if (p.lse) p.lse[hr] = (M + log2f(L)) * (1.0f / kLog2e);
+      if (p.lse) p.lse[hr0 + h] = (M + log2f(L)) * (1.0f / kLog2e);
     }
   }
   __syncthreads();
   const int n_cand = p.n_blk - 1;
-  float *sc = p.scores + ((int64_t)bi * p.hkv + g) * p.n_blk;
   const float *lg = p.logits + ((int64_t)bi * p.hq + g * G) * p.n_blk;
+#pragma unroll 4
   for (int b = tid; b < n_cand; b += kDecThreads) {
     float s = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) s += exp2f(lg[(int64_t)h * p.n_blk + b] - lse2s[h]);
     sc[b] = s;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    select_topk_row<NPL>(sc, n_cand, p.topk, p.sel + ((int64_t)bi * p.hkv + g) * p.topk, hist, lane);
+    return;
+  }
+  {
+    // o_cmp, by waves 1.. while wave 0 selects: thread u owns outputs
+    // u + NO j (head, dim); the chunk loop is unrolled so each thread keeps
+    // many loads in flight
+    const int u = tid - 64;
+    float acc[OPT];
+    int hh[OPT], dd[OPT];
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int i = min(u + NO * j, G * D - 1);
+      hh[j] = i / D;
+      dd[j] = i % D;
+      acc[j] = 0.f;
+    }
+#pragma unroll 8
+    for (int c = 0; c < p.n_chunk; ++c)
+#pragma unroll
+      for (int j = 0; j < OPT; ++j) acc[j] += wt[hh[j]][c] * part[hh[j] * hs + (int64_t)c * (D + 2) + 2 + dd[j]];
+#pragma unroll
+    for (int j = 0; j < OPT; ++j)
+      if (u + NO * j < G * D) p.ocmp[(hr0 + hh[j]) * D + dd[j]] = acc[j];
   }
 }
 
@@ -284,24 +319,23 @@ hipError_t run_decode(const DecodeParams &p, hipStream_t st) {
   const unsigned pairs = (unsigned)p.batch * p.hkv;
   {
     Timed t("dec_item_cmp_win", st);
-    hipLaunchKernelGGL((dec_item_kernel<D, G>), dim3(pairs * (p.n_chunk + p.n_win)), dim3(64), 0, st, p, 0);
+    hipLaunchKernelGGL((dec_item_kernel<D, G>), dim3(pairs * (p.n_chunk + p.n_win)), dim3(64 * kItemWaves), 0,
+                       st, p, 0);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   {
     Timed t("dec_select", st);
-    hipLaunchKernelGGL((dec_select_kernel<D, G>), dim3(pairs), dim3(kDecThreads), 0, st, p);
+    // candidates per lane of the selecting wave: 32 covers caches of up to
+    // 2049 blocks (131,136 tokens)
+    if (p.n_blk - 1 <= 64 * 32)
+      hipLaunchKernelGGL((dec_select_kernel<D, G, 32>), dim3(pairs), dim3(kDecThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((dec_select_kernel<D, G, kDecMaxBlk / 64>), dim3(pairs), dim3(kDecThreads), 0, st, p);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   {
-    Timed t("dec_topk", st);
-    TopkParams tp{p.scores, p.sel, (int)pairs, p.hkv, p.topk};
-    tp.row_stride = p.n_blk;
-    tp.fixed_f = p.n_blk - 1;
-    if (launch_topk(tp, p.n_blk - 1, st) != hipSuccess) return hipErrorLaunchFailure;
-  }
-  {
     Timed t("dec_item_sel", st);
-    hipLaunchKernelGGL((dec_item_kernel<D, G>), dim3(pairs * p.topk), dim3(64), 0, st, p, 1);
+    hipLaunchKernelGGL((dec_item_kernel<D, G>), dim3(pairs * p.topk), dim3(64 * kItemWaves), 0, st, p, 1);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   {
@@ -342,7 +376,6 @@ nsa_status plan_decode(const nsa_decode_desc *ds, DecPlan &pl) {
   auto take = [&](size_t bytes) { const size_t o = off; off = (off + bytes + 255) / 256 * 256; return o; };
   const size_t BH = (size_t)pl.batch * pl.hq;
   pl.off_logits = take(sizeof(float) * BH * pl.n_blk);
-  pl.off_scores = take(sizeof(float) * (size_t)pl.batch * pl.hkv * pl.n_blk);
   pl.off_cmp = take(sizeof(float) * BH * pl.n_chunk * (pl.d + 2));
   pl.off_ocmp = take(sizeof(float) * BH * pl.d);
   pl.off_fine = take(sizeof(float) * BH * pl.n_items * (pl.d + 2));
@@ -422,7 +455,6 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
   p.sel = sel_idx_out ? sel_idx_out : reinterpret_cast<int32_t *>(ws + pl.off_sel);
   p.lse = lse_out;
   p.logits = reinterpret_cast<float *>(ws + pl.off_logits);
-  p.scores = reinterpret_cast<float *>(ws + pl.off_scores);
   p.cmp_part = reinterpret_cast<float *>(ws + pl.off_cmp);
   p.ocmp = reinterpret_cast<float *>(ws + pl.off_ocmp);
   p.fine_part = reinterpret_cast<float *>(ws + pl.off_fine);

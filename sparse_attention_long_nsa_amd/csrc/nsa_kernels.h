@@ -42,10 +42,6 @@ struct TopkParams {
   const float *gs;
   int32_t *sel;            // [n_vis, Hkv, k]
   int n_vis, hkv, k;
-  // row mode (row_stride > 0): row r = gs + r * row_stride holds fixed_f
-  // candidate scores, its answer goes to sel + r * k; n_vis counts the rows
-  int64_t row_stride = 0;
-  int fixed_f = 0;
 };
 
 struct SwaParams {
@@ -90,7 +86,6 @@ struct DecodeParams {
   int32_t *sel;                     // [Bt, Hkv, k]
   float *lse;                       // [Bt, Hq] or null
   float *logits;                    // workspace [Bt, Hq, n_blk] scaled log2 logits
-  float *scores;                    // workspace [Bt, Hkv, n_blk] group importance
   float *cmp_part;                  // workspace [Bt, Hq, n_chunk, d + 2] (max, sum, o)
   float *ocmp;                      // workspace [Bt, Hq, d]
   float *fine_part;                 // workspace [Bt, Hq, n_items, d + 2]

@@ -1,22 +1,8 @@
-// Top-k block selection (VideoNSA paper summary page, "Method", branch (b):
-// keep the top blocks by importance score). Readings: the query's own block
-// is always kept and counts toward k; the other k-1 are the highest-scoring
-// complete earlier blocks, ties going to the lower block index; the result
-// is emitted in ascending block order, -1 padded.
-//
-// One wave per (vision query, KV group). The wave streams the query's row of
-// group scores (frame-packed, written by the compression kernel) once into
-// registers (non-negative floats order like their bit patterns). Fast path:
-// the (k-1)-th largest of the 64 lane maxima is a lower bound T0 for the
-// (k-1)-th largest score (those lane maxima are k-1 distinct scores >= T0),
-// so every score of the answer is >= T0; when at most 64 scores reach T0 the
-// wave compacts just those (one per lane, ascending index), finds the
-// (k-1)-th largest of them, and keeps every larger one plus the lowest-index
-// ones equal to it. Both order statistics come from a bitwise search over
-// 64 lane values (32 ballot counts, mostly scalar work). Otherwise it finds
-// the (k-1)-th largest score exactly by an MSB-first radix select over all
-// scores. The chosen indices are emitted in ascending order.
+// Top-k block selection kernel: one wave per (vision query, KV group) row of
+// the frame-packed group scores written by the compression kernel. The
+// selection itself is select_topk_row.
 #include "nsa_kernels.h"
+#include "nsa_select.h"
 
 namespace nsa {
 
@@ -24,158 +10,23 @@ namespace {
 
 constexpr int kWavesPerWG = 1;  // one wave per workgroup: early exits need no barrier care
 
-// The largest T with at least `need` lanes holding v >= T (need <= lanes with
-// a nonzero v): the need-th largest of the 64 lane values. Bits MSB first.
-__device__ __forceinline__ uint32_t kth_largest_lane(uint32_t v, int need) {
-  uint32_t t = 0;
-#pragma unroll
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = t | (1u << b);
-    if (__popcll(__ballot(v >= c)) >= need) t = c;
-  }
-  return t;
-}
-
 template <int NPL>
 __global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
   __shared__ uint32_t hist[256];
   const int lane = threadIdx.x;
   const int64_t wid = blockIdx.x;
-  int f;  // own block == number of candidate blocks
-  int32_t *out;
-  const float *row;
-  if (p.row_stride > 0) {
-    if (wid >= p.n_vis) return;
-    f = p.fixed_f;
-    out = p.sel + wid * p.k;
-    row = p.gs + wid * p.row_stride;
-  } else {
-    const int t = (int)(wid / p.hkv);
-    const int g = (int)(wid % p.hkv);
-    if (t >= p.n_vis) return;
-    f = t / kBlk;
-    out = p.sel + ((int64_t)t * p.hkv + g) * p.k;
-    row = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + (t - f * kBlk)) * f;
-  }
-  const int need = p.k - 1;
-
-  if (f <= need) {  // every candidate is kept
-    for (int i = lane; i < p.k; i += 64) out[i] = i < f ? i : (i == f ? f : -1);
-    return;
-  }
-
-  // key = bits + 1 for candidates (so 0.0f still beats padding), 0 otherwise
-  uint32_t key[NPL];
-#pragma unroll
-  for (int s = 0; s < NPL; ++s) {
-    const int e = s * 64 + lane;
-    key[s] = 0u;
-    if (s * 64 < f) {  // wave-uniform; lanes past the row re-read its last entry
-      const uint32_t bits = __float_as_uint(row[min(e, f - 1)]);
-      key[s] = e < f ? bits + 1u : 0u;
-    }
-  }
-
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  {
-    uint32_t lm = 0;
-#pragma unroll
-    for (int s = 0; s < NPL; ++s) lm = max(lm, key[s]);
-    const uint32_t t0 = kth_largest_lane(lm, need);
-    int c0 = 0;
-#pragma unroll
-    for (int s = 0; s < NPL; ++s) c0 += __popcll(__ballot(key[s] >= t0));
-    if (c0 <= 64) {
-      // compact the candidates (ascending index order) into LDS
-      int base = 0;
-#pragma unroll
-      for (int s = 0; s < NPL; ++s) {
-        const bool cand = key[s] >= t0;
-        const uint64_t cb = __ballot(cand);
-        if (cand) {
-          const int q = base + __popcll(cb & below);
-          hist[q] = key[s];
-          hist[64 + q] = (uint32_t)(s * 64 + lane);
-        }
-        base += __popcll(cb);
-      }
-      __syncthreads();
-      const uint32_t ck = lane < c0 ? hist[lane] : 0u;
-      const uint32_t ci = lane < c0 ? hist[64 + lane] : 0xffffffffu;
-      // keep the candidates above the need-th largest key, then the
-      // lowest-index ones equal to it (candidates sit in ascending index order)
-      const uint32_t t1 = kth_largest_lane(ck, need);
-      const uint64_t gt = __ballot(ck > t1), eq = __ballot(ck == t1);
-      const int rest = need - __popcll(gt);
-      const bool take = (ck > t1) || (ck == t1 && __popcll(eq & below) < rest);
-      const uint64_t tb = __ballot(take);
-      if (take) out[__popcll(tb & below)] = (int32_t)ci;
-      if (lane == 0) out[need] = f;  // own block, larger than every candidate
-      return;
-    }
-  }
-
-  uint32_t prefix = 0, pmask = 0;
-  int rem = need;  // how many of the elements matching `prefix` are still wanted
-#pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = lane; i < 256; i += 64) hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < NPL; ++s)
-      if (key[s] != 0u && (key[s] & pmask) == prefix) atomicAdd(&hist[(key[s] >> shift) & 255u], 1u);
-    __syncthreads();
-    // lane L owns digits 255-4L .. 252-4L (descending)
-    uint32_t c[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
-    const uint32_t tot = c[0] + c[1] + c[2] + c[3];
-    uint32_t incl = tot;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    const uint64_t hit = __ballot(incl >= (uint32_t)rem);
-    const int lt = __ffsll((unsigned long long)hit) - 1;
-    uint32_t digit = 0, before = 0;
-    if (lane == lt) {
-      uint32_t cum = incl - tot;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (cum + c[i] >= (uint32_t)rem) { digit = 255 - 4 * lane - i; before = cum; break; }
-        cum += c[i];
-      }
-    }
-    digit = __shfl(digit, lt);
-    before = __shfl(before, lt);
-    rem -= (int)before;
-    prefix |= digit << shift;
-    pmask |= 255u << shift;
-    __syncthreads();
-  }
-
-  // keys > prefix are all kept; of the keys == prefix keep the `rem` lowest indices
-  int pos = 0, eq_taken = 0;
-#pragma unroll
-  for (int s = 0; s < NPL; ++s) {
-    const bool gt = key[s] > prefix;
-    const bool eq = key[s] == prefix;
-    const uint64_t eqb = __ballot(eq);
-    const bool eq_take = eq && (eq_taken + __popcll(eqb & below) < rem);
-    const bool take = gt || eq_take;
-    const uint64_t tb = __ballot(take);
-    if (take) out[pos + __popcll(tb & below)] = s * 64 + lane;
-    pos += __popcll(tb);
-    eq_taken += __popcll(__ballot(eq_take));
-  }
-  if (lane == 0) out[need] = f;  // own block, larger than every candidate
+  const int t = (int)(wid / p.hkv);
+  const int g = (int)(wid % p.hkv);
+  if (t >= p.n_vis) return;
+  const int f = t / kBlk;  // own block == number of candidate blocks
+  int32_t *out = p.sel + ((int64_t)t * p.hkv + g) * p.k;
+  const float *row = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + (t - f * kBlk)) * f;
+  select_topk_row<NPL>(row, f, p.k, out, hist, lane);
 }
 
 template <int NPL>
 hipError_t run(const TopkParams &p, hipStream_t st) {
-  const int64_t n = p.row_stride > 0 ? (int64_t)p.n_vis : (int64_t)p.n_vis * p.hkv;
+  const int64_t n = (int64_t)p.n_vis * p.hkv;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((topk_kernel<NPL>), dim3((unsigned)n), dim3(64 * kWavesPerWG), 0, st, p);
   return hipGetLastError();

@@ -46,6 +46,7 @@ def check(inp, name):
     DecodeShape(2, 1024, 8, 2, 128, 64, 32, 1024),   # k covers every block, window = cache
     DecodeShape(1, 128, 6, 3, 64, 64, 5, 1),         # fewer blocks than k
     DecodeShape(4, 8192 + 64, 16, 2, 128, 64, 8, 96),
+    DecodeShape(1, 2100 * 64, 8, 2, 128, 64, 16, 512),  # > 2048 candidates per row
 ])
 def test_decode_small(shape):
     check(make_decode_inputs(shape, seed=11), "decode_small")
