@@ -5,9 +5,9 @@
 //
 // Layout H: a wave owns 16 queries and up to three of the G query heads of
 // one KV group, so each K / V^T fragment read from LDS feeds up to three
-// matrix-core ops. Keys and
-// values come from the packed block tiles (PackedTile, one 64-key chunk per
-// tile) by direct global->LDS copies, issued several chunks ahead.
+// matrix-core ops. Keys and values come from the packed block tiles
+// (PackedTile, one 64-key chunk per tile) by direct global->LDS copies, one
+// chunk ahead; a single pass with an online softmax forms the output.
 #include "nsa_kernels.h"
 #include "nsa_tiles.h"
 
@@ -43,47 +43,17 @@ __device__ __forceinline__ void qk16(f32x4 (&s)[G], const uint16_t *ks, int kt,
   }
 }
 
-// Pass 1 on one staged key chunk: lane-partial (max, sum) of the scaled
-// logits in log2 units, with the lazily moved max. Keys klo..khi of the
-// chunk (shifted by this lane's 4*(l/16)) are valid for the lane's row.
+// One staged (K, V^T) chunk for this lane's query row and G heads, online,
+// in two halves of 32 keys: scores of the half, the row's running max moved
+// lazily (only when a new max exceeds it by kSlack, then the accumulators are
+// rescaled), probabilities against that max, then the PV product. Keys
+// klo..khi of the chunk (shifted by this lane's 4*(l/16)) are valid for the
+// lane's row.
 template <int D, int G, bool F16>
-__device__ __forceinline__ void pass1_chunk(const uint16_t *ks, const u16x8 (&qf)[G][D / 32],
-                                            float (&m)[G], float (&l)[G], float sl2, int lane,
-                                            int klo, int khi) {
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    f32x4 s[G];
-    qk16<D, G, F16>(s, ks, kt, qf, lane);
-    const int b = 16 * kt;
-    bool ok[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ok[i] = b + i >= klo && b + i <= khi;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      f32x4 x;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = ok[i] ? s[h][i] * sl2 : -INFINITY;
-      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (__builtin_amdgcn_ballot_w64(mx > m[h] + kSlack)) {
-        const float mn = fmaxf(m[h], mx);
-        l[h] = (mn == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - mn);
-        m[h] = mn;
-      }
-      const float base = (m[h] == -INFINITY) ? 0.f : m[h];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) l[h] += __builtin_amdgcn_exp2f(x[i] - base);
-    }
-  }
-}
-
-// Pass 2 on one staged chunk: exact probabilities (row lse known) and the
-// PV product. Keys klo..khi of the chunk (shifted by this lane's 4*(l/16))
-// are valid for the lane's row.
-template <int D, int G, bool F16>
-__device__ __forceinline__ void pass2_chunk(const uint16_t *ks, const uint16_t *vt,
-                                            const u16x8 (&qf)[G][D / 32], f32x4 (&o)[G][D / 16],
-                                            const float (&lse2)[G], float sl2, int lane, int klo,
-                                            int khi) {
+__device__ __forceinline__ void online_chunk(const uint16_t *ks, const uint16_t *vt,
+                                             const u16x8 (&qf)[G][D / 32], f32x4 (&o)[G][D / 16],
+                                             float (&m)[G], float (&l)[G], float sl2, int lane, int klo,
+                                             int khi) {
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2) {
     f32x4 s[2][G];
@@ -91,19 +61,40 @@ __device__ __forceinline__ void pass2_chunk(const uint16_t *ks, const uint16_t *
     for (int kk = 0; kk < 2; ++kk) {
       const int kt = 2 * ks2 + kk;
       qk16<D, G, F16>(s[kk], ks, kt, qf, lane);
-      const int b = 16 * kt;
-      bool ok[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ok[i] = b + i >= klo && b + i <= khi;
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = 16 * kt + i >= klo && 16 * kt + i <= khi;
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s[kk][h][i] = ok[i] ? __builtin_amdgcn_exp2f(fmaf(s[kk][h][i], sl2, -lse2[h])) : 0.f;
+        for (int h = 0; h < G; ++h) s[kk][h][i] = ok ? s[kk][h][i] : -INFINITY;
+      }
     }
     u16x8 pf[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) pf[h] = pack_p(s[0][h], s[1][h]);
+    for (int h = 0; h < G; ++h) {
+      float mx = s[0][h][0];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kk][h][i]);
+      mx = grp_max(mx) * sl2;  // the row's max over the half (all its lanes)
+      if (__builtin_amdgcn_ballot_w64(mx > m[h] + kSlack)) {
+        const float mn = fmaxf(m[h], mx);
+        const float alpha = (m[h] == -INFINITY) ? 1.f : exp2f(m[h] - mn);
+        l[h] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[h][dt] = o[h][dt] * alpha;
+        m[h] = mn;
+      }
+      const float nb = (m[h] == -INFINITY) ? 0.f : -m[h];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[kk][h][i] = __builtin_amdgcn_exp2f(fmaf(s[kk][h][i], sl2, nb));
+          l[h] += s[kk][h][i];
+        }
+      pf[h] = pack_p(s[0][h], s[1][h]);
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const u16x8 a = pk_v_frag<D>(vt, dt, ks2, lane);
@@ -113,96 +104,72 @@ __device__ __forceinline__ void pass2_chunk(const uint16_t *ks, const uint16_t *
   }
 }
 
-// Two passes of this lane's query row (G heads) over n_chunks packed chunks:
-// pass 1 gets the exact log-sum-exp, pass 2 forms normalised probabilities
-// for the PV product, so no accumulator is ever rescaled and the heads'
-// accumulators stay in the matrix-core register file. tile_at(c) is chunk
-// c's packed tile; key_range(c, lo, hi) gives the keys lo..hi (inclusive,
-// empty if lo > hi) of chunk c valid for this lane's row. Returns o
-// normalised and the lse (log2 units).
+// One pass of this lane's query row (G heads) over n_chunks packed chunks
+// with the online softmax above. tile_at(c) is chunk c's packed tile;
+// key_range(c, lo, hi) gives the keys lo..hi (inclusive, empty if lo > hi)
+// of chunk c valid for this lane's row. Returns o normalised and the lse
+// (log2 units).
 //
 // Copies: four separate LDS tiles (64 KB at d = 128, so that two workgroups
-// share a CU). Pass 1 rings key tiles through all four (three chunks in
-// flight), pass 2 double-buffers (K, V^T) pairs. Each ring step issues exactly one chunk's copies -- past the last
-// chunk they repeat chunk 0 into slots that are never read again -- so
-// "chunk c landed" is one straight-line vmcnt wait; the slots are separate
-// LDS objects named at compile time, so the compiler adds no waits of its
-// own.
-// The slots are the kernel's LDS tiles, passed in so that every caller in
-// one kernel shares them.
-template <int D, int G, bool F16, int SLOTS, class TileAt, class KeyRange>
-__device__ __forceinline__ void two_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G],
+// share a CU) hold two (K, V^T) chunk pairs, double-buffered: chunk c+1 is
+// in flight while chunk c is used. Each step issues exactly one chunk's
+// copies -- past the last chunk they repeat chunk 0 into slots that are
+// never read again -- so "chunk c landed" is one straight-line vmcnt wait;
+// the slots are separate LDS objects named at compile time, so the compiler
+// adds no waits of its own. The slots are the kernel's LDS tiles, passed in
+// so that every caller in one kernel shares them.
+template <int D, int G, bool F16, class TileAt, class KeyRange>
+__device__ __forceinline__ void one_pass(f32x4 (&o)[G][D / 16], float (&lse2)[G],
                                          const u16x8 (&qf)[G][D / 32], float sl2, int n_chunks,
                                          uint16_t (&r0)[PackedTile<D>::KE], uint16_t (&r1)[PackedTile<D>::KE],
                                          uint16_t (&r2)[PackedTile<D>::KE], uint16_t (&r3)[PackedTile<D>::KE],
                                          TileAt tile_at, KeyRange key_range) {
-  static_assert(SLOTS == 4, "ring size");
   using T = PackedTile<D>;
   constexpr int KE = T::KE;
   constexpr int PK = KE / 512 / 4;  // copies per wave of one tile
   const int lane = threadIdx.x & 63, g4 = 4 * (lane >> 4);
-  // wave-uniform copy offsets kept in scalar registers
   const int off = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) * PK * 512);
-
   float m[G], l[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
-#define NSA_K(DST, C) dma_pieces<PK>(tile_at((C) < n_chunks ? (C) : 0) + off, (DST) + off, lane)
-#define NSA_P1(CUR, NXT)                                                  \
-  {                                                                       \
-    wait_vm_c<(SLOTS - 2) * PK>();                                        \
-    bare_barrier();                                                       \
-    NSA_K(NXT, c + SLOTS - 1);                                            \
-    {                                                                     \
-      int lo_, hi_;                                                       \
-      key_range(c, lo_, hi_);                                             \
-      pass1_chunk<D, G, F16>(CUR, qf, m, l, sl2, lane, lo_ - g4, hi_ - g4); \
-    }                                                                     \
-    if (++c >= n_chunks) break;                                           \
-  }
-  if (n_chunks > 0) { NSA_K(r0, 0); NSA_K(r1, 1); NSA_K(r2, 2); }
-  for (int c = 0; c < n_chunks;) {
-    NSA_P1(r0, r3) NSA_P1(r1, r0) NSA_P1(r2, r1) NSA_P1(r3, r2)
-  }
-#undef NSA_P1
-#pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float M = grp_max(m[h]);
-    const float part = (m[h] == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - M);
-    const float L = grp_sum(part);
-    lse2[h] = (L > 0.f) ? M + log2f(L) : -INFINITY;
+    m[h] = -INFINITY;
+    l[h] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[h][dt] = zero4();
   }
-
-  wait_vm_c<0>();  // no pass-1 copy (padding included) still in flight
-  bare_barrier();  // every wave is done with the pass-1 slots
 #define NSA_KV(DK, DV, C)                                                             \
   {                                                                                   \
     const uint16_t *src_ = tile_at((C) < n_chunks ? (C) : 0);                         \
     dma_pieces<PK>(src_ + off, (DK) + off, lane);                                     \
     dma_pieces<PK>(src_ + KE + off, (DV) + off, lane);                                \
   }
-#define NSA_P2(CK, CV, NK, NV)                                            \
+#define NSA_P(CK, CV, NK, NV)                                             \
   {                                                                       \
-    wait_vm_c<(SLOTS / 2 - 2) * 2 * PK>();                                \
+    wait_vm_c<0>();                                                       \
     bare_barrier();                                                       \
-    NSA_KV(NK, NV, c + SLOTS / 2 - 1);                                    \
+    NSA_KV(NK, NV, c + 1);                                                \
     {                                                                     \
       int lo_, hi_;                                                       \
       key_range(c, lo_, hi_);                                             \
-      pass2_chunk<D, G, F16>(CK, CV, qf, o, lse2, sl2, lane, lo_ - g4, hi_ - g4); \
+      online_chunk<D, G, F16>(CK, CV, qf, o, m, l, sl2, lane, lo_ - g4, hi_ - g4); \
     }                                                                     \
     if (++c >= n_chunks) break;                                           \
   }
   if (n_chunks > 0) NSA_KV(r0, r1, 0);
   for (int c = 0; c < n_chunks;) {
-    NSA_P2(r0, r1, r2, r3) NSA_P2(r2, r3, r0, r1)
+    NSA_P(r0, r1, r2, r3) NSA_P(r2, r3, r0, r1)
   }
-#undef NSA_P2
+#undef NSA_P
 #undef NSA_KV
-#undef NSA_K
   wait_vm_c<0>();  // padding copies land before the workgroup's LDS is reused
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float L = grp_sum(l[h]);
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[h][dt] = o[h][dt] * inv;
+    lse2[h] = (L > 0.f) ? m[h] + log2f(L) : -INFINITY;
+  }
 }
 
 // Query heads are split over N workgroups of at most three heads each
@@ -238,7 +205,7 @@ __device__ __forceinline__ void swa_body(const SwaParams &p, int g, int f, Ring4
   f32x4 o[HW][D / 16];
   float lse2[HW];
   const uint16_t *tiles = p.kv + ((int64_t)g * p.n_tiles + b_lo) * (T::KE + T::VE);
-  two_pass<D, HW, F16, 4>(o, lse2, qf, p.sl2, f - b_lo + 1, rg.r0, rg.r1, rg.r2, rg.r3,
+  one_pass<D, HW, F16>(o, lse2, qf, p.sl2, f - b_lo + 1, rg.r0, rg.r1, rg.r2, rg.r3,
                           [&](int c) { return tiles + (int64_t)c * (T::KE + T::VE); },
                           [&](int c, int &lo, int &hi) {
                             const int key0 = (b_lo + c) * kBlk;  // keys t-w+1 .. t
@@ -304,7 +271,7 @@ __device__ __forceinline__ void text_body(const TextParams &p, int sp, int g, in
   float lse2[HW];
   const uint16_t *vis = p.kv_vis + (int64_t)g * p.n_vchunks * SE;
   const uint16_t *txt = p.kv_txt + (int64_t)g * p.n_tchunks * SE;
-  two_pass<D, HW, F16, 4>(o, lse2, qf, p.sl2, max(0, ce - cb), rg.r0, rg.r1, rg.r2, rg.r3,
+  one_pass<D, HW, F16>(o, lse2, qf, p.sl2, max(0, ce - cb), rg.r0, rg.r1, rg.r2, rg.r3,
                           [&](int c) {
                             const int cc = cb + c;
                             return cc < nvc ? vis + (int64_t)cc * SE : txt + (int64_t)(cc - nvc) * SE;
