@@ -28,9 +28,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:  # also runnable as a plain script
     sys.path.insert(0, ROOT)
 
-# kernel symbol substring -> (short name, source file); pack_kv_kernel serves
-# three launches told apart by their grid (vision blocks / compressed chunks
-# / text rows), see short_name
+# kernel symbol substring -> (short name, source file). Launches of one
+# kernel told apart by their grid (pack_kv_kernel: vision blocks /
+# compressed chunks / text rows; dec_item_kernel: compressed chunks and
+# window slices / selected blocks) are named through grid_names, see
+# short_name.
 KERNELS = [
     ("sel_attn_kernel", "sel_attn", "sparse_attention_long_nsa_amd/csrc/nsa_sel_attn.hip"),
     ("cmp_attn_dma_kernel", "cmp_attn", "sparse_attention_long_nsa_amd/csrc/nsa_cmp_attn.hip"),
@@ -40,22 +42,38 @@ KERNELS = [
     ("text_merge_kernel", "text_merge", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
     ("topk_kernel", "blk_score_topk", "sparse_attention_long_nsa_amd/csrc/nsa_topk.hip"),
     ("cmp_pool_kernel", "cmp_pool", "sparse_attention_long_nsa_amd/csrc/nsa_pool.hip"),
-    ("pack_kv_kernel", "pack", "sparse_attention_long_nsa_amd/csrc/nsa_sel_attn.hip"),
+    ("pack_kv_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_sel_attn.hip"),
+    ("dec_item_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_decode.hip"),
+    ("dec_select_kernel", "dec_select", "sparse_attention_long_nsa_amd/csrc/nsa_decode.hip"),
+    ("dec_combine_kernel", "dec_combine", "sparse_attention_long_nsa_amd/csrc/nsa_decode.hip"),
+    ("mfma_loop_kernel", "mfma_probe", "sparse_attention_long_nsa_amd/csrc/nsa_probe.hip"),
 ]
+DECODE_KERNELS = ("dec_item_cmp_win", "dec_item_sel", "dec_select", "dec_combine")
+PREFILL_KERNELS = ("sel_attn", "cmp_attn", "swa_attn", "text_attn", "text_merge", "blk_score_topk", "cmp_pool",
+                   "pack_kv", "pack_cmp", "pack_text")
 
 
-def short_name(kernel_name: str, grid: int, pack_grids: dict):
+def short_name(kernel_name: str, grid: int, grid_names: dict):
     for sub, short, src in KERNELS:
         if sub in kernel_name or sub.replace("_", "") in kernel_name:
-            if short == "pack":
-                return pack_grids.get(grid, "pack_other"), src
+            if short == "@grid":
+                return grid_names.get((sub, grid), sub + "_other"), src
             return short, src
     return None, None
 
 
 def pack_grid_names(n_frames: int, n_cch: int, n_tchunks: int, hkv: int) -> dict:
     """Grid sizes (threads) of the three packing launches -> names."""
-    return {n_frames * hkv * 256: "pack_kv", n_cch * hkv * 256: "pack_cmp", n_tchunks * hkv * 256: "pack_text"}
+    k = "pack_kv_kernel"
+    return {(k, n_frames * hkv * 256): "pack_kv", (k, n_cch * hkv * 256): "pack_cmp",
+            (k, n_tchunks * hkv * 256): "pack_text"}
+
+
+def decode_grid_names(batch: int, hkv: int, n_blk: int, top_k: int, window: int) -> dict:
+    """Grid sizes (threads) of the two decode item launches -> names."""
+    pairs, k = batch * hkv, "dec_item_kernel"
+    n_items0 = -(-n_blk // 64) + -(-window // 64)
+    return {(k, pairs * n_items0 * 256): "dec_item_cmp_win", (k, pairs * top_k * 256): "dec_item_sel"}
 
 
 def _grid(row: dict) -> int:
@@ -78,20 +96,30 @@ def source_digest(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def trace_summary(trace_csv: str, bench_log: str, pack_grids: dict, title: str, command: str,
-                  out_md: str) -> None:
+def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, command: str,
+                  out_md: str, group: str = "prefill") -> None:
+    keep = DECODE_KERNELS if group == "decode" else PREFILL_KERNELS
     dur = defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
-        name, _ = short_name(r["Kernel_Name"], _grid(r), pack_grids)
-        if name:
+        name, _ = short_name(r["Kernel_Name"], _grid(r), grid_names)
+        if name in keep:
             dur[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6)
     bench = _bench_line(bench_log)
-    kern = bench["kernels"] if bench else {}
+    if group == "decode":
+        dec = (bench or {}).get("decode") or {}
+        kern = {k: {"avg_ms": round(v["avg_us"] * 1e-3, 4)} for k, v in dec.get("kernels", {}).items()}
+    else:
+        kern = bench["kernels"] if bench else {}
     total = sum(sum(v) / len(v) for v in dur.values())
     rows = sorted(dur.items(), key=lambda kv: -sum(kv[1]) / len(kv[1]))
     lines = [f"# Kernel trace: {title}", "", "Command (from the repository root, on one MI355X):", "",
              "```", command, "```", ""]
-    if bench:
+    if bench and group == "decode" and bench.get("decode"):
+        d = bench["decode"]
+        lines += [f"bench.py in the same process reported {d['us_per_step']} us per decode step "
+                  f"({d['roofline']['frac'] * 100:.1f}% of the HBM roofline); its event-timed per-kernel "
+                  "averages are listed beside the profiler's.", ""]
+    elif bench:
         lines += [f"bench.py in the same process reported {bench['ms_per_step']} ms/step "
                   f"({bench['value']:.0f} tokens/s); its event-timed per-kernel averages are listed "
                   "beside the profiler's.", ""]
@@ -99,16 +127,16 @@ def trace_summary(trace_csv: str, bench_log: str, pack_grids: dict, title: str, 
     for name, v in rows:
         avg = sum(v) / len(v)
         ev = kern.get(name, {}).get("avg_ms", "")
-        lines.append(f"| {name} | {len(v)} | {avg:.3f} | {ev} | {100 * avg / total:.1f}% |")
+        lines.append(f"| {name} | {len(v)} | {avg:.4f} | {ev} | {100 * avg / total:.1f}% |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
-def _counter_avgs(path: str, pack_grids: dict) -> dict:
+def _counter_avgs(path: str, grid_names: dict) -> dict:
     vals = defaultdict(list)
     for r in csv.DictReader(open(path)):
-        name, src = short_name(r["Kernel_Name"], _grid(r), pack_grids)
-        if name:
+        name, src = short_name(r["Kernel_Name"], _grid(r), grid_names)
+        if name in PREFILL_KERNELS:
             vals[(name, src)].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
@@ -119,13 +147,13 @@ def _copy_kib(path: str) -> float:
 
 
 def pmc_summary(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
-                copy_mib: int, pack_grids: dict, workload: str, commands: list, bench_log: str,
+                copy_mib: int, grid_names: dict, workload: str, commands: list, bench_log: str,
                 out_md: str, out_dir: str) -> None:
     copy_kib = copy_mib * 1024.0
     f_fetch = copy_kib / _copy_kib(copy_fetch_csv)
     f_write = copy_kib / _copy_kib(copy_write_csv)
-    fetch = _counter_avgs(fetch_csv, pack_grids)
-    write = _counter_avgs(write_csv, pack_grids)
+    fetch = _counter_avgs(fetch_csv, grid_names)
+    write = _counter_avgs(write_csv, grid_names)
     bench = _bench_line(bench_log) if bench_log else None
     kern = bench["kernels"] if bench else {}
     lines = [f"# HBM-side traffic per launch: {workload}", "",
@@ -195,7 +223,10 @@ def mfma_peak(n_wg: int = 256 * 8, iters: int = 400, reps: int = 8) -> dict:
 
 
 def _layer_grids(workload: str) -> dict:
-    from sparse_attention_long_nsa_amd.inputs import PREFILL_PRESETS
+    from sparse_attention_long_nsa_amd.inputs import DECODE_PRESETS, PREFILL_PRESETS
+    if workload in DECODE_PRESETS:
+        s = DECODE_PRESETS[workload]
+        return decode_grid_names(s.batch, s.n_kv_heads, s.cache_len // s.block, s.top_k, s.window)
     s = PREFILL_PRESETS[workload]
     n_frames = -(-s.n_vis // s.block)
     n_cch = -(-(s.n_vis // s.block) // s.block)
@@ -216,6 +247,7 @@ def main(argv=None) -> None:
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--group", choices=("prefill", "decode"), default="prefill")
     m = sub.add_parser("pmc-summary")
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
         m.add_argument(f"--{k}-csv", required=True)
@@ -231,7 +263,7 @@ def main(argv=None) -> None:
     elif a.cmd == "mfma-peak":
         print(json.dumps(mfma_peak()), flush=True)
     elif a.cmd == "trace-summary":
-        trace_summary(a.trace_csv, a.bench_log, _layer_grids(a.workload), a.title, a.command, a.out)
+        trace_summary(a.trace_csv, a.bench_log, _layer_grids(a.workload), a.title, a.command, a.out, a.group)
     else:
         pmc_summary(a.fetch_csv, a.write_csv, a.copy_fetch_csv, a.copy_write_csv, a.copy_mib,
                     _layer_grids(a.workload), a.workload, a.command, a.bench_log, a.out_md, a.out_dir)

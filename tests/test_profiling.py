@@ -1,0 +1,54 @@
+"""Host-side logic of the profiling summaries (no GPU): kernel naming by
+symbol and grid, and the trace table for the prefill and decode groups."""
+import csv
+import json
+
+from sparse_attention_long_nsa_amd import profiling as prof
+
+
+def _trace(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for name, grid, ns in rows:
+            w.writerow({"Kernel_Name": name, "Grid_Size": grid, "Start_Timestamp": 1000,
+                        "End_Timestamp": 1000 + ns})
+
+
+def test_grid_names_tell_launches_apart():
+    g = prof._layer_grids("decode_16x128k")
+    # 16 sequences x 4 KV groups; 2048 compressed blocks -> 32 chunks, window 512 -> 8 slices
+    assert g[("dec_item_kernel", 64 * 40 * 256)] == "dec_item_cmp_win"
+    assert g[("dec_item_kernel", 64 * 16 * 256)] == "dec_item_sel"
+    name, src = prof.short_name("void nsa::(anonymous namespace)::dec_item_kernel<128, 7>(nsa::DecodeParams, int)",
+                                64 * 16 * 256, g)
+    assert name == "dec_item_sel" and src.endswith("nsa_decode.hip")
+    p = prof._layer_grids("qwen_128k_k32_w256")
+    assert p[("pack_kv_kernel", 2048 * 4 * 256)] == "pack_kv"
+    assert prof.short_name("pack_kv_kernel<128, true>", 12345, p)[0] == "pack_kv_kernel_other"
+    assert prof.short_name("some_other_kernel", 1, p) == (None, None)
+
+
+def test_trace_summary_groups(tmp_path):
+    trace = tmp_path / "trace.csv"
+    _trace(trace, [("sel_attn_kernel<128, 7, true>", 655360, 11_000_000),
+                   ("sel_attn_kernel<128, 7, true>", 655360, 13_000_000),
+                   ("dec_select_kernel<128, 7, 32>", 16384, 9_000),
+                   ("mfma_loop_kernel", 524288, 2_000_000)])
+    log = tmp_path / "bench.log"
+    line = {"metric": "m", "value": 1.0, "ms_per_step": 20.0,
+            "kernels": {"sel_attn": {"avg_ms": 11.9}},
+            "decode": {"us_per_step": 44.0, "roofline": {"frac": 0.33},
+                       "kernels": {"dec_select": {"avg_us": 9.5}}}}
+    log.write_text("noise\n" + json.dumps(line) + "\n")
+    out = tmp_path / "p.md"
+    prof.trace_summary(str(trace), str(log), prof._layer_grids("qwen_128k_k32_w256"), "t", "cmd", str(out))
+    text = out.read_text()
+    assert "| sel_attn | 2 | 12.0000 | 11.9 | 100.0% |" in text
+    assert "dec_select" not in text and "mfma" not in text
+    out_d = tmp_path / "d.md"
+    prof.trace_summary(str(trace), str(log), prof._layer_grids("decode_16x128k"), "t", "cmd", str(out_d),
+                       group="decode")
+    text = out_d.read_text()
+    assert "| dec_select | 1 | 0.0090 | 0.0095 | 100.0% |" in text
+    assert "44.0 us per decode step" in text
