@@ -182,6 +182,19 @@ template <int G> struct HeadSplit {
   static constexpr int first(int i) { return i == 0 ? 0 : first(i - 1) + size(i - 1); }
 };
 
+// Workgroups are handed to the eight XCDs round-robin by index, and each XCD
+// has its own L2. The launch is padded to a multiple of eight and index i is
+// mapped to the logical item (i % 8) * per + i / 8, so each XCD works through
+// one contiguous range of items; items that read the same key tiles are made
+// adjacent, so those tiles come from the XCD's L2 after the first read.
+// Returns -1 for the padding.
+__device__ __forceinline__ int xcd_item(int i, int n_items) {
+  const int per = (n_items + 7) / 8;
+  const int item = (i % 8) * per + i / 8;
+  return item < n_items ? item : -1;
+}
+__host__ inline unsigned xcd_grid(unsigned n_items) { return (n_items + 7) / 8 * 8; }
+
 // ----------------------------------------------------------- sliding window
 // A 64-query tile (vision frame f) needs keys [t0 - w + 1, t0 + 63], i.e.
 // the packed blocks from (t0 - w + 1) / 64 to f.
@@ -233,9 +246,14 @@ void swa_attn_kernel(SwaParams p) {
   constexpr int KE = PackedTile<D>::KE;
   __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
   const Ring4<D> rg{r0, r1, r2, r3};
-  const int half = blockIdx.x % S::N, rest = blockIdx.x / S::N;
-  const int g = rest % p.hkv;
-  const int f = p.n_tiles - 1 - rest / p.hkv;  // heaviest first
+  // item order: head part fastest, then frame, then KV group, so one XCD
+  // takes consecutive frames of one group (neighbouring frames' windows
+  // share all but one key tile)
+  const int item = xcd_item(blockIdx.x, p.n_tiles * p.hkv * S::N);
+  if (item < 0) return;
+  const int half = item % S::N, rest = item / S::N;
+  const int f = rest % p.n_tiles;
+  const int g = rest / p.n_tiles;
   if (half == 0) swa_body<D, G, F16, S::size(0), 0>(p, g, f, rg);
   else if constexpr (S::N > 1) {
     if (half == 1) swa_body<D, G, F16, S::size(1), S::first(1)>(p, g, f, rg);
@@ -305,12 +323,17 @@ void text_attn_kernel(TextParams p) {
   constexpr int KE = PackedTile<D>::KE;
   __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
   const Ring4<D> rg{r0, r1, r2, r3};
-  const int half = blockIdx.x % S::N;
-  const int rest0 = blockIdx.x / S::N;
-  const int sp = rest0 % p.n_split;
-  const int rest = rest0 / p.n_split;
-  const int g = rest % p.hkv;
-  const int tile = rest / p.hkv;
+  // item order: head part fastest, then query tile, then key split, then KV
+  // group, so the workgroups reading one split's key tiles run together on
+  // one XCD
+  const int item = xcd_item(blockIdx.x, p.n_tiles * p.hkv * p.n_split * S::N);
+  if (item < 0) return;
+  const int half = item % S::N;
+  const int rest0 = item / S::N;
+  const int tile = rest0 % p.n_tiles;
+  const int rest = rest0 / p.n_tiles;
+  const int sp = rest % p.n_split;
+  const int g = rest / p.n_split;
   if (half == 0) text_body<D, G, F16, S::size(0), 0>(p, sp, g, tile, rg);
   else if constexpr (S::N > 1) {
     if (half == 1) text_body<D, G, F16, S::size(1), S::first(1)>(p, sp, g, tile, rg);
@@ -343,7 +366,7 @@ template <int D, int G, bool F16>
 hipError_t run_swa(const SwaParams &p, hipStream_t st) {
   const unsigned n = (unsigned)p.n_tiles * (unsigned)p.hkv * HeadSplit<G>::N;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((swa_attn_kernel<D, G, F16>), dim3(n), dim3(kThreadsH), 0, st, p);
+  hipLaunchKernelGGL((swa_attn_kernel<D, G, F16>), dim3(xcd_grid(n)), dim3(kThreadsH), 0, st, p);
   return hipGetLastError();
 }
 
@@ -351,7 +374,7 @@ template <int D, int G, bool F16>
 hipError_t run_text(const TextParams &p, hipStream_t st) {
   const unsigned n = (unsigned)p.n_tiles * (unsigned)p.hkv * (unsigned)p.n_split * HeadSplit<G>::N;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((text_attn_kernel<D, G, F16>), dim3(n), dim3(kThreadsH), 0, st, p);
+  hipLaunchKernelGGL((text_attn_kernel<D, G, F16>), dim3(xcd_grid(n)), dim3(kThreadsH), 0, st, p);
   return hipGetLastError();
 }
 

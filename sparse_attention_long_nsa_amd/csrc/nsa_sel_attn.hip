@@ -366,8 +366,10 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
       float *dst = p.out + qrow * D + 4 * grp;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
+        // streaming read-modify-write of the output (non-temporal, so the
+        // output does not push the key tiles out of the last-level cache)
         f32x4 *d4 = reinterpret_cast<f32x4 *>(dst + 16 * dt);
-        *d4 = *d4 + o[r][dt] * gate;
+        __builtin_nontemporal_store(__builtin_nontemporal_load(d4) + o[r][dt] * gate, d4);
       }
     }
   }

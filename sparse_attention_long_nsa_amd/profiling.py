@@ -41,7 +41,7 @@ KERNELS = [
     ("text_attn_kernel", "text_attn", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
     ("text_merge_kernel", "text_merge", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
     ("topk_kernel", "blk_score_topk", "sparse_attention_long_nsa_amd/csrc/nsa_topk.hip"),
-    ("cmp_pool_kernel", "cmp_pool", "sparse_attention_long_nsa_amd/csrc/nsa_pool.hip"),
+    ("cmp_pool_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_pool.hip"),
     ("pack_kv_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_sel_attn.hip"),
     ("dec_item_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_decode.hip"),
     ("dec_select_kernel", "dec_select", "sparse_attention_long_nsa_amd/csrc/nsa_decode.hip"),
@@ -62,11 +62,13 @@ def short_name(kernel_name: str, grid: int, grid_names: dict):
     return None, None
 
 
-def pack_grid_names(n_frames: int, n_cch: int, n_tchunks: int, hkv: int) -> dict:
-    """Grid sizes (threads) of the three packing launches -> names."""
+def pack_grid_names(n_frames: int, n_cch: int, n_tchunks: int, hkv: int, n_cmp: int) -> dict:
+    """Grid sizes (threads) of the prefill's packing and pooling launches ->
+    names (the layer pools keys and values in one launch of two grid rows;
+    single-row pooling launches are other callers', e.g. cache building)."""
     k = "pack_kv_kernel"
     return {(k, n_frames * hkv * 256): "pack_kv", (k, n_cch * hkv * 256): "pack_cmp",
-            (k, n_tchunks * hkv * 256): "pack_text"}
+            (k, n_tchunks * hkv * 256): "pack_text", ("cmp_pool_kernel", 2 * min(n_cmp, 1024) * 256): "cmp_pool"}
 
 
 def decode_grid_names(batch: int, hkv: int, n_blk: int, top_k: int, window: int) -> dict:
@@ -230,7 +232,7 @@ def _layer_grids(workload: str) -> dict:
     s = PREFILL_PRESETS[workload]
     n_frames = -(-s.n_vis // s.block)
     n_cch = -(-(s.n_vis // s.block) // s.block)
-    return pack_grid_names(n_frames, n_cch, -(-s.n_text // s.block), s.n_kv_heads)
+    return pack_grid_names(n_frames, n_cch, -(-s.n_text // s.block), s.n_kv_heads, s.n_vis // s.block)
 
 
 def main(argv=None) -> None:

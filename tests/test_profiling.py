@@ -25,6 +25,7 @@ def test_grid_names_tell_launches_apart():
     assert name == "dec_item_sel" and src.endswith("nsa_decode.hip")
     p = prof._layer_grids("qwen_128k_k32_w256")
     assert p[("pack_kv_kernel", 2048 * 4 * 256)] == "pack_kv"
+    assert p[("cmp_pool_kernel", 2 * 1024 * 256)] == "cmp_pool"
     assert prof.short_name("pack_kv_kernel<128, true>", 12345, p)[0] == "pack_kv_kernel_other"
     assert prof.short_name("some_other_kernel", 1, p) == (None, None)
 
