@@ -127,7 +127,8 @@ def test_repeat_runs_are_bitwise_identical():
     assert np.array_equal(a["out"], b["out"])
 
 
-@pytest.mark.parametrize("preset", ["qwen_36k", "qwen_64k", "qwen_128k_k32_w256"])
+@pytest.mark.parametrize("preset", ["qwen_36k", "qwen_64k", "qwen_128k_k32_w256", "qwen_128k_k16_w512",
+                                    "qwen_128k_k8_w1024"])
 def test_full_size_sampled_rows(preset):
     inp = make_prefill_inputs(PREFILL_PRESETS[preset], seed=0)
     announce(preset, inp["shape"])
@@ -151,7 +152,7 @@ def test_all_tied_scores_take_lowest_blocks():
     # every vision key zero: all compressed keys are zero, every block score
     # ties, and the reading's tie rule (lowest index first) fixes the answer:
     # blocks 0 .. k-2 plus the own block. Rows with more than 64 candidates
-    # exercise the top-k's radix-select path, the others its ranking path.
+    # exercise the top-k's radix-select path, the others its compaction path.
     s = PrefillShape(64 * 100, 0, 20, 28, 4, 128, 64, 8, 128, "bf16")
     inp = make_prefill_inputs(s, seed=8)
     inp["k"][inp["is_vision"].astype(bool)] = 0.0
