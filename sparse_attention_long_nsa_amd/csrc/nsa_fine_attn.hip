@@ -346,15 +346,17 @@ void text_attn_kernel(TextParams p) {
 template <int D>
 __global__ __launch_bounds__(D) void text_merge_kernel(TextParams p) {
   const int r = blockIdx.x / p.hq, h = blockIdx.x % p.hq, d = threadIdx.x;
+  // the splits' loads are independent: unrolled, many are in flight at once
   float M = -INFINITY;
+#pragma unroll 16
   for (int sp = 0; sp < p.n_split; ++sp)
     M = fmaxf(M, p.part_ml[((int64_t)sp * p.n_text + r) * p.hq + h].x);
   float acc = 0.f, L = 0.f;
+#pragma unroll 16
   for (int sp = 0; sp < p.n_split; ++sp) {
     const int64_t pr = ((int64_t)sp * p.n_text + r) * p.hq + h;
     const float lse = p.part_ml[pr].x;
-    if (lse == -INFINITY) continue;
-    const float w = exp2f(lse - M);
+    const float w = (lse == -INFINITY) ? 0.f : exp2f(lse - M);  // an empty split weighs 0
     L += w;
     acc += w * p.part_o[pr * D + d];
   }

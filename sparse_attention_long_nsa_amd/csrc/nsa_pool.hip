@@ -46,7 +46,8 @@ __global__ __launch_bounds__(kPoolThreads) void cmp_pool_kernel(PoolJob j0, Pool
     for (int item = tid; item < P * CH; item += kPoolThreads) {
       const int ch = item % CH, rp = item / CH;
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int r = rp; r < kBlk; r += P) {
+#pragma unroll 8
+      for (int r = rp; r < kBlk; r += P) {  // independent row loads, many in flight
         float v[8];
         load8f(xb + (int64_t)r * C + ch * 8, v);
 #pragma unroll
