@@ -111,11 +111,19 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
                        void *stream);
 
 /* ------------------------------------------------------------------- decode
- * One new query per sequence, at the last slot (L-1) of its vision cache: its
- * own key and value are already in slot L-1, every one of the L/B compressed
- * blocks is complete, and block L/B-1 is the query's own. Supported: bf16,
- * head_dim in {64, 128}, block_size == 64, cache_len % 64 == 0, at most 8
- * query heads per KV head, top_k <= 64, window <= cache_len. */
+ * One new query per sequence, at the last slot (L-1) of its vision cache
+ * (VideoNSA paper summary page, "Method"; evaluated exactly as prefill's row
+ * L-1): its own key and value are already in slot L-1; the floor(L/B)
+ * complete blocks have compressed keys and values and are all visible; block
+ * (L-1)/B is the query's own -- the last complete block when B divides L,
+ * else the partial block after them. So a generating caller appends each new
+ * token's key and value, and pools a block (nsa_cmp_pool over its 64 rows,
+ * written at row b of the compressed cache) once the block is complete.
+ * Supported: bf16, head_dim in {64, 128}, block_size == 64, at most 8 query
+ * heads per KV head, top_k <= 64, window <= cache_len, cache_len <= 8192 * 64.
+ * cache_capacity: rows allocated per sequence in k_cache / v_cache (their
+ * sequence stride; 0 means cache_len; must be >= cache_len); the compressed
+ * caches then hold floor(cache_capacity / B) rows per sequence. */
 typedef struct {
   int32_t batch;      /* Bt sequences                        */
   int32_t cache_len;  /* L tokens per sequence               */
@@ -127,15 +135,16 @@ typedef struct {
   int32_t window;
   float scale;        /* <= 0 selects 1/sqrt(d)              */
   int32_t dtype;      /* NSA_DTYPE_BF16 only                 */
+  int32_t cache_capacity; /* rows per sequence; 0 = cache_len */
 } nsa_decode_desc;
 
 nsa_status nsa_decode_workspace_size(const nsa_decode_desc *desc, size_t *bytes);
 
 /*   q            device [Bt, Hq, d]        bf16
- *   k_cache      device [Bt, L, Hkv, d]    bf16
- *   v_cache      device [Bt, L, Hkv, d]    bf16
- *   k_cmp, v_cmp device [Bt, L/B, Hkv, d]  bf16  compressed cache (for example
- *                from nsa_cmp_pool)
+ *   k_cache      device [Bt, C, Hkv, d]    bf16  (C = cache capacity; rows
+ *   v_cache      device [Bt, C, Hkv, d]    bf16   0..L-1 are read)
+ *   k_cmp, v_cmp device [Bt, C/B, Hkv, d]  bf16  compressed cache, rows
+ *                0..floor(L/B)-1 read (for example from nsa_cmp_pool)
  *   gate_logits  device [Bt, Hq, 3]        float32
  *   out          device [Bt, Hq, d]        float32
  *   sel_idx_out  device [Bt, Hkv, top_k]   int32 or NULL (ascending, -1 padded)

@@ -165,7 +165,9 @@ def prefill(inp: dict, rows=None, inject_sel=None, top_k=None, window=None, scal
 def decode(inp: dict, k_cmp: np.ndarray, v_cmp: np.ndarray, inject_sel=None,
            top_k=None, window=None, scale=0.0, want=("sel", "lse", "scores", "counts")) -> dict:
     """One query per sequence at the last cache slot; ``inp`` holds q [Bt,Hq,d],
-    k_cache/v_cache [Bt,L,Hkv,d], gates [Bt,Hq,3]; compressed caches given."""
+    k_cache/v_cache [Bt,L,Hkv,d], gates [Bt,Hq,3]; compressed caches of the
+    floor(L/B) complete blocks given. The own block is (L-1)//B (partial when
+    B does not divide L)."""
     s = inp["shape"]
     q = _f32(inp["q"])
     kcache, vcache = _f32(inp["k_cache"]), _f32(inp["v_cache"])

@@ -37,7 +37,8 @@
  *   R12 the query's own block is always selected and counts toward k.
  *   R14 blocks count from the first vision token.
  * The decode entry evaluates the same steps for a query that is the last
- * token of its cache (all cache blocks complete).
+ * token of its cache: the L/B complete blocks are its compressed keys, and
+ * its own block is the last, partial when B does not divide L.
  */
 #include <math.h>
 #include <stdint.h>
@@ -440,11 +441,13 @@ int ora_prefill(const ora_desc *ds, const float *q, const float *k, const float 
 /* ------------------------------------------------------------- decode API */
 
 /* One query per sequence: the last token (position L-1) of a vision cache
- * whose own key/value already sit in slot L-1, so every one of the L/B
- * compressed blocks is complete and visible (R2) and block L/B-1 is the
- * query's own block (R12).
- * q [Bt,hq,d]; k_cache/v_cache [Bt,L,hkv,d]; k_cmp/v_cmp [Bt,L/B,hkv,d]
- * (given, float32-exact); gates [Bt,hq,3]; inject_sel NULL or [Bt,hkv,k].
+ * whose own key/value already sit in slot L-1, so every one of the floor(L/B)
+ * complete blocks has a compressed key and is visible (R2), and block
+ * (L-1)/B is the query's own (R12): the last complete block when B divides
+ * L, else the partial block after them (R3), exactly as for prefill's row
+ * L-1. q [Bt,hq,d]; k_cache/v_cache [Bt,L,hkv,d]; k_cmp/v_cmp
+ * [Bt,floor(L/B),hkv,d] (given, float32-exact); gates [Bt,hq,3]; inject_sel
+ * NULL or [Bt,hkv,k].
  * Outputs: out [Bt,hq,d]; sel, lse, scores, counts may be NULL. */
 int ora_decode(const ora_decode_desc *ds, const float *q, const float *k_cache,
                const float *v_cache, const float *k_cmp, const float *v_cmp,
@@ -455,7 +458,6 @@ int ora_decode(const ora_decode_desc *ds, const float *q, const float *k_cache,
   const int hq = ds->n_q_heads, hkv = ds->n_kv_heads, d = ds->head_dim, B = ds->block;
   const int64_t L = ds->cache_len;
   if (ds->batch < 0 || L < 1 || !check_heads(hq, hkv, d, B, ds->top_k, ds->window)) return ORA_EINVAL;
-  if (L % B != 0) return ORA_EINVAL;
   const double scale = ds->scale > 0 ? ds->scale : 1.0 / sqrt((double)d);
   const int64_t n_blk = L / B;
   int status = ORA_OK;

@@ -174,7 +174,7 @@ def check_decode(inp: dict, kc: np.ndarray, vc: np.ndarray, gpu_out: np.ndarray,
     exempt sequences."""
     s = inp["shape"]
     ref = oracle.decode(inp, kc, vc, want=("sel", "scores", "lse"))
-    cur = np.full(s.batch, s.cache_len // s.block - 1)
+    cur = np.full(s.batch, (s.cache_len - 1) // s.block)
     rep = index_parity(gpu_sel, ref["sel"], lambda idx: ref["scores"][idx], cur, tie_tol)
     out_ref = ref["out"].copy()
     if len(rep.exempt_rows):

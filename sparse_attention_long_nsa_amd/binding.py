@@ -57,6 +57,7 @@ class DecodeDesc(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("cache_capacity", ctypes.c_int32),
     ]
 
 
@@ -215,11 +216,14 @@ def prefill(q, k, v, is_vision, w_cmp_k, w_cmp_v, gate_logits, top_k, window, bl
     return res
 
 
-def decode_desc(q, k_cache, top_k, window, block=64, scale=0.0) -> DecodeDesc:
+def decode_desc(q, k_cache, top_k, window, block=64, scale=0.0, cache_len=None) -> DecodeDesc:
+    """k_cache [Bt, C, Hkv, d]: C rows allocated per sequence, the first
+    cache_len (default C) in use."""
     bt, hq, d = q.shape
-    L, hkv = k_cache.shape[1], k_cache.shape[2]
+    cap, hkv = k_cache.shape[1], k_cache.shape[2]
     dt = {torch.bfloat16: NSA_DTYPE_BF16, torch.float32: NSA_DTYPE_FP32}[q.dtype]
-    return DecodeDesc(bt, L, hq, hkv, d, block, top_k, window, float(scale), dt)
+    L = cap if cache_len is None else int(cache_len)
+    return DecodeDesc(bt, L, hq, hkv, d, block, top_k, window, float(scale), dt, cap)
 
 
 def decode_workspace_size(desc: DecodeDesc) -> int:
@@ -231,16 +235,17 @@ def decode_workspace_size(desc: DecodeDesc) -> int:
 
 
 def decode(q, k_cache, v_cache, k_cmp, v_cmp, gate_logits, top_k, window, block=64, scale=0.0,
-           out=None, want_sel=False, want_lse=False, workspace=None, stream=None) -> dict:
-    """Runs nsa_decode: q [Bt,Hq,d], caches [Bt,L,Hkv,d], compressed caches
-    [Bt,L/B,Hkv,d] (bf16), gate_logits [Bt,Hq,3] fp32."""
-    desc = decode_desc(q, k_cache, top_k, window, block, scale)
+           out=None, want_sel=False, want_lse=False, workspace=None, stream=None, cache_len=None) -> dict:
+    """Runs nsa_decode: q [Bt,Hq,d], caches [Bt,C,Hkv,d] with the first
+    cache_len rows (default C) in use, compressed caches [Bt,C//B,Hkv,d]
+    (bf16), gate_logits [Bt,Hq,3] fp32."""
+    desc = decode_desc(q, k_cache, top_k, window, block, scale, cache_len)
     bt, hq, d = q.shape
-    L, hkv = k_cache.shape[1], k_cache.shape[2]
-    for name, t, shape in (("q", q, (bt, hq, d)), ("k_cache", k_cache, (bt, L, hkv, d)),
-                           ("v_cache", v_cache, (bt, L, hkv, d)),
-                           ("k_cmp", k_cmp, (bt, L // block, hkv, d)),
-                           ("v_cmp", v_cmp, (bt, L // block, hkv, d))):
+    cap, hkv = k_cache.shape[1], k_cache.shape[2]
+    for name, t, shape in (("q", q, (bt, hq, d)), ("k_cache", k_cache, (bt, cap, hkv, d)),
+                           ("v_cache", v_cache, (bt, cap, hkv, d)),
+                           ("k_cmp", k_cmp, (bt, cap // block, hkv, d)),
+                           ("v_cmp", v_cmp, (bt, cap // block, hkv, d))):
         _check_dev(name, t, q.dtype, shape)
     _check_dev("gate_logits", gate_logits, torch.float32, (bt, hq, 3))
     dev = q.device

@@ -36,7 +36,7 @@ constexpr int kDecMaxK = 64;
 
 struct DecPlan {
   int batch = 0, L = 0, hq = 0, hkv = 0, d = 0, G = 0, k = 0, w = 0;
-  int n_blk = 0, n_chunk = 0, n_win = 0, n_items = 0;
+  int n_blk = 0, n_chunk = 0, n_win = 0, n_items = 0, cap = 0;
   float scale = 0.f;
   size_t off_logits = 0, off_cmp = 0, off_ocmp = 0, off_fine = 0, off_sel = 0, total = 0;
 };
@@ -76,14 +76,14 @@ __global__ __launch_bounds__(64 * kItemWaves) void dec_item_kernel(DecodeParams 
   const int g = (int)((blockIdx.x / n_it) % p.hkv);
   const int bi = (int)(blockIdx.x / ((unsigned)n_it * p.hkv));
   const uint16_t *kb = p.kcache, *vb = p.vcache;
-  int nrows = p.L, key0 = 0, nk = 0;
+  int nrows = p.cap, key0 = 0, nk = 0;  // rows per sequence of the array read
   bool is_cmp = false;
   float *dst;
   int64_t hstride;  // floats between consecutive heads' partials
   if (phase == 0 && it < p.n_chunk) {
     kb = p.kc;
     vb = p.vc;
-    nrows = p.n_blk;
+    nrows = p.cap_blk;
     key0 = it * kBlk;
     nk = min(kBlk, p.n_blk - key0);
     is_cmp = true;
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64 * kItemWaves) void dec_item_kernel(DecodeParams 
       const int b = p.sel[((int64_t)bi * p.hkv + g) * p.topk + it];
       if (b >= 0) {
         key0 = b * kBlk;
-        nk = kBlk;
+        nk = min(kBlk, p.L - key0);  // the own block may be partial
       }
       slot = it;
     }
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_select_kernel(DecodeParams p)
     }
   }
   __syncthreads();
-  const int n_cand = p.n_blk - 1;
+  const int n_cand = p.own;  // candidates: every block before the own one
   const float *lg = p.logits + ((int64_t)bi * p.hq + g * G) * p.n_blk;
 #pragma unroll 4
   for (int b = tid; b < n_cand; b += kDecThreads) {
@@ -327,7 +327,7 @@ hipError_t run_decode(const DecodeParams &p, hipStream_t st) {
     Timed t("dec_select", st);
     // candidates per lane of the selecting wave: 32 covers caches of up to
     // 2049 blocks (131,136 tokens)
-    if (p.n_blk - 1 <= 64 * 32)
+    if (p.own <= 64 * 32)
       hipLaunchKernelGGL((dec_select_kernel<D, G, 32>), dim3(pairs), dim3(kDecThreads), 0, st, p);
     else
       hipLaunchKernelGGL((dec_select_kernel<D, G, kDecMaxBlk / 64>), dim3(pairs), dim3(kDecThreads), 0, st, p);
@@ -363,10 +363,12 @@ nsa_status plan_decode(const nsa_decode_desc *ds, DecPlan &pl) {
   pl.k = ds->top_k;
   pl.w = ds->window;
   if (ds->dtype != NSA_DTYPE_BF16) return NSA_ERR_UNSUPPORTED;
-  if (ds->block_size != kBlk || pl.L % kBlk != 0) return NSA_ERR_UNSUPPORTED;
+  if (ds->block_size != kBlk) return NSA_ERR_UNSUPPORTED;
   if (!decode_supported(pl.d, pl.G)) return NSA_ERR_UNSUPPORTED;
   if (pl.k > kDecMaxK || pl.w > pl.L) return NSA_ERR_UNSUPPORTED;
-  pl.n_blk = pl.L / kBlk;
+  pl.cap = ds->cache_capacity > 0 ? ds->cache_capacity : pl.L;
+  if (ds->cache_capacity < 0 || pl.cap < pl.L) return NSA_ERR_INVALID_ARG;
+  pl.n_blk = pl.L / kBlk;  // complete blocks: the compressed keys
   if (pl.n_blk > kDecMaxBlk) return NSA_ERR_UNSUPPORTED;
   pl.n_chunk = (pl.n_blk + kBlk - 1) / kBlk;
   pl.n_win = (pl.w + kBlk - 1) / kBlk;
@@ -465,6 +467,9 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
   p.topk = pl.k;
   p.window = pl.w;
   p.n_blk = pl.n_blk;
+  p.cap = pl.cap;
+  p.cap_blk = pl.cap / kBlk;
+  p.own = (pl.L - 1) / kBlk;
   p.n_chunk = pl.n_chunk;
   p.n_win = pl.n_win;
   p.n_items = pl.n_items;

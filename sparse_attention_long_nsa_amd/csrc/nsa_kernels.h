@@ -90,6 +90,8 @@ struct DecodeParams {
   float *ocmp;                      // workspace [Bt, Hq, d]
   float *fine_part;                 // workspace [Bt, Hq, n_items, d + 2]
   int batch, L, hq, hkv, topk, window, n_blk, n_chunk, n_win, n_items;
+  int cap, cap_blk;  // cache rows and compressed rows per sequence (strides)
+  int own;           // the query's own block, (L - 1) / 64 (= number of candidates)
   float sl2;
 };
 

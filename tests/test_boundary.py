@@ -144,8 +144,8 @@ def test_mfma_probe_validation():
     assert L.nsa_probe_mfma_bf16(8, 10, None, None) == binding.NSA_ERR_INVALID_ARG
 
 
-def ddesc(batch=16, L=131072, hq=28, hkv=4, d=128, block=64, k=16, w=512, dtype=0):
-    return binding.DecodeDesc(batch, L, hq, hkv, d, block, k, w, 0.0, dtype)
+def ddesc(batch=16, L=131072, hq=28, hkv=4, d=128, block=64, k=16, w=512, dtype=0, cap=0):
+    return binding.DecodeDesc(batch, L, hq, hkv, d, block, k, w, 0.0, dtype, cap)
 
 
 def dws(ds):
@@ -154,7 +154,7 @@ def dws(ds):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(L=1000), binding.NSA_ERR_UNSUPPORTED),      # not a whole number of blocks
+    (dict(cap=1000, L=1001), binding.NSA_ERR_INVALID_ARG),  # fewer rows allocated than in use
     (dict(dtype=1), binding.NSA_ERR_UNSUPPORTED),
     (dict(w=131073), binding.NSA_ERR_UNSUPPORTED),
     (dict(k=65), binding.NSA_ERR_UNSUPPORTED),
@@ -163,6 +163,13 @@ def dws(ds):
 ])
 def test_decode_validation(kw, status):
     assert dws(ddesc(**kw))[0] == status
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 1000, 131071])
+def test_decode_any_cache_length(L):
+    # the own block may be partial; a larger allocation is allowed
+    assert dws(ddesc(L=L, w=1))[0] == binding.NSA_OK
+    assert dws(ddesc(L=L, w=1, cap=L + 100))[0] == binding.NSA_OK
 
 
 def test_decode_workspace_and_pointer_checks():

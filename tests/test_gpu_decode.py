@@ -19,19 +19,32 @@ def bf(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)
 
 
-def run_decode(inp, kc, vc):
+def padded(x, rows):
+    """x [Bt, n, ...] copied into a zero buffer of `rows` rows per sequence."""
+    buf = np.zeros((x.shape[0], rows) + x.shape[2:], dtype=np.float32)
+    buf[:, : x.shape[1]] = x
+    return buf
+
+
+def run_decode(inp, kc, vc, extra_rows=0):
+    """Caches handed over in buffers of capacity C = L rounded up to a whole
+    block plus extra_rows (C = L when both are zero): rows past L are never
+    read."""
     s = inp["shape"]
-    r = binding.decode(bf(inp["q"]), bf(inp["k_cache"]), bf(inp["v_cache"]), bf(kc), bf(vc),
-                       torch.from_numpy(inp["gates"]).cuda(), s.top_k, s.window, block=s.block,
-                       want_sel=True, want_lse=True)
+    L = s.cache_len
+    cap = L if (L % s.block == 0 and extra_rows == 0) else -(-L // s.block) * s.block + extra_rows
+    cb = cap // s.block
+    r = binding.decode(bf(inp["q"]), bf(padded(inp["k_cache"], cap)), bf(padded(inp["v_cache"], cap)),
+                       bf(padded(kc, cb)), bf(padded(vc, cb)), torch.from_numpy(inp["gates"]).cuda(),
+                       s.top_k, s.window, block=s.block, want_sel=True, want_lse=True, cache_len=L)
     torch.cuda.synchronize()
     return r["out"].cpu().numpy(), r["sel_idx"].cpu().numpy(), r["lse"].cpu().numpy()
 
 
-def check(inp, name):
+def check(inp, name, extra_rows=0):
     print(f"\n[case] {name}: {inp['shape']}", flush=True)
     kc, vc = parity.decode_inputs_cmp(inp, round_to_bf16)
-    out, sel, lse = run_decode(inp, kc, vc)
+    out, sel, lse = run_decode(inp, kc, vc, extra_rows)
     rep, orep, ref = parity.check_decode(inp, kc, vc, out, sel)
     print(rep, "|", orep, flush=True)
     assert rep.counted == 0, rep
@@ -50,6 +63,59 @@ def check(inp, name):
 ])
 def test_decode_small(shape):
     check(make_decode_inputs(shape, seed=11), "decode_small")
+
+
+@pytest.mark.parametrize("shape,extra", [
+    (DecodeShape(2, 64 * 20 + 37, 28, 4, 128, 64, 16, 100), 0),   # partial own block
+    (DecodeShape(3, 64 * 9 + 1, 8, 2, 128, 64, 4, 64), 128),      # one token into a block
+    (DecodeShape(2, 64 * 7 + 63, 6, 3, 64, 64, 8, 200), 64),      # one token short of a block
+    (DecodeShape(2, 63, 8, 2, 64, 64, 4, 30), 0),                  # no complete block at all
+    (DecodeShape(1, 65, 28, 4, 128, 64, 3, 65), 256),
+    (DecodeShape(2, 1024, 28, 4, 128, 64, 16, 512), 192),          # whole blocks, larger buffer
+])
+def test_decode_any_cache_length(shape, extra):
+    check(make_decode_inputs(shape, seed=13), "decode_any_length", extra)
+
+
+def test_streaming_decode_matches_oracle_across_block_boundaries():
+    # a generating caller: caches of fixed capacity, one token appended per
+    # step, a block pooled into the compressed cache (nsa_cmp_pool on its 64
+    # rows) as soon as it completes; every step decodes at the new length.
+    bt, hq, hkv, d, k, w, cap = 2, 8, 2, 128, 6, 96, 64 * 12
+    full = make_decode_inputs(DecodeShape(bt, cap, hq, hkv, d, 64, k, w), seed=21)
+    rng = np.random.Generator(np.random.PCG64(22))
+    kdev, vdev = bf(full["k_cache"]), bf(full["v_cache"])
+    wk, wv = bf(full["w_k"]), bf(full["w_v"])
+    kc = torch.zeros((bt, cap // 64, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+
+    def pool_block(b):
+        for s in range(bt):
+            kc[s, b] = binding.cmp_pool(kdev[s, 64 * b: 64 * b + 64], wk)["bf16"][0]
+            vc[s, b] = binding.cmp_pool(vdev[s, 64 * b: 64 * b + 64], wv)["bf16"][0]
+
+    L0 = 64 * 8 + 60
+    for b in range(L0 // 64):
+        pool_block(b)
+    for L in range(L0, L0 + 70):
+        if L % 64 == 0:
+            pool_block(L // 64 - 1)  # block just completed by token L-1
+        if (L - L0) % 7 and L % 64 not in (0, 1, 63):
+            continue  # check every 7th step and each step at a block boundary
+        q = round_to_bf16(rng.standard_normal((bt, hq, d)).astype(np.float32))
+        gates = rng.standard_normal((bt, hq, 3)).astype(np.float32)
+        r = binding.decode(bf(q), kdev, vdev, kc, vc, torch.from_numpy(gates).cuda(), k, w,
+                           want_sel=True, cache_len=L)
+        torch.cuda.synchronize()
+        nb = L // 64
+        kcf = kc[:, :nb].float().cpu().numpy()
+        vcf = vc[:, :nb].float().cpu().numpy()
+        inp = dict(q=q, k_cache=full["k_cache"][:, :L], v_cache=full["v_cache"][:, :L], gates=gates,
+                   shape=DecodeShape(bt, L, hq, hkv, d, 64, k, w))
+        rep, orep, _ = parity.check_decode(inp, kcf, vcf, r["out"].cpu().numpy(), r["sel_idx"].cpu().numpy())
+        print(f"L={L}", rep, "|", orep, flush=True)
+        assert rep.counted == 0, (L, rep)
+        assert orep.ok(), (L, orep)
 
 
 def test_decode_full_size_preset():

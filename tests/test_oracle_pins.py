@@ -255,9 +255,11 @@ def test_p9_all_equal_keys_tie_and_lowest_indices_win():
 
 # ---------------------------------------------------------------------- P10
 
-@pytest.mark.parametrize("k,w", [(4, 100), (16, 512)])
-def test_p10_decode_equals_prefill_last_row(k, w):
-    L = 640
+@pytest.mark.parametrize("L,k,w", [(640, 4, 100), (640, 16, 512), (641, 4, 100), (703, 6, 64), (63, 4, 30),
+                                   (64, 2, 64), (129, 3, 200)])
+def test_p10_decode_equals_prefill_last_row(L, k, w):
+    # any cache length: when 64 does not divide L the query's own block is
+    # the partial one after the L // 64 compressed blocks
     inp = small(n_vis=L, hq=6, hkv=2, d=16, k=k, w=w)
     r = oracle.prefill(inp, rows=np.array([L - 1], np.int64), want=("sel", "lse", "kcmp"))
     dec = dict(q=inp["q"][L - 1][None], k_cache=inp["k"][None], v_cache=inp["v"][None],
