@@ -116,6 +116,27 @@ def run_gpu(inp, dev, top_k, window, steps, warmup, per_kernel):
     return ms, kernels, out
 
 
+def run_spans_bench(inp, shape, steps, warmup, one_run_ms):
+    """The same tokens with the vision tokens in several runs: 8 clips of
+    16,384 vision tokens, each after 64 of the text tokens (row maps)."""
+    import torch
+    from sparse_attention_long_nsa_amd.inputs import SPAN_LAYOUTS, mask_from_runs, relayout
+    m = mask_from_runs(SPAN_LAYOUTS["8clips"])
+    if len(m) != shape.n_tokens or int(m.sum()) != shape.n_vis:
+        return None
+    mi = relayout(inp, m)
+    dev = {k: torch.from_numpy(mi[k]).to("cuda:0").to(torch.bfloat16).contiguous()
+           for k in ("q", "k", "v", "w_k", "w_v")}
+    dev["gates"] = torch.from_numpy(mi["gates"]).to("cuda:0")
+    ms, kern, _ = run_gpu(mi, dev, shape.top_k, shape.window, steps, warmup, True)
+    del dev
+    log(f"8 clips: {ms:.3f} ms/step ({ms / one_run_ms:.4f} x one run)")
+    return {"layout": "8 clips of 16,384 vision tokens, 64 text tokens before each",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(shape.n_tokens / (ms * 1e-3), 1),
+            "vs_one_run": round(ms / one_run_ms, 4),
+            "kernels_ms": {n: round(t, 4) for n, (t, _) in sorted(kern.items(), key=lambda x: -x[1][0])}}
+
+
 def cpu_baseline(inp, n_vis_rows, n_text_rows):
     """The fp64 oracle, as it stands, on a bounded row sample of the same
     workload; per-row times extrapolated to the whole sequence."""
@@ -227,6 +248,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-spans", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer library runs on a single MI355X and has no "
@@ -298,6 +320,10 @@ def main():
     if not args.no_decode:
         decode = run_decode_bench(max(10, args.steps), args.warmup)
 
+    spans = None
+    if not args.no_spans:
+        spans = run_spans_bench(inp, shape, max(3, args.steps // 2), 1, ms)
+
     # the published peak checked on this GPU with an MFMA-loop probe
     from sparse_attention_long_nsa_amd.profiling import mfma_peak
     probe = mfma_peak()
@@ -335,6 +361,7 @@ def main():
         "kernels": per_kernel,
         "sweep": sweep,
         "decode": decode,
+        "several_vision_runs": spans,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -61,10 +61,19 @@ typedef enum {
 } nsa_dtype;
 
 /* ------------------------------------------------------------------ prefill
- * One sequence of n_tokens tokens. Supported: head_dim in {64, 128},
- * block_size == 64, n_q_heads % n_kv_heads == 0 with at most 8 query heads per
- * KV head, the vision tokens forming one contiguous run (text may precede
- * and/or follow it), top_k >= 1, window >= 1. */
+ * One sequence of n_tokens tokens (VideoNSA paper summary page, "Method":
+ * the tokens split into a vision set and a text set by position; the three
+ * NSA branches run on the vision set, text tokens get dense causal GQA).
+ * The vision tokens may lie anywhere: one run, or several runs with text
+ * between them (several clips or images in one prompt). The branches see the
+ * vision tokens in position order, so blocks of 64 are counted over that
+ * order (a block may straddle two runs) and the window counts vision tokens;
+ * a text token attends to every earlier token of either kind and itself.
+ * Several runs cost 4 bytes of workspace per token (row maps) and one small
+ * launch per 16,384 tokens to build them.
+ * Supported: head_dim in {64, 128}, block_size == 64, n_q_heads % n_kv_heads
+ * == 0 with at most 8 query heads per KV head, top_k >= 1, window >= 1,
+ * N_v / 64 <= 8192. */
 typedef struct {
   int64_t n_tokens;   /* N = vision + text tokens                                 */
   int32_t n_q_heads;  /* Hq                                                       */

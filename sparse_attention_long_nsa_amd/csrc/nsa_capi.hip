@@ -21,6 +21,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct PrefillPlan {
   int64_t N = 0, v0 = 0, v1 = 0, n_vis = 0, n_text = 0;
+  bool mapped = false;  // vision tokens in several runs: rows through maps
   int hq = 0, hkv = 0, d = 0, G = 0, k = 0, w = 0;
   int n_blk = 0, n_frames = 0, n_cch = 0;
   bool fp32 = false;
@@ -28,7 +29,8 @@ struct PrefillPlan {
   int n_split = 0, chunks_per_split = 0, text_tiles = 0, n_tchunks = 0;
   size_t off_kc = 0, off_vc = 0, off_kcl = 0, off_qh = 0, off_ql = 0, off_q16 = 0, off_k16 = 0,
          off_v16 = 0;
-  size_t off_kvc = 0, off_kvt = 0, off_vt = 0, off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0, total = 0;
+  size_t off_kvc = 0, off_kvt = 0, off_vt = 0, off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0;
+  size_t off_vmap = 0, off_tmap = 0, off_tnvb = 0, total = 0;
 };
 
 nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, PrefillPlan &pl) {
@@ -53,18 +55,19 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
   if (pl.N > (int64_t)INT32_MAX / 2) return NSA_ERR_UNSUPPORTED;
   pl.scale = ds->scale > 0.f ? ds->scale : 1.0f / sqrtf((float)pl.d);
 
-  // vision tokens must form one contiguous run
-  int64_t first = -1, last = -1;
-  for (int64_t i = 0; i < pl.N; ++i)
-    if (is_vision[i]) { if (first < 0) first = i; last = i; }
-  if (first < 0) { pl.v0 = pl.v1 = 0; }
-  else {
-    for (int64_t i = first; i <= last; ++i)
-      if (!is_vision[i]) return NSA_ERR_UNSUPPORTED;
-    pl.v0 = first;
-    pl.v1 = last + 1;
+  // vision tokens: one run [v0, v1) addressed directly, or several runs
+  // addressed through row maps
+  int64_t first = -1, last = -1, runs = 0;
+  for (int64_t i = 0; i < pl.N; ++i) {
+    if (!is_vision[i]) continue;
+    if (first < 0) first = i;
+    if (i == 0 || !is_vision[i - 1]) ++runs;
+    last = i;
+    ++pl.n_vis;
   }
-  pl.n_vis = pl.v1 - pl.v0;
+  pl.v0 = first < 0 ? 0 : first;
+  pl.v1 = first < 0 ? 0 : last + 1;
+  pl.mapped = runs > 1;
   pl.n_text = pl.N - pl.n_vis;
   pl.n_blk = (int)(pl.n_vis / kBlk);
   pl.n_frames = (int)((pl.n_vis + kBlk - 1) / kBlk);
@@ -110,6 +113,11 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
   pl.off_sel = take(sizeof(int32_t) * pl.n_vis * Hk * pl.k);
   pl.off_po = take(sizeof(float) * (size_t)pl.n_split * pl.n_text * H * D);
   pl.off_pml = take(sizeof(float2) * (size_t)pl.n_split * pl.n_text * H);
+  if (pl.mapped) {
+    pl.off_vmap = take(sizeof(int32_t) * pl.n_vis);
+    pl.off_tmap = take(sizeof(int32_t) * pl.n_text);
+    pl.off_tnvb = take(sizeof(int32_t) * pl.n_text);
+  }
   pl.total = off;
   return NSA_OK;
 }
@@ -202,6 +210,26 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
   }
   const float sl2 = pl.scale * kLog2e;
 
+  // several vision runs: row maps from the mask, one slice per launch
+  const int32_t *vmap = nullptr, *tmap = nullptr, *tnvb = nullptr;
+  if (pl.mapped) {
+    int32_t *vm = at<int32_t>(workspace, pl.off_vmap), *tm = at<int32_t>(workspace, pl.off_tmap);
+    int32_t *tb = at<int32_t>(workspace, pl.off_tnvb);
+    MaskSlice m;
+    m.vis_before = 0;
+    for (int64_t base = 0; base < pl.N; base += 32 * kMaskWords) {
+      m.base = base;
+      m.n = (int)(pl.N - base < 32 * kMaskWords ? pl.N - base : 32 * kMaskWords);
+      memset(m.bits, 0, sizeof(m.bits));
+      int64_t nv = 0;
+      for (int j = 0; j < m.n; ++j)
+        if (is_vision[base + j]) { m.bits[j >> 5] |= 1u << (j & 31); ++nv; }
+      NSA_LAUNCH("row_maps", launch_row_maps(m, vm, tm, tb, s));
+      m.vis_before += nv;
+    }
+    vmap = vm; tmap = tm; tnvb = tb;
+  }
+
   if (pl.n_vis > 0) {
     float *lse = lse_out ? lse_out : at<float>(workspace, pl.off_lse);
     int32_t *sel = sel_idx_out ? sel_idx_out : at<int32_t>(workspace, pl.off_sel);
@@ -209,10 +237,11 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
     const size_t esz = pl.fp32 ? sizeof(float) : sizeof(uint16_t);
     if (pl.n_blk > 0) {
       // compressed keys: fp16 (bf16 hi/lo for fp32 inputs); values: fp16
-      PoolJob jk{static_cast<const char *>(k) + esz * pl.v0 * Hk * D, w_cmp_k, pl.hkv, pl.n_blk,
-                 pl.fp32 ? kc : nullptr, kcl, pl.fp32 ? nullptr : kc, k_cmp_out};
-      PoolJob jv{static_cast<const char *>(v) + esz * pl.v0 * Hk * D, w_cmp_v, pl.hkv, pl.n_blk,
-                 nullptr, nullptr, vc, v_cmp_out};
+      const int64_t r0 = pl.mapped ? 0 : pl.v0;  // rows through vmap when mapped
+      PoolJob jk{static_cast<const char *>(k) + esz * r0 * Hk * D, w_cmp_k, pl.hkv, pl.n_blk,
+                 pl.fp32 ? kc : nullptr, kcl, pl.fp32 ? nullptr : kc, k_cmp_out, vmap};
+      PoolJob jv{static_cast<const char *>(v) + esz * r0 * Hk * D, w_cmp_v, pl.hkv, pl.n_blk,
+                 nullptr, nullptr, vc, v_cmp_out, vmap};
       NSA_LAUNCH("cmp_pool", launch_cmp_pool(jk, &jv, pl.d, pl.fp32, s));
     }
     uint16_t *kvc = nullptr;
@@ -221,26 +250,26 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
       NSA_LAUNCH("pack_cmp", launch_pack_tiles(kc, vc, 0, pl.n_blk, pl.hkv, pl.n_cch, kvc, pl.d, true, s));
     }
     CmpAttnParams cp{qc, ql, kc, kcl, vc, kvc, pl.n_cch, gate_logits, out, lse, gs, pl.v0,
-                     (int)pl.n_vis, pl.hq, pl.hkv, pl.n_frames, sl2};
+                     (int)pl.n_vis, pl.hq, pl.hkv, pl.n_frames, sl2, vmap};
     NSA_LAUNCH("cmp_attn", launch_cmp_attn(cp, pl.d, pl.G, pl.fp32, s));
     TopkParams tp{gs, sel, (int)pl.n_vis, pl.hkv, pl.k};
     NSA_LAUNCH("blk_score_topk", launch_topk(tp, pl.n_frames, s));
     SelParams sp{qb, kb, vb, at<uint16_t>(workspace, pl.off_vt), sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
-                 pl.n_frames, sl2};
+                 pl.n_frames, sl2, vmap};
     NSA_LAUNCH("pack_kv", launch_pack_kv(sp, pl.d, pl.fp32, s));
     SwaParams wp{qb, at<uint16_t>(workspace, pl.off_vt), gate_logits, out, pl.v0, (int)pl.n_vis,
-                 pl.hq, pl.hkv, pl.w, pl.n_frames, sl2};
+                 pl.hq, pl.hkv, pl.w, pl.n_frames, sl2, vmap};
     NSA_LAUNCH("swa_attn", launch_swa_attn(wp, pl.d, pl.G, pl.fp32, s));
     NSA_LAUNCH("sel_attn", launch_sel_attn(sp, pl.d, pl.G, pl.fp32, s));
   }
   if (pl.n_text > 0) {
     uint16_t *kvt = at<uint16_t>(workspace, pl.off_kvt);
     NSA_LAUNCH("pack_text", launch_pack_tiles(kb, vb, 0, (int)pl.n_text, pl.hkv, pl.n_tchunks, kvt,
-                                              pl.d, pl.fp32, s, (int)pl.v0, pl.v1 - pl.v0));
+                                              pl.d, pl.fp32, s, (int)pl.v0, pl.v1 - pl.v0, tmap));
     TextParams tp{qb, at<uint16_t>(workspace, pl.off_vt), kvt, at<float>(workspace, pl.off_po),
                   at<float2>(workspace, pl.off_pml), out, pl.v0, pl.v1, pl.N, (int)pl.n_text,
                   pl.hq, pl.hkv, pl.n_split, pl.chunks_per_split, pl.text_tiles,
-                  (int)(pl.n_vis > 0 ? pl.n_frames : 0), pl.n_tchunks, sl2};
+                  (int)(pl.n_vis > 0 ? pl.n_frames : 0), pl.n_tchunks, sl2, tmap, tnvb};
     NSA_LAUNCH("text_attn", launch_text_attn(tp, pl.d, pl.G, pl.fp32, s));
     NSA_LAUNCH("text_merge", launch_text_merge(tp, pl.d, s));
   }

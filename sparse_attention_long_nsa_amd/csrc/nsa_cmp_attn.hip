@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_kernel(CmpAttnParams p) {
   u16x8 qf[G][DS];
   u16x8 ql[SPLIT ? G : 1][DS];
   {
-    const int64_t q0 = ((p.v0 + (tvalid ? t : 0)) * p.hq + (int64_t)g * G) * D;
+    const int64_t q0 = (row_pos(p.vmap, p.v0, tvalid ? t : 0) * p.hq + (int64_t)g * G) * D;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_kernel(CmpAttnParams p) {
 
   // ---- epilogue: out = sigmoid(g_cmp) * o_cmp (first writer of vision rows)
   if (tvalid) {
-    const int64_t r0 = (p.v0 + t) * p.hq + (int64_t)g * G;
+    const int64_t r0 = row_pos(p.vmap, p.v0, t) * p.hq + (int64_t)g * G;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float gate = sigmoidf_(p.gates[(r0 + h) * 3 + 0]);
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
 
   u16x8 qf[G][DS];
   {
-    const int64_t q0 = ((p.v0 + (tvalid ? t : 0)) * p.hq + (int64_t)g * G) * D;
+    const int64_t q0 = (row_pos(p.vmap, p.v0, tvalid ? t : 0) * p.hq + (int64_t)g * G) * D;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
 
   // ---- epilogue: out = sigmoid(g_cmp) * o_cmp (first writer of vision rows)
   if (tvalid) {
-    const int64_t r0w = (p.v0 + t) * p.hq + (int64_t)g * G;
+    const int64_t r0w = row_pos(p.vmap, p.v0, t) * p.hq + (int64_t)g * G;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float gate = sigmoidf_(p.gates[(r0w + h) * 3 + 0]);

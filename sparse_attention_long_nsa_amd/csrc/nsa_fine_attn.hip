@@ -213,7 +213,7 @@ __device__ __forceinline__ void swa_body(const SwaParams &p, int g, int f, Ring4
   const int wnd = p.window;
 
   u16x8 qf[HW][D / 32];
-  const int64_t qrow = (p.v0 + (tvalid ? t : 0)) * p.hq + (int64_t)g * G + H0;
+  const int64_t qrow = row_pos(p.vmap, p.v0, tvalid ? t : 0) * p.hq + (int64_t)g * G + H0;
   load_q_h<D, HW>(qf, p.q, qrow, tvalid, lane);
   f32x4 o[HW][D / 16];
   float lse2[HW];
@@ -262,8 +262,10 @@ void swa_attn_kernel(SwaParams p) {
 }
 
 // --------------------------------------------------------------- text rows
-__device__ __forceinline__ int64_t text_pos(int r, int64_t v0, int64_t v1) {
-  return r < v0 ? (int64_t)r : v1 + (r - v0);
+// Position of text row r: from the map when the vision tokens lie in several
+// runs, else the rows before the one vision run [v0, v1), then those after.
+__device__ __forceinline__ int64_t text_pos(const TextParams &p, int r) {
+  return p.tmap ? (int64_t)p.tmap[r] : r < p.v0 ? (int64_t)r : p.v1 + (r - p.v0);
 }
 
 // One (64-query text tile, KV group, key split, head part) per workgroup.
@@ -277,10 +279,11 @@ __device__ __forceinline__ void text_body(const TextParams &p, int sp, int g, in
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4;
   const int r = tile * kBlk + wv * 16 + (lane & 15);
   const bool rvalid = r < p.n_text;
-  const int64_t pos = rvalid ? text_pos(r, p.v0, p.v1) : -1;
+  const int64_t pos = rvalid ? text_pos(p, r) : -1;
   const int nvc = p.n_vchunks, nch = p.n_vchunks + p.n_tchunks;
   const int cb = sp * p.chunks_per_split, ce = min(cb + p.chunks_per_split, nch);
-  const int64_t n_vis = p.v1 - p.v0;
+  // vision keys before the query: a prefix of the vision rows
+  const int64_t n_vb = !rvalid ? 0 : p.tnvb ? (int64_t)p.tnvb[r] : pos < p.v0 ? 0 : p.v1 - p.v0;
 
   u16x8 qf[HW][D / 32];
   const int64_t qrow = (rvalid ? pos : 0) * p.hq + (int64_t)g * G + H0;
@@ -297,9 +300,8 @@ __device__ __forceinline__ void text_body(const TextParams &p, int sp, int g, in
                           [&](int c, int &lo, int &hi) {
                             const int cc = cb + c;
                             lo = 0;
-                            if (cc < nvc) {  // vision-local keys j: j < n_vis, v0 + j <= pos
-                              const int key0 = cc * kBlk;
-                              hi = (int)min((int64_t)n_vis - 1, pos - p.v0) - key0;
+                            if (cc < nvc) {  // vision-local keys j < n_vb
+                              hi = (int)n_vb - 1 - cc * kBlk;
                             } else {  // text-local keys j: positions increase with j, so j <= r
                               hi = (rvalid ? r : -1) - (cc - nvc) * kBlk;
                             }
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(D) void text_merge_kernel(TextParams p) {
     L += w;
     acc += w * p.part_o[pr * D + d];
   }
-  p.out[(text_pos(r, p.v0, p.v1) * p.hq + h) * D + d] = acc / L;
+  p.out[(text_pos(p, r) * p.hq + h) * D + d] = acc / L;
 }
 
 // ------------------------------------------------------------- launchers

@@ -12,6 +12,13 @@ __host__ __device__ __forceinline__ int64_t frame_off(int64_t f, int hkv) {
   return (int64_t)kBlk * hkv * (f * (f - 1) / 2);
 }
 
+// Global position of row i of a token set (the vision tokens, or the text
+// tokens): map[i] when the set is scattered over several runs of the
+// sequence, else row0 + i.
+__device__ __forceinline__ int64_t row_pos(const int32_t *map, int64_t row0, int64_t i) {
+  return map ? (int64_t)map[i] : row0 + i;
+}
+
 struct PoolJob {
   const void *x;     // first row of the pooled run, [n_rows, n_heads, d]
   const void *w;     // [d, d]
@@ -21,6 +28,7 @@ struct PoolJob {
   uint16_t *out_lo;  // bf16 residual (or null)
   uint16_t *out_h16; // fp16 rounding of the result (or null)
   float *out_f32;    // fp32 result (or null)
+  const int32_t *rows = nullptr;  // pooled row i is x row rows[i] (or i)
 };
 
 struct CmpAttnParams {
@@ -36,6 +44,7 @@ struct CmpAttnParams {
   int64_t v0;              // first vision position
   int n_vis, hq, hkv, n_frames;
   float sl2;               // softmax scale * log2(e)
+  const int32_t *vmap = nullptr;  // vision row -> position (several vision runs)
 };
 
 struct TopkParams {
@@ -52,6 +61,7 @@ struct SwaParams {
   int64_t v0;
   int n_vis, hq, hkv, window, n_tiles;
   float sl2;
+  const int32_t *vmap = nullptr;
 };
 
 struct SelParams {
@@ -63,6 +73,7 @@ struct SelParams {
   int64_t v0;
   int n_vis, hq, hkv, topk, n_frames;
   float sl2;
+  const int32_t *vmap = nullptr;
 };
 
 struct TextParams {
@@ -75,6 +86,18 @@ struct TextParams {
   int64_t v0, v1, n_tokens;
   int n_text, hq, hkv, n_split, chunks_per_split, n_tiles, n_vchunks, n_tchunks;
   float sl2;
+  const int32_t *tmap = nullptr;  // text row -> position (several vision runs)
+  const int32_t *tnvb = nullptr;  // text row -> vision tokens before it
+};
+
+// One slice of the token-kind mask, as kernel arguments: bit j of word i
+// says whether position base + 32 i + j is a vision token.
+constexpr int kMaskWords = 512;
+struct MaskSlice {
+  uint32_t bits[kMaskWords];
+  int64_t base;        // first position of the slice
+  int64_t vis_before;  // vision tokens before `base`
+  int n;               // positions in the slice (<= 32 * kMaskWords)
 };
 
 struct DecodeParams {
@@ -106,12 +129,17 @@ hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st);
 hipError_t launch_swa_attn(const SwaParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st);
 // Packs n_rows rows of k, v ([rows][Hkv][d]) into PackedTile blocks
-// [Hkv][n_chunks][K tile, V^T tile]: packed row i is source row row0 + i,
-// plus `jump` for i >= split_at; v_f16: v is fp16 already (else bf16,
-// converted).
+// [Hkv][n_chunks][K tile, V^T tile]: packed row i is source row rows[i] when
+// a map is given, else row0 + i, plus `jump` for i >= split_at; v_f16: v is
+// fp16 already (else bf16, converted).
 hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
                              int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st,
-                             int split_at = 0x7fffffff, int64_t jump = 0);
+                             int split_at = 0x7fffffff, int64_t jump = 0,
+                             const int32_t *rows = nullptr);
+// Writes the row maps of one mask slice: vmap[t] = position of vision row t,
+// tmap[r] = position of text row r, tnvb[r] = vision tokens before it.
+hipError_t launch_row_maps(const MaskSlice &m, int32_t *vmap, int32_t *tmap, int32_t *tnvb,
+                           hipStream_t st);
 size_t packed_kv_block_elems(int d);  // elements of one packed (K, V^T) block
 hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st);

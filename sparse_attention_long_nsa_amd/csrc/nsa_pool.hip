@@ -5,7 +5,8 @@
 // block-level key/value). Reading: y = W * mean, no bias.
 //
 // HBM-bound: each workgroup streams one block (64 rows x Hkv x d, contiguous
-// in the token-major layout) with 16-byte loads, reduces the rows in fp32,
+// in the token-major layout, or gathered through a row map when the vision
+// tokens lie in several runs) with 16-byte loads, reduces the rows in fp32,
 // and applies W from the L1/L2-resident copy.
 #include "nsa_kernels.h"
 
@@ -43,13 +44,14 @@ __global__ __launch_bounds__(kPoolThreads) void cmp_pool_kernel(PoolJob j0, Pool
 
   for (int64_t b = blockIdx.x; b < jb.n_blk; b += gridDim.x) {
     const T *xb = x + b * kBlk * (int64_t)C;
+    const int32_t *rb = jb.rows ? jb.rows + b * kBlk : nullptr;
     for (int item = tid; item < P * CH; item += kPoolThreads) {
       const int ch = item % CH, rp = item / CH;
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll 8
       for (int r = rp; r < kBlk; r += P) {  // independent row loads, many in flight
         float v[8];
-        load8f(xb + (int64_t)r * C + ch * 8, v);
+        load8f((rb ? x + (int64_t)rb[r] * C : xb + (int64_t)r * C) + ch * 8, v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += v[i];
       }

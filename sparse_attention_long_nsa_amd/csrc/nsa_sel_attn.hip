@@ -142,6 +142,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   __shared__ uint32_t ubits[kSelMaxBlk / 32];  // union as a bitmask over blocks
   __shared__ int16_t wpre[kSelMaxBlk / 32];    // union entries before each bitmask word
   __shared__ int pass_[NC], ready_[C::NPW];
+  __shared__ int tpos[TOK];                    // position of each token of the chunk
   __shared__ int n_union;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -169,6 +170,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   for (int w = tid; w < nwords; w += C::NT) ubits[w] = 0u;
   if (tid < NC) pass_[tid] = 0;
   if (tid < C::NPW) ready_[tid] = 0;
+  if (tid < TOK) tpos[tid] = tid < ntok ? (int)row_pos(p.vmap, p.v0, tok0 + tid) : 0;
   for (int idx = tid; idx < TOK * k; idx += C::NT) {
     const int tk = idx / k;
     int b = tk < ntok ? p.sel[((int64_t)(tok0 + tk) * p.hkv + g) * k + (idx % k)] : -1;
@@ -277,7 +279,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
     const int tk = c * TT + r * TP + tau;
     rowvalid[r] = tau < TP && tk < ntok;
     trow[r] = tok0 + tk;
-    const int64_t qrow = (p.v0 + (rowvalid[r] ? trow[r] : 0)) * p.hq + (int64_t)g * G + hh;
+    const int64_t qrow = (int64_t)tpos[rowvalid[r] ? tk : 0] * p.hq + (int64_t)g * G + hh;
 #pragma unroll
     for (int ds = 0; ds < D / 32; ++ds)
       qf[r][ds] = rowvalid[r] ? q_frag_global(p.q + qrow * D, ds, lane) : zero8();
@@ -361,7 +363,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   for (int r = 0; r < RT; ++r) {
     const float L = grp_sum(l[r]);
     if (rowvalid[r]) {
-      const int64_t qrow = (p.v0 + trow[r]) * p.hq + (int64_t)g * G + hh;
+      const int64_t qrow = (int64_t)tpos[c * TT + r * TP + tau] * p.hq + (int64_t)g * G + hh;
       const float gate = bad ? __builtin_nanf("") : sigmoidf_(p.gates[qrow * 3 + 1]) / L;
       float *dst = p.out + qrow * D + 4 * grp;
 #pragma unroll
@@ -378,13 +380,15 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
 // Packs one KV head's keys and values into the block layout (PackedTile):
 // per (head, block) the swizzled K tile (as given: bf16, or fp16 for fp32
 // inputs) followed by the swizzled, key-permuted V^T tile in fp16; rows past
-// n_vis are zero. Packed row t reads source row v0 + t, plus `jump` from
-// row split_at on (to skip a run of rows, e.g. the vision run for text).
+// n_vis are zero. Packed row t reads source row rows[t] when a row map is
+// given, else v0 + t, plus `jump` from row split_at on (to skip a run of
+// rows, e.g. the vision run for text).
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v, int64_t v0,
                                                       int n_vis, int split_at, int64_t jump, int hkv,
-                                                      int n_frames, uint16_t *__restrict__ kv) {
+                                                      int n_frames, uint16_t *__restrict__ kv,
+                                                      const int32_t *__restrict__ rows) {
   using T = PackedTile<D>;
   __shared__ uint16_t tile[kBlk][D + 2];
   const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
@@ -395,7 +399,10 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict
     const int r = idx / (D / 8), c = idx % (D / 8);
     const int t = b * kBlk + r;
     u16x8 val = zero8();
-    if (t < n_vis) val = *reinterpret_cast<const u16x8 *>(k + ((v0 + t + (t >= split_at ? jump : 0)) * hkv + g) * (int64_t)D + 8 * c);
+    if (t < n_vis) {
+      const int64_t src = rows ? (int64_t)rows[t] : v0 + t + (t >= split_at ? jump : 0);
+      val = *reinterpret_cast<const u16x8 *>(k + (src * hkv + g) * (int64_t)D + 8 * c);
+    }
     *reinterpret_cast<u16x8 *>(dst + r * D + 8 * T::template swz<2 * D>(r, c)) = val;
   }
   for (int idx = tid; idx < kBlk * D; idx += 256) {
@@ -403,7 +410,8 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict
     const int t = b * kBlk + key;
     uint16_t x = 0;
     if (t < n_vis) {
-      x = v[((v0 + t + (t >= split_at ? jump : 0)) * hkv + g) * (int64_t)D + d];
+      const int64_t src = rows ? (int64_t)rows[t] : v0 + t + (t >= split_at ? jump : 0);
+      x = v[(src * hkv + g) * (int64_t)D + d];
       if (!F16) x = bf2h_bits(x);
     }
     tile[key][d] = x;
@@ -466,21 +474,22 @@ hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream
 
 hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
                              int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st,
-                             int split_at, int64_t jump) {
+                             int split_at, int64_t jump, const int32_t *rows) {
   const unsigned n = (unsigned)n_chunks * (unsigned)hkv;
   if (n == 0) return hipSuccess;
   if (d == 64) {
-    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<64, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out);
-    else hipLaunchKernelGGL((pack_kv_kernel<64, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out);
+    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<64, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows);
+    else hipLaunchKernelGGL((pack_kv_kernel<64, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows);
   } else {
-    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<128, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out);
-    else hipLaunchKernelGGL((pack_kv_kernel<128, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out);
+    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<128, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows);
+    else hipLaunchKernelGGL((pack_kv_kernel<128, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st) {
-  return launch_pack_tiles(p.k, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.kv, d, f16, st);
+  return launch_pack_tiles(p.k, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.kv, d, f16, st,
+                           0x7fffffff, 0, p.vmap);
 }
 
 size_t packed_kv_block_elems(int d) { return (size_t)2 * kBlk * d; }

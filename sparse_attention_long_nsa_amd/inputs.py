@@ -162,6 +162,43 @@ def make_prefill_inputs(shape: PrefillShape, seed: int = 0) -> dict:
     return out
 
 
+def mask_from_runs(runs) -> np.ndarray:
+    """Token-kind mask (uint8, 1 = vision) of a sequence written as runs
+    [("t", n), ("v", n), ...] in position order."""
+    parts = []
+    for kind, n in runs:
+        if kind not in ("t", "v") or n < 0:
+            raise ValueError(f"bad run {(kind, n)}")
+        parts.append(np.full(n, 1 if kind == "v" else 0, dtype=np.uint8))
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.uint8)
+
+
+def relayout(inp: dict, is_vision: np.ndarray) -> dict:
+    """The same tokens at new positions: the vision rows of `inp` keep their
+    order and move to the positions where `is_vision` is 1, the text rows keep
+    theirs and fill the rest; gates travel with their rows."""
+    old = np.asarray(inp["is_vision"]).astype(bool)
+    new = np.asarray(is_vision).astype(bool)
+    if new.shape != old.shape or new.sum() != old.sum():
+        raise ValueError("the new mask must hold as many vision tokens as the old one")
+    perm = np.empty(old.shape[0], dtype=np.int64)  # new position -> old row
+    perm[np.nonzero(new)[0]] = np.nonzero(old)[0]
+    perm[np.nonzero(~new)[0]] = np.nonzero(~old)[0]
+    out = dict(inp)
+    for x in ("q", "k", "v", "gates"):
+        out[x] = np.ascontiguousarray(inp[x][perm])
+    out["is_vision"] = new.astype(np.uint8)
+    return out
+
+
+# Layouts with several vision runs (several clips or images in one prompt,
+# text between them), as run lists over the tokens of a prefill preset.
+SPAN_LAYOUTS = {
+    # 128K vision tokens as 8 clips of 16,384, each after a 64-token text run
+    "8clips": [("t", 64), ("v", 16384)] * 8,
+}
+
+
 def make_decode_inputs(shape: DecodeShape, seed: int = 0) -> dict:
     """Draw one decode workload: per sequence a frame-correlated vision K/V
     cache [Bt,L,Hkv,d]; the query is the last cache token, so it is drawn from

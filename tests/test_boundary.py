@@ -101,10 +101,15 @@ def test_misaligned_pointer_rejected():
     assert call_prefill(desc(), mask, {"q": FAKE + 2}) == binding.NSA_ERR_INVALID_ARG
 
 
-def test_interleaved_vision_spans_unsupported():
-    mask = vision_mask(1024, 0, 1024)
-    mask[500] = 0
-    assert call_prefill(desc(), mask) == binding.NSA_ERR_UNSUPPORTED
+def test_several_vision_runs_accepted_with_row_maps_in_the_workspace():
+    one = np.concatenate([np.zeros(10, np.uint8), np.ones(1014, np.uint8)])
+    two = np.concatenate([np.ones(500, np.uint8), np.zeros(10, np.uint8), np.ones(514, np.uint8)])
+    st1, n1 = ws_size(desc(), one)
+    st2, n2 = ws_size(desc(), two)
+    assert st1 == st2 == binding.NSA_OK
+    up = lambda x: (x + 255) // 256 * 256
+    # vision row -> position, text row -> position and vision tokens before it
+    assert n2 - n1 == up(4 * 1014) + 2 * up(4 * 10)
 
 
 def test_workspace_checks():

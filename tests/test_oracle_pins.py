@@ -13,6 +13,8 @@ Each test names the pin it checks:
   P12        linearity in v, invariance to a common key shift
   P13        permuting KV groups with their query heads permutes the output
   P14        one head per group: score == that head's compression probability
+  P15        several vision runs: vision rows see only the vision tokens in
+             position order (equal to the one-run layout), text rows dense causal
 """
 import json
 import math
@@ -25,7 +27,7 @@ import torch
 import oracle
 from oracle import brute
 from sparse_attention_long_nsa_amd.inputs import (
-    DecodeShape, PrefillShape, make_decode_inputs, make_prefill_inputs)
+    DecodeShape, PrefillShape, make_decode_inputs, make_prefill_inputs, mask_from_runs, relayout)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -348,3 +350,55 @@ def test_generator_is_seeded_and_frame_correlated():
     within = vis[:64].std(axis=0).mean()
     across = vis[::64].std(axis=0).mean()
     assert within < 0.7 < across
+
+
+# ---------------------------------------------------------------------- P15
+
+# Several vision runs in one sequence (paper summary page, "Method": tokens
+# are split into vision and text sets by position; the NSA branches take the
+# vision set). Runs straddle block boundaries, text runs are 1..many tokens.
+SPAN_RUNS = [
+    [("v", 100), ("t", 7), ("v", 120), ("t", 30)],
+    [("t", 3), ("v", 64), ("t", 1), ("v", 64), ("t", 5), ("v", 92), ("t", 9)],
+    [("v", 1), ("t", 2), ("v", 150), ("t", 40), ("v", 105)],
+    [("t", 20), ("v", 70), ("t", 1), ("v", 1), ("t", 1), ("v", 184)],
+]
+
+
+def _spans_case(runs, hq=4, hkv=2, d=16, k=3, w=50, seed=5):
+    m = mask_from_runs(runs)
+    nv = int(m.sum())
+    base = small(n_vis=nv, before=0, after=len(m) - nv, hq=hq, hkv=hkv, d=d, k=k, w=w, seed=seed)
+    return base, relayout(base, m)
+
+
+@pytest.mark.parametrize("runs", SPAN_RUNS)
+def test_p15_vision_rows_see_the_vision_tokens_in_order(runs):
+    base, inp = _spans_case(runs)
+    a = oracle.prefill(base, want=("lse", "sel", "ocmp", "osel", "oswa"))
+    b = oracle.prefill(inp, want=("lse", "sel", "ocmp", "osel", "oswa"))
+    va = np.nonzero(base["is_vision"])[0]
+    vb = np.nonzero(inp["is_vision"])[0]
+    for name in ("out", "lse", "sel", "ocmp", "osel", "oswa"):
+        np.testing.assert_array_equal(a[name][va], b[name][vb], err_msg=name)
+
+
+@pytest.mark.parametrize("runs", SPAN_RUNS)
+def test_p15_text_rows_dense_causal_with_several_vision_runs(runs):
+    _, inp = _spans_case(runs)
+    r = oracle.prefill(inp)
+    ref = sdpa_causal(inp["q"], inp["k"], inp["v"], 4, 2)
+    text = np.nonzero(inp["is_vision"] == 0)[0]
+    np.testing.assert_allclose(r["out"][text], ref[text], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("runs", SPAN_RUNS[:2])
+def test_p15_oracle_equals_brute_force_with_several_vision_runs(runs):
+    _, inp = _spans_case(runs)
+    r = oracle.prefill(inp, want=("sel", "ocmp", "osel", "oswa"))
+    b = brute.layer(inp)
+    V = b["vis"]
+    np.testing.assert_allclose(r["out"], b["out"], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(r["sel"][V], b["sel"])
+    for name in ("ocmp", "osel", "oswa"):
+        np.testing.assert_allclose(r[name][V], b[name], rtol=0, atol=1e-12)
