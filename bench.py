@@ -137,6 +137,42 @@ def run_spans_bench(inp, shape, steps, warmup, one_run_ms):
             "kernels_ms": {n: round(t, 4) for n, (t, _) in sorted(kern.items(), key=lambda x: -x[1][0])}}
 
 
+def run_dense_bench(dev, shape, steps, warmup, nsa_ms):
+    """Dense-NSA mode on the same tokens: dense causal GQA over all of them."""
+    import torch
+    from sparse_attention_long_nsa_amd import binding
+    r = binding.prefill_dense(dev["q"], dev["k"], dev["v"])
+    out, ws = r["out"], r["workspace"]
+    for _ in range(warmup):
+        binding.prefill_dense(dev["q"], dev["k"], dev["v"], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        binding.prefill_dense(dev["q"], dev["k"], dev["v"], out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    binding.timing_reset()
+    binding.timing_enable(True)
+    for _ in range(steps):
+        binding.prefill_dense(dev["q"], dev["k"], dev["v"], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    kern = {k: {"avg_ms": round(tot / cnt, 4), "launches": cnt}
+            for k, (tot, cnt) in binding.timing_read().items()}
+    binding.timing_enable(False)
+    binding.timing_reset()
+    n = shape.n_tokens
+    flops = 4.0 * shape.head_dim * shape.n_q_heads * n * (n + 1) / 2
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"dense: {ms:.3f} ms/step, {tf:.1f} TF/s ({nsa_ms / ms:.4f} of its time for NSA)")
+    return {"ms_per_step": round(ms, 3), "tokens_per_s": round(n / (ms * 1e-3), 1),
+            "algorithmic_tflop": round(flops / 1e12, 3), "tflops": round(tf, 1),
+            "mfma_peak_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "nsa_speedup": round(ms / nsa_ms, 2), "steps": steps, "kernels": kern}
+
+
 def cpu_baseline(inp, n_vis_rows, n_text_rows):
     """The fp64 oracle, as it stands, on a bounded row sample of the same
     workload; per-row times extrapolated to the whole sequence."""
@@ -249,6 +285,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-spans", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer library runs on a single MI355X and has no "
@@ -320,6 +357,10 @@ def main():
     if not args.no_decode:
         decode = run_decode_bench(max(10, args.steps), args.warmup)
 
+    dense = None
+    if not args.no_dense:
+        dense = run_dense_bench(dev, shape, 3, 1, ms)
+
     spans = None
     if not args.no_spans:
         spans = run_spans_bench(inp, shape, max(3, args.steps // 2), 1, ms)
@@ -362,6 +403,7 @@ def main():
         "sweep": sweep,
         "decode": decode,
         "several_vision_runs": spans,
+        "dense_mode": dense,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -119,6 +119,31 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
                        float *lse_out, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* -------------------------------------------------------------- dense mode
+ * Dense-NSA inference (VideoNSA paper summary page, "Key claims" and
+ * "Results": the sparse-trained weights run under full attention): every
+ * token, vision or text, attends to every earlier token and itself with
+ * dense causal GQA (query head h reads KV head h / (Hq / Hkv)); no branches,
+ * gates or compression. Uses n_tokens, n_q_heads, n_kv_heads, head_dim,
+ * scale and dtype of the descriptor; block_size, top_k and window are not
+ * read. Supported: head_dim in {64, 128}, at most 8 query heads per KV head
+ * (7 at d = 128). fp32 inputs are used as fp16 (products in fp16, fp32
+ * accumulation).
+ *   q            device [N, Hq, d]   (dtype)
+ *   k, v         device [N, Hkv, d]  (dtype)
+ *   out          device [N, Hq, d]   float32
+ *   lse_out      device [N, Hq] float32 natural-log log-sum-exp of the scaled
+ *                logits, or NULL
+ *   workspace    device, >= nsa_prefill_dense_workspace_size bytes, 256-B
+ *                aligned (the packed key/value tiles: 4 * N * Hkv * d bytes
+ *                rounded up to whole 64-token blocks, plus fp16 copies of q, k,
+ *                v for fp32 inputs)
+ * Errors as for nsa_prefill: nothing is launched unless the status is NSA_OK. */
+nsa_status nsa_prefill_dense_workspace_size(const nsa_prefill_desc *desc, size_t *bytes);
+nsa_status nsa_prefill_dense(const nsa_prefill_desc *desc, const void *q, const void *k,
+                             const void *v, float *out, float *lse_out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------- decode
  * One new query per sequence, at the last slot (L-1) of its vision cache
  * (VideoNSA paper summary page, "Method"; evaluated exactly as prefill's row

@@ -162,6 +162,17 @@ def prefill(inp: dict, rows=None, inject_sel=None, top_k=None, window=None, scal
     return res
 
 
+def dense(inp: dict, rows=None) -> np.ndarray:
+    """Dense-NSA mode (paper summary page, "Key claims" and "Results": the same
+    weights under full attention): every token attends causally to all earlier
+    tokens with GQA, which is the oracle's text-row path applied to every row,
+    so this evaluates the layer with every token marked as text. Returns
+    out [n_rows,Hq,d] fp64."""
+    all_text = dict(inp)
+    all_text["is_vision"] = np.zeros_like(np.asarray(inp["is_vision"]), dtype=np.uint8)
+    return prefill(all_text, rows=rows, want=())["out"]
+
+
 def decode(inp: dict, k_cmp: np.ndarray, v_cmp: np.ndarray, inject_sel=None,
            top_k=None, window=None, scale=0.0, want=("sel", "lse", "scores", "counts")) -> dict:
     """One query per sequence at the last cache slot; ``inp`` holds q [Bt,Hq,d],

@@ -22,6 +22,7 @@ EXPORTED = (
     "nsa_prefill_workspace_size", "nsa_prefill", "nsa_decode_workspace_size", "nsa_decode",
     "nsa_cmp_pool", "nsa_timing_enable", "nsa_timing_reset", "nsa_timing_read",
     "nsa_status_string", "nsa_version", "nsa_probe_mfma_bf16",
+    "nsa_prefill_dense_workspace_size", "nsa_prefill_dense",
 )
 
 
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.nsa_prefill_workspace_size.restype = ctypes.c_int
         L.nsa_prefill.argtypes = [ctypes.POINTER(PrefillDesc)] + [P] * 13 + [S, P]
         L.nsa_prefill.restype = ctypes.c_int
+        L.nsa_prefill_dense_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.POINTER(S)]
+        L.nsa_prefill_dense_workspace_size.restype = ctypes.c_int
+        L.nsa_prefill_dense.argtypes = [ctypes.POINTER(PrefillDesc)] + [P] * 6 + [S, P]
+        L.nsa_prefill_dense.restype = ctypes.c_int
         L.nsa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.POINTER(S)]
         L.nsa_decode_workspace_size.restype = ctypes.c_int
         L.nsa_decode.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 10 + [S, P]
@@ -212,6 +217,42 @@ def prefill(q, k, v, is_vision, w_cmp_k, w_cmp_v, gate_logits, top_k, window, bl
                            _stream(stream))
     if st != NSA_OK:
         raise NsaError(st, "nsa_prefill")
+    res["workspace"] = workspace
+    return res
+
+
+def prefill_dense_workspace_size(desc: PrefillDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().nsa_prefill_dense_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_prefill_dense_workspace_size")
+    return n.value
+
+
+def prefill_dense(q, k, v, scale=0.0, out=None, want_lse=False, workspace=None, stream=None) -> dict:
+    """Runs nsa_prefill_dense (dense causal GQA over every token). q [N,Hq,d],
+    k/v [N,Hkv,d] on the device (bf16 or fp32, one dtype). Returns a dict with
+    "out" (fp32) and optionally "lse"."""
+    desc = prefill_desc(q, k, 1, 1, 64, scale)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    for name, t, shape in (("q", q, (n, hq, d)), ("k", k, (n, hkv, d)), ("v", v, (n, hkv, d))):
+        _check_dev(name, t, q.dtype, shape)
+    dev = q.device
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (n, hq, d))
+    res = {"out": out}
+    lse = None
+    if want_lse:
+        lse = res["lse"] = torch.empty((n, hq), dtype=torch.float32, device=dev)
+    ws_bytes = prefill_dense_workspace_size(desc)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    st = lib().nsa_prefill_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_prefill_dense")
     res["workspace"] = workspace
     return res
 

@@ -122,6 +122,45 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
   return NSA_OK;
 }
 
+// Dense causal GQA over all tokens (Dense-NSA mode).
+struct DensePlan {
+  int64_t N = 0;
+  int hq = 0, hkv = 0, d = 0, G = 0, n_tiles = 0;
+  bool fp32 = false;
+  float scale = 0.f;
+  size_t off_q16 = 0, off_k16 = 0, off_v16 = 0, off_kv = 0, total = 0;
+};
+
+nsa_status plan_dense(const nsa_prefill_desc *ds, DensePlan &pl) {
+  if (!ds) return NSA_ERR_INVALID_ARG;
+  if (ds->n_tokens < 1 || ds->n_q_heads < 1 || ds->n_kv_heads < 1 || ds->head_dim < 1)
+    return NSA_ERR_INVALID_ARG;
+  if (ds->n_q_heads % ds->n_kv_heads != 0) return NSA_ERR_INVALID_ARG;
+  if (ds->dtype != NSA_DTYPE_BF16 && ds->dtype != NSA_DTYPE_FP32) return NSA_ERR_INVALID_ARG;
+  if (!(ds->scale == ds->scale)) return NSA_ERR_INVALID_ARG;  // NaN
+  pl.N = ds->n_tokens;
+  pl.hq = ds->n_q_heads;
+  pl.hkv = ds->n_kv_heads;
+  pl.d = ds->head_dim;
+  pl.G = pl.hq / pl.hkv;
+  pl.fp32 = ds->dtype == NSA_DTYPE_FP32;
+  if (!supported_heads(pl.d, pl.G, false)) return NSA_ERR_UNSUPPORTED;
+  if (pl.N > (int64_t)INT32_MAX / 2) return NSA_ERR_UNSUPPORTED;
+  pl.scale = ds->scale > 0.f ? ds->scale : 1.0f / sqrtf((float)pl.d);
+  pl.n_tiles = (int)((pl.N + kBlk - 1) / kBlk);
+  const size_t H = (size_t)pl.hq, Hk = (size_t)pl.hkv, D = (size_t)pl.d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  if (pl.fp32) {
+    pl.off_q16 = take(sizeof(uint16_t) * pl.N * H * D);
+    pl.off_k16 = take(sizeof(uint16_t) * pl.N * Hk * D);
+    pl.off_v16 = take(sizeof(uint16_t) * pl.N * Hk * D);
+  }
+  pl.off_kv = take(sizeof(uint16_t) * (size_t)pl.n_tiles * Hk * packed_kv_block_elems(pl.d));
+  pl.total = off;
+  return NSA_OK;
+}
+
 template <class T> T *at(void *base, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(base) + off);
 }
@@ -289,6 +328,49 @@ nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim, int32
   PoolJob j{x, w, n_heads, n_rows / kBlk, static_cast<uint16_t *>(out_bf16), nullptr, nullptr, out_f32};
   if (launch_cmp_pool(j, nullptr, head_dim, dtype == NSA_DTYPE_FP32, static_cast<hipStream_t>(stream)) != hipSuccess)
     return NSA_ERR_HIP;
+  return NSA_OK;
+}
+
+nsa_status nsa_prefill_dense_workspace_size(const nsa_prefill_desc *desc, size_t *bytes) {
+  if (!bytes) return NSA_ERR_INVALID_ARG;
+  DensePlan pl;
+  const nsa_status st = plan_dense(desc, pl);
+  if (st != NSA_OK) return st;
+  *bytes = pl.total;
+  return NSA_OK;
+}
+
+nsa_status nsa_prefill_dense(const nsa_prefill_desc *desc, const void *q, const void *k,
+                             const void *v, float *out, float *lse_out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  DensePlan pl;
+  const nsa_status st = plan_dense(desc, pl);
+  if (st != NSA_OK) return st;
+  if (!q || !k || !v || !out) return NSA_ERR_INVALID_ARG;
+  const void *ptrs[] = {q, k, v, out, lse_out};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return NSA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < pl.total) return NSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return NSA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t H = pl.hq, Hk = pl.hkv, D = pl.d;
+  const uint16_t *qb = static_cast<const uint16_t *>(q);
+  const uint16_t *kb = static_cast<const uint16_t *>(k);
+  const uint16_t *vb = static_cast<const uint16_t *>(v);
+  hipError_t e = hipSuccess;
+  if (pl.fp32) {  // every product in fp16, as the text rows of nsa_prefill
+    uint16_t *q16 = at<uint16_t>(workspace, pl.off_q16), *k16 = at<uint16_t>(workspace, pl.off_k16);
+    uint16_t *v16 = at<uint16_t>(workspace, pl.off_v16);
+    NSA_LAUNCH("to_f16_q", launch_to_f16(static_cast<const float *>(q), pl.N * H * D, q16, s));
+    NSA_LAUNCH("to_f16_k", launch_to_f16(static_cast<const float *>(k), pl.N * Hk * D, k16, s));
+    NSA_LAUNCH("to_f16_v", launch_to_f16(static_cast<const float *>(v), pl.N * Hk * D, v16, s));
+    qb = q16; kb = k16; vb = v16;
+  }
+  uint16_t *kv = at<uint16_t>(workspace, pl.off_kv);
+  NSA_LAUNCH("pack_dense", launch_pack_tiles(kb, vb, 0, (int)pl.N, pl.hkv, pl.n_tiles, kv, pl.d,
+                                             pl.fp32, s));
+  DenseParams dp{qb, kv, out, lse_out, pl.N, pl.hq, pl.hkv, pl.n_tiles, pl.scale * kLog2e};
+  NSA_LAUNCH("dense_attn", launch_dense_attn(dp, pl.d, pl.G, pl.fp32, s));
   return NSA_OK;
 }
 

@@ -365,6 +365,66 @@ __global__ __launch_bounds__(D) void text_merge_kernel(TextParams p) {
   p.out[(text_pos(p, r) * p.hq + h) * D + d] = acc / L;
 }
 
+// ------------------------------------------------------- dense causal GQA
+// Every token attends to every earlier token and itself (the Dense-NSA mode
+// of the VideoNSA paper summary page, "Key claims" and "Results": the
+// sparse-trained weights run under full attention). One (64-query tile, KV
+// group, head part) per workgroup over the packed chunks 0 .. tile; only the
+// last chunk is masked. Work per tile grows with the tile index, so tiles go
+// heaviest first (longest-processing-time order as slots free up); the head
+// parts of one (tile, group) sit eight ids apart, i.e. on one XCD at about
+// the same time, and share its L2 for the key tiles.
+template <int D, int G, bool F16, int HW, int H0>
+__device__ __forceinline__ void dense_body(const DenseParams &p, int g, int tile, Ring4<D> rg) {
+  using T = PackedTile<D>;
+  constexpr int SE = T::KE + T::VE;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4;
+  const int64_t r = (int64_t)tile * kBlk + wv * 16 + (lane & 15);
+  const bool rvalid = r < p.n;
+  u16x8 qf[HW][D / 32];
+  const int64_t qrow = (rvalid ? r : 0) * p.hq + (int64_t)g * G + H0;
+  load_q_h<D, HW>(qf, p.q, qrow, rvalid, lane);
+  f32x4 o[HW][D / 16];
+  float lse2[HW];
+  const uint16_t *kv = p.kv + (int64_t)g * p.n_tiles * SE;
+  const int rl = rvalid ? (int)(r - (int64_t)tile * kBlk) : -1;  // row within the last chunk
+  one_pass<D, HW, F16>(o, lse2, qf, p.sl2, tile + 1, rg.r0, rg.r1, rg.r2, rg.r3,
+                       [&](int c) { return kv + (int64_t)c * SE; },
+                       [&](int c, int &lo, int &hi) {
+                         lo = 0;
+                         hi = !rvalid ? -1 : c < tile ? kBlk - 1 : rl;
+                       });
+  if (rvalid) {
+#pragma unroll
+    for (int h = 0; h < HW; ++h) {
+      if (p.lse && grp == 0) p.lse[qrow + h] = lse2[h] * 0.69314718055994531f;
+      float *dst = p.out + (qrow + h) * D + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[h][dt];
+    }
+  }
+}
+
+template <int D, int G, bool F16>
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dense_attn_kernel(DenseParams p) {
+  using S = HeadSplit<G>;
+  constexpr int KE = PackedTile<D>::KE;
+  __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
+  const Ring4<D> rg{r0, r1, r2, r3};
+  const int i = blockIdx.x;
+  const int half = (i >> 3) % S::N;
+  const int u = (i / (8 * S::N)) * 8 + (i & 7);  // (tile, group), heaviest first
+  if (u >= p.n_tiles * p.hkv) return;
+  const int tile = p.n_tiles - 1 - u / p.hkv;
+  const int g = u % p.hkv;
+  if (half == 0) dense_body<D, G, F16, S::size(0), 0>(p, g, tile, rg);
+  else if constexpr (S::N > 1) {
+    if (half == 1) dense_body<D, G, F16, S::size(1), S::first(1)>(p, g, tile, rg);
+    else if constexpr (S::N > 2) dense_body<D, G, F16, S::size(2), S::first(2)>(p, g, tile, rg);
+  }
+}
+
 // ------------------------------------------------------------- launchers
 template <int D, int G, bool F16>
 hipError_t run_swa(const SwaParams &p, hipStream_t st) {
@@ -379,6 +439,15 @@ hipError_t run_text(const TextParams &p, hipStream_t st) {
   const unsigned n = (unsigned)p.n_tiles * (unsigned)p.hkv * (unsigned)p.n_split * HeadSplit<G>::N;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((text_attn_kernel<D, G, F16>), dim3(xcd_grid(n)), dim3(kThreadsH), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int D, int G, bool F16>
+hipError_t run_dense(const DenseParams &p, hipStream_t st) {
+  const unsigned u = (unsigned)p.n_tiles * (unsigned)p.hkv;
+  if (u == 0) return hipSuccess;
+  const unsigned n = (u + 7) / 8 * 8 * HeadSplit<G>::N;
+  hipLaunchKernelGGL((dense_attn_kernel<D, G, F16>), dim3(n), dim3(kThreadsH), 0, st, p);
   return hipGetLastError();
 }
 
@@ -423,5 +492,10 @@ hipError_t launch_text_merge(const TextParams &p, int d, hipStream_t st) {
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st) {
   if (f16) { NSA_SWITCH_G(run_text, true, p, st) }
   NSA_SWITCH_G(run_text, false, p, st)
+}
+
+hipError_t launch_dense_attn(const DenseParams &p, int d, int G, bool f16, hipStream_t st) {
+  if (f16) { NSA_SWITCH_G(run_dense, true, p, st) }
+  NSA_SWITCH_G(run_dense, false, p, st)
 }
 }  // namespace nsa

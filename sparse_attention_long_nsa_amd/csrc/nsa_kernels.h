@@ -90,6 +90,16 @@ struct TextParams {
   const int32_t *tnvb = nullptr;  // text row -> vision tokens before it
 };
 
+struct DenseParams {
+  const uint16_t *q;       // [N, Hq, d]: bf16, or fp16
+  const uint16_t *kv;      // packed rows [Hkv][n_tiles][K, V^T]
+  float *out;              // [N, Hq, d]
+  float *lse;              // [N, Hq] natural log, or null
+  int64_t n;               // tokens
+  int hq, hkv, n_tiles;
+  float sl2;
+};
+
 // One slice of the token-kind mask, as kernel arguments: bit j of word i
 // says whether position base + 32 i + j is a vision token.
 constexpr int kMaskWords = 512;
@@ -144,6 +154,7 @@ size_t packed_kv_block_elems(int d);  // elements of one packed (K, V^T) block
 hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_merge(const TextParams &p, int d, hipStream_t st);
+hipError_t launch_dense_attn(const DenseParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_decode(const DecodeParams &p, int d, int G, hipStream_t st);
 
 // Which (head_dim, query heads per KV head) pairs have kernels.

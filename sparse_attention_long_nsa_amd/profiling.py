@@ -40,6 +40,8 @@ KERNELS = [
     ("swa_attn_kernel", "swa_attn", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
     ("text_attn_kernel", "text_attn", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
     ("text_merge_kernel", "text_merge", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
+    ("dense_attn_kernel", "dense_attn", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
+    ("row_map_kernel", "row_maps", "sparse_attention_long_nsa_amd/csrc/nsa_rowmap.hip"),
     ("topk_kernel", "blk_score_topk", "sparse_attention_long_nsa_amd/csrc/nsa_topk.hip"),
     ("cmp_pool_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_pool.hip"),
     ("pack_kv_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_sel_attn.hip"),
@@ -49,6 +51,7 @@ KERNELS = [
     ("mfma_loop_kernel", "mfma_probe", "sparse_attention_long_nsa_amd/csrc/nsa_probe.hip"),
 ]
 DECODE_KERNELS = ("dec_item_cmp_win", "dec_item_sel", "dec_select", "dec_combine")
+DENSE_KERNELS = ("pack_dense", "dense_attn")
 PREFILL_KERNELS = ("sel_attn", "cmp_attn", "swa_attn", "text_attn", "text_merge", "blk_score_topk", "cmp_pool",
                    "pack_kv", "pack_cmp", "pack_text")
 
@@ -62,13 +65,19 @@ def short_name(kernel_name: str, grid: int, grid_names: dict):
     return None, None
 
 
-def pack_grid_names(n_frames: int, n_cch: int, n_tchunks: int, hkv: int, n_cmp: int) -> dict:
+def pack_grid_names(n_frames: int, n_cch: int, n_tchunks: int, hkv: int, n_cmp: int,
+                    n_all_tiles: int = 0) -> dict:
     """Grid sizes (threads) of the prefill's packing and pooling launches ->
     names (the layer pools keys and values in one launch of two grid rows;
-    single-row pooling launches are other callers', e.g. cache building)."""
+    single-row pooling launches are other callers', e.g. cache building);
+    n_all_tiles: 64-token tiles of the whole sequence (the dense mode packs
+    them all)."""
     k = "pack_kv_kernel"
-    return {(k, n_frames * hkv * 256): "pack_kv", (k, n_cch * hkv * 256): "pack_cmp",
-            (k, n_tchunks * hkv * 256): "pack_text", ("cmp_pool_kernel", 2 * min(n_cmp, 1024) * 256): "cmp_pool"}
+    names = {(k, n_frames * hkv * 256): "pack_kv", (k, n_cch * hkv * 256): "pack_cmp",
+             (k, n_tchunks * hkv * 256): "pack_text", ("cmp_pool_kernel", 2 * min(n_cmp, 1024) * 256): "cmp_pool"}
+    if n_all_tiles:
+        names[(k, n_all_tiles * hkv * 256)] = "pack_dense"
+    return names
 
 
 def decode_grid_names(batch: int, hkv: int, n_blk: int, top_k: int, window: int) -> dict:
@@ -100,7 +109,7 @@ def source_digest(path: str) -> str:
 
 def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, command: str,
                   out_md: str, group: str = "prefill") -> None:
-    keep = DECODE_KERNELS if group == "decode" else PREFILL_KERNELS
+    keep = {"decode": DECODE_KERNELS, "dense": DENSE_KERNELS}.get(group, PREFILL_KERNELS)
     dur = defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
         name, _ = short_name(r["Kernel_Name"], _grid(r), grid_names)
@@ -110,6 +119,8 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
     if group == "decode":
         dec = (bench or {}).get("decode") or {}
         kern = {k: {"avg_ms": round(v["avg_us"] * 1e-3, 4)} for k, v in dec.get("kernels", {}).items()}
+    elif group == "dense":
+        kern = ((bench or {}).get("dense_mode") or {}).get("kernels", {})
     else:
         kern = bench["kernels"] if bench else {}
     total = sum(sum(v) / len(v) for v in dur.values())
@@ -121,6 +132,11 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
         lines += [f"bench.py in the same process reported {d['us_per_step']} us per decode step "
                   f"({d['roofline']['frac'] * 100:.1f}% of the HBM roofline); its event-timed per-kernel "
                   "averages are listed beside the profiler's.", ""]
+    elif bench and group == "dense" and bench.get("dense_mode"):
+        d = bench["dense_mode"]
+        lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per dense step "
+                  f"({d['tflops']} TF/s of algorithmic flops, {d['mfma_peak_frac'] * 100:.1f}% of the bf16 "
+                  "peak); its event-timed per-kernel averages are listed beside the profiler's.", ""]
     elif bench:
         lines += [f"bench.py in the same process reported {bench['ms_per_step']} ms/step "
                   f"({bench['value']:.0f} tokens/s); its event-timed per-kernel averages are listed "
@@ -232,7 +248,8 @@ def _layer_grids(workload: str) -> dict:
     s = PREFILL_PRESETS[workload]
     n_frames = -(-s.n_vis // s.block)
     n_cch = -(-(s.n_vis // s.block) // s.block)
-    return pack_grid_names(n_frames, n_cch, -(-s.n_text // s.block), s.n_kv_heads, s.n_vis // s.block)
+    return pack_grid_names(n_frames, n_cch, -(-s.n_text // s.block), s.n_kv_heads, s.n_vis // s.block,
+                           -(-s.n_tokens // s.block))
 
 
 def main(argv=None) -> None:
@@ -249,7 +266,7 @@ def main(argv=None) -> None:
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
-    t.add_argument("--group", choices=("prefill", "decode"), default="prefill")
+    t.add_argument("--group", choices=("prefill", "decode", "dense"), default="prefill")
     m = sub.add_parser("pmc-summary")
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
         m.add_argument(f"--{k}-csv", required=True)

@@ -185,3 +185,46 @@ def test_decode_workspace_and_pointer_checks():
     assert L.nsa_decode(ctypes.byref(ddesc()), *args, None, None, FAKE, need - 1, None) == binding.NSA_ERR_WORKSPACE
     args[0] = None
     assert L.nsa_decode(ctypes.byref(ddesc()), *args, None, None, FAKE, need, None) == binding.NSA_ERR_INVALID_ARG
+
+
+def dense_ws(ds):
+    n = ctypes.c_size_t(0)
+    return binding.lib().nsa_prefill_dense_workspace_size(ctypes.byref(ds), ctypes.byref(n)), n.value
+
+
+def call_dense(ds, ptrs=None, ws=FAKE, ws_bytes=1 << 40):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None)
+    if ptrs:
+        p.update(ptrs)
+    return binding.lib().nsa_prefill_dense(ctypes.byref(ds) if ds is not None else None, p["q"], p["k"],
+                                           p["v"], p["out"], p["lse"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=28, hkv=5), binding.NSA_ERR_INVALID_ARG),
+    (dict(n=0), binding.NSA_ERR_INVALID_ARG),
+    (dict(dtype=7), binding.NSA_ERR_INVALID_ARG),
+    (dict(d=96), binding.NSA_ERR_UNSUPPORTED),
+    (dict(hq=32, hkv=4), binding.NSA_ERR_UNSUPPORTED),  # 8 query heads per KV head at d = 128
+    # block, top_k and window are not read by the dense mode
+    (dict(block=32, k=0, w=0), binding.NSA_OK),
+    (dict(dtype=1), binding.NSA_OK),
+])
+def test_dense_validation(kw, status):
+    assert dense_ws(desc(**kw))[0] == status
+
+
+def test_dense_workspace_and_pointer_checks():
+    ds = desc(n=1000)
+    st, need = dense_ws(ds)
+    # packed key and value tiles of 16 blocks of 64 tokens, bf16
+    assert st == binding.NSA_OK and need == 16 * 4 * 2 * 64 * 128 * 2
+    st32, need32 = dense_ws(desc(n=1000, dtype=1))
+    assert st32 == binding.NSA_OK and need32 > need  # plus fp16 copies of q, k, v
+    assert call_dense(None) == binding.NSA_ERR_INVALID_ARG
+    for name in ("q", "k", "v", "out"):
+        assert call_dense(ds, {name: None}) == binding.NSA_ERR_INVALID_ARG, name
+    assert call_dense(ds, {"lse": FAKE + 4}) == binding.NSA_ERR_INVALID_ARG
+    assert call_dense(ds, ws=None) == binding.NSA_ERR_WORKSPACE
+    assert call_dense(ds, ws_bytes=need - 1) == binding.NSA_ERR_WORKSPACE
+    assert call_dense(ds, ws=FAKE + 16, ws_bytes=need) == binding.NSA_ERR_WORKSPACE

@@ -13,6 +13,7 @@ Each test names the pin it checks:
   P12        linearity in v, invariance to a common key shift
   P13        permuting KV groups with their query heads permutes the output
   P14        one head per group: score == that head's compression probability
+  P16        Dense-NSA mode: every row == torch fp64 SDPA causal
   P15        several vision runs: vision rows see only the vision tokens in
              position order (equal to the one-run layout), text rows dense causal
 """
@@ -402,3 +403,13 @@ def test_p15_oracle_equals_brute_force_with_several_vision_runs(runs):
     np.testing.assert_array_equal(r["sel"][V], b["sel"])
     for name in ("ocmp", "osel", "oswa"):
         np.testing.assert_allclose(r[name][V], b[name], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------- P16
+
+@pytest.mark.parametrize("n,hq,hkv", [(300, 6, 2), (129, 4, 1), (1, 4, 4)])
+def test_p16_dense_mode_is_dense_causal_on_every_row(n, hq, hkv):
+    inp = small(n_vis=n, hq=hq, hkv=hkv)
+    out = oracle.dense(inp)
+    ref = sdpa_causal(inp["q"], inp["k"], inp["v"], hq, hkv)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
