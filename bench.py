@@ -260,6 +260,33 @@ def run_decode_bench(steps, warmup):
     torch.cuda.synchronize()
     kern = binding.timing_read()
     binding.timing_enable(False)
+    binding.timing_reset()
+
+    # cache maintenance per generated token: nsa_cache_append rewriting the
+    # cache's own last rows (so the caches stay as they are), without and
+    # with the pooling of a block the token completes
+    def append_us(L, n=50):
+        kn, vn = kcache[:, L - 1].contiguous(), vcache[:, L - 1].contiguous()
+        binding.cache_append(kn, vn, kcache, vcache, wk, wv, kc, vc, L)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(n):
+            binding.cache_append(kn, vn, kcache, vcache, wk, wv, kc, vc, L)
+        a1.record()
+        torch.cuda.synchronize()
+        binding.timing_reset()
+        binding.timing_enable(True)
+        for _ in range(n):
+            binding.cache_append(kn, vn, kcache, vcache, wk, wv, kc, vc, L)
+        torch.cuda.synchronize()
+        kt = {k: round(v[0] / v[1] * 1e3, 2) for k, v in binding.timing_read().items()}
+        binding.timing_enable(False)
+        binding.timing_reset()
+        return {"us_per_call": round(a0.elapsed_time(a1) / n * 1e3, 2), "kernel_us": kt}
+
+    # us_per_call includes the host's per-call cost (back-to-back calls)
+    append = {"row": append_us(s.cache_len - 1), "row_and_block_pool": append_us(s.cache_len)}
     nbytes = decode_bytes(s)
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {"workload": name, "batch": s.batch, "cache_len": s.cache_len, "top_k": s.top_k,
@@ -268,7 +295,8 @@ def run_decode_bench(steps, warmup):
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "algorithmic_bytes": nbytes},
-           "kernels": {k: {"avg_us": round(v[0] / v[1] * 1e3, 2), "launches": v[1]} for k, v in kern.items()}}
+           "kernels": {k: {"avg_us": round(v[0] / v[1] * 1e3, 2), "launches": v[1]} for k, v in kern.items()},
+           "cache_append": append}
     log(f"decode {name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s algorithmic")
     return res
 

@@ -190,6 +190,22 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
                       float *lse_out, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/* Appends one token per sequence to the decode caches and keeps the
+ * compressed caches current, so that nsa_decode can run at length cache_len
+ * next (the streaming use described above, in one call): k_new / v_new
+ * device [Bt, Hkv, d] bf16 are written to row cache_len - 1 of k_cache /
+ * v_cache [Bt, C, Hkv, d]; when 64 divides cache_len, the block that token
+ * completes (rows cache_len - 64 .. cache_len - 1 of every sequence) is
+ * pooled -- block mean, then y = W x with w_cmp_k / w_cmp_v [d, d] bf16, fp32
+ * arithmetic, bf16 rounding -- into row cache_len / 64 - 1 of k_cmp / v_cmp
+ * [Bt, C/64, Hkv, d]. Reads batch, cache_len, n_kv_heads, head_dim,
+ * block_size, dtype and cache_capacity of the descriptor (C =
+ * cache_capacity, or cache_len when 0). All pointers are required and
+ * 16-byte aligned. Supported: bf16, block_size 64, head_dim 64 or 128. */
+nsa_status nsa_cache_append(const nsa_decode_desc *desc, const void *k_new, const void *v_new,
+                            void *k_cache, void *v_cache, const void *w_cmp_k,
+                            const void *w_cmp_v, void *k_cmp, void *v_cmp, void *stream);
+
 /* ------------------------------------------------------------- compression
  * The compression branch's pooling step on its own (VideoNSA model card,
  * "Model Architecture": frame KV blocks are averaged; paper summary,

@@ -22,7 +22,7 @@ EXPORTED = (
     "nsa_prefill_workspace_size", "nsa_prefill", "nsa_decode_workspace_size", "nsa_decode",
     "nsa_cmp_pool", "nsa_timing_enable", "nsa_timing_reset", "nsa_timing_read",
     "nsa_status_string", "nsa_version", "nsa_probe_mfma_bf16",
-    "nsa_prefill_dense_workspace_size", "nsa_prefill_dense",
+    "nsa_prefill_dense_workspace_size", "nsa_prefill_dense", "nsa_cache_append",
 )
 
 
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_prefill_dense_workspace_size.restype = ctypes.c_int
         L.nsa_prefill_dense.argtypes = [ctypes.POINTER(PrefillDesc)] + [P] * 6 + [S, P]
         L.nsa_prefill_dense.restype = ctypes.c_int
+        L.nsa_cache_append.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 9
+        L.nsa_cache_append.restype = ctypes.c_int
         L.nsa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.POINTER(S)]
         L.nsa_decode_workspace_size.restype = ctypes.c_int
         L.nsa_decode.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 10 + [S, P]
@@ -255,6 +257,26 @@ def prefill_dense(q, k, v, scale=0.0, out=None, want_lse=False, workspace=None, 
         raise NsaError(st, "nsa_prefill_dense")
     res["workspace"] = workspace
     return res
+
+
+def cache_append(k_new, v_new, k_cache, v_cache, w_cmp_k, w_cmp_v, k_cmp, v_cmp, cache_len,
+                 block=64, stream=None) -> None:
+    """Runs nsa_cache_append: the new token's k/v [Bt,Hkv,d] go to row
+    cache_len - 1 of the caches [Bt,C,Hkv,d]; a block completed by it is pooled
+    into the compressed caches [Bt,C//block,Hkv,d] (all bf16 on the device)."""
+    bt, cap, hkv, d = k_cache.shape
+    for name, t, shape in (("k_cache", k_cache, (bt, cap, hkv, d)), ("k_new", k_new, (bt, hkv, d)),
+                           ("v_new", v_new, (bt, hkv, d)),
+                           ("v_cache", v_cache, (bt, cap, hkv, d)), ("w_cmp_k", w_cmp_k, (d, d)),
+                           ("w_cmp_v", w_cmp_v, (d, d)), ("k_cmp", k_cmp, (bt, cap // block, hkv, d)),
+                           ("v_cmp", v_cmp, (bt, cap // block, hkv, d))):
+        _check_dev(name, t, k_cache.dtype, shape)
+    desc = DecodeDesc(bt, int(cache_len), hkv, hkv, d, block, 1, 1, 0.0,
+                      {torch.bfloat16: NSA_DTYPE_BF16, torch.float32: NSA_DTYPE_FP32}[k_cache.dtype], cap)
+    st = lib().nsa_cache_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(w_cmp_k), _ptr(w_cmp_v), _ptr(k_cmp), _ptr(v_cmp), _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_cache_append")
 
 
 def decode_desc(q, k_cache, top_k, window, block=64, scale=0.0, cache_len=None) -> DecodeDesc:

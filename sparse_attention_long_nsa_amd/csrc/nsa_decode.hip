@@ -478,4 +478,43 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
   return NSA_OK;
 }
 
+nsa_status nsa_cache_append(const nsa_decode_desc *desc, const void *k_new, const void *v_new,
+                            void *k_cache, void *v_cache, const void *w_cmp_k, const void *w_cmp_v,
+                            void *k_cmp, void *v_cmp, void *stream) {
+  if (!desc) return NSA_ERR_INVALID_ARG;
+  const nsa_decode_desc &ds = *desc;
+  if (ds.batch < 1 || ds.cache_len < 1 || ds.n_kv_heads < 1 || ds.head_dim < 1 || ds.cache_capacity < 0)
+    return NSA_ERR_INVALID_ARG;
+  if (ds.dtype != NSA_DTYPE_BF16 && ds.dtype != NSA_DTYPE_FP32) return NSA_ERR_INVALID_ARG;
+  const int64_t L = ds.cache_len;
+  const int64_t cap = ds.cache_capacity > 0 ? ds.cache_capacity : L;
+  if (cap < L) return NSA_ERR_INVALID_ARG;
+  const void *ptrs[] = {k_new, v_new, k_cache, v_cache, w_cmp_k, w_cmp_v, k_cmp, v_cmp};
+  for (const void *ptr : ptrs)
+    if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0) return NSA_ERR_INVALID_ARG;
+  if (ds.dtype != NSA_DTYPE_BF16 || ds.block_size != kBlk) return NSA_ERR_UNSUPPORTED;
+  if (ds.head_dim != 64 && ds.head_dim != 128) return NSA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int C = ds.n_kv_heads * ds.head_dim;  // columns of one cache row
+  {
+    Timed tm("cache_append", s);
+    if (launch_append_rows(static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
+                           static_cast<uint16_t *>(k_cache), static_cast<uint16_t *>(v_cache), ds.batch, C,
+                           cap, L - 1, s) != hipSuccess)
+      return NSA_ERR_HIP;
+  }
+  if (L % kBlk == 0) {  // the token completed block L/64 - 1: pool it for every sequence
+    const int64_t row0 = L - kBlk, cap_blk = cap / kBlk, b = L / kBlk - 1;
+    PoolJob jk{static_cast<const uint16_t *>(k_cache) + row0 * C, w_cmp_k, ds.n_kv_heads, ds.batch,
+               static_cast<uint16_t *>(k_cmp) + b * C, nullptr, nullptr, nullptr};
+    PoolJob jv{static_cast<const uint16_t *>(v_cache) + row0 * C, w_cmp_v, ds.n_kv_heads, ds.batch,
+               static_cast<uint16_t *>(v_cmp) + b * C, nullptr, nullptr, nullptr};
+    jk.in_stride = jv.in_stride = cap;       // sequence s's block starts cap rows after s-1's
+    jk.out_stride = jv.out_stride = cap_blk;
+    Timed tm("cache_pool", s);
+    if (launch_cmp_pool(jk, &jv, ds.head_dim, false, s) != hipSuccess) return NSA_ERR_HIP;
+  }
+  return NSA_OK;
+}
+
 }  // extern "C"

@@ -29,6 +29,8 @@ struct PoolJob {
   uint16_t *out_h16; // fp16 rounding of the result (or null)
   float *out_f32;    // fp32 result (or null)
   const int32_t *rows = nullptr;  // pooled row i is x row rows[i] (or i)
+  int64_t in_stride = kBlk;       // rows of x between the first rows of blocks
+  int64_t out_stride = 1;         // output rows between consecutive blocks
 };
 
 struct CmpAttnParams {
@@ -130,6 +132,11 @@ struct DecodeParams {
 
 size_t pool_smem_bytes(int n_heads, int d);
 hipError_t launch_cmp_pool(const PoolJob &j0, const PoolJob *j1, int d, bool fp32, hipStream_t st);
+// Copies one row of n_cols bf16 per sequence (src [Bt, n_cols]) to row `row`
+// of dst [Bt, cap, n_cols], for keys and values at once.
+hipError_t launch_append_rows(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_cache,
+                              uint16_t *v_cache, int batch, int n_cols, int64_t cap, int64_t row,
+                              hipStream_t st);
 // fp32 -> bf16 high part (+ optional bf16 residual), or fp32 -> fp16.
 hipError_t launch_split_bf16(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t st);
 hipError_t launch_to_f16(const float *x, int64_t n, uint16_t *out, hipStream_t st);

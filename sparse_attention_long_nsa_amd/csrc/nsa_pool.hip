@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kPoolThreads) void cmp_pool_kernel(PoolJob j0, Pool
   const int tid = threadIdx.x;
 
   for (int64_t b = blockIdx.x; b < jb.n_blk; b += gridDim.x) {
-    const T *xb = x + b * kBlk * (int64_t)C;
+    const T *xb = x + b * jb.in_stride * (int64_t)C;
     const int32_t *rb = jb.rows ? jb.rows + b * kBlk : nullptr;
     for (int item = tid; item < P * CH; item += kPoolThreads) {
       const int ch = item % CH, rp = item / CH;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kPoolThreads) void cmp_pool_kernel(PoolJob j0, Pool
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc += wv[e] * mg[i + e];
       }
-      const int64_t dst = (b * hkv + g) * (int64_t)D + r;
+      const int64_t dst = (b * jb.out_stride * hkv + g) * (int64_t)D + r;
       const uint16_t hi = f2bf_bits(acc);
       if (jb.out_hi) jb.out_hi[dst] = hi;
       if (jb.out_lo) jb.out_lo[dst] = f2bf_bits(acc - bfbits2f(hi));
@@ -85,6 +85,22 @@ __global__ __launch_bounds__(kPoolThreads) void cmp_pool_kernel(PoolJob j0, Pool
     }
     __syncthreads();
   }
+}
+
+// One new row per sequence into its cache, 16 bytes per thread.
+__global__ __launch_bounds__(256) void append_rows_kernel(const uint16_t *__restrict__ k_new,
+                                                          const uint16_t *__restrict__ v_new,
+                                                          uint16_t *__restrict__ k_cache,
+                                                          uint16_t *__restrict__ v_cache, int batch,
+                                                          int n_cols, int64_t cap, int64_t row) {
+  const int per = n_cols / 8;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 2 * batch * per) return;
+  const int kv = i / (batch * per), rest = i % (batch * per);
+  const int b = rest / per, c = rest % per;
+  const uint16_t *src = (kv ? v_new : k_new) + (int64_t)b * n_cols + 8 * c;
+  uint16_t *dst = (kv ? v_cache : k_cache) + ((int64_t)b * cap + row) * n_cols + 8 * c;
+  *reinterpret_cast<u16x8 *>(dst) = *reinterpret_cast<const u16x8 *>(src);
 }
 
 // fp32 inputs -> bf16 high part (and optionally the bf16 residual).
@@ -129,6 +145,16 @@ hipError_t launch_cmp_pool(const PoolJob &j0, const PoolJob *j1, int d, bool fp3
     if (d == 64) hipLaunchKernelGGL((cmp_pool_kernel<bf16, 64>), grid, dim3(kPoolThreads), smem, st, j0, jj);
     else hipLaunchKernelGGL((cmp_pool_kernel<bf16, 128>), grid, dim3(kPoolThreads), smem, st, j0, jj);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_append_rows(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_cache,
+                              uint16_t *v_cache, int batch, int n_cols, int64_t cap, int64_t row,
+                              hipStream_t st) {
+  const int n = 2 * batch * (n_cols / 8);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, st, k_new, v_new,
+                     k_cache, v_cache, batch, n_cols, cap, row);
   return hipGetLastError();
 }
 

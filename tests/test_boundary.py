@@ -228,3 +228,30 @@ def test_dense_workspace_and_pointer_checks():
     assert call_dense(ds, ws=None) == binding.NSA_ERR_WORKSPACE
     assert call_dense(ds, ws_bytes=need - 1) == binding.NSA_ERR_WORKSPACE
     assert call_dense(ds, ws=FAKE + 16, ws_bytes=need) == binding.NSA_ERR_WORKSPACE
+
+
+def call_append(ds, ptrs=None):
+    p = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, wk=FAKE, wv=FAKE, kcmp=FAKE, vcmp=FAKE)
+    if ptrs:
+        p.update(ptrs)
+    return binding.lib().nsa_cache_append(ctypes.byref(ds) if ds is not None else None, p["kn"], p["vn"],
+                                          p["kc"], p["vc"], p["wk"], p["wv"], p["kcmp"], p["vcmp"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), binding.NSA_ERR_INVALID_ARG),
+    (dict(L=0), binding.NSA_ERR_INVALID_ARG),
+    (dict(cap=100, L=101), binding.NSA_ERR_INVALID_ARG),   # the new row does not fit
+    (dict(dtype=1), binding.NSA_ERR_UNSUPPORTED),
+    (dict(block=32), binding.NSA_ERR_UNSUPPORTED),
+    (dict(d=96), binding.NSA_ERR_UNSUPPORTED),
+])
+def test_cache_append_validation(kw, status):
+    assert call_append(ddesc(**kw)) == status
+
+
+def test_cache_append_pointer_checks():
+    assert call_append(None) == binding.NSA_ERR_INVALID_ARG
+    for name in ("kn", "vn", "kc", "vc", "wk", "wv", "kcmp", "vcmp"):
+        assert call_append(ddesc(), {name: None}) == binding.NSA_ERR_INVALID_ARG, name
+    assert call_append(ddesc(), {"kc": FAKE + 8}) == binding.NSA_ERR_INVALID_ARG

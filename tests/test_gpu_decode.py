@@ -118,6 +118,53 @@ def test_streaming_decode_matches_oracle_across_block_boundaries():
         assert orep.ok(), (L, orep)
 
 
+def test_generation_with_cache_append():
+    # nsa_cache_append keeps the caches: one token appended per step (its
+    # block pooled in the same call when it completes); the caches must equal
+    # the reference rows and the compressed caches nsa_cmp_pool's result,
+    # bit for bit, and each decode step must match the oracle
+    bt, hq, hkv, d, k, w, cap = 3, 8, 2, 128, 6, 96, 64 * 12
+    print(f"\n[case] cache_append: bt {bt} hq {hq} hkv {hkv} d {d} cap {cap}", flush=True)
+    full = make_decode_inputs(DecodeShape(bt, cap, hq, hkv, d, 64, k, w), seed=31)
+    rng = np.random.Generator(np.random.PCG64(32))
+    kref, vref = bf(full["k_cache"]), bf(full["v_cache"])
+    wk, wv = bf(full["w_k"]), bf(full["w_v"])
+    kdev, vdev = torch.zeros_like(kref), torch.zeros_like(vref)
+    kc = torch.zeros((bt, cap // 64, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    L0 = 64 * 3 + 5
+    for L in range(1, L0 + 1):  # build the first L0 rows through the entry point too
+        binding.cache_append(kref[:, L - 1].contiguous(), vref[:, L - 1].contiguous(), kdev, vdev, wk, wv,
+                             kc, vc, L)
+    for L in range(L0 + 1, L0 + 140):
+        binding.cache_append(kref[:, L - 1].contiguous(), vref[:, L - 1].contiguous(), kdev, vdev, wk, wv,
+                             kc, vc, L)
+        if (L - L0) % 9 and L % 64 not in (0, 1):
+            continue
+        torch.cuda.synchronize()
+        assert torch.equal(kdev[:, :L], kref[:, :L]) and torch.equal(vdev[:, :L], vref[:, :L]), L
+        assert not kdev[:, L:].any(), L  # nothing written past the new row
+        nb = L // 64
+        for s_ in range(bt):
+            for b in range(nb):
+                want_k = binding.cmp_pool(kref[s_, 64 * b: 64 * b + 64], wk)["bf16"][0]
+                want_v = binding.cmp_pool(vref[s_, 64 * b: 64 * b + 64], wv)["bf16"][0]
+                assert torch.equal(kc[s_, b], want_k) and torch.equal(vc[s_, b], want_v), (L, s_, b)
+        assert not kc[:, nb:].any(), L
+        q = round_to_bf16(rng.standard_normal((bt, hq, d)).astype(np.float32))
+        gates = rng.standard_normal((bt, hq, 3)).astype(np.float32)
+        r = binding.decode(bf(q), kdev, vdev, kc, vc, torch.from_numpy(gates).cuda(), k, w,
+                           want_sel=True, cache_len=L)
+        torch.cuda.synchronize()
+        inp = dict(q=q, k_cache=full["k_cache"][:, :L], v_cache=full["v_cache"][:, :L], gates=gates,
+                   shape=DecodeShape(bt, L, hq, hkv, d, 64, k, w))
+        rep, orep, _ = parity.check_decode(inp, kc[:, :nb].float().cpu().numpy(), vc[:, :nb].float().cpu().numpy(),
+                                           r["out"].cpu().numpy(), r["sel_idx"].cpu().numpy())
+        print(f"L={L}", rep, "|", orep, flush=True)
+        assert rep.counted == 0, (L, rep)
+        assert orep.ok(), (L, orep)
+
+
 def test_decode_full_size_preset():
     check(make_decode_inputs(DECODE_PRESETS["decode_16x128k"], seed=0), "decode_16x128k")
 
