@@ -129,12 +129,38 @@ def run_spans_bench(inp, shape, steps, warmup, one_run_ms):
            for k in ("q", "k", "v", "w_k", "w_v")}
     dev["gates"] = torch.from_numpy(mi["gates"]).to("cuda:0")
     ms, kern, _ = run_gpu(mi, dev, shape.top_k, shape.window, steps, warmup, True)
-    del dev
     log(f"8 clips: {ms:.3f} ms/step ({ms / one_run_ms:.4f} x one run)")
+
+    # the same rows as 8 independent sequences of one clip each (varlen batch)
+    from sparse_attention_long_nsa_amd import binding
+    per = len(m) // 8
+    cu = np.arange(9, dtype=np.int64) * per
+
+    def call(out, ws):
+        return binding.prefill_varlen(dev["q"], dev["k"], dev["v"], cu, m, dev["w_k"], dev["w_v"],
+                                      dev["gates"], shape.top_k, shape.window, out=out, workspace=ws)
+
+    r = call(None, None)
+    out, ws = r["out"], r["workspace"]
+    for _ in range(warmup):
+        call(out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call(out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    vms = e0.elapsed_time(e1) / steps
+    del dev, out, ws, r
+    log(f"varlen 8 x {per}: {vms:.3f} ms/step")
     return {"layout": "8 clips of 16,384 vision tokens, 64 text tokens before each",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(shape.n_tokens / (ms * 1e-3), 1),
             "vs_one_run": round(ms / one_run_ms, 4),
-            "kernels_ms": {n: round(t, 4) for n, (t, _) in sorted(kern.items(), key=lambda x: -x[1][0])}}
+            "kernels_ms": {n: round(t, 4) for n, (t, _) in sorted(kern.items(), key=lambda x: -x[1][0])},
+            "varlen_8_sequences": {"sequence": f"{per} tokens (64 text, then 16,384 vision)",
+                                   "ms_per_step": round(vms, 4),
+                                   "tokens_per_s": round(shape.n_tokens / (vms * 1e-3), 1)}}
 
 
 def run_dense_bench(dev, shape, steps, warmup, nsa_ms):

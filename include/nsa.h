@@ -119,6 +119,31 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
                        float *lse_out, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* Several independent sequences in one call (varlen batch): tokens of
+ * sequence i are rows cu_seqlens[i] .. cu_seqlens[i+1]-1 of q, k, v,
+ * is_vision, gate_logits and out (cu_seqlens: host [n_seqs + 1], starting at 0,
+ * strictly increasing, ending at desc->n_tokens). Each sequence is its own
+ * layer call: its vision tokens, blocks, selection and window never reach
+ * another sequence, and its text tokens see only its own earlier tokens. The
+ * optional outputs are concatenated over the sequences in order: k_cmp_out /
+ * v_cmp_out [sum of N_v,i / B, Hkv, d], sel_idx_out [sum of N_v,i, Hkv, top_k]
+ * (numbering local to each sequence), lse_out [sum of N_v,i, Hq]. The
+ * sequences run one after another on the stream and share the workspace,
+ * sized for the largest (nsa_prefill_varlen_workspace_size). Every
+ * sequence is validated before anything is enqueued; each sequence's slices
+ * must meet nsa_prefill's 16-byte alignment (always so when Hq is a multiple
+ * of 4). */
+nsa_status nsa_prefill_varlen_workspace_size(const nsa_prefill_desc *desc, int32_t n_seqs,
+                                             const int64_t *cu_seqlens,
+                                             const uint8_t *is_vision, size_t *bytes);
+nsa_status nsa_prefill_varlen(const nsa_prefill_desc *desc, int32_t n_seqs,
+                              const int64_t *cu_seqlens, const void *q, const void *k,
+                              const void *v, const uint8_t *is_vision, const void *w_cmp_k,
+                              const void *w_cmp_v, const float *gate_logits, float *out,
+                              float *k_cmp_out, float *v_cmp_out, int32_t *sel_idx_out,
+                              float *lse_out, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /* -------------------------------------------------------------- dense mode
  * Dense-NSA inference (VideoNSA paper summary page, "Key claims" and
  * "Results": the sparse-trained weights run under full attention): every

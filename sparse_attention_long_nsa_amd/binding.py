@@ -23,6 +23,7 @@ EXPORTED = (
     "nsa_cmp_pool", "nsa_timing_enable", "nsa_timing_reset", "nsa_timing_read",
     "nsa_status_string", "nsa_version", "nsa_probe_mfma_bf16",
     "nsa_prefill_dense_workspace_size", "nsa_prefill_dense", "nsa_cache_append",
+    "nsa_prefill_varlen_workspace_size", "nsa_prefill_varlen",
 )
 
 
@@ -82,6 +83,11 @@ def lib() -> ctypes.CDLL:
         L.nsa_prefill_dense_workspace_size.restype = ctypes.c_int
         L.nsa_prefill_dense.argtypes = [ctypes.POINTER(PrefillDesc)] + [P] * 6 + [S, P]
         L.nsa_prefill_dense.restype = ctypes.c_int
+        L.nsa_prefill_varlen_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_int32, P, P,
+                                                        ctypes.POINTER(S)]
+        L.nsa_prefill_varlen_workspace_size.restype = ctypes.c_int
+        L.nsa_prefill_varlen.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_int32] + [P] * 14 + [S, P]
+        L.nsa_prefill_varlen.restype = ctypes.c_int
         L.nsa_cache_append.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 9
         L.nsa_cache_append.restype = ctypes.c_int
         L.nsa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.POINTER(S)]
@@ -219,6 +225,57 @@ def prefill(q, k, v, is_vision, w_cmp_k, w_cmp_v, gate_logits, top_k, window, bl
                            _stream(stream))
     if st != NSA_OK:
         raise NsaError(st, "nsa_prefill")
+    res["workspace"] = workspace
+    return res
+
+
+def prefill_varlen(q, k, v, cu_seqlens, is_vision, w_cmp_k, w_cmp_v, gate_logits, top_k, window,
+                   block=64, scale=0.0, out=None, want_kcmp=False, want_sel=False, want_lse=False,
+                   workspace=None, stream=None) -> dict:
+    """Runs nsa_prefill_varlen: sequences i = rows cu_seqlens[i] .. cu_seqlens[i+1]-1
+    (cu_seqlens on the host); tensors as for prefill over all rows. Optional
+    outputs are concatenated over the sequences."""
+    desc = prefill_desc(q, k, top_k, window, block, scale)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    for name, t, shape in (("q", q, (n, hq, d)), ("k", k, (n, hkv, d)), ("v", v, (n, hkv, d)),
+                           ("w_cmp_k", w_cmp_k, (d, d)), ("w_cmp_v", w_cmp_v, (d, d))):
+        _check_dev(name, t, q.dtype, shape)
+    _check_dev("gate_logits", gate_logits, torch.float32, (n, hq, 3))
+    mask = _mask_host(is_vision)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    if mask.shape != (n,) or cu.ndim != 1 or len(cu) < 2:
+        raise ValueError("is_vision needs one entry per token and cu_seqlens at least two")
+    ns = len(cu) - 1
+    isv = mask.astype(bool)
+    n_vis = int(isv.sum())
+    n_blk = sum(int(isv[cu[i]:cu[i + 1]].sum()) // block for i in range(ns))
+    dev = q.device
+    res = {}
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (n, hq, d))
+    res["out"] = out
+    kc = vc = sel = lse = None
+    if want_kcmp:
+        kc = res["k_cmp"] = torch.empty((n_blk, hkv, d), dtype=torch.float32, device=dev)
+        vc = res["v_cmp"] = torch.empty((n_blk, hkv, d), dtype=torch.float32, device=dev)
+    if want_sel:
+        sel = res["sel_idx"] = torch.empty((n_vis, hkv, top_k), dtype=torch.int32, device=dev)
+    if want_lse:
+        lse = res["lse"] = torch.empty((n_vis, hq), dtype=torch.float32, device=dev)
+    nb = ctypes.c_size_t(0)
+    st = lib().nsa_prefill_varlen_workspace_size(ctypes.byref(desc), ns, _ptr(cu), _ptr(mask), ctypes.byref(nb))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_prefill_varlen_workspace_size")
+    if workspace is None or workspace.numel() < nb.value:
+        workspace = torch.empty(max(nb.value, 256), dtype=torch.uint8, device=dev)
+    st = lib().nsa_prefill_varlen(ctypes.byref(desc), ns, _ptr(cu), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
+                                  _ptr(w_cmp_k), _ptr(w_cmp_v), _ptr(gate_logits), _ptr(out), _ptr(kc),
+                                  _ptr(vc), _ptr(sel), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_prefill_varlen")
     res["workspace"] = workspace
     return res
 

@@ -195,14 +195,15 @@ nsa_status nsa_prefill_workspace_size(const nsa_prefill_desc *desc, const uint8_
   return NSA_OK;
 }
 
-nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *k, const void *v,
-                       const uint8_t *is_vision, const void *w_cmp_k, const void *w_cmp_v,
-                       const float *gate_logits, float *out, float *k_cmp_out, float *v_cmp_out,
-                       int32_t *sel_idx_out, float *lse_out, void *workspace,
-                       size_t workspace_bytes, void *stream) {
-  PrefillPlan pl;
-  nsa_status st = plan_prefill(desc, is_vision, pl);
-  if (st != NSA_OK) return st;
+}  // extern "C"
+
+namespace nsa {
+namespace {
+
+nsa_status check_prefill_args(const PrefillPlan &pl, const void *q, const void *k, const void *v,
+                              const void *w_cmp_k, const void *w_cmp_v, const float *gate_logits,
+                              float *out, float *k_cmp_out, float *v_cmp_out, int32_t *sel_idx_out,
+                              float *lse_out, void *workspace, size_t workspace_bytes) {
   if (!q || !k || !v || !gate_logits || !out) return NSA_ERR_INVALID_ARG;
   if (pl.n_blk > 0 && (!w_cmp_k || !w_cmp_v)) return NSA_ERR_INVALID_ARG;
   const void *ptrs[] = {q, k, v, w_cmp_k, w_cmp_v, gate_logits, out, k_cmp_out, v_cmp_out,
@@ -211,8 +212,14 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
     if (p && !aligned16(p)) return NSA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < pl.total) return NSA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return NSA_ERR_WORKSPACE;
+  return NSA_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// Enqueues the layer for one planned, validated sequence.
+nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, const void *v,
+                           const uint8_t *is_vision, const void *w_cmp_k, const void *w_cmp_v,
+                           const float *gate_logits, float *out, float *k_cmp_out, float *v_cmp_out,
+                           int32_t *sel_idx_out, float *lse_out, void *workspace, hipStream_t s) {
   const int64_t H = pl.hq, Hk = pl.hkv, D = pl.d;
   const uint16_t *qb = static_cast<const uint16_t *>(q);
   const uint16_t *kb = static_cast<const uint16_t *>(k);
@@ -311,6 +318,100 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
                   (int)(pl.n_vis > 0 ? pl.n_frames : 0), pl.n_tchunks, sl2, tmap, tnvb};
     NSA_LAUNCH("text_attn", launch_text_attn(tp, pl.d, pl.G, pl.fp32, s));
     NSA_LAUNCH("text_merge", launch_text_merge(tp, pl.d, s));
+  }
+  return NSA_OK;
+}
+
+}  // namespace
+}  // namespace nsa
+
+extern "C" {
+
+nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *k, const void *v,
+                       const uint8_t *is_vision, const void *w_cmp_k, const void *w_cmp_v,
+                       const float *gate_logits, float *out, float *k_cmp_out, float *v_cmp_out,
+                       int32_t *sel_idx_out, float *lse_out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  PrefillPlan pl;
+  nsa_status st = plan_prefill(desc, is_vision, pl);
+  if (st != NSA_OK) return st;
+  st = check_prefill_args(pl, q, k, v, w_cmp_k, w_cmp_v, gate_logits, out, k_cmp_out, v_cmp_out,
+                          sel_idx_out, lse_out, workspace, workspace_bytes);
+  if (st != NSA_OK) return st;
+  return enqueue_prefill(pl, q, k, v, is_vision, w_cmp_k, w_cmp_v, gate_logits, out, k_cmp_out,
+                         v_cmp_out, sel_idx_out, lse_out, workspace, static_cast<hipStream_t>(stream));
+}
+
+// Several independent sequences, one after another on the stream.
+static nsa_status plan_varlen(const nsa_prefill_desc *desc, int32_t n_seqs, const int64_t *cu,
+                              const uint8_t *is_vision, size_t *max_ws) {
+  if (!desc || !cu || !is_vision || n_seqs < 1) return NSA_ERR_INVALID_ARG;
+  if (cu[0] != 0 || cu[n_seqs] != desc->n_tokens) return NSA_ERR_INVALID_ARG;
+  *max_ws = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if (cu[i + 1] <= cu[i]) return NSA_ERR_INVALID_ARG;  // every sequence holds a token
+    nsa_prefill_desc di = *desc;
+    di.n_tokens = cu[i + 1] - cu[i];
+    PrefillPlan pl;
+    const nsa_status st = plan_prefill(&di, is_vision + cu[i], pl);
+    if (st != NSA_OK) return st;
+    if (pl.total > *max_ws) *max_ws = pl.total;
+  }
+  return NSA_OK;
+}
+
+nsa_status nsa_prefill_varlen_workspace_size(const nsa_prefill_desc *desc, int32_t n_seqs,
+                                             const int64_t *cu_seqlens, const uint8_t *is_vision,
+                                             size_t *bytes) {
+  if (!bytes) return NSA_ERR_INVALID_ARG;
+  size_t need = 0;
+  const nsa_status st = plan_varlen(desc, n_seqs, cu_seqlens, is_vision, &need);
+  if (st != NSA_OK) return st;
+  *bytes = need;
+  return NSA_OK;
+}
+
+nsa_status nsa_prefill_varlen(const nsa_prefill_desc *desc, int32_t n_seqs, const int64_t *cu_seqlens,
+                              const void *q, const void *k, const void *v, const uint8_t *is_vision,
+                              const void *w_cmp_k, const void *w_cmp_v, const float *gate_logits,
+                              float *out, float *k_cmp_out, float *v_cmp_out, int32_t *sel_idx_out,
+                              float *lse_out, void *workspace, size_t workspace_bytes, void *stream) {
+  size_t need = 0;
+  nsa_status st = plan_varlen(desc, n_seqs, cu_seqlens, is_vision, &need);
+  if (st != NSA_OK) return st;
+  // validate every sequence's slice before anything is enqueued
+  const size_t esz = desc->dtype == NSA_DTYPE_FP32 ? sizeof(float) : sizeof(uint16_t);
+  const int64_t H = desc->n_q_heads, Hk = desc->n_kv_heads, D = desc->head_dim;
+  for (int pass = 0; pass < 2; ++pass) {
+    int64_t vis0 = 0, blk0 = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      const int64_t t0 = cu_seqlens[i];
+      nsa_prefill_desc di = *desc;
+      di.n_tokens = cu_seqlens[i + 1] - t0;
+      PrefillPlan pl;
+      st = plan_prefill(&di, is_vision + t0, pl);
+      if (st != NSA_OK) return st;
+      auto off = [](const void *p, int64_t bytes) -> const char * {
+        return p ? static_cast<const char *>(p) + bytes : nullptr;
+      };
+      const void *qi = off(q, t0 * H * D * esz), *ki = off(k, t0 * Hk * D * esz), *vi = off(v, t0 * Hk * D * esz);
+      const float *gi = gate_logits ? gate_logits + t0 * H * 3 : nullptr;
+      float *oi = out ? out + t0 * H * D : nullptr;
+      float *kci = k_cmp_out ? k_cmp_out + blk0 * Hk * D : nullptr;
+      float *vci = v_cmp_out ? v_cmp_out + blk0 * Hk * D : nullptr;
+      int32_t *si = sel_idx_out ? sel_idx_out + vis0 * Hk * desc->top_k : nullptr;
+      float *li = lse_out ? lse_out + vis0 * H : nullptr;
+      if (pass == 0) {
+        st = check_prefill_args(pl, qi, ki, vi, w_cmp_k, w_cmp_v, gi, oi, kci, vci, si, li, workspace,
+                                workspace_bytes);
+      } else {
+        st = enqueue_prefill(pl, qi, ki, vi, is_vision + t0, w_cmp_k, w_cmp_v, gi, oi, kci, vci, si, li,
+                             workspace, static_cast<hipStream_t>(stream));
+      }
+      if (st != NSA_OK) return st;
+      vis0 += pl.n_vis;
+      blk0 += pl.n_blk;
+    }
   }
   return NSA_OK;
 }

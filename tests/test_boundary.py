@@ -255,3 +255,46 @@ def test_cache_append_pointer_checks():
     for name in ("kn", "vn", "kc", "vc", "wk", "wv", "kcmp", "vcmp"):
         assert call_append(ddesc(), {name: None}) == binding.NSA_ERR_INVALID_ARG, name
     assert call_append(ddesc(), {"kc": FAKE + 8}) == binding.NSA_ERR_INVALID_ARG
+
+
+def varlen_ws(ds, cu, mask):
+    cu = np.asarray(cu, np.int64)
+    n = ctypes.c_size_t(0)
+    st = binding.lib().nsa_prefill_varlen_workspace_size(
+        ctypes.byref(ds), len(cu) - 1, cu.ctypes.data_as(ctypes.c_void_p),
+        mask.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n))
+    return st, n.value
+
+
+def test_varlen_workspace_is_the_largest_sequence():
+    m1 = vision_mask(1024 + 64, 0, 1024)
+    m2 = vision_mask(4096 + 32, 32, 4096 + 32)
+    mask = np.concatenate([m1, m2])
+    ds = desc(n=len(mask))
+    st, n = varlen_ws(ds, [0, len(m1), len(mask)], mask)
+    assert st == binding.NSA_OK
+    assert n == max(ws_size(desc(n=len(m1)), m1)[1], ws_size(desc(n=len(m2)), m2)[1])
+
+
+@pytest.mark.parametrize("cu", [[0, 500, 1000], [1, 1024], [0, 1025], [0, 600, 600, 1024], [0, 700, 500, 1024]])
+def test_varlen_bad_offsets(cu):
+    mask = vision_mask(1024, 0, 1024)
+    ok = cu == [0, 500, 1000]
+    st, _ = varlen_ws(desc(n=1000 if ok else 1024), cu, mask)
+    assert st == (binding.NSA_OK if ok else binding.NSA_ERR_INVALID_ARG)
+
+
+def test_varlen_validates_every_sequence_first():
+    mask = vision_mask(2048, 0, 2048)
+    cu = np.array([0, 1024, 2048], np.int64)
+    L = binding.lib()
+
+    def call(ptrs):
+        p = dict(q=FAKE, k=FAKE, v=FAKE, wk=FAKE, wv=FAKE, g=FAKE, out=FAKE, ws=FAKE)
+        p.update(ptrs)
+        return L.nsa_prefill_varlen(ctypes.byref(desc(n=2048)), 2, cu.ctypes.data_as(ctypes.c_void_p),
+                                    p["q"], p["k"], p["v"], mask.ctypes.data_as(ctypes.c_void_p), p["wk"],
+                                    p["wv"], p["g"], p["out"], None, None, None, None, p["ws"], 1 << 40, None)
+    assert call({"q": None}) == binding.NSA_ERR_INVALID_ARG
+    assert call({"ws": None}) == binding.NSA_ERR_WORKSPACE
+    assert call({"g": FAKE + 4}) == binding.NSA_ERR_INVALID_ARG
