@@ -199,6 +199,35 @@ def run_dense_bench(dev, shape, steps, warmup, nsa_ms):
             "nsa_speedup": round(ms / nsa_ms, 2), "steps": steps, "kernels": kern}
 
 
+def run_scaling_bench(shape, steps, warmup):
+    """Step time against context length at the workload's k and w: 16K to
+    512K vision tokens (the largest the kernels take) plus its text tokens."""
+    import torch
+    from sparse_attention_long_nsa_amd.inputs import make_prefill_inputs
+    rows = []
+    for n_vis in (16384, 32768, 65536, 131072, 262144, 524288):
+        s = shape.replace(n_vis=n_vis)
+        inp = make_prefill_inputs(s, seed=0)
+        dev = {k: torch.from_numpy(inp[k]).to("cuda:0").to(torch.bfloat16).contiguous()
+               for k in ("q", "k", "v", "w_k", "w_v")}
+        dev["gates"] = torch.from_numpy(inp["gates"]).to("cuda:0")
+        ms, kern, out = run_gpu(inp, dev, s.top_k, s.window, steps, warmup, True)
+        del dev, out, inp
+        torch.cuda.empty_cache()
+
+        def ms_of(*names):
+            return round(sum(kern.get(n, (0.0, 0))[0] for n in names), 4)
+
+        row = {"n_vision": n_vis, "n_tokens": s.n_tokens, "ms_per_step": round(ms, 4),
+               "tokens_per_s": round(s.n_tokens / (ms * 1e-3), 1),
+               "branch_ms": {"cmp": ms_of("cmp_pool", "pack_cmp", "cmp_attn"), "topk": ms_of("blk_score_topk"),
+                             "sel": ms_of("pack_kv", "sel_attn"), "swa": ms_of("swa_attn"),
+                             "text": ms_of("pack_text", "text_attn", "text_merge")}}
+        rows.append(row)
+        log(f"scaling {n_vis}: {ms:.3f} ms {row['branch_ms']}")
+    return rows
+
+
 def cpu_baseline(inp, n_vis_rows, n_text_rows):
     """The fp64 oracle, as it stands, on a bounded row sample of the same
     workload; per-row times extrapolated to the whole sequence."""
@@ -340,6 +369,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-spans", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--scaling", action="store_true",
+                    help="also time 16K..512K vision tokens (about a minute more, mostly input generation)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer library runs on a single MI355X and has no "
@@ -419,6 +450,10 @@ def main():
     if not args.no_spans:
         spans = run_spans_bench(inp, shape, max(3, args.steps // 2), 1, ms)
 
+    scaling = None
+    if args.scaling:
+        scaling = run_scaling_bench(shape, max(3, args.steps // 2), 1)
+
     # the published peak checked on this GPU with an MFMA-loop probe
     from sparse_attention_long_nsa_amd.profiling import mfma_peak
     probe = mfma_peak()
@@ -458,6 +493,7 @@ def main():
         "decode": decode,
         "several_vision_runs": spans,
         "dense_mode": dense,
+        "context_scaling": scaling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

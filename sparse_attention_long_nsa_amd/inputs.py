@@ -85,10 +85,15 @@ PREFILL_PRESETS = {
     "qwen_128k_k32_w256": PrefillShape(131072, 0, 512, 28, 4, 128, 64, 32, 256, "bf16"),
     "qwen_128k_k16_w512": PrefillShape(131072, 0, 512, 28, 4, 128, 64, 16, 512, "bf16"),
     "qwen_128k_k8_w1024": PrefillShape(131072, 0, 512, 28, 4, 128, 64, 8, 1024, "bf16"),
+    # longer contexts, up to the largest the kernels take (8,192 blocks of 64)
+    "qwen_256k_k32_w256": PrefillShape(262144, 0, 512, 28, 4, 128, 64, 32, 256, "bf16"),
+    "qwen_512k_k32_w256": PrefillShape(524288, 0, 512, 28, 4, 128, 64, 32, 256, "bf16"),
 }
 
 DECODE_PRESETS = {
     "decode_16x128k": DecodeShape(16, 131072, 28, 4, 128, 64, 16, 512, "bf16"),
+    # the longest cache the kernels take (8,192 blocks of 64)
+    "decode_2x512k": DecodeShape(2, 524288, 28, 4, 128, 64, 16, 512, "bf16"),
 }
 
 

@@ -165,8 +165,9 @@ def test_generation_with_cache_append():
         assert orep.ok(), (L, orep)
 
 
-def test_decode_full_size_preset():
-    check(make_decode_inputs(DECODE_PRESETS["decode_16x128k"], seed=0), "decode_16x128k")
+@pytest.mark.parametrize("preset", ["decode_16x128k", "decode_2x512k"])
+def test_decode_full_size_preset(preset):
+    check(make_decode_inputs(DECODE_PRESETS[preset], seed=0), preset)
 
 
 def test_decode_equals_prefill_last_row_on_gpu():

@@ -128,7 +128,7 @@ def test_repeat_runs_are_bitwise_identical():
 
 
 @pytest.mark.parametrize("preset", ["qwen_36k", "qwen_64k", "qwen_128k_k32_w256", "qwen_128k_k16_w512",
-                                    "qwen_128k_k8_w1024"])
+                                    "qwen_128k_k8_w1024", "qwen_256k_k32_w256", "qwen_512k_k32_w256"])
 def test_full_size_sampled_rows(preset):
     inp = make_prefill_inputs(PREFILL_PRESETS[preset], seed=0)
     announce(preset, inp["shape"])
