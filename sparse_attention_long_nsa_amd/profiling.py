@@ -205,6 +205,65 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_
             json.dump(rec, f, indent=1)
 
 
+def counter_summary(csv_a: str, csv_b: str, grid_names: dict, workload: str, commands: list,
+                    bench_log: str, out_md: str) -> None:
+    """Instruction mix and pipe utilisation per kernel from two SQ counter runs.
+
+    Cycle counters of the SQ (SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_ACTIVE_INST_*)
+    count in units of four clocks, summed over waves; SQ_VALU_MFMA_BUSY_CYCLES
+    counts clocks summed over SIMDs. Utilisation is taken against 256 CUs x 4
+    SIMDs at 2.4 GHz over the dispatch's duration."""
+    simds, clk = 256 * 4, 2.4e9
+    vals = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(list)
+    for path in (csv_a, csv_b):
+        for r in csv.DictReader(open(path)):
+            name, _ = short_name(r["Kernel_Name"], _grid(r), grid_names)
+            if name not in PREFILL_KERNELS:
+                continue
+            vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    bench = _bench_line(bench_log) if bench_log else None
+    kern = bench["kernels"] if bench else {}
+    lines = [f"# Instruction mix and pipe utilisation: {workload}", "",
+             "Counters: two rocprofv3 --pmc runs of SQ counters (one dispatch per kernel each). "
+             "SQ cycle counters count units of four clocks summed over waves; the matrix-core busy "
+             "counter counts clocks summed over SIMDs. Utilisation is against 256 CUs x 4 SIMDs at "
+             "2.4 GHz over the dispatch; `issued TF` counts every 16x16x32 matrix instruction "
+             "(16,384 flops), `useful` is the kernel's algorithmic flops from bench.py over the issued ones.",
+             "", "Commands (from the repository root, on one MI355X):", "", "```"] + commands + ["```", ""]
+    lines += ["| kernel | ms | waves | VALU / wave | MFMA / wave | LDS / wave | SALU / wave | exp share of VALU | "
+              "VALU busy | MFMA busy | waiting | LDS bank-conflict cycles | issued TF | useful |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name in sorted(vals, key=lambda n: -sum(dur[n]) / len(dur[n])):
+        v = {c: sum(x) / len(x) for c, x in vals[name].items()}
+        secs = sum(dur[name]) / len(dur[name])
+        cyc = secs * clk
+        waves = v.get("SQ_WAVES", 0.0) or 1.0
+
+        def per_wave(c):
+            return f"{v[c] / waves:.0f}" if c in v else ""
+
+        valu_busy = v.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (simds * cyc)
+        mfma_busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (simds * cyc)
+        wait = v.get("SQ_WAIT_ANY", 0.0) / v["SQ_WAVE_CYCLES"] if v.get("SQ_WAVE_CYCLES") else 0.0
+        exp_share = 4 * v.get("SQ_INSTS_VALU_TRANS_F32", 0.0) / (
+            v.get("SQ_INSTS_VALU", 1.0) + 3 * v.get("SQ_INSTS_VALU_TRANS_F32", 0.0))
+        conflict = v.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(v.get("SQ_ACTIVE_INST_LDS", 0.0), 1.0)
+        issued = v.get("SQ_INSTS_MFMA", 0.0) * 16384 / 1e12
+        tf = kern.get(name, {}).get("tflops")
+        ms = kern.get(name, {}).get("avg_ms")
+        useful = f"{tf * ms * 1e-3 / issued:.0%}" if (tf and ms and issued) else ""
+        lines.append(f"| {name} | {secs * 1e3:.3f} | {waves:.0f} | {per_wave('SQ_INSTS_VALU')} | "
+                     f"{per_wave('SQ_INSTS_MFMA')} | {per_wave('SQ_INSTS_LDS')} | {per_wave('SQ_INSTS_SALU')} | "
+                     f"{exp_share:.0%} | {valu_busy:.0%} | {mfma_busy:.0%} | {wait:.0%} | {conflict:.2%} | "
+                     f"{issued:.2f} | {useful} |")
+    lines += ["", "`exp share` weights the transcendental instructions (exp2) four times, their issue cost "
+              "relative to plain fp32 vector instructions."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def copy_probe(mib: int, reps: int) -> None:
     import torch
     n = mib * 1024 * 1024 // 2
@@ -276,6 +335,13 @@ def main(argv=None) -> None:
     m.add_argument("--command", action="append", default=[])
     m.add_argument("--out-md", required=True)
     m.add_argument("--out-dir", required=True)
+    x = sub.add_parser("counter-summary")
+    x.add_argument("--csv-a", required=True)
+    x.add_argument("--csv-b", required=True)
+    x.add_argument("--workload", default="qwen_128k_k32_w256")
+    x.add_argument("--bench-log", default=None)
+    x.add_argument("--command", action="append", default=[])
+    x.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         copy_probe(a.mib, a.reps)
@@ -283,6 +349,8 @@ def main(argv=None) -> None:
         print(json.dumps(mfma_peak()), flush=True)
     elif a.cmd == "trace-summary":
         trace_summary(a.trace_csv, a.bench_log, _layer_grids(a.workload), a.title, a.command, a.out, a.group)
+    elif a.cmd == "counter-summary":
+        counter_summary(a.csv_a, a.csv_b, _layer_grids(a.workload), a.workload, a.command, a.bench_log, a.out)
     else:
         pmc_summary(a.fetch_csv, a.write_csv, a.copy_fetch_csv, a.copy_write_csv, a.copy_mib,
                     _layer_grids(a.workload), a.workload, a.command, a.bench_log, a.out_md, a.out_dir)
