@@ -53,3 +53,33 @@ def test_trace_summary_groups(tmp_path):
     text = out_d.read_text()
     assert "| dec_select | 1 | 0.0090 | 0.0095 | 100.0% |" in text
     assert "44.0 us per decode step" in text
+
+
+def test_counter_summary_utilisation(tmp_path):
+    # one sel_attn dispatch of 1 ms: 1,024 SIMDs x 2.4e6 clocks; counters
+    # chosen so that vector busy = 50%, matrix busy = 25%, waiting = 40%
+    cyc = 2.4e6 * 1024
+    a = {"SQ_WAVES": 100.0, "SQ_INSTS_VALU": 1000.0, "SQ_INSTS_MFMA": 1e9, "SQ_INSTS_LDS": 300.0,
+         "SQ_INSTS_SALU": 50.0, "SQ_WAVE_CYCLES": 1e9, "SQ_BUSY_CYCLES": 1.0, "SQ_WAIT_INST_ANY": 1.0}
+    b = {"SQ_ACTIVE_INST_VALU": 0.5 * cyc / 4, "SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * cyc, "SQ_WAIT_ANY": 0.4e9,
+         "SQ_ACTIVE_INST_LDS": 100.0, "SQ_LDS_BANK_CONFLICT": 1.0, "SQ_INSTS_VALU_TRANS_F32": 0.0,
+         "SQ_ACTIVE_INST_ANY": 1.0, "SQ_ACTIVE_INST_MISC": 1.0}
+    paths = []
+    for tag, counters in (("a", a), ("b", b)):
+        path = tmp_path / f"{tag}.csv"
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value",
+                                              "Start_Timestamp", "End_Timestamp"])
+            w.writeheader()
+            for c, v in counters.items():
+                w.writerow({"Kernel_Name": "sel_attn_kernel<128, 7, false>", "Grid_Size": 1, "Counter_Name": c,
+                            "Counter_Value": v, "Start_Timestamp": 0, "End_Timestamp": 1_000_000})
+        paths.append(str(path))
+    out = tmp_path / "mix.md"
+    prof.counter_summary(paths[0], paths[1], prof._layer_grids("qwen_128k_k32_w256"), "w", ["cmd"], None,
+                         str(out))
+    row = [l for l in out.read_text().splitlines() if l.startswith("| sel_attn")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1] == "1.000" and cells[3] == "10"          # ms, VALU per wave
+    assert cells[8:11] == ["50%", "25%", "40%"]               # vector busy, matrix busy, waiting
+    assert cells[12] == "16.38"                               # 1e9 matrix instructions x 16,384 flops
