@@ -65,3 +65,19 @@ def test_dense_every_head_shape(d, G):
     rep = parity.compare(r["out"].cpu().numpy(), oracle.dense(inp))
     print(rep, flush=True)
     assert rep.ok(), rep
+
+
+# fp32 inputs: split-bf16 block scores need G * d <= 512
+HEADS_FP32 = [(64, g) for g in range(1, 9)] + [(128, g) for g in range(1, 5)]
+
+
+@pytest.mark.parametrize("d,G", HEADS_FP32)
+def test_prefill_fp32_every_head_shape(d, G):
+    s = PrefillShape(650, 7, 21, 2 * G, 2, d, 64, 4, 100, "fp32")
+    print(f"\n[case] prefill fp32 heads: {s}", flush=True)
+    inp = make_prefill_inputs(s, seed=400 + d + G)
+    gpu = run_prefill(inp)
+    rep, orep, _ = parity.check_prefill(inp, gpu, np.arange(s.n_tokens))
+    print(rep, "|", orep, flush=True)
+    assert rep.counted == 0, rep
+    assert orep.ok(), orep
