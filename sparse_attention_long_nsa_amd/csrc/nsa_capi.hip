@@ -30,7 +30,7 @@ struct PrefillPlan {
   size_t off_kc = 0, off_vc = 0, off_kcl = 0, off_qh = 0, off_ql = 0, off_q16 = 0, off_k16 = 0,
          off_v16 = 0;
   size_t off_kvc = 0, off_kvt = 0, off_vt = 0, off_lse = 0, off_gs = 0, off_sel = 0, off_po = 0, off_pml = 0;
-  size_t off_vmap = 0, off_tmap = 0, off_tnvb = 0, total = 0;
+  size_t off_vmap = 0, off_tmap = 0, off_tnvb = 0, off_means = 0, total = 0;
 };
 
 nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, PrefillPlan &pl) {
@@ -91,6 +91,7 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
   const size_t H = (size_t)pl.hq, Hk = (size_t)pl.hkv, D = (size_t)pl.d;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  pl.off_means = take(sizeof(float) * 2 * (size_t)pl.n_blk * Hk * D);  // block means of keys, values
   pl.off_kc = take(sizeof(uint16_t) * pl.n_blk * Hk * D);
   pl.off_vc = take(sizeof(uint16_t) * pl.n_blk * Hk * D);
   if (pl.fp32) {
@@ -288,7 +289,7 @@ nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, 
                  pl.fp32 ? kc : nullptr, kcl, pl.fp32 ? nullptr : kc, k_cmp_out, vmap};
       PoolJob jv{static_cast<const char *>(v) + esz * r0 * Hk * D, w_cmp_v, pl.hkv, pl.n_blk,
                  nullptr, nullptr, vc, v_cmp_out, vmap};
-      NSA_LAUNCH("cmp_pool", launch_cmp_pool(jk, &jv, pl.d, pl.fp32, s));
+      NSA_LAUNCH("cmp_pool", launch_cmp_pool_split(jk, jv, pl.d, pl.fp32, at<float>(workspace, pl.off_means), s));
     }
     uint16_t *kvc = nullptr;
     if (!pl.fp32 && pl.n_cch > 0) {

@@ -303,7 +303,10 @@ __global__ __launch_bounds__(D) void dec_combine_kernel(DecodeParams p) {
 #pragma unroll 8
     for (int i = i0; i < i1; ++i) {
       const float m = part[(int64_t)i * (D + 2)];
-      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      // an unused selection slot carries only (-inf, 0): its output entries
+      // were never written, so they are not read (0 * stale NaN is NaN)
+      if (m == -INFINITY) continue;
+      const float w = exp2f(m - M);
       L += w * part[(int64_t)i * (D + 2) + 1];
       o += w * part[(int64_t)i * (D + 2) + 2 + d];
     }

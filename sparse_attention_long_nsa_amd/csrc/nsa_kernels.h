@@ -132,6 +132,10 @@ struct DecodeParams {
 
 size_t pool_smem_bytes(int n_heads, int d);
 hipError_t launch_cmp_pool(const PoolJob &j0, const PoolJob *j1, int d, bool fp32, hipStream_t st);
+// The same pooling of two jobs (keys, values) as a block-mean launch into
+// `means` (2 * n_blk * Hkv * d floats) and a map launch; identical results.
+hipError_t launch_cmp_pool_split(const PoolJob &j0, const PoolJob &j1, int d, bool fp32, float *means,
+                                 hipStream_t st);
 // Copies one row of n_cols bf16 per sequence (src [Bt, n_cols]) to row `row`
 // of dst [Bt, cap, n_cols], for keys and values at once.
 hipError_t launch_append_rows(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_cache,

@@ -4,10 +4,13 @@
 // paper summary page, "Method": a learned map turns each block into one
 // block-level key/value). Reading: y = W * mean, no bias.
 //
-// HBM-bound: each workgroup streams one block (64 rows x Hkv x d, contiguous
-// in the token-major layout, or gathered through a row map when the vision
-// tokens lie in several runs) with 16-byte loads, reduces the rows in fp32,
-// and applies W from the L1/L2-resident copy.
+// HBM-bound: a workgroup streams one block (64 rows x Hkv x d, contiguous in
+// the token-major layout, or gathered through a row map when the vision
+// tokens lie in several runs) with 16-byte loads and reduces the rows in
+// fp32; W is applied from its L1/L2-resident copy. The layer runs the two
+// steps as separate launches (means through the workspace) so the row
+// streaming is not held up by the maps; single calls run both in one kernel.
+// Both orders of arithmetic are the same, so the results are identical.
 #include "nsa_kernels.h"
 
 namespace nsa {
@@ -28,62 +31,153 @@ __device__ __forceinline__ void load8f(const float *p, float v[8]) {
 
 constexpr int kPoolThreads = 256;
 
+// Column sums of block b's 64 rows, then the mean: thread items (row phase,
+// 16-byte column chunk) sum every P-th row, and the P partials are added in
+// phase order. `mean` (LDS or global, C floats) gets the result; `part` is
+// LDS scratch of P * C floats.
+template <typename T, int D>
+__device__ __forceinline__ void block_mean(const PoolJob &jb, int64_t b, float *part, float *mean, int tid) {
+  const T *x = static_cast<const T *>(jb.x);
+  const int C = jb.n_heads * D;  // columns of one token row
+  const int CH = C / 8;          // 16-byte (bf16) column chunks
+  const int P = CH >= kPoolThreads ? 1 : kPoolThreads / CH;  // row phases
+  const T *xb = x + b * jb.in_stride * (int64_t)C;
+  const int32_t *rb = jb.rows ? jb.rows + b * kBlk : nullptr;
+  for (int item = tid; item < P * CH; item += kPoolThreads) {
+    const int ch = item % CH, rp = item / CH;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 8
+    for (int r = rp; r < kBlk; r += P) {  // independent row loads, many in flight
+      float v[8];
+      load8f((rb ? x + (int64_t)rb[r] * C : xb + (int64_t)r * C) + ch * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[rp * C + ch * 8 + i] = acc[i];
+  }
+  __syncthreads();
+  for (int col = tid; col < C; col += kPoolThreads) {
+    float s = 0.f;
+    for (int rp = 0; rp < P; ++rp) s += part[rp * C + col];
+    mean[col] = s * (1.0f / kBlk);
+  }
+}
+
+// Output o = (head g, row r) of block b: y = W[r, :] . mean_g, in index order.
+template <typename T, int D>
+__device__ __forceinline__ void map_out(const PoolJob &jb, int64_t b, const float *mean, int o) {
+  const T *w = static_cast<const T *>(jb.w);
+  const int g = o / D, r = o % D;
+  const T *wr = w + (int64_t)r * D;
+  const float *mg = mean + g * D;
+  float acc = 0.f;
+  for (int i = 0; i < D; i += 8) {
+    float wv[8];
+    load8f(wr + i, wv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += wv[e] * mg[i + e];
+  }
+  const int64_t dst = (b * jb.out_stride * jb.n_heads + g) * (int64_t)D + r;
+  const uint16_t hi = f2bf_bits(acc);
+  if (jb.out_hi) jb.out_hi[dst] = hi;
+  if (jb.out_lo) jb.out_lo[dst] = f2bf_bits(acc - bfbits2f(hi));
+  if (jb.out_h16) jb.out_h16[dst] = f2h_bits(acc);
+  if (jb.out_f32) jb.out_f32[dst] = acc;
+}
+
+// Both steps in one workgroup per block (small jobs: one block per sequence
+// while generating, or a cache built once).
 template <typename T, int D>
 __global__ __launch_bounds__(kPoolThreads) void cmp_pool_kernel(PoolJob j0, PoolJob j1) {
   const PoolJob &jb = blockIdx.y == 0 ? j0 : j1;
-  const T *x = static_cast<const T *>(jb.x);
-  const T *w = static_cast<const T *>(jb.w);
-  const int hkv = jb.n_heads;
-  const int C = hkv * D;     // columns of one token row
-  const int CH = C / 8;      // 16-byte (bf16) column chunks
-  const int P = CH >= kPoolThreads ? 1 : kPoolThreads / CH;  // row phases
+  const int C = jb.n_heads * D;
+  const int CH = C / 8;
+  const int P = CH >= kPoolThreads ? 1 : kPoolThreads / CH;
   extern __shared__ float smem[];
   float *part = smem;             // [P][C]
   float *mean = smem + P * C;     // [C]
   const int tid = threadIdx.x;
-
   for (int64_t b = blockIdx.x; b < jb.n_blk; b += gridDim.x) {
-    const T *xb = x + b * jb.in_stride * (int64_t)C;
-    const int32_t *rb = jb.rows ? jb.rows + b * kBlk : nullptr;
-    for (int item = tid; item < P * CH; item += kPoolThreads) {
-      const int ch = item % CH, rp = item / CH;
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 8
-      for (int r = rp; r < kBlk; r += P) {  // independent row loads, many in flight
-        float v[8];
-        load8f((rb ? x + (int64_t)rb[r] * C : xb + (int64_t)r * C) + ch * 8, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) part[rp * C + ch * 8 + i] = acc[i];
-    }
+    block_mean<T, D>(jb, b, part, mean, tid);
     __syncthreads();
-    for (int col = tid; col < C; col += kPoolThreads) {
-      float s = 0.f;
-      for (int rp = 0; rp < P; ++rp) s += part[rp * C + col];
-      mean[col] = s * (1.0f / kBlk);
-    }
+    for (int o = tid; o < C; o += kPoolThreads) map_out<T, D>(jb, b, mean, o);
     __syncthreads();
-    for (int o = tid; o < C; o += kPoolThreads) {
-      const int g = o / D, r = o % D;
-      const T *wr = w + (int64_t)r * D;
-      const float *mg = mean + g * D;
-      float acc = 0.f;
-      for (int i = 0; i < D; i += 8) {
-        float wv[8];
-        load8f(wr + i, wv);
+  }
+}
+
+// The layer's pooling in two launches, so that the streaming of the rows is
+// not held up by the maps: block means into a workspace, then the maps, one
+// output per thread. Same arithmetic in the same order as cmp_pool_kernel.
+template <typename T, int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_mean_kernel(PoolJob j0, PoolJob j1, float *m0, float *m1) {
+  const PoolJob &jb = blockIdx.y == 0 ? j0 : j1;
+  const int64_t b = blockIdx.x;
+  if (b >= jb.n_blk) return;
+  extern __shared__ float smem[];
+  const int C = jb.n_heads * D;
+  block_mean<T, D>(jb, b, smem, (blockIdx.y == 0 ? m0 : m1) + b * C, threadIdx.x);
+}
+
+// kMapBlocks blocks per workgroup of kMapThreads: W is staged once in LDS,
+// transposed with a padded row (conflict-free both ways). A thread owns one
+// output row r and walks eight (block, head) mean vectors at once, read with
+// wave-uniform addresses (scalar loads): eight independent index-ordered
+// fp32 sums, each the same as map_out's. (Measured: 4 blocks per workgroup
+// is 10x slower -- every workgroup reads the same W lines at once -- and 64
+// is 3.5x slower -- too few workgroups.)
+constexpr int kMapBlocks = 16;
+constexpr int kMapThreads = 512;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMapThreads) void pool_map_kernel(PoolJob j0, PoolJob j1, const float *m0,
+                                                               const float *m1) {
+  constexpr int WS = D + 1, NQ = 8, TPR = kMapThreads / D;
+  const PoolJob &jb = blockIdx.y == 0 ? j0 : j1;
+  const int hkv = jb.n_heads, C = hkv * D;
+  const int64_t b0 = (int64_t)blockIdx.x * kMapBlocks;
+  if (b0 >= jb.n_blk) return;
+  const int nv = (int)min((int64_t)kMapBlocks, jb.n_blk - b0) * hkv;  // (block, head) vectors
+  const float *means = (blockIdx.y == 0 ? m0 : m1) + b0 * C;
+  extern __shared__ float wt[];  // [D][WS]: wt[i * WS + r] = W[r][i]
+  const T *w = static_cast<const T *>(jb.w);
+  const int tid = threadIdx.x;
+  for (int e = tid; e < D * D / 8; e += kMapThreads) {  // W's rows, 16-byte (bf16) chunks
+    const int r = (8 * e) / D, i0 = (8 * e) % D;
+    float v[8];
+    load8f(w + 8 * e, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc += wv[e] * mg[i + e];
+    for (int j = 0; j < 8; ++j) wt[(i0 + j) * WS + r] = v[j];
+  }
+  __syncthreads();
+  const int r = tid % D;
+  const int part = __builtin_amdgcn_readfirstlane(tid / D);  // D >= 64: one value per wave
+  for (int v0 = part * NQ; v0 < nv; v0 += TPR * NQ) {
+    float acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = 0.f;
+    for (int i0 = 0; i0 < D; i0 += 16) {
+      float wv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) wv[j] = wt[(i0 + j) * WS + r];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const float *mq = means + (int64_t)min(v0 + q, nv - 1) * D + i0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[q] += wv[j] * mq[j];
       }
-      const int64_t dst = (b * jb.out_stride * hkv + g) * (int64_t)D + r;
-      const uint16_t hi = f2bf_bits(acc);
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (v0 + q >= nv) break;
+      const int bl = (v0 + q) / hkv, g = (v0 + q) % hkv;
+      const int64_t dst = ((b0 + bl) * jb.out_stride * hkv + g) * (int64_t)D + r;
+      const uint16_t hi = f2bf_bits(acc[q]);
       if (jb.out_hi) jb.out_hi[dst] = hi;
-      if (jb.out_lo) jb.out_lo[dst] = f2bf_bits(acc - bfbits2f(hi));
-      if (jb.out_h16) jb.out_h16[dst] = f2h_bits(acc);
-      if (jb.out_f32) jb.out_f32[dst] = acc;
+      if (jb.out_lo) jb.out_lo[dst] = f2bf_bits(acc[q] - bfbits2f(hi));
+      if (jb.out_h16) jb.out_h16[dst] = f2h_bits(acc[q]);
+      if (jb.out_f32) jb.out_f32[dst] = acc[q];
     }
-    __syncthreads();
   }
 }
 
@@ -145,6 +239,27 @@ hipError_t launch_cmp_pool(const PoolJob &j0, const PoolJob *j1, int d, bool fp3
     if (d == 64) hipLaunchKernelGGL((cmp_pool_kernel<bf16, 64>), grid, dim3(kPoolThreads), smem, st, j0, jj);
     else hipLaunchKernelGGL((cmp_pool_kernel<bf16, 128>), grid, dim3(kPoolThreads), smem, st, j0, jj);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_cmp_pool_split(const PoolJob &j0, const PoolJob &j1, int d, bool fp32, float *means,
+                                 hipStream_t st) {
+  const int64_t nb = j0.n_blk > j1.n_blk ? j0.n_blk : j1.n_blk;
+  if (nb <= 0) return hipSuccess;
+  const int64_t C = (int64_t)j0.n_heads * d;
+  float *m0 = means, *m1 = means + j0.n_blk * C;
+  const size_t smem = pool_smem_bytes(j0.n_heads, d);
+  const dim3 g1((unsigned)nb, 2), g2((unsigned)((nb + kMapBlocks - 1) / kMapBlocks), 2);
+  const size_t smem2 = sizeof(float) * (size_t)d * (d + 1);
+#define NSA_POOL2(T, D)                                                                                  \
+  hipLaunchKernelGGL((pool_mean_kernel<T, D>), g1, dim3(kPoolThreads), smem, st, j0, j1, m0, m1);       \
+  hipLaunchKernelGGL((pool_map_kernel<T, D>), g2, dim3(kMapThreads), smem2, st, j0, j1, m0, m1);
+  if (fp32) {
+    if (d == 64) { NSA_POOL2(float, 64) } else { NSA_POOL2(float, 128) }
+  } else {
+    if (d == 64) { NSA_POOL2(bf16, 64) } else { NSA_POOL2(bf16, 128) }
+  }
+#undef NSA_POOL2
   return hipGetLastError();
 }
 

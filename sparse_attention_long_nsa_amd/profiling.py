@@ -44,6 +44,8 @@ KERNELS = [
     ("row_map_kernel", "row_maps", "sparse_attention_long_nsa_amd/csrc/nsa_rowmap.hip"),
     ("topk_kernel", "blk_score_topk", "sparse_attention_long_nsa_amd/csrc/nsa_topk.hip"),
     ("cmp_pool_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_pool.hip"),
+    ("pool_mean_kernel", "cmp_pool_mean", "sparse_attention_long_nsa_amd/csrc/nsa_pool.hip"),
+    ("pool_map_kernel", "cmp_pool_map", "sparse_attention_long_nsa_amd/csrc/nsa_pool.hip"),
     ("pack_kv_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_sel_attn.hip"),
     ("dec_item_kernel", "@grid", "sparse_attention_long_nsa_amd/csrc/nsa_decode.hip"),
     ("dec_select_kernel", "dec_select", "sparse_attention_long_nsa_amd/csrc/nsa_decode.hip"),
@@ -53,7 +55,7 @@ KERNELS = [
 DECODE_KERNELS = ("dec_item_cmp_win", "dec_item_sel", "dec_select", "dec_combine")
 DENSE_KERNELS = ("pack_dense", "dense_attn")
 PREFILL_KERNELS = ("sel_attn", "cmp_attn", "swa_attn", "text_attn", "text_merge", "blk_score_topk", "cmp_pool",
-                   "pack_kv", "pack_cmp", "pack_text")
+                   "cmp_pool_mean", "cmp_pool_map", "pack_kv", "pack_cmp", "pack_text")
 
 
 def short_name(kernel_name: str, grid: int, grid_names: dict):

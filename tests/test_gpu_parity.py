@@ -13,6 +13,7 @@ import torch
 
 import oracle
 from oracle import parity
+from sparse_attention_long_nsa_amd import binding
 from sparse_attention_long_nsa_amd.inputs import PREFILL_PRESETS, PrefillShape, make_prefill_inputs
 
 from gpu_util import run_prefill, upload
@@ -111,6 +112,13 @@ def test_intermediates_kcmp_lse():
     for key in ("kcmp", "vcmp"):
         d = np.abs(gpu[key] - ref[key])
         assert d.max() <= 1e-3 * max(1.0, np.abs(ref[key]).max()), (key, d.max())
+    # the layer's two-launch pooling gives bit for bit what nsa_cmp_pool gives
+    dev = upload(inp)
+    V0, V1 = V[0], V[-1] + 1
+    for key, x, w in (("kcmp", dev["k"], dev["w_k"]), ("vcmp", dev["v"], dev["w_v"])):
+        one = binding.cmp_pool(x[V0:V1].contiguous(), w, out_bf16=False, out_f32=True)["f32"]
+        torch.cuda.synchronize()
+        assert np.array_equal(one.cpu().numpy(), gpu[key]), key
     fin = np.isfinite(ref["lse"])
     assert np.array_equal(fin, np.isfinite(gpu["lse"]))
     assert np.abs(gpu["lse"][fin] - ref["lse"][fin]).max() < 2e-2
