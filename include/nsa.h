@@ -28,7 +28,9 @@
  *   - All tensors are dense, row-major, with the last dimension contiguous,
  *     and 16-byte aligned.
  *   - The caller owns every buffer, including the workspace; the library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no state between calls (the opt-in
+ *     benchmark timing below is the one exception: while enabled it creates
+ *     HIP events and keeps per-kernel totals).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously; the call does not synchronise.
  *   - Every argument is validated before anything is enqueued. On any
@@ -252,7 +254,9 @@ nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim,
  * launch stream. nsa_timing_read() waits for the recorded events, folds them
  * into per-kernel totals and returns the number of distinct kernels; names
  * point into library storage valid until the next read or reset. Entries are
- * copied for the first max_entries kernels (arrays may be NULL). */
+ * copied for the first max_entries kernels (arrays may be NULL). The
+ * registry is process-wide (calls from several threads are serialised by a
+ * lock). */
 nsa_status nsa_timing_enable(int enable);
 nsa_status nsa_timing_reset(void);
 int nsa_timing_read(int max_entries, const char **names, double *total_ms, int *counts);
