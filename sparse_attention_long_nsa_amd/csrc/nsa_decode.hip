@@ -304,11 +304,13 @@ __global__ __launch_bounds__(D) void dec_combine_kernel(DecodeParams p) {
     for (int i = i0; i < i1; ++i) {
       const float m = part[(int64_t)i * (D + 2)];
       // an unused selection slot carries only (-inf, 0): its output entries
-      // were never written, so they are not read (0 * stale NaN is NaN)
-      if (m == -INFINITY) continue;
-      const float w = exp2f(m - M);
+      // were never written, so their values are selected away, not scaled
+      // by zero (0 * a stale NaN is NaN); branch-free, so the loads batch
+      const bool used = m != -INFINITY;
+      const float w = used ? exp2f(m - M) : 0.f;
       L += w * part[(int64_t)i * (D + 2) + 1];
-      o += w * part[(int64_t)i * (D + 2) + 2 + d];
+      const float ov = part[(int64_t)i * (D + 2) + 2 + d];
+      o += used ? w * ov : 0.f;
     }
     res[br] = o / L;
   }

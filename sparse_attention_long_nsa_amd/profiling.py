@@ -133,7 +133,9 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
         d = bench["decode"]
         lines += [f"bench.py in the same process reported {d['us_per_step']} us per decode step "
                   f"({d['roofline']['frac'] * 100:.1f}% of the HBM roofline); its event-timed per-kernel "
-                  "averages are listed beside the profiler's.", ""]
+                  "averages are listed beside the profiler's. Under the profiler every launch of these "
+                  "few-microsecond kernels gets a gap of its own, so that step time is inflated; the kernel "
+                  "durations are not, and their sum is the unprofiled step.", ""]
     elif bench and group == "dense" and bench.get("dense_mode"):
         d = bench["dense_mode"]
         lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per dense step "
