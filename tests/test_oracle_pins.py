@@ -14,6 +14,8 @@ Each test names the pin it checks:
   P13        permuting KV groups with their query heads permutes the output
   P14        one head per group: score == that head's compression probability
   P16        Dense-NSA mode: every row == torch fp64 SDPA causal
+  P17        gate prologue: activations == their library forms, identity layers,
+             a hand-worked example, affinity in the second layer
   P15        several vision runs: vision rows see only the vision tokens in
              position order (equal to the one-run layout), text rows dense causal
 """
@@ -413,3 +415,51 @@ def test_p16_dense_mode_is_dense_causal_on_every_row(n, hq, hkv):
     out = oracle.dense(inp)
     ref = sdpa_causal(inp["q"], inp["k"], inp["v"], hq, hkv)
     np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------- P17
+
+from oracle import gate_mlp  # noqa: E402
+
+
+@pytest.mark.parametrize("act", gate_mlp.ACTIVATIONS)
+def test_p17_activations_match_their_library_forms(act):
+    x = np.linspace(-6.0, 6.0, 2001)
+    t = torch.from_numpy(x)
+    ref = {"silu": torch.nn.functional.silu(t),
+           "gelu_tanh": torch.nn.functional.gelu(t, approximate="tanh"),
+           "relu": torch.relu(t)}[act].numpy()
+    np.testing.assert_allclose(gate_mlp.activation(x, act), ref, rtol=0, atol=1e-14)
+
+
+def test_p17_identity_layers_give_the_activation_of_the_input():
+    # W1 = I, no biases, W2 = I: the logits are act(x), laid out head-major
+    rng = np.random.default_rng(7)
+    hq = 4
+    x = rng.standard_normal((5, 3 * hq))
+    eye = np.eye(3 * hq)
+    for act in gate_mlp.ACTIVATIONS:
+        out = gate_mlp.gate_logits(x, eye, None, eye, None, act, hq)
+        np.testing.assert_allclose(out, gate_mlp.activation(x, act).reshape(5, hq, 3), rtol=0, atol=0)
+
+
+def test_p17_hand_worked_example():
+    # d_model 2, d_hidden 2, one head: W1 = [[1, 2], [0, -1]], b1 = [0.5, 0],
+    # x = [1, -1]: pre = [1 - 2 + 0.5, 0 + 1] = [-0.5, 1]; relu -> [0, 1];
+    # W2 rows [1, 1], [2, 0], [0, -3], b2 = [0, 1, 2]: logits = [1, 1, -1]
+    x = np.array([[1.0, -1.0]])
+    w1 = np.array([[1.0, 2.0], [0.0, -1.0]])
+    w2 = np.array([[1.0, 1.0], [2.0, 0.0], [0.0, -3.0]])
+    out = gate_mlp.gate_logits(x, w1, [0.5, 0.0], w2, [0.0, 1.0, 2.0], "relu", 1)
+    np.testing.assert_array_equal(out, [[[1.0, 1.0, -1.0]]])
+
+
+def test_p17_logits_are_affine_in_the_second_layer():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((6, 16))
+    w1, b1 = rng.standard_normal((8, 16)), rng.standard_normal(8)
+    w2a, w2b = rng.standard_normal((6, 8)), rng.standard_normal((6, 8))
+    ga = gate_mlp.gate_logits(x, w1, b1, w2a, None, "silu", 2)
+    gb = gate_mlp.gate_logits(x, w1, b1, w2b, None, "silu", 2)
+    gab = gate_mlp.gate_logits(x, w1, b1, w2a + 2 * w2b, None, "silu", 2)
+    np.testing.assert_allclose(gab, ga + 2 * gb, rtol=0, atol=1e-12)
