@@ -199,6 +199,59 @@ def run_dense_bench(dev, shape, steps, warmup, nsa_ms):
             "nsa_speedup": round(ms / nsa_ms, 2), "steps": steps, "kernels": kern}
 
 
+GATE_D_MODEL, GATE_D_HIDDEN = 3584, 1024  # Qwen2.5-VL-7B width; the MLP width is not given
+
+
+def run_gate_bench(shape, steps, warmup):
+    """Gate prologue on the layer's tokens: hidden states [N, 3584] -> gate
+    logits [N, Hq, 3] through a 1,024-unit SiLU MLP."""
+    import torch
+    from sparse_attention_long_nsa_amd import binding
+    from sparse_attention_long_nsa_amd.inputs import make_gate_inputs
+    n, hq = shape.n_tokens, shape.n_q_heads
+    g = make_gate_inputs(n, GATE_D_MODEL, GATE_D_HIDDEN, hq, seed=0)
+    d = {k: torch.from_numpy(g[k]).to("cuda:0").to(torch.bfloat16).contiguous() for k in ("x", "w1", "w2")}
+    b1, b2 = torch.from_numpy(g["b1"]).to("cuda:0"), torch.from_numpy(g["b2"]).to("cuda:0")
+    del g
+
+    def call(out=None, ws=None):
+        return binding.gate_logits(d["x"], d["w1"], b1, d["w2"], b2, hq, "silu", out=out, workspace=ws)
+    out = call()
+    ws = torch.empty(binding.gate_workspace_size(binding.GateDesc(n, GATE_D_MODEL, GATE_D_HIDDEN, hq, 0, 0)),
+                     dtype=torch.uint8, device="cuda:0")
+    for _ in range(warmup):
+        call(out, ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call(out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    binding.timing_reset()
+    binding.timing_enable(True)
+    for _ in range(steps):
+        call(out, ws)
+    torch.cuda.synchronize()
+    kern = {k: round(tot / cnt, 4) for k, (tot, cnt) in binding.timing_read().items()}
+    binding.timing_enable(False)
+    binding.timing_reset()
+    flops_h = 2.0 * n * GATE_D_MODEL * GATE_D_HIDDEN
+    bytes_o = 2.0 * n * GATE_D_HIDDEN + 4.0 * n * 3 * hq  # read the fp16 hidden layer, write the logits
+    res = {"ms_per_step": round(ms, 4), "n_tokens": n, "d_model": GATE_D_MODEL, "d_hidden": GATE_D_HIDDEN,
+           "activation": "silu", "steps": steps, "kernels": kern}
+    if "gate_hidden" in kern:
+        tf = flops_h / (kern["gate_hidden"] * 1e-3) / 1e12
+        res["gate_hidden"] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    if "gate_out" in kern:
+        gbs = bytes_o / (kern["gate_out"] * 1e-3) / 1e9
+        res["gate_out"] = {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    log(f"gate prologue: {res}")
+    return res
+
+
 def run_scaling_bench(shape, steps, warmup):
     """Step time against context length at the workload's k and w: 16K to
     512K vision tokens (the largest the kernels take) plus its text tokens."""
@@ -369,6 +422,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-spans", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--scaling", action="store_true",
                     help="also time 16K..512K vision tokens (about a minute more, mostly input generation)")
     args = ap.parse_args()
@@ -446,6 +500,10 @@ def main():
     if not args.no_dense:
         dense = run_dense_bench(dev, shape, 3, 1, ms)
 
+    gate = None
+    if not args.no_gate:
+        gate = run_gate_bench(shape, max(3, args.steps // 2), 1)
+
     spans = None
     if not args.no_spans:
         spans = run_spans_bench(inp, shape, max(3, args.steps // 2), 1, ms)
@@ -493,6 +551,7 @@ def main():
         "decode": decode,
         "several_vision_runs": spans,
         "dense_mode": dense,
+        "gate_prologue": gate,
         "context_scaling": scaling,
         "cpu_baseline": cpu,
     }

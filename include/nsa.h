@@ -171,6 +171,41 @@ nsa_status nsa_prefill_dense(const nsa_prefill_desc *desc, const void *q, const 
                              const void *v, float *out, float *lse_out, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------- gate prologue
+ * Gate logits from hidden states (VideoNSA paper summary page, "Method";
+ * model card, "Model Architecture": a two-layer MLP and a sigmoid give each
+ * head its three branch gates). Reading: logits = W2 . act(W1 . x + b1) + b2
+ * per token, W1 [d_hidden, d_model], W2 [3 Hq, d_hidden] with row 3 h + c
+ * giving head h's logit for branch c (compression, selection, window), so the
+ * output is exactly the gate_logits argument of nsa_prefill; the pages give
+ * neither the width nor the activation, so both are the caller's. The
+ * sigmoid is applied by the layer. Enqueue it before nsa_prefill on the same
+ * stream to feed the layer from hidden states.
+ * Supported: bf16 x / W1 / W2 (fp32 biases, optional), d_model a multiple of
+ * 64, d_hidden a multiple of 128, 3 Hq <= 96, N <= 2^30 and N d_hidden <= 2^37;
+ * anything else returns NSA_ERR_UNSUPPORTED. Arithmetic: bf16 products with
+ * fp32 sums for the hidden layer, which is kept in fp16; fp16 products with
+ * fp32 sums for the logits.
+ *   x            device [N, d_model]       bf16
+ *   w1, b1       device [d_hidden, d_model] bf16, [d_hidden] float32 or NULL
+ *   w2, b2       device [3 Hq, d_hidden]   bf16, [3 Hq] float32 or NULL
+ *   gate_logits  device [N, Hq, 3]         float32 (written)
+ *   workspace    device, >= nsa_gate_workspace_size bytes (2 N d_hidden), 256-B aligned */
+typedef enum { NSA_ACT_SILU = 0, NSA_ACT_GELU_TANH = 1, NSA_ACT_RELU = 2 } nsa_activation;
+typedef struct {
+  int64_t n_tokens;
+  int32_t d_model;
+  int32_t d_hidden;
+  int32_t n_q_heads;
+  int32_t activation; /* nsa_activation */
+  int32_t dtype;      /* NSA_DTYPE_BF16 */
+} nsa_gate_desc;
+nsa_status nsa_gate_workspace_size(const nsa_gate_desc *desc, size_t *bytes);
+nsa_status nsa_gate_logits(const nsa_gate_desc *desc, const void *x, const void *w1,
+                           const float *b1, const void *w2, const float *b2,
+                           float *gate_logits, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 /* ------------------------------------------------------------------- decode
  * One new query per sequence, at the last slot (L-1) of its vision cache
  * (VideoNSA paper summary page, "Method"; evaluated exactly as prefill's row

@@ -24,7 +24,9 @@ EXPORTED = (
     "nsa_status_string", "nsa_version", "nsa_probe_mfma_bf16",
     "nsa_prefill_dense_workspace_size", "nsa_prefill_dense", "nsa_cache_append",
     "nsa_prefill_varlen_workspace_size", "nsa_prefill_varlen",
+    "nsa_gate_workspace_size", "nsa_gate_logits",
 )
+NSA_ACTIVATIONS = {"silu": 0, "gelu_tanh": 1, "relu": 2}
 
 
 class NsaError(RuntimeError):
@@ -63,6 +65,17 @@ class DecodeDesc(ctypes.Structure):
     ]
 
 
+class GateDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("d_model", ctypes.c_int32),
+        ("d_hidden", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("activation", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -88,6 +101,10 @@ def lib() -> ctypes.CDLL:
         L.nsa_prefill_varlen_workspace_size.restype = ctypes.c_int
         L.nsa_prefill_varlen.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_int32] + [P] * 14 + [S, P]
         L.nsa_prefill_varlen.restype = ctypes.c_int
+        L.nsa_gate_workspace_size.argtypes = [ctypes.POINTER(GateDesc), ctypes.POINTER(S)]
+        L.nsa_gate_workspace_size.restype = ctypes.c_int
+        L.nsa_gate_logits.argtypes = [ctypes.POINTER(GateDesc)] + [P] * 7 + [S, P]
+        L.nsa_gate_logits.restype = ctypes.c_int
         L.nsa_cache_append.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 9
         L.nsa_cache_append.restype = ctypes.c_int
         L.nsa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.POINTER(S)]
@@ -314,6 +331,44 @@ def prefill_dense(q, k, v, scale=0.0, out=None, want_lse=False, workspace=None, 
         raise NsaError(st, "nsa_prefill_dense")
     res["workspace"] = workspace
     return res
+
+
+def gate_workspace_size(desc: GateDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().nsa_gate_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_gate_workspace_size")
+    return n.value
+
+
+def gate_logits(x, w1, b1, w2, b2, n_q_heads, activation="silu", out=None, workspace=None,
+                stream=None) -> torch.Tensor:
+    """Runs nsa_gate_logits: gate logits [N, Hq, 3] (fp32) of hidden states
+    x [N, d_model] through W1 [d_hidden, d_model], act, W2 [3 Hq, d_hidden]
+    (bf16 on the device; biases fp32 or None)."""
+    n, dm = x.shape
+    dh = w1.shape[0]
+    _check_dev("x", x, torch.bfloat16, (n, dm))
+    _check_dev("w1", w1, torch.bfloat16, (dh, dm))
+    _check_dev("w2", w2, torch.bfloat16, (3 * n_q_heads, dh))
+    if b1 is not None:
+        _check_dev("b1", b1, torch.float32, (dh,))
+    if b2 is not None:
+        _check_dev("b2", b2, torch.float32, (3 * n_q_heads,))
+    if activation not in NSA_ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(NSA_ACTIVATIONS)}")
+    desc = GateDesc(n, dm, dh, n_q_heads, NSA_ACTIVATIONS[activation], NSA_DTYPE_BF16)
+    if out is None:
+        out = torch.empty((n, n_q_heads, 3), dtype=torch.float32, device=x.device)
+    _check_dev("out", out, torch.float32, (n, n_q_heads, 3))
+    ws_bytes = gate_workspace_size(desc)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=x.device)
+    st = lib().nsa_gate_logits(ctypes.byref(desc), _ptr(x), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out),
+                               _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_gate_logits")
+    return out
 
 
 def cache_append(k_new, v_new, k_cache, v_cache, w_cmp_k, w_cmp_v, k_cmp, v_cmp, cache_len,

@@ -433,6 +433,51 @@ nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim, int32
   return NSA_OK;
 }
 
+static nsa_status plan_gate(const nsa_gate_desc *ds, size_t *bytes) {
+  if (!ds) return NSA_ERR_INVALID_ARG;
+  if (ds->n_tokens < 1 || ds->d_model < 1 || ds->d_hidden < 1 || ds->n_q_heads < 1) return NSA_ERR_INVALID_ARG;
+  if (ds->activation < NSA_ACT_SILU || ds->activation > NSA_ACT_RELU) return NSA_ERR_INVALID_ARG;
+  if (ds->dtype != NSA_DTYPE_BF16 && ds->dtype != NSA_DTYPE_FP32) return NSA_ERR_INVALID_ARG;
+  if (ds->dtype != NSA_DTYPE_BF16 || ds->d_model % 64 != 0 || ds->d_hidden % 128 != 0 || 3 * ds->n_q_heads > 96)
+    return NSA_ERR_UNSUPPORTED;
+  // launch grids: ceil(N / 128) * (d_hidden / 128) and ceil(N / 64) workgroups of 256 threads
+  if (ds->n_tokens > ((int64_t)1 << 30) || ds->n_tokens * (int64_t)ds->d_hidden > ((int64_t)1 << 37))
+    return NSA_ERR_UNSUPPORTED;
+  *bytes = align_up(sizeof(uint16_t) * (size_t)ds->n_tokens * (size_t)ds->d_hidden);
+  return NSA_OK;
+}
+
+nsa_status nsa_gate_workspace_size(const nsa_gate_desc *desc, size_t *bytes) {
+  if (!bytes) return NSA_ERR_INVALID_ARG;
+  size_t need = 0;
+  const nsa_status st = plan_gate(desc, &need);
+  if (st != NSA_OK) return st;
+  *bytes = need;
+  return NSA_OK;
+}
+
+nsa_status nsa_gate_logits(const nsa_gate_desc *desc, const void *x, const void *w1, const float *b1,
+                           const void *w2, const float *b2, float *gate_logits, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  size_t need = 0;
+  const nsa_status st = plan_gate(desc, &need);
+  if (st != NSA_OK) return st;
+  if (!x || !w1 || !w2 || !gate_logits) return NSA_ERR_INVALID_ARG;
+  const void *ptrs[] = {x, w1, b1, w2, b2, gate_logits};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return NSA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < need) return NSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return NSA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GateParams gp{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w1), b1,
+                static_cast<const uint16_t *>(w2), b2, static_cast<uint16_t *>(workspace), gate_logits,
+                desc->n_tokens, desc->d_model, desc->d_hidden, desc->n_q_heads, desc->activation};
+  hipError_t e = hipSuccess;
+  NSA_LAUNCH("gate_hidden", launch_gate(gp, 0, s));
+  NSA_LAUNCH("gate_out", launch_gate(gp, 1, s));
+  return NSA_OK;
+}
+
 nsa_status nsa_prefill_dense_workspace_size(const nsa_prefill_desc *desc, size_t *bytes) {
   if (!bytes) return NSA_ERR_INVALID_ARG;
   DensePlan pl;

@@ -102,6 +102,18 @@ struct DenseParams {
   float sl2;
 };
 
+struct GateParams {
+  const uint16_t *x;       // [N, d_model] bf16 hidden states
+  const uint16_t *w1;      // [d_hidden, d_model] bf16
+  const float *b1;         // [d_hidden] or null
+  const uint16_t *w2;      // [3 Hq, d_hidden] bf16
+  const float *b2;         // [3 Hq] or null
+  uint16_t *h;             // workspace [N, d_hidden] fp16
+  float *logits;           // [N, Hq, 3]
+  int64_t n;
+  int d_model, d_hidden, hq, act;  // act: 0 SiLU, 1 GELU (tanh form), 2 ReLU
+};
+
 // One slice of the token-kind mask, as kernel arguments: bit j of word i
 // says whether position base + 32 i + j is a vision token.
 constexpr int kMaskWords = 512;
@@ -166,6 +178,8 @@ hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_merge(const TextParams &p, int d, hipStream_t st);
 hipError_t launch_dense_attn(const DenseParams &p, int d, int G, bool f16, hipStream_t st);
+// layer 0: hidden layer into p.h; layer 1: logits from p.h
+hipError_t launch_gate(const GateParams &p, int layer, hipStream_t st);
 hipError_t launch_decode(const DecodeParams &p, int d, int G, hipStream_t st);
 
 // Which (head_dim, query heads per KV head) pairs have kernels.

@@ -204,6 +204,26 @@ SPAN_LAYOUTS = {
 }
 
 
+def make_gate_inputs(n: int, d_model: int, d_hidden: int, n_q_heads: int, seed: int = 0,
+                     bias: bool = True) -> dict:
+    """Draw one gate-prologue workload: hidden states x [n, d_model] ~ N(0, 1)
+    (a decoder layer's normalised input has unit RMS per token), W1
+    [d_hidden, d_model] ~ N(0, 1/d_model), W2 [3 Hq, d_hidden] ~ N(0,
+    1/d_hidden), biases b1 [d_hidden], b2 [3 Hq] ~ N(0, 0.1^2) (or None).
+    Draw order x, W1, W2, b1, b2; x, W1, W2 are rounded to bf16, the biases
+    stay float32."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = np.empty((n, d_model), dtype=np.float32)
+    step = 8192
+    for r0 in range(0, n, step):  # bounded temporaries at long contexts
+        x[r0:r0 + step] = round_to_bf16(_normal(rng, (min(step, n - r0), d_model)))
+    w1 = round_to_bf16(_normal(rng, (d_hidden, d_model)) * np.float32(1.0 / math.sqrt(d_model)))
+    w2 = round_to_bf16(_normal(rng, (3 * n_q_heads, d_hidden)) * np.float32(1.0 / math.sqrt(d_hidden)))
+    b1 = _normal(rng, (d_hidden,)) * np.float32(0.1)
+    b2 = _normal(rng, (3 * n_q_heads,)) * np.float32(0.1)
+    return dict(x=x, w1=w1, w2=w2, b1=b1 if bias else None, b2=b2 if bias else None, n_q_heads=n_q_heads)
+
+
 def make_decode_inputs(shape: DecodeShape, seed: int = 0) -> dict:
     """Draw one decode workload: per sequence a frame-correlated vision K/V
     cache [Bt,L,Hkv,d]; the query is the last cache token, so it is drawn from

@@ -51,9 +51,12 @@ KERNELS = [
     ("dec_select_kernel", "dec_select", "sparse_attention_long_nsa_amd/csrc/nsa_decode.hip"),
     ("dec_combine_kernel", "dec_combine", "sparse_attention_long_nsa_amd/csrc/nsa_decode.hip"),
     ("mfma_loop_kernel", "mfma_probe", "sparse_attention_long_nsa_amd/csrc/nsa_probe.hip"),
+    ("gate_hidden_kernel", "gate_hidden", "sparse_attention_long_nsa_amd/csrc/nsa_gate.hip"),
+    ("gate_out_kernel", "gate_out", "sparse_attention_long_nsa_amd/csrc/nsa_gate.hip"),
 ]
 DECODE_KERNELS = ("dec_item_cmp_win", "dec_item_sel", "dec_select", "dec_combine")
 DENSE_KERNELS = ("pack_dense", "dense_attn")
+GATE_KERNELS = ("gate_hidden", "gate_out")
 PREFILL_KERNELS = ("sel_attn", "cmp_attn", "swa_attn", "text_attn", "text_merge", "blk_score_topk", "cmp_pool",
                    "cmp_pool_mean", "cmp_pool_map", "pack_kv", "pack_cmp", "pack_text")
 
@@ -111,7 +114,7 @@ def source_digest(path: str) -> str:
 
 def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, command: str,
                   out_md: str, group: str = "prefill") -> None:
-    keep = {"decode": DECODE_KERNELS, "dense": DENSE_KERNELS}.get(group, PREFILL_KERNELS)
+    keep = {"decode": DECODE_KERNELS, "dense": DENSE_KERNELS, "gate": GATE_KERNELS}.get(group, PREFILL_KERNELS)
     dur = defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
         name, _ = short_name(r["Kernel_Name"], _grid(r), grid_names)
@@ -123,6 +126,8 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
         kern = {k: {"avg_ms": round(v["avg_us"] * 1e-3, 4)} for k, v in dec.get("kernels", {}).items()}
     elif group == "dense":
         kern = ((bench or {}).get("dense_mode") or {}).get("kernels", {})
+    elif group == "gate":
+        kern = {k: {"avg_ms": v} for k, v in ((bench or {}).get("gate_prologue") or {}).get("kernels", {}).items()}
     else:
         kern = bench["kernels"] if bench else {}
     total = sum(sum(v) / len(v) for v in dur.values())
@@ -141,6 +146,12 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
         lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per dense step "
                   f"({d['tflops']} TF/s of algorithmic flops, {d['mfma_peak_frac'] * 100:.1f}% of the bf16 "
                   "peak); its event-timed per-kernel averages are listed beside the profiler's.", ""]
+    elif bench and group == "gate" and bench.get("gate_prologue"):
+        d = bench["gate_prologue"]
+        lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per gate prologue over "
+                  f"{d['n_tokens']} tokens (d_model {d['d_model']}, d_hidden {d['d_hidden']}); hidden layer "
+                  f"{d.get('gate_hidden')}, output layer {d.get('gate_out')}; its event-timed per-kernel "
+                  "averages are listed beside the profiler's.", ""]
     elif bench:
         lines += [f"bench.py in the same process reported {bench['ms_per_step']} ms/step "
                   f"({bench['value']:.0f} tokens/s); its event-timed per-kernel averages are listed "
@@ -329,7 +340,7 @@ def main(argv=None) -> None:
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
-    t.add_argument("--group", choices=("prefill", "decode", "dense"), default="prefill")
+    t.add_argument("--group", choices=("prefill", "decode", "dense", "gate"), default="prefill")
     m = sub.add_parser("pmc-summary")
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
         m.add_argument(f"--{k}-csv", required=True)

@@ -298,3 +298,55 @@ def test_varlen_validates_every_sequence_first():
     assert call({"q": None}) == binding.NSA_ERR_INVALID_ARG
     assert call({"ws": None}) == binding.NSA_ERR_WORKSPACE
     assert call({"g": FAKE + 4}) == binding.NSA_ERR_INVALID_ARG
+
+
+def gdesc(n=1000, dm=3584, dh=1024, hq=28, act=0, dtype=0):
+    return binding.GateDesc(n, dm, dh, hq, act, dtype)
+
+
+def gate_ws(ds):
+    n = ctypes.c_size_t(0)
+    st = binding.lib().nsa_gate_workspace_size(ctypes.byref(ds) if ds is not None else None, ctypes.byref(n))
+    return st, n.value
+
+
+def call_gate(ds, ptrs=None, ws=FAKE, ws_bytes=1 << 40):
+    p = dict(x=FAKE, w1=FAKE, b1=None, w2=FAKE, b2=None, out=FAKE)
+    if ptrs:
+        p.update(ptrs)
+    return binding.lib().nsa_gate_logits(ctypes.byref(ds) if ds is not None else None, p["x"], p["w1"], p["b1"],
+                                         p["w2"], p["b2"], p["out"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), binding.NSA_ERR_INVALID_ARG),
+    (dict(dh=0), binding.NSA_ERR_INVALID_ARG),
+    (dict(act=3), binding.NSA_ERR_INVALID_ARG),
+    (dict(dtype=7), binding.NSA_ERR_INVALID_ARG),
+    (dict(dtype=1), binding.NSA_ERR_UNSUPPORTED),
+    (dict(dm=3584 + 32), binding.NSA_ERR_UNSUPPORTED),
+    (dict(dh=1024 + 64), binding.NSA_ERR_UNSUPPORTED),
+    (dict(hq=33), binding.NSA_ERR_UNSUPPORTED),   # 99 outputs > 96
+    (dict(hq=32, act=2), binding.NSA_OK),
+])
+def test_gate_validation(kw, status):
+    assert gate_ws(gdesc(**kw))[0] == status
+
+
+def test_gate_workspace_and_pointer_checks():
+    st, need = gate_ws(gdesc())
+    assert st == binding.NSA_OK and need == 1000 * 1024 * 2  # the fp16 hidden layer
+    assert gate_ws(None)[0] == binding.NSA_ERR_INVALID_ARG
+    assert call_gate(None) == binding.NSA_ERR_INVALID_ARG
+    for name in ("x", "w1", "w2", "out"):
+        assert call_gate(gdesc(), {name: None}) == binding.NSA_ERR_INVALID_ARG, name
+    assert call_gate(gdesc(), {"b1": FAKE + 4}) == binding.NSA_ERR_INVALID_ARG
+    assert call_gate(gdesc(), ws=None) == binding.NSA_ERR_WORKSPACE
+    assert call_gate(gdesc(), ws_bytes=need - 1) == binding.NSA_ERR_WORKSPACE
+    assert call_gate(gdesc(), ws=FAKE + 16, ws_bytes=need) == binding.NSA_ERR_WORKSPACE
+
+
+def test_gate_size_limits():
+    assert gate_ws(gdesc(n=(1 << 30) + 1, dh=128))[0] == binding.NSA_ERR_UNSUPPORTED
+    assert gate_ws(gdesc(n=1 << 27, dh=2048))[0] == binding.NSA_ERR_UNSUPPORTED
+    assert gate_ws(gdesc(n=1 << 26, dh=2048))[0] == binding.NSA_OK
