@@ -440,7 +440,7 @@ static nsa_status plan_gate(const nsa_gate_desc *ds, size_t *bytes) {
   if (ds->dtype != NSA_DTYPE_BF16 && ds->dtype != NSA_DTYPE_FP32) return NSA_ERR_INVALID_ARG;
   if (ds->dtype != NSA_DTYPE_BF16 || ds->d_model % 64 != 0 || ds->d_hidden % 128 != 0 || 3 * ds->n_q_heads > 96)
     return NSA_ERR_UNSUPPORTED;
-  // launch grids: ceil(N / 128) * (d_hidden / 128) and ceil(N / 64) workgroups of 256 threads
+  // launch grids: ceil(N / 256) * (d_hidden / 128) and ceil(N / 256) workgroups of 256 threads
   if (ds->n_tokens > ((int64_t)1 << 30) || ds->n_tokens * (int64_t)ds->d_hidden > ((int64_t)1 << 37))
     return NSA_ERR_UNSUPPORTED;
   *bytes = align_up(sizeof(uint16_t) * (size_t)ds->n_tokens * (size_t)ds->d_hidden);

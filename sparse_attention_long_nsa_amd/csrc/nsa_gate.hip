@@ -9,11 +9,11 @@
 // Two matrix-core launches:
 //   gate_hidden_kernel  H = act(X W1^T + b1) as fp16 [N, d_hidden]: bf16
 //                       operands (exact products), fp32 accumulation, 128 x
-//                       128 output tiles of 4 waves (64 x 64 each), both
-//                       operand tiles staged through LDS in 64-wide k slices
-//                       with 16-byte chunks swizzled per row, double-buffered
-//                       through registers;
-//   gate_out_kernel     logits = H W2^T + b2: fp16 operands, one wave per 16
+//                       256 (hidden x token) tiles of 4 waves (64 x 128
+//                       each), both operands staged through a three-slot LDS
+//                       ring of 64-wide k slices by direct global->LDS
+//                       copies, 16-byte chunks swizzled per row;
+//   gate_out_kernel     logits = H W2^T + b2: fp16 operands, one wave per 64
 //                       tokens and all 3 Hq outputs, operands straight from
 //                       global memory (W2 stays in the L2).
 #include "nsa_kernels.h"
@@ -23,9 +23,14 @@ namespace nsa {
 
 namespace {
 
-constexpr int kGT = 128;  // output tile edge of the hidden layer
-constexpr int kGK = 64;   // k slice staged per step
+// Hidden layer: a workgroup computes a 128 (hidden) x 256 (token) tile of
+// H^T with four waves of 64 x 128; k advances in 64-wide slices through a
+// ring of kGS LDS stages filled by direct global->LDS copies, so two slices
+// are in flight while one is multiplied.
+constexpr int kGH = 128, kGTok = 256, kGK = 64, kGS = 3;
 constexpr int kGThreads = 256;
+constexpr int kStageW = kGH * kGK, kStage = (kGH + kGTok) * kGK;  // elements
+constexpr int kPiecesPerWave = (kGH + kGTok) * kGK / 512 / 4;     // 1 KB copies per wave per stage
 
 __device__ __forceinline__ float act_fn(float h, int act) {
   if (act == 0) return h / (1.f + expf(-h));                       // SiLU
@@ -36,72 +41,76 @@ __device__ __forceinline__ float act_fn(float h, int act) {
   return fmaxf(h, 0.f);                                            // ReLU
 }
 
-// Loads this thread's four 16-byte chunks of a [128 rows][64] bf16 slice
-// (rows past n_rows read as zeros).
-__device__ __forceinline__ void load_slice(const uint16_t *src, int64_t ld, int64_t row0, int64_t n_rows, int k0,
-                                           int tid, u16x8 (&v)[4]) {
+// Issues this wave's share of one stage: 1 KB pieces of eight 128-byte rows
+// (W1 rows hid0.., then token rows tok0..; rows past the last token re-read
+// it). Each lane fetches the logical chunk whose swizzled slot it fills, so
+// the stage holds the K-tile layout of 128-byte rows.
+__device__ __forceinline__ void gate_stage(const GateParams &p, int hid0, int64_t tok0, int k0, uint16_t *stage,
+                                           int wv, int lane) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = tid + kGThreads * j;  // chunk id: row e / 8, chunk e % 8
-    const int r = e >> 3, c = e & 7;
-    const int64_t row = row0 + r;
-    v[j] = row < n_rows ? *reinterpret_cast<const u16x8 *>(src + row * ld + k0 + 8 * c) : zero8();
+  for (int j = 0; j < kPiecesPerWave; ++j) {
+    const int q = wv * kPiecesPerWave + j;  // piece id: rows 8q .. 8q + 7 of the stage
+    const int r = 8 * q + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const uint16_t *src;
+    if (r < kGH) {
+      src = p.w1 + (int64_t)(hid0 + r) * p.d_model;
+    } else {
+      const int64_t t = min(tok0 + (r - kGH), p.n - 1);
+      src = p.x + t * p.d_model;
+    }
+    __builtin_amdgcn_global_load_lds(src + k0 + 8 * c, (lds_void *)(stage + 8 * q * kGK), 16, 0, 0);
   }
 }
 
-// Stores them swizzled (the K-tile layout of 128-byte rows).
-__device__ __forceinline__ void store_slice(uint16_t *dst, int tid, const u16x8 (&v)[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = tid + kGThreads * j;
-    const int r = e >> 3, c = e & 7;
-    *reinterpret_cast<u16x8 *>(dst + r * kGK + 8 * PackedTile<kGK>::template swz<2 * kGK>(r, c)) = v[j];
-  }
-}
-
-__global__ __launch_bounds__(kGThreads) void gate_hidden_kernel(GateParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sw[2][kGT * kGK], sx[2][kGT * kGK];
+__global__ __launch_bounds__(kGThreads) void gate_hidden_kernel(GateParams p, int n_tt) {
+  __shared__ __attribute__((aligned(16))) uint16_t ring[kGS * kStage];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n_ht = p.d_hidden / kGT;
-  const int hid0 = (int)(blockIdx.x % n_ht) * kGT;
-  const int64_t tok0 = (int64_t)(blockIdx.x / n_ht) * kGT;
-  const int wh = (wv & 1) * 64, wt = (wv >> 1) * 64;  // this wave's 64 x 64 quadrant
-  f32x4 acc[4][4];
+  const int n_ht = p.d_hidden / kGH;
+  // XCD-aware order: ids 8 apart run on one XCD; each XCD walks all hidden
+  // tiles of one token tile before the next, so the token rows stay in its L2
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int tt = (j / n_ht) * 8 + xcd;
+  if (tt >= n_tt) return;
+  const int hid0 = (j % n_ht) * kGH;
+  const int64_t tok0 = (int64_t)tt * kGTok;
+  const int wh = (wv & 1) * 64, wt = (wv >> 1) * 128;  // this wave's 64 x 128 part
+  f32x4 acc[4][8];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = zero4();
-  u16x8 rw[4], rx[4];
-  load_slice(p.w1, p.d_model, hid0, p.d_hidden, 0, tid, rw);
-  load_slice(p.x, p.d_model, tok0, p.n, 0, tid, rx);
+    for (int b = 0; b < 8; ++b) acc[a][b] = zero4();
   const int n_k = p.d_model / kGK;
+  gate_stage(p, hid0, tok0, 0, ring, wv, lane);
+  if (n_k > 1) gate_stage(p, hid0, tok0, kGK, ring + kStage, wv, lane);
   for (int s = 0; s < n_k; ++s) {
-    uint16_t *cw = sw[s & 1], *cx = sx[s & 1];
-    store_slice(cw, tid, rw);
-    store_slice(cx, tid, rx);
-    __syncthreads();
-    if (s + 1 < n_k) {  // the next slice flies while this one is used
-      load_slice(p.w1, p.d_model, hid0, p.d_hidden, (s + 1) * kGK, tid, rw);
-      load_slice(p.x, p.d_model, tok0, p.n, (s + 1) * kGK, tid, rx);
-    }
+    if (s + 1 < n_k) wait_vm_c<kPiecesPerWave>();  // this wave's copies of slice s have landed
+    else wait_vm_c<0>();
+    bare_barrier();  // everyone's have; and slot (s - 1) % kGS is no longer read
+    if (s + 2 < n_k) gate_stage(p, hid0, tok0, (s + 2) * kGK, ring + ((s + 2) % kGS) * kStage, wv, lane);
+    const uint16_t *cw = ring + (s % kGS) * kStage, *cx = cw + kStageW;
 #pragma unroll
     for (int ks = 0; ks < kGK / 32; ++ks) {
-      u16x8 fa[4], fb[4];
+      u16x8 fa[4], fb[8];
 #pragma unroll
       for (int a = 0; a < 4; ++a) fa[a] = pk_k_frag<kGK>(cw + wh * kGK, a, ks, lane);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) fb[b] = pk_k_frag<kGK>(cx + wt * kGK, b, ks, lane);
+      for (int b = 0; b < 8; ++b) fb[b] = pk_k_frag<kGK>(cx + wt * kGK, b, ks, lane);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma_bf16(fa[a], fb[b], acc[a][b]);
+        for (int b = 0; b < 8; ++b) acc[a][b] = mfma_bf16(fa[a], fb[b], acc[a][b]);
     }
-    // the other buffer is overwritten only after the next barrier
   }
   // acc[a][b][i]: hidden hid0 + wh + 16a + 4 (lane / 16) + i, token tok0 + wt + 16b + lane % 16
   const int grp = lane >> 4;
+  float bias[4][4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias[a][i] = p.b1 ? p.b1[hid0 + wh + 16 * a + 4 * grp + i] : 0.f;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
     const int64_t tok = tok0 + wt + 16 * b + (lane & 15);
     if (tok >= p.n) continue;
 #pragma unroll
@@ -109,30 +118,36 @@ __global__ __launch_bounds__(kGThreads) void gate_hidden_kernel(GateParams p) {
       const int h0 = hid0 + wh + 16 * a + 4 * grp;
       u16x4 hv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pre = acc[a][b][i] + (p.b1 ? p.b1[h0 + i] : 0.f);
-        hv[i] = f2h_bits(act_fn(pre, p.act));
-      }
+      for (int i = 0; i < 4; ++i) hv[i] = f2h_bits(act_fn(acc[a][b][i] + bias[a][i], p.act));
       *reinterpret_cast<u16x4 *>(p.h + tok * p.d_hidden + h0) = hv;
     }
   }
 }
 
-// One wave per 16 tokens; 4 waves per workgroup.
-constexpr int kOutTiles = 6;  // 96 outputs: 3 Hq <= 96
+// Output layer: one wave per 64 tokens (four 16-token column groups sharing
+// each W2 fragment), all 3 Hq <= 96 outputs; W2 is read from the L2 and
+// converted to fp16 once per fragment.
+constexpr int kOutTiles = 6;   // 96 outputs
+constexpr int kOutGroups = 4;  // 16-token groups per wave
 
 __global__ __launch_bounds__(256) void gate_out_kernel(GateParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4;
-  const int64_t tok0 = ((int64_t)blockIdx.x * 4 + wv) * 16;
+  const int64_t tok0 = ((int64_t)blockIdx.x * 4 + wv) * (16 * kOutGroups);
   if (tok0 >= p.n) return;
   const int n_out = 3 * p.hq;
-  const int64_t tok = min(tok0 + (lane & 15), p.n - 1);  // rows past n re-read the last one
-  const uint16_t *hr = p.h + tok * p.d_hidden + 8 * grp;
-  f32x4 acc[kOutTiles];
+  const uint16_t *hr[kOutGroups];
 #pragma unroll
-  for (int a = 0; a < kOutTiles; ++a) acc[a] = zero4();
+  for (int g = 0; g < kOutGroups; ++g)  // rows past n re-read the last one
+    hr[g] = p.h + min(tok0 + 16 * g + (lane & 15), p.n - 1) * p.d_hidden + 8 * grp;
+  f32x4 acc[kOutTiles][kOutGroups];
+#pragma unroll
+  for (int a = 0; a < kOutTiles; ++a)
+#pragma unroll
+    for (int g = 0; g < kOutGroups; ++g) acc[a][g] = zero4();
   for (int j0 = 0; j0 < p.d_hidden; j0 += 32) {
-    const u16x8 fb = *reinterpret_cast<const u16x8 *>(hr + j0);
+    u16x8 fb[kOutGroups];
+#pragma unroll
+    for (int g = 0; g < kOutGroups; ++g) fb[g] = *reinterpret_cast<const u16x8 *>(hr[g] + j0);
 #pragma unroll
     for (int a = 0; a < kOutTiles; ++a) {
       const int o = min(16 * a + (lane & 15), n_out - 1);  // rows past 3 Hq repeat the last
@@ -140,19 +155,23 @@ __global__ __launch_bounds__(256) void gate_out_kernel(GateParams p) {
       u16x8 wf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) wf[e] = bf2h_bits(w[e]);
-      acc[a] = mfma_f16(wf, fb, acc[a]);
+#pragma unroll
+      for (int g = 0; g < kOutGroups; ++g) acc[a][g] = mfma_f16(wf, fb[g], acc[a][g]);
     }
   }
-  // acc[a][i]: output 16a + 4 (lane / 16) + i, token tok0 + lane % 16
-  const int64_t t = tok0 + (lane & 15);
-  if (t >= p.n) return;
+  // acc[a][g][i]: output 16a + 4 (lane / 16) + i, token tok0 + 16g + lane % 16
 #pragma unroll
-  for (int a = 0; a < kOutTiles; ++a)
+  for (int g = 0; g < kOutGroups; ++g) {
+    const int64_t t = tok0 + 16 * g + (lane & 15);
+    if (t >= p.n) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int o = 16 * a + 4 * grp + i;
-      if (o < n_out) p.logits[t * n_out + o] = acc[a][i] + (p.b2 ? p.b2[o] : 0.f);
-    }
+    for (int a = 0; a < kOutTiles; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 16 * a + 4 * grp + i;
+        if (o < n_out) p.logits[t * n_out + o] = acc[a][g][i] + (p.b2 ? p.b2[o] : 0.f);
+      }
+  }
 }
 
 }  // namespace
@@ -160,11 +179,11 @@ __global__ __launch_bounds__(256) void gate_out_kernel(GateParams p) {
 hipError_t launch_gate(const GateParams &p, int layer, hipStream_t st) {
   if (p.n <= 0) return hipSuccess;
   if (layer == 0) {
-    const int64_t n_tt = (p.n + kGT - 1) / kGT;
-    hipLaunchKernelGGL(gate_hidden_kernel, dim3((unsigned)(n_tt * (p.d_hidden / kGT))), dim3(kGThreads), 0, st,
-                       p);
+    const int64_t n_tt = (p.n + kGTok - 1) / kGTok, n_tt8 = (n_tt + 7) / 8 * 8;
+    hipLaunchKernelGGL(gate_hidden_kernel, dim3((unsigned)(n_tt8 * (p.d_hidden / kGH))), dim3(kGThreads), 0, st,
+                       p, (int)n_tt);
   } else {
-    const int64_t n_wg = (p.n + 63) / 64;
+    const int64_t n_wg = (p.n + 4 * 16 * kOutGroups - 1) / (4 * 16 * kOutGroups);
     hipLaunchKernelGGL(gate_out_kernel, dim3((unsigned)n_wg), dim3(256), 0, st, p);
   }
   return hipGetLastError();

@@ -347,6 +347,6 @@ def test_gate_workspace_and_pointer_checks():
 
 
 def test_gate_size_limits():
-    assert gate_ws(gdesc(n=(1 << 30) + 1, dh=128))[0] == binding.NSA_ERR_UNSUPPORTED
+    assert gate_ws(gdesc(n=(1 << 30) + 1, dh=256))[0] == binding.NSA_ERR_UNSUPPORTED
     assert gate_ws(gdesc(n=1 << 27, dh=2048))[0] == binding.NSA_ERR_UNSUPPORTED
     assert gate_ws(gdesc(n=1 << 26, dh=2048))[0] == binding.NSA_OK

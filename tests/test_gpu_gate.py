@@ -58,12 +58,12 @@ def check(g, got, rows, act, label):
 
 CASES = [
     # (n, d_model, d_hidden, Hq, act, bias): ragged token counts against the
-    # 128-token tile and the 16-token wave; 3 Hq = 84 (ragged), 96 (full), 3
+    # 256-token tile and the 64-token wave; 3 Hq = 84 (ragged), 96 (full), 3
     (300, 256, 256, 28, "silu", True),
     (300, 256, 256, 28, "gelu_tanh", True),
     (300, 256, 256, 28, "relu", False),
     (1, 64, 128, 28, "silu", True),
-    (17, 128, 128, 32, "silu", True),
+    (17, 128, 256, 32, "silu", True),
     (129, 192, 384, 1, "gelu_tanh", True),
     (1000, 3584, 1024, 28, "silu", True),
 ]
