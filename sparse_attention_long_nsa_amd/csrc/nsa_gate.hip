@@ -89,18 +89,29 @@ __global__ __launch_bounds__(kGThreads) void gate_hidden_kernel(GateParams p, in
     bare_barrier();  // everyone's have; and slot (s - 1) % kGS is no longer read
     if (s + 2 < n_k) gate_stage(p, hid0, tok0, (s + 2) * kGK, ring + ((s + 2) % kGS) * kStage, wv, lane);
     const uint16_t *cw = ring + (s % kGS) * kStage, *cx = cw + kStageW;
+    // all 24 fragments of the slice are read up front; the reads of the
+    // second half are interleaved with the first half's matrix instructions
+    u16x8 fa[2][4], fb[2][8];
 #pragma unroll
-    for (int ks = 0; ks < kGK / 32; ++ks) {
-      u16x8 fa[4], fb[8];
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) fa[a] = pk_k_frag<kGK>(cw + wh * kGK, a, ks, lane);
+      for (int a = 0; a < 4; ++a) fa[ks][a] = pk_k_frag<kGK>(cw + wh * kGK, a, ks, lane);
 #pragma unroll
-      for (int b = 0; b < 8; ++b) fb[b] = pk_k_frag<kGK>(cx + wt * kGK, b, ks, lane);
+      for (int b = 0; b < 8; ++b) fb[ks][b] = pk_k_frag<kGK>(cx + wt * kGK, b, ks, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = mfma_bf16(fa[a], fb[b], acc[a][b]);
+        for (int b = 0; b < 8; ++b) acc[a][b] = mfma_bf16(fa[ks][a], fb[ks][b], acc[a][b]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // the first half's LDS reads
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read of the second half
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 52, 0);
   }
   // acc[a][b][i]: hidden hid0 + wh + 16a + 4 (lane / 16) + i, token tok0 + wt + 16b + lane % 16
   const int grp = lane >> 4;
