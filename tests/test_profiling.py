@@ -55,6 +55,26 @@ def test_trace_summary_groups(tmp_path):
     assert "44.0 us per decode step" in text
 
 
+def test_trace_summary_gate_group(tmp_path):
+    trace = tmp_path / "trace.csv"
+    _trace(trace, [("nsa::(anonymous namespace)::gate_hidden_kernel(nsa::GateParams, int)", 1064960, 1_450_000),
+                   ("nsa::(anonymous namespace)::gate_out_kernel(nsa::GateParams)", 131584, 220_000),
+                   ("sel_attn_kernel<128, 7, true>", 655360, 11_000_000)])
+    log = tmp_path / "bench.log"
+    line = {"metric": "m", "value": 1.0, "ms_per_step": 20.0, "kernels": {},
+            "gate_prologue": {"ms_per_step": 1.7, "n_tokens": 131584, "d_model": 3584, "d_hidden": 1024,
+                              "kernels": {"gate_hidden": 1.45, "gate_out": 0.22},
+                              "gate_hidden": {"tflops": 665.0}, "gate_out": {"gbs": 1400.0}}}
+    log.write_text(json.dumps(line) + "\n")
+    out = tmp_path / "g.md"
+    prof.trace_summary(str(trace), str(log), prof._layer_grids("qwen_128k_k32_w256"), "t", "cmd", str(out),
+                       group="gate")
+    text = out.read_text()
+    assert "| gate_hidden | 1 | 1.4500 | 1.45 |" in text
+    assert "| gate_out | 1 | 0.2200 | 0.22 |" in text
+    assert "sel_attn" not in text and "1.7 ms per gate prologue" in text
+
+
 def test_counter_summary_utilisation(tmp_path):
     # one sel_attn dispatch of 1 ms: 1,024 SIMDs x 2.4e6 clocks; counters
     # chosen so that vector busy = 50%, matrix busy = 25%, waiting = 40%
