@@ -18,6 +18,9 @@ Each test names the pin it checks:
              a hand-worked example, affinity in the second layer
   P15        several vision runs: vision rows see only the vision tokens in
              position order (equal to the one-run layout), text rows dense causal
+  P18        backward oracle: its forward == the C oracle's output and branch
+             outputs; its gradients == finite differences (gradcheck); the gate
+             gradient == the closed form from the C oracle's branch outputs
 """
 import json
 import math
@@ -463,3 +466,58 @@ def test_p17_logits_are_affine_in_the_second_layer():
     gb = gate_mlp.gate_logits(x, w1, b1, w2b, None, "silu", 2)
     gab = gate_mlp.gate_logits(x, w1, b1, w2a + 2 * w2b, None, "silu", 2)
     np.testing.assert_allclose(gab, ga + 2 * gb, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------- P18
+
+from oracle import backward as bwd  # noqa: E402
+
+
+def _vision_sel(inp):
+    r = oracle.prefill(inp)
+    return r, r["sel"][np.asarray(inp["is_vision"]).astype(bool)]
+
+
+@pytest.mark.parametrize("case", [dict(n_vis=300, before=5, after=7, hq=4, hkv=2, d=16, k=3, w=50),
+                                  dict(n_vis=260, before=0, after=0, hq=6, hkv=3, d=8, k=2, w=70)])
+def test_p18_backward_oracle_forward_equals_the_c_oracle(case):
+    inp = small(**case)
+    r, sel = _vision_sel(inp)
+    t = {n: torch.tensor(np.asarray(inp[n], dtype=np.float64)) for n in ("q", "k", "v", "w_k", "w_v", "gates")}
+    out, (oc, os_, ow) = bwd.forward(t["q"], t["k"], t["v"], t["w_k"], t["w_v"], t["gates"], inp["is_vision"],
+                                     sel, 64, case["w"], 1.0 / math.sqrt(case["d"]), branches=True)
+    np.testing.assert_allclose(out.numpy(), r["out"], rtol=0, atol=1e-12)
+    vis = np.asarray(inp["is_vision"]).astype(bool)
+    for mine, ref in ((oc, r["ocmp"]), (os_, r["osel"]), (ow, r["oswa"])):
+        np.testing.assert_allclose(mine.numpy(), ref[vis], rtol=0, atol=1e-12)
+
+
+def test_p18_gradients_match_finite_differences():
+    # tiny layout: 2 text tokens, 14 vision tokens in blocks of 4 (one partial),
+    # 2 query heads on 1 KV head, d 3; every input is perturbed numerically
+    rng = np.random.default_rng(3)
+    N, hq, hkv, d, B, w = 18, 2, 1, 3, 4, 5
+    isv = np.array([0] + [1] * 9 + [0] + [1] * 5 + [0, 0], dtype=np.uint8)[:N]
+    nv = int(isv.sum())
+    sel = np.full((nv, hkv, 2), -1, dtype=np.int32)
+    for t in range(nv):  # own block plus the earliest complete one, as a fixed choice
+        cur = t // B
+        sel[t, 0, 0] = 0 if cur > 0 else cur
+        sel[t, 0, 1] = cur if cur > 0 else -1
+    args = [torch.tensor(rng.standard_normal(sh), dtype=torch.float64, requires_grad=True)
+            for sh in ((N, hq, d), (N, hkv, d), (N, hkv, d), (d, d), (d, d), (N, hq, 3))]
+    fn = lambda *a: bwd.forward(*a, isv, sel, B, w, 0.7)  # noqa: E731
+    assert torch.autograd.gradcheck(fn, args, eps=1e-6, atol=1e-7, rtol=1e-5)
+
+
+def test_p18_gate_gradient_closed_form():
+    inp = small(n_vis=200, before=3, after=4, hq=4, hkv=2, d=8, k=2, w=40)
+    r, sel = _vision_sel(inp)
+    dout = np.random.default_rng(5).standard_normal(r["out"].shape)
+    g = bwd.gradients(inp, sel, dout)
+    vis = np.asarray(inp["is_vision"]).astype(bool)
+    sig = 1.0 / (1.0 + np.exp(-np.asarray(inp["gates"], np.float64)[vis]))
+    for c, name in enumerate(("ocmp", "osel", "oswa")):
+        ref = (dout[vis] * r[name][vis]).sum(-1) * sig[..., c] * (1 - sig[..., c])
+        np.testing.assert_allclose(g["gates"][vis][..., c], ref, rtol=0, atol=1e-12)
+    assert np.all(g["gates"][~vis] == 0)
