@@ -171,6 +171,30 @@ nsa_status nsa_prefill_dense(const nsa_prefill_desc *desc, const void *q, const 
                              const void *v, float *out, float *lse_out, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* ----------------------------------------------------------------- backward
+ * Gradients of the layer for training (model card, "Training Details"; paper
+ * summary, "Method": the model is trained end to end). The selection of
+ * blocks is discrete and has no gradient: the caller passes the forward's
+ * sel_idx (nsa_prefill's sel_idx_out). Given dout = dL/d(out), writes
+ *   dq [N, Hq, d], dk, dv [N, Hkv, d], dw_cmp_k, dw_cmp_v [d, d],
+ *   dgate [N, Hq, 3] (dL/d gate logit; zero on text rows), all float32,
+ * through the three branches of the vision rows, the text rows' dense
+ * attention and both compression maps. Same descriptor and inputs as
+ * nsa_prefill; supported: bf16, one vision run (text before and/or after),
+ * the head sizes and limits of nsa_prefill; else NSA_ERR_UNSUPPORTED.
+ * Arithmetic is fp32 throughout; dk, dv and the compressed-key gradients are
+ * accumulated with float atomics, so their low bits vary from run to run.
+ *   sel_idx   device [N_v, Hkv, top_k] int32 (may be NULL when N_v = 0)
+ *   dout      device [N, Hq, d] float32
+ *   workspace device, >= nsa_prefill_backward_workspace_size bytes, 256-B aligned */
+nsa_status nsa_prefill_backward_workspace_size(const nsa_prefill_desc *desc, const uint8_t *is_vision,
+                                               size_t *bytes);
+nsa_status nsa_prefill_backward(const nsa_prefill_desc *desc, const void *q, const void *k, const void *v,
+                                const uint8_t *is_vision, const void *w_cmp_k, const void *w_cmp_v,
+                                const float *gate_logits, const int32_t *sel_idx, const float *dout,
+                                float *dq, float *dk, float *dv, float *dw_cmp_k, float *dw_cmp_v,
+                                float *dgate, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------- gate prologue
  * Gate logits from hidden states (VideoNSA paper summary page, "Method";
  * model card, "Model Architecture": a two-layer MLP and a sigmoid give each

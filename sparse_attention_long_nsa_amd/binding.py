@@ -25,6 +25,7 @@ EXPORTED = (
     "nsa_prefill_dense_workspace_size", "nsa_prefill_dense", "nsa_cache_append",
     "nsa_prefill_varlen_workspace_size", "nsa_prefill_varlen",
     "nsa_gate_workspace_size", "nsa_gate_logits",
+    "nsa_prefill_backward_workspace_size", "nsa_prefill_backward",
 )
 NSA_ACTIVATIONS = {"silu": 0, "gelu_tanh": 1, "relu": 2}
 
@@ -101,6 +102,10 @@ def lib() -> ctypes.CDLL:
         L.nsa_prefill_varlen_workspace_size.restype = ctypes.c_int
         L.nsa_prefill_varlen.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_int32] + [P] * 14 + [S, P]
         L.nsa_prefill_varlen.restype = ctypes.c_int
+        L.nsa_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), P, ctypes.POINTER(S)]
+        L.nsa_prefill_backward_workspace_size.restype = ctypes.c_int
+        L.nsa_prefill_backward.argtypes = [ctypes.POINTER(PrefillDesc)] + [P] * 16 + [S, P]
+        L.nsa_prefill_backward.restype = ctypes.c_int
         L.nsa_gate_workspace_size.argtypes = [ctypes.POINTER(GateDesc), ctypes.POINTER(S)]
         L.nsa_gate_workspace_size.restype = ctypes.c_int
         L.nsa_gate_logits.argtypes = [ctypes.POINTER(GateDesc)] + [P] * 7 + [S, P]
@@ -330,6 +335,43 @@ def prefill_dense(q, k, v, scale=0.0, out=None, want_lse=False, workspace=None, 
     if st != NSA_OK:
         raise NsaError(st, "nsa_prefill_dense")
     res["workspace"] = workspace
+    return res
+
+
+def prefill_backward(q, k, v, is_vision, w_cmp_k, w_cmp_v, gate_logits, sel_idx, dout, top_k, window,
+                     block=64, scale=0.0, stream=None) -> dict:
+    """Runs nsa_prefill_backward: gradients (fp32, on the device) of the layer
+    for the output gradient dout [N,Hq,d], reusing the forward's selection
+    sel_idx [N_v,Hkv,top_k]. Returns dq, dk, dv, dw_cmp_k, dw_cmp_v, dgate."""
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    for name, t, shape in (("q", q, (n, hq, d)), ("k", k, (n, hkv, d)), ("v", v, (n, hkv, d)),
+                           ("w_cmp_k", w_cmp_k, (d, d)), ("w_cmp_v", w_cmp_v, (d, d))):
+        _check_dev(name, t, torch.bfloat16, shape)
+    _check_dev("gate_logits", gate_logits, torch.float32, (n, hq, 3))
+    _check_dev("dout", dout, torch.float32, (n, hq, d))
+    mask = _mask_host(is_vision)
+    nv = int(mask.sum())
+    if nv > 0:
+        _check_dev("sel_idx", sel_idx, torch.int32, (nv, hkv, top_k))
+    desc = prefill_desc(q, k, top_k, window, block, scale)
+    nb = ctypes.c_size_t(0)
+    st = lib().nsa_prefill_backward_workspace_size(ctypes.byref(desc), _ptr(mask), ctypes.byref(nb))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_prefill_backward_workspace_size")
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    res = {"dq": torch.empty((n, hq, d), **f32), "dk": torch.empty((n, hkv, d), **f32),
+           "dv": torch.empty((n, hkv, d), **f32), "dw_cmp_k": torch.empty((d, d), **f32),
+           "dw_cmp_v": torch.empty((d, d), **f32), "dgate": torch.empty((n, hq, 3), **f32)}
+    ws = torch.empty(max(nb.value, 256), dtype=torch.uint8, device=dev)
+    st = lib().nsa_prefill_backward(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(w_cmp_k), _ptr(w_cmp_v),
+        _ptr(gate_logits), _ptr(sel_idx if nv > 0 else None), _ptr(dout), _ptr(res["dq"]), _ptr(res["dk"]),
+        _ptr(res["dv"]), _ptr(res["dw_cmp_k"]), _ptr(res["dw_cmp_v"]), _ptr(res["dgate"]), _ptr(ws),
+        ws.numel(), _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_prefill_backward")
     return res
 
 

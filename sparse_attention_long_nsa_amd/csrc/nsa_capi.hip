@@ -433,6 +433,59 @@ nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim, int32
   return NSA_OK;
 }
 
+static nsa_status plan_backward(const nsa_prefill_desc *ds, const uint8_t *is_vision, PrefillPlan &pl,
+                                size_t *bytes) {
+  const nsa_status st = plan_prefill(ds, is_vision, pl);
+  if (st != NSA_OK) return st;
+  if (pl.fp32 || pl.mapped) return NSA_ERR_UNSUPPORTED;  // bf16, one vision run
+  const size_t one = align_up(sizeof(float) * (size_t)pl.n_blk * pl.hkv * pl.d);
+  *bytes = 6 * one + kAlign;
+  return NSA_OK;
+}
+
+nsa_status nsa_prefill_backward_workspace_size(const nsa_prefill_desc *desc, const uint8_t *is_vision,
+                                               size_t *bytes) {
+  if (!bytes) return NSA_ERR_INVALID_ARG;
+  PrefillPlan pl;
+  size_t need = 0;
+  const nsa_status st = plan_backward(desc, is_vision, pl, &need);
+  if (st != NSA_OK) return st;
+  *bytes = need;
+  return NSA_OK;
+}
+
+nsa_status nsa_prefill_backward(const nsa_prefill_desc *desc, const void *q, const void *k, const void *v,
+                                const uint8_t *is_vision, const void *w_cmp_k, const void *w_cmp_v,
+                                const float *gate_logits, const int32_t *sel_idx, const float *dout,
+                                float *dq, float *dk, float *dv, float *dw_cmp_k, float *dw_cmp_v,
+                                float *dgate, void *workspace, size_t workspace_bytes, void *stream) {
+  PrefillPlan pl;
+  size_t need = 0;
+  const nsa_status st = plan_backward(desc, is_vision, pl, &need);
+  if (st != NSA_OK) return st;
+  const void *req[] = {q, k, v, w_cmp_k, w_cmp_v, gate_logits, dout, dq, dk, dv, dw_cmp_k, dw_cmp_v, dgate};
+  for (const void *p : req)
+    if (!p || !aligned16(p)) return NSA_ERR_INVALID_ARG;
+  if (pl.n_vis > 0 && (!sel_idx || !aligned16(sel_idx))) return NSA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < need) return NSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return NSA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t one = align_up(sizeof(float) * (size_t)pl.n_blk * pl.hkv * pl.d);
+  float *ws = static_cast<float *>(workspace);
+  auto slot = [&](int i) { return reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + i * one); };
+  BwdParams bp{static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+               static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(w_cmp_k),
+               static_cast<const uint16_t *>(w_cmp_v), gate_logits, dout, sel_idx, dq, dk, dv, dgate,
+               dw_cmp_k, dw_cmp_v, slot(0), slot(1), slot(2), slot(3), slot(4), slot(5),
+               pl.N, pl.v0, pl.n_vis, pl.hq, pl.hkv, pl.k, pl.w, pl.n_blk, pl.scale};
+  hipError_t e = hipSuccess;
+  NSA_LAUNCH("bwd_zero", launch_backward(bp, pl.d, 0, s));
+  NSA_LAUNCH("bwd_pool", launch_backward(bp, pl.d, 1, s));
+  NSA_LAUNCH("bwd_rows", launch_backward(bp, pl.d, 2, s));
+  NSA_LAUNCH("bwd_cmp_w", launch_backward(bp, pl.d, 3, s));
+  return NSA_OK;
+}
+
 static nsa_status plan_gate(const nsa_gate_desc *ds, size_t *bytes) {
   if (!ds) return NSA_ERR_INVALID_ARG;
   if (ds->n_tokens < 1 || ds->d_model < 1 || ds->d_hidden < 1 || ds->n_q_heads < 1) return NSA_ERR_INVALID_ARG;

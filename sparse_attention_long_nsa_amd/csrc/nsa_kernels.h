@@ -114,6 +114,17 @@ struct GateParams {
   int d_model, d_hidden, hq, act;  // act: 0 SiLU, 1 GELU (tanh form), 2 ReLU
 };
 
+struct BwdParams {
+  const uint16_t *q, *k, *v, *wk, *wv;  // bf16: [N,Hq,d], [N,Hkv,d] x2, [d,d] x2
+  const float *gates, *dout;            // [N,Hq,3], [N,Hq,d]
+  const int32_t *sel;                   // [N_v,Hkv,k] selected blocks of the forward
+  float *dq, *dk, *dv, *dgate, *dwk, *dwv;
+  float *kc, *vc, *kbar, *vbar, *dkc, *dvc;  // workspace [n_blk,Hkv,d] each
+  int64_t n, v0, n_vis;
+  int hq, hkv, topk, window, n_blk;
+  float scale;
+};
+
 // One slice of the token-kind mask, as kernel arguments: bit j of word i
 // says whether position base + 32 i + j is a vision token.
 constexpr int kMaskWords = 512;
@@ -180,6 +191,8 @@ hipError_t launch_text_merge(const TextParams &p, int d, hipStream_t st);
 hipError_t launch_dense_attn(const DenseParams &p, int d, int G, bool f16, hipStream_t st);
 // layer 0: hidden layer into p.h; layer 1: logits from p.h
 hipError_t launch_gate(const GateParams &p, int layer, hipStream_t st);
+// stage 0: clear accumulators; 1: pooling; 2: per-row gradients; 3: compression maps
+hipError_t launch_backward(const BwdParams &p, int d, int stage, hipStream_t st);
 hipError_t launch_decode(const DecodeParams &p, int d, int G, hipStream_t st);
 
 // Which (head_dim, query heads per KV head) pairs have kernels.

@@ -224,6 +224,13 @@ def make_gate_inputs(n: int, d_model: int, d_hidden: int, n_q_heads: int, seed: 
     return dict(x=x, w1=w1, w2=w2, b1=b1 if bias else None, b2=b2 if bias else None, n_q_heads=n_q_heads)
 
 
+def make_output_grad(shape, seed: int = 0) -> np.ndarray:
+    """A seeded upstream gradient dL/d(out) for the backward pass: i.i.d.
+    N(0, 1) float32 of the given shape."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _normal(rng, tuple(shape))
+
+
 def make_decode_inputs(shape: DecodeShape, seed: int = 0) -> dict:
     """Draw one decode workload: per sequence a frame-correlated vision K/V
     cache [Bt,L,Hkv,d]; the query is the last cache token, so it is drawn from

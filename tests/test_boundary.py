@@ -350,3 +350,39 @@ def test_gate_size_limits():
     assert gate_ws(gdesc(n=(1 << 30) + 1, dh=256))[0] == binding.NSA_ERR_UNSUPPORTED
     assert gate_ws(gdesc(n=1 << 27, dh=2048))[0] == binding.NSA_ERR_UNSUPPORTED
     assert gate_ws(gdesc(n=1 << 26, dh=2048))[0] == binding.NSA_OK
+
+
+def bwd_ws(ds, mask):
+    n = ctypes.c_size_t(0)
+    st = binding.lib().nsa_prefill_backward_workspace_size(ctypes.byref(ds), mask.ctypes.data_as(ctypes.c_void_p),
+                                                          ctypes.byref(n))
+    return st, n.value
+
+
+def call_bwd(ds, mask, ptrs=None, ws=FAKE, ws_bytes=1 << 40):
+    names = ("q", "k", "v", "wk", "wv", "g", "sel", "dout", "dq", "dk", "dv", "dwk", "dwv", "dg")
+    p = {n: FAKE for n in names}
+    if ptrs:
+        p.update(ptrs)
+    return binding.lib().nsa_prefill_backward(
+        ctypes.byref(ds), p["q"], p["k"], p["v"], mask.ctypes.data_as(ctypes.c_void_p), p["wk"], p["wv"], p["g"],
+        p["sel"], p["dout"], p["dq"], p["dk"], p["dv"], p["dwk"], p["dwv"], p["dg"], ws, ws_bytes, None)
+
+
+def test_backward_validation_and_workspace():
+    m = vision_mask(1024 + 64, 32, 1024 + 32)
+    st, need = bwd_ws(desc(n=len(m)), m)
+    # fp32 compressed keys, values, their means and their gradients: 6 x 16 blocks x 4 groups x 128
+    assert st == binding.NSA_OK and need == 6 * 16 * 4 * 128 * 4 + 256
+    assert bwd_ws(desc(n=len(m), dtype=1), m)[0] == binding.NSA_ERR_UNSUPPORTED
+    two_runs = vision_mask(len(m), 0, 500) | vision_mask(len(m), 600, 1000)
+    assert bwd_ws(desc(n=len(m)), two_runs)[0] == binding.NSA_ERR_UNSUPPORTED
+    assert bwd_ws(desc(n=len(m), k=0), m)[0] == binding.NSA_ERR_INVALID_ARG
+    ds = desc(n=len(m))
+    for name in ("q", "k", "v", "wk", "wv", "g", "sel", "dout", "dq", "dk", "dv", "dwk", "dwv", "dg"):
+        assert call_bwd(ds, m, {name: None}) == binding.NSA_ERR_INVALID_ARG, name
+    assert call_bwd(ds, m, {"dq": FAKE + 4}) == binding.NSA_ERR_INVALID_ARG
+    assert call_bwd(ds, m, ws=None) == binding.NSA_ERR_WORKSPACE
+    assert call_bwd(ds, m, ws_bytes=need - 1) == binding.NSA_ERR_WORKSPACE
+    text_only = np.zeros(64, np.uint8)  # no vision rows: no selection needed
+    assert bwd_ws(desc(n=64), text_only)[0] == binding.NSA_OK
