@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "NSA attention tokens/s/layer at 128K vision tokens; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector peak
 SWEEP = ((8, 1024), (16, 512))  # fixed-budget trade of blocks against window
 
 
@@ -252,6 +253,63 @@ def run_gate_bench(shape, steps, warmup):
     return res
 
 
+BWD_SHAPE = dict(n_vis=4096, n_text_after=512)  # the first backward design is timed on a shorter context
+
+
+def run_backward_bench(shape, steps, warmup):
+    """Backward pass (training) of the layer on 4,096 vision + 512 text
+    tokens with the headline's heads, k and w, reusing the forward's
+    selection; reports time per call and the rate of algorithmic flops."""
+    import torch
+    from sparse_attention_long_nsa_amd import binding
+    from sparse_attention_long_nsa_amd.inputs import make_output_grad, make_prefill_inputs
+    s = shape.replace(n_vis=BWD_SHAPE["n_vis"], n_text_before=0, n_text_after=BWD_SHAPE["n_text_after"])
+    inp = make_prefill_inputs(s, seed=0)
+    dev = {k: torch.from_numpy(inp[k]).to("cuda:0").to(torch.bfloat16).contiguous()
+           for k in ("q", "k", "v", "w_k", "w_v")}
+    gates = torch.from_numpy(inp["gates"]).to("cuda:0")
+    fwd = binding.prefill(dev["q"], dev["k"], dev["v"], inp["is_vision"], dev["w_k"], dev["w_v"], gates,
+                          s.top_k, s.window, want_sel=True)
+    vis = np.asarray(inp["is_vision"]).astype(bool)
+    sel = fwd["sel_idx"]  # [N_v, Hkv, k]: the forward's choice is reused
+    dout = torch.from_numpy(make_output_grad((s.n_tokens, s.n_q_heads, s.head_dim), seed=1)).to("cuda:0")
+
+    def call():
+        return binding.prefill_backward(dev["q"], dev["k"], dev["v"], inp["is_vision"], dev["w_k"], dev["w_v"],
+                                        gates, sel, dout, s.top_k, s.window)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    binding.timing_reset()
+    binding.timing_enable(True)
+    call()
+    torch.cuda.synchronize()
+    kern = {k: round(tot / cnt, 4) for k, (tot, cnt) in binding.timing_read().items()}
+    binding.timing_enable(False)
+    binding.timing_reset()
+    # algorithmic flops: per attended (query, head, key) pair the backward
+    # recomputes nothing in principle and does dV, dP, dQ, dK: 4 products of
+    # 2 d flops each (the forward's two are not counted)
+    text_pos = np.nonzero(~vis)[0]
+    work = closed_form_work(s, text_pos)
+    fwd_flops = sum(v for kind, v in work.values() if kind == "flops")
+    flops = 2.0 * fwd_flops
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"ms_per_step": round(ms, 3), "n_vision": s.n_vis, "n_text": s.n_text, "top_k": s.top_k,
+           "window": s.window, "algorithmic_tflop": round(flops / 1e12, 4), "tflops": round(tf, 2),
+           "frac_of_fp32_vector_peak": round(tf / PEAK_FP32_TFLOPS, 4), "kernels": kern, "steps": steps}
+    log(f"backward: {res}")
+    return res
+
+
 def run_scaling_bench(shape, steps, warmup):
     """Step time against context length at the workload's k and w: 16K to
     512K vision tokens (the largest the kernels take) plus its text tokens."""
@@ -423,6 +481,7 @@ def main():
     ap.add_argument("--no-spans", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-gate", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--scaling", action="store_true",
                     help="also time 16K..512K vision tokens (about a minute more, mostly input generation)")
     args = ap.parse_args()
@@ -504,6 +563,10 @@ def main():
     if not args.no_gate:
         gate = run_gate_bench(shape, max(3, args.steps // 2), 1)
 
+    backward = None
+    if not args.no_backward:
+        backward = run_backward_bench(shape, 3, 1)
+
     spans = None
     if not args.no_spans:
         spans = run_spans_bench(inp, shape, max(3, args.steps // 2), 1, ms)
@@ -552,6 +615,7 @@ def main():
         "several_vision_runs": spans,
         "dense_mode": dense,
         "gate_prologue": gate,
+        "backward": backward,
         "context_scaling": scaling,
         "cpu_baseline": cpu,
     }

@@ -53,10 +53,16 @@ KERNELS = [
     ("mfma_loop_kernel", "mfma_probe", "sparse_attention_long_nsa_amd/csrc/nsa_probe.hip"),
     ("gate_hidden_kernel", "gate_hidden", "sparse_attention_long_nsa_amd/csrc/nsa_gate.hip"),
     ("gate_out_kernel", "gate_out", "sparse_attention_long_nsa_amd/csrc/nsa_gate.hip"),
+    ("bwd_zero_kernel", "bwd_zero", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_pool_kernel", "bwd_pool", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_rows_kernel", "bwd_rows", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_cmp_w_kernel", "bwd_cmp_w", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_cmp_tok_kernel", "bwd_cmp_tok", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
 ]
 DECODE_KERNELS = ("dec_item_cmp_win", "dec_item_sel", "dec_select", "dec_combine")
 DENSE_KERNELS = ("pack_dense", "dense_attn")
 GATE_KERNELS = ("gate_hidden", "gate_out")
+BWD_KERNELS = ("bwd_zero", "bwd_pool", "bwd_rows", "bwd_cmp_w", "bwd_cmp_tok")
 PREFILL_KERNELS = ("sel_attn", "cmp_attn", "swa_attn", "text_attn", "text_merge", "blk_score_topk", "cmp_pool",
                    "cmp_pool_mean", "cmp_pool_map", "pack_kv", "pack_cmp", "pack_text")
 
@@ -114,7 +120,8 @@ def source_digest(path: str) -> str:
 
 def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, command: str,
                   out_md: str, group: str = "prefill") -> None:
-    keep = {"decode": DECODE_KERNELS, "dense": DENSE_KERNELS, "gate": GATE_KERNELS}.get(group, PREFILL_KERNELS)
+    keep = {"decode": DECODE_KERNELS, "dense": DENSE_KERNELS, "gate": GATE_KERNELS,
+            "backward": BWD_KERNELS}.get(group, PREFILL_KERNELS)
     dur = defaultdict(list)
     for r in csv.DictReader(open(trace_csv)):
         name, _ = short_name(r["Kernel_Name"], _grid(r), grid_names)
@@ -126,6 +133,8 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
         kern = {k: {"avg_ms": round(v["avg_us"] * 1e-3, 4)} for k, v in dec.get("kernels", {}).items()}
     elif group == "dense":
         kern = ((bench or {}).get("dense_mode") or {}).get("kernels", {})
+    elif group == "backward":
+        kern = {k: {"avg_ms": v} for k, v in ((bench or {}).get("backward") or {}).get("kernels", {}).items()}
     elif group == "gate":
         kern = {k: {"avg_ms": v} for k, v in ((bench or {}).get("gate_prologue") or {}).get("kernels", {}).items()}
     else:
@@ -146,6 +155,12 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
         lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per dense step "
                   f"({d['tflops']} TF/s of algorithmic flops, {d['mfma_peak_frac'] * 100:.1f}% of the bf16 "
                   "peak); its event-timed per-kernel averages are listed beside the profiler's.", ""]
+    elif bench and group == "backward" and bench.get("backward"):
+        d = bench["backward"]
+        lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per backward call over "
+                  f"{d['n_vision']} vision + {d['n_text']} text tokens (k {d['top_k']}, w {d['window']}): "
+                  f"{d['tflops']} TF/s of algorithmic flops; its event-timed per-kernel averages are "
+                  "listed beside the profiler's.", ""]
     elif bench and group == "gate" and bench.get("gate_prologue"):
         d = bench["gate_prologue"]
         lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per gate prologue over "
@@ -340,7 +355,7 @@ def main(argv=None) -> None:
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
-    t.add_argument("--group", choices=("prefill", "decode", "dense", "gate"), default="prefill")
+    t.add_argument("--group", choices=("prefill", "decode", "dense", "gate", "backward"), default="prefill")
     m = sub.add_parser("pmc-summary")
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
         m.add_argument(f"--{k}-csv", required=True)
