@@ -8,12 +8,13 @@
 // A first, plain design in fp32 on the vector units (no matrix cores):
 //   bwd_zero   clears the accumulated gradients
 //   bwd_pool   block means and compressed keys/values, fp32
-//   bwd_rows   one wave per (row, query head); per branch three passes over
-//              its keys, lane = key for dot products and lane = dimension for
-//              sums over keys: (1) max and sum of the exponentials, (2)
-//              output o and D = dO . o (and the gate gradient), (3)
-//              dS = P (dP - D): dq in registers, dk / dv (or the compressed
-//              dK / dV) accumulated with float atomics
+//   bwd_rows   one wave per (row, KV group) with all its query heads; per
+//              branch three passes over its keys, lane = key for dot
+//              products and lane = dimension for sums over keys: (1) max
+//              and sum of the exponentials, (2) output o and D = dO . o (and
+//              the gate gradient), (3) dS = P (dP - D): dq in registers,
+//              dk / dv (or the compressed dK / dV) summed over the heads and
+//              accumulated with float atomics
 //   bwd_cmp_w  dW = sum over blocks of dK_cmp x mean^T, and each block's
 //              W^T dK_cmp / 64 added to its 64 tokens' dk (dv likewise)
 #include "nsa_kernels.h"
@@ -22,8 +23,6 @@
 namespace nsa {
 
 namespace {
-
-constexpr int kBwdWaves = 4;
 
 __device__ __forceinline__ float wsum(float v) {
 #pragma unroll
@@ -83,17 +82,12 @@ struct KeySet {
 };
 
 // Token row of key i of a selected-block set (vision keys j <= t of the
-// selected blocks, in block order): walks the block list.
+// selected blocks, in block order). The blocks come in ascending order,
+// -1 padded: every one but the last is a complete earlier block of 64 keys,
+// and the last is the query's own block, cut at t; so key i is key i % 64
+// of entry i / 64.
 __device__ __forceinline__ int64_t sel_row(const BwdParams &p, const KeySet &ks, int i) {
-  for (int e = 0; e < ks.nsel; ++e) {
-    const int b = ks.blocks[e];
-    if (b < 0) continue;
-    const int len = min(kBlk, ks.t - b * kBlk + 1);
-    if (len <= 0) continue;
-    if (i < len) return p.v0 + (int64_t)b * kBlk + i;
-    i -= len;
-  }
-  return -1;
+  return p.v0 + (int64_t)ks.blocks[i / kBlk] * kBlk + (i % kBlk);
 }
 
 template <int D>
@@ -103,6 +97,20 @@ struct KeyRef {
   float *dk = nullptr, *dv = nullptr;
   __device__ __forceinline__ float k(int j) const { return kb ? bfbits2f(kb[j]) : kf[j]; }
   __device__ __forceinline__ float v(int j) const { return vb ? bfbits2f(vb[j]) : vf[j]; }
+  // eight consecutive values from j (a multiple of 8) in one or two loads
+  __device__ __forceinline__ static void load8(const uint16_t *b16, const float *f32, int j, float (&x)[8]) {
+    if (b16) {
+      const u16x8 u = *reinterpret_cast<const u16x8 *>(b16 + j);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bfbits2f(u[e]);
+    } else {
+      const float4 a = *reinterpret_cast<const float4 *>(f32 + j), c = *reinterpret_cast<const float4 *>(f32 + j + 4);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+    }
+  }
+  __device__ __forceinline__ void k8(int j, float (&x)[8]) const { load8(kb, kf, j, x); }
+  __device__ __forceinline__ void v8(int j, float (&x)[8]) const { load8(vb, vf, j, x); }
 };
 
 template <int D>
@@ -125,155 +133,237 @@ __device__ __forceinline__ KeyRef<D> key_ref(const BwdParams &p, const KeySet &k
   return r;
 }
 
-// One branch for one (row, head) held by one wave. q and dO (already scaled
-// by the branch's gate) sit in LDS (qs, dos); lane owns dims lane + 64 e.
-// Returns the branch output's dot with the raw output gradient (for the gate
-// gradient) and adds the branch's dq into dq_acc.
-template <int D>
-__device__ float branch_bwd(const BwdParams &p, const KeySet &ks, int g, const float *qs, const float *dos,
-                            const float *dout_s, float *pb, float *db, float (&dq_acc)[D / 64], int lane) {
+// One branch for one (row, KV group) held by one wave, all G query heads of
+// the group together so that every key row is read once for the group and
+// its gradients are summed over the heads before the atomics. q, dO (scaled
+// by each head's gate) and the raw output gradient sit in LDS; for sums over
+// keys lane l owns dims l + 64 e. Adds the branch's dq into dq and returns,
+// per head, the branch output's dot with the raw output gradient (go).
+template <int D, int G>
+__device__ void branch_bwd(const BwdParams &p, const KeySet &ks, int g, const float (*qs)[D],
+                           const float (*dos)[D], const float (*douts)[D], float (*pb)[64], float (*db)[64],
+                           float (&dq)[G][D / 64], float (&go)[G], int lane) {
   constexpr int E = D / 64;
-  if (ks.n <= 0) return 0.f;
-  // (1) max and sum of exp over the keys
-  float m = -INFINITY, l = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) go[h] = 0.f;
+  if (ks.n <= 0) return;
+  // (1) per head: max and sum of exp over the keys
+  float m[G], l[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
   for (int c0 = 0; c0 < ks.n; c0 += 64) {
     const int i = c0 + lane;
-    float s = -INFINITY;
+    float sc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc[h] = -INFINITY;
     if (i < ks.n) {
       const KeyRef<D> kr = key_ref<D>(p, ks, i, g);
-      float a = 0.f;
-      for (int j = 0; j < D; ++j) a = fmaf(qs[j], kr.k(j), a);
-      s = a * p.scale;
-    }
-    const float mc = wmax(s);
-    const float mn = fmaxf(m, mc);
-    l = l * expf(m - mn) + wsum(i < ks.n ? expf(s - mn) : 0.f);
-    m = mn;
-  }
-  const float lse = m + logf(l);
-  // (2) o = sum p v; lane owns dims lane + 64 e
-  float o[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  for (int c0 = 0; c0 < ks.n; c0 += 64) {
-    const int i = c0 + lane;
-    float pi = 0.f;
-    if (i < ks.n) {
-      const KeyRef<D> kr = key_ref<D>(p, ks, i, g);
-      float a = 0.f;
-      for (int j = 0; j < D; ++j) a = fmaf(qs[j], kr.k(j), a);
-      pi = expf(a * p.scale - lse);
-    }
-    pb[lane] = pi;
-    wave_lds_sync();
-    const int nc = min(64, ks.n - c0);
-    for (int ii = 0; ii < nc; ++ii) {
-      const KeyRef<D> kr = key_ref<D>(p, ks, c0 + ii, g);
+      for (int h = 0; h < G; ++h) sc[h] = 0.f;
+      for (int j0 = 0; j0 < D; j0 += 8) {
+        float kv[8];
+        kr.k8(j0, kv);
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = fmaf(pb[ii], kr.v(lane + 64 * e), o[e]);
-    }
-    wave_lds_sync();
-  }
-  float dd = 0.f, go = 0.f;
+        for (int jj = 0; jj < 8; ++jj)
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    dd = fmaf(dos[lane + 64 * e], o[e], dd);
-    go = fmaf(dout_s[lane + 64 * e], o[e], go);
-  }
-  dd = wsum(dd);  // D = dO . o
-  go = wsum(go);
-  // (3) dS = P (dP - D); dq += scale dS k; dk += scale dS q; dv += P dO
-  for (int c0 = 0; c0 < ks.n; c0 += 64) {
-    const int i = c0 + lane;
-    float pi = 0.f, dsi = 0.f;
-    if (i < ks.n) {
-      const KeyRef<D> kr = key_ref<D>(p, ks, i, g);
-      float a = 0.f, dp = 0.f;
-      for (int j = 0; j < D; ++j) {
-        a = fmaf(qs[j], kr.k(j), a);
-        dp = fmaf(dos[j], kr.v(j), dp);
+          for (int h = 0; h < G; ++h) sc[h] = fmaf(qs[h][j0 + jj], kv[jj], sc[h]);
       }
-      pi = expf(a * p.scale - lse);
-      dsi = pi * (dp - dd);
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] *= p.scale;
     }
-    pb[lane] = pi;
-    db[lane] = dsi;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(m[h], wmax(sc[h]));
+      l[h] = l[h] * expf(m[h] - mn) + wsum(i < ks.n ? expf(sc[h] - mn) : 0.f);
+      m[h] = mn;
+    }
+  }
+  float lse[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) lse[h] = m[h] + logf(l[h]);
+  // (2) o = sum p v per head, then D = dO . o and go = dout . o
+  float o[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+  for (int c0 = 0; c0 < ks.n; c0 += 64) {
+    const int i = c0 + lane;
+    float sc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc[h] = 0.f;
+    if (i < ks.n) {
+      const KeyRef<D> kr = key_ref<D>(p, ks, i, g);
+      for (int j0 = 0; j0 < D; j0 += 8) {
+        float kv[8];
+        kr.k8(j0, kv);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+          for (int h = 0; h < G; ++h) sc[h] = fmaf(qs[h][j0 + jj], kv[jj], sc[h]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = expf(sc[h] * p.scale - lse[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) pb[h][lane] = sc[h];
     wave_lds_sync();
     const int nc = min(64, ks.n - c0);
     for (int ii = 0; ii < nc; ++ii) {
       const KeyRef<D> kr = key_ref<D>(p, ks, c0 + ii, g);
-      const float ds = db[ii] * p.scale, pw = pb[ii];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float vv = kr.v(lane + 64 * e);
+#pragma unroll
+        for (int h = 0; h < G; ++h) o[h][e] = fmaf(pb[h][ii], vv, o[h][e]);
+      }
+    }
+    wave_lds_sync();
+  }
+  float dd[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      a = fmaf(dos[h][lane + 64 * e], o[h][e], a);
+      b = fmaf(douts[h][lane + 64 * e], o[h][e], b);
+    }
+    dd[h] = wsum(a);
+    go[h] = wsum(b);
+  }
+  // (3) dS = P (dP - D); dq += scale dS k; dk += scale sum_h dS q; dv += sum_h P dO
+  for (int c0 = 0; c0 < ks.n; c0 += 64) {
+    const int i = c0 + lane;
+    float pr[G], dsr[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) { pr[h] = 0.f; dsr[h] = 0.f; }
+    if (i < ks.n) {
+      const KeyRef<D> kr = key_ref<D>(p, ks, i, g);
+      float sc[G], dp[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) { sc[h] = 0.f; dp[h] = 0.f; }
+      for (int j0 = 0; j0 < D; j0 += 8) {
+        float kv[8], vv[8];
+        kr.k8(j0, kv);
+        kr.v8(j0, vv);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            sc[h] = fmaf(qs[h][j0 + jj], kv[jj], sc[h]);
+            dp[h] = fmaf(dos[h][j0 + jj], vv[jj], dp[h]);
+          }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        pr[h] = expf(sc[h] * p.scale - lse[h]);
+        dsr[h] = pr[h] * (dp[h] - dd[h]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      pb[h][lane] = pr[h];
+      db[h][lane] = dsr[h];
+    }
+    wave_lds_sync();
+    const int nc = min(64, ks.n - c0);
+    for (int ii = 0; ii < nc; ++ii) {
+      const KeyRef<D> kr = key_ref<D>(p, ks, c0 + ii, g);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int j = lane + 64 * e;
-        dq_acc[e] = fmaf(ds, kr.k(j), dq_acc[e]);
-        unsafeAtomicAdd(kr.dk + j, ds * qs[j]);
-        unsafeAtomicAdd(kr.dv + j, pw * dos[j]);
+        const float kv = kr.k(j);
+        float gk = 0.f, gv = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ds = db[h][ii] * p.scale;
+          dq[h][e] = fmaf(ds, kv, dq[h][e]);
+          gk = fmaf(ds, qs[h][j], gk);
+          gv = fmaf(pb[h][ii], dos[h][j], gv);
+        }
+        unsafeAtomicAdd(kr.dk + j, gk);
+        unsafeAtomicAdd(kr.dv + j, gv);
       }
     }
     wave_lds_sync();
   }
-  return go;
 }
 
-template <int D>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_kernel(BwdParams p) {
+constexpr int kBwdWavesG = 2;  // (row, group) items per workgroup
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kBwdWavesG) void bwd_rows_kernel(BwdParams p) {
   constexpr int E = D / 64;
-  __shared__ float qs_[kBwdWaves][D], dos_[kBwdWaves][D], dout_[kBwdWaves][D];
-  __shared__ float pb_[kBwdWaves][64], db_[kBwdWaves][64];
+  __shared__ float qs_[kBwdWavesG][G][D], dos_[kBwdWavesG][G][D], dout_[kBwdWavesG][G][D];
+  __shared__ float pb_[kBwdWavesG][G][64], db_[kBwdWavesG][G][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t item = (int64_t)blockIdx.x * kBwdWaves + wv;
-  if (item >= p.n * p.hq) return;
-  const int64_t row = item / p.hq;
-  const int h = (int)(item % p.hq), g = h / (p.hq / p.hkv);
-  float *qs = qs_[wv], *dos = dos_[wv], *douts = dout_[wv], *pb = pb_[wv], *db = db_[wv];
-  const int64_t oq = (row * p.hq + h) * D;
+  const int64_t item = (int64_t)blockIdx.x * kBwdWavesG + wv;
+  if (item >= p.n * p.hkv) return;
+  const int64_t row = item / p.hkv;
+  const int g = (int)(item % p.hkv);
+  float(*qs)[D] = qs_[wv];
+  float(*dos)[D] = dos_[wv];
+  float(*douts)[D] = dout_[wv];
+  const int64_t oq = (row * p.hq + (int64_t)g * G) * D;  // the group's first head
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    qs[lane + 64 * e] = bfbits2f(p.q[oq + lane + 64 * e]);
-    douts[lane + 64 * e] = p.dout[oq + lane + 64 * e];
-  }
-  float dq[E];
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-  for (int e = 0; e < E; ++e) dq[e] = 0.f;
+    for (int e = 0; e < E; ++e) {
+      qs[h][lane + 64 * e] = bfbits2f(p.q[oq + h * D + lane + 64 * e]);
+      douts[h][lane + 64 * e] = p.dout[oq + h * D + lane + 64 * e];
+    }
+  float dq[G][E], go[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) dq[h][e] = 0.f;
   const bool vis = row >= p.v0 && row < p.v0 + p.n_vis;
-  float *dg = p.dgate + (row * p.hq + h) * 3;
+  float *dg = p.dgate + (row * p.hq + (int64_t)g * G) * 3;
   if (!vis) {  // text row: dense causal over every earlier position
 #pragma unroll
-    for (int e = 0; e < E; ++e) dos[lane + 64 * e] = douts[lane + 64 * e];
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) dos[h][lane + 64 * e] = douts[h][lane + 64 * e];
     wave_lds_sync();
     KeySet ks{1, (int)(row + 1), 0, nullptr, 0, 0};
-    branch_bwd<D>(p, ks, g, qs, dos, douts, pb, db, dq, lane);
-    if (lane < 3) dg[lane] = 0.f;
+    branch_bwd<D, G>(p, ks, g, qs, dos, douts, pb_[wv], db_[wv], dq, go, lane);
+    if (lane < 3 * G) dg[lane] = 0.f;
   } else {
     const int t = (int)(row - p.v0);
-    const float *gl = p.gates + (row * p.hq + h) * 3;
-    const KeySet sets[3] = {
-        KeySet{0, (t + 1) / kBlk, 0, nullptr, 0, 0},
-        KeySet{2, 0, 0, p.sel + ((int64_t)t * p.hkv + g) * p.topk, p.topk, t},
-        KeySet{1, min(p.window, t + 1), p.v0 + t - min(p.window, t + 1) + 1, nullptr, 0, 0}};
+    const float *gl = p.gates + (row * p.hq + (int64_t)g * G) * 3;
+    const int32_t *blocks = p.sel + ((int64_t)t * p.hkv + g) * p.topk;
+    int n_sel = 0;
+    for (int e = 0; e < p.topk; ++e) {
+      const int b = blocks[e];
+      if (b >= 0) n_sel += max(0, min(kBlk, t - b * kBlk + 1));
+    }
+    const int nw = min(p.window, t + 1);
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
-      KeySet ks = sets[c];
-      if (c == 1) {  // keys of the selected blocks up to t
-        int n = 0;
-        for (int e = 0; e < ks.nsel; ++e) {
-          const int b = ks.blocks[e];
-          if (b >= 0) n += max(0, min(kBlk, t - b * kBlk + 1));
-        }
-        ks.n = n;
-      }
-      const float sg = 1.f / (1.f + expf(-gl[c]));
+      const KeySet ks = c == 0 ? KeySet{0, (t + 1) / kBlk, 0, nullptr, 0, 0}
+                      : c == 1 ? KeySet{2, n_sel, 0, blocks, p.topk, t}
+                               : KeySet{1, nw, p.v0 + t - nw + 1, nullptr, 0, 0};
+      float sg[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) sg[h] = 1.f / (1.f + expf(-gl[h * 3 + c]));
       wave_lds_sync();
 #pragma unroll
-      for (int e = 0; e < E; ++e) dos[lane + 64 * e] = sg * douts[lane + 64 * e];
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) dos[h][lane + 64 * e] = sg[h] * douts[h][lane + 64 * e];
       wave_lds_sync();
-      const float go = branch_bwd<D>(p, ks, g, qs, dos, douts, pb, db, dq, lane);
-      if (lane == 0) dg[c] = go * sg * (1.f - sg);
+      branch_bwd<D, G>(p, ks, g, qs, dos, douts, pb_[wv], db_[wv], dq, go, lane);
+      if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) dg[h * 3 + c] = go[h] * sg[h] * (1.f - sg[h]);
+      }
     }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) p.dq[oq + lane + 64 * e] = dq[e];
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) p.dq[oq + h * D + lane + 64 * e] = dq[h][e];
 }
 
 // dW = sum over (block, group) of dK_cmp (x) mean; one workgroup of D
@@ -313,6 +403,14 @@ __global__ __launch_bounds__(D) void bwd_cmp_tok_kernel(BwdParams p) {
   }
 }
 
+template <int D, int G>
+hipError_t run_rows(const BwdParams &p, hipStream_t st) {
+  const int64_t items = p.n * p.hkv;
+  hipLaunchKernelGGL((bwd_rows_kernel<D, G>), dim3((unsigned)((items + kBwdWavesG - 1) / kBwdWavesG)),
+                     dim3(64 * kBwdWavesG), 0, st, p);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t run(const BwdParams &p, int stage, hipStream_t st) {
   switch (stage) {
@@ -329,12 +427,18 @@ hipError_t run(const BwdParams &p, int stage, hipStream_t st) {
     case 1:
       if (p.n_blk > 0) hipLaunchKernelGGL((bwd_pool_kernel<D>), dim3(p.n_blk * p.hkv), dim3(D), 0, st, p);
       break;
-    case 2: {
-      const int64_t items = p.n * p.hq;
-      hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3((unsigned)((items + kBwdWaves - 1) / kBwdWaves)),
-                         dim3(64 * kBwdWaves), 0, st, p);
-      break;
-    }
+    case 2:
+      switch (p.hq / p.hkv) {
+        case 1: return run_rows<D, 1>(p, st);
+        case 2: return run_rows<D, 2>(p, st);
+        case 3: return run_rows<D, 3>(p, st);
+        case 4: return run_rows<D, 4>(p, st);
+        case 5: return run_rows<D, 5>(p, st);
+        case 6: return run_rows<D, 6>(p, st);
+        case 7: return run_rows<D, 7>(p, st);
+        case 8: return run_rows<D, 8>(p, st);
+        default: return hipErrorInvalidValue;
+      }
     default:
       hipLaunchKernelGGL((bwd_cmp_w_kernel<D>), dim3(2 * D), dim3(D), 0, st, p);
       if (p.n_blk > 0) hipLaunchKernelGGL((bwd_cmp_tok_kernel<D>), dim3(p.n_blk * p.hkv), dim3(D), 0, st, p);
