@@ -184,7 +184,10 @@ nsa_status nsa_prefill_dense(const nsa_prefill_desc *desc, const void *q, const 
  * the head sizes and limits of nsa_prefill; else NSA_ERR_UNSUPPORTED.
  * Arithmetic is fp32 throughout; dk, dv and the compressed-key gradients are
  * accumulated with float atomics, so their low bits vary from run to run.
- *   sel_idx   device [N_v, Hkv, top_k] int32 (may be NULL when N_v = 0)
+ *   sel_idx   device [N_v, Hkv, top_k] int32 (may be NULL when N_v = 0): the
+ *             forward's list (ascending, -1 padded, the own block last); any
+ *             other contents give meaningless gradients, never an access
+ *             outside the inputs
  *   dout      device [N, Hq, d] float32
  *   workspace device, >= nsa_prefill_backward_workspace_size bytes, 256-B aligned */
 nsa_status nsa_prefill_backward_workspace_size(const nsa_prefill_desc *desc, const uint8_t *is_vision,

@@ -85,9 +85,11 @@ struct KeySet {
 // selected blocks, in block order). The blocks come in ascending order,
 // -1 padded: every one but the last is a complete earlier block of 64 keys,
 // and the last is the query's own block, cut at t; so key i is key i % 64
-// of entry i / 64.
+// of entry i / 64. Any other list (not the forward's) gives meaningless
+// gradients but no access outside the rows 0 .. t.
 __device__ __forceinline__ int64_t sel_row(const BwdParams &p, const KeySet &ks, int i) {
-  return p.v0 + (int64_t)ks.blocks[i / kBlk] * kBlk + (i % kBlk);
+  const int b = max(ks.blocks[i / kBlk], 0);
+  return p.v0 + min(b * kBlk + (i % kBlk), ks.t);
 }
 
 template <int D>
