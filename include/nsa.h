@@ -26,7 +26,9 @@
  * Conventions for every entry point:
  *   - Device pointers are HIP device memory; "host" marks host memory.
  *   - All tensors are dense, row-major, with the last dimension contiguous,
- *     and 16-byte aligned.
+ *     and 16-byte aligned, except gate logits, selected block indices and
+ *     log-sum-exp outputs (float32 / int32 arrays accessed element by
+ *     element), which need only their 4-byte element alignment.
  *   - The caller owns every buffer, including the workspace; the library
  *     allocates nothing and keeps no state between calls (the opt-in
  *     benchmark timing below is the one exception: while enabled it creates
@@ -107,7 +109,8 @@ nsa_status nsa_prefill_workspace_size(const nsa_prefill_desc *desc,
  *   out          device [N, Hq, d]   float32   written for every token
  * Optional outputs (NULL to skip):
  *   k_cmp_out, v_cmp_out device [N_v/B, Hkv, d] float32  compressed keys/values
- *                                                          before bf16 rounding
+ *                as computed in fp32, before the kernels round them to fp16
+ *                (bf16 hi/lo parts for fp32 keys) for their own use
  *   sel_idx_out  device [N_v, Hkv, top_k] int32  selected block indices per
  *                vision query (vision-local numbering), ascending, -1 padded
  *   lse_out      device [N_v, Hq] float32  log-sum-exp of the compression
@@ -132,9 +135,9 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
  * (numbering local to each sequence), lse_out [sum of N_v,i, Hq]. The
  * sequences run one after another on the stream and share the workspace,
  * sized for the largest (nsa_prefill_varlen_workspace_size). Every
- * sequence is validated before anything is enqueued; each sequence's slices
- * must meet nsa_prefill's 16-byte alignment (always so when Hq is a multiple
- * of 4). */
+ * sequence is validated before anything is enqueued. Each sequence's slices
+ * meet nsa_prefill's alignment whenever the whole arrays do (a slice starts a
+ * whole number of d-element rows, or 4-byte elements, into its array). */
 nsa_status nsa_prefill_varlen_workspace_size(const nsa_prefill_desc *desc, int32_t n_seqs,
                                              const int64_t *cu_seqlens,
                                              const uint8_t *is_vision, size_t *bytes);

@@ -111,12 +111,16 @@ def cmp_pool(x: np.ndarray, w: np.ndarray, block: int) -> np.ndarray:
 
 
 def prefill(inp: dict, rows=None, inject_sel=None, top_k=None, window=None, scale=0.0,
-            want=("out", "lse", "sel", "ocmp", "osel", "oswa", "counts", "kcmp")) -> dict:
+            want=("out", "lse", "sel", "ocmp", "osel", "oswa", "counts", "kcmp"),
+            outputs: bool = True) -> dict:
     """Evaluate the layer at global positions ``rows`` (default: all).
 
     ``inp`` holds q [N,Hq,d], k/v [N,Hkv,d], is_vision [N], w_k, w_v [d,d],
     gates [N,Hq,3] and ``shape`` (for block, top_k, window). Returns fp64
-    arrays indexed by the requested rows."""
+    arrays indexed by the requested rows. With ``outputs=False`` the layer
+    output ("out") and the branch outputs are not computed: a selection-only
+    evaluation (pooling, compression attention, scores and selection), a
+    fraction of the cost, whose sel/lse/scores equal the full call's."""
     s = inp["shape"]
     q, k, v = _f32(inp["q"]), _f32(inp["k"]), _f32(inp["v"])
     gates = _f32(inp["gates"])
@@ -139,8 +143,11 @@ def prefill(inp: dict, rows=None, inject_sel=None, top_k=None, window=None, scal
             return res[name]
         return None
 
-    out = np.empty((n, hq, d), dtype=np.float64)
-    res["out"] = out
+    if not outputs:
+        want = tuple(w for w in want if w not in ("ocmp", "osel", "oswa"))
+    out = np.empty((n, hq, d), dtype=np.float64) if outputs else None
+    if outputs:
+        res["out"] = out
     lse = alloc("lse", (n, hq))
     sel = alloc("sel", (n, hkv, kk), np.int32)
     ocmp = alloc("ocmp", (n, hq, d))

@@ -267,6 +267,9 @@ static int vision_query(const vis_ctx *c, scratch_t *w, int64_t t, const float *
       for (int64_t j = b0; j <= b1; ++j) w->rows[n_rows++] = vrow(c, j);
     }
     if (g == 0) cnt_sel = n_rows;
+    /* with no output requested (a selection-only call) the attention of
+     * O6-O8 is skipped; every quantity of O2-O5 above is unchanged */
+    if (!out && !osel && !oswa) continue;
     for (int hh = 0; hh < c->G; ++hh) {
       const int h = g * c->G + hh;
       for (int i = 0; i < d; ++i) w->qv[i] = (double)q[(int64_t)h * d + i];
@@ -285,7 +288,7 @@ static int vision_query(const vis_ctx *c, scratch_t *w, int64_t t, const float *
   if (j0 < 0) j0 = 0;
   int64_t n_swa = 0;
   for (int64_t j = j0; j <= t; ++j) w->rows[n_swa++] = vrow(c, j);
-  for (int h = 0; h < c->hq; ++h) {
+  for (int h = 0; h < c->hq && (out || oswa); ++h) {
     const int g = h / c->G;
     for (int i = 0; i < d; ++i) w->qv[i] = (double)q[(int64_t)h * d + i];
     double *ow = oswa ? oswa + (int64_t)h * d : w->o3 + 2 * d;
@@ -415,13 +418,15 @@ int ora_prefill(const ora_desc *ds, const float *q, const float *k, const float 
         /* O9: text query, dense causal GQA over every earlier position (R1) */
         int64_t nk = pos + 1;
         for (int64_t j = 0; j < nk; ++j) w.rows[j] = j;
-        for (int h = 0; h < hq; ++h) {
+        for (int h = 0; h < hq && o_r; ++h) {
           const int g = h / (hq / hkv);
           for (int i = 0; i < d; ++i) w.qv[i] = (double)qr[(int64_t)h * d + i];
           double tmp_lse = attend_f(w.qv, d, scale, nk, w.rows, k + g * (int64_t)d,
                                     v + g * (int64_t)d, (int64_t)hkv * d, w.s,
                                     o_r ? o_r + (int64_t)h * d : w.o3);
           (void)tmp_lse;
+        }
+        for (int h = 0; h < hq; ++h) {
           if (lse) lse[r * hq + h] = NAN;
           if (ocmp) for (int i = 0; i < d; ++i) ocmp[(r * hq + h) * (int64_t)d + i] = NAN;
           if (osel) for (int i = 0; i < d; ++i) osel[(r * hq + h) * (int64_t)d + i] = NAN;

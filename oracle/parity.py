@@ -154,6 +154,30 @@ def sample_rows(inp: dict, n_random: int = 256, seed: int = 0, n_text: int = 32)
     return np.unique(np.concatenate(picks))
 
 
+def stratified_rows(inp: dict, n_vision: int = 8192, n_boundary_blocks: int = 64, n_last: int = 1024,
+                    seed: int = 0) -> np.ndarray:
+    """Row sample for the largest workloads: the first two blocks, every row
+    of the edges of ``n_boundary_blocks`` random blocks (their first two, middle
+    and last two rows), the last ``n_last`` vision rows, random vision rows up
+    to ``n_vision`` in all, and every text row."""
+    s = inp["shape"]
+    isv = np.asarray(inp["is_vision"]).astype(bool)
+    V = np.nonzero(isv)[0]
+    T = np.nonzero(~isv)[0]
+    rng = np.random.default_rng(seed)
+    picks = [V[: 2 * s.block], V[-n_last:]]
+    nb = len(V) // s.block
+    if nb > 2:
+        blocks = rng.choice(np.arange(2, nb), size=min(n_boundary_blocks, nb - 2), replace=False)
+        for b in blocks:
+            picks.append(V[b * s.block + np.array([0, 1, s.block // 2, s.block - 2, s.block - 1])])
+    vis = np.unique(np.concatenate(picks))
+    rest = np.setdiff1d(V, vis)
+    extra = max(0, min(n_vision - len(vis), len(rest)))
+    vis = np.union1d(vis, rng.choice(rest, size=extra, replace=False))
+    return np.union1d(vis, T)
+
+
 def decode_inputs_cmp(inp: dict, round_fn) -> tuple:
     """Compressed caches for a decode workload, pooled by the oracle and
     rounded by round_fn (to the dtype both sides then consume)."""

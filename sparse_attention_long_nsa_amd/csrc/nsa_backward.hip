@@ -18,6 +18,7 @@
 //   bwd_cmp_w  dW = sum over blocks of dK_cmp x mean^T, and each block's
 //              W^T dK_cmp / 64 added to its 64 tokens' dk (dv likewise)
 #include "nsa_kernels.h"
+#include "nsa_index.h"
 #include "nsa_select.h"
 
 namespace nsa {
@@ -88,8 +89,7 @@ struct KeySet {
 // of entry i / 64. Any other list (not the forward's) gives meaningless
 // gradients but no access outside the rows 0 .. t.
 __device__ __forceinline__ int64_t sel_row(const BwdParams &p, const KeySet &ks, int i) {
-  const int b = max(ks.blocks[i / kBlk], 0);
-  return p.v0 + min(b * kBlk + (i % kBlk), ks.t);
+  return p.v0 + sel_key_row(ks.blocks[i / kBlk], i % kBlk, ks.t);
 }
 
 template <int D>
@@ -337,8 +337,7 @@ __global__ __launch_bounds__(64 * kBwdWavesG) void bwd_rows_kernel(BwdParams p) 
     const int32_t *blocks = p.sel + ((int64_t)t * p.hkv + g) * p.topk;
     int n_sel = 0;
     for (int e = 0; e < p.topk; ++e) {
-      const int b = blocks[e];
-      if (b >= 0) n_sel += max(0, min(kBlk, t - b * kBlk + 1));
+      n_sel += sel_block_keys(blocks[e], t);
     }
     const int nw = min(p.window, t + 1);
 #pragma unroll

@@ -18,6 +18,7 @@ constexpr int kMaxBlocks = 8192;  // selection union bitmask / top-k register bu
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 struct PrefillPlan {
   int64_t N = 0, v0 = 0, v1 = 0, n_vis = 0, n_text = 0;
@@ -207,10 +208,14 @@ nsa_status check_prefill_args(const PrefillPlan &pl, const void *q, const void *
                               float *lse_out, void *workspace, size_t workspace_bytes) {
   if (!q || !k || !v || !gate_logits || !out) return NSA_ERR_INVALID_ARG;
   if (pl.n_blk > 0 && (!w_cmp_k || !w_cmp_v)) return NSA_ERR_INVALID_ARG;
-  const void *ptrs[] = {q, k, v, w_cmp_k, w_cmp_v, gate_logits, out, k_cmp_out, v_cmp_out,
-                        sel_idx_out, lse_out};
+  // tensors read or written in 16-byte pieces; gate logits, selected
+  // indices and lse are accessed one 4-byte element at a time
+  const void *ptrs[] = {q, k, v, w_cmp_k, w_cmp_v, out, k_cmp_out, v_cmp_out};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return NSA_ERR_INVALID_ARG;
+  const void *ptrs4[] = {gate_logits, sel_idx_out, lse_out};
+  for (const void *p : ptrs4)
+    if (p && !aligned4(p)) return NSA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < pl.total) return NSA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return NSA_ERR_WORKSPACE;
   return NSA_OK;

@@ -445,9 +445,12 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
   const nsa_status st = plan_decode(desc, pl);
   if (st != NSA_OK) return st;
   if (!q || !k_cache || !v_cache || !k_cmp || !v_cmp || !gate_logits || !out) return NSA_ERR_INVALID_ARG;
-  const void *ptrs[] = {q, k_cache, v_cache, k_cmp, v_cmp, gate_logits, out, sel_idx_out, lse_out};
+  const void *ptrs[] = {q, k_cache, v_cache, k_cmp, v_cmp, out};
   for (const void *p : ptrs)
     if (p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0) return NSA_ERR_INVALID_ARG;
+  const void *ptrs4[] = {gate_logits, sel_idx_out, lse_out};  // element-wise accesses
+  for (const void *p : ptrs4)
+    if (p && (reinterpret_cast<uintptr_t>(p) & 3u) != 0) return NSA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < pl.total) return NSA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NSA_ERR_WORKSPACE;
   char *ws = static_cast<char *>(workspace);

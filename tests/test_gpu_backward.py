@@ -25,10 +25,13 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # n_vis, before, after, Hq, Hkv, d, k, w: partial last block, text on
-    # both sides, a window wider than the vision run, no text, d 64 and 128
+    # both sides, a window wider than the vision run, no text, d 64 and 128,
+    # one and eight query heads per KV head
     PrefillShape(300, 5, 7, 4, 2, 64, 64, 3, 50, "bf16"),
     PrefillShape(200, 0, 0, 4, 1, 64, 64, 2, 400, "bf16"),
     PrefillShape(1045, 16, 48, 28, 4, 128, 64, 8, 256, "bf16"),
+    PrefillShape(333, 3, 9, 3, 3, 64, 64, 4, 90, "bf16"),
+    PrefillShape(400, 0, 20, 16, 2, 64, 64, 5, 128, "bf16"),
 ]
 
 
@@ -62,3 +65,81 @@ def test_backward_parity(shape):
         err = np.abs(g - rf)
         assert err.max() <= 1e-3 * big, f"{gname}: max |d| {err.max():.3e} vs {big:.3e}"
         assert err.mean() <= 1e-5 * big, f"{gname}: mean |d| {err.mean():.3e} vs {big:.3e}"
+
+
+def upload(inp):
+    dev = {n: torch.from_numpy(np.ascontiguousarray(inp[n])).to("cuda:0").to(torch.bfloat16).contiguous()
+           for n in ("q", "k", "v", "w_k", "w_v")}
+    dev["gates"] = torch.from_numpy(np.ascontiguousarray(inp["gates"])).to("cuda:0")
+    return dev
+
+
+def sample_rows(inp, n_vis_rows, n_text_rows, seed=0):
+    isv = np.asarray(inp["is_vision"]).astype(bool)
+    V, T = np.nonzero(isv)[0], np.nonzero(~isv)[0]
+    rng = np.random.default_rng(seed)
+    picks = [V[:3], V[[63, 64, 65, 127, 128]], V[-3:], rng.choice(V, n_vis_rows, replace=False)]
+    if len(T):
+        picks += [T[[0, -1]], rng.choice(T, n_text_rows, replace=False)]
+    return np.unique(np.concatenate(picks))
+
+
+# The benchmarked backward (4,096 vision + 512 text tokens, k 32, w 256) and
+# the pages' training length (36,864 + 512, k 16, w 512; model card,
+# "Training Details"), on sampled rows: the upstream gradient is zero outside
+# the sample, so the oracle needs only those queries (its row-restricted
+# form), while the GPU runs the whole layer. The selection is the GPU
+# forward's own sel_idx, handed to the backward as a caller would.
+@pytest.mark.parametrize("shape,n_vis_rows,n_text_rows", [
+    (PrefillShape(4096, 0, 512, 28, 4, 128, 64, 32, 256, "bf16"), 160, 24),
+    (PrefillShape(36864, 0, 512, 28, 4, 128, 64, 16, 512, "bf16"), 64, 8),
+], ids=["bench_4k_k32_w256", "train_36k_k16_w512"])
+def test_backward_parity_sampled_rows_on_the_forwards_selection(shape, n_vis_rows, n_text_rows):
+    print(f"backward sampled rows {shape}", flush=True)
+    inp = make_prefill_inputs(shape, seed=13)
+    dev = upload(inp)
+    fwd = binding.prefill(dev["q"], dev["k"], dev["v"], inp["is_vision"], dev["w_k"], dev["w_v"], dev["gates"],
+                          shape.top_k, shape.window, want_sel=True)
+    torch.cuda.synchronize()
+    sel = fwd["sel_idx"].cpu().numpy()
+    rows = sample_rows(inp, n_vis_rows, n_text_rows)
+    dout = np.zeros((shape.n_tokens, shape.n_q_heads, shape.head_dim), np.float32)
+    dout[rows] = make_output_grad((len(rows), shape.n_q_heads, shape.head_dim), seed=14)
+    got = binding.prefill_backward(dev["q"], dev["k"], dev["v"], inp["is_vision"], dev["w_k"], dev["w_v"],
+                                   dev["gates"], fwd["sel_idx"], torch.from_numpy(dout).to("cuda:0"),
+                                   shape.top_k, shape.window, block=shape.block)
+    torch.cuda.synchronize()
+    got = {n: t.cpu().numpy().astype(np.float64) for n, t in got.items()}
+    print(f"  {len(rows)} rows, oracle ...", flush=True)
+    ref = bwd.gradients(inp, sel, dout, rows=rows)
+    others = np.setdiff1d(np.arange(shape.n_tokens), rows)
+    assert np.all(got["dq"][others] == 0) and np.all(got["dgate"][others] == 0)
+    pairs = (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dw_cmp_k", "w_k"), ("dw_cmp_v", "w_v"), ("dgate", "gates"))
+    for gname, rname in pairs:
+        g, rf = got[gname], ref[rname]
+        assert np.all(np.isfinite(g)), gname
+        big = np.abs(rf).max()
+        err = np.abs(g - rf)
+        print(f"  {gname}: max |d| {err.max():.3e} mean {err.mean():.3e} (max |ref| {big:.3e})", flush=True)
+        assert err.max() <= 1e-3 * big, f"{gname}: max |d| {err.max():.3e} vs {big:.3e}"
+        assert err.mean() <= 1e-5 * big, f"{gname}: mean |d| {err.mean():.3e} vs {big:.3e}"
+
+
+def test_backward_hostile_selection_lists_stay_in_bounds():
+    """Selection entries far outside the valid range (negative, beyond the
+    query's own block, 2^25, INT32_MAX) are clamped before any index
+    arithmetic: the call completes with finite gradients."""
+    shape = PrefillShape(640, 4, 8, 8, 2, 64, 64, 4, 100, "bf16")
+    print(f"backward hostile lists {shape}", flush=True)
+    inp = make_prefill_inputs(shape, seed=15)
+    dev = upload(inp)
+    nv = shape.n_vis
+    rng = np.random.default_rng(16)
+    bad = rng.choice(np.array([-7, -1, 0, 3, 9, 1 << 25, (1 << 31) - 1], np.int64), size=(nv, 2, 4)).astype(np.int32)
+    dout = make_output_grad((shape.n_tokens, shape.n_q_heads, shape.head_dim), seed=17)
+    got = binding.prefill_backward(dev["q"], dev["k"], dev["v"], inp["is_vision"], dev["w_k"], dev["w_v"],
+                                   dev["gates"], torch.from_numpy(bad).to("cuda:0"),
+                                   torch.from_numpy(dout).to("cuda:0"), shape.top_k, shape.window, block=shape.block)
+    torch.cuda.synchronize()
+    for n, t in got.items():
+        assert torch.isfinite(t).all(), n

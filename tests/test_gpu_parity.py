@@ -135,8 +135,10 @@ def test_repeat_runs_are_bitwise_identical():
     assert np.array_equal(a["out"], b["out"])
 
 
-@pytest.mark.parametrize("preset", ["qwen_36k", "qwen_64k", "qwen_128k_k32_w256", "qwen_128k_k16_w512",
-                                    "qwen_128k_k8_w1024", "qwen_256k_k32_w256", "qwen_512k_k32_w256"])
+# qwen_36k, qwen_64k and qwen_128k_k32_w256 are checked at full row coverage
+# in test_gpu_parity_full.py
+@pytest.mark.parametrize("preset", ["qwen_128k_k16_w512", "qwen_128k_k8_w1024", "qwen_256k_k32_w256",
+                                    "qwen_512k_k32_w256"])
 def test_full_size_sampled_rows(preset):
     inp = make_prefill_inputs(PREFILL_PRESETS[preset], seed=0)
     announce(preset, inp["shape"])

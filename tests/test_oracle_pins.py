@@ -521,3 +521,28 @@ def test_p18_gate_gradient_closed_form():
         ref = (dout[vis] * r[name][vis]).sum(-1) * sig[..., c] * (1 - sig[..., c])
         np.testing.assert_allclose(g["gates"][vis][..., c], ref, rtol=0, atol=1e-12)
     assert np.all(g["gates"][~vis] == 0)
+
+
+def test_p18_row_restricted_form_equals_the_full_form():
+    """The row-restricted backward oracle (queries limited to a sample of
+    rows) gives exactly the full form's rows, and its gradients equal the full
+    form's gradients when dout is zero outside the sample; the restriction
+    changes which queries are evaluated, not any formula."""
+    inp = small(n_vis=300, before=5, after=7, hq=4, hkv=2, d=16, k=3, w=50)
+    _, sel = _vision_sel(inp)
+    N = inp["q"].shape[0]
+    rows = np.array([0, 3, 5, 6, 70, 127, 128, 200, 304, 305, N - 2, N - 1])
+    t = {n: torch.tensor(np.asarray(inp[n], dtype=np.float64)) for n in ("q", "k", "v", "w_k", "w_v", "gates")}
+    args = (t["q"], t["k"], t["v"], t["w_k"], t["w_v"], t["gates"], inp["is_vision"], sel, 64, 50, 0.25)
+    full = bwd.forward(*args).numpy()
+    part = bwd.forward(*args, rows=rows).numpy()
+    np.testing.assert_array_equal(part, full[rows])
+    dout = np.random.default_rng(6).standard_normal(full.shape)
+    dz = np.zeros_like(dout)
+    dz[rows] = dout[rows]
+    g_full = bwd.gradients(inp, sel, dz, scale=0.25)
+    g_part = bwd.gradients(inp, sel, dout, scale=0.25, rows=rows)
+    for n in g_full:
+        np.testing.assert_allclose(g_part[n], g_full[n], rtol=0, atol=1e-12, err_msg=n)
+    # and a restriction that drops a row drops exactly its contribution
+    assert np.abs(g_part["q"][np.setdiff1d(np.arange(N), rows)]).max() == 0

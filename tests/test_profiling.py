@@ -103,3 +103,23 @@ def test_counter_summary_utilisation(tmp_path):
     assert cells[1] == "1.000" and cells[3] == "10"          # ms, VALU per wave
     assert cells[8:11] == ["50%", "25%", "40%"]               # vector busy, matrix busy, waiting
     assert cells[12] == "16.38"                               # 1e9 matrix instructions x 16,384 flops
+
+
+def test_committed_counter_profiles_match_their_current_sources():
+    """A *_pmc.json records the hash of the source its kernel was built from;
+    a profile of a kernel that has changed since is stale and must be retaken
+    or removed (the benchmark also reports no traffic figure for it)."""
+    import glob
+    import hashlib
+    import json
+    import os
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for path in sorted(glob.glob(os.path.join(root, "profiles", "*_pmc.json"))):
+        with open(path) as f:
+            rec = json.load(f)
+        src = os.path.join(root, rec["source"])
+        assert os.path.exists(src), (path, rec["source"])
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()[:16]
+        assert digest == rec["source_sha256_16"], f"{os.path.basename(path)} is stale: retake or remove it"
