@@ -282,6 +282,24 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
                       float *lse_out, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/* nsa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step with the same results, its scratch taken from a fixed array of
+ * NSA_DECODE_NOALLOC_SCRATCH_BYTES in device memory that the library holds on
+ * every GPU it runs on until the process ends. No allocation happens in the
+ * call. Needs plan <= that size (nsa_decode_workspace_size reports the need;
+ * 16 sequences of 131,072 tokens with 28 query heads and d 128 use about
+ * 17 MB); a larger step returns NSA_ERR_WORKSPACE before anything is
+ * launched. All calls on one GPU share its array, and the contents of one
+ * call are not kept for the next: calls that overlap in time on the same
+ * GPU (several streams or host threads) race and must be serialised by the
+ * caller. Arguments and errors otherwise as nsa_decode. */
+#define NSA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+nsa_status nsa_decode_noalloc(const nsa_decode_desc *desc, const void *q, const void *k_cache,
+                              const void *v_cache, const void *k_cmp, const void *v_cmp,
+                              const float *gate_logits, float *out, int32_t *sel_idx_out,
+                              float *lse_out, void *stream);
+
 /* Appends one token per sequence to the decode caches and keeps the
  * compressed caches current, so that nsa_decode can run at length cache_len
  * next (the streaming use described above, in one call): k_new / v_new

@@ -25,8 +25,11 @@ EXPORTED = (
     "nsa_prefill_dense_workspace_size", "nsa_prefill_dense", "nsa_cache_append",
     "nsa_prefill_varlen_workspace_size", "nsa_prefill_varlen",
     "nsa_gate_workspace_size", "nsa_gate_logits",
-    "nsa_prefill_backward_workspace_size", "nsa_prefill_backward",
+    "nsa_prefill_backward_workspace_size", "nsa_prefill_backward", "nsa_decode_noalloc",
 )
+
+# size of the library's fixed decode scratch (nsa.h NSA_DECODE_NOALLOC_SCRATCH_BYTES)
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 NSA_ACTIVATIONS = {"silu": 0, "gelu_tanh": 1, "relu": 2}
 
 
@@ -115,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.POINTER(S)]
         L.nsa_decode_workspace_size.restype = ctypes.c_int
         L.nsa_decode.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 10 + [S, P]
+        L.nsa_decode_noalloc.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 10
+        L.nsa_decode_noalloc.restype = ctypes.c_int
         L.nsa_decode.restype = ctypes.c_int
         L.nsa_cmp_pool.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, P, P, P, P, P]
@@ -484,6 +489,40 @@ def decode(q, k_cache, v_cache, k_cmp, v_cmp, gate_logits, top_k, window, block=
     if st != NSA_OK:
         raise NsaError(st, "nsa_decode")
     res["workspace"] = workspace
+    return res
+
+
+def decode_noalloc(q, k_cache, v_cache, k_cmp, v_cmp, gate_logits, top_k, window, block=64, scale=0.0,
+                   out=None, sel_idx=None, lse=None, stream=None, cache_len=None) -> dict:
+    """Runs nsa_decode_noalloc (decode with the library's fixed device
+    scratch, no workspace): arguments as decode(); preallocated out / sel_idx
+    / lse tensors may be passed so that the call itself allocates nothing."""
+    desc = decode_desc(q, k_cache, top_k, window, block, scale, cache_len)
+    bt, hq, d = q.shape
+    cap, hkv = k_cache.shape[1], k_cache.shape[2]
+    for name, t, shape in (("q", q, (bt, hq, d)), ("k_cache", k_cache, (bt, cap, hkv, d)),
+                           ("v_cache", v_cache, (bt, cap, hkv, d)),
+                           ("k_cmp", k_cmp, (bt, cap // block, hkv, d)),
+                           ("v_cmp", v_cmp, (bt, cap // block, hkv, d))):
+        _check_dev(name, t, q.dtype, shape)
+    _check_dev("gate_logits", gate_logits, torch.float32, (bt, hq, 3))
+    if out is None:
+        out = torch.empty((bt, hq, d), dtype=torch.float32, device=q.device)
+    _check_dev("out", out, torch.float32, (bt, hq, d))
+    if sel_idx is not None:
+        _check_dev("sel_idx", sel_idx, torch.int32, (bt, hkv, top_k))
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32, (bt, hq))
+    st = lib().nsa_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_cmp),
+                                  _ptr(v_cmp), _ptr(gate_logits), _ptr(out), _ptr(sel_idx), _ptr(lse),
+                                  _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_decode_noalloc")
+    res = {"out": out}
+    if sel_idx is not None:
+        res["sel_idx"] = sel_idx
+    if lse is not None:
+        res["lse"] = lse
     return res
 
 

@@ -19,6 +19,7 @@
 //   dec_item (phase 1) one selected block per item
 //   dec_combine        per (sequence, query head): merge the partials of the
 //                      selected and window branches, apply the gates
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/nsa.h"
@@ -437,11 +438,17 @@ nsa_status nsa_decode_workspace_size(const nsa_decode_desc *desc, size_t *bytes)
   return NSA_OK;
 }
 
-nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_cache,
-                      const void *v_cache, const void *k_cmp, const void *v_cmp,
-                      const float *gate_logits, float *out, int32_t *sel_idx_out, float *lse_out,
-                      void *workspace, size_t workspace_bytes, void *stream) {
-  DecPlan pl;
+}  // extern "C"
+
+namespace nsa {
+namespace {
+
+// Argument checks shared by nsa_decode and nsa_decode_noalloc (everything
+// but the workspace).
+nsa_status check_decode_args(const nsa_decode_desc *desc, DecPlan &pl, const void *q, const void *k_cache,
+                             const void *v_cache, const void *k_cmp, const void *v_cmp,
+                             const float *gate_logits, const float *out, const int32_t *sel_idx_out,
+                             const float *lse_out) {
   const nsa_status st = plan_decode(desc, pl);
   if (st != NSA_OK) return st;
   if (!q || !k_cache || !v_cache || !k_cmp || !v_cmp || !gate_logits || !out) return NSA_ERR_INVALID_ARG;
@@ -451,9 +458,14 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
   const void *ptrs4[] = {gate_logits, sel_idx_out, lse_out};  // element-wise accesses
   for (const void *p : ptrs4)
     if (p && (reinterpret_cast<uintptr_t>(p) & 3u) != 0) return NSA_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < pl.total) return NSA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NSA_ERR_WORKSPACE;
-  char *ws = static_cast<char *>(workspace);
+  return NSA_OK;
+}
+
+// Enqueues a validated decode step with `ws` (pl.total bytes, 256-B aligned)
+// as its scratch.
+nsa_status enqueue_decode(const DecPlan &pl, const void *q, const void *k_cache, const void *v_cache,
+                          const void *k_cmp, const void *v_cmp, const float *gate_logits, float *out,
+                          int32_t *sel_idx_out, float *lse_out, char *ws, hipStream_t stream) {
   DecodeParams p{};
   p.q = static_cast<const uint16_t *>(q);
   p.kcache = static_cast<const uint16_t *>(k_cache);
@@ -482,8 +494,68 @@ nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_
   p.n_win = pl.n_win;
   p.n_items = pl.n_items;
   p.sl2 = pl.scale * kLog2e;
-  if (launch_decode(p, pl.d, pl.G, static_cast<hipStream_t>(stream)) != hipSuccess) return NSA_ERR_HIP;
+  if (launch_decode(p, pl.d, pl.G, stream) != hipSuccess) return NSA_ERR_HIP;
   return NSA_OK;
+}
+
+// Decode scratch that lives in device memory for the life of the process,
+// for callers that cannot allocate (nsa_decode_noalloc). Each GPU holds its
+// own copy; host code reaches it only through the address
+// hipGetSymbolAddress returns on that device, never through the name.
+constexpr size_t kNoallocBytes = (size_t)NSA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_lock;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch, looked up once per device.
+nsa_status device_scratch(char **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_lock);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return NSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char *>(g_scratch_ptr[dev]);
+  return NSA_OK;
+}
+
+}  // namespace
+}  // namespace nsa
+
+extern "C" {
+
+nsa_status nsa_decode(const nsa_decode_desc *desc, const void *q, const void *k_cache,
+                      const void *v_cache, const void *k_cmp, const void *v_cmp,
+                      const float *gate_logits, float *out, int32_t *sel_idx_out, float *lse_out,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  DecPlan pl;
+  const nsa_status st = check_decode_args(desc, pl, q, k_cache, v_cache, k_cmp, v_cmp, gate_logits, out,
+                                          sel_idx_out, lse_out);
+  if (st != NSA_OK) return st;
+  if (!workspace || workspace_bytes < pl.total) return NSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NSA_ERR_WORKSPACE;
+  return enqueue_decode(pl, q, k_cache, v_cache, k_cmp, v_cmp, gate_logits, out, sel_idx_out, lse_out,
+                        static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
+}
+
+nsa_status nsa_decode_noalloc(const nsa_decode_desc *desc, const void *q, const void *k_cache,
+                              const void *v_cache, const void *k_cmp, const void *v_cmp,
+                              const float *gate_logits, float *out, int32_t *sel_idx_out, float *lse_out,
+                              void *stream) {
+  DecPlan pl;
+  const nsa_status st = check_decode_args(desc, pl, q, k_cache, v_cache, k_cmp, v_cmp, gate_logits, out,
+                                          sel_idx_out, lse_out);
+  if (st != NSA_OK) return st;
+  if (pl.total > kNoallocBytes) return NSA_ERR_WORKSPACE;  // beyond the fixed scratch
+  char *ws = nullptr;
+  const nsa_status sst = device_scratch(&ws);
+  if (sst != NSA_OK) return sst;
+  return enqueue_decode(pl, q, k_cache, v_cache, k_cmp, v_cmp, gate_logits, out, sel_idx_out, lse_out, ws,
+                        static_cast<hipStream_t>(stream));
 }
 
 nsa_status nsa_cache_append(const nsa_decode_desc *desc, const void *k_new, const void *v_new,

@@ -158,6 +158,18 @@ int main() {
     CHECK(nsa_decode_workspace_size(&bad, &b) != NSA_OK, "decode batch 0");
     CHECK(nsa_cache_append(&dd, nullptr, fake(), fake(), fake(), fake(), fake(), fake(), fake(), nullptr) ==
               NSA_ERR_INVALID_ARG, "append null");
+    // the no-allocation variant: same argument checks, and a step beyond its
+    // fixed scratch is refused before any HIP call
+    CHECK(nsa_decode_noalloc(&dd, nullptr, fake(), fake(), fake(), fake(), (const float *)fake(), (float *)fake(),
+                             nullptr, nullptr, nullptr) == NSA_ERR_INVALID_ARG, "noalloc null q");
+    CHECK(nsa_decode_noalloc(&dd, fake(), fake(), fake(), fake(), fake(), (const float *)fake(), (float *)fake(),
+                             (int32_t *)fake(2), nullptr, nullptr) == NSA_ERR_INVALID_ARG, "noalloc misaligned sel");
+    nsa_decode_desc huge = dd;
+    huge.batch = 64;
+    huge.cache_len = 524288;
+    CHECK(nsa_decode_workspace_size(&huge, &b) == NSA_OK && b > NSA_DECODE_NOALLOC_SCRATCH_BYTES, "huge ws");
+    CHECK(nsa_decode_noalloc(&huge, fake(), fake(), fake(), fake(), fake(), (const float *)fake(), (float *)fake(),
+                             nullptr, nullptr, nullptr) == NSA_ERR_WORKSPACE, "noalloc beyond scratch");
   }
 
   // gate prologue
