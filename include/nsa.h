@@ -38,7 +38,15 @@
  *   - Every argument is validated before anything is enqueued. On any
  *     non-OK status nothing has been written or launched.
  *   - Kernel faults surface at the caller's next synchronisation;
- *     NSA_ERR_HIP reports errors returned by launches themselves.
+ *     NSA_ERR_HIP reports errors returned by launches themselves. The
+ *     prefill kernels' waits on each other inside a workgroup are bounded:
+ *     one that gives up (about 0.1 s without progress, which a correct run
+ *     never reaches) ends its kernel normally with NaN outputs and sets the
+ *     status word of the call's workspace, which nsa_workspace_status reads.
+ *   - Value range: queries, values and the compressed keys/values are used
+ *     in fp16 by the kernels (bf16 -> fp16 is exact inside fp16's range), so
+ *     their magnitudes must stay below 65504; larger bf16 inputs overflow to
+ *     infinity and give non-finite outputs for the rows that touch them.
  */
 #ifndef NSA_H_
 #define NSA_H_
@@ -55,7 +63,9 @@ typedef enum {
   NSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer    */
   NSA_ERR_UNSUPPORTED = 2, /* valid arguments outside what the kernels take */
   NSA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than needed */
-  NSA_ERR_HIP = 4          /* a HIP launch reported an error                */
+  NSA_ERR_HIP = 4,         /* a HIP launch reported an error                */
+  NSA_ERR_KERNEL = 5       /* a kernel gave up a bounded wait (see
+                              nsa_workspace_status)                         */
 } nsa_status;
 
 typedef enum {
@@ -353,6 +363,21 @@ int nsa_timing_read(int max_entries, const char **names, double *total_ms, int *
  * on `stream`.
  * NSA_ERR_INVALID_ARG for n_wg < 1, iters < 1 or out == NULL. */
 nsa_status nsa_probe_mfma_bf16(int32_t n_wg, int32_t iters, float *out, void *stream);
+
+/* Status word of a prefill workspace (the first 4 bytes of the workspace
+ * passed to nsa_prefill or nsa_prefill_varlen, cleared at the start of every
+ * such call): waits on `stream` for the work enqueued so far, copies the word
+ * to *flags and returns NSA_ERR_KERNEL if it is nonzero (bit 0: a bounded
+ * wait gave up and that call's outputs are invalid), NSA_OK otherwise.
+ * workspace: device, 256-B aligned; NSA_ERR_INVALID_ARG for NULL arguments. */
+nsa_status nsa_workspace_status(const void *workspace, void *stream, int32_t *flags);
+
+/* Test aid: the number of s_sleep rounds a bounded wait of the prefill
+ * kernels spins before giving up, for calls enqueued afterwards in this
+ * process (rounds <= 0 restores the default, about 0.1 s). A tiny limit
+ * makes the waits give up, so that the failure path -- every kernel ending
+ * normally, NaN outputs, the status word set -- can be exercised. */
+nsa_status nsa_debug_set_spin_limit(int32_t rounds);
 
 /* Static description of a status code. */
 const char *nsa_status_string(nsa_status status);

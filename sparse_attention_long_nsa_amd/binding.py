@@ -15,7 +15,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnsa.so")
 
-NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP = range(5)
+NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP, NSA_ERR_KERNEL = range(6)
 NSA_DTYPE_BF16, NSA_DTYPE_FP32 = 0, 1
 
 EXPORTED = (
@@ -26,6 +26,7 @@ EXPORTED = (
     "nsa_prefill_varlen_workspace_size", "nsa_prefill_varlen",
     "nsa_gate_workspace_size", "nsa_gate_logits",
     "nsa_prefill_backward_workspace_size", "nsa_prefill_backward", "nsa_decode_noalloc",
+    "nsa_workspace_status", "nsa_debug_set_spin_limit",
 )
 
 # size of the library's fixed decode scratch (nsa.h NSA_DECODE_NOALLOC_SCRATCH_BYTES)
@@ -120,6 +121,10 @@ def lib() -> ctypes.CDLL:
         L.nsa_decode.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 10 + [S, P]
         L.nsa_decode_noalloc.argtypes = [ctypes.POINTER(DecodeDesc)] + [P] * 10
         L.nsa_decode_noalloc.restype = ctypes.c_int
+        L.nsa_workspace_status.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
+        L.nsa_workspace_status.restype = ctypes.c_int
+        L.nsa_debug_set_spin_limit.argtypes = [ctypes.c_int32]
+        L.nsa_debug_set_spin_limit.restype = ctypes.c_int
         L.nsa_decode.restype = ctypes.c_int
         L.nsa_cmp_pool.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, P, P, P, P, P]
@@ -155,6 +160,24 @@ def timing_read() -> dict:
     cnt = (ctypes.c_int * max(n, 1))()
     n = lib().nsa_timing_read(n, names, ms, cnt)
     return {names[i].decode(): (ms[i], cnt[i]) for i in range(n)}
+
+
+def workspace_status(workspace, stream=None) -> int:
+    """Runs nsa_workspace_status on a prefill workspace: waits for the stream
+    and returns the status word (0 = every wait completed and every fp16
+    value was in range; bit 0: a bounded wait gave up; bit 1: an fp16
+    overflow)."""
+    flags = ctypes.c_int32(0)
+    st = lib().nsa_workspace_status(_ptr(workspace), _stream(stream), ctypes.byref(flags))
+    if st not in (NSA_OK, NSA_ERR_KERNEL):
+        raise NsaError(st, "nsa_workspace_status")
+    return int(flags.value)
+
+
+def set_spin_limit(rounds: int) -> None:
+    """Test aid (nsa_debug_set_spin_limit): bounded-wait rounds of the prefill
+    kernels for later calls; <= 0 restores the default."""
+    lib().nsa_debug_set_spin_limit(int(rounds))
 
 
 def status_string(status: int) -> str:

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/nsa.h"
 #include "nsa_kernels.h"
 #include "nsa_timing.h"
@@ -92,6 +94,7 @@ nsa_status plan_prefill(const nsa_prefill_desc *ds, const uint8_t *is_vision, Pr
   const size_t H = (size_t)pl.hq, Hk = (size_t)pl.hkv, D = (size_t)pl.d;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  take(sizeof(int32_t));  // offset 0: the status word (nsa_workspace_status)
   pl.off_means = take(sizeof(float) * 2 * (size_t)pl.n_blk * Hk * D);  // block means of keys, values
   pl.off_kc = take(sizeof(uint16_t) * pl.n_blk * Hk * D);
   pl.off_vc = take(sizeof(uint16_t) * pl.n_blk * Hk * D);
@@ -167,6 +170,9 @@ template <class T> T *at(void *base, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(base) + off);
 }
 
+constexpr int kDefaultSpinLimit = 1 << 22;  // s_sleep(1) rounds, about 0.1 s
+std::atomic<int> g_spin_limit{kDefaultSpinLimit};
+
 }  // namespace
 }  // namespace nsa
 
@@ -181,11 +187,28 @@ const char *nsa_status_string(nsa_status s) {
     case NSA_ERR_UNSUPPORTED: return "unsupported configuration";
     case NSA_ERR_WORKSPACE: return "workspace missing or too small";
     case NSA_ERR_HIP: return "HIP launch error";
+    case NSA_ERR_KERNEL: return "a kernel's bounded wait gave up: that call's outputs are invalid";
   }
   return "unknown status";
 }
 
-const char *nsa_version(void) { return "0.1.0"; }
+const char *nsa_version(void) { return "0.2.0"; }
+
+nsa_status nsa_workspace_status(const void *workspace, void *stream, int32_t *flags) {
+  if (!workspace || !flags) return NSA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return NSA_ERR_INVALID_ARG;
+  int32_t word = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess) return NSA_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return NSA_ERR_HIP;
+  *flags = word;
+  return word ? NSA_ERR_KERNEL : NSA_OK;
+}
+
+nsa_status nsa_debug_set_spin_limit(int32_t rounds) {
+  g_spin_limit.store(rounds > 0 ? rounds : kDefaultSpinLimit, std::memory_order_relaxed);
+  return NSA_OK;
+}
 
 nsa_status nsa_prefill_workspace_size(const nsa_prefill_desc *desc, const uint8_t *is_vision,
                                       size_t *bytes) {
@@ -225,7 +248,8 @@ nsa_status check_prefill_args(const PrefillPlan &pl, const void *q, const void *
 nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, const void *v,
                            const uint8_t *is_vision, const void *w_cmp_k, const void *w_cmp_v,
                            const float *gate_logits, float *out, float *k_cmp_out, float *v_cmp_out,
-                           int32_t *sel_idx_out, float *lse_out, void *workspace, hipStream_t s) {
+                           int32_t *sel_idx_out, float *lse_out, void *workspace, hipStream_t s,
+                           bool clear_status) {
   const int64_t H = pl.hq, Hk = pl.hkv, D = pl.d;
   const uint16_t *qb = static_cast<const uint16_t *>(q);
   const uint16_t *kb = static_cast<const uint16_t *>(k);
@@ -246,6 +270,9 @@ nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, 
     NSA_CHECK(expr);           \
   } while (0)
 
+  int32_t *status = at<int32_t>(workspace, 0);
+  if (clear_status) NSA_LAUNCH("status_clear", launch_status_clear(status, s));
+
   // fp32 inputs: block scores from split bf16 operands (q_hi, q_lo), every
   // other product in fp16
   const uint16_t *qc = qb;  // queries of the compression branch
@@ -254,9 +281,9 @@ nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, 
     uint16_t *q16 = at<uint16_t>(workspace, pl.off_q16), *k16 = at<uint16_t>(workspace, pl.off_k16);
     uint16_t *v16 = at<uint16_t>(workspace, pl.off_v16);
     NSA_LAUNCH("split_q", launch_split_bf16(static_cast<const float *>(q), pl.N * H * D, qh, qlo, s));
-    NSA_LAUNCH("to_f16_q", launch_to_f16(static_cast<const float *>(q), pl.N * H * D, q16, s));
-    NSA_LAUNCH("to_f16_k", launch_to_f16(static_cast<const float *>(k), pl.N * Hk * D, k16, s));
-    NSA_LAUNCH("to_f16_v", launch_to_f16(static_cast<const float *>(v), pl.N * Hk * D, v16, s));
+    NSA_LAUNCH("to_f16_q", launch_to_f16(static_cast<const float *>(q), pl.N * H * D, q16, s, status));
+    NSA_LAUNCH("to_f16_k", launch_to_f16(static_cast<const float *>(k), pl.N * Hk * D, k16, s, status));
+    NSA_LAUNCH("to_f16_v", launch_to_f16(static_cast<const float *>(v), pl.N * Hk * D, v16, s, status));
     qc = qh; ql = qlo; qb = q16; kb = k16; vb = v16;
     kcl = at<uint16_t>(workspace, pl.off_kcl);
   }
@@ -294,6 +321,7 @@ nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, 
                  pl.fp32 ? kc : nullptr, kcl, pl.fp32 ? nullptr : kc, k_cmp_out, vmap};
       PoolJob jv{static_cast<const char *>(v) + esz * r0 * Hk * D, w_cmp_v, pl.hkv, pl.n_blk,
                  nullptr, nullptr, vc, v_cmp_out, vmap};
+      jk.status = jv.status = status;
       NSA_LAUNCH("cmp_pool", launch_cmp_pool_split(jk, jv, pl.d, pl.fp32, at<float>(workspace, pl.off_means), s));
     }
     uint16_t *kvc = nullptr;
@@ -302,12 +330,12 @@ nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, 
       NSA_LAUNCH("pack_cmp", launch_pack_tiles(kc, vc, 0, pl.n_blk, pl.hkv, pl.n_cch, kvc, pl.d, true, s));
     }
     CmpAttnParams cp{qc, ql, kc, kcl, vc, kvc, pl.n_cch, gate_logits, out, lse, gs, pl.v0,
-                     (int)pl.n_vis, pl.hq, pl.hkv, pl.n_frames, sl2, vmap};
+                     (int)pl.n_vis, pl.hq, pl.hkv, pl.n_frames, sl2, vmap, status};
     NSA_LAUNCH("cmp_attn", launch_cmp_attn(cp, pl.d, pl.G, pl.fp32, s));
     TopkParams tp{gs, sel, (int)pl.n_vis, pl.hkv, pl.k};
     NSA_LAUNCH("blk_score_topk", launch_topk(tp, pl.n_frames, s));
     SelParams sp{qb, kb, vb, at<uint16_t>(workspace, pl.off_vt), sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
-                 pl.n_frames, sl2, vmap};
+                 pl.n_frames, sl2, vmap, g_spin_limit.load(std::memory_order_relaxed), status};
     NSA_LAUNCH("pack_kv", launch_pack_kv(sp, pl.d, pl.fp32, s));
     SwaParams wp{qb, at<uint16_t>(workspace, pl.off_vt), gate_logits, out, pl.v0, (int)pl.n_vis,
                  pl.hq, pl.hkv, pl.w, pl.n_frames, sl2, vmap};
@@ -317,7 +345,7 @@ nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, 
   if (pl.n_text > 0) {
     uint16_t *kvt = at<uint16_t>(workspace, pl.off_kvt);
     NSA_LAUNCH("pack_text", launch_pack_tiles(kb, vb, 0, (int)pl.n_text, pl.hkv, pl.n_tchunks, kvt,
-                                              pl.d, pl.fp32, s, (int)pl.v0, pl.v1 - pl.v0, tmap));
+                                              pl.d, pl.fp32, s, (int)pl.v0, pl.v1 - pl.v0, tmap, status));
     TextParams tp{qb, at<uint16_t>(workspace, pl.off_vt), kvt, at<float>(workspace, pl.off_po),
                   at<float2>(workspace, pl.off_pml), out, pl.v0, pl.v1, pl.N, (int)pl.n_text,
                   pl.hq, pl.hkv, pl.n_split, pl.chunks_per_split, pl.text_tiles,
@@ -345,7 +373,7 @@ nsa_status nsa_prefill(const nsa_prefill_desc *desc, const void *q, const void *
                           sel_idx_out, lse_out, workspace, workspace_bytes);
   if (st != NSA_OK) return st;
   return enqueue_prefill(pl, q, k, v, is_vision, w_cmp_k, w_cmp_v, gate_logits, out, k_cmp_out,
-                         v_cmp_out, sel_idx_out, lse_out, workspace, static_cast<hipStream_t>(stream));
+                         v_cmp_out, sel_idx_out, lse_out, workspace, static_cast<hipStream_t>(stream), true);
 }
 
 // Several independent sequences, one after another on the stream.
@@ -412,7 +440,7 @@ nsa_status nsa_prefill_varlen(const nsa_prefill_desc *desc, int32_t n_seqs, cons
                                 workspace_bytes);
       } else {
         st = enqueue_prefill(pl, qi, ki, vi, is_vision + t0, w_cmp_k, w_cmp_v, gi, oi, kci, vci, si, li,
-                             workspace, static_cast<hipStream_t>(stream));
+                             workspace, static_cast<hipStream_t>(stream), i == 0);
       }
       if (st != NSA_OK) return st;
       vis0 += pl.n_vis;

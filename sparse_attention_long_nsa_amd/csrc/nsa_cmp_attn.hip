@@ -192,15 +192,16 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_kernel(CmpAttnParams p) {
     }
   }
 
-  // ---- epilogue: out = sigmoid(g_cmp) * o_cmp (first writer of vision rows)
+  // ---- epilogue: sigmoid(g_cmp) * o_cmp as the fp16 part 0 of the row's
+  // output slots (the selection kernel adds the branches and writes fp32)
   if (tvalid) {
     const int64_t r0 = row_pos(p.vmap, p.v0, t) * p.hq + (int64_t)g * G;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float gate = sigmoidf_(p.gates[(r0 + h) * 3 + 0]);
-      float *dst = p.out + (r0 + h) * D + 4 * grp;
+      float *slot = p.out + (r0 + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[h][dt] * gate;
+      for (int dt = 0; dt < DT; ++dt) store_partial4<D>(slot, 0, 16 * dt + 4 * grp, o[h][dt] * gate);
     }
   }
 }
@@ -353,10 +354,16 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
   u16x8 qf[G][DS];
   {
     const int64_t q0 = (row_pos(p.vmap, p.v0, tvalid ? t : 0) * p.hq + (int64_t)g * G) * D;
+    bool ovf = false;  // a query past fp16's range (flagged in the status word)
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) qf[h][ds] = tvalid ? bf2h8(q_frag_global(p.q + q0 + h * D, ds, lane)) : zero8();
+      for (int ds = 0; ds < DS; ++ds) {
+        qf[h][ds] = tvalid ? bf2h8(q_frag_global(p.q + q0 + h * D, ds, lane)) : zero8();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ovf |= h16_nonfinite(qf[h][ds][e]);
+      }
+    if (ovf && p.status) atomicOr(p.status, kStatusRange);
   }
 
   // ---- pass 1: log-sum-exp of every (query, head); keys only, 8-slot ring
@@ -452,15 +459,16 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
 #undef NSA_ISSUE_KV
 #undef NSA_ISSUE_K
 
-  // ---- epilogue: out = sigmoid(g_cmp) * o_cmp (first writer of vision rows)
+  // ---- epilogue: sigmoid(g_cmp) * o_cmp as the fp16 part 0 of the row's
+  // output slots (the selection kernel adds the branches and writes fp32)
   if (tvalid) {
     const int64_t r0w = row_pos(p.vmap, p.v0, t) * p.hq + (int64_t)g * G;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float gate = sigmoidf_(p.gates[(r0w + h) * 3 + 0]);
-      float *dst = p.out + (r0w + h) * D + 4 * grp;
+      float *slot = p.out + (r0w + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = o[h][dt] * gate;
+      for (int dt = 0; dt < DT; ++dt) store_partial4<D>(slot, 0, 16 * dt + 4 * grp, o[h][dt] * gate);
     }
   }
 }

@@ -175,4 +175,28 @@ __device__ __forceinline__ u16x8 bf2h8(u16x8 x) {
   return r;
 }
 
+// True when a 16-bit fp16 pattern is an infinity or NaN (exponent all ones):
+// a value that overflowed fp16's range on conversion.
+__device__ __forceinline__ bool h16_nonfinite(uint16_t h) { return (h & 0x7C00u) == 0x7C00u; }
+
+// ------------------------------------------------------ branch partials
+// Until the selection kernel writes a vision row's final output, the row's
+// fp32 output slot of D floats for head h holds two fp16 partials: the gated
+// compression-branch output in its first D halves (part 0) and the gated
+// window-branch output in its second D halves (part 1). Each kernel writes
+// only its part; the selection kernel's wave that owns the (row, head)
+// reads both, adds its own gated branch and overwrites the slot with the
+// fp32 sum, so the output is written once in fp32 and never read back.
+template <int D>
+__device__ __forceinline__ void store_partial4(float *slot, int part, int d, f32x4 v) {
+  const u16x4 h = {f2h_bits(v[0]), f2h_bits(v[1]), f2h_bits(v[2]), f2h_bits(v[3])};
+  *reinterpret_cast<u16x4 *>(reinterpret_cast<uint16_t *>(slot) + part * D + d) = h;
+}
+template <int D>
+__device__ __forceinline__ f32x4 load_partial4(const float *slot, int part, int d) {
+  const u16x4 h = __builtin_nontemporal_load(reinterpret_cast<const u16x4 *>(reinterpret_cast<const uint16_t *>(slot) + part * D + d));
+  return f32x4{static_cast<float>(__builtin_bit_cast(f16, h[0])), static_cast<float>(__builtin_bit_cast(f16, h[1])),
+               static_cast<float>(__builtin_bit_cast(f16, h[2])), static_cast<float>(__builtin_bit_cast(f16, h[3]))};
+}
+
 }  // namespace nsa

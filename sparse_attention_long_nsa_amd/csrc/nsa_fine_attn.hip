@@ -225,16 +225,13 @@ __device__ __forceinline__ void swa_body(const SwaParams &p, int g, int f, Ring4
                             lo = t - wnd + 1 - key0;
                             hi = tvalid ? t - key0 : -1;
                           });
-  if (tvalid) {
+  if (tvalid) {  // sigmoid(g_swa) * o_swa as the fp16 part 1 of the row's output slots
 #pragma unroll
     for (int h = 0; h < HW; ++h) {
       const float gate = sigmoidf_(p.gates[(qrow + h) * 3 + 2]);
-      float *dst = p.out + (qrow + h) * D + 4 * grp;
+      float *slot = p.out + (qrow + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        f32x4 *d4 = reinterpret_cast<f32x4 *>(dst + 16 * dt);
-        *d4 = *d4 + o[h][dt] * gate;
-      }
+      for (int dt = 0; dt < D / 16; ++dt) store_partial4<D>(slot, 1, 16 * dt + 4 * grp, o[h][dt] * gate);
     }
   }
 }

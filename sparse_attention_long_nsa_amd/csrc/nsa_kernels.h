@@ -31,6 +31,7 @@ struct PoolJob {
   const int32_t *rows = nullptr;  // pooled row i is x row rows[i] (or i)
   int64_t in_stride = kBlk;       // rows of x between the first rows of blocks
   int64_t out_stride = 1;         // output rows between consecutive blocks
+  int32_t *status = nullptr;      // workspace status word: kStatusRange on an fp16 overflow
 };
 
 struct CmpAttnParams {
@@ -47,6 +48,7 @@ struct CmpAttnParams {
   int n_vis, hq, hkv, n_frames;
   float sl2;               // softmax scale * log2(e)
   const int32_t *vmap = nullptr;  // vision row -> position (several vision runs)
+  int32_t *status = nullptr;  // workspace status word (kStatusRange)
 };
 
 struct TopkParams {
@@ -76,6 +78,8 @@ struct SelParams {
   int n_vis, hq, hkv, topk, n_frames;
   float sl2;
   const int32_t *vmap = nullptr;
+  int spin_limit = 1 << 22;      // bounded-wait rounds before a wave gives up
+  int32_t *status = nullptr;     // workspace status word (kStatusWaitGaveUp on give-up)
 };
 
 struct TextParams {
@@ -166,7 +170,7 @@ hipError_t launch_append_rows(const uint16_t *k_new, const uint16_t *v_new, uint
                               hipStream_t st);
 // fp32 -> bf16 high part (+ optional bf16 residual), or fp32 -> fp16.
 hipError_t launch_split_bf16(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t st);
-hipError_t launch_to_f16(const float *x, int64_t n, uint16_t *out, hipStream_t st);
+hipError_t launch_to_f16(const float *x, int64_t n, uint16_t *out, hipStream_t st, int32_t *status = nullptr);
 hipError_t launch_cmp_attn(const CmpAttnParams &p, int d, int G, bool split, hipStream_t st);
 hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st);
 // f16: q, k, v hold fp16 (else bf16; values are converted while staging)
@@ -179,13 +183,18 @@ hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st);
 hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
                              int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st,
                              int split_at = 0x7fffffff, int64_t jump = 0,
-                             const int32_t *rows = nullptr);
+                             const int32_t *rows = nullptr, int32_t *status = nullptr);
 // Writes the row maps of one mask slice: vmap[t] = position of vision row t,
 // tmap[r] = position of text row r, tnvb[r] = vision tokens before it.
 hipError_t launch_row_maps(const MaskSlice &m, int32_t *vmap, int32_t *tmap, int32_t *tnvb,
                            hipStream_t st);
 size_t packed_kv_block_elems(int d);  // elements of one packed (K, V^T) block
 hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream_t st);
+// Sets the workspace status word to zero (a one-thread kernel, so the call
+// stays free of memset nodes when captured into a graph).
+hipError_t launch_status_clear(int32_t *status, hipStream_t st);
+constexpr int32_t kStatusWaitGaveUp = 1;  // a bounded wait ran out: outputs are NaN
+constexpr int32_t kStatusRange = 2;       // a value the kernels use in fp16 overflowed fp16's range
 hipError_t launch_text_attn(const TextParams &p, int d, int G, bool f16, hipStream_t st);
 hipError_t launch_text_merge(const TextParams &p, int d, hipStream_t st);
 hipError_t launch_dense_attn(const DenseParams &p, int d, int G, bool f16, hipStream_t st);

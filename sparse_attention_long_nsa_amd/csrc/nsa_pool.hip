@@ -82,7 +82,11 @@ __device__ __forceinline__ void map_out(const PoolJob &jb, int64_t b, const floa
   const uint16_t hi = f2bf_bits(acc);
   if (jb.out_hi) jb.out_hi[dst] = hi;
   if (jb.out_lo) jb.out_lo[dst] = f2bf_bits(acc - bfbits2f(hi));
-  if (jb.out_h16) jb.out_h16[dst] = f2h_bits(acc);
+  if (jb.out_h16) {
+    const uint16_t h = f2h_bits(acc);
+    jb.out_h16[dst] = h;
+    if (jb.status && h16_nonfinite(h)) atomicOr(jb.status, kStatusRange);
+  }
   if (jb.out_f32) jb.out_f32[dst] = acc;
 }
 
@@ -175,7 +179,11 @@ __global__ __launch_bounds__(kMapThreads) void pool_map_kernel(PoolJob j0, PoolJ
       const uint16_t hi = f2bf_bits(acc[q]);
       if (jb.out_hi) jb.out_hi[dst] = hi;
       if (jb.out_lo) jb.out_lo[dst] = f2bf_bits(acc[q] - bfbits2f(hi));
-      if (jb.out_h16) jb.out_h16[dst] = f2h_bits(acc[q]);
+      if (jb.out_h16) {
+        const uint16_t h = f2h_bits(acc[q]);
+        jb.out_h16[dst] = h;
+        if (jb.status && h16_nonfinite(h)) atomicOr(jb.status, kStatusRange);
+      }
       if (jb.out_f32) jb.out_f32[dst] = acc[q];
     }
   }
@@ -209,12 +217,17 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(const float *__restrict
   }
 }
 
-// fp32 inputs -> fp16.
+// fp32 inputs -> fp16 (values past fp16's range flagged in *status).
 __global__ __launch_bounds__(256) void to_f16_kernel(const float *__restrict__ x, int64_t n,
-                                                     uint16_t *__restrict__ out) {
+                                                     uint16_t *__restrict__ out, int32_t *status) {
+  bool ovf = false;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    out[i] = f2h_bits(x[i]);
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint16_t h = f2h_bits(x[i]);
+    out[i] = h;
+    ovf |= h16_nonfinite(h);
+  }
+  if (ovf && status) atomicOr(status, kStatusRange);
 }
 
 }  // namespace
@@ -281,11 +294,11 @@ hipError_t launch_split_bf16(const float *x, int64_t n, uint16_t *hi, uint16_t *
   return hipGetLastError();
 }
 
-hipError_t launch_to_f16(const float *x, int64_t n, uint16_t *out, hipStream_t st) {
+hipError_t launch_to_f16(const float *x, int64_t n, uint16_t *out, hipStream_t st, int32_t *status) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n, out);
+  hipLaunchKernelGGL(to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n, out, status);
   return hipGetLastError();
 }
 

@@ -47,6 +47,13 @@ __global__ __launch_bounds__(kMaskWords) void row_map_kernel(MaskSlice m, int32_
 
 }  // namespace
 
+__global__ void status_clear_kernel(int32_t *status) { *status = 0; }
+
+hipError_t launch_status_clear(int32_t *status, hipStream_t st) {
+  hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(1), 0, st, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_row_maps(const MaskSlice &m, int32_t *vmap, int32_t *tmap, int32_t *tnvb,
                            hipStream_t st) {
   if (m.n <= 0) return hipSuccess;

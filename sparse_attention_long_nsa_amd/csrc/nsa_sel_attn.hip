@@ -25,7 +25,12 @@
 // Producer p issues block j into slot j % R once min(pass) >= j - R + 1, and
 // publishes a block after waiting for its own copies (in-order vmcnt).
 // Every wait is a bounded spin, so a broken protocol ends the kernel with
-// NaN outputs instead of a hang.
+// NaN outputs and a flag in the workspace status word instead of a hang.
+//
+// Output: the (row, head) slots of the output hold the fp16 partials of the
+// compression and window branches (written by their kernels); the consumer
+// wave that owns a slot reads both, adds its gated selection output and
+// writes the slot's final fp32 value, the only fp32 write of vision rows.
 #include "nsa_kernels.h"
 #include "nsa_tiles.h"
 
@@ -33,9 +38,11 @@ namespace nsa {
 
 namespace {
 
+#ifndef NSA_SEL_PREFETCH
+#define NSA_SEL_PREFETCH 0
+#endif
 constexpr int kSelMaxK = 64;
 constexpr int kSelMaxBlk = 8192;
-constexpr int kSpinLimit = 1 << 22;   // s_sleep(1) rounds, about 0.1 s
 constexpr float kRescaleSlack = 8.f;  // log2 units a running max may lag behind
 
 template <int D, int G>
@@ -53,7 +60,9 @@ struct SelCfg {
   static constexpr int NP = SE / 512;                 // 1-KB copy pieces per block
   static constexpr int PPP = NP / NPW;                // pieces per producer per block
   static constexpr int R = (D == 64) ? 8 : 4;         // ring slots
-  static constexpr int INFL = (63 / PPP < R) ? 63 / PPP : R;  // blocks in flight per producer
+  static constexpr int PF = NSA_SEL_PREFETCH;         // L2 prefetch distance past the ring (0: none)
+  static constexpr int OPB = PPP + (PF > 0 ? 2 : 0);  // memory ops per block per producer
+  static constexpr int INFL = (63 / OPB < R) ? 63 / OPB : R;  // blocks in flight per producer
   static_assert(NP % NPW == 0 && PPP % 4 == 0, "pieces split evenly, four per address set-up");
   static_assert(TOK <= 32 && NW <= 16, "workgroup shape");
 };
@@ -142,6 +151,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   __shared__ uint32_t ubits[kSelMaxBlk / 32];  // union as a bitmask over blocks
   __shared__ int16_t wpre[kSelMaxBlk / 32];    // union entries before each bitmask word
   __shared__ int pass_[NC], ready_[C::NPW];
+  __shared__ uint32_t junk[64];                // destination of the L2 prefetches (never read)
   __shared__ int tpos[TOK];                    // position of each token of the chunk
   __shared__ int n_union;
 
@@ -244,24 +254,39 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
           uint16_t *dst = ring + (issued % R) * C::SE + pw * C::PPP * 512;
           asm volatile("" ::: "memory");
           dma_pieces<C::PPP>(src, dst, lane);
+          if constexpr (C::PF > 0) {
+            // touch this producer's half of the block PF places past the
+            // ring's reach, one 4-byte load per 128-byte line, so that its
+            // copy later finds it in L2 (past the union's end: the current
+            // block again, to keep every step at OPB operations)
+            const int pos = issued + R - 1 + C::PF;
+            const int pb = pos < nU ? __builtin_amdgcn_readlane((pos >> 6) == (issued >> 6) ? ul : ul_next, pos & 63) : blk;
+            const uint16_t *ps = kvg + (int64_t)pb * C::SE + lane * 64;
+            __builtin_amdgcn_global_load_lds(ps, (lds_void *)junk, 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(ps + 4096, (lds_void *)junk, 4, 0, 0);
+          }
           issued = __builtin_amdgcn_readfirstlane(issued + 1);
           continue;
         }
       }
       if (issued > pub) {  // publish the oldest block in flight
-        wait_blocks<C::PPP>(issued - pub - 1);
+        wait_blocks<C::OPB>(issued - pub - 1);
         asm volatile("" ::: "memory");
         pub = __builtin_amdgcn_readfirstlane(pub + 1);
         if (lane == 0) lds_store(&ready_[pw], pub);
         asm volatile("" ::: "memory");
       } else {
         __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {  // consumers stalled: give up, release them
-          if (lane == 0) lds_store(&ready_[pw], nU);
+        if (++spins > p.spin_limit) {  // consumers stalled: give up, release them
+          if (lane == 0) {
+            lds_store(&ready_[pw], nU);
+            if (p.status) atomicOr(p.status, kStatusWaitGaveUp);
+          }
           break;
         }
       }
     }
+    wait_vm_c<0>();  // no copy into this workgroup's LDS outlives the wave
     return;
   }
 
@@ -340,7 +365,7 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
     };
     while (min_ready() <= u) {
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) { bad = true; break; }
+      if (++spins > p.spin_limit) { bad = true; break; }
     }
     asm volatile("" ::: "memory");
     const uint16_t *ks = ring + (u % R) * C::SE;
@@ -356,7 +381,10 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   }
   // all reads of ring slots have returned before the final release
   __builtin_amdgcn_s_waitcnt(0xC07F);
-  if (lane == 0) lds_store(&pass_[c], nU);
+  if (lane == 0) {
+    lds_store(&pass_[c], nU);
+    if (bad && p.status) atomicOr(p.status, kStatusWaitGaveUp);  // the caller can ask
+  }
 
   const int grp = lane >> 4;
 #pragma unroll
@@ -365,14 +393,21 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
     if (rowvalid[r]) {
       const int64_t qrow = (int64_t)tpos[c * TT + r * TP + tau] * p.hq + (int64_t)g * G + hh;
       const float gate = bad ? __builtin_nanf("") : sigmoidf_(p.gates[qrow * 3 + 1]) / L;
-      float *dst = p.out + qrow * D + 4 * grp;
+      float *slot = p.out + qrow * D;
+      // the slot's fp16 partials of the compression and window branches,
+      // read in full before the fp32 sum overwrites the slot (other lanes of
+      // this wave read bytes this lane writes): all loads return first
+      f32x4 part[D / 16];
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        // streaming read-modify-write of the output (non-temporal, so the
-        // output does not push the key tiles out of the last-level cache)
-        f32x4 *d4 = reinterpret_cast<f32x4 *>(dst + 16 * dt);
-        __builtin_nontemporal_store(__builtin_nontemporal_load(d4) + o[r][dt] * gate, d4);
-      }
+      for (int dt = 0; dt < D / 16; ++dt)
+        part[dt] = load_partial4<D>(slot, 0, 16 * dt + 4 * grp) + load_partial4<D>(slot, 1, 16 * dt + 4 * grp);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)  // streaming (non-temporal) final write
+        __builtin_nontemporal_store(part[dt] + o[r][dt] * gate,
+                                    reinterpret_cast<f32x4 *>(slot + 16 * dt + 4 * grp));
     }
   }
 }
@@ -388,7 +423,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict
                                                       const uint16_t *__restrict__ v, int64_t v0,
                                                       int n_vis, int split_at, int64_t jump, int hkv,
                                                       int n_frames, uint16_t *__restrict__ kv,
-                                                      const int32_t *__restrict__ rows) {
+                                                      const int32_t *__restrict__ rows, int32_t *status) {
   using T = PackedTile<D>;
   __shared__ uint16_t tile[kBlk][D + 2];
   const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
@@ -405,6 +440,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict
     }
     *reinterpret_cast<u16x8 *>(dst + r * D + 8 * T::template swz<2 * D>(r, c)) = val;
   }
+  bool ovf = false;  // a value past fp16's range (flagged in *status)
   for (int idx = tid; idx < kBlk * D; idx += 256) {
     const int key = idx / D, d = idx % D;
     const int t = b * kBlk + key;
@@ -413,9 +449,11 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict
       const int64_t src = rows ? (int64_t)rows[t] : v0 + t + (t >= split_at ? jump : 0);
       x = v[(src * hkv + g) * (int64_t)D + d];
       if (!F16) x = bf2h_bits(x);
+      ovf |= h16_nonfinite(x);
     }
     tile[key][d] = x;
   }
+  if (ovf && status) atomicOr(status, kStatusRange);
   __syncthreads();
   // V^T: row d, stored key slot s <- key vkey(s); chunk c at swz(d, c)
   for (int idx = tid; idx < D * (kBlk / 8); idx += 256) {
@@ -474,22 +512,22 @@ hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream
 
 hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
                              int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st,
-                             int split_at, int64_t jump, const int32_t *rows) {
+                             int split_at, int64_t jump, const int32_t *rows, int32_t *status) {
   const unsigned n = (unsigned)n_chunks * (unsigned)hkv;
   if (n == 0) return hipSuccess;
   if (d == 64) {
-    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<64, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows);
-    else hipLaunchKernelGGL((pack_kv_kernel<64, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows);
+    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<64, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows, status);
+    else hipLaunchKernelGGL((pack_kv_kernel<64, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows, status);
   } else {
-    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<128, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows);
-    else hipLaunchKernelGGL((pack_kv_kernel<128, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows);
+    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<128, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows, status);
+    else hipLaunchKernelGGL((pack_kv_kernel<128, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows, status);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st) {
   return launch_pack_tiles(p.k, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.kv, d, f16, st,
-                           0x7fffffff, 0, p.vmap);
+                           0x7fffffff, 0, p.vmap, p.status);
 }
 
 size_t packed_kv_block_elems(int d) { return (size_t)2 * kBlk * d; }

@@ -1,6 +1,8 @@
-// Top-k block selection kernel: one wave per (vision query, KV group) row of
-// the frame-packed group scores written by the compression kernel. The
-// selection itself is select_topk_row.
+// Top-k block selection kernel over the frame-packed group scores written
+// by the compression kernel (per frame f and KV group g a [64 tokens][f]
+// block of scores). One wave per (token, group) row; a workgroup holds
+// kWaves consecutive tokens of one (frame, group), heaviest frames first.
+// The selection itself is select_topk_row.
 #include "nsa_kernels.h"
 #include "nsa_select.h"
 
@@ -8,38 +10,44 @@ namespace nsa {
 
 namespace {
 
-constexpr int kWavesPerWG = 1;  // one wave per workgroup: early exits need no barrier care
+#ifndef NSA_TOPK_WAVES
+#define NSA_TOPK_WAVES 4
+#endif
+constexpr int kWaves = NSA_TOPK_WAVES;  // rows (one per wave) per workgroup
 
 template <int NPL>
-__global__ __launch_bounds__(64) void topk_kernel(TopkParams p) {
-  __shared__ uint32_t hist[256];
-  const int lane = threadIdx.x;
-  const int64_t wid = blockIdx.x;
-  const int t = (int)(wid / p.hkv);
-  const int g = (int)(wid % p.hkv);
-  if (t >= p.n_vis) return;
-  const int f = t / kBlk;  // own block == number of candidate blocks
-  int32_t *out = p.sel + ((int64_t)t * p.hkv + g) * p.k;
-  const float *row = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + (t - f * kBlk)) * f;
-  select_topk_row<NPL>(row, f, p.k, out, hist, lane);
+__global__ __launch_bounds__(64 * kWaves) void topk_kernel(TopkParams p, int n_frames) {
+  __shared__ uint32_t hist[kWaves][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar addressing
+  constexpr int per_group = kBlk / kWaves;
+  const int per_frame = p.hkv * per_group;
+  const int f = n_frames - 1 - (int)(blockIdx.x / per_frame);  // own block == number of candidates
+  const int rem = (int)(blockIdx.x % per_frame);
+  const int g = rem / per_group;
+  const int tl = (rem % per_group) * kWaves + wv;
+  if (f * kBlk + tl >= p.n_vis) return;
+  const float *row = p.gs + frame_off(f, p.hkv) + (int64_t)(g * kBlk + tl) * f;
+  select_topk_row<NPL>(row, f, p.k, p.sel + ((int64_t)(f * kBlk + tl) * p.hkv + g) * p.k, hist[wv], lane);
 }
 
 template <int NPL>
-hipError_t run(const TopkParams &p, hipStream_t st) {
-  const int64_t n = (int64_t)p.n_vis * p.hkv;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL((topk_kernel<NPL>), dim3((unsigned)n), dim3(64 * kWavesPerWG), 0, st, p);
+hipError_t run(const TopkParams &p, int n_frames, hipStream_t st) {
+  const int64_t n_wg = (int64_t)n_frames * p.hkv * (kBlk / kWaves);
+  if (n_wg == 0) return hipSuccess;
+  hipLaunchKernelGGL((topk_kernel<NPL>), dim3((unsigned)n_wg), dim3(64 * kWaves), 0, st, p, n_frames);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st) {
-  if (n_blk_max <= 64 * 4) return run<4>(p, st);
-  if (n_blk_max <= 64 * 16) return run<16>(p, st);
-  if (n_blk_max <= 64 * 32) return run<32>(p, st);
-  if (n_blk_max <= 64 * 64) return run<64>(p, st);
-  if (n_blk_max <= 64 * 128) return run<128>(p, st);
+  const int n_frames = (p.n_vis + kBlk - 1) / kBlk;
+  if (n_blk_max <= 64 * 4) return run<4>(p, n_frames, st);
+  if (n_blk_max <= 64 * 16) return run<16>(p, n_frames, st);
+  if (n_blk_max <= 64 * 32) return run<32>(p, n_frames, st);
+  if (n_blk_max <= 64 * 64) return run<64>(p, n_frames, st);
+  if (n_blk_max <= 64 * 128) return run<128>(p, n_frames, st);
   return hipErrorInvalidValue;
 }
 

@@ -410,3 +410,21 @@ def test_backward_validation_and_workspace():
     assert call_bwd(ds, m, ws_bytes=need - 1) == binding.NSA_ERR_WORKSPACE
     text_only = np.zeros(64, np.uint8)  # no vision rows: no selection needed
     assert bwd_ws(desc(n=64), text_only)[0] == binding.NSA_OK
+
+
+def test_workspace_status_and_spin_limit_arguments():
+    L = binding.lib()
+    flags = ctypes.c_int32(0)
+    assert L.nsa_workspace_status(None, None, ctypes.byref(flags)) == binding.NSA_ERR_INVALID_ARG
+    assert L.nsa_workspace_status(FAKE, None, None) == binding.NSA_ERR_INVALID_ARG
+    assert L.nsa_workspace_status(FAKE + 16, None, ctypes.byref(flags)) == binding.NSA_ERR_INVALID_ARG
+    assert L.nsa_debug_set_spin_limit(5) == binding.NSA_OK
+    assert L.nsa_debug_set_spin_limit(0) == binding.NSA_OK  # default restored
+    assert "bounded wait" in binding.status_string(binding.NSA_ERR_KERNEL)
+
+
+def test_prefill_workspace_starts_with_the_status_word():
+    # the status word takes the workspace's first 256-byte slot
+    one = vision_mask(1024, 0, 1024)
+    st, n = ws_size(desc(), one)
+    assert st == binding.NSA_OK and n % 256 == 0 and n >= 256
