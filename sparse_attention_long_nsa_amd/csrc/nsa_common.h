@@ -187,16 +187,21 @@ __device__ __forceinline__ bool h16_nonfinite(uint16_t h) { return (h & 0x7C00u)
 // only its part; the selection kernel's wave that owns the (row, head)
 // reads both, adds its own gated branch and overwrites the slot with the
 // fp32 sum, so the output is written once in fp32 and never read back.
+// Four partial values (dims d .. d+3, d a multiple of 4) move as one 8-byte
+// access of two 32-bit words, each holding two fp16 values (low half first).
 template <int D>
 __device__ __forceinline__ void store_partial4(float *slot, int part, int d, f32x4 v) {
-  const u16x4 h = {f2h_bits(v[0]), f2h_bits(v[1]), f2h_bits(v[2]), f2h_bits(v[3])};
-  *reinterpret_cast<u16x4 *>(reinterpret_cast<uint16_t *>(slot) + part * D + d) = h;
+  const uint2 w = {uint32_t(f2h_bits(v[0])) | (uint32_t(f2h_bits(v[1])) << 16),
+                   uint32_t(f2h_bits(v[2])) | (uint32_t(f2h_bits(v[3])) << 16)};
+  *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(slot) + part * D + d) = w;
+}
+__device__ __forceinline__ float h16_to_f32(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(f16, static_cast<uint16_t>(bits & 0xffffu)));
 }
 template <int D>
 __device__ __forceinline__ f32x4 load_partial4(const float *slot, int part, int d) {
-  const u16x4 h = __builtin_nontemporal_load(reinterpret_cast<const u16x4 *>(reinterpret_cast<const uint16_t *>(slot) + part * D + d));
-  return f32x4{static_cast<float>(__builtin_bit_cast(f16, h[0])), static_cast<float>(__builtin_bit_cast(f16, h[1])),
-               static_cast<float>(__builtin_bit_cast(f16, h[2])), static_cast<float>(__builtin_bit_cast(f16, h[3]))};
+  const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(slot) + part * D + d);
+  return f32x4{h16_to_f32(w.x), h16_to_f32(w.x >> 16), h16_to_f32(w.y), h16_to_f32(w.y >> 16)};
 }
 
 }  // namespace nsa

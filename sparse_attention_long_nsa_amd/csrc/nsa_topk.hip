@@ -11,7 +11,7 @@ namespace nsa {
 namespace {
 
 #ifndef NSA_TOPK_WAVES
-#define NSA_TOPK_WAVES 4
+#define NSA_TOPK_WAVES 1
 #endif
 constexpr int kWaves = NSA_TOPK_WAVES;  // rows (one per wave) per workgroup
 
