@@ -253,17 +253,16 @@ def run_gate_bench(shape, steps, warmup):
     return res
 
 
-BWD_SHAPE = dict(n_vis=4096, n_text_after=512)  # the first backward design is timed on a shorter context
+BWD_SHAPE = dict(n_vis=4096, n_text_after=512)  # a short context with the headline's heads, k and w
 
 
 def run_backward_bench(shape, steps, warmup):
-    """Backward pass (training) of the layer on 4,096 vision + 512 text
-    tokens with the headline's heads, k and w, reusing the forward's
+    """Backward pass (training) of the layer, reusing the forward's
     selection; reports time per call and the rate of algorithmic flops."""
     import torch
     from sparse_attention_long_nsa_amd import binding
     from sparse_attention_long_nsa_amd.inputs import make_output_grad, make_prefill_inputs
-    s = shape.replace(n_vis=BWD_SHAPE["n_vis"], n_text_before=0, n_text_after=BWD_SHAPE["n_text_after"])
+    s = shape
     inp = make_prefill_inputs(s, seed=0)
     dev = {k: torch.from_numpy(inp[k]).to("cuda:0").to(torch.bfloat16).contiguous()
            for k in ("q", "k", "v", "w_k", "w_v")}
@@ -336,6 +335,39 @@ def run_scaling_bench(shape, steps, warmup):
                              "text": ms_of("pack_text", "text_attn", "text_merge")}}
         rows.append(row)
         log(f"scaling {n_vis}: {ms:.3f} ms {row['branch_ms']}")
+    return rows
+
+
+def run_context_bench(presets, steps, warmup):
+    """Step time and per-branch split of other prefill workloads (each its
+    own k and w)."""
+    import torch
+    from sparse_attention_long_nsa_amd.inputs import PREFILL_PRESETS, make_prefill_inputs
+    rows = []
+    for name in presets:
+        s = PREFILL_PRESETS[name]
+        inp = make_prefill_inputs(s, seed=0)
+        dev = {k: torch.from_numpy(inp[k]).to("cuda:0").to(torch.bfloat16).contiguous()
+               for k in ("q", "k", "v", "w_k", "w_v")}
+        dev["gates"] = torch.from_numpy(inp["gates"]).to("cuda:0")
+        ms, kern, out = run_gpu(inp, dev, s.top_k, s.window, steps, warmup, True)
+        text_pos = np.nonzero(inp["is_vision"] == 0)[0]
+        fl = sum(v for kind, v in closed_form_work(s, text_pos).values() if kind == "flops")
+        del dev, out, inp
+        torch.cuda.empty_cache()
+
+        def ms_of(*names):
+            return round(sum(kern.get(n, (0.0, 0))[0] for n in names), 4)
+
+        row = {"workload": name, "n_vision": s.n_vis, "n_text": s.n_text, "top_k": s.top_k, "window": s.window,
+               "ms_per_step": round(ms, 4), "tokens_per_s": round(s.n_tokens / (ms * 1e-3), 1),
+               "mfma_peak_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "branch_ms": {"cmp": ms_of("cmp_pool", "pack_cmp", "cmp_attn"), "topk": ms_of("blk_score_topk"),
+                             "sel": ms_of("pack_kv", "sel_attn"), "swa": ms_of("swa_attn"),
+                             "text": ms_of("pack_text", "text_attn", "text_merge")},
+               "kernels_ms": {k: round(v[0], 4) for k, v in sorted(kern.items(), key=lambda x: -x[1][0])}}
+        rows.append(row)
+        log(f"context {name}: {ms:.3f} ms {row['branch_ms']}")
     return rows
 
 
@@ -565,15 +597,21 @@ def main():
 
     backward = None
     if not args.no_backward:
-        backward = run_backward_bench(shape, 3, 1)
+        short = shape.replace(n_vis=BWD_SHAPE["n_vis"], n_text_before=0, n_text_after=BWD_SHAPE["n_text_after"])
+        backward = run_backward_bench(short, 3, 1)
+        # the pages' training context (model card, "Training Details": 36K tokens)
+        backward["training_length"] = run_backward_bench(PREFILL_PRESETS["qwen_36k"], 2, 1)
 
     spans = None
     if not args.no_spans:
         spans = run_spans_bench(inp, shape, max(3, args.steps // 2), 1, ms)
 
-    scaling = None
+    # the pages' training length and the per-branch split workload (36,864
+    # and 65,536 vision + 512 text tokens, k 16, w 512), always; 16K..512K
+    # at the headline's k and w on request
+    scaling = run_context_bench(("qwen_36k", "qwen_64k"), max(3, args.steps // 2), 1)
     if args.scaling:
-        scaling = run_scaling_bench(shape, max(3, args.steps // 2), 1)
+        scaling += run_scaling_bench(shape, max(3, args.steps // 2), 1)
 
     # the published peak checked on this GPU with an MFMA-loop probe
     from sparse_attention_long_nsa_amd.profiling import mfma_peak

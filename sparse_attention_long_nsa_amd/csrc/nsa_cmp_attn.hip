@@ -34,10 +34,6 @@ namespace nsa {
 namespace {
 
 constexpr int kThreadsH = 256;  // 4 waves x 16 tokens
-#ifndef NSA_CMP_HEAD_SPLIT
-#define NSA_CMP_HEAD_SPLIT 1
-#endif
-constexpr bool kCmpHeadSplit = NSA_CMP_HEAD_SPLIT;
 constexpr int kBufWord3 = 0x00020000;  // buffer resource word 3 (raw, 32-bit) on gfx9
 
 // Folds four scaled logits (log2 units, -inf = masked) into a lane-partial
@@ -330,88 +326,6 @@ __device__ __forceinline__ void cmp_pass2_chunk(const uint16_t *ks, const uint16
   }
 }
 
-// Pass 2 of one chunk for the wave's NH heads: the PV products and, per
-// lane, the sum over those heads of the probabilities of its 16 (query,
-// block) pairs: gsum[2 ks2 + kk][i] is block c*64 + 32 ks2 + 16 kk + 4 grp + i.
-template <int D, int NH>
-__device__ __forceinline__ void cmp_pass2_chunk_hs(const uint16_t *ks, const uint16_t *vt, int c,
-                                                   const u16x8 (&qf)[NH][D / 32], f32x4 (&o)[NH][D / 16],
-                                                   const float (&nlse2)[NH], f32x4 (&gsum)[4], int nc_t,
-                                                   float sl2, int lane) {
-  const int grp = lane >> 4;
-#pragma unroll
-  for (int ks2 = 0; ks2 < 2; ++ks2) {
-    u16x8 kf[2][D / 32], vf[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) kf[kk][ds] = pk_k_frag<D>(ks, 2 * ks2 + kk, ds, lane);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = pk_v_frag<D>(vt, dt, ks2, lane);
-    const int b0 = c * kBlk + 32 * ks2 + 4 * grp;
-    f32x4 bias[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bias[kk][i] = (b0 + 16 * kk + i < nc_t) ? 0.f : -INFINITY;
-    f32x4 sc[2], sn[2];
-    gsum[2 * ks2] = zero4();
-    gsum[2 * ks2 + 1] = zero4();
-    cmp_scores<D, 2>(kf, qf[0], bias, sc);
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      if (h + 1 < NH) cmp_scores<D, 2>(kf, qf[h + 1], bias, sn);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[kk][i] = __builtin_amdgcn_exp2f(fmaf(sc[kk][i], sl2, nlse2[h]));
-        gsum[2 * ks2 + kk] += sc[kk];
-      }
-      const u16x8 pf = pack_p(sc[0], sc[1]);
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[h][dt] = mfma_f16(vf[dt], pf, o[h][dt]);
-      if (h + 1 < NH) {
-        sc[0] = sn[0];
-        sc[1] = sn[1];
-      }
-    }
-  }
-}
-
-// Group scores of one chunk: the waves of head parts 1.. hand their partial
-// sums to the part-0 wave of the same queries through LDS (xq: this query
-// group's exchange area), which adds them and stores the score rows. Every
-// wave of the workgroup calls it (it holds a barrier).
-template <int HP>
-__device__ __forceinline__ void cmp_scores_out(f32x4 (&gsum)[4], float (*xq)[16][64], int hp,
-                                               __amdgpu_buffer_rsrc_t gsr, int srow, int c, int f, int lane) {
-  if constexpr (HP > 1) {
-    if (hp > 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xq[hp - 1][4 * j + i][lane] = gsum[j][i];
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
-    bare_barrier();
-    if (hp > 0) return;
-#pragma unroll
-    for (int q = 0; q < HP - 1; ++q)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gsum[j][i] += xq[q][4 * j + i][lane];
-  }
-  const int grp = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = c * kBlk + 32 * (j >> 1) + 16 * (j & 1) + 4 * grp + i;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gsum[j][i]), gsr, b < f ? srow + 4 * b : 0x7ffffff0, 0, 0);
-    }
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p) {
   using T = PackedTile<D>;
@@ -559,185 +473,6 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
   }
 }
 
-// ---------------------------------------------------------------------------
-// Head-split variant (fp16 operands, packed chunks; used for 7 and 8 query
-// heads per KV group, where all heads in one wave leave one wave per SIMD). A workgroup takes half a frame (32 queries) of
-// one KV group; each of its waves owns 16 queries x two query heads, so its
-// query fragments and output accumulators take about a third of the register
-// file and two waves share each SIMD: one's exponentials overlap the other's
-// matrix products (a wave holding all seven heads fills the register file
-// alone). The group importance score sums the normalised probabilities over
-// the group's heads, which now live in different waves: per chunk, the waves
-// of head parts 1.. leave their partial sums in LDS and the part-0 wave of
-// the same 16 queries adds them and stores the score rows. An odd last head
-// part carries one real head and one whose probabilities are forced to zero.
-template <int D, int G>
-struct CmpHs {
-  static constexpr int HPW = 2;                  // heads per wave
-  static constexpr int HP = (G + HPW - 1) / HPW; // head parts
-  static constexpr int QG = 2;                   // 16-query groups per workgroup
-  static constexpr int NW = QG * HP;             // waves
-  static constexpr int NT = 64 * NW;
-  static constexpr int NP = PackedTile<D>::KE / 512;  // 1-KB pieces of a key (or value) tile
-  static constexpr bool ok = NP % NW == 0;            // the pieces split evenly over the waves
-  static constexpr int PK = ok ? NP / NW : 1;         // pieces per wave
-};
-
-template <int D, int G>
-__global__ __launch_bounds__((CmpHs<D, G>::NT)) void cmp_attn_hs_kernel(CmpAttnParams p) {
-  using T = PackedTile<D>;
-  using C = CmpHs<D, G>;
-  static_assert(C::ok, "tile pieces split evenly over the waves");
-  constexpr int KE = T::KE, SE = T::KE + T::VE;
-  constexpr int PK = C::PK, HPW = C::HPW, HP = C::HP;
-  constexpr int DS = D / 32, DT = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
-  __shared__ __attribute__((aligned(16))) uint16_t r4[KE], r5[KE], r6[KE], r7[KE];
-  // partial group scores of head parts 1.. for the part-0 wave: [qg][part][16 values][lane]
-  __shared__ float xs[C::QG][HP > 1 ? HP - 1 : 1][16][64];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qg = wv % C::QG, hp = wv / C::QG;
-  const int h0 = hp * HPW;                        // this wave's first head
-  const int nh = min(HPW, G - h0);                // real heads of this wave
-  const int row = lane & 15, grp = lane >> 4;
-  // workgroup -> (KV group, frame, half): KV group fastest, so each XCD keeps
-  // one group's compressed tiles in its L2; latest (heaviest) frames first
-  const int g = blockIdx.x % p.hkv;
-  const int rest = blockIdx.x / p.hkv;
-  const int f = p.n_frames - 1 - rest / 2;
-  const int half = rest % 2;
-  const int tq0 = f * kBlk + half * 32;           // first query of the workgroup
-  const int t = tq0 + qg * 16 + row;              // this lane's query (vision-local)
-  if (tq0 >= p.n_vis) return;                     // uniform: a half frame past the end
-  const bool tvalid = t < p.n_vis;
-  const int nc_t = tvalid ? (t + 1) / kBlk : 0;   // complete blocks visible to it
-  const int t_last = min(tq0 + 31, p.n_vis - 1);
-  const int nk = (t_last + 1) / kBlk;             // blocks any query of the workgroup sees
-  const int nch = (nk + kBlk - 1) / kBlk;         // packed chunks holding them
-  const int off = __builtin_amdgcn_readfirstlane(wv * PK * 512);  // wave-uniform, scalar
-  const uint16_t *cg = p.kvc + (int64_t)g * p.n_cch * SE + off;
-
-  u16x8 qf[HPW][DS];
-  {
-    const int64_t q0 = (row_pos(p.vmap, p.v0, tvalid ? t : 0) * p.hq + (int64_t)g * G + h0) * D;
-    bool ovf = false;  // a query past fp16's range (flagged in the status word)
-#pragma unroll
-    for (int h = 0; h < HPW; ++h)
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        qf[h][ds] = (tvalid && h < nh) ? bf2h8(q_frag_global(p.q + q0 + h * D, ds, lane)) : zero8();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ovf |= h16_nonfinite(qf[h][ds][e]);
-      }
-    if (ovf && p.status) atomicOr(p.status, kStatusRange);
-  }
-
-  // ---- pass 1: log-sum-exp of every (query, head); keys only, 8-slot ring
-  float m[HPW], l[HPW];
-#pragma unroll
-  for (int h = 0; h < HPW; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
-#define NSA_ISSUE_K(DST, C) dma_pieces<PK>(cg + (int64_t)(C) * SE, (DST) + off, lane)
-#define NSA_ISSUE_K_OR_PAD(DST, C) NSA_ISSUE_K(DST, ((C) < nch ? (C) : 0))
-#define NSA_P1_STEP(CUR, NXT)                                             \
-  {                                                                       \
-    wait_vm_c<6 * PK>();                                                  \
-    bare_barrier();                                                       \
-    NSA_ISSUE_K_OR_PAD(NXT, c + 7);                                       \
-    cmp_pass1_chunk<D, HPW>(CUR, c, qf, m, l, nc_t, p.sl2, lane);         \
-    if (++c >= nch) break;                                                \
-  }
-  if (nch > 0) {
-    NSA_ISSUE_K_OR_PAD(r0, 0);
-    NSA_ISSUE_K_OR_PAD(r1, 1);
-    NSA_ISSUE_K_OR_PAD(r2, 2);
-    NSA_ISSUE_K_OR_PAD(r3, 3);
-    NSA_ISSUE_K_OR_PAD(r4, 4);
-    NSA_ISSUE_K_OR_PAD(r5, 5);
-    NSA_ISSUE_K_OR_PAD(r6, 6);
-  }
-  for (int c = 0; c < nch;) {
-    NSA_P1_STEP(r0, r7)
-    NSA_P1_STEP(r1, r0)
-    NSA_P1_STEP(r2, r1)
-    NSA_P1_STEP(r3, r2)
-    NSA_P1_STEP(r4, r3)
-    NSA_P1_STEP(r5, r4)
-    NSA_P1_STEP(r6, r5)
-    NSA_P1_STEP(r7, r6)
-  }
-#undef NSA_P1_STEP
-#undef NSA_ISSUE_K_OR_PAD
-  float lse2[HPW], nlse2[HPW];
-#pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    const float M = grp_max(m[h]);
-    const float part = (m[h] == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - M);
-    const float L = grp_sum(part);
-    lse2[h] = (L > 0.f) ? M + log2f(L) : -INFINITY;
-    // -lse2 (0 where no block is visible: every score is masked); a head
-    // slot past the group's heads gets probability zero everywhere
-    nlse2[h] = h >= nh ? -INFINITY : (lse2[h] == -INFINITY) ? 0.f : -lse2[h];
-  }
-  if (tvalid && grp == 0) {
-#pragma unroll
-    for (int h = 0; h < HPW; ++h)
-      if (h < nh) p.lse[(int64_t)t * p.hq + g * G + h0 + h] = lse2[h] * (1.0f / kLog2e);
-  }
-
-  // ---- pass 2: probabilities -> o_cmp and partial group scores
-  f32x4 o[HPW][DT];
-#pragma unroll
-  for (int h = 0; h < HPW; ++h)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[h][dt] = zero4();
-  // score rows of the frame (64 rows of f floats, this half's 32 of them);
-  // stores past a row's end fall outside the resource and are dropped
-  const __amdgpu_buffer_rsrc_t gsr = __builtin_amdgcn_make_buffer_rsrc(
-      p.gs + frame_off(f, p.hkv) + (int64_t)g * kBlk * f, 0, kBlk * f * (int)sizeof(float), kBufWord3);
-  const int srow = (t - f * kBlk) * f * (int)sizeof(float);
-#define NSA_ISSUE_KV(DK, DV, C)                                           \
-  {                                                                       \
-    NSA_ISSUE_K(DK, C);                                                   \
-    dma_pieces<PK>(cg + (int64_t)(C) * SE + KE, (DV) + off, lane);        \
-  }
-  wait_vm_c<0>();  // no copy of pass 1 (padding included) still in flight
-  bare_barrier();  // every wave is done with the pass-1 slots
-  if (nch > 0) NSA_ISSUE_KV(r0, r1, 0);
-#define NSA_P2_STEP(CK, CV, NK, NV)                                       \
-  {                                                                       \
-    wait_vm_c<0>();                                                       \
-    bare_barrier();                                                       \
-    if (c + 1 < nch) NSA_ISSUE_KV(NK, NV, c + 1);                         \
-    f32x4 gsum[4];                                                        \
-    cmp_pass2_chunk_hs<D, HPW>(CK, CV, c, qf, o, nlse2, gsum, nc_t, p.sl2, lane); \
-    cmp_scores_out<HP>(gsum, xs[qg], hp, gsr, srow, c, f, lane);          \
-    if (++c >= nch) break;                                                \
-  }
-  for (int c = 0; c < nch;) {
-    NSA_P2_STEP(r0, r1, r2, r3)
-    NSA_P2_STEP(r2, r3, r0, r1)
-  }
-#undef NSA_P2_STEP
-#undef NSA_ISSUE_KV
-#undef NSA_ISSUE_K
-
-  // ---- epilogue: sigmoid(g_cmp) * o_cmp as the fp16 part 0 of the row's
-  // output slots (the selection kernel adds the branches and writes fp32)
-  if (tvalid) {
-    const int64_t r0w = row_pos(p.vmap, p.v0, t) * p.hq + (int64_t)g * G + h0;
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-      if (h >= nh) break;
-      const float gate = sigmoidf_(p.gates[(r0w + h) * 3 + 0]);
-      float *slot = p.out + (r0w + h) * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) store_partial4<D>(slot, 0, 16 * dt + 4 * grp, o[h][dt] * gate);
-    }
-  }
-}
-
 template <int D, int G, bool SPLIT>
 hipError_t run(const CmpAttnParams &p, hipStream_t st) {
   const unsigned nwg = (unsigned)p.n_frames * (unsigned)p.hkv;
@@ -746,11 +481,7 @@ hipError_t run(const CmpAttnParams &p, hipStream_t st) {
     hipLaunchKernelGGL((cmp_attn_kernel<D, G, true>), dim3(nwg), dim3(kThreadsH), 0, st, p);
   } else {
     if (!p.kvc && p.n_cch > 0) return hipErrorInvalidValue;
-    if constexpr (kCmpHeadSplit && G >= 7 && CmpHs<D, G>::ok) {
-      hipLaunchKernelGGL((cmp_attn_hs_kernel<D, G>), dim3(2 * nwg), dim3(CmpHs<D, G>::NT), 0, st, p);
-    } else {
-      hipLaunchKernelGGL((cmp_attn_dma_kernel<D, G>), dim3(nwg), dim3(kThreadsH), 0, st, p);
-    }
+    hipLaunchKernelGGL((cmp_attn_dma_kernel<D, G>), dim3(nwg), dim3(kThreadsH), 0, st, p);
   }
   return hipGetLastError();
 }

@@ -38,9 +38,6 @@ namespace nsa {
 
 namespace {
 
-#ifndef NSA_SEL_PREFETCH
-#define NSA_SEL_PREFETCH 0
-#endif
 constexpr int kSelMaxK = 64;
 constexpr int kSelMaxBlk = 8192;
 constexpr float kRescaleSlack = 8.f;  // log2 units a running max may lag behind
@@ -60,9 +57,7 @@ struct SelCfg {
   static constexpr int NP = SE / 512;                 // 1-KB copy pieces per block
   static constexpr int PPP = NP / NPW;                // pieces per producer per block
   static constexpr int R = (D == 64) ? 8 : 4;         // ring slots
-  static constexpr int PF = NSA_SEL_PREFETCH;         // L2 prefetch distance past the ring (0: none)
-  static constexpr int OPB = PPP + (PF > 0 ? 2 : 0);  // memory ops per block per producer
-  static constexpr int INFL = (63 / OPB < R) ? 63 / OPB : R;  // blocks in flight per producer
+  static constexpr int INFL = (63 / PPP < R) ? 63 / PPP : R;  // blocks in flight per producer
   static_assert(NP % NPW == 0 && PPP % 4 == 0, "pieces split evenly, four per address set-up");
   static_assert(TOK <= 32 && NW <= 16, "workgroup shape");
 };
@@ -151,7 +146,6 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   __shared__ uint32_t ubits[kSelMaxBlk / 32];  // union as a bitmask over blocks
   __shared__ int16_t wpre[kSelMaxBlk / 32];    // union entries before each bitmask word
   __shared__ int pass_[NC], ready_[C::NPW];
-  __shared__ uint32_t junk[64];                // destination of the L2 prefetches (never read)
   __shared__ int tpos[TOK];                    // position of each token of the chunk
   __shared__ int n_union;
 
@@ -254,23 +248,12 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
           uint16_t *dst = ring + (issued % R) * C::SE + pw * C::PPP * 512;
           asm volatile("" ::: "memory");
           dma_pieces<C::PPP>(src, dst, lane);
-          if constexpr (C::PF > 0) {
-            // touch this producer's half of the block PF places past the
-            // ring's reach, one 4-byte load per 128-byte line, so that its
-            // copy later finds it in L2 (past the union's end: the current
-            // block again, to keep every step at OPB operations)
-            const int pos = issued + R - 1 + C::PF;
-            const int pb = pos < nU ? __builtin_amdgcn_readlane((pos >> 6) == (issued >> 6) ? ul : ul_next, pos & 63) : blk;
-            const uint16_t *ps = kvg + (int64_t)pb * C::SE + lane * 64;
-            __builtin_amdgcn_global_load_lds(ps, (lds_void *)junk, 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(ps + 4096, (lds_void *)junk, 4, 0, 0);
-          }
           issued = __builtin_amdgcn_readfirstlane(issued + 1);
           continue;
         }
       }
       if (issued > pub) {  // publish the oldest block in flight
-        wait_blocks<C::OPB>(issued - pub - 1);
+        wait_blocks<C::PPP>(issued - pub - 1);
         asm volatile("" ::: "memory");
         pub = __builtin_amdgcn_readfirstlane(pub + 1);
         if (lane == 0) lds_store(&ready_[pw], pub);
