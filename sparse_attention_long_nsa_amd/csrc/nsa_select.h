@@ -45,7 +45,8 @@ __device__ __forceinline__ uint32_t kth_largest_lane(uint32_t v, int need) {
 // Selects for one row of f candidate scores (row[0..f-1], global or LDS):
 // out[0..k-2] = the top k-1 block indices ascending (fewer: all of them,
 // then -1 padding), out[k-1] = f (the own block). One wave; hist is a
-// 256-entry LDS scratch of the calling workgroup. NPL * 64 >= f.
+// 256-entry LDS scratch of the calling workgroup. NPL * 64 >= f; NPL loads
+// per lane are issued whatever f is.
 template <int NPL>
 __device__ __forceinline__ void select_topk_row(const float *row, int f, int k, int32_t *out, uint32_t *hist,
                                                 int lane) {
@@ -56,17 +57,15 @@ __device__ __forceinline__ void select_topk_row(const float *row, int f, int k, 
     return;
   }
 
-  // key = bits + 1 for candidates (so 0.0f still beats padding), 0 otherwise
+  // key = bits + 1 for candidates (so 0.0f still beats padding), 0 otherwise.
+  // Every load is issued before the first is used (no branch between them,
+  // so one wait covers all): lanes past the row re-read its last entry, so
+  // callers pick NPL close to ceil(f / 64).
   uint32_t key[NPL];
 #pragma unroll
-  for (int s = 0; s < NPL; ++s) {
-    const int e = s * 64 + lane;
-    key[s] = 0u;
-    if (s * 64 < f) {  // wave-uniform; lanes past the row re-read its last entry
-      const uint32_t bits = __float_as_uint(row[min(e, f - 1)]);
-      key[s] = e < f ? bits + 1u : 0u;
-    }
-  }
+  for (int s = 0; s < NPL; ++s) key[s] = __float_as_uint(row[min(s * 64 + lane, f - 1)]);
+#pragma unroll
+  for (int s = 0; s < NPL; ++s) key[s] = s * 64 + lane < f ? key[s] + 1u : 0u;
 
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   {
