@@ -195,8 +195,10 @@ nsa_status nsa_prefill_dense(const nsa_prefill_desc *desc, const void *q, const 
  * attention and both compression maps. Same descriptor and inputs as
  * nsa_prefill; supported: bf16, one vision run (text before and/or after),
  * the head sizes and limits of nsa_prefill; else NSA_ERR_UNSUPPORTED.
- * Arithmetic is fp32 throughout; dk, dv and the compressed-key gradients are
- * accumulated with float atomics, so their low bits vary from run to run.
+ * Arithmetic: fp16 operands on the matrix cores (q, k, v exactly; dout, the
+ * probabilities, the score gradients and the compressed keys / values
+ * rounded to fp16) with fp32 accumulation. Every gradient element is
+ * written by one thread in a fixed order, so results are bitwise repeatable.
  *   sel_idx   device [N_v, Hkv, top_k] int32 (may be NULL when N_v = 0): the
  *             forward's list (ascending, -1 padded, the own block last); any
  *             other contents give meaningless gradients, never an access

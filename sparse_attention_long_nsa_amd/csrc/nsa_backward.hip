@@ -5,40 +5,53 @@
 // q, k, v (all three branches and the text rows), the gate logits and both
 // compression maps.
 //
-// A first, plain design in fp32 on the vector units (no matrix cores):
-//   bwd_zero   clears the accumulated gradients
-//   bwd_pool   block means and compressed keys/values, fp32
-//   bwd_rows   one wave per (row, KV group) with all its query heads; per
-//              branch three passes over its keys, lane = key for dot
-//              products and lane = dimension for sums over keys: (1) max
-//              and sum of the exponentials, (2) output o and D = dO . o (and
-//              the gate gradient), (3) dS = P (dP - D): dq in registers,
-//              dk / dv (or the compressed dK / dV) summed over the heads and
-//              accumulated with float atomics
-//   bwd_cmp_w  dW = sum over blocks of dK_cmp x mean^T, and each block's
-//              W^T dK_cmp / 64 added to its 64 tokens' dk (dv likewise)
+// Every attention branch is differentiated the same way, on the matrix
+// cores (fp16 operands, fp32 accumulation), with each gradient element
+// written by exactly one thread and no atomics, so results are bitwise
+// repeatable:
+//   bwd_pool      block means and compressed keys / values (fp32, plus fp16
+//                 copies for the matrix cores)
+//   bwd_pack      per (64-key tile, KV group) four fp16 sections: K rows,
+//                 V rows, K^T and V^T (the transposed ones in the forward's
+//                 key-permuted layout), for the vision blocks, for every
+//                 position (text queries) and for the compressed keys
+//   bwd_selmask.. the tokens that chose each (group, block), ascending: a
+//                 bitmask over tokens, its row counts, their prefix sum and
+//                 the decoded lists
+//   bwd_q         query side, one wave per (tile of 16/G tokens, KV group):
+//                 per branch, pass 1 recomputes the branch's log-sum-exp and
+//                 output o (online softmax), giving D = dout . o and the gate
+//                 gradient; pass 2 forms dS = sigma P (dP - D) and
+//                 dq^T += K^T dS^T; dq is written once after all branches
+//   bwd_kv        key side, one workgroup per (64-key tile, KV group), a
+//                 wave per 16 keys: walks every query row that attends the
+//                 tile (window range, selection list, text rows) 32 rows at
+//                 a time; dV^T += dO^T P and dK^T += Q^T dS with the rows'
+//                 Q^T and dO^T staged transposed in LDS; dk, dv written once
+//   bwd_kvc /     the same for the compressed keys over chunks of 2,048
+//   bwd_creduce   query tokens, the chunks' partial sums then added in order
+//   bwd_cmp_w /   dW = sum over blocks of dK_cmp x mean^T, and each block's
+//   bwd_cmp_tok   W^T dK_cmp / 64 added to its 64 tokens' dk (dv likewise)
 #include "nsa_kernels.h"
 #include "nsa_index.h"
-#include "nsa_select.h"
+#include "nsa_tiles.h"
 
 namespace nsa {
 
 namespace {
 
-__device__ __forceinline__ float wsum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ float wmax(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
+constexpr int kSentinel = 0x7fffffff;
+constexpr int kChunkTok = 2048;  // query tokens per compressed-key partial
 
-__global__ void bwd_zero_kernel(float *a, int64_t n) {
+template <int D>
+struct BwdTile {
+  static constexpr int SEC = kBlk * D;  // elements per section
+  static constexpr int E = 4 * SEC;     // sections: K rows, V rows, K^T, V^T
+};
+
+__global__ void bwd_fill_kernel(uint32_t *a, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    a[i] = 0.f;
+    a[i] = 0u;
 }
 
 // One workgroup of D threads per (block, KV group): means of the block's 64
@@ -69,302 +82,679 @@ __global__ __launch_bounds__(D) void bwd_pool_kernel(BwdParams p) {
   }
   p.kc[ob] = yk;
   p.vc[ob] = yv;
+  p.kc16[ob] = f2h_bits(yk);
+  p.vc16[ob] = f2h_bits(yv);
 }
 
-// A branch's key set for one row: n keys; key i is row `row(i)` of either
-// the token arrays (bf16, gradients into dk / dv) or the compressed arrays
-// (fp32, gradients into dkc / dvc).
-struct KeySet {
-  int kind;      // 0 compressed blocks 0..n-1, 1 contiguous token rows, 2 selected blocks
-  int n;         // number of keys
-  int64_t row0;  // kind 1: first token row
-  const int32_t *blocks;  // kind 2: selected blocks (ascending, -1 pads)
-  int nsel, t;   // kind 2: entries, vision index of the query (keys j <= t)
+// Packs rows row0 .. row0 + n_rows - 1 of a [rows][Hkv][D] key and value
+// array (bf16, converted, or fp16) into backward tiles: tile i holds rows
+// row0 + 64 i .. +63 (zero past n_rows). One workgroup per (tile, group).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t *ksrc, const uint16_t *vsrc, int64_t row0,
+                                                       int64_t n_rows, int hkv, int n_tiles, uint16_t *dst) {
+  constexpr int SEC = BwdTile<D>::SEC, CH = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t st[2][kBlk][D + 8];
+  const int tile = blockIdx.x % n_tiles, g = blockIdx.x / n_tiles;
+  uint16_t *out = dst + ((int64_t)g * n_tiles + tile) * BwdTile<D>::E;
+  for (int idx = threadIdx.x; idx < 2 * kBlk * CH; idx += 256) {
+    const int w = idx / (kBlk * CH), r = (idx / CH) % kBlk, c = idx % CH;
+    const int64_t row = (int64_t)tile * kBlk + r;
+    u16x8 x = zero8();
+    if (row < n_rows) {
+      x = *reinterpret_cast<const u16x8 *>((w ? vsrc : ksrc) + ((row0 + row) * hkv + g) * D + 8 * c);
+      if constexpr (BF16) x = bf2h8(x);
+    }
+    *reinterpret_cast<u16x8 *>(&st[w][r][8 * c]) = x;
+    *reinterpret_cast<u16x8 *>(out + w * SEC + r * D + 8 * PackedTile<D>::template swz<2 * D>(r, c)) = x;
+  }
+  __syncthreads();
+  // transposed sections: row = dim, eight chunks of eight key slots
+  for (int idx = threadIdx.x; idx < 2 * D * 8; idx += 256) {
+    const int w = idx / (D * 8), r = (idx / 8) % D, c = idx % 8;
+    u16x8 x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = st[w][PackedTile<D>::vkey(8 * c + i)][r];
+    *reinterpret_cast<u16x8 *>(out + (2 + w) * SEC + r * kBlk + 8 * PackedTile<D>::template swz<2 * kBlk>(r, c)) = x;
+  }
+}
+
+// ------------------------------------------------- who chose which block
+// bit t of selmask[g][b] = vision token t has block b in its list (entries
+// outside 0 .. t / 64 are ignored, as on the query side).
+__global__ void bwd_selmask_kernel(BwdParams p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (t, g, e)
+  if (i >= p.n_vis * p.hkv * p.topk) return;
+  const int t = (int)(i / ((int64_t)p.hkv * p.topk));
+  const int g = (int)((i / p.topk) % p.hkv);
+  const int32_t b = p.sel[i];
+  if (!sel_entry_valid(b, t)) return;
+  atomicOr(&p.selmask[((int64_t)g * p.n_vtile + b) * p.mask_words + (t >> 5)], 1u << (t & 31));
+}
+
+// One wave per (group, block): number of tokens that chose it.
+__global__ __launch_bounds__(64) void bwd_selcount_kernel(BwdParams p) {
+  const int gb = blockIdx.x, lane = threadIdx.x;
+  const uint32_t *row = p.selmask + (int64_t)gb * p.mask_words;
+  int c = 0;
+  for (int w = lane; w < p.mask_words; w += 64) c += __popc(row[w]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 0) p.selcnt[gb] = c;
+}
+
+// Exclusive prefix sum of the counts (one workgroup): seloff[i] = sum of
+// counts before i, seloff[n] = the total.
+__global__ __launch_bounds__(256) void bwd_selscan_kernel(BwdParams p, int n) {
+  __shared__ int part[256];
+  const int tid = threadIdx.x, per = (n + 255) / 256;
+  const int a = min(n, tid * per), b = min(n, a + per);
+  int s = 0;
+  for (int i = a; i < b; ++i) s += p.selcnt[i];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    p.seloff[n] = run;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int i = a; i < b; ++i) {
+    p.seloff[i] = run;
+    run += p.selcnt[i];
+  }
+}
+
+// One wave per (group, block): writes the tokens of its bitmask row, in
+// ascending order, at its offset.
+__global__ __launch_bounds__(64) void bwd_selfill_kernel(BwdParams p) {
+  const int gb = blockIdx.x, lane = threadIdx.x;
+  const uint32_t *row = p.selmask + (int64_t)gb * p.mask_words;
+  int base = p.seloff[gb];
+  for (int w0 = 0; w0 < p.mask_words; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t bits = w < p.mask_words ? row[w] : 0u;
+    const int c = __popc(bits);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int at = base + incl - c;
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      p.selrows[at++] = 32 * w + bit;
+      bits &= bits - 1u;
+    }
+    base += __shfl(incl, 63);
+  }
+}
+
+// ------------------------------------------------------------ query side
+// Scores of one tile transposed: s[kt] = K_kt Q^T (16 keys x 16 rows each)
+// from the tile's section `sec` (K rows, or V rows for dP^T = V dO^T).
+template <int D>
+__device__ __forceinline__ void tile_scores(const uint16_t *sec, const u16x8 (&b)[D / 32], f32x4 (&s)[4],
+                                            int lane) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) s[kt] = zero4();
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) s[kt] = mfma_f16(pk_k_frag<D>(sec, kt, ds, lane), b[ds], s[kt]);
+}
+
+// Pass 1 over one tile: online max and sum of the row's exponentials
+// (log2 domain) and O^T += V^T P^T. valid(kt, i) says whether the row sees
+// key 16 kt + 4 (lane / 16) + i of the tile.
+template <int D, class Valid>
+__device__ __forceinline__ void q_pass1(const uint16_t *tile, const u16x8 (&qf)[D / 32], f32x4 (&oa)[D / 16],
+                                        float &m, float &l, float sl2, Valid valid, int lane) {
+  constexpr int SEC = BwdTile<D>::SEC;
+  f32x4 s[4];
+  tile_scores<D>(tile, qf, s, lane);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = valid(kt, i) ? s[kt][i] * sl2 : -INFINITY;
+      s[kt][i] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = grp_max(mx);
+  const float mn = fmaxf(m, mx);
+  const bool live = mn != -INFINITY;
+  const float alpha = live ? exp2f(m - mn) : 1.f;
+  l *= alpha;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) oa[dt] = oa[dt] * alpha;
+  float ls = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = live ? __builtin_amdgcn_exp2f(s[kt][i] - mn) : 0.f;
+      s[kt][i] = pv;
+      ls += pv;
+    }
+  l += ls;
+  m = mn;
+  const u16x8 pp[2] = {pack_p(s[0], s[1]), pack_p(s[2], s[3])};
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) oa[dt] = mfma_f16(pk_v_frag<D>(tile + 3 * SEC, dt, kh, lane), pp[kh], oa[dt]);
+}
+
+// Pass 2 over one tile: P from the row's log-sum-exp, dP^T = V dO^T,
+// dS = sig P (dP - dd), dq^T += K^T dS^T.
+template <int D, class Valid>
+__device__ __forceinline__ void q_pass2(const uint16_t *tile, const u16x8 (&qf)[D / 32], const u16x8 (&of)[D / 32],
+                                        f32x4 (&dqa)[D / 16], float lse2, float dd, float sig, float sl2,
+                                        Valid valid, int lane) {
+  constexpr int SEC = BwdTile<D>::SEC;
+  f32x4 s[4], dp[4];
+  tile_scores<D>(tile, qf, s, lane);
+  tile_scores<D>(tile + SEC, of, dp, lane);
+  const bool has = lse2 != -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = (has && valid(kt, i)) ? __builtin_amdgcn_exp2f(fmaf(s[kt][i], sl2, -lse2)) : 0.f;
+      s[kt][i] = sig * pv * (dp[kt][i] - dd);
+    }
+  const u16x8 pd[2] = {pack_p(s[0], s[1]), pack_p(s[2], s[3])};
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      dqa[dt] = mfma_f16(pk_v_frag<D>(tile + 2 * SEC, dt, kh, lane), pd[kh], dqa[dt]);
+}
+
+// Query rows of one wave: TP tokens x G heads (+ padding rows) of one KV
+// group; lane l owns row l % 16. TXT: text rows (index u among the text
+// tokens), else vision rows.
+template <int D, int G, bool TXT>
+struct QRows {
+  static constexpr int TP = 16 / G;
+  int tau, hh, grp, tok, hq;
+  bool rv;
+  int64_t pos, qrow;
+  __device__ QRows(const BwdParams &p, int qt, int g, int lane) {
+    const int r16 = lane & 15;
+    tau = r16 / G;
+    hh = r16 % G;
+    grp = lane >> 4;
+    const int n_tok = TXT ? (int)(p.n - p.n_vis) : (int)p.n_vis;
+    tok = qt * TP + tau;
+    rv = tau < TP && tok < n_tok;
+    const int tc = rv ? tok : 0;
+    pos = TXT ? (tc < p.v0 ? (int64_t)tc : (int64_t)tc + p.n_vis) : p.v0 + tc;
+    hq = g * G + hh;
+    qrow = pos * p.hq + hq;
+  }
 };
 
-// Token row of key i of a selected-block set (vision keys j <= t of the
-// selected blocks, in block order). The blocks come in ascending order,
-// -1 padded: every one but the last is a complete earlier block of 64 keys,
-// and the last is the query's own block, cut at t; so key i is key i % 64
-// of entry i / 64. Any other list (not the forward's) gives meaningless
-// gradients but no access outside the rows 0 .. t.
-__device__ __forceinline__ int64_t sel_row(const BwdParams &p, const KeySet &ks, int i) {
-  return p.v0 + sel_key_row(ks.blocks[i / kBlk], i % kBlk, ks.t);
+// The wave's two passes over one branch's key tiles (walk(f) calls
+// f(tile pointer, valid functor) for every tile, in the same order both
+// times), with the row statistics and gate gradient written in between.
+template <int D, class Walk>
+__device__ __forceinline__ void q_branch(const BwdParams &p, Walk walk, const u16x8 (&qf)[D / 32],
+                                         const u16x8 (&of)[D / 32], f32x4 (&dqa)[D / 16], bool rv,
+                                         int64_t qrow, float sig, float sl2, float *stat, float *dgate,
+                                         int lane) {
+  constexpr int DT = D / 16;
+  f32x4 oa[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oa[dt] = zero4();
+  float m = -INFINITY, l = 0.f;
+  walk([&](const uint16_t *tile, auto valid) { q_pass1<D>(tile, qf, oa, m, l, sl2, valid, lane); });
+  const float L = grp_sum(l);
+  const bool has = rv && L > 0.f;
+  const float lse2 = has ? m + __log2f(L) : -INFINITY;
+  const int grp = lane >> 4;
+  float part = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const f32x4 dv = rv ? *reinterpret_cast<const f32x4 *>(p.dout + qrow * D + 16 * dt + 4 * grp) : zero4();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part = fmaf(dv[i], oa[dt][i], part);
+  }
+  part = grp_sum(part);
+  const float dd = has ? part / L : 0.f;
+  if (rv && grp == 0) {
+    stat[0] = lse2;
+    stat[1] = dd;
+    if (dgate) *dgate = sig * (1.f - sig) * dd;
+  }
+  walk([&](const uint16_t *tile, auto valid) { q_pass2<D>(tile, qf, of, dqa, lse2, dd, sig, sl2, valid, lane); });
 }
 
-template <int D>
-struct KeyRef {
-  const uint16_t *kb = nullptr, *vb = nullptr;  // token rows (bf16)
-  const float *kf = nullptr, *vf = nullptr;     // compressed rows (fp32)
-  float *dk = nullptr, *dv = nullptr;
-  __device__ __forceinline__ float k(int j) const { return kb ? bfbits2f(kb[j]) : kf[j]; }
-  __device__ __forceinline__ float v(int j) const { return vb ? bfbits2f(vb[j]) : vf[j]; }
-  // eight consecutive values from j (a multiple of 8) in one or two loads
-  __device__ __forceinline__ static void load8(const uint16_t *b16, const float *f32, int j, float (&x)[8]) {
-    if (b16) {
-      const u16x8 u = *reinterpret_cast<const u16x8 *>(b16 + j);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = bfbits2f(u[e]);
-    } else {
-      const float4 a = *reinterpret_cast<const float4 *>(f32 + j), c = *reinterpret_cast<const float4 *>(f32 + j + 4);
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-      x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
-    }
-  }
-  __device__ __forceinline__ void k8(int j, float (&x)[8]) const { load8(kb, kf, j, x); }
-  __device__ __forceinline__ void v8(int j, float (&x)[8]) const { load8(vb, vf, j, x); }
-};
-
-template <int D>
-__device__ __forceinline__ KeyRef<D> key_ref(const BwdParams &p, const KeySet &ks, int i, int g) {
-  KeyRef<D> r;
-  if (ks.kind == 0) {
-    const int64_t o = ((int64_t)i * p.hkv + g) * D;
-    r.kf = p.kc + o;
-    r.vf = p.vc + o;
-    r.dk = p.dkc + o;
-    r.dv = p.dvc + o;
-  } else {
-    const int64_t row = ks.kind == 1 ? ks.row0 + i : sel_row(p, ks, i);
-    const int64_t o = (row * p.hkv + g) * D;
-    r.kb = p.k + o;
-    r.vb = p.v + o;
-    r.dk = p.dk + o;
-    r.dv = p.dv + o;
-  }
-  return r;
-}
-
-// One branch for one (row, KV group) held by one wave, all G query heads of
-// the group together so that every key row is read once for the group and
-// its gradients are summed over the heads before the atomics. q, dO (scaled
-// by each head's gate) and the raw output gradient sit in LDS; for sums over
-// keys lane l owns dims l + 64 e. Adds the branch's dq into dq and returns,
-// per head, the branch output's dot with the raw output gradient (go).
-template <int D, int G>
-__device__ void branch_bwd(const BwdParams &p, const KeySet &ks, int g, const float (*qs)[D],
-                           const float (*dos)[D], const float (*douts)[D], float (*pb)[64], float (*db)[64],
-                           float (&dq)[G][D / 64], float (&go)[G], int lane) {
-  constexpr int E = D / 64;
-#pragma unroll
-  for (int h = 0; h < G; ++h) go[h] = 0.f;
-  if (ks.n <= 0) return;
-  // (1) per head: max and sum of exp over the keys
-  float m[G], l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
-  for (int c0 = 0; c0 < ks.n; c0 += 64) {
-    const int i = c0 + lane;
-    float sc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) sc[h] = -INFINITY;
-    if (i < ks.n) {
-      const KeyRef<D> kr = key_ref<D>(p, ks, i, g);
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = 0.f;
-      for (int j0 = 0; j0 < D; j0 += 8) {
-        float kv[8];
-        kr.k8(j0, kv);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-          for (int h = 0; h < G; ++h) sc[h] = fmaf(qs[h][j0 + jj], kv[jj], sc[h]);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] *= p.scale;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mn = fmaxf(m[h], wmax(sc[h]));
-      l[h] = l[h] * expf(m[h] - mn) + wsum(i < ks.n ? expf(sc[h] - mn) : 0.f);
-      m[h] = mn;
-    }
-  }
-  float lse[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) lse[h] = m[h] + logf(l[h]);
-  // (2) o = sum p v per head, then D = dO . o and go = dout . o
-  float o[G][E];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[h][e] = 0.f;
-  for (int c0 = 0; c0 < ks.n; c0 += 64) {
-    const int i = c0 + lane;
-    float sc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) sc[h] = 0.f;
-    if (i < ks.n) {
-      const KeyRef<D> kr = key_ref<D>(p, ks, i, g);
-      for (int j0 = 0; j0 < D; j0 += 8) {
-        float kv[8];
-        kr.k8(j0, kv);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-          for (int h = 0; h < G; ++h) sc[h] = fmaf(qs[h][j0 + jj], kv[jj], sc[h]);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = expf(sc[h] * p.scale - lse[h]);
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) pb[h][lane] = sc[h];
-    wave_lds_sync();
-    const int nc = min(64, ks.n - c0);
-    for (int ii = 0; ii < nc; ++ii) {
-      const KeyRef<D> kr = key_ref<D>(p, ks, c0 + ii, g);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float vv = kr.v(lane + 64 * e);
-#pragma unroll
-        for (int h = 0; h < G; ++h) o[h][e] = fmaf(pb[h][ii], vv, o[h][e]);
-      }
-    }
-    wave_lds_sync();
-  }
-  float dd[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float a = 0.f, b = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      a = fmaf(dos[h][lane + 64 * e], o[h][e], a);
-      b = fmaf(douts[h][lane + 64 * e], o[h][e], b);
-    }
-    dd[h] = wsum(a);
-    go[h] = wsum(b);
-  }
-  // (3) dS = P (dP - D); dq += scale dS k; dk += scale sum_h dS q; dv += sum_h P dO
-  for (int c0 = 0; c0 < ks.n; c0 += 64) {
-    const int i = c0 + lane;
-    float pr[G], dsr[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) { pr[h] = 0.f; dsr[h] = 0.f; }
-    if (i < ks.n) {
-      const KeyRef<D> kr = key_ref<D>(p, ks, i, g);
-      float sc[G], dp[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) { sc[h] = 0.f; dp[h] = 0.f; }
-      for (int j0 = 0; j0 < D; j0 += 8) {
-        float kv[8], vv[8];
-        kr.k8(j0, kv);
-        kr.v8(j0, vv);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            sc[h] = fmaf(qs[h][j0 + jj], kv[jj], sc[h]);
-            dp[h] = fmaf(dos[h][j0 + jj], vv[jj], dp[h]);
-          }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        pr[h] = expf(sc[h] * p.scale - lse[h]);
-        dsr[h] = pr[h] * (dp[h] - dd[h]);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      pb[h][lane] = pr[h];
-      db[h][lane] = dsr[h];
-    }
-    wave_lds_sync();
-    const int nc = min(64, ks.n - c0);
-    for (int ii = 0; ii < nc; ++ii) {
-      const KeyRef<D> kr = key_ref<D>(p, ks, c0 + ii, g);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int j = lane + 64 * e;
-        const float kv = kr.k(j);
-        float gk = 0.f, gv = 0.f;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float ds = db[h][ii] * p.scale;
-          dq[h][e] = fmaf(ds, kv, dq[h][e]);
-          gk = fmaf(ds, qs[h][j], gk);
-          gv = fmaf(pb[h][ii], dos[h][j], gv);
-        }
-        unsafeAtomicAdd(kr.dk + j, gk);
-        unsafeAtomicAdd(kr.dv + j, gv);
-      }
-    }
-    wave_lds_sync();
-  }
-}
-
-constexpr int kBwdWavesG = 2;  // (row, group) items per workgroup
-
-template <int D, int G>
-__global__ __launch_bounds__(64 * kBwdWavesG) void bwd_rows_kernel(BwdParams p) {
-  constexpr int E = D / 64;
-  __shared__ float qs_[kBwdWavesG][G][D], dos_[kBwdWavesG][G][D], dout_[kBwdWavesG][G][D];
-  __shared__ float pb_[kBwdWavesG][G][64], db_[kBwdWavesG][G][64];
+template <int D, int G, bool TXT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_q_kernel(BwdParams p, int n_qt) {
+  using R = QRows<D, G, TXT>;
+  constexpr int TP = R::TP, DS = D / 32, DT = D / 16, SEC4 = BwdTile<D>::E;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t item = (int64_t)blockIdx.x * kBwdWavesG + wv;
-  if (item >= p.n * p.hkv) return;
-  const int64_t row = item / p.hkv;
-  const int g = (int)(item % p.hkv);
-  float(*qs)[D] = qs_[wv];
-  float(*dos)[D] = dos_[wv];
-  float(*douts)[D] = dout_[wv];
-  const int64_t oq = (row * p.hq + (int64_t)g * G) * D;  // the group's first head
+  // workgroups go to the eight XCDs round-robin: give each XCD one
+  // contiguous run of query tiles (neighbours share key tiles in its L2)
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int wg = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  const int item = wg * 4 + wv;
+  if (item >= n_qt * p.hkv) return;
+  const int g = item / n_qt, qt = item % n_qt;
+  const R r(p, qt, g, lane);
+  const float sl2 = p.scale * kLog2e;
+  u16x8 qf[DS], of[DS];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      qs[h][lane + 64 * e] = bfbits2f(p.q[oq + h * D + lane + 64 * e]);
-      douts[h][lane + 64 * e] = p.dout[oq + h * D + lane + 64 * e];
+  for (int ds = 0; ds < DS; ++ds) {
+    qf[ds] = r.rv ? bf2h8(q_frag_global(p.q + r.qrow * D, ds, lane)) : zero8();
+    u16x8 o = zero8();
+    if (r.rv) {
+      const float *src = p.dout + r.qrow * D + 32 * ds + 8 * r.grp;
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(src), b = *reinterpret_cast<const f32x4 *>(src + 4);
+      o = pack_p(a, b);
     }
-  float dq[G][E], go[G];
+    of[ds] = o;
+  }
+  f32x4 dqa[DT];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < E; ++e) dq[h][e] = 0.f;
-  const bool vis = row >= p.v0 && row < p.v0 + p.n_vis;
-  float *dg = p.dgate + (row * p.hq + (int64_t)g * G) * 3;
-  if (!vis) {  // text row: dense causal over every earlier position
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < E; ++e) dos[h][lane + 64 * e] = douts[h][lane + 64 * e];
-    wave_lds_sync();
-    KeySet ks{1, (int)(row + 1), 0, nullptr, 0, 0};
-    branch_bwd<D, G>(p, ks, g, qs, dos, douts, pb_[wv], db_[wv], dq, go, lane);
-    if (lane < 3 * G) dg[lane] = 0.f;
-  } else {
-    const int t = (int)(row - p.v0);
-    const float *gl = p.gates + (row * p.hq + (int64_t)g * G) * 3;
-    const int32_t *blocks = p.sel + ((int64_t)t * p.hkv + g) * p.topk;
-    int n_sel = 0;
-    for (int e = 0; e < p.topk; ++e) {
-      n_sel += sel_block_keys(blocks[e], t);
-    }
-    const int nw = min(p.window, t + 1);
-#pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      const KeySet ks = c == 0 ? KeySet{0, (t + 1) / kBlk, 0, nullptr, 0, 0}
-                      : c == 1 ? KeySet{2, n_sel, 0, blocks, p.topk, t}
-                               : KeySet{1, nw, p.v0 + t - nw + 1, nullptr, 0, 0};
-      float sg[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) sg[h] = 1.f / (1.f + expf(-gl[h * 3 + c]));
-      wave_lds_sync();
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < E; ++e) dos[h][lane + 64 * e] = sg[h] * douts[h][lane + 64 * e];
-      wave_lds_sync();
-      branch_bwd<D, G>(p, ks, g, qs, dos, douts, pb_[wv], db_[wv], dq, go, lane);
-      if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) dg[h * 3 + c] = go[h] * sg[h] * (1.f - sg[h]);
+  for (int dt = 0; dt < DT; ++dt) dqa[dt] = zero4();
+  const int n_tok = TXT ? (int)(p.n - p.n_vis) : (int)p.n_vis;
+  const int t_first = qt * TP, t_last = min(qt * TP + TP, n_tok) - 1;
+  const int grp = r.grp, tok = r.tok;
+
+  if constexpr (TXT) {
+    // dense causal over every earlier position
+    const int64_t pos_last = t_last < p.v0 ? (int64_t)t_last : (int64_t)t_last + p.n_vis;
+    const int64_t mypos = r.pos;
+    const int n_tiles = (int)(pos_last / kBlk) + 1;
+    auto walk = [&](auto f) {
+      for (int tl = 0; tl < n_tiles; ++tl) {
+        const int64_t k0 = (int64_t)tl * kBlk + 4 * grp;
+        f(p.tile_p + ((int64_t)g * p.n_ptile + tl) * SEC4,
+          [&](int kt, int i) { return k0 + 16 * kt + i <= mypos; });
       }
+    };
+    q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, 1.f, sl2, p.tstat + ((int64_t)tok * p.hq + r.hq) * 2, nullptr,
+                lane);
+    if (r.rv && grp == 0) {
+#pragma unroll
+      for (int c = 0; c < 3; ++c) p.dgate[r.qrow * 3 + c] = 0.f;
+    }
+  } else {
+    float *stat = p.vstat + ((int64_t)(r.rv ? tok : 0) * p.hq + r.hq) * 6;
+    float *dg = p.dgate + r.qrow * 3;
+    float sig[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) sig[c] = r.rv ? sigmoidf_(p.gates[r.qrow * 3 + c]) : 0.f;
+    // compression: compressed keys b with (b + 1) 64 <= t + 1
+    {
+      const int nc = (t_last + 1) / kBlk;
+      const int n_tiles = (nc + kBlk - 1) / kBlk;
+      auto walk = [&](auto f) {
+        for (int tl = 0; tl < n_tiles; ++tl) {
+          const int b0 = tl * kBlk + 4 * grp;
+          f(p.tile_c + ((int64_t)g * p.n_ctile + tl) * SEC4,
+            [&](int kt, int i) { return (b0 + 16 * kt + i + 1) * kBlk <= tok + 1; });
+        }
+      };
+      q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[0], sl2, stat, dg, lane);
+    }
+    // selection: the union of the tile's tokens' lists, each row masked to
+    // its own token's blocks (keys j <= t)
+    {
+      int lst[TP];
+#pragma unroll
+      for (int q = 0; q < TP; ++q) {
+        const int tq = t_first + q;
+        int b = kSentinel;
+        if (tq <= t_last && lane < p.topk) {
+          const int32_t e = p.sel[((int64_t)tq * p.hkv + g) * p.topk + lane];
+          b = sel_entry_valid(e, tq) ? (int)e : kSentinel;
+        }
+        lst[q] = b;
+      }
+      const int tau = r.tau;
+      auto walk = [&](auto f) {
+        int cur[TP], nxt[TP];
+#pragma unroll
+        for (int q = 0; q < TP; ++q) {
+          cur[q] = 0;
+          nxt[q] = __builtin_amdgcn_readlane(lst[q], 0);
+        }
+        for (;;) {
+          int u = kSentinel;
+#pragma unroll
+          for (int q = 0; q < TP; ++q) u = min(u, nxt[q]);
+          if (u == kSentinel) break;
+          uint32_t need = 0u;
+#pragma unroll
+          for (int q = 0; q < TP; ++q) {
+            if (nxt[q] == u) {
+              need |= 1u << q;
+              ++cur[q];
+              nxt[q] = cur[q] < p.topk ? __builtin_amdgcn_readlane(lst[q], cur[q]) : kSentinel;
+            }
+          }
+          const bool rowneed = r.rv && ((need >> tau) & 1u);
+          const int j0 = u * kBlk + 4 * grp;
+          f(p.tile_v + ((int64_t)g * p.n_vtile + u) * SEC4,
+            [&](int kt, int i) { return rowneed && j0 + 16 * kt + i <= tok; });
+        }
+      };
+      q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[1], sl2, stat + 2, dg + 1, lane);
+    }
+    // sliding window: keys t - w < j <= t
+    {
+      const int lo = max(0, t_first - p.window + 1) / kBlk, hi = t_last / kBlk;
+      const int w = p.window;
+      auto walk = [&](auto f) {
+        for (int tl = lo; tl <= hi; ++tl) {
+          const int j0 = tl * kBlk + 4 * grp;
+          f(p.tile_v + ((int64_t)g * p.n_vtile + tl) * SEC4, [&](int kt, int i) {
+            const int j = j0 + 16 * kt + i;
+            return j <= tok && j > tok - w;
+          });
+        }
+      };
+      q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[2], sl2, stat + 4, dg + 2, lane);
     }
   }
+  if (r.rv) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4 *>(p.dq + r.qrow * D + 16 * dt + 4 * grp) = dqa[dt] * p.scale;
+  }
+}
+
+// -------------------------------------------------------------- key side
+// Query tokens walked by a key-side workgroup: tokens a + i (range) or
+// list[i], i < n; `mask` picks the visibility rule, `br` the branch whose
+// statistics and gate apply.
+enum { kMaskWin = 0, kMaskSel = 1, kMaskAll = 2, kMaskTxt = 3, kMaskCmp = 4 };
+struct TokSrc {
+  int a, n;
+  const int32_t *list;
+  int mask, br;  // br: 0..2 vision branch, 3 text rows
+};
+
+// Rows of one step (32 at most: TS tokens x G heads), staged in LDS by the
+// whole workgroup: row-major fp16 copies of q and dout (A operands of S and
+// dP) and transposed copies whose key slots follow the permutation of the
+// P / dS B operand (slot 8 j + i <- row 4 j + i for i < 4, 16 + 4 j + i - 4
+// for i >= 4), plus each row's statistics.
+template <int D>
+struct KvStage {
+  static constexpr int RS = D + 8, TS_ = 40;
+  uint16_t qs[32][RS], ds_[32][RS];
+  uint16_t qt[D][TS_], dt_[D][TS_];
+  float l2[32], dd[32], sig[32];
+  int tok[32];
+};
+
+__device__ __forceinline__ int row_slot(int r) {
+  return r < 16 ? 8 * (r >> 2) + (r & 3) : 8 * ((r - 16) >> 2) + 4 + ((r - 16) & 3);
+}
+
+template <int D, int G>
+__device__ __forceinline__ void kv_stage(const BwdParams &p, KvStage<D> &sm, const TokSrc &src, int step, int g,
+                                         int tid) {
+  constexpr int TS = 32 / G, PER = D / 8;  // tokens per step, dims per thread
+  const int r = tid >> 3, seg = tid & 7;
+  const int tau = r / G, hh = r % G;
+  const int i = step * TS + tau;
+  const bool ok = r < TS * G && i < src.n;
+  int tok = -1;
+  int64_t qrow = 0;
+  if (ok) {
+    tok = src.list ? src.list[i] : src.a + i;
+    const int64_t pos = src.br == 3 ? (tok < p.v0 ? (int64_t)tok : (int64_t)tok + p.n_vis) : p.v0 + tok;
+    qrow = pos * p.hq + g * G + hh;
+  }
+  uint16_t qv[PER], dv[PER];
 #pragma unroll
-    for (int e = 0; e < E; ++e) p.dq[oq + h * D + lane + 64 * e] = dq[h][e];
+  for (int c = 0; c < PER / 8; ++c) {
+    u16x8 q8 = zero8();
+    f32x4 a = zero4(), b = zero4();
+    if (ok) {
+      q8 = bf2h8(*reinterpret_cast<const u16x8 *>(p.q + qrow * D + seg * PER + 8 * c));
+      a = *reinterpret_cast<const f32x4 *>(p.dout + qrow * D + seg * PER + 8 * c);
+      b = *reinterpret_cast<const f32x4 *>(p.dout + qrow * D + seg * PER + 8 * c + 4);
+    }
+    const u16x8 d8 = pack_p(a, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[8 * c + e] = q8[e];
+      dv[8 * c + e] = d8[e];
+    }
+    *reinterpret_cast<u16x8 *>(&sm.qs[r][seg * PER + 8 * c]) = q8;
+    *reinterpret_cast<u16x8 *>(&sm.ds_[r][seg * PER + 8 * c]) = d8;
+  }
+  const int sl = row_slot(r);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    sm.qt[seg * PER + e][sl] = qv[e];
+    sm.dt_[seg * PER + e][sl] = dv[e];
+  }
+  if (seg == 0) {
+    float l2 = INFINITY, dd = 0.f, sg = 0.f;
+    if (ok) {
+      const int hq = g * G + hh;
+      if (src.br == 3) {
+        const float *st = p.tstat + ((int64_t)tok * p.hq + hq) * 2;
+        l2 = st[0];
+        dd = st[1];
+        sg = 1.f;
+      } else {
+        const float *st = p.vstat + ((int64_t)tok * p.hq + hq) * 6 + 2 * src.br;
+        l2 = st[0];
+        dd = st[1];
+        sg = sigmoidf_(p.gates[qrow * 3 + src.br]);
+      }
+      if (l2 == -INFINITY) {  // the row has no keys in this branch
+        l2 = INFINITY;
+        sg = 0.f;
+      }
+    }
+    sm.l2[r] = l2;
+    sm.dd[r] = dd;
+    sm.sig[r] = sg;
+    sm.tok[r] = tok;
+  }
+}
+
+// One step for one wave (16 keys of the tile): kf / vf hold the keys' K and
+// V rows as B operands; key is this lane's key index in the mask's space.
+template <int D>
+__device__ __forceinline__ void kv_step(const KvStage<D> &sm, const u16x8 (&kf)[D / 32], const u16x8 (&vf)[D / 32],
+                                        f32x4 (&dkt)[D / 16], f32x4 (&dvt)[D / 16], int key, int mask, int window,
+                                        float sl2, int lane) {
+  const int r16 = lane & 15, grp = lane >> 4;
+  f32x4 s[2], dp[2];
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs) {
+    s[rs] = zero4();
+    dp[rs] = zero4();
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const u16x8 qa = *reinterpret_cast<const u16x8 *>(&sm.qs[16 * rs + r16][32 * ds + 8 * grp]);
+      const u16x8 da = *reinterpret_cast<const u16x8 *>(&sm.ds_[16 * rs + r16][32 * ds + 8 * grp]);
+      s[rs] = mfma_f16(qa, kf[ds], s[rs]);
+      dp[rs] = mfma_f16(da, vf[ds], dp[rs]);
+    }
+  }
+  f32x4 pm[2], dsm[2];
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rs + 4 * grp + i;
+      const int t = sm.tok[row];
+      bool ok;
+      switch (mask) {
+        case kMaskWin: ok = t >= 0 && key <= t && key > t - window; break;
+        case kMaskSel: ok = t >= 0 && key <= t; break;
+        case kMaskAll: ok = t >= 0; break;
+        case kMaskTxt: ok = t >= 0 && key <= t; break;
+        default: ok = t >= 0 && (key + 1) * kBlk <= t + 1; break;  // compressed key
+      }
+      // dO of the branch is sig * dout: dV takes sig P against the staged dout
+      const float pv = ok ? sm.sig[row] * __builtin_amdgcn_exp2f(fmaf(s[rs][i], sl2, -sm.l2[row])) : 0.f;
+      pm[rs][i] = pv;
+      dsm[rs][i] = pv * (dp[rs][i] - sm.dd[row]);
+    }
+  const u16x8 pp = pack_p(pm[0], pm[1]), pd = pack_p(dsm[0], dsm[1]);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const u16x8 da = *reinterpret_cast<const u16x8 *>(&sm.dt_[16 * dt + r16][8 * grp]);
+    const u16x8 qa = *reinterpret_cast<const u16x8 *>(&sm.qt[16 * dt + r16][8 * grp]);
+    dvt[dt] = mfma_f16(da, pp, dvt[dt]);
+    dkt[dt] = mfma_f16(qa, pd, dkt[dt]);
+  }
+}
+
+// Walks one token source: stage, then every wave's step, 32 rows at a time.
+template <int D, int G>
+__device__ __forceinline__ void kv_walk(const BwdParams &p, KvStage<D> &sm, const TokSrc &src, int g,
+                                        const u16x8 (&kf)[D / 32], const u16x8 (&vf)[D / 32], f32x4 (&dkt)[D / 16],
+                                        f32x4 (&dvt)[D / 16], int key, float sl2, int tid) {
+  constexpr int TS = 32 / G;
+  const int n_steps = (src.n + TS - 1) / TS;
+  for (int st = 0; st < n_steps; ++st) {
+    kv_stage<D, G>(p, sm, src, st, g, tid);
+    __syncthreads();
+    kv_step<D>(sm, kf, vf, dkt, dvt, key, src.mask, p.window, sl2, tid & 63);
+    __syncthreads();
+  }
+}
+
+// Key rows of the wave's 16 keys as B operands (lane: key l % 16, dims
+// 32 ds + 8 (l / 16) .. +7), fp16.
+template <int D, bool BF16>
+__device__ __forceinline__ void kv_keys(const uint16_t *kb, const uint16_t *vb, int64_t row, bool valid, int hkv,
+                                        int g, u16x8 (&kf)[D / 32], u16x8 (&vf)[D / 32], int lane) {
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) {
+    u16x8 a = zero8(), b = zero8();
+    if (valid) {
+      const int64_t o = (row * hkv + g) * D + 32 * ds + 8 * (lane >> 4);
+      a = *reinterpret_cast<const u16x8 *>(kb + o);
+      b = *reinterpret_cast<const u16x8 *>(vb + o);
+      if constexpr (BF16) {
+        a = bf2h8(a);
+        b = bf2h8(b);
+      }
+    }
+    kf[ds] = a;
+    vf[ds] = b;
+  }
+}
+
+// Vision blocks (workgroups 0 .. n_vtile Hkv - 1) then text tiles of 64
+// text tokens: dk and dv of the tile's rows from every query that sees them.
+template <int D, int G>
+__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
+  constexpr int DS = D / 32, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) KvStage<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n_vwg = p.n_vtile * p.hkv;
+  const bool vis = (int)blockIdx.x < n_vwg;
+  const int id = vis ? (int)blockIdx.x : (int)blockIdx.x - n_vwg;
+  const int tl = id / p.hkv, g = id % p.hkv;
+  const int n_text = (int)(p.n - p.n_vis);
+  const int key = tl * kBlk + 16 * wv + (lane & 15);  // vision index or text index
+  const bool kvalid = vis ? key < p.n_vis : key < n_text;
+  const int64_t krow = vis ? p.v0 + key : (key < p.v0 ? (int64_t)key : (int64_t)key + p.n_vis);
+  u16x8 kf[DS], vf[DS];
+  kv_keys<D, true>(p.k, p.v, krow, kvalid, p.hkv, g, kf, vf, lane);
+  f32x4 dkt[DT], dvt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dkt[dt] = zero4();
+    dvt[dt] = zero4();
+  }
+  const float sl2 = p.scale * kLog2e;
+  if (vis) {
+    const int a = tl * kBlk;
+    const int b = (int)min((int64_t)a + kBlk + p.window - 1, p.n_vis);
+    kv_walk<D, G>(p, sm, TokSrc{a, b - a, nullptr, kMaskWin, 2}, g, kf, vf, dkt, dvt, key, sl2, tid);
+    const int gb = g * p.n_vtile + tl;
+    const int s0 = p.seloff[gb];
+    kv_walk<D, G>(p, sm, TokSrc{0, p.seloff[gb + 1] - s0, p.selrows + s0, kMaskSel, 1}, g, kf, vf, dkt, dvt, key,
+                  sl2, tid);
+    if (n_text > p.v0)  // text rows after the vision run see every vision key
+      kv_walk<D, G>(p, sm, TokSrc{(int)p.v0, n_text - (int)p.v0, nullptr, kMaskAll, 3}, g, kf, vf, dkt, dvt, key,
+                    sl2, tid);
+  } else {
+    kv_walk<D, G>(p, sm, TokSrc{tl * kBlk, n_text - tl * kBlk, nullptr, kMaskTxt, 3}, g, kf, vf, dkt, dvt, key, sl2,
+                  tid);
+  }
+  if (kvalid) {
+    const int grp = lane >> 4;
+    float *dk = p.dk + (krow * p.hkv + g) * D, *dv = p.dv + (krow * p.hkv + g) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      *reinterpret_cast<f32x4 *>(dk + 16 * dt + 4 * grp) = dkt[dt] * p.scale;
+      *reinterpret_cast<f32x4 *>(dv + 16 * dt + 4 * grp) = dvt[dt];
+    }
+  }
+}
+
+// Compressed keys: workgroup (tile c, chunk, group) takes the vision tokens
+// of its chunk that see any key of the tile and writes the partial
+// gradients of the tile's 64 compressed keys.
+template <int D, int G>
+__global__ __launch_bounds__(256) void bwd_kvc_kernel(BwdParams p) {
+  constexpr int DS = D / 32, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) KvStage<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = blockIdx.x % p.hkv, chunk = (blockIdx.x / p.hkv) % p.n_chunk, c = blockIdx.x / (p.hkv * p.n_chunk);
+  const int t_min = (c * kBlk + 1) * kBlk - 1;  // first token that sees the tile's first key
+  const int a = max(chunk * kChunkTok, t_min), b = (int)min((int64_t)(chunk + 1) * kChunkTok, p.n_vis);
+  if (a >= b) return;  // uniform: the reduction skips this chunk
+  const int key = c * kBlk + 16 * wv + (lane & 15);
+  const bool kvalid = key < p.n_blk;
+  u16x8 kf[DS], vf[DS];
+  kv_keys<D, false>(p.kc16, p.vc16, key, kvalid, p.hkv, g, kf, vf, lane);
+  f32x4 dkt[DT], dvt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dkt[dt] = zero4();
+    dvt[dt] = zero4();
+  }
+  kv_walk<D, G>(p, sm, TokSrc{a, b - a, nullptr, kMaskCmp, 0}, g, kf, vf, dkt, dvt, key, p.scale * kLog2e, tid);
+  const int grp = lane >> 4;
+  float *dst = p.cpart + (((int64_t)c * p.n_chunk + chunk) * p.hkv + g) * 2 * kBlk * D;
+  const int kr = 16 * wv + (lane & 15);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    *reinterpret_cast<f32x4 *>(dst + kr * D + 16 * dt + 4 * grp) = dkt[dt] * p.scale;
+    *reinterpret_cast<f32x4 *>(dst + (kBlk + kr) * D + 16 * dt + 4 * grp) = dvt[dt];
+  }
+}
+
+// dK_cmp, dV_cmp = the chunks' partial sums, added in chunk order.
+template <int D>
+__global__ __launch_bounds__(D) void bwd_creduce_kernel(BwdParams p) {
+  const int b = blockIdx.x / p.hkv, g = blockIdx.x % p.hkv, d = threadIdx.x;
+  const int c = b / kBlk, kr = b % kBlk;
+  const int first = ((c * kBlk + 1) * kBlk - 1) / kChunkTok;
+  float sk = 0.f, sv = 0.f;
+  for (int ch = first; ch < p.n_chunk; ++ch) {
+    const float *src = p.cpart + (((int64_t)c * p.n_chunk + ch) * p.hkv + g) * 2 * kBlk * D;
+    sk += src[kr * D + d];
+    sv += src[(kBlk + kr) * D + d];
+  }
+  const int64_t o = ((int64_t)b * p.hkv + g) * D + d;
+  p.dkc[o] = sk;
+  p.dvc[o] = sv;
 }
 
 // dW = sum over (block, group) of dK_cmp (x) mean; one workgroup of D
@@ -405,43 +795,93 @@ __global__ __launch_bounds__(D) void bwd_cmp_tok_kernel(BwdParams p) {
 }
 
 template <int D, int G>
-hipError_t run_rows(const BwdParams &p, hipStream_t st) {
-  const int64_t items = p.n * p.hkv;
-  hipLaunchKernelGGL((bwd_rows_kernel<D, G>), dim3((unsigned)((items + kBwdWavesG - 1) / kBwdWavesG)),
-                     dim3(64 * kBwdWavesG), 0, st, p);
+hipError_t run_g(const BwdParams &p, int stage, hipStream_t st) {
+  constexpr int TP = 16 / G;
+  switch (stage) {
+    case 7: {  // query side, vision rows
+      const int n_qt = (int)((p.n_vis + TP - 1) / TP);
+      const int64_t n_wg = ((int64_t)n_qt * p.hkv + 3) / 4;
+      if (n_wg == 0) return hipSuccess;
+      hipLaunchKernelGGL((bwd_q_kernel<D, G, false>), dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(256), 0, st, p,
+                         n_qt);
+      break;
+    }
+    case 8: {  // query side, text rows
+      const int n_qt = (int)((p.n - p.n_vis + TP - 1) / TP);
+      const int64_t n_wg = ((int64_t)n_qt * p.hkv + 3) / 4;
+      if (n_wg == 0) return hipSuccess;
+      hipLaunchKernelGGL((bwd_q_kernel<D, G, true>), dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(256), 0, st, p,
+                         n_qt);
+      break;
+    }
+    case 9: {  // key side: vision blocks and text tiles
+      const int n_ttile = (int)((p.n - p.n_vis + kBlk - 1) / kBlk);
+      const int64_t n_wg = (int64_t)(p.n_vtile + n_ttile) * p.hkv;
+      if (n_wg == 0) return hipSuccess;
+      hipLaunchKernelGGL((bwd_kv_kernel<D, G>), dim3((unsigned)n_wg), dim3(256), 0, st, p);
+      break;
+    }
+    default: {  // key side: compressed keys
+      const int64_t n_wg = (int64_t)p.n_ctile * p.n_chunk * p.hkv;
+      if (n_wg == 0) return hipSuccess;
+      hipLaunchKernelGGL((bwd_kvc_kernel<D, G>), dim3((unsigned)n_wg), dim3(256), 0, st, p);
+      break;
+    }
+  }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t run(const BwdParams &p, int stage, hipStream_t st) {
   switch (stage) {
-    case 0: {  // clear dk, dv, dkc, dvc
-      const int64_t nt = p.n * p.hkv * D, nb = (int64_t)p.n_blk * p.hkv * D;
-      hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, st, p.dk, nt);
-      hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, st, p.dv, nt);
-      if (nb > 0) {
-        hipLaunchKernelGGL(bwd_zero_kernel, dim3(256), dim3(256), 0, st, p.dkc, nb);
-        hipLaunchKernelGGL(bwd_zero_kernel, dim3(256), dim3(256), 0, st, p.dvc, nb);
-      }
+    case 0: {  // clear the selection bitmask
+      const int64_t n = (int64_t)p.hkv * p.n_vtile * p.mask_words;
+      if (n > 0) hipLaunchKernelGGL(bwd_fill_kernel, dim3(1024), dim3(256), 0, st, p.selmask, n);
       break;
     }
     case 1:
       if (p.n_blk > 0) hipLaunchKernelGGL((bwd_pool_kernel<D>), dim3(p.n_blk * p.hkv), dim3(D), 0, st, p);
       break;
-    case 2:
+    case 2: {  // backward tiles
+      if (p.n_vtile > 0)
+        hipLaunchKernelGGL((bwd_pack_kernel<D, true>), dim3(p.n_vtile * p.hkv), dim3(256), 0, st, p.k, p.v, p.v0,
+                           p.n_vis, p.hkv, p.n_vtile, p.tile_v);
+      if (p.n > p.n_vis)
+        hipLaunchKernelGGL((bwd_pack_kernel<D, true>), dim3(p.n_ptile * p.hkv), dim3(256), 0, st, p.k, p.v,
+                           (int64_t)0, p.n, p.hkv, p.n_ptile, p.tile_p);
+      if (p.n_ctile > 0)
+        hipLaunchKernelGGL((bwd_pack_kernel<D, false>), dim3(p.n_ctile * p.hkv), dim3(256), 0, st, p.kc16, p.vc16,
+                           (int64_t)0, (int64_t)p.n_blk, p.hkv, p.n_ctile, p.tile_c);
+      break;
+    }
+    case 3: {  // who chose which block
+      const int64_t n = p.n_vis * p.hkv * p.topk;
+      if (n == 0) break;
+      hipLaunchKernelGGL(bwd_selmask_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+      hipLaunchKernelGGL(bwd_selcount_kernel, dim3(p.hkv * p.n_vtile), dim3(64), 0, st, p);
+      hipLaunchKernelGGL(bwd_selscan_kernel, dim3(1), dim3(256), 0, st, p, p.hkv * p.n_vtile);
+      hipLaunchKernelGGL(bwd_selfill_kernel, dim3(p.hkv * p.n_vtile), dim3(64), 0, st, p);
+      break;
+    }
+    case 7: case 8: case 9: case 10:
       switch (p.hq / p.hkv) {
-        case 1: return run_rows<D, 1>(p, st);
-        case 2: return run_rows<D, 2>(p, st);
-        case 3: return run_rows<D, 3>(p, st);
-        case 4: return run_rows<D, 4>(p, st);
-        case 5: return run_rows<D, 5>(p, st);
-        case 6: return run_rows<D, 6>(p, st);
-        case 7: return run_rows<D, 7>(p, st);
-        case 8: return run_rows<D, 8>(p, st);
+        case 1: return run_g<D, 1>(p, stage, st);
+        case 2: return run_g<D, 2>(p, stage, st);
+        case 3: return run_g<D, 3>(p, stage, st);
+        case 4: return run_g<D, 4>(p, stage, st);
+        case 5: return run_g<D, 5>(p, stage, st);
+        case 6: return run_g<D, 6>(p, stage, st);
+        case 7: return run_g<D, 7>(p, stage, st);
+        case 8: return run_g<D, 8>(p, stage, st);
         default: return hipErrorInvalidValue;
       }
-    default:
+    case 11:
+      if (p.n_blk > 0) hipLaunchKernelGGL((bwd_creduce_kernel<D>), dim3(p.n_blk * p.hkv), dim3(D), 0, st, p);
+      break;
+    case 12:
       hipLaunchKernelGGL((bwd_cmp_w_kernel<D>), dim3(2 * D), dim3(D), 0, st, p);
+      break;
+    default:
       if (p.n_blk > 0) hipLaunchKernelGGL((bwd_cmp_tok_kernel<D>), dim3(p.n_blk * p.hkv), dim3(D), 0, st, p);
       break;
   }

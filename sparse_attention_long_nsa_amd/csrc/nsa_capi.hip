@@ -466,13 +466,47 @@ nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim, int32
   return NSA_OK;
 }
 
+// Backward workspace: offsets of every array of BwdParams that lives in it.
+struct BwdLayout {
+  int n_vtile = 0, n_ptile = 0, n_ctile = 0, mask_words = 0, n_chunk = 0;
+  size_t kc = 0, vc = 0, kbar = 0, vbar = 0, dkc = 0, dvc = 0, kc16 = 0, vc16 = 0, tile_v = 0, tile_p = 0,
+         tile_c = 0, vstat = 0, tstat = 0, selmask = 0, selcnt = 0, seloff = 0, selrows = 0, cpart = 0, total = 0;
+};
+
 static nsa_status plan_backward(const nsa_prefill_desc *ds, const uint8_t *is_vision, PrefillPlan &pl,
-                                size_t *bytes) {
+                                BwdLayout &L) {
   const nsa_status st = plan_prefill(ds, is_vision, pl);
   if (st != NSA_OK) return st;
   if (pl.fp32 || pl.mapped) return NSA_ERR_UNSUPPORTED;  // bf16, one vision run
-  const size_t one = align_up(sizeof(float) * (size_t)pl.n_blk * pl.hkv * pl.d);
-  *bytes = 6 * one + kAlign;
+  const size_t nb = (size_t)pl.n_blk * pl.hkv * pl.d;
+  const int64_t n_text = pl.N - pl.n_vis;
+  L.n_vtile = (int)((pl.n_vis + kBlk - 1) / kBlk);
+  L.n_ptile = n_text > 0 ? (int)((pl.N + kBlk - 1) / kBlk) : 0;
+  L.n_ctile = (pl.n_blk + kBlk - 1) / kBlk;
+  L.mask_words = (int)((pl.n_vis + 31) / 32);
+  L.n_chunk = (int)((pl.n_vis + 2047) / 2048);
+  const size_t tile = sizeof(uint16_t) * 4 * kBlk * (size_t)pl.d * pl.hkv;  // one tile, every group
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  L.kc = take(sizeof(float) * nb);
+  L.vc = take(sizeof(float) * nb);
+  L.kbar = take(sizeof(float) * nb);
+  L.vbar = take(sizeof(float) * nb);
+  L.dkc = take(sizeof(float) * nb);
+  L.dvc = take(sizeof(float) * nb);
+  L.kc16 = take(sizeof(uint16_t) * nb);
+  L.vc16 = take(sizeof(uint16_t) * nb);
+  L.tile_v = take(tile * L.n_vtile);
+  L.tile_p = take(tile * L.n_ptile);
+  L.tile_c = take(tile * L.n_ctile);
+  L.vstat = take(sizeof(float) * 6 * (size_t)pl.n_vis * pl.hq);
+  L.tstat = take(sizeof(float) * 2 * (size_t)n_text * pl.hq);
+  L.selmask = take(sizeof(uint32_t) * (size_t)pl.hkv * L.n_vtile * L.mask_words);
+  L.selcnt = take(sizeof(int32_t) * (size_t)pl.hkv * L.n_vtile);
+  L.seloff = take(sizeof(int32_t) * ((size_t)pl.hkv * L.n_vtile + 1));
+  L.selrows = take(sizeof(int32_t) * (size_t)pl.n_vis * pl.hkv * pl.k);
+  L.cpart = take(sizeof(float) * (size_t)L.n_ctile * L.n_chunk * pl.hkv * 2 * kBlk * pl.d);
+  L.total = off + kAlign;
   return NSA_OK;
 }
 
@@ -480,10 +514,10 @@ nsa_status nsa_prefill_backward_workspace_size(const nsa_prefill_desc *desc, con
                                                size_t *bytes) {
   if (!bytes) return NSA_ERR_INVALID_ARG;
   PrefillPlan pl;
-  size_t need = 0;
-  const nsa_status st = plan_backward(desc, is_vision, pl, &need);
+  BwdLayout L;
+  const nsa_status st = plan_backward(desc, is_vision, pl, L);
   if (st != NSA_OK) return st;
-  *bytes = need;
+  *bytes = L.total;
   return NSA_OK;
 }
 
@@ -493,29 +527,76 @@ nsa_status nsa_prefill_backward(const nsa_prefill_desc *desc, const void *q, con
                                 float *dq, float *dk, float *dv, float *dw_cmp_k, float *dw_cmp_v,
                                 float *dgate, void *workspace, size_t workspace_bytes, void *stream) {
   PrefillPlan pl;
-  size_t need = 0;
-  const nsa_status st = plan_backward(desc, is_vision, pl, &need);
+  BwdLayout L;
+  const nsa_status st = plan_backward(desc, is_vision, pl, L);
   if (st != NSA_OK) return st;
   const void *req[] = {q, k, v, w_cmp_k, w_cmp_v, gate_logits, dout, dq, dk, dv, dw_cmp_k, dw_cmp_v, dgate};
   for (const void *p : req)
     if (!p || !aligned16(p)) return NSA_ERR_INVALID_ARG;
   if (pl.n_vis > 0 && (!sel_idx || !aligned16(sel_idx))) return NSA_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < need) return NSA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < L.total) return NSA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return NSA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t one = align_up(sizeof(float) * (size_t)pl.n_blk * pl.hkv * pl.d);
-  float *ws = static_cast<float *>(workspace);
-  auto slot = [&](int i) { return reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + i * one); };
-  BwdParams bp{static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-               static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(w_cmp_k),
-               static_cast<const uint16_t *>(w_cmp_v), gate_logits, dout, sel_idx, dq, dk, dv, dgate,
-               dw_cmp_k, dw_cmp_v, slot(0), slot(1), slot(2), slot(3), slot(4), slot(5),
-               pl.N, pl.v0, pl.n_vis, pl.hq, pl.hkv, pl.k, pl.w, pl.n_blk, pl.scale};
+  char *ws = static_cast<char *>(workspace);
+  BwdParams bp{};
+  bp.q = static_cast<const uint16_t *>(q);
+  bp.k = static_cast<const uint16_t *>(k);
+  bp.v = static_cast<const uint16_t *>(v);
+  bp.wk = static_cast<const uint16_t *>(w_cmp_k);
+  bp.wv = static_cast<const uint16_t *>(w_cmp_v);
+  bp.gates = gate_logits;
+  bp.dout = dout;
+  bp.sel = sel_idx;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.dgate = dgate;
+  bp.dwk = dw_cmp_k;
+  bp.dwv = dw_cmp_v;
+  bp.kc = reinterpret_cast<float *>(ws + L.kc);
+  bp.vc = reinterpret_cast<float *>(ws + L.vc);
+  bp.kbar = reinterpret_cast<float *>(ws + L.kbar);
+  bp.vbar = reinterpret_cast<float *>(ws + L.vbar);
+  bp.dkc = reinterpret_cast<float *>(ws + L.dkc);
+  bp.dvc = reinterpret_cast<float *>(ws + L.dvc);
+  bp.kc16 = reinterpret_cast<uint16_t *>(ws + L.kc16);
+  bp.vc16 = reinterpret_cast<uint16_t *>(ws + L.vc16);
+  bp.tile_v = reinterpret_cast<uint16_t *>(ws + L.tile_v);
+  bp.tile_p = reinterpret_cast<uint16_t *>(ws + L.tile_p);
+  bp.tile_c = reinterpret_cast<uint16_t *>(ws + L.tile_c);
+  bp.vstat = reinterpret_cast<float *>(ws + L.vstat);
+  bp.tstat = reinterpret_cast<float *>(ws + L.tstat);
+  bp.selmask = reinterpret_cast<uint32_t *>(ws + L.selmask);
+  bp.selcnt = reinterpret_cast<int32_t *>(ws + L.selcnt);
+  bp.seloff = reinterpret_cast<int32_t *>(ws + L.seloff);
+  bp.selrows = reinterpret_cast<int32_t *>(ws + L.selrows);
+  bp.cpart = reinterpret_cast<float *>(ws + L.cpart);
+  bp.n = pl.N;
+  bp.v0 = pl.v0;
+  bp.n_vis = pl.n_vis;
+  bp.hq = pl.hq;
+  bp.hkv = pl.hkv;
+  bp.topk = pl.k;
+  bp.window = pl.w;
+  bp.n_blk = pl.n_blk;
+  bp.scale = pl.scale;
+  bp.n_vtile = L.n_vtile;
+  bp.n_ptile = L.n_ptile;
+  bp.n_ctile = L.n_ctile;
+  bp.mask_words = L.mask_words;
+  bp.n_chunk = L.n_chunk;
   hipError_t e = hipSuccess;
-  NSA_LAUNCH("bwd_zero", launch_backward(bp, pl.d, 0, s));
+  NSA_LAUNCH("bwd_selclear", launch_backward(bp, pl.d, 0, s));
   NSA_LAUNCH("bwd_pool", launch_backward(bp, pl.d, 1, s));
-  NSA_LAUNCH("bwd_rows", launch_backward(bp, pl.d, 2, s));
-  NSA_LAUNCH("bwd_cmp_w", launch_backward(bp, pl.d, 3, s));
+  NSA_LAUNCH("bwd_pack", launch_backward(bp, pl.d, 2, s));
+  NSA_LAUNCH("bwd_sellist", launch_backward(bp, pl.d, 3, s));
+  NSA_LAUNCH("bwd_q_vis", launch_backward(bp, pl.d, 7, s));
+  NSA_LAUNCH("bwd_q_text", launch_backward(bp, pl.d, 8, s));
+  NSA_LAUNCH("bwd_kv", launch_backward(bp, pl.d, 9, s));
+  NSA_LAUNCH("bwd_kv_cmp", launch_backward(bp, pl.d, 10, s));
+  NSA_LAUNCH("bwd_cmp_sum", launch_backward(bp, pl.d, 11, s));
+  NSA_LAUNCH("bwd_cmp_w", launch_backward(bp, pl.d, 12, s));
+  NSA_LAUNCH("bwd_cmp_tok", launch_backward(bp, pl.d, 13, s));
   return NSA_OK;
 }
 

@@ -27,6 +27,9 @@ __host__ __device__ inline int sel_block_keys(int32_t b, int t) {
   return n < kSelBlk ? n : kSelBlk;
 }
 
+// Whether list entry b names a block query t may attend (0 .. t / 64).
+__host__ __device__ inline bool sel_entry_valid(int32_t b, int t) { return b >= 0 && t >= 0 && b <= t / kSelBlk; }
+
 // Vision row of key i_in_blk (0 .. 63) of list entry b for query t, clamped
 // to rows 0 .. t for any entry value (meaningful only for a valid list).
 __host__ __device__ inline int sel_key_row(int32_t b, int i_in_blk, int t) {

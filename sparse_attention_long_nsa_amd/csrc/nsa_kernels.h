@@ -124,9 +124,19 @@ struct BwdParams {
   const int32_t *sel;                   // [N_v,Hkv,k] selected blocks of the forward
   float *dq, *dk, *dv, *dgate, *dwk, *dwv;
   float *kc, *vc, *kbar, *vbar, *dkc, *dvc;  // workspace [n_blk,Hkv,d] each
+  uint16_t *kc16, *vc16;                // workspace [n_blk,Hkv,d] fp16 compressed keys / values
+  uint16_t *tile_v, *tile_p, *tile_c;   // backward tiles of the vision blocks, of all positions, of
+                                        // the compressed keys: [Hkv][tiles][4 sections][64 d] fp16
+  float *vstat;                         // [N_v,Hq,3,2]: per branch log2-sum-exp and dout . o
+  float *tstat;                         // [N_t,Hq,2] the same for the text rows
+  uint32_t *selmask;                    // [Hkv][n_vtile][mask_words]: bit t = vision token t chose it
+  int32_t *selcnt, *seloff, *selrows;   // [Hkv n_vtile], [Hkv n_vtile + 1], [N_v Hkv k]: the tokens
+                                        // that chose each (group, block), ascending
+  float *cpart;                         // [n_ctile][n_chunk][Hkv][2][64][d] partial compressed grads
   int64_t n, v0, n_vis;
   int hq, hkv, topk, window, n_blk;
   float scale;
+  int n_vtile, n_ptile, n_ctile, mask_words, n_chunk;
 };
 
 // One slice of the token-kind mask, as kernel arguments: bit j of word i

@@ -53,16 +53,22 @@ KERNELS = [
     ("mfma_loop_kernel", "mfma_probe", "sparse_attention_long_nsa_amd/csrc/nsa_probe.hip"),
     ("gate_hidden_kernel", "gate_hidden", "sparse_attention_long_nsa_amd/csrc/nsa_gate.hip"),
     ("gate_out_kernel", "gate_out", "sparse_attention_long_nsa_amd/csrc/nsa_gate.hip"),
-    ("bwd_zero_kernel", "bwd_zero", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_fill_kernel", "bwd_selclear", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
     ("bwd_pool_kernel", "bwd_pool", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
-    ("bwd_rows_kernel", "bwd_rows", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_pack_kernel", "bwd_pack", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_sel", "bwd_sellist", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_q_kernel", "bwd_q", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_kv_kernel", "bwd_kv", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_kvc_kernel", "bwd_kv_cmp", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_creduce_kernel", "bwd_cmp_sum", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
     ("bwd_cmp_w_kernel", "bwd_cmp_w", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
     ("bwd_cmp_tok_kernel", "bwd_cmp_tok", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
 ]
 DECODE_KERNELS = ("dec_item_cmp_win", "dec_item_sel", "dec_select", "dec_combine")
 DENSE_KERNELS = ("pack_dense", "dense_attn")
 GATE_KERNELS = ("gate_hidden", "gate_out")
-BWD_KERNELS = ("bwd_zero", "bwd_pool", "bwd_rows", "bwd_cmp_w", "bwd_cmp_tok")
+BWD_KERNELS = ("bwd_selclear", "bwd_pool", "bwd_pack", "bwd_sellist", "bwd_q", "bwd_kv", "bwd_kv_cmp",
+               "bwd_cmp_sum", "bwd_cmp_w", "bwd_cmp_tok")
 PREFILL_KERNELS = ("sel_attn", "cmp_attn", "swa_attn", "text_attn", "text_merge", "blk_score_topk", "cmp_pool",
                    "cmp_pool_mean", "cmp_pool_map", "pack_kv", "pack_cmp", "pack_text")
 

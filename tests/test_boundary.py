@@ -396,8 +396,16 @@ def call_bwd(ds, mask, ptrs=None, ws=FAKE, ws_bytes=1 << 40):
 def test_backward_validation_and_workspace():
     m = vision_mask(1024 + 64, 32, 1024 + 32)
     st, need = bwd_ws(desc(n=len(m)), m)
-    # fp32 compressed keys, values, their means and their gradients: 6 x 16 blocks x 4 groups x 128
-    assert st == binding.NSA_OK and need == 6 * 16 * 4 * 128 * 4 + 256
+    # 1,024 vision tokens (16 blocks, one 2,048-token chunk), 64 text tokens,
+    # 28 / 4 heads, d 128, k 16; every array rounded up to 256 bytes
+    a = lambda x: (x + 255) // 256 * 256
+    nb, tile = 16 * 4 * 128, 4 * 64 * 128 * 2 * 4
+    parts = [4 * nb] * 6 + [2 * nb] * 2          # compressed k / v, means, their gradients; fp16 copies
+    parts += [tile * 16, tile * 17, tile * 1]     # tiles: vision blocks, positions, compressed keys
+    parts += [4 * 6 * 1024 * 28, 4 * 2 * 64 * 28]  # per-branch statistics: vision rows, text rows
+    parts += [4 * 4 * 16 * 32, 4 * 4 * 16, 4 * (4 * 16 + 1), 4 * 1024 * 4 * 16]  # who chose which block
+    parts += [4 * 1 * 1 * 4 * 2 * 64 * 128]       # partial compressed-key gradients
+    assert st == binding.NSA_OK and need == sum(a(x) for x in parts) + 256
     assert bwd_ws(desc(n=len(m), dtype=1), m)[0] == binding.NSA_ERR_UNSUPPORTED
     two_runs = vision_mask(len(m), 0, 500) | vision_mask(len(m), 600, 1000)
     assert bwd_ws(desc(n=len(m)), two_runs)[0] == binding.NSA_ERR_UNSUPPORTED

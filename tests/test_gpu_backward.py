@@ -1,17 +1,25 @@
 """GPU parity of the backward pass (nsa_prefill_backward) against the fp64
 autograd oracle (oracle/backward.py), through the C ABI.
 
-Both sides take the C oracle's own block selection, so the comparison is
-free of selection ties. Bar, from the arithmetic: the kernels work in fp32
-(unit roundoff u = 2^-24) on bf16 inputs that are exact in fp32; every
-gradient entry is a sum over at most N keys of products that are themselves
-d-term dot products of O(1) values, so its relative error is about
-(N + d) u, below 1e-4 for the sizes here. Each array must agree within 1e-3
-of its largest magnitude (max |d| <= 1e-3 max |ref|) and on average within
-1e-5 of it. Each case prints its name and shape before touching the GPU.
+Both sides take the same block selection (the C oracle's own, or the GPU
+forward's handed over as a caller would), so the comparison is free of
+selection ties. Bar, from the arithmetic: the kernels multiply fp16 operands
+on the matrix cores with fp32 accumulation. q, k and v are bf16 and convert
+to fp16 exactly; dout, the probabilities P, the score gradients dS and the
+compressed keys / values are rounded to fp16 (unit roundoff u = 2^-11). A
+gradient element is a sum of products of two such operands, one of them
+(dS) itself carrying the rounding of dP = dout . v and of P, so each term's
+relative error is a few u and the element's error a few u times the sum of
+its terms' magnitudes, which for these inputs is within a small factor of
+the array's largest element. Each array must agree within 8 u of its
+largest magnitude (max |d| <= 8 u max |ref|, 3.9e-3) and on average within
+4 u of its mean magnitude (mean |d| <= 4 u mean |ref|, 2.0e-3); measured
+on these cases: at most 1.3e-3 and 8e-4. Each case prints its name and shape
+before touching the GPU.
 """
 import math
 
+U16 = 2.0 ** -11  # fp16 unit roundoff
 import numpy as np
 import pytest
 import torch
@@ -48,6 +56,16 @@ def run(inp, sel, dout):
     return {n: t.cpu().numpy().astype(np.float64) for n, t in r.items()}
 
 
+def check_bar(gname, g, rf):
+    assert np.all(np.isfinite(g)), gname
+    big, avg = np.abs(rf).max(), np.abs(rf).mean()
+    err = np.abs(g - rf)
+    print(f"  {gname}: max |d| {err.max():.3e} ({err.max() / big:.2e} of max |ref|), "
+          f"mean |d| {err.mean():.3e} ({err.mean() / avg:.2e} of mean |ref|)", flush=True)
+    assert err.max() <= 8 * U16 * big, f"{gname}: max |d| {err.max():.3e} vs {big:.3e}"
+    assert err.mean() <= 4 * U16 * avg, f"{gname}: mean |d| {err.mean():.3e} vs mean |ref| {avg:.3e}"
+
+
 @pytest.mark.parametrize("shape", CASES, ids=lambda s: f"nv{s.n_vis}_t{s.n_text}_h{s.n_q_heads}_d{s.head_dim}")
 def test_backward_parity(shape):
     print(f"backward {shape}", flush=True)
@@ -59,12 +77,7 @@ def test_backward_parity(shape):
     got = run(inp, sel, dout)
     pairs = (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dw_cmp_k", "w_k"), ("dw_cmp_v", "w_v"), ("dgate", "gates"))
     for gname, rname in pairs:
-        g, rf = got[gname], ref[rname]
-        assert np.all(np.isfinite(g)), gname
-        big = np.abs(rf).max()
-        err = np.abs(g - rf)
-        assert err.max() <= 1e-3 * big, f"{gname}: max |d| {err.max():.3e} vs {big:.3e}"
-        assert err.mean() <= 1e-5 * big, f"{gname}: mean |d| {err.mean():.3e} vs {big:.3e}"
+        check_bar(gname, got[gname], ref[rname])
 
 
 def upload(inp):
@@ -116,13 +129,7 @@ def test_backward_parity_sampled_rows_on_the_forwards_selection(shape, n_vis_row
     assert np.all(got["dq"][others] == 0) and np.all(got["dgate"][others] == 0)
     pairs = (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dw_cmp_k", "w_k"), ("dw_cmp_v", "w_v"), ("dgate", "gates"))
     for gname, rname in pairs:
-        g, rf = got[gname], ref[rname]
-        assert np.all(np.isfinite(g)), gname
-        big = np.abs(rf).max()
-        err = np.abs(g - rf)
-        print(f"  {gname}: max |d| {err.max():.3e} mean {err.mean():.3e} (max |ref| {big:.3e})", flush=True)
-        assert err.max() <= 1e-3 * big, f"{gname}: max |d| {err.max():.3e} vs {big:.3e}"
-        assert err.mean() <= 1e-5 * big, f"{gname}: mean |d| {err.mean():.3e} vs {big:.3e}"
+        check_bar(gname, got[gname], ref[rname])
 
 
 def test_backward_hostile_selection_lists_stay_in_bounds():
@@ -143,3 +150,17 @@ def test_backward_hostile_selection_lists_stay_in_bounds():
     torch.cuda.synchronize()
     for n, t in got.items():
         assert torch.isfinite(t).all(), n
+
+
+def test_backward_is_bitwise_repeatable():
+    """Every gradient element is written by one thread in a fixed order (no
+    atomics): two calls give identical bits."""
+    shape = PrefillShape(1045, 16, 48, 28, 4, 128, 64, 8, 256, "bf16")
+    print(f"backward repeatability {shape}", flush=True)
+    inp = make_prefill_inputs(shape, seed=18)
+    vis = np.asarray(inp["is_vision"]).astype(bool)
+    sel = oracle.prefill(inp, want=("sel",))["sel"][vis]
+    dout = make_output_grad((shape.n_tokens, shape.n_q_heads, shape.head_dim), seed=19)
+    a, b = run(inp, sel, dout), run(inp, sel, dout)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
