@@ -337,9 +337,9 @@ __device__ __forceinline__ void q_branch(const BwdParams &p, Walk walk, const u1
   walk([&](const uint16_t *tile, auto valid) { q_pass2<D>(tile, qf, of, dqa, lse2, dd, sig, sl2, valid, lane); });
 }
 
-template <int D, int G, bool TXT>
+template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_q_kernel(BwdParams p, int n_qt) {
-  using R = QRows<D, G, TXT>;
+  using R = QRows<D, G, false>;
   constexpr int TP = R::TP, DS = D / 32, DT = D / 16, SEC4 = BwdTile<D>::E;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   // workgroups go to the eight XCDs round-robin: give each XCD one
@@ -366,29 +366,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   f32x4 dqa[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dqa[dt] = zero4();
-  const int n_tok = TXT ? (int)(p.n - p.n_vis) : (int)p.n_vis;
+  const int n_tok = (int)p.n_vis;
   const int t_first = qt * TP, t_last = min(qt * TP + TP, n_tok) - 1;
   const int grp = r.grp, tok = r.tok;
 
-  if constexpr (TXT) {
-    // dense causal over every earlier position
-    const int64_t pos_last = t_last < p.v0 ? (int64_t)t_last : (int64_t)t_last + p.n_vis;
-    const int64_t mypos = r.pos;
-    const int n_tiles = (int)(pos_last / kBlk) + 1;
-    auto walk = [&](auto f) {
-      for (int tl = 0; tl < n_tiles; ++tl) {
-        const int64_t k0 = (int64_t)tl * kBlk + 4 * grp;
-        f(p.tile_p + ((int64_t)g * p.n_ptile + tl) * SEC4,
-          [&](int kt, int i) { return k0 + 16 * kt + i <= mypos; });
-      }
-    };
-    q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, 1.f, sl2, p.tstat + ((int64_t)tok * p.hq + r.hq) * 2, nullptr,
-                lane);
-    if (r.rv && grp == 0) {
-#pragma unroll
-      for (int c = 0; c < 3; ++c) p.dgate[r.qrow * 3 + c] = 0.f;
-    }
-  } else {
+  {
     float *stat = p.vstat + ((int64_t)(r.rv ? tok : 0) * p.hq + r.hq) * 6;
     float *dg = p.dgate + r.qrow * 3;
     float sig[3];
@@ -474,6 +456,134 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   }
 }
 
+// Text rows: dense causal attention over every earlier position, split
+// over the key tiles so that the few text rows still fill the chip. Wave
+// (split, group, tile of 16/G text tokens) takes its split's share of the
+// position tiles. Pass 1 writes the split's (max, sum, unnormalised o) per
+// row; bwd_qtmerge combines the splits into the row statistics; pass 2
+// writes the split's share of dq, which bwd_qtsum adds in split order.
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_qt_kernel(BwdParams p, int n_qt,
+                                                                                           int pass) {
+  using R = QRows<D, G, true>;
+  constexpr int TP = R::TP, DS = D / 32, DT = D / 16, SEC4 = BwdTile<D>::E;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int item = blockIdx.x * 4 + wv;
+  if (item >= p.n_tsplit * p.hkv * n_qt) return;
+  const int qt = item % n_qt, g = (item / n_qt) % p.hkv, sp = item / (n_qt * p.hkv);
+  const R r(p, qt, g, lane);
+  const int n_text = (int)(p.n - p.n_vis);
+  const int t_last = min(qt * TP + TP, n_text) - 1;
+  const int64_t pos_last = t_last < p.v0 ? (int64_t)t_last : (int64_t)t_last + p.n_vis;
+  const int n_tiles = (int)(pos_last / kBlk) + 1;
+  const int lo = (int)((int64_t)sp * n_tiles / p.n_tsplit), hi = (int)((int64_t)(sp + 1) * n_tiles / p.n_tsplit);
+  const float sl2 = p.scale * kLog2e;
+  const int grp = r.grp;
+  const int64_t mypos = r.pos;
+  const int64_t trow = (int64_t)(r.rv ? r.tok : 0) * p.hq + r.hq;  // text row x head
+  float *part = p.tpart + ((int64_t)sp * n_text * p.hq + trow) * (D + 2);
+  u16x8 qf[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) qf[ds] = r.rv ? bf2h8(q_frag_global(p.q + r.qrow * D, ds, lane)) : zero8();
+  if (pass == 1) {
+    f32x4 oa[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oa[dt] = zero4();
+    float m = -INFINITY, l = 0.f;
+    for (int tl = lo; tl < hi; ++tl) {
+      const int64_t k0 = (int64_t)tl * kBlk + 4 * grp;
+      q_pass1<D>(p.tile_p + ((int64_t)g * p.n_ptile + tl) * SEC4, qf, oa, m, l, sl2,
+                 [&](int kt, int i) { return k0 + 16 * kt + i <= mypos; }, lane);
+    }
+    const float L = grp_sum(l);
+    if (r.rv) {
+      if (grp == 0) {
+        part[0] = m;
+        part[1] = L;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[2 + 16 * dt + 4 * grp + i] = oa[dt][i];
+      }
+    }
+  } else {
+    u16x8 of[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      u16x8 o = zero8();
+      if (r.rv) {
+        const float *src = p.dout + r.qrow * D + 32 * ds + 8 * grp;
+        o = pack_p(*reinterpret_cast<const f32x4 *>(src), *reinterpret_cast<const f32x4 *>(src + 4));
+      }
+      of[ds] = o;
+    }
+    const float lse2 = r.rv ? p.tstat[trow * 2] : -INFINITY, dd = r.rv ? p.tstat[trow * 2 + 1] : 0.f;
+    f32x4 dqa[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dqa[dt] = zero4();
+    for (int tl = lo; tl < hi; ++tl) {
+      const int64_t k0 = (int64_t)tl * kBlk + 4 * grp;
+      q_pass2<D>(p.tile_p + ((int64_t)g * p.n_ptile + tl) * SEC4, qf, of, dqa, lse2, dd, 1.f, sl2,
+                 [&](int kt, int i) { return k0 + 16 * kt + i <= mypos; }, lane);
+    }
+    if (r.rv) {
+      float *dst = p.tpart + ((int64_t)sp * n_text * p.hq + trow) * D;  // pass-1 partials are merged by now
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt + 4 * grp) = dqa[dt];
+    }
+  }
+}
+
+// One workgroup of D threads per (text row, head): the splits' partials
+// combined into the row's log2-sum-exp and dout . o; text rows get no gate
+// gradient.
+template <int D>
+__global__ __launch_bounds__(D) void bwd_qtmerge_kernel(BwdParams p) {
+  __shared__ float red[D / 64];
+  const int64_t trow = blockIdx.x;  // text token x Hq + head
+  const int d = threadIdx.x, n_text = (int)(p.n - p.n_vis);
+  const int64_t stride = (int64_t)n_text * p.hq * (D + 2);
+  const float *part = p.tpart + trow * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < p.n_tsplit; ++s) M = fmaxf(M, part[s * stride]);
+  float L = 0.f, o = 0.f;
+  for (int s = 0; s < p.n_tsplit; ++s) {
+    const float ms = part[s * stride];
+    const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    L += part[s * stride + 1] * w;
+    o += part[s * stride + 2 + d] * w;
+  }
+  const int64_t tok = trow / p.hq, h = trow % p.hq;
+  const int64_t pos = tok < p.v0 ? tok : tok + p.n_vis;
+  float x = L > 0.f ? p.dout[(pos * p.hq + h) * D + d] * o / L : 0.f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if ((d & 63) == 0) red[d >> 6] = x;
+  __syncthreads();
+  if (d == 0) {
+    float dd = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) dd += red[w];
+    p.tstat[trow * 2] = L > 0.f ? M + __log2f(L) : -INFINITY;
+    p.tstat[trow * 2 + 1] = dd;
+  }
+  if (d < 3) p.dgate[(pos * p.hq + h) * 3 + d] = 0.f;
+}
+
+// dq of the text rows: the splits' shares added in split order.
+template <int D>
+__global__ __launch_bounds__(D) void bwd_qtsum_kernel(BwdParams p) {
+  const int64_t trow = blockIdx.x;
+  const int d = threadIdx.x, n_text = (int)(p.n - p.n_vis);
+  const int64_t stride = (int64_t)n_text * p.hq * D;
+  float acc = 0.f;
+  for (int s = 0; s < p.n_tsplit; ++s) acc += p.tpart[s * stride + trow * D + d];
+  const int64_t tok = trow / p.hq, h = trow % p.hq;
+  const int64_t pos = tok < p.v0 ? tok : tok + p.n_vis;
+  p.dq[(pos * p.hq + h) * D + d] = acc * p.scale;
+}
+
 // -------------------------------------------------------------- key side
 // Query tokens walked by a key-side workgroup: tokens a + i (range) or
 // list[i], i < n; `mask` picks the visibility rule, `br` the branch whose
@@ -489,7 +599,9 @@ struct TokSrc {
 // whole workgroup: row-major fp16 copies of q and dout (A operands of S and
 // dP) and transposed copies whose key slots follow the permutation of the
 // P / dS B operand (slot 8 j + i <- row 4 j + i for i < 4, 16 + 4 j + i - 4
-// for i >= 4), plus each row's statistics.
+// for i >= 4), plus each row's statistics. The transposed rows rotate their
+// four 8-slot chunks by (dim / 16) mod 4, so that the 2-byte stores of
+// threads 16 dims apart fall in different LDS banks.
 template <int D>
 struct KvStage {
   static constexpr int RS = D + 8, TS_ = 40;
@@ -503,70 +615,94 @@ __device__ __forceinline__ int row_slot(int r) {
   return r < 16 ? 8 * (r >> 2) + (r & 3) : 8 * ((r - 16) >> 2) + 4 + ((r - 16) & 3);
 }
 
+// One thread's share of a step's rows: row r = tid / 8 (token r / G of the
+// step, head r % G), dims seg PER .. +PER-1 with seg = tid % 8, loaded from
+// global memory one step ahead and stored into the other LDS buffer after
+// the current step's products.
+template <int D>
+struct KvRowRegs {
+  static constexpr int PER = D / 8;
+  u16x8 q[PER / 8];
+  f32x4 d[PER / 4];
+  float l2, dd, sg;
+  int tok;
+};
+
+// The query token of this thread's row in step `step` (-1: no row).
+template <int G>
+__device__ __forceinline__ int kv_tok(const TokSrc &src, int step, int tid) {
+  constexpr int TS = 32 / G;
+  const int r = tid >> 3, tau = r / G, i = step * TS + tau;
+  if (r >= TS * G || i >= src.n) return -1;
+  return src.list ? src.list[i] : src.a + i;
+}
+
 template <int D, int G>
-__device__ __forceinline__ void kv_stage(const BwdParams &p, KvStage<D> &sm, const TokSrc &src, int step, int g,
-                                         int tid) {
-  constexpr int TS = 32 / G, PER = D / 8;  // tokens per step, dims per thread
+__device__ __forceinline__ void kv_load(const BwdParams &p, const TokSrc &src, int tok, int g, int tid,
+                                        KvRowRegs<D> &rr) {
+  constexpr int PER = D / 8;  // dims per thread
   const int r = tid >> 3, seg = tid & 7;
-  const int tau = r / G, hh = r % G;
-  const int i = step * TS + tau;
-  const bool ok = r < TS * G && i < src.n;
-  int tok = -1;
+  const int hh = r % G;
+  const bool ok = tok >= 0;
   int64_t qrow = 0;
   if (ok) {
-    tok = src.list ? src.list[i] : src.a + i;
     const int64_t pos = src.br == 3 ? (tok < p.v0 ? (int64_t)tok : (int64_t)tok + p.n_vis) : p.v0 + tok;
     qrow = pos * p.hq + g * G + hh;
   }
-  uint16_t qv[PER], dv[PER];
+#pragma unroll
+  for (int c = 0; c < PER / 8; ++c) rr.q[c] = ok ? *reinterpret_cast<const u16x8 *>(p.q + qrow * D + seg * PER + 8 * c)
+                                                 : zero8();
+#pragma unroll
+  for (int c = 0; c < PER / 4; ++c)
+    rr.d[c] = ok ? *reinterpret_cast<const f32x4 *>(p.dout + qrow * D + seg * PER + 4 * c) : zero4();
+  rr.tok = tok;
+  rr.l2 = INFINITY;
+  rr.dd = 0.f;
+  rr.sg = 0.f;
+  if (ok && seg == 0) {
+    const int hq = g * G + hh;
+    if (src.br == 3) {
+      const float *st = p.tstat + ((int64_t)tok * p.hq + hq) * 2;
+      rr.l2 = st[0];
+      rr.dd = st[1];
+      rr.sg = 1.f;
+    } else {
+      const float *st = p.vstat + ((int64_t)tok * p.hq + hq) * 6 + 2 * src.br;
+      rr.l2 = st[0];
+      rr.dd = st[1];
+      rr.sg = sigmoidf_(p.gates[qrow * 3 + src.br]);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kv_store(KvStage<D> &sm, const KvRowRegs<D> &rr, int tid) {
+  constexpr int PER = D / 8;
+  const int r = tid >> 3, seg = tid & 7, sl = row_slot(r);
 #pragma unroll
   for (int c = 0; c < PER / 8; ++c) {
-    u16x8 q8 = zero8();
-    f32x4 a = zero4(), b = zero4();
-    if (ok) {
-      q8 = bf2h8(*reinterpret_cast<const u16x8 *>(p.q + qrow * D + seg * PER + 8 * c));
-      a = *reinterpret_cast<const f32x4 *>(p.dout + qrow * D + seg * PER + 8 * c);
-      b = *reinterpret_cast<const f32x4 *>(p.dout + qrow * D + seg * PER + 8 * c + 4);
-    }
-    const u16x8 d8 = pack_p(a, b);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qv[8 * c + e] = q8[e];
-      dv[8 * c + e] = d8[e];
-    }
+    const u16x8 q8 = bf2h8(rr.q[c]);
+    const u16x8 d8 = pack_p(rr.d[2 * c], rr.d[2 * c + 1]);
     *reinterpret_cast<u16x8 *>(&sm.qs[r][seg * PER + 8 * c]) = q8;
     *reinterpret_cast<u16x8 *>(&sm.ds_[r][seg * PER + 8 * c]) = d8;
-  }
-  const int sl = row_slot(r);
+    const int dim0 = seg * PER + 8 * c;
+    const int col = (sl + 8 * ((dim0 >> 4) & 3)) & 31;  // eight dims share dim / 16
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    sm.qt[seg * PER + e][sl] = qv[e];
-    sm.dt_[seg * PER + e][sl] = dv[e];
+    for (int e = 0; e < 8; ++e) {
+      sm.qt[dim0 + e][col] = q8[e];
+      sm.dt_[dim0 + e][col] = d8[e];
+    }
   }
   if (seg == 0) {
-    float l2 = INFINITY, dd = 0.f, sg = 0.f;
-    if (ok) {
-      const int hq = g * G + hh;
-      if (src.br == 3) {
-        const float *st = p.tstat + ((int64_t)tok * p.hq + hq) * 2;
-        l2 = st[0];
-        dd = st[1];
-        sg = 1.f;
-      } else {
-        const float *st = p.vstat + ((int64_t)tok * p.hq + hq) * 6 + 2 * src.br;
-        l2 = st[0];
-        dd = st[1];
-        sg = sigmoidf_(p.gates[qrow * 3 + src.br]);
-      }
-      if (l2 == -INFINITY) {  // the row has no keys in this branch
-        l2 = INFINITY;
-        sg = 0.f;
-      }
+    float l2 = rr.l2, sg = rr.sg;
+    if (l2 == -INFINITY) {  // the row has no keys in this branch
+      l2 = INFINITY;
+      sg = 0.f;
     }
     sm.l2[r] = l2;
-    sm.dd[r] = dd;
+    sm.dd[r] = rr.dd;
     sm.sig[r] = sg;
-    sm.tok[r] = tok;
+    sm.tok[r] = rr.tok;
   }
 }
 
@@ -613,24 +749,43 @@ __device__ __forceinline__ void kv_step(const KvStage<D> &sm, const u16x8 (&kf)[
   const u16x8 pp = pack_p(pm[0], pm[1]), pd = pack_p(dsm[0], dsm[1]);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
-    const u16x8 da = *reinterpret_cast<const u16x8 *>(&sm.dt_[16 * dt + r16][8 * grp]);
-    const u16x8 qa = *reinterpret_cast<const u16x8 *>(&sm.qt[16 * dt + r16][8 * grp]);
+    const int ch = 8 * ((grp + dt) & 3);
+    const u16x8 da = *reinterpret_cast<const u16x8 *>(&sm.dt_[16 * dt + r16][ch]);
+    const u16x8 qa = *reinterpret_cast<const u16x8 *>(&sm.qt[16 * dt + r16][ch]);
     dvt[dt] = mfma_f16(da, pp, dvt[dt]);
     dkt[dt] = mfma_f16(qa, pd, dkt[dt]);
   }
 }
 
-// Walks one token source: stage, then every wave's step, 32 rows at a time.
+// Walks one token source 32 rows at a time through two LDS buffers. Loads
+// run two steps ahead of the products (two register sets) and the tokens of
+// the rows three steps ahead, so a row's address never waits on its list
+// entry; each step's rows are stored into the free LDS buffer after the
+// current step's products, one barrier a step.
 template <int D, int G>
-__device__ __forceinline__ void kv_walk(const BwdParams &p, KvStage<D> &sm, const TokSrc &src, int g,
+__device__ __forceinline__ void kv_walk(const BwdParams &p, KvStage<D> (&sm)[2], const TokSrc &src, int g,
                                         const u16x8 (&kf)[D / 32], const u16x8 (&vf)[D / 32], f32x4 (&dkt)[D / 16],
                                         f32x4 (&dvt)[D / 16], int key, float sl2, int tid) {
   constexpr int TS = 32 / G;
   const int n_steps = (src.n + TS - 1) / TS;
+  if (n_steps == 0) return;
+  KvRowRegs<D> rr[2];
+  kv_load<D, G>(p, src, kv_tok<G>(src, 0, tid), g, tid, rr[0]);
+  kv_load<D, G>(p, src, kv_tok<G>(src, 1, tid), g, tid, rr[1]);
+  int tk_next = kv_tok<G>(src, 2, tid);
+  kv_store<D>(sm[0], rr[0], tid);
+  __syncthreads();
   for (int st = 0; st < n_steps; ++st) {
-    kv_stage<D, G>(p, sm, src, st, g, tid);
-    __syncthreads();
-    kv_step<D>(sm, kf, vf, dkt, dvt, key, src.mask, p.window, sl2, tid & 63);
+    if (st + 2 < n_steps) {
+      if (st & 1) kv_load<D, G>(p, src, tk_next, g, tid, rr[1]);
+      else kv_load<D, G>(p, src, tk_next, g, tid, rr[0]);
+    }
+    tk_next = kv_tok<G>(src, st + 3, tid);
+    kv_step<D>(sm[st & 1], kf, vf, dkt, dvt, key, src.mask, p.window, sl2, tid & 63);
+    if (st + 1 < n_steps) {
+      if (st & 1) kv_store<D>(sm[0], rr[0], tid);
+      else kv_store<D>(sm[1], rr[1], tid);
+    }
     __syncthreads();
   }
 }
@@ -662,7 +817,7 @@ __device__ __forceinline__ void kv_keys(const uint16_t *kb, const uint16_t *vb, 
 template <int D, int G>
 __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   constexpr int DS = D / 32, DT = D / 16;
-  __shared__ __attribute__((aligned(16))) KvStage<D> sm;
+  __shared__ __attribute__((aligned(16))) KvStage<D> sm[2];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n_vwg = p.n_vtile * p.hkv;
   const bool vis = (int)blockIdx.x < n_vwg;
@@ -713,7 +868,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
 template <int D, int G>
 __global__ __launch_bounds__(256) void bwd_kvc_kernel(BwdParams p) {
   constexpr int DS = D / 32, DT = D / 16;
-  __shared__ __attribute__((aligned(16))) KvStage<D> sm;
+  __shared__ __attribute__((aligned(16))) KvStage<D> sm[2];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = blockIdx.x % p.hkv, chunk = (blockIdx.x / p.hkv) % p.n_chunk, c = blockIdx.x / (p.hkv * p.n_chunk);
   const int t_min = (c * kBlk + 1) * kBlk - 1;  // first token that sees the tile's first key
@@ -802,16 +957,18 @@ hipError_t run_g(const BwdParams &p, int stage, hipStream_t st) {
       const int n_qt = (int)((p.n_vis + TP - 1) / TP);
       const int64_t n_wg = ((int64_t)n_qt * p.hkv + 3) / 4;
       if (n_wg == 0) return hipSuccess;
-      hipLaunchKernelGGL((bwd_q_kernel<D, G, false>), dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(256), 0, st, p,
-                         n_qt);
+      hipLaunchKernelGGL((bwd_q_kernel<D, G>), dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(256), 0, st, p, n_qt);
       break;
     }
-    case 8: {  // query side, text rows
-      const int n_qt = (int)((p.n - p.n_vis + TP - 1) / TP);
-      const int64_t n_wg = ((int64_t)n_qt * p.hkv + 3) / 4;
+    case 8: {  // query side, text rows: split pass 1, merge, split pass 2, sum
+      const int64_t n_text = p.n - p.n_vis;
+      const int n_qt = (int)((n_text + TP - 1) / TP);
+      const int64_t n_wg = ((int64_t)n_qt * p.hkv * p.n_tsplit + 3) / 4;
       if (n_wg == 0) return hipSuccess;
-      hipLaunchKernelGGL((bwd_q_kernel<D, G, true>), dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(256), 0, st, p,
-                         n_qt);
+      hipLaunchKernelGGL((bwd_qt_kernel<D, G>), dim3((unsigned)n_wg), dim3(256), 0, st, p, n_qt, 1);
+      hipLaunchKernelGGL((bwd_qtmerge_kernel<D>), dim3((unsigned)(n_text * p.hq)), dim3(D), 0, st, p);
+      hipLaunchKernelGGL((bwd_qt_kernel<D, G>), dim3((unsigned)n_wg), dim3(256), 0, st, p, n_qt, 2);
+      hipLaunchKernelGGL((bwd_qtsum_kernel<D>), dim3((unsigned)(n_text * p.hq)), dim3(D), 0, st, p);
       break;
     }
     case 9: {  // key side: vision blocks and text tiles

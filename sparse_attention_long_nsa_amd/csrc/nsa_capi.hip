@@ -468,8 +468,8 @@ nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim, int32
 
 // Backward workspace: offsets of every array of BwdParams that lives in it.
 struct BwdLayout {
-  int n_vtile = 0, n_ptile = 0, n_ctile = 0, mask_words = 0, n_chunk = 0;
-  size_t kc = 0, vc = 0, kbar = 0, vbar = 0, dkc = 0, dvc = 0, kc16 = 0, vc16 = 0, tile_v = 0, tile_p = 0,
+  int n_vtile = 0, n_ptile = 0, n_ctile = 0, mask_words = 0, n_chunk = 0, n_tsplit = 0;
+  size_t tpart = 0, kc = 0, vc = 0, kbar = 0, vbar = 0, dkc = 0, dvc = 0, kc16 = 0, vc16 = 0, tile_v = 0, tile_p = 0,
          tile_c = 0, vstat = 0, tstat = 0, selmask = 0, selcnt = 0, seloff = 0, selrows = 0, cpart = 0, total = 0;
 };
 
@@ -485,6 +485,7 @@ static nsa_status plan_backward(const nsa_prefill_desc *ds, const uint8_t *is_vi
   L.n_ctile = (pl.n_blk + kBlk - 1) / kBlk;
   L.mask_words = (int)((pl.n_vis + 31) / 32);
   L.n_chunk = (int)((pl.n_vis + 2047) / 2048);
+  L.n_tsplit = n_text > 0 ? 8 : 0;  // text rows' key-tile splits
   const size_t tile = sizeof(uint16_t) * 4 * kBlk * (size_t)pl.d * pl.hkv;  // one tile, every group
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
@@ -506,6 +507,7 @@ static nsa_status plan_backward(const nsa_prefill_desc *ds, const uint8_t *is_vi
   L.seloff = take(sizeof(int32_t) * ((size_t)pl.hkv * L.n_vtile + 1));
   L.selrows = take(sizeof(int32_t) * (size_t)pl.n_vis * pl.hkv * pl.k);
   L.cpart = take(sizeof(float) * (size_t)L.n_ctile * L.n_chunk * pl.hkv * 2 * kBlk * pl.d);
+  L.tpart = take(sizeof(float) * (size_t)L.n_tsplit * n_text * pl.hq * (pl.d + 2));
   L.total = off + kAlign;
   return NSA_OK;
 }
@@ -571,6 +573,7 @@ nsa_status nsa_prefill_backward(const nsa_prefill_desc *desc, const void *q, con
   bp.seloff = reinterpret_cast<int32_t *>(ws + L.seloff);
   bp.selrows = reinterpret_cast<int32_t *>(ws + L.selrows);
   bp.cpart = reinterpret_cast<float *>(ws + L.cpart);
+  bp.tpart = reinterpret_cast<float *>(ws + L.tpart);
   bp.n = pl.N;
   bp.v0 = pl.v0;
   bp.n_vis = pl.n_vis;
@@ -585,6 +588,7 @@ nsa_status nsa_prefill_backward(const nsa_prefill_desc *desc, const void *q, con
   bp.n_ctile = L.n_ctile;
   bp.mask_words = L.mask_words;
   bp.n_chunk = L.n_chunk;
+  bp.n_tsplit = L.n_tsplit;
   hipError_t e = hipSuccess;
   NSA_LAUNCH("bwd_selclear", launch_backward(bp, pl.d, 0, s));
   NSA_LAUNCH("bwd_pool", launch_backward(bp, pl.d, 1, s));

@@ -133,10 +133,11 @@ struct BwdParams {
   int32_t *selcnt, *seloff, *selrows;   // [Hkv n_vtile], [Hkv n_vtile + 1], [N_v Hkv k]: the tokens
                                         // that chose each (group, block), ascending
   float *cpart;                         // [n_ctile][n_chunk][Hkv][2][64][d] partial compressed grads
+  float *tpart;                         // [n_tsplit][N_t Hq][d + 2] text rows' per-split partials
   int64_t n, v0, n_vis;
   int hq, hkv, topk, window, n_blk;
   float scale;
-  int n_vtile, n_ptile, n_ctile, mask_words, n_chunk;
+  int n_vtile, n_ptile, n_ctile, mask_words, n_chunk, n_tsplit;
 };
 
 // One slice of the token-kind mask, as kernel arguments: bit j of word i

@@ -405,6 +405,7 @@ def test_backward_validation_and_workspace():
     parts += [4 * 6 * 1024 * 28, 4 * 2 * 64 * 28]  # per-branch statistics: vision rows, text rows
     parts += [4 * 4 * 16 * 32, 4 * 4 * 16, 4 * (4 * 16 + 1), 4 * 1024 * 4 * 16]  # who chose which block
     parts += [4 * 1 * 1 * 4 * 2 * 64 * 128]       # partial compressed-key gradients
+    parts += [4 * 8 * 64 * 28 * 130]              # text rows: eight key-tile splits
     assert st == binding.NSA_OK and need == sum(a(x) for x in parts) + 256
     assert bwd_ws(desc(n=len(m), dtype=1), m)[0] == binding.NSA_ERR_UNSUPPORTED
     two_runs = vision_mask(len(m), 0, 500) | vision_mask(len(m), 600, 1000)
