@@ -18,11 +18,13 @@
 //   bwd_selmask.. the tokens that chose each (group, block), ascending: a
 //                 bitmask over tokens, its row counts, their prefix sum and
 //                 the decoded lists
-//   bwd_q         query side, one wave per (tile of 16/G tokens, KV group):
-//                 per branch, pass 1 recomputes the branch's log-sum-exp and
-//                 output o (online softmax), giving D = dout . o and the gate
-//                 gradient; pass 2 forms dS = sigma P (dP - D) and
-//                 dq^T += K^T dS^T; dq is written once after all branches
+//   bwd_q         query side, one wave per (tile of 16/G tokens, KV group),
+//                 eight consecutive tiles per workgroup sharing each key tile
+//                 staged once in LDS: per branch, pass 1 recomputes the
+//                 branch's log-sum-exp and output o (online softmax), giving
+//                 D = dout . o and the gate gradient; pass 2 forms
+//                 dS = sigma P (dP - D) and dq^T += K^T dS^T; dq is written
+//                 once after all branches (text rows: split over key tiles)
 //   bwd_kv        key side, one workgroup per (64-key tile, KV group), a
 //                 wave per 16 keys: walks every query row that attends the
 //                 tile (window range, selection list, text rows) 32 rows at
@@ -32,6 +34,8 @@
 //   bwd_creduce   query tokens, the chunks' partial sums then added in order
 //   bwd_cmp_w /   dW = sum over blocks of dK_cmp x mean^T, and each block's
 //   bwd_cmp_tok   W^T dK_cmp / 64 added to its 64 tokens' dk (dv likewise)
+#include <type_traits>
+
 #include "nsa_kernels.h"
 #include "nsa_index.h"
 #include "nsa_tiles.h"
@@ -196,8 +200,12 @@ __global__ __launch_bounds__(64) void bwd_selfill_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------ query side
+constexpr int kQWaves = 8;        // query tiles (one per wave) per workgroup
+constexpr int kMaxVTile = 8192;   // vision blocks (the prefill limit)
+constexpr int kMaxTopk = 64;
+
 // Scores of one tile transposed: s[kt] = K_kt Q^T (16 keys x 16 rows each)
-// from the tile's section `sec` (K rows, or V rows for dP^T = V dO^T).
+// from a section of K rows (or of V rows, for dP^T = V dO^T).
 template <int D>
 __device__ __forceinline__ void tile_scores(const uint16_t *sec, const u16x8 (&b)[D / 32], f32x4 (&s)[4],
                                             int lane) {
@@ -209,15 +217,14 @@ __device__ __forceinline__ void tile_scores(const uint16_t *sec, const u16x8 (&b
     for (int kt = 0; kt < 4; ++kt) s[kt] = mfma_f16(pk_k_frag<D>(sec, kt, ds, lane), b[ds], s[kt]);
 }
 
-// Pass 1 over one tile: online max and sum of the row's exponentials
-// (log2 domain) and O^T += V^T P^T. valid(kt, i) says whether the row sees
-// key 16 kt + 4 (lane / 16) + i of the tile.
+// Pass 1 over one tile (sections K rows and V^T): online max and sum of the
+// row's exponentials (log2 domain) and O^T += V^T P^T. valid(kt, i) says
+// whether the row sees key 16 kt + 4 (lane / 16) + i of the tile.
 template <int D, class Valid>
-__device__ __forceinline__ void q_pass1(const uint16_t *tile, const u16x8 (&qf)[D / 32], f32x4 (&oa)[D / 16],
-                                        float &m, float &l, float sl2, Valid valid, int lane) {
-  constexpr int SEC = BwdTile<D>::SEC;
+__device__ __forceinline__ void q_pass1(const uint16_t *kp, const uint16_t *vtp, const u16x8 (&qf)[D / 32],
+                                        f32x4 (&oa)[D / 16], float &m, float &l, float sl2, Valid valid, int lane) {
   f32x4 s[4];
-  tile_scores<D>(tile, qf, s, lane);
+  tile_scores<D>(kp, qf, s, lane);
   float mx = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
@@ -249,19 +256,18 @@ __device__ __forceinline__ void q_pass1(const uint16_t *tile, const u16x8 (&qf)[
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) oa[dt] = mfma_f16(pk_v_frag<D>(tile + 3 * SEC, dt, kh, lane), pp[kh], oa[dt]);
+    for (int dt = 0; dt < D / 16; ++dt) oa[dt] = mfma_f16(pk_v_frag<D>(vtp, dt, kh, lane), pp[kh], oa[dt]);
 }
 
-// Pass 2 over one tile: P from the row's log-sum-exp, dP^T = V dO^T,
-// dS = sig P (dP - dd), dq^T += K^T dS^T.
+// Pass 2 over one tile (sections K rows, V rows, K^T): P from the row's
+// log-sum-exp, dP^T = V dO^T, dS = sig P (dP - dd), dq^T += K^T dS^T.
 template <int D, class Valid>
-__device__ __forceinline__ void q_pass2(const uint16_t *tile, const u16x8 (&qf)[D / 32], const u16x8 (&of)[D / 32],
-                                        f32x4 (&dqa)[D / 16], float lse2, float dd, float sig, float sl2,
-                                        Valid valid, int lane) {
-  constexpr int SEC = BwdTile<D>::SEC;
+__device__ __forceinline__ void q_pass2(const uint16_t *kp, const uint16_t *vp, const uint16_t *ktp,
+                                        const u16x8 (&qf)[D / 32], const u16x8 (&of)[D / 32], f32x4 (&dqa)[D / 16],
+                                        float lse2, float dd, float sig, float sl2, Valid valid, int lane) {
   f32x4 s[4], dp[4];
-  tile_scores<D>(tile, qf, s, lane);
-  tile_scores<D>(tile + SEC, of, dp, lane);
+  tile_scores<D>(kp, qf, s, lane);
+  tile_scores<D>(vp, of, dp, lane);
   const bool has = lse2 != -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
@@ -274,8 +280,7 @@ __device__ __forceinline__ void q_pass2(const uint16_t *tile, const u16x8 (&qf)[
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      dqa[dt] = mfma_f16(pk_v_frag<D>(tile + 2 * SEC, dt, kh, lane), pd[kh], dqa[dt]);
+    for (int dt = 0; dt < D / 16; ++dt) dqa[dt] = mfma_f16(pk_v_frag<D>(ktp, dt, kh, lane), pd[kh], dqa[dt]);
 }
 
 // Query rows of one wave: TP tokens x G heads (+ padding rows) of one KV
@@ -302,9 +307,61 @@ struct QRows {
   }
 };
 
-// The wave's two passes over one branch's key tiles (walk(f) calls
-// f(tile pointer, valid functor) for every tile, in the same order both
-// times), with the row statistics and gate gradient written in between.
+// The query operands of a wave: Q^T and dO^T fragments (B operands, fp16).
+template <int D>
+__device__ __forceinline__ void q_operands(const BwdParams &p, bool rv, int64_t qrow, u16x8 (&qf)[D / 32],
+                                           u16x8 (&of)[D / 32], int lane) {
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) {
+    qf[ds] = rv ? bf2h8(q_frag_global(p.q + qrow * D, ds, lane)) : zero8();
+    u16x8 o = zero8();
+    if (rv) {
+      const float *src = p.dout + qrow * D + 32 * ds + 8 * (lane >> 4);
+      o = pack_p(*reinterpret_cast<const f32x4 *>(src), *reinterpret_cast<const f32x4 *>(src + 4));
+    }
+    of[ds] = o;
+  }
+}
+
+// Global section of backward-tile slot s in each pass: pass 1 stages K rows
+// and V^T, pass 2 K rows, V rows and K^T.
+template <int PASS>
+__device__ __forceinline__ constexpr int pass_sec(int s) { return PASS == 1 ? (s == 0 ? 0 : 3) : s; }
+
+// The workgroup walks n tiles in lockstep (n and tile_of(i), the global
+// base of tile i, are the same for every wave): each step copies the next
+// tile's sections of this pass into the other LDS buffer by direct
+// global->LDS loads, the copies split over the waves, while every wave runs
+// body(i, staged sections) on the current tile; then each wave waits for its
+// own copies and the workgroup meets at a barrier.
+template <int D, int PASS, class TileOf, class Body>
+__device__ __forceinline__ void lockstep(int n, TileOf tile_of, uint16_t *lds, Body body, int wv, int lane) {
+  constexpr int SEC = BwdTile<D>::SEC, NSEC = PASS == 1 ? 2 : 3, PPS = SEC / 512, PPW = NSEC * PPS / kQWaves;
+  static_assert((NSEC * PPS) % kQWaves == 0, "copies split evenly over the waves");
+  auto copy = [&](const uint16_t *src, uint16_t *dst) {
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const int pc = wv * PPW + j, sl = pc / PPS, off = pc % PPS;
+      __builtin_amdgcn_global_load_lds(src + pass_sec<PASS>(sl) * SEC + off * 512 + lane * 8,
+                                       (lds_void *)(dst + sl * SEC + off * 512), 16, 0, 0);
+    }
+  };
+  if (n <= 0) return;
+  copy(tile_of(0), lds);
+  wait_vm_c<0>();
+  bare_barrier();
+  for (int i = 0; i < n; ++i) {
+    if (i + 1 < n) copy(tile_of(i + 1), lds + ((i + 1) & 1) * 3 * SEC);
+    body(i, lds + (i & 1) * 3 * SEC);
+    wait_vm_c<0>();
+    bare_barrier();
+  }
+}
+
+// One branch for the wave's rows: pass 1 (log-sum-exp, o, then D = dout . o,
+// the statistics for the key side and the gate gradient), pass 2 (dq).
+// walk(pass tag, f) calls f(section 0, 1, 2, valid) for the tiles the wave
+// needs, in the same order in both passes.
 template <int D, class Walk>
 __device__ __forceinline__ void q_branch(const BwdParams &p, Walk walk, const u16x8 (&qf)[D / 32],
                                          const u16x8 (&of)[D / 32], f32x4 (&dqa)[D / 16], bool rv,
@@ -315,7 +372,9 @@ __device__ __forceinline__ void q_branch(const BwdParams &p, Walk walk, const u1
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oa[dt] = zero4();
   float m = -INFINITY, l = 0.f;
-  walk([&](const uint16_t *tile, auto valid) { q_pass1<D>(tile, qf, oa, m, l, sl2, valid, lane); });
+  walk(std::integral_constant<int, 1>(), [&](const uint16_t *s0, const uint16_t *s1, const uint16_t *, auto valid) {
+    q_pass1<D>(s0, s1, qf, oa, m, l, sl2, valid, lane);
+  });
   const float L = grp_sum(l);
   const bool has = rv && L > 0.f;
   const float lse2 = has ? m + __log2f(L) : -INFINITY;
@@ -334,120 +393,153 @@ __device__ __forceinline__ void q_branch(const BwdParams &p, Walk walk, const u1
     stat[1] = dd;
     if (dgate) *dgate = sig * (1.f - sig) * dd;
   }
-  walk([&](const uint16_t *tile, auto valid) { q_pass2<D>(tile, qf, of, dqa, lse2, dd, sig, sl2, valid, lane); });
+  walk(std::integral_constant<int, 2>(), [&](const uint16_t *s0, const uint16_t *s1, const uint16_t *s2, auto valid) {
+    q_pass2<D>(s0, s1, s2, qf, of, dqa, lse2, dd, sig, sl2, valid, lane);
+  });
 }
 
+// Vision rows: workgroup = kQWaves consecutive query tiles of one KV group;
+// the three branches' key tiles are staged once for all its waves.
 template <int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_q_kernel(BwdParams p, int n_qt) {
+__global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_q_kernel(BwdParams p,
+                                                                                                    int n_qt) {
   using R = QRows<D, G, false>;
-  constexpr int TP = R::TP, DS = D / 32, DT = D / 16, SEC4 = BwdTile<D>::E;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int TP = R::TP, DT = D / 16, SEC = BwdTile<D>::SEC, E = BwdTile<D>::E, TW = TP * kQWaves;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * SEC];
+  __shared__ uint32_t ubits[kMaxVTile / 32];   // union of the workgroup's selected blocks
+  __shared__ uint16_t ulist[TW * kMaxTopk];    // the union, ascending
+  __shared__ int n_union;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // workgroups go to the eight XCDs round-robin: give each XCD one
   // contiguous run of query tiles (neighbours share key tiles in its L2)
   const int nwg = gridDim.x, bid = blockIdx.x;
   const int wg = (bid & 7) * (nwg >> 3) + (bid >> 3);
-  const int item = wg * 4 + wv;
-  if (item >= n_qt * p.hkv) return;
-  const int g = item / n_qt, qt = item % n_qt;
+  const int n_grp = (n_qt + kQWaves - 1) / kQWaves;
+  if (wg >= n_grp * p.hkv) return;  // the whole workgroup
+  const int g = wg / n_grp, qg = wg % n_grp, qt = qg * kQWaves + wv;
   const R r(p, qt, g, lane);
   const float sl2 = p.scale * kLog2e;
-  u16x8 qf[DS], of[DS];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    qf[ds] = r.rv ? bf2h8(q_frag_global(p.q + r.qrow * D, ds, lane)) : zero8();
-    u16x8 o = zero8();
-    if (r.rv) {
-      const float *src = p.dout + r.qrow * D + 32 * ds + 8 * r.grp;
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(src), b = *reinterpret_cast<const f32x4 *>(src + 4);
-      o = pack_p(a, b);
-    }
-    of[ds] = o;
-  }
+  const int n_tok = (int)p.n_vis;
+  const int wt_first = qg * TW, wt_last = min(qg * TW + TW, n_tok) - 1;  // the workgroup's tokens
+  const int t_first = qt * TP, t_last = min(qt * TP + TP, n_tok) - 1;    // the wave's (t_last < t_first: none)
+  const int grp = r.grp, tok = r.tok;
+  u16x8 qf[D / 32], of[D / 32];
+  q_operands<D>(p, r.rv, r.qrow, qf, of, lane);
   f32x4 dqa[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dqa[dt] = zero4();
-  const int n_tok = (int)p.n_vis;
-  const int t_first = qt * TP, t_last = min(qt * TP + TP, n_tok) - 1;
-  const int grp = r.grp, tok = r.tok;
-
-  {
-    float *stat = p.vstat + ((int64_t)(r.rv ? tok : 0) * p.hq + r.hq) * 6;
-    float *dg = p.dgate + r.qrow * 3;
-    float sig[3];
+  float *stat = p.vstat + ((int64_t)(r.rv ? tok : 0) * p.hq + r.hq) * 6;
+  float *dg = p.dgate + r.qrow * 3;
+  float sig[3];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) sig[c] = r.rv ? sigmoidf_(p.gates[r.qrow * 3 + c]) : 0.f;
-    // compression: compressed keys b with (b + 1) 64 <= t + 1
-    {
-      const int nc = (t_last + 1) / kBlk;
-      const int n_tiles = (nc + kBlk - 1) / kBlk;
-      auto walk = [&](auto f) {
-        for (int tl = 0; tl < n_tiles; ++tl) {
-          const int b0 = tl * kBlk + 4 * grp;
-          f(p.tile_c + ((int64_t)g * p.n_ctile + tl) * SEC4,
-            [&](int kt, int i) { return (b0 + 16 * kt + i + 1) * kBlk <= tok + 1; });
-        }
-      };
-      q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[0], sl2, stat, dg, lane);
+  for (int c = 0; c < 3; ++c) sig[c] = r.rv ? sigmoidf_(p.gates[r.qrow * 3 + c]) : 0.f;
+
+  // compression: compressed keys b with (b + 1) 64 <= t + 1
+  {
+    const int nc = (wt_last + 1) / kBlk;
+    const int n_tiles = (nc + kBlk - 1) / kBlk;
+    auto walk = [&](auto pass, auto f) {
+      lockstep<D, decltype(pass)::value>(
+          n_tiles, [&](int i) { return p.tile_c + ((int64_t)g * p.n_ctile + i) * E; }, lds,
+          [&](int i, const uint16_t *b) {
+            const int b0 = i * kBlk + 4 * grp;
+            f(b, b + SEC, b + 2 * SEC, [&](int kt, int e) { return (b0 + 16 * kt + e + 1) * kBlk <= tok + 1; });
+          },
+          wv, lane);
+    };
+    q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[0], sl2, stat, dg, lane);
+  }
+  // selection: the union of the workgroup's lists, each wave computing the
+  // tiles its tokens chose (rows masked to their own token's blocks, keys
+  // j <= t)
+  {
+    int lst[TP];
+#pragma unroll
+    for (int q = 0; q < TP; ++q) {
+      const int tq = t_first + q;
+      int b = kSentinel;
+      if (tq <= t_last && lane < p.topk) {
+        const int32_t e = p.sel[((int64_t)tq * p.hkv + g) * p.topk + lane];
+        b = sel_entry_valid(e, tq) ? (int)e : kSentinel;
+      }
+      lst[q] = b;
     }
-    // selection: the union of the tile's tokens' lists, each row masked to
-    // its own token's blocks (keys j <= t)
-    {
-      int lst[TP];
+    const int n_words = (p.n_vtile + 31) / 32;
+    for (int w = tid; w < n_words; w += 64 * kQWaves) ubits[w] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < TP; ++q)
+      if (lst[q] != kSentinel) atomicOr(&ubits[lst[q] >> 5], 1u << (lst[q] & 31));
+    __syncthreads();
+    if (wv == 0) {  // compact the bitmask into the ascending union
+      int base = 0;
+      for (int w0 = 0; w0 < n_words; w0 += 64) {
+        uint32_t bits = w0 + lane < n_words ? ubits[w0 + lane] : 0u;
+        const int c = __popc(bits);
+        int incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_up(incl, o);
+          if (lane >= o) incl += v;
+        }
+        int at = base + incl - c;
+        while (bits) {
+          ulist[at++] = (uint16_t)(32 * (w0 + lane) + __ffs(bits) - 1);
+          bits &= bits - 1u;
+        }
+        base += __shfl(incl, 63);
+      }
+      if (lane == 0) n_union = base;
+    }
+    __syncthreads();
+    const int nu = n_union, tau = r.tau;
+    auto walk = [&](auto pass, auto f) {
+      int cur[TP], nxt[TP];
 #pragma unroll
       for (int q = 0; q < TP; ++q) {
-        const int tq = t_first + q;
-        int b = kSentinel;
-        if (tq <= t_last && lane < p.topk) {
-          const int32_t e = p.sel[((int64_t)tq * p.hkv + g) * p.topk + lane];
-          b = sel_entry_valid(e, tq) ? (int)e : kSentinel;
-        }
-        lst[q] = b;
+        cur[q] = 0;
+        nxt[q] = __builtin_amdgcn_readlane(lst[q], 0);
       }
-      const int tau = r.tau;
-      auto walk = [&](auto f) {
-        int cur[TP], nxt[TP];
+      lockstep<D, decltype(pass)::value>(
+          nu, [&](int i) { return p.tile_v + ((int64_t)g * p.n_vtile + ulist[i]) * E; }, lds,
+          [&](int i, const uint16_t *b) {
+            const int u = ulist[i];
+            uint32_t need = 0u;
 #pragma unroll
-        for (int q = 0; q < TP; ++q) {
-          cur[q] = 0;
-          nxt[q] = __builtin_amdgcn_readlane(lst[q], 0);
-        }
-        for (;;) {
-          int u = kSentinel;
-#pragma unroll
-          for (int q = 0; q < TP; ++q) u = min(u, nxt[q]);
-          if (u == kSentinel) break;
-          uint32_t need = 0u;
-#pragma unroll
-          for (int q = 0; q < TP; ++q) {
-            if (nxt[q] == u) {
-              need |= 1u << q;
-              ++cur[q];
-              nxt[q] = cur[q] < p.topk ? __builtin_amdgcn_readlane(lst[q], cur[q]) : kSentinel;
+            for (int q = 0; q < TP; ++q) {
+              if (nxt[q] == u) {
+                need |= 1u << q;
+                ++cur[q];
+                nxt[q] = cur[q] < p.topk ? __builtin_amdgcn_readlane(lst[q], cur[q]) : kSentinel;
+              }
             }
-          }
-          const bool rowneed = r.rv && ((need >> tau) & 1u);
-          const int j0 = u * kBlk + 4 * grp;
-          f(p.tile_v + ((int64_t)g * p.n_vtile + u) * SEC4,
-            [&](int kt, int i) { return rowneed && j0 + 16 * kt + i <= tok; });
-        }
-      };
-      q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[1], sl2, stat + 2, dg + 1, lane);
-    }
-    // sliding window: keys t - w < j <= t
-    {
-      const int lo = max(0, t_first - p.window + 1) / kBlk, hi = t_last / kBlk;
-      const int w = p.window;
-      auto walk = [&](auto f) {
-        for (int tl = lo; tl <= hi; ++tl) {
-          const int j0 = tl * kBlk + 4 * grp;
-          f(p.tile_v + ((int64_t)g * p.n_vtile + tl) * SEC4, [&](int kt, int i) {
-            const int j = j0 + 16 * kt + i;
-            return j <= tok && j > tok - w;
-          });
-        }
-      };
-      q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[2], sl2, stat + 4, dg + 2, lane);
-    }
+            if (need) {  // wave-uniform
+              const bool rowneed = r.rv && ((need >> tau) & 1u);
+              const int j0 = u * kBlk + 4 * grp;
+              f(b, b + SEC, b + 2 * SEC, [&](int kt, int e) { return rowneed && j0 + 16 * kt + e <= tok; });
+            }
+          },
+          wv, lane);
+    };
+    q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[1], sl2, stat + 2, dg + 1, lane);
+  }
+  // sliding window: keys t - w < j <= t
+  {
+    const int lo = max(0, wt_first - p.window + 1) / kBlk, hi = wt_last / kBlk;
+    const int w = p.window;
+    auto walk = [&](auto pass, auto f) {
+      lockstep<D, decltype(pass)::value>(
+          hi - lo + 1, [&](int i) { return p.tile_v + ((int64_t)g * p.n_vtile + lo + i) * E; }, lds,
+          [&](int i, const uint16_t *b) {
+            const int j0 = (lo + i) * kBlk + 4 * grp;
+            f(b, b + SEC, b + 2 * SEC, [&](int kt, int e) {
+              const int j = j0 + 16 * kt + e;
+              return j <= tok && j > tok - w;
+            });
+          },
+          wv, lane);
+    };
+    q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[2], sl2, stat + 4, dg + 2, lane);
   }
   if (r.rv) {
 #pragma unroll
@@ -457,46 +549,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 }
 
 // Text rows: dense causal attention over every earlier position, split
-// over the key tiles so that the few text rows still fill the chip. Wave
-// (split, group, tile of 16/G text tokens) takes its split's share of the
-// position tiles. Pass 1 writes the split's (max, sum, unnormalised o) per
-// row; bwd_qtmerge combines the splits into the row statistics; pass 2
-// writes the split's share of dq, which bwd_qtsum adds in split order.
+// over the key tiles so that the few text rows still fill the chip. A
+// workgroup is (split, group, kQWaves tiles of 16/G text tokens) and walks
+// its split's share of the position tiles in lockstep. Pass 1 writes the
+// split's (max, sum, unnormalised o) per row; bwd_qtmerge combines the
+// splits into the row statistics; pass 2 writes the split's share of dq,
+// which bwd_qtsum adds in split order.
 template <int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_qt_kernel(BwdParams p, int n_qt,
-                                                                                           int pass) {
+__global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_qt_kernel(BwdParams p,
+                                                                                                     int n_qt,
+                                                                                                     int pass) {
   using R = QRows<D, G, true>;
-  constexpr int TP = R::TP, DS = D / 32, DT = D / 16, SEC4 = BwdTile<D>::E;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int item = blockIdx.x * 4 + wv;
-  if (item >= p.n_tsplit * p.hkv * n_qt) return;
-  const int qt = item % n_qt, g = (item / n_qt) % p.hkv, sp = item / (n_qt * p.hkv);
+  constexpr int TP = R::TP, DT = D / 16, SEC = BwdTile<D>::SEC, E = BwdTile<D>::E, TW = TP * kQWaves;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * SEC];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n_grp = (n_qt + kQWaves - 1) / kQWaves;
+  const int wg = blockIdx.x;
+  const int qg = wg % n_grp, g = (wg / n_grp) % p.hkv, sp = wg / (n_grp * p.hkv);
+  const int qt = qg * kQWaves + wv;
   const R r(p, qt, g, lane);
   const int n_text = (int)(p.n - p.n_vis);
-  const int t_last = min(qt * TP + TP, n_text) - 1;
-  const int64_t pos_last = t_last < p.v0 ? (int64_t)t_last : (int64_t)t_last + p.n_vis;
+  const int wt_last = min(qg * TW + TW, n_text) - 1;
+  const int64_t pos_last = wt_last < p.v0 ? (int64_t)wt_last : (int64_t)wt_last + p.n_vis;
   const int n_tiles = (int)(pos_last / kBlk) + 1;
   const int lo = (int)((int64_t)sp * n_tiles / p.n_tsplit), hi = (int)((int64_t)(sp + 1) * n_tiles / p.n_tsplit);
   const float sl2 = p.scale * kLog2e;
   const int grp = r.grp;
   const int64_t mypos = r.pos;
   const int64_t trow = (int64_t)(r.rv ? r.tok : 0) * p.hq + r.hq;  // text row x head
-  float *part = p.tpart + ((int64_t)sp * n_text * p.hq + trow) * (D + 2);
-  u16x8 qf[DS];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) qf[ds] = r.rv ? bf2h8(q_frag_global(p.q + r.qrow * D, ds, lane)) : zero8();
+  u16x8 qf[D / 32], of[D / 32];
+  q_operands<D>(p, r.rv, r.qrow, qf, of, lane);
+  auto tile_of = [&](int i) { return p.tile_p + ((int64_t)g * p.n_ptile + lo + i) * E; };
   if (pass == 1) {
     f32x4 oa[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oa[dt] = zero4();
     float m = -INFINITY, l = 0.f;
-    for (int tl = lo; tl < hi; ++tl) {
-      const int64_t k0 = (int64_t)tl * kBlk + 4 * grp;
-      q_pass1<D>(p.tile_p + ((int64_t)g * p.n_ptile + tl) * SEC4, qf, oa, m, l, sl2,
-                 [&](int kt, int i) { return k0 + 16 * kt + i <= mypos; }, lane);
-    }
+    lockstep<D, 1>(hi - lo, tile_of, lds, [&](int i, const uint16_t *b) {
+      const int64_t k0 = (int64_t)(lo + i) * kBlk + 4 * grp;
+      q_pass1<D>(b, b + SEC, qf, oa, m, l, sl2, [&](int kt, int e) { return k0 + 16 * kt + e <= mypos; }, lane);
+    }, wv, lane);
     const float L = grp_sum(l);
     if (r.rv) {
+      float *part = p.tpart + ((int64_t)sp * n_text * p.hq + trow) * (D + 2);
       if (grp == 0) {
         part[0] = m;
         part[1] = L;
@@ -508,25 +603,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       }
     }
   } else {
-    u16x8 of[DS];
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      u16x8 o = zero8();
-      if (r.rv) {
-        const float *src = p.dout + r.qrow * D + 32 * ds + 8 * grp;
-        o = pack_p(*reinterpret_cast<const f32x4 *>(src), *reinterpret_cast<const f32x4 *>(src + 4));
-      }
-      of[ds] = o;
-    }
     const float lse2 = r.rv ? p.tstat[trow * 2] : -INFINITY, dd = r.rv ? p.tstat[trow * 2 + 1] : 0.f;
     f32x4 dqa[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dqa[dt] = zero4();
-    for (int tl = lo; tl < hi; ++tl) {
-      const int64_t k0 = (int64_t)tl * kBlk + 4 * grp;
-      q_pass2<D>(p.tile_p + ((int64_t)g * p.n_ptile + tl) * SEC4, qf, of, dqa, lse2, dd, 1.f, sl2,
-                 [&](int kt, int i) { return k0 + 16 * kt + i <= mypos; }, lane);
-    }
+    lockstep<D, 2>(hi - lo, tile_of, lds, [&](int i, const uint16_t *b) {
+      const int64_t k0 = (int64_t)(lo + i) * kBlk + 4 * grp;
+      q_pass2<D>(b, b + SEC, b + 2 * SEC, qf, of, dqa, lse2, dd, 1.f, sl2,
+                 [&](int kt, int e) { return k0 + 16 * kt + e <= mypos; }, lane);
+    }, wv, lane);
     if (r.rv) {
       float *dst = p.tpart + ((int64_t)sp * n_text * p.hq + trow) * D;  // pass-1 partials are merged by now
 #pragma unroll
@@ -955,19 +1040,20 @@ hipError_t run_g(const BwdParams &p, int stage, hipStream_t st) {
   switch (stage) {
     case 7: {  // query side, vision rows
       const int n_qt = (int)((p.n_vis + TP - 1) / TP);
-      const int64_t n_wg = ((int64_t)n_qt * p.hkv + 3) / 4;
+      const int64_t n_wg = (int64_t)((n_qt + kQWaves - 1) / kQWaves) * p.hkv;
       if (n_wg == 0) return hipSuccess;
-      hipLaunchKernelGGL((bwd_q_kernel<D, G>), dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(256), 0, st, p, n_qt);
+      hipLaunchKernelGGL((bwd_q_kernel<D, G>), dim3((unsigned)((n_wg + 7) / 8 * 8)), dim3(64 * kQWaves), 0, st, p,
+                         n_qt);
       break;
     }
     case 8: {  // query side, text rows: split pass 1, merge, split pass 2, sum
       const int64_t n_text = p.n - p.n_vis;
       const int n_qt = (int)((n_text + TP - 1) / TP);
-      const int64_t n_wg = ((int64_t)n_qt * p.hkv * p.n_tsplit + 3) / 4;
+      const int64_t n_wg = (int64_t)((n_qt + kQWaves - 1) / kQWaves) * p.hkv * p.n_tsplit;
       if (n_wg == 0) return hipSuccess;
-      hipLaunchKernelGGL((bwd_qt_kernel<D, G>), dim3((unsigned)n_wg), dim3(256), 0, st, p, n_qt, 1);
+      hipLaunchKernelGGL((bwd_qt_kernel<D, G>), dim3((unsigned)n_wg), dim3(64 * kQWaves), 0, st, p, n_qt, 1);
       hipLaunchKernelGGL((bwd_qtmerge_kernel<D>), dim3((unsigned)(n_text * p.hq)), dim3(D), 0, st, p);
-      hipLaunchKernelGGL((bwd_qt_kernel<D, G>), dim3((unsigned)n_wg), dim3(256), 0, st, p, n_qt, 2);
+      hipLaunchKernelGGL((bwd_qt_kernel<D, G>), dim3((unsigned)n_wg), dim3(64 * kQWaves), 0, st, p, n_qt, 2);
       hipLaunchKernelGGL((bwd_qtsum_kernel<D>), dim3((unsigned)(n_text * p.hq)), dim3(D), 0, st, p);
       break;
     }
