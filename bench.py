@@ -516,6 +516,10 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-workload", choices=("both", "short", "qwen_36k"), default="both",
+                    help="backward legs: 4,096 + 512 tokens, the 36,864 + 512 training length, or both")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the 36K / 64K per-branch legs (for profiler runs of the headline workload)")
     ap.add_argument("--scaling", action="store_true",
                     help="also time 16K..512K vision tokens (about a minute more, mostly input generation)")
     args = ap.parse_args()
@@ -600,9 +604,13 @@ def main():
     backward = None
     if not args.no_backward:
         short = shape.replace(n_vis=BWD_SHAPE["n_vis"], n_text_before=0, n_text_after=BWD_SHAPE["n_text_after"])
-        backward = run_backward_bench(short, 3, 1)
         # the pages' training context (model card, "Training Details": 36K tokens)
-        backward["training_length"] = run_backward_bench(PREFILL_PRESETS["qwen_36k"], 2, 1)
+        if args.backward_workload == "qwen_36k":
+            backward = run_backward_bench(PREFILL_PRESETS["qwen_36k"], 3, 1)
+        else:
+            backward = run_backward_bench(short, 3, 1)
+            if args.backward_workload == "both":
+                backward["training_length"] = run_backward_bench(PREFILL_PRESETS["qwen_36k"], 3, 1)
 
     spans = None
     if not args.no_spans:
@@ -611,7 +619,7 @@ def main():
     # the pages' training length and the per-branch split workload (36,864
     # and 65,536 vision + 512 text tokens, k 16, w 512), always; 16K..512K
     # at the headline's k and w on request
-    scaling = run_context_bench(("qwen_36k", "qwen_64k"), max(3, args.steps // 2), 1)
+    scaling = [] if args.no_context else run_context_bench(("qwen_36k", "qwen_64k"), max(3, args.steps // 2), 1)
     if args.scaling:
         scaling += run_scaling_bench(shape, max(3, args.steps // 2), 1)
 

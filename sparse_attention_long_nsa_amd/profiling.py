@@ -165,8 +165,8 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
         d = bench["backward"]
         lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per backward call over "
                   f"{d['n_vision']} vision + {d['n_text']} text tokens (k {d['top_k']}, w {d['window']}): "
-                  f"{d['tflops']} TF/s of algorithmic flops; its event-timed per-kernel averages are "
-                  "listed beside the profiler's.", ""]
+                  f"{d['tflops']} TF/s of algorithmic flops ({d.get('mfma_peak_frac', 0) * 100:.1f}% of the "
+                  "fp16 matrix peak); its event-timed per-kernel averages are listed beside the profiler's.", ""]
     elif bench and group == "gate" and bench.get("gate_prologue"):
         d = bench["gate_prologue"]
         lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per gate prologue over "
