@@ -626,6 +626,11 @@ def main():
     # the published peak checked on this GPU with an MFMA-loop probe
     from sparse_attention_long_nsa_amd.profiling import mfma_peak
     probe = mfma_peak()
+    # the fabric rate of the selection kernel's block copies (pseudo-random
+    # whole 32 KB blocks) at buffer sizes from L2-resident to far beyond it
+    from sparse_attention_long_nsa_amd.profiling import block_stream
+    stream_probe = block_stream()
+    log(f"block-stream probe: {stream_probe}")
     probe["frac_of_published"] = round(probe["tflops"] / PEAK_BF16_TFLOPS, 4)
     log(f"mfma loop probe: {probe}")
 
@@ -655,6 +660,7 @@ def main():
         "mfma_peak_frac": round(layer_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "algorithmic_tflop": round(layer_flops / 1e12, 3),
         "mfma_loop_probe": probe,
+        "block_stream_probe": stream_probe,
         "roofline": roofline,
         "branch_ms": branch_ms,
         "kernels": per_kernel,

@@ -366,6 +366,20 @@ int nsa_timing_read(int max_entries, const char **names, double *total_ms, int *
  * NSA_ERR_INVALID_ARG for n_wg < 1, iters < 1 or out == NULL. */
 nsa_status nsa_probe_mfma_bf16(int32_t n_wg, int32_t iters, float *out, void *stream);
 
+/* Block-stream probe (measurement aid; computes nothing of the layer): the
+ * fabric rate of the selection kernel's access pattern. Launches n_wg
+ * workgroups of eight waves; each reads `iters` pseudo-random whole 32 KB
+ * blocks of buf (n_blocks blocks, device, 16-byte aligned, caller-owned;
+ * every block index is taken modulo n_blocks) with 16-byte loads, two
+ * blocks in flight, and writes one checksum word per thread to
+ * out[n_wg * 512] (device, caller-owned). Bytes read per call:
+ * n_wg * iters * 32768; time it with events on `stream`. With buf much
+ * larger than the L2 the rate is what L2 misses of such blocks reach.
+ * NSA_ERR_INVALID_ARG for a NULL or misaligned pointer, n_blocks < 1,
+ * n_wg < 1, or iters not a positive even number. */
+nsa_status nsa_probe_block_stream(const void *buf, int64_t n_blocks, int32_t n_wg, int32_t iters,
+                                  uint32_t *out, void *stream);
+
 /* Status word of a prefill workspace (the first 4 bytes of the workspace
  * passed to nsa_prefill or nsa_prefill_varlen, cleared at the start of every
  * such call): waits on `stream` for the work enqueued so far, copies the word

@@ -26,7 +26,7 @@ EXPORTED = (
     "nsa_prefill_varlen_workspace_size", "nsa_prefill_varlen",
     "nsa_gate_workspace_size", "nsa_gate_logits",
     "nsa_prefill_backward_workspace_size", "nsa_prefill_backward", "nsa_decode_noalloc",
-    "nsa_workspace_status", "nsa_debug_set_spin_limit",
+    "nsa_workspace_status", "nsa_debug_set_spin_limit", "nsa_probe_block_stream",
 )
 
 # size of the library's fixed decode scratch (nsa.h NSA_DECODE_NOALLOC_SCRATCH_BYTES)
@@ -139,6 +139,8 @@ def lib() -> ctypes.CDLL:
         L.nsa_version.restype = ctypes.c_char_p
         L.nsa_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
         L.nsa_probe_mfma_bf16.restype = ctypes.c_int
+        L.nsa_probe_block_stream.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P]
+        L.nsa_probe_block_stream.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -568,6 +570,20 @@ def cmp_pool(x, w, block=64, out_bf16=True, out_f32=False, stream=None) -> dict:
 
 
 MFMA_PROBE_FLOPS_PER_WAVE_ROUND = 128 * 16384  # 128 products of 16x16x32 per round
+
+
+def probe_block_stream(buf, n_wg: int, iters: int, out, stream=None) -> int:
+    """Runs nsa_probe_block_stream over buf (a device tensor, a whole number
+    of 32 KB blocks) into out (uint32 as int32 [n_wg * 512], device); returns
+    the bytes it reads."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_cuda or not buf.is_contiguous() or nbytes % 32768 != 0:
+        raise ValueError("buf must be a contiguous device tensor of whole 32 KB blocks")
+    _check_dev("out", out, torch.int32, (n_wg * 512,))
+    st = lib().nsa_probe_block_stream(_ptr(buf), nbytes // 32768, n_wg, iters, _ptr(out), _stream(stream))
+    if st != NSA_OK:
+        raise NsaError(st, "nsa_probe_block_stream")
+    return n_wg * iters * 32768
 
 
 def probe_mfma_bf16(n_wg: int, iters: int, out, stream=None) -> int:

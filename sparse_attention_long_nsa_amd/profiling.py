@@ -335,6 +335,33 @@ def mfma_peak(n_wg: int = 256 * 8, iters: int = 400, reps: int = 8) -> dict:
             "workgroups": n_wg, "rounds": iters, "instr": "v_mfma_f32_16x16x32_bf16"}
 
 
+def block_stream(sizes_mib=(4, 64, 268, 1024), n_wg: int = 4096, iters: int = 96, reps: int = 3) -> dict:
+    """Rate of pseudo-random whole 32 KB block reads (the selection kernel's
+    copy pattern) for several buffer sizes: the best of `reps` timed launches
+    of the block-stream probe per size, in TB/s. 268 MiB is the packed
+    key/value size of the 128K workload; 4 MiB fits one XCD's L2."""
+    import torch
+    from sparse_attention_long_nsa_amd import binding
+    out = torch.empty(n_wg * 512, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    res = {}
+    for mib in sizes_mib:
+        buf = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.int32, device="cuda:0")
+        binding.probe_block_stream(buf, n_wg, 2, out, st)  # warm-up
+        best = float("inf")
+        nbytes = 0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            nbytes = binding.probe_block_stream(buf, n_wg, iters, out, st)
+            e1.record(st)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        res[f"{mib}_mib"] = round(nbytes / (best * 1e-3) / 1e12, 2)
+        del buf
+    return {"tb_per_s": res, "block_bytes": 32768, "workgroups": n_wg, "blocks_per_workgroup": iters}
+
+
 def _layer_grids(workload: str) -> dict:
     from sparse_attention_long_nsa_amd.inputs import DECODE_PRESETS, PREFILL_PRESETS
     if workload in DECODE_PRESETS:
@@ -354,6 +381,7 @@ def main(argv=None) -> None:
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=3)
     sub.add_parser("mfma-peak")
+    sub.add_parser("block-stream")
     t = sub.add_parser("trace-summary")
     t.add_argument("--trace-csv", required=True)
     t.add_argument("--bench-log", required=True)
@@ -383,6 +411,8 @@ def main(argv=None) -> None:
         copy_probe(a.mib, a.reps)
     elif a.cmd == "mfma-peak":
         print(json.dumps(mfma_peak()), flush=True)
+    elif a.cmd == "block-stream":
+        print(json.dumps(block_stream()), flush=True)
     elif a.cmd == "trace-summary":
         trace_summary(a.trace_csv, a.bench_log, _layer_grids(a.workload), a.title, a.command, a.out, a.group)
     elif a.cmd == "counter-summary":

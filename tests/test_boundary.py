@@ -437,3 +437,14 @@ def test_prefill_workspace_starts_with_the_status_word():
     one = vision_mask(1024, 0, 1024)
     st, n = ws_size(desc(), one)
     assert st == binding.NSA_OK and n % 256 == 0 and n >= 256
+
+
+def test_block_stream_probe_arguments():
+    L = binding.lib()
+    bad = binding.NSA_ERR_INVALID_ARG
+    assert L.nsa_probe_block_stream(None, 4, 1, 2, FAKE, None) == bad
+    assert L.nsa_probe_block_stream(FAKE, 4, 1, 2, None, None) == bad
+    assert L.nsa_probe_block_stream(FAKE + 4, 4, 1, 2, FAKE, None) == bad  # 16-byte alignment
+    assert L.nsa_probe_block_stream(FAKE, 0, 1, 2, FAKE, None) == bad
+    assert L.nsa_probe_block_stream(FAKE, 4, 0, 2, FAKE, None) == bad
+    assert L.nsa_probe_block_stream(FAKE, 4, 1, 3, FAKE, None) == bad  # blocks go two at a time
