@@ -31,7 +31,12 @@ namespace nsa {
 
 namespace {
 
-constexpr int kDecThreads = 256;
+// Threads of the selection kernel: every chunk partial, score and o_cmp
+// term is loaded in one or two rounds (1,024 threads: 40.9 us per 16 x 128K
+// step against 42.7 at 256); rows of more than 2,048 candidates keep 512
+// threads, where the 128-register cap of 1,024 would spill.
+template <int NPL>
+constexpr int dec_select_threads() { return NPL <= 32 ? 1024 : 512; }
 constexpr int kDecMaxBlk = 8192;
 constexpr int kDecMaxK = 64;
 
@@ -214,7 +219,8 @@ __global__ __launch_bounds__(64 * kItemWaves) void dec_item_kernel(DecodeParams 
 // group's heads of the normalised probability) into LDS, and select the
 // top k-1 of them plus the own block (select_topk_row, wave 0).
 template <int D, int G, int NPL>
-__global__ __launch_bounds__(kDecThreads) void dec_select_kernel(DecodeParams p) {
+__global__ __launch_bounds__(dec_select_threads<NPL>()) void dec_select_kernel(DecodeParams p) {
+  constexpr int kDecThreads = dec_select_threads<NPL>();
   constexpr int NO = kDecThreads - 64;             // threads of waves 1..
   constexpr int OPT = (G * D + NO - 1) / NO;       // o_cmp outputs per thread
   __shared__ float lse2s[G];
@@ -277,7 +283,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_select_kernel(DecodeParams p)
       dd[j] = i % D;
       acc[j] = 0.f;
     }
-#pragma unroll 8
+#pragma unroll 16
     for (int c = 0; c < p.n_chunk; ++c)
 #pragma unroll
       for (int j = 0; j < OPT; ++j) acc[j] += wt[hh[j]][c] * part[hh[j] * hs + (int64_t)c * (D + 2) + 2 + dd[j]];
@@ -334,9 +340,10 @@ hipError_t run_decode(const DecodeParams &p, hipStream_t st) {
     // candidates per lane of the selecting wave: 32 covers caches of up to
     // 2049 blocks (131,136 tokens)
     if (p.own <= 64 * 32)
-      hipLaunchKernelGGL((dec_select_kernel<D, G, 32>), dim3(pairs), dim3(kDecThreads), 0, st, p);
+      hipLaunchKernelGGL((dec_select_kernel<D, G, 32>), dim3(pairs), dim3(dec_select_threads<32>()), 0, st, p);
     else
-      hipLaunchKernelGGL((dec_select_kernel<D, G, kDecMaxBlk / 64>), dim3(pairs), dim3(kDecThreads), 0, st, p);
+      hipLaunchKernelGGL((dec_select_kernel<D, G, kDecMaxBlk / 64>), dim3(pairs),
+                         dim3(dec_select_threads<kDecMaxBlk / 64>()), 0, st, p);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   {

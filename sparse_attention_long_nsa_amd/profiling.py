@@ -57,7 +57,10 @@ KERNELS = [
     ("bwd_pool_kernel", "bwd_pool", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
     ("bwd_pack_kernel", "bwd_pack", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
     ("bwd_sel", "bwd_sellist", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
-    ("bwd_q_kernel", "bwd_q", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_qt_kernel", "bwd_q_text", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_qtmerge_kernel", "bwd_q_text", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_qtsum_kernel", "bwd_q_text", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
+    ("bwd_q_kernel", "bwd_q_vis", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
     ("bwd_kv_kernel", "bwd_kv", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
     ("bwd_kvc_kernel", "bwd_kv_cmp", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
     ("bwd_creduce_kernel", "bwd_cmp_sum", "sparse_attention_long_nsa_amd/csrc/nsa_backward.hip"),
@@ -67,8 +70,8 @@ KERNELS = [
 DECODE_KERNELS = ("dec_item_cmp_win", "dec_item_sel", "dec_select", "dec_combine")
 DENSE_KERNELS = ("pack_dense", "dense_attn")
 GATE_KERNELS = ("gate_hidden", "gate_out")
-BWD_KERNELS = ("bwd_selclear", "bwd_pool", "bwd_pack", "bwd_sellist", "bwd_q", "bwd_kv", "bwd_kv_cmp",
-               "bwd_cmp_sum", "bwd_cmp_w", "bwd_cmp_tok")
+BWD_KERNELS = ("bwd_selclear", "bwd_pool", "bwd_pack", "bwd_sellist", "bwd_q_vis", "bwd_q_text", "bwd_kv",
+               "bwd_kv_cmp", "bwd_cmp_sum", "bwd_cmp_w", "bwd_cmp_tok")
 PREFILL_KERNELS = ("sel_attn", "cmp_attn", "swa_attn", "text_attn", "text_merge", "blk_score_topk", "cmp_pool",
                    "cmp_pool_mean", "cmp_pool_map", "pack_kv", "pack_cmp", "pack_text")
 
@@ -166,7 +169,10 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
         lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per backward call over "
                   f"{d['n_vision']} vision + {d['n_text']} text tokens (k {d['top_k']}, w {d['window']}): "
                   f"{d['tflops']} TF/s of algorithmic flops ({d.get('mfma_peak_frac', 0) * 100:.1f}% of the "
-                  "fp16 matrix peak); its event-timed per-kernel averages are listed beside the profiler's.", ""]
+                  "fp16 matrix peak); its event-timed per-kernel averages are listed beside the profiler's. "
+                  "Rows that stand for several launches per call (bwd_sellist: mask, count, prefix sum, "
+                  "decode; bwd_pack: three tile sets; bwd_q_text: two split passes, merge, sum) give the "
+                  "profiler's average per launch and the events' time for the whole group.", ""]
     elif bench and group == "gate" and bench.get("gate_prologue"):
         d = bench["gate_prologue"]
         lines += [f"bench.py in the same process reported {d['ms_per_step']} ms per gate prologue over "
