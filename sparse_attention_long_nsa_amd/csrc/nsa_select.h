@@ -42,30 +42,31 @@ __device__ __forceinline__ uint32_t kth_largest_lane(uint32_t v, int need) {
   return t;
 }
 
-// Selects for one row of f candidate scores (row[0..f-1], global or LDS):
-// out[0..k-2] = the top k-1 block indices ascending (fewer: all of them,
-// then -1 padding), out[k-1] = f (the own block). One wave; hist is a
-// 256-entry LDS scratch of the calling workgroup. NPL * 64 >= f; NPL loads
-// per lane are issued whatever f is.
+// The row's candidate keys: key = bits + 1 for candidates (so 0.0f still
+// beats padding), 0 otherwise. Every load is issued before the first is
+// used (no branch between them, so one wait covers all): lanes past the row
+// re-read its last entry, so callers pick NPL close to ceil(f / 64). f >= 1.
 template <int NPL>
-__device__ __forceinline__ void select_topk_row(const float *row, int f, int k, int32_t *out, uint32_t *hist,
-                                                int lane) {
+__device__ __forceinline__ void topk_load_keys(const float *row, int f, uint32_t (&key)[NPL], int lane) {
+#pragma unroll
+  for (int s = 0; s < NPL; ++s) key[s] = __float_as_uint(row[min(s * 64 + lane, f - 1)]);
+#pragma unroll
+  for (int s = 0; s < NPL; ++s) key[s] = s * 64 + lane < f ? key[s] + 1u : 0u;
+}
+
+// Selects for one row of f candidate scores whose keys topk_load_keys
+// produced: out[0..k-2] = the top k-1 block indices ascending (fewer: all of
+// them, then -1 padding), out[k-1] = f (the own block). One wave; hist is a
+// 256-entry LDS scratch of the calling wave. NPL * 64 >= f.
+template <int NPL>
+__device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[NPL], int f, int k, int32_t *out,
+                                                 uint32_t *hist, int lane) {
   const int need = k - 1;
 
   if (f <= need) {  // every candidate is kept
     for (int i = lane; i < k; i += 64) out[i] = i < f ? i : (i == f ? f : -1);
     return;
   }
-
-  // key = bits + 1 for candidates (so 0.0f still beats padding), 0 otherwise.
-  // Every load is issued before the first is used (no branch between them,
-  // so one wait covers all): lanes past the row re-read its last entry, so
-  // callers pick NPL close to ceil(f / 64).
-  uint32_t key[NPL];
-#pragma unroll
-  for (int s = 0; s < NPL; ++s) key[s] = __float_as_uint(row[min(s * 64 + lane, f - 1)]);
-#pragma unroll
-  for (int s = 0; s < NPL; ++s) key[s] = s * 64 + lane < f ? key[s] + 1u : 0u;
 
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   {
@@ -162,6 +163,18 @@ __device__ __forceinline__ void select_topk_row(const float *row, int f, int k, 
     eq_taken += __popcll(__ballot(eq_take));
   }
   if (lane == 0) out[need] = f;  // own block, larger than every candidate
+}
+
+// Selects for one row of f candidate scores (row[0..f-1], global or LDS):
+// out[0..k-2] = the top k-1 block indices ascending (fewer: all of them,
+// then -1 padding), out[k-1] = f (the own block). NPL loads per lane are
+// issued whatever f is; a row of at most k - 1 candidates reads nothing.
+template <int NPL>
+__device__ __forceinline__ void select_topk_row(const float *row, int f, int k, int32_t *out, uint32_t *hist,
+                                                int lane) {
+  uint32_t key[NPL];
+  if (f > k - 1) topk_load_keys<NPL>(row, f, key, lane);  // wave-uniform
+  topk_select_keys<NPL>(key, f, k, out, hist, lane);
 }
 
 }  // namespace nsa

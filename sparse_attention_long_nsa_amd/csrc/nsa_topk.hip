@@ -28,11 +28,12 @@ __device__ __forceinline__ void select_sized(const float *row, int f, int k, int
   select_topk_row<NPL>(row, f, k, out, hist, lane);
 }
 
-// Rows of up to 2,048 candidates are held in at most 80 registers (six waves
-// per SIMD: 0.50 ms at 131,072 tokens against 0.52 ms at five); longer rows
-// keep every candidate in registers at lower occupancy.
+// Rows of up to 2,048 candidates run at six waves per SIMD (0.50 ms at
+// 131,072 tokens against 0.52 ms at five); longer rows keep every candidate
+// in registers at lower occupancy.
 template <int NPL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NPL <= 32 ? 6 : 1))) void topk_kernel(TopkParams p, int n_frames) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NPL <= 32 ? 6 : 1)))
+void topk_kernel(TopkParams p, int n_frames) {
   __shared__ uint32_t hist[256];
   const int lane = threadIdx.x & 63;
   const int per_frame = p.hkv * kBlk;
