@@ -379,12 +379,14 @@ __device__ __forceinline__ void q_branch(const BwdParams &p, Walk walk, const u1
   const bool has = rv && L > 0.f;
   const float lse2 = has ? m + __log2f(L) : -INFINITY;
   const int grp = lane >> 4;
+  // D from dout rounded to fp16 as in the products that form dP, so that
+  // dP - D cancels exactly where the row's probability mass sits on one key
   float part = 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     const f32x4 dv = rv ? *reinterpret_cast<const f32x4 *>(p.dout + qrow * D + 16 * dt + 4 * grp) : zero4();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part = fmaf(dv[i], oa[dt][i], part);
+    for (int i = 0; i < 4; ++i) part = fmaf(h16_to_f32(f2h_bits(dv[i])), oa[dt][i], part);
   }
   part = grp_sum(part);
   const float dd = has ? part / L : 0.f;
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(D) void bwd_qtmerge_kernel(BwdParams p) {
   }
   const int64_t tok = trow / p.hq, h = trow % p.hq;
   const int64_t pos = tok < p.v0 ? tok : tok + p.n_vis;
-  float x = L > 0.f ? p.dout[(pos * p.hq + h) * D + d] * o / L : 0.f;
+  float x = L > 0.f ? h16_to_f32(f2h_bits(p.dout[(pos * p.hq + h) * D + d])) * o / L : 0.f;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
   if ((d & 63) == 0) red[d >> 6] = x;

@@ -13,8 +13,11 @@ relative error is a few u and the element's error a few u times the sum of
 its terms' magnitudes, which for these inputs is within a small factor of
 the array's largest element. Each array must agree within 8 u of its
 largest magnitude (max |d| <= 8 u max |ref|, 3.9e-3) and on average within
-4 u of its mean magnitude (mean |d| <= 4 u mean |ref|, 2.0e-3); measured
-on these cases: at most 1.3e-3 and 8e-4. Each case prints its name and shape
+4 u of its mean magnitude (mean |d| <= 4 u mean |ref|, 2.0e-3), each plus
+1e-6 absolute for arrays whose reference cancels to zero; measured on these
+cases: at most 7.0e-4 and 6.5e-4. D = dout . o is formed from dout rounded to
+fp16, as in the products that give dP, so that dP - D cancels exactly where
+a row's probability sits on one key. Each case prints its name and shape
 before touching the GPU.
 """
 import math
@@ -40,6 +43,11 @@ CASES = [
     PrefillShape(1045, 16, 48, 28, 4, 128, 64, 8, 256, "bf16"),
     PrefillShape(333, 3, 9, 3, 3, 64, 64, 4, 90, "bf16"),
     PrefillShape(400, 0, 20, 16, 2, 64, 64, 5, 128, "bf16"),
+    # edge cases: no complete block (no compressed keys), text only (no vision
+    # rows at all), exactly one block (one compressed key, seen by one token)
+    PrefillShape(40, 10, 5, 4, 2, 64, 64, 2, 16, "bf16"),
+    PrefillShape(0, 70, 0, 4, 2, 64, 64, 2, 16, "bf16"),
+    PrefillShape(64, 0, 0, 8, 1, 64, 64, 3, 64, "bf16"),
 ]
 
 
@@ -48,7 +56,7 @@ def run(inp, sel, dout):
     dev = {n: torch.from_numpy(np.ascontiguousarray(inp[n])).to("cuda:0").to(torch.bfloat16).contiguous()
            for n in ("q", "k", "v", "w_k", "w_v")}
     gates = torch.from_numpy(np.ascontiguousarray(inp["gates"])).to("cuda:0")
-    sel_d = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).to("cuda:0")
+    sel_d = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).to("cuda:0") if len(sel) else None
     dout_d = torch.from_numpy(dout).to("cuda:0")
     r = binding.prefill_backward(dev["q"], dev["k"], dev["v"], inp["is_vision"], dev["w_k"], dev["w_v"], gates,
                                  sel_d, dout_d, s.top_k, s.window, block=s.block)
@@ -60,10 +68,14 @@ def check_bar(gname, g, rf):
     assert np.all(np.isfinite(g)), gname
     big, avg = np.abs(rf).max(), np.abs(rf).mean()
     err = np.abs(g - rf)
-    print(f"  {gname}: max |d| {err.max():.3e} ({err.max() / big:.2e} of max |ref|), "
-          f"mean |d| {err.mean():.3e} ({err.mean() / avg:.2e} of mean |ref|)", flush=True)
-    assert err.max() <= 8 * U16 * big, f"{gname}: max |d| {err.max():.3e} vs {big:.3e}"
-    assert err.mean() <= 4 * U16 * avg, f"{gname}: mean |d| {err.mean():.3e} vs mean |ref| {avg:.3e}"
+    print(f"  {gname}: max |d| {err.max():.3e} (max |ref| {big:.3e}), "
+          f"mean |d| {err.mean():.3e} (mean |ref| {avg:.3e})", flush=True)
+    # plus 1e-6 absolute: where the reference cancels to exactly zero (a
+    # compressed key seen by a single query, whose dS is P (dP - D) with one
+    # probability of 1), the fp32 sums leave residues of order 2^-24 times
+    # the terms' magnitude
+    assert err.max() <= 8 * U16 * big + 1e-6, f"{gname}: max |d| {err.max():.3e} vs {big:.3e}"
+    assert err.mean() <= 4 * U16 * avg + 1e-6, f"{gname}: mean |d| {err.mean():.3e} vs mean |ref| {avg:.3e}"
 
 
 @pytest.mark.parametrize("shape", CASES, ids=lambda s: f"nv{s.n_vis}_t{s.n_text}_h{s.n_q_heads}_d{s.head_dim}")
@@ -71,7 +83,10 @@ def test_backward_parity(shape):
     print(f"backward {shape}", flush=True)
     inp = make_prefill_inputs(shape, seed=11)
     vis = np.asarray(inp["is_vision"]).astype(bool)
-    sel = oracle.prefill(inp, want=("out", "sel"))["sel"][vis]
+    if vis.any():
+        sel = oracle.prefill(inp, want=("out", "sel"))["sel"][vis]
+    else:
+        sel = np.zeros((0, shape.n_kv_heads, shape.top_k), np.int32)
     dout = make_output_grad((shape.n_tokens, shape.n_q_heads, shape.head_dim), seed=12)
     ref = bwd.gradients(inp, sel, dout)
     got = run(inp, sel, dout)
