@@ -197,8 +197,11 @@ nsa_status nsa_prefill_dense(const nsa_prefill_desc *desc, const void *q, const 
  * the head sizes and limits of nsa_prefill; else NSA_ERR_UNSUPPORTED.
  * Arithmetic: fp16 operands on the matrix cores (q, k, v exactly; dout, the
  * probabilities, the score gradients and the compressed keys / values
- * rounded to fp16) with fp32 accumulation. Every gradient element is
- * written by one thread in a fixed order, so results are bitwise repeatable.
+ * rounded to fp16) with fp32 accumulation, so q, k, v, dout and the
+ * compressed keys / values must lie within the fp16 range (a value outside
+ * it sets bit 1 of the workspace's status word, nsa_workspace_status).
+ * Every gradient element is written by one thread in a fixed order, so
+ * results are bitwise repeatable.
  *   sel_idx   device [N_v, Hkv, top_k] int32 (may be NULL when N_v = 0): the
  *             forward's list (ascending, -1 padded, the own block last); any
  *             other contents give meaningless gradients, never an access
@@ -380,11 +383,15 @@ nsa_status nsa_probe_mfma_bf16(int32_t n_wg, int32_t iters, float *out, void *st
 nsa_status nsa_probe_block_stream(const void *buf, int64_t n_blocks, int32_t n_wg, int32_t iters,
                                   uint32_t *out, void *stream);
 
-/* Status word of a prefill workspace (the first 4 bytes of the workspace
- * passed to nsa_prefill or nsa_prefill_varlen, cleared at the start of every
- * such call): waits on `stream` for the work enqueued so far, copies the word
- * to *flags and returns NSA_ERR_KERNEL if it is nonzero (bit 0: a bounded
- * wait gave up and that call's outputs are invalid), NSA_OK otherwise.
+/* Status word of a prefill or backward workspace (the first 4 bytes of the
+ * workspace passed to nsa_prefill, nsa_prefill_varlen or
+ * nsa_prefill_backward, cleared at the start of every such call): waits on
+ * `stream` for the work enqueued so far, copies the word to *flags and
+ * returns NSA_ERR_KERNEL if it is nonzero, NSA_OK otherwise. Bit 0: a bounded
+ * wait gave up and that call's outputs are invalid (prefill). Bit 1: a value
+ * converted to fp16 for the matrix cores left the fp16 range (q, a value or
+ * a compressed key / value in prefill; q, k, v, dout or a compressed key /
+ * value in the backward), so the results hold infinities or NaN.
  * workspace: device, 256-B aligned; NSA_ERR_INVALID_ARG for NULL arguments. */
 nsa_status nsa_workspace_status(const void *workspace, void *stream, int32_t *flags);
 

@@ -369,10 +369,12 @@ def prefill_dense(q, k, v, scale=0.0, out=None, want_lse=False, workspace=None, 
 
 
 def prefill_backward(q, k, v, is_vision, w_cmp_k, w_cmp_v, gate_logits, sel_idx, dout, top_k, window,
-                     block=64, scale=0.0, stream=None) -> dict:
+                     block=64, scale=0.0, stream=None, workspace=None) -> dict:
     """Runs nsa_prefill_backward: gradients (fp32, on the device) of the layer
     for the output gradient dout [N,Hq,d], reusing the forward's selection
-    sel_idx [N_v,Hkv,top_k]. Returns dq, dk, dv, dw_cmp_k, dw_cmp_v, dgate."""
+    sel_idx [N_v,Hkv,top_k]. Returns dq, dk, dv, dw_cmp_k, dw_cmp_v, dgate.
+    workspace: an optional uint8 device tensor of at least the required size
+    (its status word can then be read with workspace_status)."""
     n, hq, d = q.shape
     hkv = k.shape[1]
     for name, t, shape in (("q", q, (n, hq, d)), ("k", k, (n, hkv, d)), ("v", v, (n, hkv, d)),
@@ -394,7 +396,9 @@ def prefill_backward(q, k, v, is_vision, w_cmp_k, w_cmp_v, gate_logits, sel_idx,
     res = {"dq": torch.empty((n, hq, d), **f32), "dk": torch.empty((n, hkv, d), **f32),
            "dv": torch.empty((n, hkv, d), **f32), "dw_cmp_k": torch.empty((d, d), **f32),
            "dw_cmp_v": torch.empty((d, d), **f32), "dgate": torch.empty((n, hq, 3), **f32)}
-    ws = torch.empty(max(nb.value, 256), dtype=torch.uint8, device=dev)
+    ws = workspace
+    if ws is None or ws.numel() < nb.value:
+        ws = torch.empty(max(nb.value, 256), dtype=torch.uint8, device=dev)
     st = lib().nsa_prefill_backward(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(w_cmp_k), _ptr(w_cmp_v),
         _ptr(gate_logits), _ptr(sel_idx if nv > 0 else None), _ptr(dout), _ptr(res["dq"]), _ptr(res["dk"]),

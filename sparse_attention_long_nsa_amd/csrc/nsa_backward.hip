@@ -47,6 +47,14 @@ namespace {
 constexpr int kSentinel = 0x7fffffff;
 constexpr int kChunkTok = 2048;  // query tokens per compressed-key partial
 
+// Whether any of eight fp16 values overflowed the fp16 range on conversion.
+__device__ __forceinline__ bool any_nonfinite8(u16x8 x) {
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bad |= h16_nonfinite(x[i]);
+  return bad;
+}
+
 template <int D>
 struct BwdTile {
   static constexpr int SEC = kBlk * D;  // elements per section
@@ -88,6 +96,7 @@ __global__ __launch_bounds__(D) void bwd_pool_kernel(BwdParams p) {
   p.vc[ob] = yv;
   p.kc16[ob] = f2h_bits(yk);
   p.vc16[ob] = f2h_bits(yv);
+  if (h16_nonfinite(f2h_bits(yk)) || h16_nonfinite(f2h_bits(yv))) atomicOr(p.status, kStatusRange);
 }
 
 // Packs rows row0 .. row0 + n_rows - 1 of a [rows][Hkv][D] key and value
@@ -95,7 +104,8 @@ __global__ __launch_bounds__(D) void bwd_pool_kernel(BwdParams p) {
 // row0 + 64 i .. +63 (zero past n_rows). One workgroup per (tile, group).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t *ksrc, const uint16_t *vsrc, int64_t row0,
-                                                       int64_t n_rows, int hkv, int n_tiles, uint16_t *dst) {
+                                                       int64_t n_rows, int hkv, int n_tiles, uint16_t *dst,
+                                                       int32_t *status) {
   constexpr int SEC = BwdTile<D>::SEC, CH = D / 8;
   __shared__ __attribute__((aligned(16))) uint16_t st[2][kBlk][D + 8];
   const int tile = blockIdx.x % n_tiles, g = blockIdx.x / n_tiles;
@@ -106,7 +116,10 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t *ksrc, con
     u16x8 x = zero8();
     if (row < n_rows) {
       x = *reinterpret_cast<const u16x8 *>((w ? vsrc : ksrc) + ((row0 + row) * hkv + g) * D + 8 * c);
-      if constexpr (BF16) x = bf2h8(x);
+      if constexpr (BF16) {
+        x = bf2h8(x);
+        if (any_nonfinite8(x)) atomicOr(status, kStatusRange);
+      }
     }
     *reinterpret_cast<u16x8 *>(&st[w][r][8 * c]) = x;
     *reinterpret_cast<u16x8 *>(out + w * SEC + r * D + 8 * PackedTile<D>::template swz<2 * D>(r, c)) = x;
@@ -307,10 +320,12 @@ struct QRows {
   }
 };
 
-// The query operands of a wave: Q^T and dO^T fragments (B operands, fp16).
+// The query operands of a wave: Q^T and dO^T fragments (B operands, fp16;
+// a value past the fp16 range sets the status word).
 template <int D>
 __device__ __forceinline__ void q_operands(const BwdParams &p, bool rv, int64_t qrow, u16x8 (&qf)[D / 32],
                                            u16x8 (&of)[D / 32], int lane) {
+  bool bad = false;
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) {
     qf[ds] = rv ? bf2h8(q_frag_global(p.q + qrow * D, ds, lane)) : zero8();
@@ -320,7 +335,9 @@ __device__ __forceinline__ void q_operands(const BwdParams &p, bool rv, int64_t 
       o = pack_p(*reinterpret_cast<const f32x4 *>(src), *reinterpret_cast<const f32x4 *>(src + 4));
     }
     of[ds] = o;
+    bad |= any_nonfinite8(qf[ds]) || any_nonfinite8(o);
   }
+  if (bad) atomicOr(p.status, kStatusRange);
 }
 
 // Global section of backward-tile slot s in each pass: pass 1 stages K rows
@@ -763,13 +780,15 @@ __device__ __forceinline__ void kv_load(const BwdParams &p, const TokSrc &src, i
 }
 
 template <int D>
-__device__ __forceinline__ void kv_store(KvStage<D> &sm, const KvRowRegs<D> &rr, int tid) {
+__device__ __forceinline__ void kv_store(KvStage<D> &sm, const KvRowRegs<D> &rr, int tid, int32_t *status) {
   constexpr int PER = D / 8;
   const int r = tid >> 3, seg = tid & 7, sl = row_slot(r);
+  bool bad = false;
 #pragma unroll
   for (int c = 0; c < PER / 8; ++c) {
     const u16x8 q8 = bf2h8(rr.q[c]);
     const u16x8 d8 = pack_p(rr.d[2 * c], rr.d[2 * c + 1]);
+    bad |= any_nonfinite8(q8) || any_nonfinite8(d8);
     *reinterpret_cast<u16x8 *>(&sm.qs[r][seg * PER + 8 * c]) = q8;
     *reinterpret_cast<u16x8 *>(&sm.ds_[r][seg * PER + 8 * c]) = d8;
     const int dim0 = seg * PER + 8 * c;
@@ -780,6 +799,7 @@ __device__ __forceinline__ void kv_store(KvStage<D> &sm, const KvRowRegs<D> &rr,
       sm.dt_[dim0 + e][col] = d8[e];
     }
   }
+  if (bad) atomicOr(status, kStatusRange);
   if (seg == 0) {
     float l2 = rr.l2, sg = rr.sg;
     if (l2 == -INFINITY) {  // the row has no keys in this branch
@@ -860,7 +880,7 @@ __device__ __forceinline__ void kv_walk(const BwdParams &p, KvStage<D> (&sm)[2],
   kv_load<D, G>(p, src, kv_tok<G>(src, 0, tid), g, tid, rr[0]);
   kv_load<D, G>(p, src, kv_tok<G>(src, 1, tid), g, tid, rr[1]);
   int tk_next = kv_tok<G>(src, 2, tid);
-  kv_store<D>(sm[0], rr[0], tid);
+  kv_store<D>(sm[0], rr[0], tid, p.status);
   __syncthreads();
   for (int st = 0; st < n_steps; ++st) {
     if (st + 2 < n_steps) {
@@ -870,8 +890,8 @@ __device__ __forceinline__ void kv_walk(const BwdParams &p, KvStage<D> (&sm)[2],
     tk_next = kv_tok<G>(src, st + 3, tid);
     kv_step<D>(sm[st & 1], kf, vf, dkt, dvt, key, src.mask, p.window, sl2, tid & 63);
     if (st + 1 < n_steps) {
-      if (st & 1) kv_store<D>(sm[0], rr[0], tid);
-      else kv_store<D>(sm[1], rr[1], tid);
+      if (st & 1) kv_store<D>(sm[0], rr[0], tid, p.status);
+      else kv_store<D>(sm[1], rr[1], tid, p.status);
     }
     __syncthreads();
   }
@@ -1090,13 +1110,13 @@ hipError_t run(const BwdParams &p, int stage, hipStream_t st) {
     case 2: {  // backward tiles
       if (p.n_vtile > 0)
         hipLaunchKernelGGL((bwd_pack_kernel<D, true>), dim3(p.n_vtile * p.hkv), dim3(256), 0, st, p.k, p.v, p.v0,
-                           p.n_vis, p.hkv, p.n_vtile, p.tile_v);
+                           p.n_vis, p.hkv, p.n_vtile, p.tile_v, p.status);
       if (p.n > p.n_vis)
         hipLaunchKernelGGL((bwd_pack_kernel<D, true>), dim3(p.n_ptile * p.hkv), dim3(256), 0, st, p.k, p.v,
-                           (int64_t)0, p.n, p.hkv, p.n_ptile, p.tile_p);
+                           (int64_t)0, p.n, p.hkv, p.n_ptile, p.tile_p, p.status);
       if (p.n_ctile > 0)
         hipLaunchKernelGGL((bwd_pack_kernel<D, false>), dim3(p.n_ctile * p.hkv), dim3(256), 0, st, p.kc16, p.vc16,
-                           (int64_t)0, (int64_t)p.n_blk, p.hkv, p.n_ctile, p.tile_c);
+                           (int64_t)0, (int64_t)p.n_blk, p.hkv, p.n_ctile, p.tile_c, p.status);
       break;
     }
     case 3: {  // who chose which block

@@ -469,7 +469,7 @@ nsa_status nsa_cmp_pool(int64_t n_rows, int32_t n_heads, int32_t head_dim, int32
 // Backward workspace: offsets of every array of BwdParams that lives in it.
 struct BwdLayout {
   int n_vtile = 0, n_ptile = 0, n_ctile = 0, mask_words = 0, n_chunk = 0, n_tsplit = 0;
-  size_t tpart = 0, kc = 0, vc = 0, kbar = 0, vbar = 0, dkc = 0, dvc = 0, kc16 = 0, vc16 = 0, tile_v = 0, tile_p = 0,
+  size_t status = 0, tpart = 0, kc = 0, vc = 0, kbar = 0, vbar = 0, dkc = 0, dvc = 0, kc16 = 0, vc16 = 0, tile_v = 0, tile_p = 0,
          tile_c = 0, vstat = 0, tstat = 0, selmask = 0, selcnt = 0, seloff = 0, selrows = 0, cpart = 0, total = 0;
 };
 
@@ -489,6 +489,7 @@ static nsa_status plan_backward(const nsa_prefill_desc *ds, const uint8_t *is_vi
   const size_t tile = sizeof(uint16_t) * 4 * kBlk * (size_t)pl.d * pl.hkv;  // one tile, every group
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  L.status = take(sizeof(int32_t));  // offset 0: the status word (nsa_workspace_status)
   L.kc = take(sizeof(float) * nb);
   L.vc = take(sizeof(float) * nb);
   L.kbar = take(sizeof(float) * nb);
@@ -574,6 +575,7 @@ nsa_status nsa_prefill_backward(const nsa_prefill_desc *desc, const void *q, con
   bp.selrows = reinterpret_cast<int32_t *>(ws + L.selrows);
   bp.cpart = reinterpret_cast<float *>(ws + L.cpart);
   bp.tpart = reinterpret_cast<float *>(ws + L.tpart);
+  bp.status = reinterpret_cast<int32_t *>(ws + L.status);
   bp.n = pl.N;
   bp.v0 = pl.v0;
   bp.n_vis = pl.n_vis;
@@ -590,6 +592,7 @@ nsa_status nsa_prefill_backward(const nsa_prefill_desc *desc, const void *q, con
   bp.n_chunk = L.n_chunk;
   bp.n_tsplit = L.n_tsplit;
   hipError_t e = hipSuccess;
+  NSA_LAUNCH("status_clear", launch_status_clear(bp.status, s));
   NSA_LAUNCH("bwd_selclear", launch_backward(bp, pl.d, 0, s));
   NSA_LAUNCH("bwd_pool", launch_backward(bp, pl.d, 1, s));
   NSA_LAUNCH("bwd_pack", launch_backward(bp, pl.d, 2, s));

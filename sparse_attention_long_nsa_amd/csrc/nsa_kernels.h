@@ -134,6 +134,7 @@ struct BwdParams {
                                         // that chose each (group, block), ascending
   float *cpart;                         // [n_ctile][n_chunk][Hkv][2][64][d] partial compressed grads
   float *tpart;                         // [n_tsplit][N_t Hq][d + 2] text rows' per-split partials
+  int32_t *status;                      // the workspace's status word (bit 1: an fp16 range overflow)
   int64_t n, v0, n_vis;
   int hq, hkv, topk, window, n_blk;
   float scale;

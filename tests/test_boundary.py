@@ -400,7 +400,8 @@ def test_backward_validation_and_workspace():
     # 28 / 4 heads, d 128, k 16; every array rounded up to 256 bytes
     a = lambda x: (x + 255) // 256 * 256
     nb, tile = 16 * 4 * 128, 4 * 64 * 128 * 2 * 4
-    parts = [4 * nb] * 6 + [2 * nb] * 2          # compressed k / v, means, their gradients; fp16 copies
+    parts = [4]                                   # the status word
+    parts += [4 * nb] * 6 + [2 * nb] * 2          # compressed k / v, means, their gradients; fp16 copies
     parts += [tile * 16, tile * 17, tile * 1]     # tiles: vision blocks, positions, compressed keys
     parts += [4 * 6 * 1024 * 28, 4 * 2 * 64 * 28]  # per-branch statistics: vision rows, text rows
     parts += [4 * 4 * 16 * 32, 4 * 4 * 16, 4 * (4 * 16 + 1), 4 * 1024 * 4 * 16]  # who chose which block

@@ -9,7 +9,9 @@
 * fp16 range (queries, values and compressed keys/values are used in fp16):
   values scaled by 2^10 stay in range -- no flag, and the output scales
   exactly with v (linearity in v), so out / 2^10 is at parity with the
-  oracle on the unscaled inputs; values past 65504 set bit 1.
+  oracle on the unscaled inputs; values past 65504 set bit 1. The
+  backward's workspace carries the same word: dout or keys past 65504 set
+  bit 1 there too.
 """
 import numpy as np
 import pytest
@@ -84,3 +86,35 @@ def test_values_past_fp16_range_are_flagged(what):
     flags = binding.workspace_status(r["workspace"])
     print("status word:", flags, flush=True)
     assert flags & 2
+
+
+BWD_SHAPE = PrefillShape(700, 8, 24, 28, 4, 128, 64, 8, 128, "bf16")
+
+
+@pytest.mark.parametrize("what", ["none", "dout", "k"])
+def test_backward_flags_values_past_fp16_range(what):
+    """The backward's workspace carries the same status word: inputs in range
+    leave it 0; dout or keys scaled past 65504 (converted to fp16 for the
+    matrix cores) set bit 1."""
+    from sparse_attention_long_nsa_amd.inputs import make_output_grad
+    import oracle
+    inp = make_prefill_inputs(BWD_SHAPE, seed=24)
+    print(f"\n[case] backward, {what} past fp16 range: {BWD_SHAPE}", flush=True)
+    vis = np.asarray(inp["is_vision"]).astype(bool)
+    sel = oracle.prefill(inp, want=("sel",))["sel"][vis]
+    dout = make_output_grad((BWD_SHAPE.n_tokens, BWD_SHAPE.n_q_heads, BWD_SHAPE.head_dim), seed=25)
+    bad = dict(inp)
+    if what == "dout":
+        dout[100:104] *= 2.0 ** 17
+    elif what == "k":
+        x = np.array(inp["k"], copy=True)
+        x[300:302] *= 2.0 ** 17
+        bad["k"] = x
+    dev = upload(bad)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    binding.prefill_backward(dev["q"], dev["k"], dev["v"], inp["is_vision"], dev["w_k"], dev["w_v"], dev["gates"],
+                             torch.from_numpy(sel).to("cuda:0"), torch.from_numpy(dout).to("cuda:0"),
+                             BWD_SHAPE.top_k, BWD_SHAPE.window, workspace=ws)
+    flags = binding.workspace_status(ws)
+    print("status word:", flags, flush=True)
+    assert (flags & 2) == (0 if what == "none" else 2)
