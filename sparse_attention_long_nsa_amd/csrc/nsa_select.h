@@ -30,12 +30,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The largest T with at least `need` lanes holding v >= T (need <= lanes with
-// a nonzero v): the need-th largest of the 64 lane values. Bits MSB first.
+// The largest T whose bits below LOW are zero with at least `need` lanes
+// holding v >= T (need <= lanes with a nonzero v). With LOW = 0 it is the
+// need-th largest of the 64 lane values; with LOW > 0 a lower bound of it
+// found in 32 - LOW steps. Bits MSB first; each step is one ballot count,
+// scalar work that the CU's one scalar unit serves for all its waves.
+template <int LOW = 0>
 __device__ __forceinline__ uint32_t kth_largest_lane(uint32_t v, int need) {
   uint32_t t = 0;
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= LOW; --b) {
     const uint32_t c = t | (1u << b);
     if (__popcll(__ballot(v >= c)) >= need) t = c;
   }
@@ -73,30 +77,33 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[NPL], int
     uint32_t lm = 0;
 #pragma unroll
     for (int s = 0; s < NPL; ++s) lm = max(lm, key[s]);
-    const uint32_t t0 = kth_largest_lane(lm, need);
+    // a lower bound of the (k-1)-th largest lane maximum from its top 16
+    // bits (bits below are zero): every answer score still reaches it, and
+    // at most a few more candidates than with the exact value do
+    const uint32_t t0 = kth_largest_lane<16>(lm, need);
+    // compact the candidates (ascending index order) into LDS while counting
+    // them; past 64 the slow path below takes over
     int c0 = 0;
 #pragma unroll
-    for (int s = 0; s < NPL; ++s) c0 += __popcll(__ballot(key[s] >= t0));
-    if (c0 <= 64) {
-      // compact the candidates (ascending index order) into LDS
-      int base = 0;
-#pragma unroll
-      for (int s = 0; s < NPL; ++s) {
-        const bool cand = key[s] >= t0;
-        const uint64_t cb = __ballot(cand);
-        if (cand) {
-          const int q = base + __popcll(cb & below);
+    for (int s = 0; s < NPL; ++s) {
+      const bool cand = key[s] >= t0;
+      const uint64_t cb = __ballot(cand);
+      if (cand) {
+        const int q = c0 + __popcll(cb & below);
+        if (q < 64) {
           hist[q] = key[s];
           hist[64 + q] = (uint32_t)(s * 64 + lane);
         }
-        base += __popcll(cb);
       }
+      c0 += __popcll(cb);
+    }
+    if (c0 <= 64) {
       wave_lds_sync();
       const uint32_t ck = lane < c0 ? hist[lane] : 0u;
       const uint32_t ci = lane < c0 ? hist[64 + lane] : 0xffffffffu;
       // keep the candidates above the need-th largest key, then the
       // lowest-index ones equal to it (candidates sit in ascending index order)
-      const uint32_t t1 = kth_largest_lane(ck, need);
+      const uint32_t t1 = kth_largest_lane<0>(ck, need);
       const uint64_t gt = __ballot(ck > t1), eq = __ballot(ck == t1);
       const int rest = need - __popcll(gt);
       const bool take = (ck > t1) || (ck == t1 && __popcll(eq & below) < rest);
