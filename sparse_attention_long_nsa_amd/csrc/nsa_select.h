@@ -35,11 +35,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // need-th largest of the 64 lane values; with LOW > 0 a lower bound of it
 // found in 32 - LOW steps. Bits MSB first; each step is one ballot count,
 // scalar work that the CU's one scalar unit serves for all its waves.
-template <int LOW = 0>
-__device__ __forceinline__ uint32_t kth_largest_lane(uint32_t v, int need) {
-  uint32_t t = 0;
+template <int LOW = 0, int HI = 31>
+__device__ __forceinline__ uint32_t kth_largest_lane(uint32_t v, int need, uint32_t t = 0) {
 #pragma unroll
-  for (int b = 31; b >= LOW; --b) {
+  for (int b = HI; b >= LOW; --b) {
     const uint32_t c = t | (1u << b);
     if (__popcll(__ballot(v >= c)) >= need) t = c;
   }
@@ -102,11 +101,20 @@ __device__ __forceinline__ void topk_select_keys(const uint32_t (&key)[NPL], int
       const uint32_t ck = lane < c0 ? hist[lane] : 0u;
       const uint32_t ci = lane < c0 ? hist[64 + lane] : 0xffffffffu;
       // keep the candidates above the need-th largest key, then the
-      // lowest-index ones equal to it (candidates sit in ascending index order)
-      const uint32_t t1 = kth_largest_lane<0>(ck, need);
-      const uint64_t gt = __ballot(ck > t1), eq = __ballot(ck == t1);
-      const int rest = need - __popcll(gt);
-      const bool take = (ck > t1) || (ck == t1 && __popcll(eq & below) < rest);
+      // lowest-index ones equal to it (candidates sit in ascending index
+      // order). The key's top 16 bits first: when exactly `need` candidates
+      // reach that prefix they are the answer (the next one lies below it, so
+      // no tie crosses the boundary) and the low bits are never searched.
+      uint32_t t1 = kth_largest_lane<16>(ck, need);
+      bool take;
+      if (__popcll(__ballot(ck >= t1)) == need) {  // wave-uniform
+        take = ck >= t1;
+      } else {
+        t1 = kth_largest_lane<0, 15>(ck, need, t1);
+        const uint64_t gt = __ballot(ck > t1), eq = __ballot(ck == t1);
+        const int rest = need - __popcll(gt);
+        take = (ck > t1) || (ck == t1 && __popcll(eq & below) < rest);
+      }
       const uint64_t tb = __ballot(take);
       if (take) out[__popcll(tb & below)] = (int32_t)ci;
       if (lane == 0) out[need] = f;  // own block, larger than every candidate
