@@ -29,7 +29,8 @@
 //                 wave per 16 keys: walks every query row that attends the
 //                 tile (window range, selection list, text rows) 32 rows at
 //                 a time; dV^T += dO^T P and dK^T += Q^T dS with the rows'
-//                 Q^T and dO^T staged transposed in LDS; dk, dv written once
+//                 Q^T and dO^T read from their row-major LDS staging by the
+//                 transposing LDS read; dk, dv written once
 //   bwd_kvc /     the same for the compressed keys over chunks of 2,048
 //   bwd_creduce   query tokens, the chunks' partial sums then added in order
 //   bwd_cmp_w /   dW = sum over blocks of dK_cmp x mean^T, and each block's
@@ -699,24 +700,39 @@ struct TokSrc {
   int mask, br;  // br: 0..2 vision branch, 3 text rows
 };
 
-// Rows of one step (32 at most: TS tokens x G heads), staged in LDS by the
-// whole workgroup: row-major fp16 copies of q and dout (A operands of S and
-// dP) and transposed copies whose key slots follow the permutation of the
-// P / dS B operand (slot 8 j + i <- row 4 j + i for i < 4, 16 + 4 j + i - 4
-// for i >= 4), plus each row's statistics. The transposed rows rotate their
-// four 8-slot chunks by (dim / 16) mod 4, so that the 2-byte stores of
-// threads 16 dims apart fall in different LDS banks.
+// Rows of one step (32 at most: TS tokens x G heads), staged row-major in
+// LDS by the whole workgroup (fp16 copies of q and dout) with each row's
+// statistics. The rows are the A operands of S = Q K^T and dP = dO V^T as
+// stored, and of dV^T = dO^T P and dK^T = Q^T dS through the gfx950
+// transposing LDS read (ds_read_b64_tr_b16), so no transposed copy is
+// staged. Row stride D + 24 elements: both the 16-byte row reads and the
+// transposing reads of 16 lanes fall in distinct banks.
 template <int D>
 struct KvStage {
-  static constexpr int RS = D + 8, TS_ = 40;
+  static constexpr int RS = D + 24;
   uint16_t qs[32][RS], ds_[32][RS];
-  uint16_t qt[D][TS_], dt_[D][TS_];
   float l2[32], dd[32], sig[32];
   int tok[32];
 };
 
-__device__ __forceinline__ int row_slot(int r) {
-  return r < 16 ? 8 * (r >> 2) + (r & 3) : 8 * ((r - 16) >> 2) + 4 + ((r - 16) & 3);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// A operand (16 dims x 32 rows) of a product over the step's rows from a
+// row-major staged array: lane l takes dim 16 dt + (l % 16) and, as its
+// eight k-slots, rows 4 (l / 16) + j and 16 + 4 (l / 16) + j (j < 4) -- the
+// row order of the P / dS B operand. Each transposing read hands lane i of a
+// 16-lane group element (i % 4) of the 8 bytes that lane (i / 4 + 4 j)
+// addressed, so lane s addresses row 4 g + s / 4, dims 16 dt + 4 (s % 4).
+template <int D>
+__device__ __forceinline__ u16x8 kv_tr_frag(const uint16_t (*arr)[KvStage<D>::RS], int dt, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const uint16_t *p0 = &arr[4 * g + (s >> 2)][16 * dt + 4 * (s & 3)];
+  const uint16_t *p1 = &arr[16 + 4 * g + (s >> 2)][16 * dt + 4 * (s & 3)];
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p0);
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p1);
+  return u16x8{(uint16_t)a[0], (uint16_t)a[1], (uint16_t)a[2], (uint16_t)a[3],
+               (uint16_t)b[0], (uint16_t)b[1], (uint16_t)b[2], (uint16_t)b[3]};
 }
 
 // One thread's share of a step's rows: row r = tid / 8 (token r / G of the
@@ -782,7 +798,7 @@ __device__ __forceinline__ void kv_load(const BwdParams &p, const TokSrc &src, i
 template <int D>
 __device__ __forceinline__ void kv_store(KvStage<D> &sm, const KvRowRegs<D> &rr, int tid, int32_t *status) {
   constexpr int PER = D / 8;
-  const int r = tid >> 3, seg = tid & 7, sl = row_slot(r);
+  const int r = tid >> 3, seg = tid & 7;
   bool bad = false;
 #pragma unroll
   for (int c = 0; c < PER / 8; ++c) {
@@ -791,13 +807,6 @@ __device__ __forceinline__ void kv_store(KvStage<D> &sm, const KvRowRegs<D> &rr,
     bad |= any_nonfinite8(q8) || any_nonfinite8(d8);
     *reinterpret_cast<u16x8 *>(&sm.qs[r][seg * PER + 8 * c]) = q8;
     *reinterpret_cast<u16x8 *>(&sm.ds_[r][seg * PER + 8 * c]) = d8;
-    const int dim0 = seg * PER + 8 * c;
-    const int col = (sl + 8 * ((dim0 >> 4) & 3)) & 31;  // eight dims share dim / 16
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sm.qt[dim0 + e][col] = q8[e];
-      sm.dt_[dim0 + e][col] = d8[e];
-    }
   }
   if (bad) atomicOr(status, kStatusRange);
   if (seg == 0) {
@@ -856,9 +865,8 @@ __device__ __forceinline__ void kv_step(const KvStage<D> &sm, const u16x8 (&kf)[
   const u16x8 pp = pack_p(pm[0], pm[1]), pd = pack_p(dsm[0], dsm[1]);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
-    const int ch = 8 * ((grp + dt) & 3);
-    const u16x8 da = *reinterpret_cast<const u16x8 *>(&sm.dt_[16 * dt + r16][ch]);
-    const u16x8 qa = *reinterpret_cast<const u16x8 *>(&sm.qt[16 * dt + r16][ch]);
+    const u16x8 da = kv_tr_frag<D>(sm.ds_, dt, lane);
+    const u16x8 qa = kv_tr_frag<D>(sm.qs, dt, lane);
     dvt[dt] = mfma_f16(da, pp, dvt[dt]);
     dkt[dt] = mfma_f16(qa, pd, dkt[dt]);
   }
