@@ -21,11 +21,14 @@
 //
 // Staging (bf16 inputs): the compressed keys/values are first packed into
 // PackedTile chunks of 64 blocks, which stream into LDS by direct
-// global->LDS copies: pass 1 (keys only, no global stores in flight) runs a
-// ring of eight chunk slots with explicit vmcnt waits; pass 2 writes the
-// score rows as it goes, so it double-buffers and waits for all of its
-// memory operations before each chunk. fp32 inputs (split operands) keep
-// the synchronous staging.
+// global->LDS copies. The two passes are two kernels: pass 1 (keys only,
+// no global stores in flight) fits 256 registers, so two of its workgroups
+// share a CU, each ringing keys through four chunk slots with explicit
+// vmcnt waits; pass 2 (seven heads' output accumulators fill the register
+// file: one wave per SIMD) writes the score rows as it goes, so it
+// double-buffers and waits for all of its memory operations before each
+// chunk. fp32 inputs (split operands) keep one kernel with synchronous
+// staging.
 #include "nsa_kernels.h"
 #include "nsa_tiles.h"
 
@@ -206,75 +209,83 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_kernel(CmpAttnParams p) {
   }
 }
 
-// Pipelined variant for fp16 operands (bf16 inputs); same math as above.
+// Pipelined kernels for fp16 operands (bf16 inputs); same math as above.
 // The ring slots are separate LDS objects and every step names its slot at
 // compile time: reads of one slot then need not wait for copies still
 // landing in another.
 // Both passes walk a chunk head by head as a software pipeline: the scores of
 // head h+1 are issued to the matrix cores before head h's exponentials, so
 // the two overlap within the one wave. The K fragments (and in pass 2 the V
-// fragments) of the chunk stay in registers across the heads. Blocks a query
-// must not see are masked by starting their score accumulators at -inf (one
-// bias per block, shared by every head), and score rows are written with
-// buffer stores whose out-of-range lanes the hardware drops: no branches, so
-// each chunk is one straight run of instructions the scheduler can interleave.
-template <int D, int NT>
+// fragments) of a half chunk stay in registers across the heads. Only a
+// frame's last chunk holds blocks some of its queries must not see (every
+// earlier chunk ends before the frame's first block, f), so only that chunk
+// runs the masked form: its score accumulators start at -inf for the hidden
+// blocks (one bias per block, shared by every head) and its score rows are
+// written with buffer stores whose out-of-range lanes the hardware drops.
+// The other chunks start from zero accumulators and store unguarded.
+template <int D, int NT, bool MASKED>
 __device__ __forceinline__ void cmp_scores(const u16x8 (&kf)[NT][D / 32], const u16x8 (&q)[D / 32],
                                            const f32x4 (&bias)[NT], f32x4 (&s)[NT]) {
 #pragma unroll
-  for (int kt = 0; kt < NT; ++kt) s[kt] = bias[kt];
+  for (int kt = 0; kt < NT; ++kt) s[kt] = MASKED ? bias[kt] : zero4();
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds)
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt) s[kt] = mfma_f16(kf[kt][ds], q[ds], s[kt]);
 }
 
-template <int D, int G>
+// One chunk of pass 1, in two halves of 32 keys: a half's key fragments
+// stay in registers across the heads (half a chunk keeps the kernel within
+// 256 registers), with an exact running max per half and head.
+template <int D, int G, bool MASKED>
 __device__ __forceinline__ void cmp_pass1_chunk(const uint16_t *ks, int c, const u16x8 (&qf)[G][D / 32],
                                                 float (&m)[G], float (&l)[G], int nc_t, float sl2, int lane) {
   const int grp = lane >> 4;
-  u16x8 kf[4][D / 32];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+    u16x8 kf[2][D / 32];
 #pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) kf[kt][ds] = pk_k_frag<D>(ks, kt, ds, lane);
-  const int b0 = c * kBlk + 4 * grp;  // block of element (kt, i): b0 + 16 kt + i
-  f32x4 bias[4];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
+      for (int ds = 0; ds < D / 32; ++ds) kf[kk][ds] = pk_k_frag<D>(ks, 2 * ks2 + kk, ds, lane);
+    const int b0 = c * kBlk + 32 * ks2 + 4 * grp;  // block of element (kk, i): b0 + 16 kk + i
+    f32x4 bias[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bias[kt][i] = (b0 + 16 * kt + i < nc_t) ? 0.f : -INFINITY;
-  f32x4 sc[4], sn[4];
-  cmp_scores<D, 4>(kf, qf[0], bias, sc);
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (h + 1 < G) cmp_scores<D, 4>(kf, qf[h + 1], bias, sn);
-    float mx = sc[0][0];
+      for (int i = 0; i < 4; ++i) bias[kk][i] = (!MASKED || b0 + 16 * kk + i < nc_t) ? 0.f : -INFINITY;
+    f32x4 sc[2], sn[2];
+    cmp_scores<D, 2, MASKED>(kf, qf[0], bias, sc);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int h = 0; h < G; ++h) {
+      if (h + 1 < G) cmp_scores<D, 2, MASKED>(kf, qf[h + 1], bias, sn);
+      float mx = sc[0][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kt][i]);
-    // exact running max per chunk and head (raw scores; the scale sl2 > 0
-    // is folded into the exponent)
-    const float mn = fmaxf(m[h], mx * sl2);
-    const float nb = (mn == -INFINITY) ? 0.f : -mn;
-    float acc = (m[h] == -INFINITY) ? 0.f : l[h] * __builtin_amdgcn_exp2f(m[h] + nb);
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kk][i]);
+      // raw scores; the scale sl2 > 0 is folded into the exponent
+      const float mn = fmaxf(m[h], mx * sl2);
+      const float nb = (mn == -INFINITY) ? 0.f : -mn;
+      float acc = (m[h] == -INFINITY) ? 0.f : l[h] * __builtin_amdgcn_exp2f(m[h] + nb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc += __builtin_amdgcn_exp2f(fmaf(sc[kt][i], sl2, nb));
-    l[h] = acc;
-    m[h] = mn;
-    if (h + 1 < G) {
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) sc[kt] = sn[kt];
+        for (int i = 0; i < 4; ++i) acc += __builtin_amdgcn_exp2f(fmaf(sc[kk][i], sl2, nb));
+      l[h] = acc;
+      m[h] = mn;
+      if (h + 1 < G) {
+        sc[0] = sn[0];
+        sc[1] = sn[1];
+      }
     }
   }
 }
 
 // gsr: buffer resource over this workgroup's score rows (64 rows of f
-// floats); srow: byte offset of this lane's row.
-template <int D, int G>
+// floats); srow: byte offset of this lane's row. nlse2: minus each head's
+// log2-sum-exp, -inf where the query sees no block.
+template <int D, int G, bool MASKED>
 __device__ __forceinline__ void cmp_pass2_chunk(const uint16_t *ks, const uint16_t *vt, int c,
                                                 const u16x8 (&qf)[G][D / 32], f32x4 (&o)[G][D / 16],
                                                 const float (&nlse2)[G], __amdgpu_buffer_rsrc_t gsr,
@@ -295,17 +306,17 @@ __device__ __forceinline__ void cmp_pass2_chunk(const uint16_t *ks, const uint16
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bias[kk][i] = (b0 + 16 * kk + i < nc_t) ? 0.f : -INFINITY;
-    f32x4 sc[2], sn[2], gsum[2] = {zero4(), zero4()};
-    cmp_scores<D, 2>(kf, qf[0], bias, sc);
+      for (int i = 0; i < 4; ++i) bias[kk][i] = (!MASKED || b0 + 16 * kk + i < nc_t) ? 0.f : -INFINITY;
+    f32x4 sc[2], sn[2], gsum[2];
+    cmp_scores<D, 2, MASKED>(kf, qf[0], bias, sc);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      if (h + 1 < G) cmp_scores<D, 2>(kf, qf[h + 1], bias, sn);
+      if (h + 1 < G) cmp_scores<D, 2, MASKED>(kf, qf[h + 1], bias, sn);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[kk][i] = __builtin_amdgcn_exp2f(fmaf(sc[kk][i], sl2, nlse2[h]));
-        gsum[kk] += sc[kk];
+        gsum[kk] = h == 0 ? sc[kk] : gsum[kk] + sc[kk];
       }
       const u16x8 pf = pack_p(sc[0], sc[1]);
 #pragma unroll
@@ -321,22 +332,27 @@ __device__ __forceinline__ void cmp_pass2_chunk(const uint16_t *ks, const uint16
       for (int i = 0; i < 4; ++i) {
         const int b = b0 + 16 * kk + i;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gsum[kk][i]), gsr,
-                                              b < f ? srow + 4 * b : 0x7ffffff0, 0, 0);
+                                              (!MASKED || b < f) ? srow + 4 * b : 0x7ffffff0, 0, 0);
       }
   }
 }
 
+// Pass 1 for fp16 operands: every query's log-sum-exp over the compressed
+// keys, written to lse in log2 units (pass 2 reads it there and leaves it in
+// natural-log units). It is a kernel of its own so that it fits 256
+// registers (the query fragments, one chunk's key fragments, two heads'
+// scores): two workgroups share a CU, and one wave's exponentials run while
+// the other's products are on the matrix cores. Keys ring through four slots
+// (three chunks in flight) with explicit vmcnt waits; no other memory
+// operation is in flight during the walk.
 template <int D, int G>
-__global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p) {
+__global__ __launch_bounds__(kThreadsH) __attribute__((amdgpu_waves_per_eu(2))) void cmp_lse_kernel(
+    CmpAttnParams p) {
   using T = PackedTile<D>;
   constexpr int KE = T::KE, SE = T::KE + T::VE;
-  constexpr int PK = KE / 512 / 4;  // pieces per wave of a key tile (a value tile alike)
-  static_assert(T::VE == KE, "square tiles");
-  // eight slots of one tile each: pass 1 rings keys through all eight,
-  // pass 2 pairs them (K, V^T) into two double-buffered chunk slots
+  constexpr int PK = KE / 512 / 4;  // pieces per wave of a key tile
   __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
-  __shared__ __attribute__((aligned(16))) uint16_t r4[KE], r5[KE], r6[KE], r7[KE];
-  constexpr int DS = D / 32, DT = D / 16;
+  constexpr int DS = D / 32;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int row = lane & 15, grp = lane >> 4;
@@ -366,62 +382,94 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
     if (ovf && p.status) atomicOr(p.status, kStatusRange);
   }
 
-  // ---- pass 1: log-sum-exp of every (query, head); keys only, 8-slot ring
-  // (7 chunks in flight), explicit vmcnt waits (no other memory operations)
   float m[G], l[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
-#define NSA_ISSUE_K(DST, C) dma_pieces<PK>(cg + (int64_t)(C) * SE, (DST) + off, lane)
   // Every step issues exactly PK copies, so "chunk c landed" is always
-  // vmcnt <= 6 * PK (one straight-line wait the compiler's own tracking
-  // follows too). Past the last chunk the copies repeat chunk 0 into slots
-  // that are never read again.
-#define NSA_ISSUE_K_OR_PAD(DST, C) NSA_ISSUE_K(DST, ((C) < nch ? (C) : 0))
+  // vmcnt <= 2 * PK. Past the last chunk the copies repeat chunk 0 into
+  // slots that are never read again.
+#define NSA_ISSUE_K_OR_PAD(DST, C) dma_pieces<PK>(cg + (int64_t)((C) < nch ? (C) : 0) * SE, (DST) + off, lane)
 #define NSA_P1_STEP(CUR, NXT)                                             \
   {                                                                       \
-    wait_vm_c<6 * PK>();                                                  \
+    wait_vm_c<2 * PK>();                                                  \
     bare_barrier();                                                       \
-    NSA_ISSUE_K_OR_PAD(NXT, c + 7);                                       \
-    cmp_pass1_chunk<D, G>(CUR, c, qf, m, l, nc_t, p.sl2, lane);           \
-    if (++c >= nch) break;                                                \
+    NSA_ISSUE_K_OR_PAD(NXT, c + 3);                                       \
+    cmp_pass1_chunk<D, G, false>(CUR, c, qf, m, l, nc_t, p.sl2, lane);    \
+    if (++c >= nch - 1) break;                                            \
   }
   if (nch > 0) {
     NSA_ISSUE_K_OR_PAD(r0, 0);
     NSA_ISSUE_K_OR_PAD(r1, 1);
     NSA_ISSUE_K_OR_PAD(r2, 2);
-    NSA_ISSUE_K_OR_PAD(r3, 3);
-    NSA_ISSUE_K_OR_PAD(r4, 4);
-    NSA_ISSUE_K_OR_PAD(r5, 5);
-    NSA_ISSUE_K_OR_PAD(r6, 6);
   }
-  for (int c = 0; c < nch;) {
-    NSA_P1_STEP(r0, r7)
+  for (int c = 0; c < nch - 1;) {  // every chunk but the last: nothing hidden
+    NSA_P1_STEP(r0, r3)
     NSA_P1_STEP(r1, r0)
     NSA_P1_STEP(r2, r1)
     NSA_P1_STEP(r3, r2)
-    NSA_P1_STEP(r4, r3)
-    NSA_P1_STEP(r5, r4)
-    NSA_P1_STEP(r6, r5)
-    NSA_P1_STEP(r7, r6)
   }
 #undef NSA_P1_STEP
 #undef NSA_ISSUE_K_OR_PAD
-  float lse2[G];
+  wait_vm_c<0>();  // the last chunk and every padding copy have landed
+  if (nch > 0) {
+    bare_barrier();
+    const int cl = nch - 1, sl = cl & 3;
+    const uint16_t *ks = sl == 0 ? r0 : sl == 1 ? r1 : sl == 2 ? r2 : r3;
+    cmp_pass1_chunk<D, G, true>(ks, cl, qf, m, l, nc_t, p.sl2, lane);
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float M = grp_max(m[h]);
     const float part = (m[h] == -INFINITY) ? 0.f : l[h] * exp2f(m[h] - M);
     const float L = grp_sum(part);
-    lse2[h] = (L > 0.f) ? M + log2f(L) : -INFINITY;
+    m[h] = (L > 0.f) ? M + log2f(L) : -INFINITY;
   }
   if (tvalid && grp == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) p.lse[(int64_t)t * p.hq + g * G + h] = lse2[h] * (1.0f / kLog2e);
+    for (int h = 0; h < G; ++h) p.lse[(int64_t)t * p.hq + g * G + h] = m[h];
+  }
+}
+
+// Pass 2 for fp16 operands: probabilities from pass 1's log-sum-exp ->
+// o_cmp and the group scores. The score rows are stored as the loop goes,
+// so each chunk waits for all of this wave's memory operations (double
+// buffering: chunk c+1 flies during chunk c).
+template <int D, int G>
+__global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p) {
+  using T = PackedTile<D>;
+  constexpr int KE = T::KE, SE = T::KE + T::VE;
+  constexpr int PK = KE / 512 / 4;  // pieces per wave of a key tile (a value tile alike)
+  static_assert(T::VE == KE, "square tiles");
+  // two chunk slots of (K, V^T), double-buffered
+  __shared__ __attribute__((aligned(16))) uint16_t r0[KE], r1[KE], r2[KE], r3[KE];
+  constexpr int DS = D / 32, DT = D / 16;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int row = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.x % p.hkv;
+  const int f = p.n_frames - 1 - (int)(blockIdx.x / p.hkv);
+  const int t = f * kBlk + wv * 16 + row;  // this lane's query (vision-local)
+  const bool tvalid = t < p.n_vis;
+  const int nc_t = tvalid ? (t + 1) / kBlk : 0;  // complete blocks visible to it
+  const int t_last = min(f * kBlk + kBlk - 1, p.n_vis - 1);
+  const int nk = (t_last + 1) / kBlk;            // blocks any query of the frame sees
+  const int nch = (nk + kBlk - 1) / kBlk;        // packed chunks holding them
+  const int off = __builtin_amdgcn_readfirstlane(wv * PK * 512);  // wave-uniform, scalar
+  const uint16_t *cg = p.kvc + (int64_t)g * p.n_cch * SE + off;
+
+  u16x8 qf[G][DS];
+  float lse2[G];  // log2 units, from pass 1
+  {
+    const int64_t q0 = (row_pos(p.vmap, p.v0, tvalid ? t : 0) * p.hq + (int64_t)g * G) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) qf[h][ds] = tvalid ? bf2h8(q_frag_global(p.q + q0 + h * D, ds, lane)) : zero8();
+    const float *lr = p.lse + (int64_t)(tvalid ? t : 0) * p.hq + g * G;
+#pragma unroll
+    for (int h = 0; h < G; ++h) lse2[h] = tvalid ? lr[h] : -INFINITY;
   }
 
-  // ---- pass 2: probabilities -> o_cmp and group scores. The score rows are
-  // stored as the loop goes, so each chunk waits for all of this wave's
-  // memory operations (double buffering: chunk c+1 flies during chunk c).
   f32x4 o[G][DT];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -432,35 +480,41 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
   const __amdgpu_buffer_rsrc_t gsr = __builtin_amdgcn_make_buffer_rsrc(
       p.gs + frame_off(f, p.hkv) + (int64_t)g * kBlk * f, 0, kBlk * f * (int)sizeof(float), kBufWord3);
   const int srow = (t - f * kBlk) * f * (int)sizeof(float);
-  float nlse2[G];  // -lse2, 0 where no block is visible (every score masked)
+  float nlse2[G];  // -lse2; -inf where no block is visible (every probability 0)
 #pragma unroll
-  for (int h = 0; h < G; ++h) nlse2[h] = (lse2[h] == -INFINITY) ? 0.f : -lse2[h];
+  for (int h = 0; h < G; ++h) nlse2[h] = (lse2[h] == -INFINITY) ? -INFINITY : -lse2[h];
 #define NSA_ISSUE_KV(DK, DV, C)                                           \
   {                                                                       \
-    NSA_ISSUE_K(DK, C);                                                   \
+    dma_pieces<PK>(cg + (int64_t)(C) * SE, (DK) + off, lane);             \
     dma_pieces<PK>(cg + (int64_t)(C) * SE + KE, (DV) + off, lane);        \
   }
-  wait_vm_c<0>();  // no copy of pass 1 (padding included) still in flight
-  bare_barrier();  // every wave is done with the pass-1 slots
   if (nch > 0) NSA_ISSUE_KV(r0, r1, 0);
 #define NSA_P2_STEP(CK, CV, NK, NV)                                       \
   {                                                                       \
     wait_vm_c<0>();                                                       \
     bare_barrier();                                                       \
-    if (c + 1 < nch) NSA_ISSUE_KV(NK, NV, c + 1);                         \
-    cmp_pass2_chunk<D, G>(CK, CV, c, qf, o, nlse2, gsr, srow, f, nc_t, p.sl2, lane); \
-    if (++c >= nch) break;                                                \
+    NSA_ISSUE_KV(NK, NV, c + 1);                                          \
+    cmp_pass2_chunk<D, G, false>(CK, CV, c, qf, o, nlse2, gsr, srow, f, nc_t, p.sl2, lane); \
+    if (++c >= nch - 1) break;                                            \
   }
-  for (int c = 0; c < nch;) {
+  for (int c = 0; c < nch - 1;) {  // every chunk but the last: nothing hidden
     NSA_P2_STEP(r0, r1, r2, r3)
     NSA_P2_STEP(r2, r3, r0, r1)
   }
 #undef NSA_P2_STEP
 #undef NSA_ISSUE_KV
-#undef NSA_ISSUE_K
+  if (nch > 0) {  // the last chunk, in slot pair (nch - 1) mod 2
+    wait_vm_c<0>();
+    bare_barrier();
+    const int cl = nch - 1;
+    const uint16_t *ck = (cl & 1) ? r2 : r0, *cv = (cl & 1) ? r3 : r1;
+    cmp_pass2_chunk<D, G, true>(ck, cv, cl, qf, o, nlse2, gsr, srow, f, nc_t, p.sl2, lane);
+  }
 
   // ---- epilogue: sigmoid(g_cmp) * o_cmp as the fp16 part 0 of the row's
-  // output slots (the selection kernel adds the branches and writes fp32)
+  // output slots (the selection kernel adds the branches and writes fp32);
+  // the log-sum-exp leaves in natural-log units (every lane of the row has
+  // read it: the loads returned before the walk used them)
   if (tvalid) {
     const int64_t r0w = row_pos(p.vmap, p.v0, t) * p.hq + (int64_t)g * G;
 #pragma unroll
@@ -469,6 +523,10 @@ __global__ __launch_bounds__(kThreadsH) void cmp_attn_dma_kernel(CmpAttnParams p
       float *slot = p.out + (r0w + h) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) store_partial4<D>(slot, 0, 16 * dt + 4 * grp, o[h][dt] * gate);
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) p.lse[(int64_t)t * p.hq + g * G + h] = lse2[h] * (1.0f / kLog2e);
     }
   }
 }
@@ -481,6 +539,7 @@ hipError_t run(const CmpAttnParams &p, hipStream_t st) {
     hipLaunchKernelGGL((cmp_attn_kernel<D, G, true>), dim3(nwg), dim3(kThreadsH), 0, st, p);
   } else {
     if (!p.kvc && p.n_cch > 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((cmp_lse_kernel<D, G>), dim3(nwg), dim3(kThreadsH), 0, st, p);
     hipLaunchKernelGGL((cmp_attn_dma_kernel<D, G>), dim3(nwg), dim3(kThreadsH), 0, st, p);
   }
   return hipGetLastError();
