@@ -50,11 +50,13 @@ def closed_form_work(shape, n_text_positions):
     f4 = 4.0 * d * hq
     kv_block = 2 * B * d
     return {
-        "cmp_pool": ("bytes", 2.0 * n_blk * B * hkv * d * 2 + 2.0 * n_blk * hkv * d * 2),
+        # the maps: block means in (fp32), each result out twice in fp16 (plain
+        # and packed); the means themselves come out of pack_kv's read of the rows
+        "cmp_pool": ("bytes", 2.0 * n_blk * hkv * d * 4 + 2.0 * n_blk * hkv * d * 2 * 2),
         "cmp_attn": ("flops", f4 * float(n_cmp.sum())),
         "blk_score_topk": ("bytes", 4.0 * hkv * float(cur.sum()) + 4.0 * s.n_vis * hkv * k),
         "swa_attn": ("flops", f4 * float(n_swa.sum())),
-        "pack_kv": ("bytes", 4.0 * s.n_vis * hkv * d + 2.0 * n_frames * hkv * kv_block),
+        "pack_kv": ("bytes", 4.0 * s.n_vis * hkv * d + 2.0 * n_frames * hkv * kv_block + 8.0 * n_blk * hkv * d),
         "pack_cmp": ("bytes", 4.0 * n_blk * hkv * d + 2.0 * (-(-n_blk // B)) * hkv * kv_block),
         "pack_text": ("bytes", 4.0 * len(text_keys) * hkv * d + 2.0 * (-(-len(text_keys) // B)) * hkv * kv_block),
         "sel_attn": ("flops", f4 * float(n_sel.sum())),

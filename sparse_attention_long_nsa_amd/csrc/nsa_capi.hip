@@ -314,6 +314,15 @@ nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, 
     int32_t *sel = sel_idx_out ? sel_idx_out : at<int32_t>(workspace, pl.off_sel);
     float *gs = at<float>(workspace, pl.off_gs);
     const size_t esz = pl.fp32 ? sizeof(float) : sizeof(uint16_t);
+    SelParams sp{qb, kb, vb, at<uint16_t>(workspace, pl.off_vt), sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
+                 pl.n_frames, sl2, vmap, g_spin_limit.load(std::memory_order_relaxed), status};
+    float *means = at<float>(workspace, pl.off_means);
+    uint16_t *kvc = (!pl.fp32 && pl.n_cch > 0) ? at<uint16_t>(workspace, pl.off_kvc) : nullptr;
+    // bf16: the block means ride in pack_kv's read of the rows, and the maps
+    // write the packed compressed chunks themselves
+    const int64_t C = (int64_t)pl.hkv * pl.d;
+    NSA_LAUNCH("pack_kv", pl.fp32 ? launch_pack_kv(sp, pl.d, true, s)
+                                  : launch_pack_kv(sp, pl.d, false, s, means, means + pl.n_blk * C, pl.n_blk));
     if (pl.n_blk > 0) {
       // compressed keys: fp16 (bf16 hi/lo for fp32 inputs); values: fp16
       const int64_t r0 = pl.mapped ? 0 : pl.v0;  // rows through vmap when mapped
@@ -322,21 +331,20 @@ nsa_status enqueue_prefill(const PrefillPlan &pl, const void *q, const void *k, 
       PoolJob jv{static_cast<const char *>(v) + esz * r0 * Hk * D, w_cmp_v, pl.hkv, pl.n_blk,
                  nullptr, nullptr, vc, v_cmp_out, vmap};
       jk.status = jv.status = status;
-      NSA_LAUNCH("cmp_pool", launch_cmp_pool_split(jk, jv, pl.d, pl.fp32, at<float>(workspace, pl.off_means), s));
-    }
-    uint16_t *kvc = nullptr;
-    if (!pl.fp32 && pl.n_cch > 0) {
-      kvc = at<uint16_t>(workspace, pl.off_kvc);
-      NSA_LAUNCH("pack_cmp", launch_pack_tiles(kc, vc, 0, pl.n_blk, pl.hkv, pl.n_cch, kvc, pl.d, true, s));
+      if (pl.fp32) {
+        NSA_LAUNCH("cmp_pool", launch_cmp_pool_split(jk, jv, pl.d, true, means, s));
+      } else {
+        jk.packed = jv.packed = kvc;
+        jk.n_cch = jv.n_cch = pl.n_cch;
+        jv.packed_v = 1;
+        NSA_LAUNCH("cmp_pool", launch_cmp_map(jk, jv, pl.d, false, means, s));
+      }
     }
     CmpAttnParams cp{qc, ql, kc, kcl, vc, kvc, pl.n_cch, gate_logits, out, lse, gs, pl.v0,
                      (int)pl.n_vis, pl.hq, pl.hkv, pl.n_frames, sl2, vmap, status};
     NSA_LAUNCH("cmp_attn", launch_cmp_attn(cp, pl.d, pl.G, pl.fp32, s));
     TopkParams tp{gs, sel, (int)pl.n_vis, pl.hkv, pl.k};
     NSA_LAUNCH("blk_score_topk", launch_topk(tp, pl.n_frames, s));
-    SelParams sp{qb, kb, vb, at<uint16_t>(workspace, pl.off_vt), sel, gate_logits, out, pl.v0, (int)pl.n_vis, pl.hq, pl.hkv, pl.k,
-                 pl.n_frames, sl2, vmap, g_spin_limit.load(std::memory_order_relaxed), status};
-    NSA_LAUNCH("pack_kv", launch_pack_kv(sp, pl.d, pl.fp32, s));
     SwaParams wp{qb, at<uint16_t>(workspace, pl.off_vt), gate_logits, out, pl.v0, (int)pl.n_vis,
                  pl.hq, pl.hkv, pl.w, pl.n_frames, sl2, vmap};
     NSA_LAUNCH("swa_attn", launch_swa_attn(wp, pl.d, pl.G, pl.fp32, s));

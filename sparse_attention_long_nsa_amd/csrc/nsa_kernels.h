@@ -32,6 +32,11 @@ struct PoolJob {
   int64_t in_stride = kBlk;       // rows of x between the first rows of blocks
   int64_t out_stride = 1;         // output rows between consecutive blocks
   int32_t *status = nullptr;      // workspace status word: kStatusRange on an fp16 overflow
+  // PackedTile chunks [n_heads][n_cch] (or null): the fp16 result also goes
+  // straight into the K rows (packed_v 0) or the V^T rows (packed_v 1) of
+  // the chunk holding its block; rows past n_blk are zeroed
+  uint16_t *packed = nullptr;
+  int n_cch = 0, packed_v = 0;
 };
 
 struct CmpAttnParams {
@@ -175,6 +180,10 @@ hipError_t launch_cmp_pool(const PoolJob &j0, const PoolJob *j1, int d, bool fp3
 // `means` (2 * n_blk * Hkv * d floats) and a map launch; identical results.
 hipError_t launch_cmp_pool_split(const PoolJob &j0, const PoolJob &j1, int d, bool fp32, float *means,
                                  hipStream_t st);
+// The map launch alone, over block means already in `means` (laid out as
+// above; pack_kv with mean outputs writes them for bf16 layers).
+hipError_t launch_cmp_map(const PoolJob &j0, const PoolJob &j1, int d, bool fp32, const float *means,
+                          hipStream_t st);
 // Copies one row of n_cols bf16 per sequence (src [Bt, n_cols]) to row `row`
 // of dst [Bt, cap, n_cols], for keys and values at once.
 hipError_t launch_append_rows(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_cache,
@@ -187,7 +196,11 @@ hipError_t launch_cmp_attn(const CmpAttnParams &p, int d, int G, bool split, hip
 hipError_t launch_topk(const TopkParams &p, int n_blk_max, hipStream_t st);
 // f16: q, k, v hold fp16 (else bf16; values are converted while staging)
 hipError_t launch_swa_attn(const SwaParams &p, int d, int G, bool f16, hipStream_t st);
-hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st);
+// mk, mv (or null): the column means of each complete block's keys and
+// values ([n_mean][Hkv][d] floats, the pooling's block means, bitwise), taken
+// from the bf16 rows as they are packed.
+hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st, float *mk = nullptr,
+                          float *mv = nullptr, int64_t n_mean = 0);
 // Packs n_rows rows of k, v ([rows][Hkv][d]) into PackedTile blocks
 // [Hkv][n_chunks][K tile, V^T tile]: packed row i is source row rows[i] when
 // a map is given, else row0 + i, plus `jump` for i >= split_at; v_f16: v is
@@ -195,7 +208,8 @@ hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st);
 hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
                              int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st,
                              int split_at = 0x7fffffff, int64_t jump = 0,
-                             const int32_t *rows = nullptr, int32_t *status = nullptr);
+                             const int32_t *rows = nullptr, int32_t *status = nullptr,
+                             float *mk = nullptr, float *mv = nullptr, int64_t n_mean = 0);
 // Writes the row maps of one mask slice: vmap[t] = position of vision row t,
 // tmap[r] = position of text row r, tnvb[r] = vision tokens before it.
 hipError_t launch_row_maps(const MaskSlice &m, int32_t *vmap, int32_t *tmap, int32_t *tnvb,

@@ -12,6 +12,7 @@
 // streaming is not held up by the maps; single calls run both in one kernel.
 // Both orders of arithmetic are the same, so the results are identical.
 #include "nsa_kernels.h"
+#include "nsa_tiles.h"
 
 namespace nsa {
 
@@ -133,6 +134,19 @@ __global__ __launch_bounds__(kPoolThreads) void pool_mean_kernel(PoolJob j0, Poo
 constexpr int kMapBlocks = 16;
 constexpr int kMapThreads = 512;
 
+// Element (block blk, head g, dim r) of a job's packed output: row blk % 64
+// of the K tile, or column blk % 64 (its key slot) of the V^T tile, in chunk
+// blk / 64 of head g.
+template <int D>
+__device__ __forceinline__ int64_t packed_at(const PoolJob &jb, int64_t blk, int g, int r) {
+  using T = PackedTile<D>;
+  const int key = (int)(blk % kBlk);
+  const int64_t base = ((int64_t)g * jb.n_cch + blk / kBlk) * (T::KE + T::VE);
+  if (!jb.packed_v) return base + key * D + 8 * T::template swz<2 * D>(key, r / 8) + r % 8;
+  const int sl = T::vslot(key);
+  return base + T::KE + r * kBlk + 8 * T::template swz<2 * kBlk>(r, sl / 8) + sl % 8;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kMapThreads) void pool_map_kernel(PoolJob j0, PoolJob j1, const float *m0,
                                                                const float *m1) {
@@ -182,9 +196,18 @@ __global__ __launch_bounds__(kMapThreads) void pool_map_kernel(PoolJob j0, PoolJ
       if (jb.out_h16) {
         const uint16_t h = f2h_bits(acc[q]);
         jb.out_h16[dst] = h;
+        if (jb.packed) jb.packed[packed_at<D>(jb, b0 + bl, g, r)] = h;
         if (jb.status && h16_nonfinite(h)) atomicOr(jb.status, kStatusRange);
       }
       if (jb.out_f32) jb.out_f32[dst] = acc[q];
+    }
+  }
+  // the last workgroup zeroes the packed rows past the last block
+  if (jb.packed && b0 + kMapBlocks >= jb.n_blk) {
+    const int64_t n_pad = (int64_t)jb.n_cch * kBlk - jb.n_blk;
+    for (int64_t e = tid; e < n_pad * hkv * D; e += kMapThreads) {
+      const int rr = (int)(e % D), g = (int)((e / D) % hkv);
+      jb.packed[packed_at<D>(jb, jb.n_blk + e / ((int64_t)D * hkv), g, rr)] = 0;
     }
   }
 }
@@ -273,6 +296,24 @@ hipError_t launch_cmp_pool_split(const PoolJob &j0, const PoolJob &j1, int d, bo
     if (d == 64) { NSA_POOL2(bf16, 64) } else { NSA_POOL2(bf16, 128) }
   }
 #undef NSA_POOL2
+  return hipGetLastError();
+}
+
+hipError_t launch_cmp_map(const PoolJob &j0, const PoolJob &j1, int d, bool fp32, const float *means,
+                          hipStream_t st) {
+  const int64_t nb = j0.n_blk > j1.n_blk ? j0.n_blk : j1.n_blk;
+  if (nb <= 0) return hipSuccess;
+  const int64_t C = (int64_t)j0.n_heads * d;
+  const float *m0 = means, *m1 = means + j0.n_blk * C;
+  const dim3 g2((unsigned)((nb + kMapBlocks - 1) / kMapBlocks), 2);
+  const size_t smem2 = sizeof(float) * (size_t)d * (d + 1);
+#define NSA_MAP(T, D) hipLaunchKernelGGL((pool_map_kernel<T, D>), g2, dim3(kMapThreads), smem2, st, j0, j1, m0, m1);
+  if (fp32) {
+    if (d == 64) { NSA_MAP(float, 64) } else { NSA_MAP(float, 128) }
+  } else {
+    if (d == 64) { NSA_MAP(bf16, 64) } else { NSA_MAP(bf16, 128) }
+  }
+#undef NSA_MAP
   return hipGetLastError();
 }
 

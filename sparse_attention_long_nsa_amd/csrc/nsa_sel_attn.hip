@@ -400,51 +400,86 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
 // inputs) followed by the swizzled, key-permuted V^T tile in fp16; rows past
 // n_vis are zero. Packed row t reads source row rows[t] when a row map is
 // given, else v0 + t, plus `jump` from row split_at on (to skip a run of
-// rows, e.g. the vision run for text).
+// rows, e.g. the vision run for text). Rows arrive as 16-byte loads, all
+// issued before the first store; the values are transposed through LDS.
+//
+// With mk (bf16 inputs), blocks b < n_mean also yield the pooling's block
+// means of their key and value columns (VideoNSA model card, "Model
+// Architecture": frame blocks averaged), from the rows already in LDS, in
+// the exact order of the pooling kernel's block_mean (row phases of
+// 256 / (Hkv d / 8) rows, each summed in row order, then the phases in
+// order, times 1/64), so the results are bitwise the pooling's own.
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v, int64_t v0,
                                                       int n_vis, int split_at, int64_t jump, int hkv,
                                                       int n_frames, uint16_t *__restrict__ kv,
-                                                      const int32_t *__restrict__ rows, int32_t *status) {
+                                                      const int32_t *__restrict__ rows, int32_t *status,
+                                                      float *__restrict__ mk, float *__restrict__ mv,
+                                                      int64_t n_mean) {
   using T = PackedTile<D>;
-  __shared__ uint16_t tile[kBlk][D + 2];
+  constexpr int RS = D + 8;          // LDS row stride (16-byte rows)
+  constexpr int IT = kBlk * (D / 8) / 256;  // 16-byte chunks per thread, per tensor
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kBlk][RS];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kBlk][RS];
+  __shared__ float part[2048];
   const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
   const int tid = threadIdx.x;
+  const bool means = mk && b < n_mean;  // uniform over the workgroup
   uint16_t *dst = kv + ((int64_t)g * n_frames + b) * (T::KE + T::VE);
-  // K: chunk c of key row r goes to chunk position swz(r, c)
-  for (int idx = tid; idx < kBlk * (D / 8); idx += 256) {
-    const int r = idx / (D / 8), c = idx % (D / 8);
+  u16x8 kx[IT], vx[IT];
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    const int idx = tid + 256 * j, r = idx / (D / 8), c = idx % (D / 8);
     const int t = b * kBlk + r;
-    u16x8 val = zero8();
+    kx[j] = vx[j] = zero8();
     if (t < n_vis) {
       const int64_t src = rows ? (int64_t)rows[t] : v0 + t + (t >= split_at ? jump : 0);
-      val = *reinterpret_cast<const u16x8 *>(k + (src * hkv + g) * (int64_t)D + 8 * c);
+      kx[j] = *reinterpret_cast<const u16x8 *>(k + (src * hkv + g) * (int64_t)D + 8 * c);
+      vx[j] = *reinterpret_cast<const u16x8 *>(v + (src * hkv + g) * (int64_t)D + 8 * c);
     }
-    *reinterpret_cast<u16x8 *>(dst + r * D + 8 * T::template swz<2 * D>(r, c)) = val;
   }
-  bool ovf = false;  // a value past fp16's range (flagged in *status)
-  for (int idx = tid; idx < kBlk * D; idx += 256) {
-    const int key = idx / D, d = idx % D;
-    const int t = b * kBlk + key;
-    uint16_t x = 0;
-    if (t < n_vis) {
-      const int64_t src = rows ? (int64_t)rows[t] : v0 + t + (t >= split_at ? jump : 0);
-      x = v[(src * hkv + g) * (int64_t)D + d];
-      if (!F16) x = bf2h_bits(x);
-      ovf |= h16_nonfinite(x);
-    }
-    tile[key][d] = x;
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    const int idx = tid + 256 * j, r = idx / (D / 8), c = idx % (D / 8);
+    // K: chunk c of key row r goes to chunk position swz(r, c)
+    *reinterpret_cast<u16x8 *>(dst + r * D + 8 * T::template swz<2 * D>(r, c)) = kx[j];
+    if (means) *reinterpret_cast<u16x8 *>(&kt[r][8 * c]) = kx[j];
+    *reinterpret_cast<u16x8 *>(&vt[r][8 * c]) = vx[j];
   }
-  if (ovf && status) atomicOr(status, kStatusRange);
   __syncthreads();
   // V^T: row d, stored key slot s <- key vkey(s); chunk c at swz(d, c)
+  bool ovf = false;  // a value past fp16's range (flagged in *status)
   for (int idx = tid; idx < D * (kBlk / 8); idx += 256) {
     const int d = idx / (kBlk / 8), c = idx % (kBlk / 8);
     u16x8 val;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) val[i] = tile[T::vkey(8 * c + i)][d];
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t x = vt[T::vkey(8 * c + i)][d];
+      val[i] = F16 ? x : bf2h_bits(x);
+      ovf |= h16_nonfinite(val[i]);
+    }
     *reinterpret_cast<u16x8 *>(dst + T::KE + d * kBlk + 8 * T::template swz<2 * kBlk>(d, c)) = val;
+  }
+  if (ovf && status) atomicOr(status, kStatusRange);
+  if (!means) return;
+  const int C = hkv * D, CH = C / 8, P = CH >= 256 ? 1 : 256 / CH;  // P * D <= 2048
+#pragma unroll
+  for (int kvsel = 0; kvsel < 2; ++kvsel) {
+    const uint16_t(*x)[RS] = kvsel ? vt : kt;
+    for (int item = tid; item < P * D; item += 256) {
+      const int rp = item / D, col = item % D;
+      float acc = 0.f;
+      for (int r = rp; r < kBlk; r += P) acc += bfbits2f(x[r][col]);
+      part[rp * D + col] = acc;
+    }
+    __syncthreads();
+    for (int col = tid; col < D; col += 256) {
+      float sum = 0.f;
+      for (int rp = 0; rp < P; ++rp) sum += part[rp * D + col];
+      (kvsel ? mv : mk)[(int64_t)b * C + g * D + col] = sum * (1.0f / kBlk);
+    }
+    __syncthreads();
   }
 }
 
@@ -495,22 +530,27 @@ hipError_t launch_sel_attn(const SelParams &p, int d, int G, bool f16, hipStream
 
 hipError_t launch_pack_tiles(const uint16_t *k, const uint16_t *v, int64_t row0, int n_rows, int hkv,
                              int n_chunks, uint16_t *out, int d, bool v_f16, hipStream_t st,
-                             int split_at, int64_t jump, const int32_t *rows, int32_t *status) {
+                             int split_at, int64_t jump, const int32_t *rows, int32_t *status,
+                             float *mk, float *mv, int64_t n_mean) {
   const unsigned n = (unsigned)n_chunks * (unsigned)hkv;
   if (n == 0) return hipSuccess;
+  if (v_f16 && mk) return hipErrorInvalidValue;  // means come from bf16 rows only
+#define NSA_PACK(D, F)                                                                                  \
+  hipLaunchKernelGGL((pack_kv_kernel<D, F>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, \
+                     hkv, n_chunks, out, rows, status, mk, mv, n_mean)
   if (d == 64) {
-    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<64, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows, status);
-    else hipLaunchKernelGGL((pack_kv_kernel<64, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows, status);
+    if (v_f16) NSA_PACK(64, true); else NSA_PACK(64, false);
   } else {
-    if (v_f16) hipLaunchKernelGGL((pack_kv_kernel<128, true>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows, status);
-    else hipLaunchKernelGGL((pack_kv_kernel<128, false>), dim3(n), dim3(256), 0, st, k, v, row0, n_rows, split_at, jump, hkv, n_chunks, out, rows, status);
+    if (v_f16) NSA_PACK(128, true); else NSA_PACK(128, false);
   }
+#undef NSA_PACK
   return hipGetLastError();
 }
 
-hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st) {
+hipError_t launch_pack_kv(const SelParams &p, int d, bool f16, hipStream_t st, float *mk, float *mv,
+                          int64_t n_mean) {
   return launch_pack_tiles(p.k, p.v, p.v0, p.n_vis, p.hkv, p.n_frames, p.kv, d, f16, st,
-                           0x7fffffff, 0, p.vmap, p.status);
+                           0x7fffffff, 0, p.vmap, p.status, mk, mv, n_mean);
 }
 
 size_t packed_kv_block_elems(int d) { return (size_t)2 * kBlk * d; }

@@ -24,6 +24,11 @@ struct PackedTile {
     const int h = slot / 32, p = slot % 32, j = p / 8, i = p % 8;
     return 32 * h + (i < 4 ? 4 * j + i : 16 + 4 * j + (i - 4));
   }
+  // the stored slot of key `key` (inverse of vkey)
+  __host__ __device__ static constexpr int vslot(int key) {
+    const int h = key / 32, q = key % 32, r = q & 15;
+    return 32 * h + 8 * (r / 4) + (r % 4) + (q >= 16 ? 4 : 0);
+  }
 };
 
 // A operand of S^T = K Q^T from a staged K tile: keys 16*kt + (l%16), dims

@@ -35,6 +35,7 @@ if ROOT not in sys.path:  # also runnable as a plain script
 # short_name.
 KERNELS = [
     ("sel_attn_kernel", "sel_attn", "sparse_attention_long_nsa_amd/csrc/nsa_sel_attn.hip"),
+    ("cmp_lse_kernel", "cmp_lse", "sparse_attention_long_nsa_amd/csrc/nsa_cmp_attn.hip"),
     ("cmp_attn_dma_kernel", "cmp_attn", "sparse_attention_long_nsa_amd/csrc/nsa_cmp_attn.hip"),
     ("cmp_attn_kernel", "cmp_attn", "sparse_attention_long_nsa_amd/csrc/nsa_cmp_attn.hip"),
     ("swa_attn_kernel", "swa_attn", "sparse_attention_long_nsa_amd/csrc/nsa_fine_attn.hip"),
@@ -72,7 +73,7 @@ DENSE_KERNELS = ("pack_dense", "dense_attn")
 GATE_KERNELS = ("gate_hidden", "gate_out")
 BWD_KERNELS = ("bwd_selclear", "bwd_pool", "bwd_pack", "bwd_sellist", "bwd_q_vis", "bwd_q_text", "bwd_kv",
                "bwd_kv_cmp", "bwd_cmp_sum", "bwd_cmp_w", "bwd_cmp_tok")
-PREFILL_KERNELS = ("sel_attn", "cmp_attn", "swa_attn", "text_attn", "text_merge", "blk_score_topk", "cmp_pool",
+PREFILL_KERNELS = ("sel_attn", "cmp_lse", "cmp_attn", "swa_attn", "text_attn", "text_merge", "blk_score_topk", "cmp_pool",
                    "cmp_pool_mean", "cmp_pool_map", "pack_kv", "pack_cmp", "pack_text")
 
 
@@ -182,7 +183,13 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
     elif bench:
         lines += [f"bench.py in the same process reported {bench['ms_per_step']} ms/step "
                   f"({bench['value']:.0f} tokens/s); its event-timed per-kernel averages are listed "
-                  "beside the profiler's.", ""]
+                  "beside the profiler's."
+                  + (" The compression attention is two kernels (cmp_lse: pass 1, the log-sum-exp; "
+                     "cmp_attn: pass 2); the events time them together, under cmp_attn."
+                     if "cmp_lse" in dur else "")
+                  + (" The pooling's block means are taken inside pack_kv; cmp_pool is the maps alone "
+                     "(they also write the packed compressed chunks)."
+                     if "cmp_pool_map" in dur and "cmp_pool_mean" not in dur else ""), ""]
     lines += ["| kernel | calls | avg ms (rocprofv3) | avg ms (bench events) | share |", "|---|---|---|---|---|"]
     for name, v in rows:
         avg = sum(v) / len(v)
