@@ -194,6 +194,8 @@ def trace_summary(trace_csv: str, bench_log: str, grid_names: dict, title: str, 
     for name, v in rows:
         avg = sum(v) / len(v)
         ev = kern.get(name, {}).get("avg_ms", "")
+        if name == "cmp_pool_map" and "cmp_pool_mean" not in dur:  # the maps alone are the event "cmp_pool"
+            ev = kern.get("cmp_pool", {}).get("avg_ms", "")
         lines.append(f"| {name} | {len(v)} | {avg:.4f} | {ev} | {100 * avg / total:.1f}% |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -302,13 +304,21 @@ def counter_summary(csv_a: str, csv_b: str, grid_names: dict, workload: str, com
         issued = v.get("SQ_INSTS_MFMA", 0.0) * 16384 / 1e12
         tf = kern.get(name, {}).get("tflops")
         ms = kern.get(name, {}).get("avg_ms")
-        useful = f"{tf * ms * 1e-3 / issued:.0%}" if (tf and ms and issued) else ""
+        both = issued
+        if name == "cmp_attn" and "cmp_lse" in vals:  # the events time both passes as cmp_attn
+            lse = vals["cmp_lse"].get("SQ_INSTS_MFMA", [])
+            both += (sum(lse) / len(lse) if lse else 0.0) * 16384 / 1e12
+        useful = f"{tf * ms * 1e-3 / both:.0%}" if (tf and ms and both) else ""
         lines.append(f"| {name} | {secs * 1e3:.3f} | {waves:.0f} | {per_wave('SQ_INSTS_VALU')} | "
                      f"{per_wave('SQ_INSTS_MFMA')} | {per_wave('SQ_INSTS_LDS')} | {per_wave('SQ_INSTS_SALU')} | "
                      f"{exp_share:.0%} | {valu_busy:.0%} | {mfma_busy:.0%} | {wait:.0%} | {conflict:.2%} | "
                      f"{issued:.2f} | {useful} |")
     lines += ["", "`exp share` weights the transcendental instructions (exp2) four times, their issue cost "
               "relative to plain fp32 vector instructions."]
+    if "cmp_lse" in vals:
+        lines += ["", "The compression attention is two kernels, cmp_lse (pass 1) and cmp_attn (pass 2); "
+                  "cmp_attn's `useful` divides the algorithmic flops of both passes by the matrix "
+                  "instructions both issue."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
