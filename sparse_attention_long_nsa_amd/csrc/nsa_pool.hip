@@ -7,10 +7,12 @@
 // HBM-bound: a workgroup streams one block (64 rows x Hkv x d, contiguous in
 // the token-major layout, or gathered through a row map when the vision
 // tokens lie in several runs) with 16-byte loads and reduces the rows in
-// fp32; W is applied from its L1/L2-resident copy. The layer runs the two
-// steps as separate launches (means through the workspace) so the row
-// streaming is not held up by the maps; single calls run both in one kernel.
-// Both orders of arithmetic are the same, so the results are identical.
+// fp32; W is applied from its L1/L2-resident copy. In a bf16 layer the block
+// means are taken by the packing kernel that reads every block anyway, and
+// only the maps run here (writing the packed compressed chunks as well); an
+// fp32 layer runs the two steps as separate launches (means through the
+// workspace); single calls run both in one kernel. Every form adds in the
+// same order, so the results are identical.
 #include "nsa_kernels.h"
 #include "nsa_tiles.h"
 
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(kPoolThreads) void cmp_pool_kernel(PoolJob j0, Pool
   }
 }
 
-// The layer's pooling in two launches, so that the streaming of the rows is
+// Pooling in two launches (fp32 layers), so that the streaming of the rows is
 // not held up by the maps: block means into a workspace, then the maps, one
 // output per thread. Same arithmetic in the same order as cmp_pool_kernel.
 template <typename T, int D>
