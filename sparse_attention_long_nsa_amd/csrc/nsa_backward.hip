@@ -11,10 +11,10 @@
 // repeatable:
 //   bwd_pool      block means and compressed keys / values (fp32, plus fp16
 //                 copies for the matrix cores)
-//   bwd_pack      per (64-key tile, KV group) four fp16 sections: K rows,
-//                 V rows, K^T and V^T (the transposed ones in the forward's
-//                 key-permuted layout), for the vision blocks, for every
-//                 position (text queries) and for the compressed keys
+//   bwd_pack      per (64-key tile, KV group) two fp16 sections, K rows
+//                 and V rows (16-byte chunks swizzled per row), for the
+//                 vision blocks, for every position (text queries) and for
+//                 the compressed keys
 //   bwd_selmask.. the tokens that chose each (group, block), ascending: a
 //                 bitmask over tokens, its row counts, their prefix sum and
 //                 the decoded lists
@@ -23,8 +23,10 @@
 //                 staged once in LDS: per branch, pass 1 recomputes the
 //                 branch's log-sum-exp and output o (online softmax), giving
 //                 D = dout . o and the gate gradient; pass 2 forms
-//                 dS = sigma P (dP - D) and dq^T += K^T dS^T; dq is written
-//                 once after all branches (text rows: split over key tiles)
+//                 dS = sigma P (dP - D) and dq^T += K^T dS^T; V^T and K^T
+//                 come out of the staged rows through the transposing LDS
+//                 read; dq is written once after all branches (text rows:
+//                 split over key tiles)
 //   bwd_kv        key side, one workgroup per (64-key tile, KV group), a
 //                 wave per 16 keys: walks every query row that attends the
 //                 tile (window range, selection list, text rows) 32 rows at
@@ -56,10 +58,14 @@ __device__ __forceinline__ bool any_nonfinite8(u16x8 x) {
   return bad;
 }
 
+// four 16-bit values, and the LDS pointer type the transposing read takes
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
 template <int D>
 struct BwdTile {
   static constexpr int SEC = kBlk * D;  // elements per section
-  static constexpr int E = 4 * SEC;     // sections: K rows, V rows, K^T, V^T
+  static constexpr int E = 2 * SEC;     // sections: K rows, V rows
 };
 
 __global__ void bwd_fill_kernel(uint32_t *a, int64_t n) {
@@ -108,7 +114,6 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t *ksrc, con
                                                        int64_t n_rows, int hkv, int n_tiles, uint16_t *dst,
                                                        int32_t *status) {
   constexpr int SEC = BwdTile<D>::SEC, CH = D / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t st[2][kBlk][D + 8];
   const int tile = blockIdx.x % n_tiles, g = blockIdx.x / n_tiles;
   uint16_t *out = dst + ((int64_t)g * n_tiles + tile) * BwdTile<D>::E;
   for (int idx = threadIdx.x; idx < 2 * kBlk * CH; idx += 256) {
@@ -122,17 +127,7 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint16_t *ksrc, con
         if (any_nonfinite8(x)) atomicOr(status, kStatusRange);
       }
     }
-    *reinterpret_cast<u16x8 *>(&st[w][r][8 * c]) = x;
     *reinterpret_cast<u16x8 *>(out + w * SEC + r * D + 8 * PackedTile<D>::template swz<2 * D>(r, c)) = x;
-  }
-  __syncthreads();
-  // transposed sections: row = dim, eight chunks of eight key slots
-  for (int idx = threadIdx.x; idx < 2 * D * 8; idx += 256) {
-    const int w = idx / (D * 8), r = (idx / 8) % D, c = idx % 8;
-    u16x8 x;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = st[w][PackedTile<D>::vkey(8 * c + i)][r];
-    *reinterpret_cast<u16x8 *>(out + (2 + w) * SEC + r * kBlk + 8 * PackedTile<D>::template swz<2 * kBlk>(r, c)) = x;
   }
 }
 
@@ -231,11 +226,32 @@ __device__ __forceinline__ void tile_scores(const uint16_t *sec, const u16x8 (&b
     for (int kt = 0; kt < 4; ++kt) s[kt] = mfma_f16(pk_k_frag<D>(sec, kt, ds, lane), b[ds], s[kt]);
 }
 
-// Pass 1 over one tile (sections K rows and V^T): online max and sum of the
+// A operand (16 dims x 32 keys) of key half kh from a staged section of K
+// or V rows (row-major, 16-byte chunks swizzled per row), through the
+// transposing LDS read: lane l gets dim 16 dt + l % 16 at keys
+// 32 kh + 4 (l / 16) + j (elements 0-3) and 32 kh + 16 + 4 (l / 16) + j
+// (elements 4-7), the key-slot order of the P and dS operands. Within each
+// 16-lane group the read hands lane i element j of the 8 bytes that lane
+// i / 4 + 4 j addressed; lane s addresses keys 4 (l / 16) + s / 4 (+ 16),
+// dims 16 dt + 4 (s % 4) .. + 3.
+template <int D>
+__device__ __forceinline__ u16x8 sec_tr_frag(const uint16_t *sec, int dt, int kh, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const int r0 = 32 * kh + 4 * g + (s >> 2), r1 = r0 + 16;
+  const int d = 16 * dt + 4 * (s & 3), c = d >> 3, h = d & 7;  // chunk of the four dims, and 0 or 4 in it
+  const uint16_t *p0 = sec + r0 * D + 8 * PackedTile<D>::template swz<2 * D>(r0, c) + h;
+  const uint16_t *p1 = sec + r1 * D + 8 * PackedTile<D>::template swz<2 * D>(r1, c) + h;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p0);
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p1);
+  return u16x8{(uint16_t)a[0], (uint16_t)a[1], (uint16_t)a[2], (uint16_t)a[3],
+               (uint16_t)b[0], (uint16_t)b[1], (uint16_t)b[2], (uint16_t)b[3]};
+}
+
+// Pass 1 over one tile (sections K rows and V rows): online max and sum of the
 // row's exponentials (log2 domain) and O^T += V^T P^T. valid(kt, i) says
 // whether the row sees key 16 kt + 4 (lane / 16) + i of the tile.
 template <int D, class Valid>
-__device__ __forceinline__ void q_pass1(const uint16_t *kp, const uint16_t *vtp, const u16x8 (&qf)[D / 32],
+__device__ __forceinline__ void q_pass1(const uint16_t *kp, const uint16_t *vp, const u16x8 (&qf)[D / 32],
                                         f32x4 (&oa)[D / 16], float &m, float &l, float sl2, Valid valid, int lane) {
   f32x4 s[4];
   tile_scores<D>(kp, qf, s, lane);
@@ -270,13 +286,13 @@ __device__ __forceinline__ void q_pass1(const uint16_t *kp, const uint16_t *vtp,
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) oa[dt] = mfma_f16(pk_v_frag<D>(vtp, dt, kh, lane), pp[kh], oa[dt]);
+    for (int dt = 0; dt < D / 16; ++dt) oa[dt] = mfma_f16(sec_tr_frag<D>(vp, dt, kh, lane), pp[kh], oa[dt]);
 }
 
-// Pass 2 over one tile (sections K rows, V rows, K^T): P from the row's
+// Pass 2 over one tile (sections K rows and V rows): P from the row's
 // log-sum-exp, dP^T = V dO^T, dS = sig P (dP - dd), dq^T += K^T dS^T.
 template <int D, class Valid>
-__device__ __forceinline__ void q_pass2(const uint16_t *kp, const uint16_t *vp, const uint16_t *ktp,
+__device__ __forceinline__ void q_pass2(const uint16_t *kp, const uint16_t *vp,
                                         const u16x8 (&qf)[D / 32], const u16x8 (&of)[D / 32], f32x4 (&dqa)[D / 16],
                                         float lse2, float dd, float sig, float sl2, Valid valid, int lane) {
   f32x4 s[4], dp[4];
@@ -294,7 +310,7 @@ __device__ __forceinline__ void q_pass2(const uint16_t *kp, const uint16_t *vp, 
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) dqa[dt] = mfma_f16(pk_v_frag<D>(ktp, dt, kh, lane), pd[kh], dqa[dt]);
+    for (int dt = 0; dt < D / 16; ++dt) dqa[dt] = mfma_f16(sec_tr_frag<D>(kp, dt, kh, lane), pd[kh], dqa[dt]);
 }
 
 // Query rows of one wave: TP tokens x G heads (+ padding rows) of one KV
@@ -341,26 +357,21 @@ __device__ __forceinline__ void q_operands(const BwdParams &p, bool rv, int64_t 
   if (bad) atomicOr(p.status, kStatusRange);
 }
 
-// Global section of backward-tile slot s in each pass: pass 1 stages K rows
-// and V^T, pass 2 K rows, V rows and K^T.
-template <int PASS>
-__device__ __forceinline__ constexpr int pass_sec(int s) { return PASS == 1 ? (s == 0 ? 0 : 3) : s; }
-
 // The workgroup walks n tiles in lockstep (n and tile_of(i), the global
 // base of tile i, are the same for every wave): each step copies the next
-// tile's sections of this pass into the other LDS buffer by direct
+// tile's two sections (K rows, V rows) into the other LDS buffer by direct
 // global->LDS loads, the copies split over the waves, while every wave runs
 // body(i, staged sections) on the current tile; then each wave waits for its
 // own copies and the workgroup meets at a barrier.
 template <int D, int PASS, class TileOf, class Body>
 __device__ __forceinline__ void lockstep(int n, TileOf tile_of, uint16_t *lds, Body body, int wv, int lane) {
-  constexpr int SEC = BwdTile<D>::SEC, NSEC = PASS == 1 ? 2 : 3, PPS = SEC / 512, PPW = NSEC * PPS / kQWaves;
+  constexpr int SEC = BwdTile<D>::SEC, NSEC = 2, PPS = SEC / 512, PPW = NSEC * PPS / kQWaves;
   static_assert((NSEC * PPS) % kQWaves == 0, "copies split evenly over the waves");
   auto copy = [&](const uint16_t *src, uint16_t *dst) {
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
       const int pc = wv * PPW + j, sl = pc / PPS, off = pc % PPS;
-      __builtin_amdgcn_global_load_lds(src + pass_sec<PASS>(sl) * SEC + off * 512 + lane * 8,
+      __builtin_amdgcn_global_load_lds(src + sl * SEC + off * 512 + lane * 8,
                                        (lds_void *)(dst + sl * SEC + off * 512), 16, 0, 0);
     }
   };
@@ -369,8 +380,8 @@ __device__ __forceinline__ void lockstep(int n, TileOf tile_of, uint16_t *lds, B
   wait_vm_c<0>();
   bare_barrier();
   for (int i = 0; i < n; ++i) {
-    if (i + 1 < n) copy(tile_of(i + 1), lds + ((i + 1) & 1) * 3 * SEC);
-    body(i, lds + (i & 1) * 3 * SEC);
+    if (i + 1 < n) copy(tile_of(i + 1), lds + ((i + 1) & 1) * NSEC * SEC);
+    body(i, lds + (i & 1) * NSEC * SEC);
     wait_vm_c<0>();
     bare_barrier();
   }
@@ -378,7 +389,7 @@ __device__ __forceinline__ void lockstep(int n, TileOf tile_of, uint16_t *lds, B
 
 // One branch for the wave's rows: pass 1 (log-sum-exp, o, then D = dout . o,
 // the statistics for the key side and the gate gradient), pass 2 (dq).
-// walk(pass tag, f) calls f(section 0, 1, 2, valid) for the tiles the wave
+// walk(pass tag, f) calls f(K rows, V rows, valid) for the tiles the wave
 // needs, in the same order in both passes.
 template <int D, class Walk>
 __device__ __forceinline__ void q_branch(const BwdParams &p, Walk walk, const u16x8 (&qf)[D / 32],
@@ -390,7 +401,7 @@ __device__ __forceinline__ void q_branch(const BwdParams &p, Walk walk, const u1
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oa[dt] = zero4();
   float m = -INFINITY, l = 0.f;
-  walk(std::integral_constant<int, 1>(), [&](const uint16_t *s0, const uint16_t *s1, const uint16_t *, auto valid) {
+  walk(std::integral_constant<int, 1>(), [&](const uint16_t *s0, const uint16_t *s1, auto valid) {
     q_pass1<D>(s0, s1, qf, oa, m, l, sl2, valid, lane);
   });
   const float L = grp_sum(l);
@@ -413,8 +424,8 @@ __device__ __forceinline__ void q_branch(const BwdParams &p, Walk walk, const u1
     stat[1] = dd;
     if (dgate) *dgate = sig * (1.f - sig) * dd;
   }
-  walk(std::integral_constant<int, 2>(), [&](const uint16_t *s0, const uint16_t *s1, const uint16_t *s2, auto valid) {
-    q_pass2<D>(s0, s1, s2, qf, of, dqa, lse2, dd, sig, sl2, valid, lane);
+  walk(std::integral_constant<int, 2>(), [&](const uint16_t *s0, const uint16_t *s1, auto valid) {
+    q_pass2<D>(s0, s1, qf, of, dqa, lse2, dd, sig, sl2, valid, lane);
   });
 }
 
@@ -425,7 +436,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
                                                                                                     int n_qt) {
   using R = QRows<D, G, false>;
   constexpr int TP = R::TP, DT = D / 16, SEC = BwdTile<D>::SEC, E = BwdTile<D>::E, TW = TP * kQWaves;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * SEC];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * SEC];
   __shared__ uint32_t ubits[kMaxVTile / 32];   // union of the workgroup's selected blocks
   __shared__ uint16_t ulist[TW * kMaxTopk];    // the union, ascending
   __shared__ int n_union;
@@ -463,7 +474,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
           n_tiles, [&](int i) { return p.tile_c + ((int64_t)g * p.n_ctile + i) * E; }, lds,
           [&](int i, const uint16_t *b) {
             const int b0 = i * kBlk + 4 * grp;
-            f(b, b + SEC, b + 2 * SEC, [&](int kt, int e) { return (b0 + 16 * kt + e + 1) * kBlk <= tok + 1; });
+            f(b, b + SEC, [&](int kt, int e) { return (b0 + 16 * kt + e + 1) * kBlk <= tok + 1; });
           },
           wv, lane);
     };
@@ -536,7 +547,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
             if (need) {  // wave-uniform
               const bool rowneed = r.rv && ((need >> tau) & 1u);
               const int j0 = u * kBlk + 4 * grp;
-              f(b, b + SEC, b + 2 * SEC, [&](int kt, int e) { return rowneed && j0 + 16 * kt + e <= tok; });
+              f(b, b + SEC, [&](int kt, int e) { return rowneed && j0 + 16 * kt + e <= tok; });
             }
           },
           wv, lane);
@@ -552,7 +563,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
           hi - lo + 1, [&](int i) { return p.tile_v + ((int64_t)g * p.n_vtile + lo + i) * E; }, lds,
           [&](int i, const uint16_t *b) {
             const int j0 = (lo + i) * kBlk + 4 * grp;
-            f(b, b + SEC, b + 2 * SEC, [&](int kt, int e) {
+            f(b, b + SEC, [&](int kt, int e) {
               const int j = j0 + 16 * kt + e;
               return j <= tok && j > tok - w;
             });
@@ -581,7 +592,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
                                                                                                      int pass) {
   using R = QRows<D, G, true>;
   constexpr int TP = R::TP, DT = D / 16, SEC = BwdTile<D>::SEC, E = BwdTile<D>::E, TW = TP * kQWaves;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 3 * SEC];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * SEC];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n_grp = (n_qt + kQWaves - 1) / kQWaves;
   const int wg = blockIdx.x;
@@ -629,7 +640,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     for (int dt = 0; dt < DT; ++dt) dqa[dt] = zero4();
     lockstep<D, 2>(hi - lo, tile_of, lds, [&](int i, const uint16_t *b) {
       const int64_t k0 = (int64_t)(lo + i) * kBlk + 4 * grp;
-      q_pass2<D>(b, b + SEC, b + 2 * SEC, qf, of, dqa, lse2, dd, 1.f, sl2,
+      q_pass2<D>(b, b + SEC, qf, of, dqa, lse2, dd, 1.f, sl2,
                  [&](int kt, int e) { return k0 + 16 * kt + e <= mypos; }, lane);
     }, wv, lane);
     if (r.rv) {
@@ -714,9 +725,6 @@ struct KvStage {
   float l2[32], dd[32], sig[32];
   int tok[32];
 };
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // A operand (16 dims x 32 rows) of a product over the step's rows from a
 // row-major staged array: lane l takes dim 16 dt + (l % 16) and, as its

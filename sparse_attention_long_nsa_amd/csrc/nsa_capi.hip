@@ -494,7 +494,7 @@ static nsa_status plan_backward(const nsa_prefill_desc *ds, const uint8_t *is_vi
   L.mask_words = (int)((pl.n_vis + 31) / 32);
   L.n_chunk = (int)((pl.n_vis + 2047) / 2048);
   L.n_tsplit = n_text > 0 ? 8 : 0;  // text rows' key-tile splits
-  const size_t tile = sizeof(uint16_t) * 4 * kBlk * (size_t)pl.d * pl.hkv;  // one tile, every group
+  const size_t tile = sizeof(uint16_t) * 2 * kBlk * (size_t)pl.d * pl.hkv;  // one tile (K, V rows), every group
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   L.status = take(sizeof(int32_t));  // offset 0: the status word (nsa_workspace_status)

@@ -399,7 +399,7 @@ def test_backward_validation_and_workspace():
     # 1,024 vision tokens (16 blocks, one 2,048-token chunk), 64 text tokens,
     # 28 / 4 heads, d 128, k 16; every array rounded up to 256 bytes
     a = lambda x: (x + 255) // 256 * 256
-    nb, tile = 16 * 4 * 128, 4 * 64 * 128 * 2 * 4
+    nb, tile = 16 * 4 * 128, 2 * 64 * 128 * 2 * 4  # a tile: K and V rows, fp16, four KV groups
     parts = [4]                                   # the status word
     parts += [4 * nb] * 6 + [2 * nb] * 2          # compressed k / v, means, their gradients; fp16 copies
     parts += [tile * 16, tile * 17, tile * 1]     # tiles: vision blocks, positions, compressed keys
