@@ -362,9 +362,12 @@ __device__ __forceinline__ void q_operands(const BwdParams &p, bool rv, int64_t 
 // tile's two sections (K rows, V rows) into the other LDS buffer by direct
 // global->LDS loads, the copies split over the waves, while every wave runs
 // body(i, staged sections) on the current tile; then each wave waits for its
-// own copies and the workgroup meets at a barrier.
+// own copies and the workgroup meets at a barrier. The two buffers are
+// separate LDS objects and each step names its buffers at compile time, so
+// the reads of one need not wait for the copies still landing in the other.
 template <int D, int PASS, class TileOf, class Body>
-__device__ __forceinline__ void lockstep(int n, TileOf tile_of, uint16_t *lds, Body body, int wv, int lane) {
+__device__ __forceinline__ void lockstep(int n, TileOf tile_of, uint16_t (&l0)[2 * BwdTile<D>::SEC],
+                                         uint16_t (&l1)[2 * BwdTile<D>::SEC], Body body, int wv, int lane) {
   constexpr int SEC = BwdTile<D>::SEC, NSEC = 2, PPS = SEC / 512, PPW = NSEC * PPS / kQWaves;
   static_assert((NSEC * PPS) % kQWaves == 0, "copies split evenly over the waves");
   auto copy = [&](const uint16_t *src, uint16_t *dst) {
@@ -376,14 +379,20 @@ __device__ __forceinline__ void lockstep(int n, TileOf tile_of, uint16_t *lds, B
     }
   };
   if (n <= 0) return;
-  copy(tile_of(0), lds);
+  copy(tile_of(0), l0);
   wait_vm_c<0>();
   bare_barrier();
-  for (int i = 0; i < n; ++i) {
-    if (i + 1 < n) copy(tile_of(i + 1), lds + ((i + 1) & 1) * NSEC * SEC);
-    body(i, lds + (i & 1) * NSEC * SEC);
+  for (int i = 0; i < n;) {
+    if (i + 1 < n) copy(tile_of(i + 1), l1);
+    body(i, static_cast<const uint16_t *>(l0));
     wait_vm_c<0>();
     bare_barrier();
+    if (++i >= n) break;
+    if (i + 1 < n) copy(tile_of(i + 1), l0);
+    body(i, static_cast<const uint16_t *>(l1));
+    wait_vm_c<0>();
+    bare_barrier();
+    ++i;
   }
 }
 
@@ -436,7 +445,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
                                                                                                     int n_qt) {
   using R = QRows<D, G, false>;
   constexpr int TP = R::TP, DT = D / 16, SEC = BwdTile<D>::SEC, E = BwdTile<D>::E, TW = TP * kQWaves;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * SEC];
+  __shared__ __attribute__((aligned(16))) uint16_t lds0[2 * SEC], lds1[2 * SEC];  // the two step buffers
   __shared__ uint32_t ubits[kMaxVTile / 32];   // union of the workgroup's selected blocks
   __shared__ uint16_t ulist[TW * kMaxTopk];    // the union, ascending
   __shared__ int n_union;
@@ -471,7 +480,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     const int n_tiles = (nc + kBlk - 1) / kBlk;
     auto walk = [&](auto pass, auto f) {
       lockstep<D, decltype(pass)::value>(
-          n_tiles, [&](int i) { return p.tile_c + ((int64_t)g * p.n_ctile + i) * E; }, lds,
+          n_tiles, [&](int i) { return p.tile_c + ((int64_t)g * p.n_ctile + i) * E; }, lds0, lds1,
           [&](int i, const uint16_t *b) {
             const int b0 = i * kBlk + 4 * grp;
             f(b, b + SEC, [&](int kt, int e) { return (b0 + 16 * kt + e + 1) * kBlk <= tok + 1; });
@@ -532,7 +541,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
         nxt[q] = __builtin_amdgcn_readlane(lst[q], 0);
       }
       lockstep<D, decltype(pass)::value>(
-          nu, [&](int i) { return p.tile_v + ((int64_t)g * p.n_vtile + ulist[i]) * E; }, lds,
+          nu, [&](int i) { return p.tile_v + ((int64_t)g * p.n_vtile + ulist[i]) * E; }, lds0, lds1,
           [&](int i, const uint16_t *b) {
             const int u = ulist[i];
             uint32_t need = 0u;
@@ -560,7 +569,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     const int w = p.window;
     auto walk = [&](auto pass, auto f) {
       lockstep<D, decltype(pass)::value>(
-          hi - lo + 1, [&](int i) { return p.tile_v + ((int64_t)g * p.n_vtile + lo + i) * E; }, lds,
+          hi - lo + 1, [&](int i) { return p.tile_v + ((int64_t)g * p.n_vtile + lo + i) * E; }, lds0, lds1,
           [&](int i, const uint16_t *b) {
             const int j0 = (lo + i) * kBlk + 4 * grp;
             f(b, b + SEC, [&](int kt, int e) {
@@ -592,7 +601,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
                                                                                                      int pass) {
   using R = QRows<D, G, true>;
   constexpr int TP = R::TP, DT = D / 16, SEC = BwdTile<D>::SEC, E = BwdTile<D>::E, TW = TP * kQWaves;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * SEC];
+  __shared__ __attribute__((aligned(16))) uint16_t lds0[2 * SEC], lds1[2 * SEC];  // the two step buffers
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n_grp = (n_qt + kQWaves - 1) / kQWaves;
   const int wg = blockIdx.x;
@@ -616,7 +625,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oa[dt] = zero4();
     float m = -INFINITY, l = 0.f;
-    lockstep<D, 1>(hi - lo, tile_of, lds, [&](int i, const uint16_t *b) {
+    lockstep<D, 1>(hi - lo, tile_of, lds0, lds1, [&](int i, const uint16_t *b) {
       const int64_t k0 = (int64_t)(lo + i) * kBlk + 4 * grp;
       q_pass1<D>(b, b + SEC, qf, oa, m, l, sl2, [&](int kt, int e) { return k0 + 16 * kt + e <= mypos; }, lane);
     }, wv, lane);
@@ -638,7 +647,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     f32x4 dqa[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dqa[dt] = zero4();
-    lockstep<D, 2>(hi - lo, tile_of, lds, [&](int i, const uint16_t *b) {
+    lockstep<D, 2>(hi - lo, tile_of, lds0, lds1, [&](int i, const uint16_t *b) {
       const int64_t k0 = (int64_t)(lo + i) * kBlk + 4 * grp;
       q_pass2<D>(b, b + SEC, qf, of, dqa, lse2, dd, 1.f, sl2,
                  [&](int kt, int e) { return k0 + 16 * kt + e <= mypos; }, lane);
