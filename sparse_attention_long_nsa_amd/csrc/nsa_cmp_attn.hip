@@ -42,8 +42,8 @@ constexpr int kBufWord3 = 0x00020000;  // buffer resource word 3 (raw, 32-bit) o
 // Folds four scaled logits (log2 units, -inf = masked) into a lane-partial
 // (max, sum) pair.
 __device__ __forceinline__ void fold4(float &m, float &l, const f32x4 x) {
-  const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  const float mn = fmaxf(m, mx);
+  const float mx = fmax_nn(fmax_nn(x[0], x[1]), fmax_nn(x[2], x[3]));
+  const float mn = fmax_nn(m, mx);
   if (mn == -INFINITY) return;
   l = l * exp2f(m - mn) + exp2f(x[0] - mn) + exp2f(x[1] - mn) + exp2f(x[2] - mn) + exp2f(x[3] - mn);
   m = mn;
@@ -263,9 +263,9 @@ __device__ __forceinline__ void cmp_pass1_chunk(const uint16_t *ks, int c, const
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kk][i]);
+        for (int i = 0; i < 4; ++i) mx = fmax_nn(mx, sc[kk][i]);
       // raw scores; the scale sl2 > 0 is folded into the exponent
-      const float mn = fmaxf(m[h], mx * sl2);
+      const float mn = fmax_nn(m[h], mx * sl2);
       const float nb = (mn == -INFINITY) ? 0.f : -mn;
       float acc = (m[h] == -INFINITY) ? 0.f : l[h] * __builtin_amdgcn_exp2f(m[h] + nb);
 #pragma unroll

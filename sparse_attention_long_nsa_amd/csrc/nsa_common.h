@@ -78,13 +78,25 @@ __device__ __forceinline__ uint16_t bf2h_bits(uint16_t b) { return f2h_bits(bfbi
 // transposed score tile) with the row-swap permutes: the 32-lane swap of x
 // with itself yields x[l mod 32] and x[(l mod 32) + 32] in the two results,
 // the 16-lane swap likewise pairs rows 0/1 and 2/3.
+// Maximum of two floats that are never NaN, as one v_med3_f32 against +inf:
+// med3(a, b, +inf) = max(a, b). fmaxf instead costs up to three
+// instructions, since LLVM quiets each operand it cannot prove canonical
+// (matrix-core and permute results) with a v_max_f32 x, x, x first. The +inf
+// comes from an opaque scalar move so that LLVM does not rewrite the med3
+// back into fmaxf's form.
+__device__ __forceinline__ float pos_inf_opaque() {
+  float x;
+  asm("s_mov_b32 %0, 0x7f800000" : "=s"(x));
+  return x;
+}
+__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, pos_inf_opaque()); }
 __device__ __forceinline__ float grp_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = fmax_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const uint32_t v = __float_as_uint(x);
   const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax_nn(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float grp_sum(float x) {
   const uint32_t u = __float_as_uint(x);

@@ -49,7 +49,7 @@ struct DecPlan {
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int o = 32; o > 0; o >>= 1) v = fmax_nn(v, __shfl_xor(v, o));
   return v;
 }
 
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(64 * kItemWaves) void dec_item_kernel(DecodeParams 
   for (int i = 0; i < 4; ++i) {
     const int key = j0 + 4 * grp + i;
     s[i] = key < nk ? s[i] * p.sl2 : -INFINITY;
-    mx = fmaxf(mx, s[i]);
+    mx = fmax_nn(mx, s[i]);
   }
   if (is_cmp && row < G) {  // logits of the compressed blocks, for the importance scores
     float *lg = p.logits + ((int64_t)bi * p.hq + g * G + row) * p.n_blk + key0;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64 * kItemWaves) void dec_item_kernel(DecodeParams 
   if (lane < 16) red[0][wv][lane] = mx;
   __syncthreads();
   // key 0 is always valid: the item's max is finite
-  const float m = fmaxf(fmaxf(red[0][0][row], red[0][1][row]), fmaxf(red[0][2][row], red[0][3][row]));
+  const float m = fmax_nn(fmax_nn(red[0][0][row], red[0][1][row]), fmax_nn(red[0][2][row], red[0][3][row]));
   float ls = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(dec_select_threads<NPL>()) void dec_select_kernel(D
   __syncthreads();
   for (int h = wv; h < G; h += kDecThreads / 64) {
     float M = -INFINITY;
-    for (int c = lane; c < p.n_chunk; c += 64) M = fmaxf(M, wt[h][c]);
+    for (int c = lane; c < p.n_chunk; c += 64) M = fmax_nn(M, wt[h][c]);
     M = wave_max(M);
     float L = 0.f;
     for (int c = lane; c < p.n_chunk; c += 64) L += ls[h][c] * exp2f(wt[h][c] - M);
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(D) void dec_combine_kernel(DecodeParams p) {
     const int i0 = br == 0 ? 0 : p.topk, i1 = br == 0 ? p.topk : p.n_items;
     float M = -INFINITY;
 #pragma unroll 8
-    for (int i = i0; i < i1; ++i) M = fmaxf(M, part[(int64_t)i * (D + 2)]);
+    for (int i = i0; i < i1; ++i) M = fmax_nn(M, part[(int64_t)i * (D + 2)]);
     float L = 0.f, o = 0.f;
 #pragma unroll 8
     for (int i = i0; i < i1; ++i) {

@@ -75,10 +75,10 @@ __device__ __forceinline__ void online_chunk(const uint16_t *ks, const uint16_t 
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kk][h][i]);
+        for (int i = 0; i < 4; ++i) mx = fmax_nn(mx, s[kk][h][i]);
       mx = grp_max(mx) * sl2;  // the row's max over the half (all its lanes)
       if (__builtin_amdgcn_ballot_w64(mx > m[h] + kSlack)) {
-        const float mn = fmaxf(m[h], mx);
+        const float mn = fmax_nn(m[h], mx);
         const float alpha = (m[h] == -INFINITY) ? 1.f : exp2f(m[h] - mn);
         l[h] *= alpha;
 #pragma unroll
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(D) void text_merge_kernel(TextParams p) {
   float M = -INFINITY;
 #pragma unroll 16
   for (int sp = 0; sp < p.n_split; ++sp)
-    M = fmaxf(M, p.part_ml[((int64_t)sp * p.n_text + r) * p.hq + h].x);
+    M = fmax_nn(M, p.part_ml[((int64_t)sp * p.n_text + r) * p.hq + h].x);
   float acc = 0.f, L = 0.f;
 #pragma unroll 16
   for (int sp = 0; sp < p.n_split; ++sp) {

@@ -93,16 +93,16 @@ __device__ __forceinline__ void sel_tile(const uint16_t *ks, const uint16_t *vt,
       for (int e = 0; e < 4; ++e) s[kt][e] = (j0 + e <= t) ? s[kt][e] : -INFINITY;
     }
   }
-  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
-                       fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+  float mx = fmax_nn(fmax_nn(fmax_nn(s[0][0], s[0][1]), fmax_nn(s[0][2], s[0][3])),
+                   fmax_nn(fmax_nn(s[1][0], s[1][1]), fmax_nn(s[1][2], s[1][3])));
+  mx = fmax_nn(mx, fmax_nn(fmax_nn(fmax_nn(s[2][0], s[2][1]), fmax_nn(s[2][2], s[2][3])),
+                       fmax_nn(fmax_nn(s[3][0], s[3][1]), fmax_nn(s[3][2], s[3][3]))));
   const float gmx = grp_max(mx);  // all lanes take part in the exchange
   mx = rowneed ? gmx * sl2 : -INFINITY;
   // the running max only moves when a row's new max exceeds it by the
   // slack; probabilities then stay below 2^slack, exact in fp16's range
   if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
-    const float mn = fmaxf(m, mx);
+    const float mn = fmax_nn(m, mx);
     const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
     l *= alpha;
 #pragma unroll
