@@ -7,25 +7,31 @@
 // a consumer wave owns RT such tiles. A workgroup takes TOK consecutive
 // tokens (half a 64-token frame where the tiles allow: tokens of one frame
 // pick largely the same blocks) of one KV group and the union of the blocks
-// they selected, in ascending order. Two producer waves stream the union's
-// blocks into a ring of LDS slots with direct global->LDS copies; each
-// consumer wave walks the union positions its own tokens selected, waits
-// only for those blocks, and runs at its own pace: there is no workgroup
-// barrier per block, so a block that few tiles need costs only those tiles.
-// A slot is refilled once every consumer has moved past its block. Keys and
-// values are first packed once per call into block-major tiles, exactly as
-// they sit in LDS (K row-major, V transposed to fp16, both with 16-byte
-// chunks XOR-swizzled per row so that the 16-byte fragment reads are free of
-// bank conflicts without padding), so each block is one contiguous 2*64*d
-// element region and the copies are plain linear ones.
+// they selected, in ascending order. The union's blocks pass through a ring
+// of LDS slots filled by direct global->LDS copies; each wave walks the union
+// positions its own tokens selected, waits only for those blocks, and runs
+// at its own pace: there is no workgroup barrier per block, so a block that
+// few tiles need costs only those tiles. A slot is refilled once every wave
+// has moved past its block. Keys and values are first packed once per call
+// into block-major tiles, exactly as they sit in LDS (K row-major, V
+// transposed to fp16, both with 16-byte chunks XOR-swizzled per row so that
+// the 16-byte fragment reads are free of bank conflicts without padding), so
+// each block is one contiguous 2*64*d element region and the copies are
+// plain linear ones.
 //
-// Producer/consumer protocol (all counters in LDS, each written by one wave):
-//   ready[p]  blocks 0..ready[p]-1 of producer p's pieces are in LDS
-//   pass[c]   consumer c no longer reads blocks 0..pass[c]-1
-// Producer p issues block j into slot j % R once min(pass) >= j - R + 1, and
-// publishes a block after waiting for its own copies (in-order vmcnt).
-// Every wait is a bounded spin, so a broken protocol ends the kernel with
-// NaN outputs and a flag in the workspace status word instead of a hang.
+// There are no copy-only waves: a wave that would wait copies instead. It
+// claims the next union block whose slot every wave has left (compare-and-
+// swap on a shared counter), issues the whole block's copies, waits for them
+// (its own vmcnt) and publishes the block in that slot's ready word. Waves
+// that are still computing leave the copying to those that are idle, and the
+// workgroup is all consumers (eight waves for 7-head groups, two per SIMD,
+// each with up to 256 registers). Counters, all in LDS:
+//   pass[c]        wave c no longer reads union blocks 0..pass[c]-1
+//   next_issue     union blocks 0..next_issue-1 have been claimed
+//   ready_slot[s]  j + 1 once union block j has landed in slot s = j % R
+// Block j may be claimed once min(pass) >= j - R + 1. Every wait is a
+// bounded spin, so a broken protocol ends the kernel with NaN outputs and a
+// flag in the workspace status word instead of a hang.
 //
 // Output: the (row, head) slots of the output hold the fp16 partials of the
 // compression and window branches (written by their kernels); the consumer
@@ -49,16 +55,13 @@ struct SelCfg {
   static constexpr int TT = RT * TP;                  // tokens per consumer wave
   static constexpr int NC = (32 / TT > 0) ? 32 / TT : 1;  // consumer waves
   static constexpr int TOK = NC * TT;                 // tokens per workgroup
-  static constexpr int NPW = 2;                       // producer waves
-  static constexpr int NW = NC + NPW;
+  static constexpr int NW = NC;                       // waves: consumers only
   static constexpr int NT = 64 * NW;
   static constexpr int KE = PackedTile<D>::KE, VE = PackedTile<D>::VE;
   static constexpr int SE = KE + VE;                  // one slot (elements)
   static constexpr int NP = SE / 512;                 // 1-KB copy pieces per block
-  static constexpr int PPP = NP / NPW;                // pieces per producer per block
   static constexpr int R = (D == 64) ? 8 : 4;         // ring slots
-  static constexpr int INFL = (63 / PPP < R) ? 63 / PPP : R;  // blocks in flight per producer
-  static_assert(NP % NPW == 0 && PPP % 4 == 0, "pieces split evenly, four per address set-up");
+  static_assert(NP % 4 == 0 && NP < 64, "pieces: four per address set-up, one vmcnt wait");
   static_assert(TOK <= 32 && NW <= 16, "workgroup shape");
 };
 
@@ -145,7 +148,8 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   __shared__ int16_t ulist[TOK * kSelMaxK];    // union, ascending
   __shared__ uint32_t ubits[kSelMaxBlk / 32];  // union as a bitmask over blocks
   __shared__ int16_t wpre[kSelMaxBlk / 32];    // union entries before each bitmask word
-  __shared__ int pass_[NC], ready_[C::NPW];
+  __shared__ int pass_[NC], ready_slot[R];   // ready_slot[s]: block + 1 landed in slot s
+  __shared__ int next_issue;                  // next union position to copy
   __shared__ int tpos[TOK];                    // position of each token of the chunk
   __shared__ int n_union;
 
@@ -173,7 +177,8 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   // ---- selected blocks of the workgroup's tokens and their union
   for (int w = tid; w < nwords; w += C::NT) ubits[w] = 0u;
   if (tid < NC) pass_[tid] = 0;
-  if (tid < C::NPW) ready_[tid] = 0;
+  if (tid < R) ready_slot[tid] = 0;
+  if (tid == 0) next_issue = 0;
   if (tid < TOK) tpos[tid] = tid < ntok ? (int)row_pos(p.vmap, p.v0, tok0 + tid) : 0;
   for (int idx = tid; idx < TOK * k; idx += C::NT) {
     const int tk = idx / k;
@@ -213,70 +218,33 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   __syncthreads();
   const int nU = n_union;
 
-  if (wv >= NC) {
-    // ---------------------------------------------------------- producer
-    // producer pw moves the contiguous pieces [pw*PPP, (pw+1)*PPP) of each
-    // block, four per address set-up (immediate offsets of 0..3 KB)
-    const int pw = __builtin_amdgcn_readfirstlane(wv - NC);
-    const uint16_t *kvg = p.kv + (int64_t)g * p.n_frames * C::SE + pw * C::PPP * 512;
-    int issued = 0, pub = 0, spins = 0;
-    int free_until = R - 1;  // highest block whose slot is known to be free
-    // union entries of the current 64-block window and of the next one
-    // (the next window is loaded a window ahead, off the critical path)
-    int ul = lane < nU ? (int)ulist[lane] : 0;
-    int ul_next = 64 + lane < nU ? (int)ulist[64 + lane] : 0;
-    // The consumers' pass counters are read one check ahead: the LDS load
-    // for the next check is issued as soon as the previous one is consumed,
-    // so its latency overlaps the copies and the waits in between.
-    int pv = lane < NC ? lds_load(&pass_[lane]) : kSent;
-    while (pub < nU) {
-      if (issued < nU && issued - pub < C::INFL) {
-        if (issued > free_until) {
-          int mn = pv;
-#pragma unroll
-          for (int q = 0; q < NC; ++q) mn = min(mn, __builtin_amdgcn_readlane(pv, q));
-          free_until = __builtin_amdgcn_readfirstlane(mn + R - 1);
-          pv = lane < NC ? lds_load(&pass_[lane]) : kSent;
-        }
-        if (issued <= free_until) {
-          if (issued > 0 && (issued & 63) == 0) {
-            ul = ul_next;
-            ul_next = issued + 64 + lane < nU ? (int)ulist[issued + 64 + lane] : 0;
-          }
-          const int blk = __builtin_amdgcn_readlane(ul, issued & 63);
-          const uint16_t *src = kvg + (int64_t)blk * C::SE;
-          uint16_t *dst = ring + (issued % R) * C::SE + pw * C::PPP * 512;
-          asm volatile("" ::: "memory");
-          dma_pieces<C::PPP>(src, dst, lane);
-          issued = __builtin_amdgcn_readfirstlane(issued + 1);
-          continue;
-        }
-      }
-      if (issued > pub) {  // publish the oldest block in flight
-        wait_blocks<C::PPP>(issued - pub - 1);
-        asm volatile("" ::: "memory");
-        pub = __builtin_amdgcn_readfirstlane(pub + 1);
-        if (lane == 0) lds_store(&ready_[pw], pub);
-        asm volatile("" ::: "memory");
-      } else {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > p.spin_limit) {  // consumers stalled: give up, release them
-          if (lane == 0) {
-            lds_store(&ready_[pw], nU);
-            if (p.status) atomicOr(p.status, kStatusWaitGaveUp);
-          }
-          break;
-        }
-      }
-    }
-    wait_vm_c<0>();  // no copy into this workgroup's LDS outlives the wave
-    return;
-  }
-
   // ------------------------------------------------------------ consumer
   const int c = wv;
   const int r16 = lane & 15, tau = r16 / G, hh = r16 % G;
   const float sl2 = p.sl2;
+  const uint16_t *kvg = p.kv + (int64_t)g * p.n_frames * C::SE;
+  // Copies are made by consumers that would otherwise wait: claim the next
+  // union block whose ring slot every consumer has left, copy it, wait for
+  // this wave's own copies, publish it. False when nothing was claimable.
+  auto try_copy = [&]() -> bool {
+    const int j = __builtin_amdgcn_readfirstlane(lds_load(&next_issue));
+    if (j >= nU) return false;
+    const int pv = lane < NC ? lds_load(&pass_[lane]) : kSent;
+    int mn = pv;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) mn = min(mn, __builtin_amdgcn_readlane(pv, q));
+    if (j > mn + R - 1) return false;  // its slot is still being read
+    int won = 0;
+    if (lane == 0) won = atomicCAS(&next_issue, j, j + 1) == j;
+    if (!__builtin_amdgcn_readfirstlane(won)) return false;
+    const int blk = __builtin_amdgcn_readfirstlane((int)ulist[j]);
+    asm volatile("" ::: "memory");
+    dma_pieces<C::NP>(kvg + (int64_t)blk * C::SE, ring + (j % R) * C::SE, lane);
+    wait_vm_c<0>();
+    asm volatile("" ::: "memory");
+    if (lane == 0) lds_store(&ready_slot[j % R], j + 1);
+    return true;
+  };
   u16x8 qf[RT][D / 32];
   f32x4 o[RT][D / 16];
   float m[RT], l[RT];
@@ -338,16 +306,10 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
       }
     }
     if (lane == 0) lds_store(&pass_[c], u);
-    // wait for every producer's pieces of block u
+    // wait until block u has landed in its slot, copying meanwhile
     int spins = 0;
-    auto min_ready = [&]() {
-      int r = lds_load(&ready_[0]);
-#pragma unroll
-      for (int q = 1; q < C::NPW; ++q) r = min(r, lds_load(&ready_[q]));
-      return r;
-    };
-    while (min_ready() <= u) {
-      __builtin_amdgcn_s_sleep(1);
+    while (lds_load(&ready_slot[u % R]) != u + 1) {
+      if (!try_copy()) __builtin_amdgcn_s_sleep(1);
       if (++spins > p.spin_limit) { bad = true; break; }
     }
     asm volatile("" ::: "memory");
@@ -367,6 +329,14 @@ __global__ __launch_bounds__((SelCfg<D, G>::NT)) void sel_attn_kernel(SelParams 
   if (lane == 0) {
     lds_store(&pass_[c], nU);
     if (bad && p.status) atomicOr(p.status, kStatusWaitGaveUp);  // the caller can ask
+  }
+  // keep copying for the consumers still walking
+  for (int spins = 0; __builtin_amdgcn_readfirstlane(lds_load(&next_issue)) < nU;) {
+    if (!try_copy()) __builtin_amdgcn_s_sleep(1);
+    if (++spins > p.spin_limit) {
+      if (lane == 0 && p.status) atomicOr(p.status, kStatusWaitGaveUp);
+      break;
+    }
   }
 
   const int grp = lane >> 4;
