@@ -47,6 +47,7 @@ namespace {
 constexpr int kSelMaxK = 64;
 constexpr int kSelMaxBlk = 8192;
 constexpr float kRescaleSlack = 8.f;  // log2 units a running max may lag behind
+constexpr uint32_t kFastMaxBits = 0x43000000u;  // bit pattern of 2^(kRescaleSlack - 1) = 128.0f
 
 template <int D, int G>
 struct SelCfg {
@@ -65,16 +66,14 @@ struct SelCfg {
   static_assert(TOK <= 32 && NW <= 16, "workgroup shape");
 };
 
-// Consumes one staged block for one row tile: S^T = K Q^T, causal mask in
-// the own block, lazily rescaled softmax, O^T += V^T P^T.
-template <int D, int G, bool F16>
-__device__ __forceinline__ void sel_tile(const uint16_t *ks, const uint16_t *vt, const u16x8 (&qf)[D / 32],
-                                         f32x4 (&o)[D / 16], float &m, float &l, bool rowneed,
-                                         int mask_b, int t, float sl2, int lane) {
+// S^T = K Q^T of one staged block for one row tile, with the causal mask
+// inside the own block (mask_b >= 0).
+template <int D, bool F16>
+__device__ __forceinline__ void sel_scores(const uint16_t *ks, const u16x8 (&qf)[D / 32], f32x4 (&s)[4],
+                                           int mask_b, int t, int lane) {
   const int grp = lane >> 4;
   // dims outer, key subtiles inner (two at a time): independent accumulators
   // keep the matrix pipe fed while the next fragments load
-  f32x4 s[4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) s[kt] = zero4();
 #pragma unroll
@@ -96,32 +95,76 @@ __device__ __forceinline__ void sel_tile(const uint16_t *ks, const uint16_t *vt,
       for (int e = 0; e < 4; ++e) s[kt][e] = (j0 + e <= t) ? s[kt][e] : -INFINITY;
     }
   }
-  float mx = fmax_nn(fmax_nn(fmax_nn(s[0][0], s[0][1]), fmax_nn(s[0][2], s[0][3])),
-                   fmax_nn(fmax_nn(s[1][0], s[1][1]), fmax_nn(s[1][2], s[1][3])));
-  mx = fmax_nn(mx, fmax_nn(fmax_nn(fmax_nn(s[2][0], s[2][1]), fmax_nn(s[2][2], s[2][3])),
-                       fmax_nn(fmax_nn(s[3][0], s[3][1]), fmax_nn(s[3][2], s[3][3]))));
-  const float gmx = grp_max(mx);  // all lanes take part in the exchange
-  mx = rowneed ? gmx * sl2 : -INFINITY;
-  // the running max only moves when a row's new max exceeds it by the
-  // slack; probabilities then stay below 2^slack, exact in fp16's range
-  if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
-    const float mn = fmax_nn(m, mx);
-    const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
-    l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
-    m = mn;
-  }
-  // rows that do not take this block get probability exp2(-inf) = 0
-  const float nbase = (rowneed && m != -INFINITY) ? -m : -INFINITY;
+}
+
+// Probabilities 2^(s sl2 + nbase) of a tile's scores, in place, and the
+// lane's share of their row sum (summed in key order).
+__device__ __forceinline__ float sel_exp(f32x4 (&s)[4], float sl2, float nbase) {
   float ls = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       s[kt][e] = __builtin_amdgcn_exp2f(fmaf(s[kt][e], sl2, nbase));
-      ls += s[kt][e];
+      ls = (kt == 0 && e == 0) ? s[kt][e] : ls + s[kt][e];
     }
+  return ls;
+}
+
+// Largest bit pattern among a lane's probabilities: they are never negative,
+// so unsigned order is float order, with +inf and NaN above every finite
+// value (integer maxima also need no NaN quieting and chain into v_max3_u32).
+__device__ __forceinline__ uint32_t sel_max_bits(const f32x4 (&s)[4]) {
+  uint32_t mb = __float_as_uint(s[0][0]);
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mb = max(mb, __float_as_uint(s[kt][e]));
+  return mb;
+}
+
+// Consumes one staged block for one row tile: S^T = K Q^T, causal mask in
+// the own block, lazily rescaled softmax, O^T += V^T P^T.
+//
+// The running max m only moves when a block's scores exceed it by the slack
+// (kRescaleSlack log2 units). So the probabilities are first formed against m
+// as it stands, without the block max. If none exceeds 2^(slack - 1), every
+// score is at least one log2 unit below m + slack (far beyond rounding): the
+// full step would not move m and forms exactly these probabilities.
+// Otherwise (a larger score; a row's first block, where m = -inf gives +inf;
+// a masked key against an unset max, NaN) the block's scores are recomputed
+// and the full step runs: block max, rescale when it exceeds m by the slack,
+// probabilities. Results are bitwise those of always running the full step.
+template <int D, int G, bool F16>
+__device__ __forceinline__ void sel_tile(const uint16_t *ks, const uint16_t *vt, const u16x8 (&qf)[D / 32],
+                                         f32x4 (&o)[D / 16], float &m, float &l, bool rowneed,
+                                         int mask_b, int t, float sl2, int lane) {
+  f32x4 s[4];
+  sel_scores<D, F16>(ks, qf, s, mask_b, t, lane);
+  float ls = sel_exp(s, sl2, rowneed ? -m : -INFINITY);
+  if (__builtin_amdgcn_ballot_w64(sel_max_bits(s) > kFastMaxBits)) {
+    // reload the key fragments rather than keep the first reads live
+    asm volatile("" ::: "memory");
+    sel_scores<D, F16>(ks, qf, s, mask_b, t, lane);
+    float mx = fmax_nn(fmax_nn(fmax_nn(s[0][0], s[0][1]), fmax_nn(s[0][2], s[0][3])),
+                       fmax_nn(fmax_nn(s[1][0], s[1][1]), fmax_nn(s[1][2], s[1][3])));
+    mx = fmax_nn(mx, fmax_nn(fmax_nn(fmax_nn(s[2][0], s[2][1]), fmax_nn(s[2][2], s[2][3])),
+                             fmax_nn(fmax_nn(s[3][0], s[3][1]), fmax_nn(s[3][2], s[3][3]))));
+    const float gmx = grp_max(mx);  // all lanes take part in the exchange
+    mx = rowneed ? gmx * sl2 : -INFINITY;
+    // the running max only moves when a row's new max exceeds it by the
+    // slack; probabilities then stay below 2^slack, exact in fp16's range
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
+      const float mn = fmax_nn(m, mx);
+      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
+      m = mn;
+    }
+    // rows that do not take this block get probability exp2(-inf) = 0
+    ls = sel_exp(s, sl2, (rowneed && m != -INFINITY) ? -m : -INFINITY);
+  }
   l += ls;
   const u16x8 pp[2] = {pack_p(s[0], s[1]), pack_p(s[2], s[3])};
   // key halves outer, dims inner: eight independent accumulators per half
