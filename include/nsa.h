@@ -199,7 +199,10 @@ nsa_status nsa_prefill_dense(const nsa_prefill_desc *desc, const void *q, const 
  * probabilities, the score gradients and the compressed keys / values
  * rounded to fp16) with fp32 accumulation, so q, k, v, dout and the
  * compressed keys / values must lie within the fp16 range (a value outside
- * it sets bit 1 of the workspace's status word, nsa_workspace_status).
+ * it sets bit 1 of the workspace's status word, nsa_workspace_status). The
+ * query side walks each workgroup's selected tiles through an LDS ring with
+ * bounded waits; a wait that gives up sets bit 0 of the status word and
+ * leaves NaN in that workgroup's dq rows (never a hang).
  * Every gradient element is written by one thread in a fixed order, so
  * results are bitwise repeatable.
  *   sel_idx   device [N_v, Hkv, top_k] int32 (may be NULL when N_v = 0): the

@@ -20,7 +20,10 @@
 //                 the decoded lists
 //   bwd_q         query side, one wave per (tile of 16/G tokens, KV group),
 //                 eight consecutive tiles per workgroup sharing each key tile
-//                 staged once in LDS: per branch, pass 1 recomputes the
+//                 staged once in LDS (window, compression: walked in
+//                 lockstep; selection: a three-slot ring that each wave walks
+//                 at its own pace over the tiles its tokens chose, refilled
+//                 by idle waves): per branch, pass 1 recomputes the
 //                 branch's log-sum-exp and output o (online softmax), giving
 //                 D = dout . o and the gate gradient; pass 2 forms
 //                 dS = sigma P (dP - D) and dq^T += K^T dS^T; V^T and K^T
@@ -212,6 +215,7 @@ __global__ __launch_bounds__(64) void bwd_selfill_kernel(BwdParams p) {
 constexpr int kQWaves = 8;        // query tiles (one per wave) per workgroup
 constexpr int kMaxVTile = 8192;   // vision blocks (the prefill limit)
 constexpr int kMaxTopk = 64;
+constexpr int kRingSpin = 1 << 22;  // bounded-wait rounds of the selection ring
 
 // Scores of one tile transposed: s[kt] = K_kt Q^T (16 keys x 16 rows each)
 // from a section of K rows (or of V rows, for dP^T = V dO^T).
@@ -446,9 +450,12 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
   using R = QRows<D, G, false>;
   constexpr int TP = R::TP, DT = D / 16, SEC = BwdTile<D>::SEC, E = BwdTile<D>::E, TW = TP * kQWaves;
   __shared__ __attribute__((aligned(16))) uint16_t lds0[2 * SEC], lds1[2 * SEC];  // the two step buffers
+  __shared__ __attribute__((aligned(16))) uint16_t lds2[2 * SEC];  // third ring slot (selection)
   __shared__ uint32_t ubits[kMaxVTile / 32];   // union of the workgroup's selected blocks
+  __shared__ int16_t wpre[kMaxVTile / 32];     // union entries before each bitmask word
   __shared__ uint16_t ulist[TW * kMaxTopk];    // the union, ascending
   __shared__ int n_union;
+  __shared__ int rpass[kQWaves], rready[3], rnext;  // selection ring: see ring_walk
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // workgroups go to the eight XCDs round-robin: give each XCD one
   // contiguous run of query tiles (neighbours share key tiles in its L2)
@@ -489,6 +496,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     };
     q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[0], sl2, stat, dg, lane);
   }
+  bool ring_bad = false;  // a bounded wait of the selection ring gave up
   // selection: the union of the workgroup's lists, each wave computing the
   // tiles its tokens chose (rows masked to their own token's blocks, keys
   // j <= t)
@@ -523,6 +531,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
           if (lane >= o) incl += v;
         }
         int at = base + incl - c;
+        if (w0 + lane < n_words) wpre[w0 + lane] = (int16_t)at;
         while (bits) {
           ulist[at++] = (uint16_t)(32 * (w0 + lane) + __ffs(bits) - 1);
           bits &= bits - 1u;
@@ -533,35 +542,86 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     }
     __syncthreads();
     const int nu = n_union, tau = r.tau;
+    // Ring walk: the union's tiles pass through three LDS slots and each wave
+    // walks only the positions its tokens chose, at its own pace (no
+    // workgroup barrier per tile). A wave that would wait copies instead: it
+    // claims the next union tile whose slot every wave has left (compare-and-
+    // swap on rnext), copies it, waits for its own copies and publishes it in
+    // the slot's ready word (rready[s] = position + 1); rpass[w] = first
+    // position wave w may still read. Waits are bounded: a wave that gives up
+    // flags the status word and writes NaN gradients.
+    constexpr int RS = 3;
+    const uint16_t *tv = p.tile_v + (int64_t)g * p.n_vtile * E;
+    auto slot_of = [&](int j) -> uint16_t * { const int sl = j % RS; return sl == 0 ? lds0 : sl == 1 ? lds1 : lds2; };
+    auto try_copy = [&]() -> bool {
+      const int j = __builtin_amdgcn_readfirstlane(lds_load(&rnext));
+      if (j >= nu) return false;
+      const int pv = lane < kQWaves ? lds_load(&rpass[lane]) : 0x7fffffff;
+      int mn = pv;
+#pragma unroll
+      for (int q = 0; q < kQWaves; ++q) mn = min(mn, __builtin_amdgcn_readlane(pv, q));
+      if (j > mn + RS - 1) return false;
+      int won = 0;
+      if (lane == 0) won = atomicCAS(&rnext, j, j + 1) == j;
+      if (!__builtin_amdgcn_readfirstlane(won)) return false;
+      const int blk = __builtin_amdgcn_readfirstlane((int)ulist[j]);
+      asm volatile("" ::: "memory");
+      dma_pieces<E / 512>(tv + (int64_t)blk * E, slot_of(j), lane);
+      wait_vm_c<0>();
+      asm volatile("" ::: "memory");
+      if (lane == 0) lds_store(&rready[j % RS], j + 1);
+      return true;
+    };
     auto walk = [&](auto pass, auto f) {
-      int cur[TP], nxt[TP];
+      __syncthreads();  // every wave has left the slots of the previous walk
+      if (tid < kQWaves) rpass[tid] = 0;
+      if (tid < RS) rready[tid] = 0;
+      if (tid == 0) rnext = 0;
+      __syncthreads();
+      int cur[TP], nxt[TP], last = -1;
 #pragma unroll
       for (int q = 0; q < TP; ++q) {
         cur[q] = 0;
         nxt[q] = __builtin_amdgcn_readlane(lst[q], 0);
       }
-      lockstep<D, decltype(pass)::value>(
-          nu, [&](int i) { return p.tile_v + ((int64_t)g * p.n_vtile + ulist[i]) * E; }, lds0, lds1,
-          [&](int i, const uint16_t *b) {
-            const int u = ulist[i];
-            uint32_t need = 0u;
+      for (;;) {
+        int u = kSentinel;
 #pragma unroll
-            for (int q = 0; q < TP; ++q) {
-              if (nxt[q] == u) {
-                need |= 1u << q;
-                ++cur[q];
-                nxt[q] = cur[q] < p.topk ? __builtin_amdgcn_readlane(lst[q], cur[q]) : kSentinel;
-              }
-            }
-            if (need) {  // wave-uniform
-              const bool rowneed = r.rv && ((need >> tau) & 1u);
-              const int j0 = u * kBlk + 4 * grp;
-              f(b, b + SEC, [&](int kt, int e) { return rowneed && j0 + 16 * kt + e <= tok; });
-            }
-          },
-          wv, lane);
+        for (int q = 0; q < TP; ++q) u = min(u, nxt[q]);
+        if (u == kSentinel) break;
+        uint32_t need = 0u;
+#pragma unroll
+        for (int q = 0; q < TP; ++q) {
+          if (nxt[q] == u) {
+            need |= 1u << q;
+            ++cur[q];
+            nxt[q] = cur[q] < p.topk ? __builtin_amdgcn_readlane(lst[q], cur[q]) : kSentinel;
+          }
+        }
+        const uint32_t wbits = ubits[u >> 5];
+        const int pos = __builtin_amdgcn_readfirstlane((int)wpre[u >> 5] + __popc(wbits & ((1u << (u & 31)) - 1u)));
+        if (pos <= last) continue;  // a list out of ascending order: its slot may be gone
+        last = pos;
+        if (lane == 0) lds_store(&rpass[wv], pos);
+        for (int spins = 0; lds_load(&rready[pos % RS]) != pos + 1;) {
+          if (!try_copy()) __builtin_amdgcn_s_sleep(1);
+          if (++spins > kRingSpin) { ring_bad = true; break; }
+        }
+        asm volatile("" ::: "memory");
+        const uint16_t *b = slot_of(pos);
+        const bool rowneed = r.rv && ((need >> tau) & 1u);
+        const int j0 = u * kBlk + 4 * grp;
+        f(b, b + SEC, [&](int kt, int e) { return rowneed && j0 + 16 * kt + e <= tok; });
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's slot reads have returned
+      if (lane == 0) lds_store(&rpass[wv], nu);
+      for (int spins = 0; __builtin_amdgcn_readfirstlane(lds_load(&rnext)) < nu;) {  // copy for the rest
+        if (!try_copy()) __builtin_amdgcn_s_sleep(1);
+        if (++spins > kRingSpin) { ring_bad = true; break; }
+      }
     };
     q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[1], sl2, stat + 2, dg + 1, lane);
+    __syncthreads();  // no wave still reads a ring slot when the next branch copies into lds0 / lds1
   }
   // sliding window: keys t - w < j <= t
   {
@@ -581,10 +641,12 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     };
     q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[2], sl2, stat + 4, dg + 2, lane);
   }
+  if (ring_bad && lane == 0 && p.status) atomicOr(p.status, kStatusWaitGaveUp);
+  const float dqs = ring_bad ? __builtin_nanf("") : p.scale;
   if (r.rv) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4 *>(p.dq + r.qrow * D + 16 * dt + 4 * grp) = dqa[dt] * p.scale;
+      *reinterpret_cast<f32x4 *>(p.dq + r.qrow * D + 16 * dt + 4 * grp) = dqa[dt] * dqs;
   }
 }
 
