@@ -399,7 +399,8 @@ nsa_status nsa_probe_block_stream(const void *buf, int64_t n_blocks, int32_t n_w
 nsa_status nsa_workspace_status(const void *workspace, void *stream, int32_t *flags);
 
 /* Test aid: the number of s_sleep rounds a bounded wait of the prefill
- * kernels spins before giving up, for calls enqueued afterwards in this
+ * kernels (and of the backward's query-side selection walk) spins before
+ * giving up, for calls enqueued afterwards in this
  * process (rounds <= 0 restores the default, about 0.1 s). A tiny limit
  * makes the waits give up, so that the failure path -- every kernel ending
  * normally, NaN outputs, the status word set -- can be exercised. */

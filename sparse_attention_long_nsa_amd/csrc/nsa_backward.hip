@@ -215,7 +215,6 @@ __global__ __launch_bounds__(64) void bwd_selfill_kernel(BwdParams p) {
 constexpr int kQWaves = 8;        // query tiles (one per wave) per workgroup
 constexpr int kMaxVTile = 8192;   // vision blocks (the prefill limit)
 constexpr int kMaxTopk = 64;
-constexpr int kRingSpin = 1 << 22;  // bounded-wait rounds of the selection ring
 
 // Scores of one tile transposed: s[kt] = K_kt Q^T (16 keys x 16 rows each)
 // from a section of K rows (or of V rows, for dP^T = V dO^T).
@@ -605,7 +604,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
         if (lane == 0) lds_store(&rpass[wv], pos);
         for (int spins = 0; lds_load(&rready[pos % RS]) != pos + 1;) {
           if (!try_copy()) __builtin_amdgcn_s_sleep(1);
-          if (++spins > kRingSpin) { ring_bad = true; break; }
+          if (++spins > p.spin_limit) { ring_bad = true; break; }
         }
         asm volatile("" ::: "memory");
         const uint16_t *b = slot_of(pos);
@@ -617,7 +616,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
       if (lane == 0) lds_store(&rpass[wv], nu);
       for (int spins = 0; __builtin_amdgcn_readfirstlane(lds_load(&rnext)) < nu;) {  // copy for the rest
         if (!try_copy()) __builtin_amdgcn_s_sleep(1);
-        if (++spins > kRingSpin) { ring_bad = true; break; }
+        if (++spins > p.spin_limit) { ring_bad = true; break; }
       }
     };
     q_branch<D>(p, walk, qf, of, dqa, r.rv, r.qrow, sig[1], sl2, stat + 2, dg + 1, lane);

@@ -550,6 +550,7 @@ nsa_status nsa_prefill_backward(const nsa_prefill_desc *desc, const void *q, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   BwdParams bp{};
+  bp.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   bp.q = static_cast<const uint16_t *>(q);
   bp.k = static_cast<const uint16_t *>(k);
   bp.v = static_cast<const uint16_t *>(v);

@@ -140,6 +140,7 @@ struct BwdParams {
   float *cpart;                         // [n_ctile][n_chunk][Hkv][2][64][d] partial compressed grads
   float *tpart;                         // [n_tsplit][N_t Hq][d + 2] text rows' per-split partials
   int32_t *status;                      // the workspace's status word (bit 1: an fp16 range overflow)
+  int spin_limit = 1 << 22;             // bounded-wait rounds of the query side's selection ring
   int64_t n, v0, n_vis;
   int hq, hkv, topk, window, n_blk;
   float scale;

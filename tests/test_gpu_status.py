@@ -118,3 +118,40 @@ def test_backward_flags_values_past_fp16_range(what):
     flags = binding.workspace_status(ws)
     print("status word:", flags, flush=True)
     assert (flags & 2) == (0 if what == "none" else 2)
+
+
+def test_backward_forced_give_up_is_reported_and_recovers():
+    """The backward's query-side selection ring waits are bounded too: with
+    the spin limit forced down they give up, every kernel still ends, bit 0
+    of the status word is set and dq holds NaN; with the default limit the
+    next call is clean and bitwise equal to a call that never gave up."""
+    from sparse_attention_long_nsa_amd.inputs import make_output_grad
+    import oracle
+    inp = make_prefill_inputs(BWD_SHAPE, seed=26)
+    print(f"\n[case] backward forced give-up: {BWD_SHAPE}", flush=True)
+    vis = np.asarray(inp["is_vision"]).astype(bool)
+    sel = torch.from_numpy(oracle.prefill(inp, want=("sel",))["sel"][vis]).to("cuda:0")
+    dout = torch.from_numpy(make_output_grad((BWD_SHAPE.n_tokens, BWD_SHAPE.n_q_heads, BWD_SHAPE.head_dim),
+                                             seed=27)).to("cuda:0")
+    dev = upload(inp)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+
+    def call():
+        return binding.prefill_backward(dev["q"], dev["k"], dev["v"], inp["is_vision"], dev["w_k"], dev["w_v"],
+                                        dev["gates"], sel, dout, BWD_SHAPE.top_k, BWD_SHAPE.window, workspace=ws)
+
+    clean = {n: t.cpu().numpy() for n, t in call().items()}
+    assert binding.workspace_status(ws) == 0
+    try:
+        binding.set_spin_limit(1)
+        r = call()
+        flags = binding.workspace_status(ws)
+        print("status word with spin limit 1:", flags, flush=True)
+        assert flags & 1
+        assert not np.all(np.isfinite(r["dq"].cpu().numpy()))
+    finally:
+        binding.set_spin_limit(0)
+    again = {n: t.cpu().numpy() for n, t in call().items()}
+    assert binding.workspace_status(ws) == 0
+    for n in clean:
+        assert np.array_equal(clean[n], again[n]), n
