@@ -1112,10 +1112,22 @@ __global__ __launch_bounds__(D) void bwd_cmp_w_kernel(BwdParams p) {
   const int i = blockIdx.x % D, which = blockIdx.x / D, j = threadIdx.x;
   const float *dy = which ? p.dvc : p.dkc;
   const float *x = which ? p.vbar : p.kbar;
-  float acc = 0.f;
+  // eight independent partial sums over rows r = 8 q + u (fixed order, so
+  // the result is bitwise repeatable): sixteen rows' loads in flight per
+  // thread instead of one dependent load-and-add chain over every row
+  float acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
   const int64_t rows = (int64_t)p.n_blk * p.hkv;
-  for (int64_t r = 0; r < rows; ++r) acc = fmaf(dy[r * D + i], x[r * D + j], acc);
-  (which ? p.dwv : p.dwk)[i * D + j] = acc;
+  int64_t r = 0;
+#pragma unroll 2
+  for (; r + 8 <= rows; r += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = fmaf(dy[(r + u) * D + i], x[(r + u) * D + j], acc[u]);
+  }
+  for (int u = 0; r < rows; ++r, ++u) acc[u] = fmaf(dy[r * D + i], x[r * D + j], acc[u]);
+  (which ? p.dwv : p.dwk)[i * D + j] =
+      ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
 // Each block's share of the tokens' gradients: W^T dK_cmp / 64 added to the
