@@ -1108,26 +1108,29 @@ __global__ __launch_bounds__(D) void bwd_creduce_kernel(BwdParams p) {
 // dW = sum over (block, group) of dK_cmp (x) mean; one workgroup of D
 // threads per row i of dW (k and v maps).
 template <int D>
-__global__ __launch_bounds__(D) void bwd_cmp_w_kernel(BwdParams p) {
-  const int i = blockIdx.x % D, which = blockIdx.x / D, j = threadIdx.x;
+__global__ __launch_bounds__(4 * D) void bwd_cmp_w_kernel(BwdParams p) {
+  __shared__ float part[4][D];
+  const int i = blockIdx.x % D, which = blockIdx.x / D, j = threadIdx.x % D, h = threadIdx.x / D;
   const float *dy = which ? p.dvc : p.dkc;
   const float *x = which ? p.vbar : p.kbar;
-  // eight independent partial sums over rows r = 8 q + u (fixed order, so
-  // the result is bitwise repeatable): sixteen rows' loads in flight per
-  // thread instead of one dependent load-and-add chain over every row
+  // four contiguous quarters of the rows, each summed in eight interleaved
+  // partial sums (sixteen rows' loads in flight), then added in quarter
+  // order: a fixed order, so the result is bitwise repeatable
+  const int64_t rows = (int64_t)p.n_blk * p.hkv, q = (rows + 3) / 4;
+  const int64_t r0 = min(rows, h * q), r1 = min(rows, r0 + q);
   float acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-  const int64_t rows = (int64_t)p.n_blk * p.hkv;
-  int64_t r = 0;
+  int64_t r = r0;
 #pragma unroll 2
-  for (; r + 8 <= rows; r += 8) {
+  for (; r + 8 <= r1; r += 8) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = fmaf(dy[(r + u) * D + i], x[(r + u) * D + j], acc[u]);
   }
-  for (int u = 0; r < rows; ++r, ++u) acc[u] = fmaf(dy[r * D + i], x[r * D + j], acc[u]);
-  (which ? p.dwv : p.dwk)[i * D + j] =
-      ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  for (int u = 0; r < r1; ++r, ++u) acc[u] = fmaf(dy[r * D + i], x[r * D + j], acc[u]);
+  part[h][j] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  __syncthreads();
+  if (h == 0) (which ? p.dwv : p.dwk)[i * D + j] = (part[0][j] + part[1][j]) + (part[2][j] + part[3][j]);
 }
 
 // Each block's share of the tokens' gradients: W^T dK_cmp / 64 added to the
@@ -1242,7 +1245,7 @@ hipError_t run(const BwdParams &p, int stage, hipStream_t st) {
       if (p.n_blk > 0) hipLaunchKernelGGL((bwd_creduce_kernel<D>), dim3(p.n_blk * p.hkv), dim3(D), 0, st, p);
       break;
     case 12:
-      hipLaunchKernelGGL((bwd_cmp_w_kernel<D>), dim3(2 * D), dim3(D), 0, st, p);
+      hipLaunchKernelGGL((bwd_cmp_w_kernel<D>), dim3(2 * D), dim3(4 * D), 0, st, p);
       break;
     default:
       if (p.n_blk > 0) hipLaunchKernelGGL((bwd_cmp_tok_kernel<D>), dim3(p.n_blk * p.hkv), dim3(D), 0, st, p);
